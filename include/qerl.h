@@ -1,0 +1,184 @@
+/*
+ * qerl.h -- C ABI of libqerl: the rollout-phase linear layer of QeRL on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, each backed by hand-written HIP kernels:
+ *   qerl_nvfp4_quantize   BF16 weight -> NVFP4 (E2M1 codes, one E4M3 scale per
+ *                         16 values along K, one FP32 tensor scale);
+ *   qerl_w4a16_lora_gemm  y = x * deq(W)^T + lora_scale * (x * A^T) * B^T with
+ *                         NVFP4 W, BF16 x, BF16 LoRA A/B, BF16 y;
+ *   qerl_aqn_rmsnorm      RMSNorm whose FP32 scale vector carries the adaptive
+ *                         quantization noise w + sigma * z (z channel-wise N(0,1)).
+ *
+ * Sources (page -- section):
+ *   NVFP4 format and block scaling: "QeRL: NVFP4-Quantized Reinforcement
+ *     Learning -- Redefining Efficiency in AI Training and Inference", section
+ *     "NVFP4: NVIDIA's FP4 Format" (16-value blocks, E4M3 block scale, FP32
+ *     tensor scale, scale = round_up(amax / vmax), value = round_to_even(v / scale)).
+ *   NVFP4 x BF16 rollout kernel with LoRA: "NVlabs/QeRL" README,
+ *     "Acknowledgement"; bitsofall page, "LoRA (Low-Rank Adaptation)" and
+ *     "Implementation and Practical Details" (weight-only; NVFP4 + LoRA sum).
+ *   AQN: "Paper 2510.11696 -- QeRL: Beyond Efficiency", "Summary" (channel-wise
+ *     Gaussian noise through the normalization layer, exponential decay);
+ *     README "Hints for QeRL training", item 3 (sigma_start, sigma_end,
+ *     num_stages).
+ *
+ * Conventions for every call:
+ *   - All array arguments are DEVICE pointers into caller-owned memory; the
+ *     library never allocates, frees or retains them.  BF16 arrays are passed as
+ *     void* to 16-bit payloads.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work: QERL_OK means "enqueued"; device faults surface at the caller's next
+ *     synchronization.  Calls are stream-ordered and thread-safe.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     the call then returns a non-OK status and touches no memory.
+ *   - Alignment (else QERL_ERR_ALIGN): the arrays a call streams with 16-byte
+ *     vector loads -- w, packed, scales, workspace of the quantizer; x, packed,
+ *     scales, lora_a, lora_b, workspace of the GEMM -- must be 16-byte aligned
+ *     and their leading dimensions (ldw, ldx of the GEMM) multiples of 8
+ *     elements.  Every other pointer needs only the alignment of its element
+ *     type, and other leading dimensions are free.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef QERL_H
+#define QERL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qerl_status {
+    QERL_OK = 0,
+    QERL_ERR_NULL = 1,      /* a required pointer is NULL */
+    QERL_ERR_SHAPE = 2,     /* a size is non-positive, too large, or k % 16 != 0 */
+    QERL_ERR_ALIGN = 3,     /* a pointer or leading dimension breaks the alignment rule */
+    QERL_ERR_ARG = 4,       /* a scalar argument is out of range (flags, rank, eps, sigma) */
+    QERL_ERR_WORKSPACE = 5, /* workspace NULL or smaller than the size query returns */
+    QERL_ERR_HIP = 6        /* the HIP runtime rejected a launch; see qerl_last_error() */
+} qerl_status;
+
+/* flags of qerl_nvfp4_quantize, bit 0: how the block scale is rounded to E4M3 */
+#define QERL_SCALE_ROUND_UP 0u /* least E4M3 value >= amax_b / (6 s_t) (default) */
+#define QERL_SCALE_RNE 1u      /* nearest E4M3 value, ties to the even code */
+
+#define QERL_MAX_LORA_RANK 128
+#define QERL_MAX_NORM_WIDTH 16384
+
+/* ----------------------------------------------------------------------- */
+/* BF16 -> NVFP4 quantizer                                                   */
+/* ----------------------------------------------------------------------- */
+/* Bytes of device workspace qerl_nvfp4_quantize needs for an [n, k] weight. */
+size_t qerl_nvfp4_quantize_workspace_size(int64_t n, int64_t k);
+
+/*
+ * Quantize W (BF16, [n, k] row-major, row stride ldw >= k elements) to NVFP4,
+ * following the block-scaling formula of the bitsofall page ("NVFP4: NVIDIA's
+ * FP4 Format"), with the two-level scale of the same section:
+ *   s_t   = fl32(amax(|W|) / 2688)          (2688 = 6 * 448; s_t = 1 if W == 0)
+ *   sb    = E4M3 rounding of amax_b / (6 s_t) per block of 16 along k, clamped
+ *           to 448 (flags: QERL_SCALE_ROUND_UP or QERL_SCALE_RNE)
+ *   code  = signbit(w) << 3 | RNE of |w| / (E4M3(sb) s_t) onto the E2M1 grid
+ *           {0, .5, 1, 1.5, 2, 3, 4, 6} (saturating at 6; all 0 when sb == 0)
+ * All rounding decisions are exact (the result is the unique one defined by
+ * exact rational arithmetic).
+ *
+ * Outputs (device, caller-owned):
+ *   packed       uint8 [n, k/2]: byte j of a row holds element 2j in its low
+ *                nibble and element 2j+1 in its high nibble;
+ *   scales       uint8 [n, k/16]: E4M3 (OCP "FN") byte of each block;
+ *   tensor_scale float [1]: s_t, a decode multiplier: w ~= e2m1 * e4m3 * s_t.
+ * tensor_scale_in (device, nullable): when given, that s_t is used unchanged
+ *   and the tensor amax pass is skipped; it must be positive and finite.
+ * Non-finite input (a NaN or Inf weight, or an invalid tensor_scale_in) is
+ * reported in-band: *tensor_scale = NaN, packed and scales unspecified.
+ * Requires n >= 1, k >= 16, k % 16 == 0, workspace_bytes >= the size query.
+ */
+qerl_status qerl_nvfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                const float *tensor_scale_in, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------- */
+/* W4A16 (NVFP4 weight x BF16 activation) linear layer with LoRA epilogue   */
+/* ----------------------------------------------------------------------- */
+/* Bytes of device workspace qerl_w4a16_lora_gemm needs. */
+size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t r);
+
+/*
+ * y[m, n] = sum_k x[m,k] * e2m1(q[n,k]) * e4m3(sb[n,k/16]) * s_t
+ *         + lora_scale * sum_j (sum_k x[m,k] * A[j,k]) * B[n,j]
+ * i.e. the frozen NVFP4 base (README "Acknowledgement": NVFP4 x BF16 kernel)
+ * plus the BF16 low-rank update (bitsofall "LoRA (Low-Rank Adaptation)";
+ * lora_scale is alpha / r).  No bias.  FP32 accumulation, BF16 (RNE) output.
+ *
+ *   x_bf16        [m, k], row stride ldx >= k
+ *   packed, scales, tensor_scale   as written by qerl_nvfp4_quantize for an
+ *                 [n, k] weight (tensor_scale is a device pointer)
+ *   lora_a_bf16   [r, k] contiguous; lora_b_bf16 [n, r] contiguous; both may be
+ *                 NULL only when r == 0 (no LoRA)
+ *   y_bf16        [m, n], row stride ldy >= n; must not overlap any input
+ * Small m takes an HBM-streaming GEMV path (E2M1 decode in registers, wave
+ * reductions); larger m a BF16-MFMA path on dequantized tiles with the LoRA
+ * product folded into the same accumulation.
+ * Requires m, n >= 1, k >= 16, k % 16 == 0, 0 <= r <= QERL_MAX_LORA_RANK,
+ * finite lora_scale, workspace_bytes >= the size query.
+ */
+qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                 const uint8_t *packed, const uint8_t *scales,
+                                 const float *tensor_scale, int64_t n,
+                                 const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                 float lora_scale, void *y_bf16, int64_t ldy,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------- */
+/* AQN RMSNorm                                                               */
+/* ----------------------------------------------------------------------- */
+/*
+ * sigma of noise stage `stage` out of `num_stages` (README "Hints for QeRL
+ * training", item 3; exponential decay per the 1kpapers "Summary"):
+ *   sigma_k = sigma_start * (sigma_end / sigma_start)^(k / (num_stages - 1)),
+ * stage clamped to [0, num_stages - 1]; num_stages <= 1 gives sigma_start.
+ * Host-only; returns NaN for non-positive or non-finite sigma_start/sigma_end.
+ */
+float qerl_aqn_sigma(int32_t stage, int32_t num_stages, float sigma_start, float sigma_end);
+
+/*
+ * y[i, c] = x[i, c] / sqrt(mean_c x[i, c]^2 + eps) * (w[c] + sigma * z[c])
+ * The noise z is one channel-wise N(0, 1) vector shared by every row (the
+ * 1kpapers "Summary": channel-wise Gaussian noise via the normalization layer;
+ * dataforcee page: it lives in the norm's scale parameters).  z is defined by
+ * counter-based Philox4x64-10 (Salmon et al., SC'11) with key (seed, layer_id)
+ * and counter (c / 4, step, 0, 0); its four words r0..r3 give channels 4i..4i+3
+ * by Box-Muller: u1 = ((ra >> 40) + 1) 2^-24, u2 = (rb >> 40) 2^-24,
+ * z = sqrt(-2 ln u1) * (cos, sin)(2 pi u2) for (ra, rb) = (r0, r1), (r2, r3).
+ *
+ *   x_bf16   [m, h] with row stride ldx >= h; weight FP32 [h]
+ *   y_f32    FP32 [m, h] (nullable), y_bf16 BF16 [m, h] (nullable, RNE of the
+ *            FP32 value); at least one must be given; both use row stride ldy
+ *   noisy_weight_out FP32 [h] (nullable): w + sigma * z
+ * Requires m, h >= 1, h <= QERL_MAX_NORM_WIDTH, eps > 0 and finite,
+ * sigma >= 0 and finite.
+ */
+qerl_status qerl_aqn_rmsnorm(const void *x_bf16, int64_t m, int64_t h, int64_t ldx,
+                             const float *weight, float eps, float sigma,
+                             uint64_t seed, uint64_t step, uint32_t layer_id,
+                             float *y_f32, void *y_bf16, int64_t ldy,
+                             float *noisy_weight_out, void *stream);
+
+/* ----------------------------------------------------------------------- */
+/* diagnostics                                                               */
+/* ----------------------------------------------------------------------- */
+/* Static English text for a status code. */
+const char *qerl_status_string(qerl_status status);
+/* Text of the last error on the calling thread ("" if none); valid until the
+ * next library call on that thread. */
+const char *qerl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QERL_H */

@@ -1,0 +1,187 @@
+// api.cpp -- the C ABI of libqerl (declared in include/qerl.h): argument
+// validation on the host, then dispatch to the HIP launchers.  Nothing is
+// enqueued when validation fails.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qerl.h"
+#include "qerl_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qerl_status fail(qerl_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+qerl_status fail(qerl_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qerl_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return QERL_OK;
+    return fail(QERL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest element count a single tensor may have (keeps 64-bit index math far
+// from overflow and every grid dimension in range).
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+const char *qerl_status_string(qerl_status s) {
+    switch (s) {
+        case QERL_OK: return "ok";
+        case QERL_ERR_NULL: return "a required pointer is NULL";
+        case QERL_ERR_SHAPE: return "a size is out of range";
+        case QERL_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+        case QERL_ERR_ARG: return "a scalar argument is out of range";
+        case QERL_ERR_WORKSPACE: return "workspace missing or too small";
+        case QERL_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *qerl_last_error(void) { return g_last_error; }
+
+size_t qerl_nvfp4_quantize_workspace_size(int64_t n, int64_t k) {
+    return qerl::quantize_workspace_bytes(n, k);
+}
+
+qerl_status qerl_nvfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                const float *tensor_scale_in, uint32_t flags,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!w_bf16 || !packed || !scales || !tensor_scale)
+        return fail(QERL_ERR_NULL, "nvfp4_quantize: w, packed, scales and tensor_scale are required");
+    if (n < 1 || k < 16 || k % 16 != 0 || ldw < k || n > kMaxElems / k || ldw > kMaxElems)
+        return fail(QERL_ERR_SHAPE, "nvfp4_quantize: need n >= 1, k >= 16, k %% 16 == 0, ldw >= k "
+                    "(got n=%lld k=%lld ldw=%lld)", (long long)n, (long long)k, (long long)ldw);
+    if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(scales) || ldw % 8 != 0 ||
+        ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)tensor_scale_in & 3u))
+        return fail(QERL_ERR_ALIGN, "nvfp4_quantize: pointers must be 16-byte aligned and ldw %% 8 == 0");
+    if (flags & ~1u) return fail(QERL_ERR_ARG, "nvfp4_quantize: unknown flag bits 0x%x", flags);
+    if (!tensor_scale_in && (!workspace || workspace_bytes < qerl::quantize_workspace_bytes(n, k)))
+        return fail(QERL_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed",
+                    qerl::quantize_workspace_bytes(n, k));
+    if (workspace && !aligned16(workspace))
+        return fail(QERL_ERR_ALIGN, "nvfp4_quantize: workspace must be 16-byte aligned");
+    return hip_status(qerl::launch_nvfp4_quantize(static_cast<const uint16_t *>(w_bf16), n, k, ldw,
+                                                  packed, scales, tensor_scale, tensor_scale_in,
+                                                  flags, workspace, static_cast<hipStream_t>(stream)),
+                      "nvfp4_quantize launch");
+}
+
+size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int32_t r) {
+    return qerl::gemm_workspace_bytes(m, n, k, r);
+}
+
+qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                 const uint8_t *packed, const uint8_t *scales,
+                                 const float *tensor_scale, int64_t n,
+                                 const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                 float lora_scale, void *y_bf16, int64_t ldy,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!x_bf16 || !packed || !scales || !tensor_scale || !y_bf16)
+        return fail(QERL_ERR_NULL, "w4a16_lora_gemm: x, packed, scales, tensor_scale and y are required");
+    if (r < 0 || r > QERL_MAX_LORA_RANK)
+        return fail(QERL_ERR_ARG, "w4a16_lora_gemm: LoRA rank %d outside [0, %d]", r, QERL_MAX_LORA_RANK);
+    if (r > 0 && (!lora_a_bf16 || !lora_b_bf16))
+        return fail(QERL_ERR_NULL, "w4a16_lora_gemm: lora_a and lora_b are required when r > 0");
+    if (!isfinite(lora_scale)) return fail(QERL_ERR_ARG, "w4a16_lora_gemm: lora_scale must be finite");
+    if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || ldx < k || ldy < n || m > kMaxElems / k ||
+        n > kMaxElems / k || m > kMaxElems / ldy || ldx > kMaxElems || m > ((int64_t)1 << 24) ||
+        n > ((int64_t)1 << 28))
+        return fail(QERL_ERR_SHAPE, "w4a16_lora_gemm: need m, n >= 1, k >= 16, k %% 16 == 0, ldx >= k, "
+                    "ldy >= n (got m=%lld n=%lld k=%lld ldx=%lld ldy=%lld)", (long long)m,
+                    (long long)n, (long long)k, (long long)ldx, (long long)ldy);
+    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(scales) || ((uintptr_t)y_bf16 & 1u) ||
+        ((uintptr_t)tensor_scale & 3u) || ldx % 8 != 0 ||
+        (r > 0 && (!aligned16(lora_a_bf16) || !aligned16(lora_b_bf16))))
+        return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm: x, packed, scales, lora_a, lora_b must be 16-byte "
+                    "aligned, y 2-byte aligned, ldx %% 8 == 0");
+    const size_t need = qerl::gemm_workspace_bytes(m, n, k, r);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm: workspace of %zu bytes needed", need);
+    if (workspace && !aligned16(workspace))
+        return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm: workspace must be 16-byte aligned");
+    qerl::GemmArgs a;
+    a.x = static_cast<const uint16_t *>(x_bf16);
+    a.m = m;
+    a.k = k;
+    a.ldx = ldx;
+    a.packed = packed;
+    a.scales = scales;
+    a.tensor_scale = tensor_scale;
+    a.n = n;
+    a.lora_a = static_cast<const uint16_t *>(lora_a_bf16);
+    a.lora_b = static_cast<const uint16_t *>(lora_b_bf16);
+    a.r = r;
+    a.lora_scale = lora_scale;
+    a.y = static_cast<uint16_t *>(y_bf16);
+    a.ldy = ldy;
+    a.workspace = workspace;
+    return hip_status(qerl::launch_w4a16_lora_gemm(a, static_cast<hipStream_t>(stream)),
+                      "w4a16_lora_gemm launch");
+}
+
+float qerl_aqn_sigma(int32_t stage, int32_t num_stages, float sigma_start, float sigma_end) {
+    if (!(sigma_start > 0.0f) || !(sigma_end > 0.0f) || !isfinite(sigma_start) || !isfinite(sigma_end))
+        return NAN;
+    if (num_stages <= 1) return sigma_start;
+    if (stage < 0) stage = 0;
+    if (stage > num_stages - 1) stage = num_stages - 1;
+    const double ratio = (double)sigma_end / (double)sigma_start;
+    return (float)((double)sigma_start * pow(ratio, (double)stage / (double)(num_stages - 1)));
+}
+
+qerl_status qerl_aqn_rmsnorm(const void *x_bf16, int64_t m, int64_t h, int64_t ldx,
+                             const float *weight, float eps, float sigma,
+                             uint64_t seed, uint64_t step, uint32_t layer_id,
+                             float *y_f32, void *y_bf16, int64_t ldy,
+                             float *noisy_weight_out, void *stream) {
+    g_last_error[0] = '\0';
+    if (!x_bf16 || !weight) return fail(QERL_ERR_NULL, "aqn_rmsnorm: x and weight are required");
+    if (!y_f32 && !y_bf16) return fail(QERL_ERR_NULL, "aqn_rmsnorm: give y_f32, y_bf16 or both");
+    if (m < 1 || h < 1 || h > QERL_MAX_NORM_WIDTH || ldx < h || ldy < h || m > kMaxElems / ldx ||
+        m > kMaxElems / ldy)
+        return fail(QERL_ERR_SHAPE, "aqn_rmsnorm: need m >= 1, 1 <= h <= %d, ldx >= h, ldy >= h "
+                    "(got m=%lld h=%lld ldx=%lld ldy=%lld)", QERL_MAX_NORM_WIDTH, (long long)m,
+                    (long long)h, (long long)ldx, (long long)ldy);
+    if (((uintptr_t)x_bf16 & 1u) || ((uintptr_t)weight & 3u) || ((uintptr_t)y_f32 & 3u) ||
+        ((uintptr_t)y_bf16 & 1u) || ((uintptr_t)noisy_weight_out & 3u))
+        return fail(QERL_ERR_ALIGN, "aqn_rmsnorm: pointers must be aligned to their element size");
+    if (!(eps > 0.0f) || !isfinite(eps)) return fail(QERL_ERR_ARG, "aqn_rmsnorm: eps must be positive and finite");
+    if (!(sigma >= 0.0f) || !isfinite(sigma))
+        return fail(QERL_ERR_ARG, "aqn_rmsnorm: sigma must be non-negative and finite");
+    qerl::AqnArgs a;
+    a.x = static_cast<const uint16_t *>(x_bf16);
+    a.m = m;
+    a.h = h;
+    a.ldx = ldx;
+    a.weight = weight;
+    a.eps = eps;
+    a.sigma = sigma;
+    a.seed = seed;
+    a.step = step;
+    a.layer = layer_id;
+    a.y_f32 = y_f32;
+    a.y_bf16 = static_cast<uint16_t *>(y_bf16);
+    a.ldy = ldy;
+    a.noisy_out = noisy_weight_out;
+    return hip_status(qerl::launch_aqn_rmsnorm(a, static_cast<hipStream_t>(stream)), "aqn_rmsnorm launch");
+}
+
+}  // extern "C"

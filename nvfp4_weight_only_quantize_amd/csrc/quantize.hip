@@ -1,0 +1,260 @@
+// quantize.hip -- BF16 -> NVFP4 quantizer for gfx950.
+//
+// Block scaling of the cuDNN formula quoted on "QeRL: NVFP4-Quantized
+// Reinforcement Learning -- Redefining Efficiency in AI Training and
+// Inference", section "NVFP4: NVIDIA's FP4 Format": per block of 16 values
+// along K, scale = round_up(amax / 6) as an E4M3 byte (relative to an FP32
+// tensor scale, the second level of the same section) and each value rounded
+// to nearest-even on the E2M1 grid.
+//
+// Two HBM passes (the tensor amax must be known before any block is encoded):
+//   pass 1  amax_kernel: 16-byte loads, integer max of (bits & 0x7FFF) -- exact
+//           for BF16 magnitudes and >= 0x7F80 exactly when a value is Inf/NaN;
+//           one partial per workgroup into the workspace.
+//   pass 2  encode_kernel: every workgroup folds the partials into s_t, then
+//           each thread encodes one 16-element block: 32 B in, 8 B + 1 B out.
+//
+// Exactness: s_t = fl32(amax / 2688) is computed as a double quotient rounded
+// to float (double rounding is harmless since 53 >= 2*24 + 2).  Block-scale
+// decisions compare E4M3 * 6 * s_t (<= 30 significant bits) with the block
+// amax in double, exactly.  Element decisions compare |w| with c * E4M3 * s_t
+// for the seven E2M1 midpoints c through the sign of one fused multiply-add
+// fmaf(c * E4M3, s_t, -|w|): c * E4M3 is exact in float and the fma rounds the
+// exact difference once, so its sign is exact whenever the difference cannot
+// fall below the float subnormal range -- guaranteed for s_t >= 2^-90 (all
+// operands are then multiples of 2^-133).  Smaller s_t takes a double path.
+#include "device_common.h"
+#include "qerl_internal.h"
+
+namespace qerl {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint32_t absmax_pair(uint32_t w) {
+    return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+__device__ __forceinline__ uint32_t absmax_vec(uint4 v) {
+    return max(max(absmax_pair(v.x), absmax_pair(v.y)), max(absmax_pair(v.z), absmax_pair(v.w)));
+}
+
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restrict__ w, int64_t n,
+                                                        int64_t k, int64_t ldw,
+                                                        uint32_t *__restrict__ partial) {
+    uint32_t m = 0;
+    const int64_t vpr = k >> 3;  // 16-byte vectors per row
+    if (ldw == k) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(w);
+        const int64_t total = n * vpr;
+        const int64_t stride = (int64_t)gridDim.x * kThreads;
+        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        for (; i + 3 * stride < total; i += 4 * stride) {
+            uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+            m = max(m, max(max(absmax_vec(a), absmax_vec(b)), max(absmax_vec(c), absmax_vec(d))));
+        }
+        for (; i < total; i += stride) m = max(m, absmax_vec(p[i]));
+    } else {
+        for (int64_t row = blockIdx.x; row < n; row += gridDim.x) {
+            const uint4 *p = reinterpret_cast<const uint4 *>(w + row * ldw);
+            for (int64_t c = threadIdx.x; c < vpr; c += kThreads) m = max(m, absmax_vec(p[c]));
+        }
+    }
+    __shared__ uint32_t red[kThreads / kWave];
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// Exact E4M3 value of code c in 0..126 (non-negative, non-NaN).
+__device__ __forceinline__ float e4m3_value(int c) {
+    const int e = c >> 3, m = c & 7;
+    return e == 0 ? (float)m * 0x1p-9f
+                  : __uint_as_float(((uint32_t)(e + 120) << 23) | ((uint32_t)m << 20));
+}
+
+// Approximate least E4M3 code with value >= t (t >= 0); corrected exactly below.
+__device__ __forceinline__ int e4m3_ceil_code_guess(float t) {
+    if (!(t > 0.0f)) return 0;
+    if (t >= 448.0f) return 126;
+    if (t < 0x1p-6f) return min((int)ceilf(t * 512.0f), 8);
+    const uint32_t u = __float_as_uint(t);
+    int c = (((int)(u >> 23) - 120) << 3) | (int)((u >> 20) & 7);
+    if (u & 0xFFFFFu) ++c;
+    return min(c, 126);
+}
+
+// Least E4M3 code v with E4M3(v) * 6 * s_t >= amax_b (saturating at 448).
+__device__ __forceinline__ int scale_code_round_up(float amax_b, float st) {
+    const double s6 = 6.0 * (double)st;  // exact
+    const double a = (double)amax_b;
+    if (448.0 * s6 < a) return 126;
+    int c = e4m3_ceil_code_guess(amax_b / (6.0f * st));
+    while (c > 0 && (double)e4m3_value(c - 1) * s6 >= a) --c;
+    while (c < 126 && (double)e4m3_value(c) * s6 < a) ++c;
+    return c;
+}
+
+// Nearest E4M3 value to amax_b / (6 s_t), ties to the even code, saturating.
+__device__ __forceinline__ int scale_code_rne(float amax_b, float st) {
+    const double s6 = 6.0 * (double)st;
+    const double a = (double)amax_b;
+    const int hi = scale_code_round_up(amax_b, st);
+    const double vhi = (double)e4m3_value(hi);
+    if (vhi * s6 < a) return 126;
+    if (hi == 0 || vhi * s6 == a) return hi;
+    const double vlo = (double)e4m3_value(hi - 1);
+    const double two_a = 2.0 * a, mid = (vlo + vhi) * s6;  // both exact
+    if (two_a < mid) return hi - 1;
+    if (two_a > mid) return hi;
+    return ((hi - 1) & 1) ? hi : hi - 1;
+}
+
+// E2M1 midpoints between grid neighbours and which side a tie takes: at .75,
+// 1.75 and 3.5 the upper neighbour has the even code, elsewhere the lower.
+__device__ __forceinline__ uint32_t e2m1_mag_f32(float a, const float (&ce)[7], float st) {
+    uint32_t mag = 0;
+    mag += __builtin_fmaf(ce[0], st, -a) < 0.0f;
+    mag += __builtin_fmaf(ce[1], st, -a) <= 0.0f;
+    mag += __builtin_fmaf(ce[2], st, -a) < 0.0f;
+    mag += __builtin_fmaf(ce[3], st, -a) <= 0.0f;
+    mag += __builtin_fmaf(ce[4], st, -a) < 0.0f;
+    mag += __builtin_fmaf(ce[5], st, -a) <= 0.0f;
+    mag += __builtin_fmaf(ce[6], st, -a) < 0.0f;
+    return mag;
+}
+
+__device__ __forceinline__ uint32_t e2m1_mag_f64(float a, const float (&ce)[7], float st) {
+    const double d = (double)a, s = (double)st;
+    uint32_t mag = 0;
+    mag += (double)ce[0] * s < d;
+    mag += (double)ce[1] * s <= d;
+    mag += (double)ce[2] * s < d;
+    mag += (double)ce[3] * s <= d;
+    mag += (double)ce[4] * s < d;
+    mag += (double)ce[5] * s <= d;
+    mag += (double)ce[6] * s < d;
+    return mag;
+}
+
+struct EncodeParams {
+    const uint16_t *w;
+    int64_t n, k, ldw;
+    uint8_t *packed;
+    uint8_t *scales;
+    float *tensor_scale_out;
+    const float *tensor_scale_in;
+    const uint32_t *partial;
+    int num_partials;
+    uint32_t flags;
+};
+
+__global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
+    __shared__ float s_st;
+    if (threadIdx.x < kWave) {
+        float st;
+        if (p.tensor_scale_in) {
+            st = *p.tensor_scale_in;
+            if (!(st > 0.0f && st < INFINITY)) st = __builtin_nanf("");
+        } else {
+            uint32_t m = 0;
+            for (int i = threadIdx.x; i < p.num_partials; i += kWave) m = max(m, p.partial[i]);
+            m = wave_max(m);
+            if (m >= 0x7F80u) st = __builtin_nanf("");
+            else if (m == 0) st = 1.0f;
+            else st = (float)((double)__uint_as_float(m << 16) / 2688.0);
+        }
+        if (threadIdx.x == 0) {
+            s_st = st;
+            if (blockIdx.x == 0) *p.tensor_scale_out = st;
+        }
+    }
+    __syncthreads();
+    const float st = s_st;
+    if (!(st > 0.0f && st < INFINITY)) return;  // non-finite input: outputs unspecified
+    const bool fma_exact = st >= 0x1p-90f;
+    const bool rne = (p.flags & 1u) != 0;
+    const int64_t bpr = p.k >> 4;
+    const int64_t total = p.n * bpr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < total; b += stride) {
+        const uint16_t *src;
+        if (p.ldw == p.k) {
+            src = p.w + b * 16;
+        } else {
+            const int64_t row = b / bpr;
+            src = p.w + row * p.ldw + (b - row * bpr) * 16;
+        }
+        const uint4 v0 = reinterpret_cast<const uint4 *>(src)[0];
+        const uint4 v1 = reinterpret_cast<const uint4 *>(src)[1];
+        const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        const uint32_t am = max(absmax_vec(v0), absmax_vec(v1));
+        const float amax_b = __uint_as_float(am << 16);
+        const int sb = rne ? scale_code_rne(amax_b, st) : scale_code_round_up(amax_b, st);
+        const float e = e4m3_value(sb);
+        uint32_t lo = 0, hi = 0;
+        if (e != 0.0f) {
+            const float ce[7] = {0.25f * e, 0.75f * e, 1.25f * e, 1.75f * e,
+                                 2.5f * e,  3.5f * e,  5.0f * e};
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
+                const float a = __uint_as_float((bits & 0x7FFFu) << 16);
+                const uint32_t mag = fma_exact ? e2m1_mag_f32(a, ce, st) : e2m1_mag_f64(a, ce, st);
+                const uint32_t code = mag | ((bits >> 12) & 8u);
+                if (j < 8) lo |= code << (4 * j);
+                else hi |= code << (4 * (j - 8));
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
+                const uint32_t code = (bits >> 12) & 8u;
+                if (j < 8) lo |= code << (4 * j);
+                else hi |= code << (4 * (j - 8));
+            }
+        }
+        reinterpret_cast<uint2 *>(p.packed)[b] = make_uint2(lo, hi);
+        p.scales[b] = (uint8_t)sb;
+    }
+}
+
+int num_cus() {
+    static int cus = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            return 256;
+        return v;
+    }();
+    return cus;
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t, int64_t) { return kAmaxMaxBlocks * sizeof(uint32_t); }
+
+hipError_t launch_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
+                                 uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                 const float *tensor_scale_in, uint32_t flags, void *workspace,
+                                 hipStream_t stream) {
+    uint32_t *partial = static_cast<uint32_t *>(workspace);
+    int g1 = 0;
+    if (!tensor_scale_in) {
+        const int64_t vecs = n * (k >> 3);
+        const int64_t want = ldw == k ? (vecs + kThreads * 4 - 1) / (kThreads * 4) : n;
+        g1 = (int)(want < kAmaxMaxBlocks ? (want < 1 ? 1 : want) : kAmaxMaxBlocks);
+        hipLaunchKernelGGL(amax_kernel, dim3(g1), dim3(kThreads), 0, stream, w, n, k, ldw, partial);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    EncodeParams p{w, n, k, ldw, packed, scales, tensor_scale, tensor_scale_in, partial, g1, flags};
+    const int64_t blocks16 = n * (k >> 4);
+    const int64_t want = (blocks16 + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)num_cus() * 16;
+    const int g2 = (int)(want < cap ? want : cap);
+    hipLaunchKernelGGL(encode_kernel, dim3(g2), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace qerl

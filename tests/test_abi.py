@@ -1,0 +1,123 @@
+"""The C ABI: libqerl.so loads, exports every function include/qerl.h
+declares, and rejects bad arguments on the host before anything is launched
+(no call here reaches the GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import nvfp4_weight_only_quantize_amd as q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qerl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q.LIB_PATH), reason="libqerl.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qerl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = _declared_functions()
+    assert {"qerl_nvfp4_quantize", "qerl_w4a16_lora_gemm", "qerl_aqn_rmsnorm"} <= set(names)
+    L = ctypes.CDLL(q.LIB_PATH)
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings():
+    L = q.lib()
+    for s in range(7):
+        assert L.qerl_status_string(s)
+    assert L.qerl_status_string(99) == b"unknown status"
+
+
+def test_sigma_schedule_matches_oracle():
+    for k in range(10):
+        got = q.aqn_sigma(k, 10, 1e-2, 5e-4)
+        want = oracle.aqn_sigma(k, 10, float(ctypes.c_float(1e-2).value), float(ctypes.c_float(5e-4).value))
+        assert abs(got - want) <= 1e-7 * want
+    assert q.aqn_sigma(0, 1, 3e-3, 1e-4) == pytest.approx(3e-3)
+    assert math.isnan(q.aqn_sigma(0, 10, 0.0, 1e-4))
+
+
+FAKE = 1 << 20  # a 16-byte-aligned address that is never dereferenced
+P = ctypes.c_void_p
+
+
+def _quant(**kw):
+    a = dict(w=FAKE, n=4, k=32, ldw=32, packed=FAKE, scales=FAKE, ts=FAKE, ts_in=None, flags=0,
+             ws=FAKE, ws_bytes=1 << 16, stream=None)
+    a.update(kw)
+    return q.lib().qerl_nvfp4_quantize(P(a["w"]), a["n"], a["k"], a["ldw"], P(a["packed"]),
+                                       P(a["scales"]), P(a["ts"]), P(a["ts_in"]), a["flags"],
+                                       P(a["ws"]), a["ws_bytes"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(packed=None), 1), (dict(scales=None), 1), (dict(ts=None), 1),
+    (dict(n=0), 2), (dict(k=24, ldw=24), 2), (dict(k=0, ldw=0), 2), (dict(ldw=16), 2),
+    (dict(w=FAKE + 2), 3), (dict(packed=FAKE + 8), 3), (dict(ldw=36), 3),
+    (dict(flags=2), 4), (dict(ws=None), 5), (dict(ws_bytes=16), 5), (dict(ws=FAKE + 4), 3),
+])
+def test_quantize_argument_errors(kw, status):
+    assert _quant(**kw) == status
+    assert q.lib().qerl_last_error()
+
+
+def _gemm(**kw):
+    a = dict(x=FAKE, m=2, k=64, ldx=64, packed=FAKE, scales=FAKE, ts=FAKE, n=32, A=FAKE, B=FAKE,
+             r=4, lam=2.0, y=FAKE, ldy=32, ws=FAKE, ws_bytes=1 << 16, stream=None)
+    a.update(kw)
+    return q.lib().qerl_w4a16_lora_gemm(P(a["x"]), a["m"], a["k"], a["ldx"], P(a["packed"]),
+                                        P(a["scales"]), P(a["ts"]), a["n"], P(a["A"]), P(a["B"]),
+                                        a["r"], a["lam"], P(a["y"]), a["ldy"], P(a["ws"]),
+                                        a["ws_bytes"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(y=None), 1), (dict(ts=None), 1), (dict(A=None), 1),
+    (dict(r=-1), 4), (dict(r=129), 4), (dict(lam=float("nan")), 4), (dict(lam=float("inf")), 4),
+    (dict(m=0), 2), (dict(n=0), 2), (dict(k=40, ldx=40), 2), (dict(ldx=48), 2), (dict(ldy=16), 2),
+    (dict(x=FAKE + 2), 3), (dict(y=FAKE + 1), 3), (dict(A=FAKE + 8), 3), (dict(ldx=68), 3),
+    (dict(ts=FAKE + 2), 3), (dict(ws=None), 5), (dict(ws_bytes=8), 5),
+])
+def test_gemm_argument_errors(kw, status):
+    assert _gemm(**kw) == status
+
+
+def test_gemm_without_lora_needs_no_lora_pointers_or_workspace_check():
+    # r == 0: A/B may be NULL; still rejected here on a bad shape, before any launch
+    assert _gemm(r=0, A=None, B=None, ws=None, ws_bytes=0, m=0) == 2
+
+
+def _aqn(**kw):
+    a = dict(x=FAKE, m=2, h=64, ldx=64, w=FAKE, eps=1e-6, sigma=1e-2, seed=1, step=0, layer=0,
+             yf=FAKE, yb=None, ldy=64, wn=None, stream=None)
+    a.update(kw)
+    return q.lib().qerl_aqn_rmsnorm(P(a["x"]), a["m"], a["h"], a["ldx"], P(a["w"]), a["eps"],
+                                    a["sigma"], a["seed"], a["step"], a["layer"], P(a["yf"]),
+                                    P(a["yb"]), a["ldy"], P(a["wn"]), P(a["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(yf=None, yb=None), 1),
+    (dict(m=0), 2), (dict(h=0), 2), (dict(h=16385, ldx=16392, ldy=16392), 2), (dict(ldx=32), 2),
+    (dict(x=FAKE + 1), 3), (dict(w=FAKE + 2), 3), (dict(wn=FAKE + 2), 3), (dict(yf=FAKE + 1), 3),
+    (dict(eps=0.0), 4), (dict(eps=-1.0), 4), (dict(eps=float("inf")), 4),
+    (dict(sigma=-1e-3), 4), (dict(sigma=float("nan")), 4),
+])
+def test_aqn_argument_errors(kw, status):
+    assert _aqn(**kw) == status
+
+
+def test_workspace_queries():
+    assert q.nvfp4_quantize_workspace_size(27648, 5120) >= 4096
+    assert q.w4a16_lora_gemm_workspace_size(64, 3584, 3584, 32) >= 64 * 32 * 4
+    assert q.w4a16_lora_gemm_workspace_size(64, 3584, 3584, 0) == 0

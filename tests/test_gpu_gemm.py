@@ -1,0 +1,163 @@
+"""GPU W4A16 + LoRA layer (qerl_w4a16_lora_gemm) against the fp64 oracle.
+
+The NVFP4 weights fed to the GPU are the oracle's own quantization, so this
+file tests the GEMM independently of the GPU quantizer.  Tolerances: relative
+L2 <= 5e-3 and max |y - y_ref| <= 1e-2 max |y_ref| (BF16 output rounding alone
+gives ~1e-3 and ~4e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import nvfp4_weight_only_quantize_amd as q
+from nvfp4_weight_only_quantize_amd import synth
+from parity import assert_gemm_close, bf16_to_f64, bits_to_gpu, dev
+
+pytestmark = pytest.mark.gpu
+
+
+class Layer:
+    """One projection: oracle-quantized NVFP4 weight + LoRA, host and GPU copies."""
+
+    def __init__(self, n, k, r, seed, row_sigma=0.5, lora_scale=2.0):
+        w = synth.weight_bf16(n, k, seed=seed, row_lognormal_sigma=row_sigma)
+        self.packed, self.scales, self.s_t = oracle.nvfp4_quantize(synth.bf16_bits(w), threads=16)
+        self.n, self.k, self.r, self.lam = n, k, r, lora_scale
+        self.wq = q.NVFP4Weight(torch.from_numpy(self.packed).to(dev()),
+                                torch.from_numpy(self.scales).to(dev()),
+                                torch.tensor([self.s_t], dtype=torch.float32, device=dev()))
+        if r:
+            a, b = synth.lora_bf16(n, k, r, seed=seed + 7)
+            self.a_bits, self.b_bits = synth.bf16_bits(a), synth.bf16_bits(b)
+            self.a, self.b = a.to(dev()), b.to(dev())
+        else:
+            self.a_bits = self.b_bits = self.a = self.b = None
+
+    def gpu(self, x_gpu):
+        y = q.w4a16_lora_gemm(x_gpu, self.wq, self.a, self.b, self.lam)
+        torch.cuda.synchronize()
+        return y
+
+    def ref(self, x_bits, rows=None):
+        return oracle.w4a16_lora_gemm(x_bits, self.packed, self.scales, self.s_t, self.a_bits,
+                                      self.b_bits, self.lam, rows=rows, threads=16)
+
+
+def _x(m, k, seed, outliers=0.005):
+    return synth.bf16_bits(synth.activation_bf16(m, k, seed=seed, outlier_col_frac=outliers))
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16, 33, 64, 100, 256])
+@pytest.mark.parametrize("nkr", [(96, 256, 16), (77, 512, 32), (130, 1024, 8), (64, 48, 4),
+                                 (33, 80, 0), (200, 2048, 64)])
+def test_small_shapes(m, nkr):
+    n, k, r = nkr
+    L = Layer(n, k, r, seed=100 + n + k + r)
+    x = _x(m, k, seed=m * 7 + k)
+    y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+    assert_gemm_close(y, L.ref(x), f"m={m} n={n} k={k} r={r}")
+
+
+@pytest.mark.parametrize("m", [1, 4, 64])
+def test_strided_activations_and_output(m):
+    n, k, r = 96, 512, 16
+    L = Layer(n, k, r, seed=300)
+    x = _x(m, k, seed=301)
+    xw = torch.zeros((m, k + 64), dtype=torch.bfloat16, device=dev())
+    xw[:, :k] = bits_to_gpu(x)
+    yw = torch.full((m, n + 32), 7.0, dtype=torch.bfloat16, device=dev())
+    q.w4a16_lora_gemm(xw[:, :k], L.wq, L.a, L.b, L.lam, out=yw[:, :n])
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_to_f64(yw[:, :n]), L.ref(x), "strided")
+    assert torch.all(yw[:, n:] == 7.0)
+
+
+@pytest.mark.parametrize("m", [1, 3, 16, 80])
+def test_zero_input_zero_lora(m):
+    n, k, r = 64, 256, 8
+    L = Layer(n, k, r, seed=400)
+    zero = torch.zeros((m, k), dtype=torch.bfloat16, device=dev())
+    assert torch.all(L.gpu(zero) == 0)
+    x = _x(m, k, seed=401)
+    base = q.w4a16_lora_gemm(bits_to_gpu(x), L.wq)
+    zb = torch.zeros_like(L.b)
+    with_zero_b = q.w4a16_lora_gemm(bits_to_gpu(x), L.wq, L.a, zb, 2.0)
+    torch.cuda.synchronize()
+    assert torch.equal(base, with_zero_b)
+    assert_gemm_close(bf16_to_f64(base), oracle.w4a16_lora_gemm(x, L.packed, L.scales, L.s_t), "r=0")
+
+
+def test_config1_single_layer():
+    L = Layer(2048, 2048, 16, seed=1001, row_sigma=0.0, lora_scale=32 / 16)
+    x = _x(1, 2048, seed=1002, outliers=0.0)
+    assert_gemm_close(bf16_to_f64(L.gpu(bits_to_gpu(x))), L.ref(x), "config1")
+
+
+@pytest.mark.parametrize("proj", synth.PROJ_ORDER)
+def test_config2_7b_layer(proj):
+    n, k = synth.QWEN25_7B[proj]
+    L = Layer(n, k, 32, seed=synth.seed_for(1002, proj))
+    for m in (1, 8, 64):
+        x = _x(m, k, seed=synth.seed_for(1002, proj, m))
+        y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+        rows = None if m <= 8 else [0, 1, 31, 62, 63]
+        ref = L.ref(x, rows=rows)
+        assert_gemm_close(y if rows is None else y[rows], ref, f"{proj} m={m}")
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_config3_32b_batched_decode(proj):
+    n, k = synth.QWEN25_32B[proj]
+    L = Layer(n, k, 32, seed=synth.seed_for(1003, proj))
+    for m in (16, 64, 128, 256):
+        x = _x(m, k, seed=synth.seed_for(1003, proj, m))
+        y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+        rows = [0, 5, m // 2, m - 1]
+        assert_gemm_close(y[rows], L.ref(x, rows=rows), f"{proj} m={m}")
+
+
+@pytest.mark.parametrize("m", [2048, 8192])
+def test_config4_prefill_fused_gate_up_and_down(m):
+    n, k = synth.QWEN25_32B["gate"]
+    r = 32
+    # fused gate/up: one NVFP4 tensor [2N, K], A = [A_g; A_u], B block-diagonal
+    w = synth.weight_bf16(2 * n, k, seed=synth.seed_for(1004, "gate_up"), row_lognormal_sigma=0.5)
+    packed, scales, s_t = oracle.nvfp4_quantize(synth.bf16_bits(w), threads=16)
+    del w
+    ag, bg = synth.lora_bf16(n, k, r, seed=synth.seed_for(1004, "gate_lora"))
+    au, bu = synth.lora_bf16(n, k, r, seed=synth.seed_for(1004, "up_lora"))
+    a = torch.cat([ag, au], 0)
+    b = torch.zeros((2 * n, 2 * r), dtype=torch.bfloat16)
+    b[:n, :r] = bg
+    b[n:, r:] = bu
+    wq = q.NVFP4Weight(torch.from_numpy(packed).to(dev()), torch.from_numpy(scales).to(dev()),
+                       torch.tensor([s_t], dtype=torch.float32, device=dev()))
+    x = _x(m, k, seed=synth.seed_for(1004, "x", m))
+    y = q.w4a16_lora_gemm(bits_to_gpu(x), wq, a.to(dev()), b.to(dev()), 2.0)
+    torch.cuda.synchronize()
+    rows = [0, 1, m // 3, m - 1]
+    yr = bf16_to_f64(y[rows])
+    del y
+    ref = oracle.w4a16_lora_gemm(x, packed, scales, s_t, synth.bf16_bits(a), synth.bf16_bits(b), 2.0,
+                                 rows=rows, threads=16)
+    assert_gemm_close(yr, ref, f"gate_up m={m}")
+    # down projection [5120, 27648]
+    n2, k2 = synth.QWEN25_32B["down"]
+    L = Layer(n2, k2, r, seed=synth.seed_for(1004, "down"))
+    x2 = _x(m, k2, seed=synth.seed_for(1004, "x2", m))
+    y2 = bf16_to_f64(L.gpu(bits_to_gpu(x2))[rows])
+    assert_gemm_close(y2, L.ref(x2, rows=rows), f"down m={m}")
+
+
+def test_gpu_quantizer_feeds_gemm():
+    # end to end on the GPU: quantize with the HIP quantizer, multiply, compare
+    n, k, r, m = 512, 3584, 32, 8
+    w = synth.weight_bf16(n, k, seed=77, row_lognormal_sigma=0.5)
+    wq = q.nvfp4_quantize(w.to(dev()))
+    a, b = synth.lora_bf16(n, k, r, seed=78)
+    x = _x(m, k, seed=79)
+    y = q.w4a16_lora_gemm(bits_to_gpu(x), wq, a.to(dev()), b.to(dev()), 2.0)
+    torch.cuda.synchronize()
+    packed, scales, s_t = oracle.nvfp4_quantize(synth.bf16_bits(w))
+    ref = oracle.w4a16_lora_gemm(x, packed, scales, s_t, synth.bf16_bits(a), synth.bf16_bits(b), 2.0)
+    assert_gemm_close(bf16_to_f64(y), ref, "quantize->gemm")
