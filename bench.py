@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Benchmark of the QeRL rollout-phase linear layer on one MI355X.
+
+One *step* is the decode pass of a Qwen2.5-7B-shaped decoder layer through
+every operation of the hot path, at each decode batch M in {1, 8, 64}:
+
+    AQN RMSNorm (attention)  -> q, k, v   (NVFP4 W4A16 + LoRA r=32, alpha=64)
+    o                        (synthetic attention output as input)
+    AQN RMSNorm (MLP)        -> gate, up
+    down                     (synthetic activation as input)
+
+The sigma of the AQN noise follows the exponential schedule 1e-2 -> 5e-4 over
+10 stages (stage = step mod 10).  Weights are cold: 8 copies of the layer's
+NVFP4 weights and LoRA (~1.1 GB, far above the 256 MB Infinity Cache) rotate
+so that no weight is re-read from cache.  The steps run as one captured HIP
+graph (the decode loop is launch-bound otherwise).
+
+``value`` = algorithmic bytes of a step / wall time of a step (GB/s), inputs
+resident in HBM.  Algorithmic bytes per projection call:
+    N*K/2 + N*K/16 + 4 (NVFP4 weight) + 2*r*(K + N) (LoRA) + 2*M*(K + N) (x, y)
+and per norm call: 2*M*H (x) + 4*H (weight) + 2*M*H (BF16 out).
+
+Extra legs in the same JSON line: ``prefill`` (32B-shaped layer, M in {2048,
+8192}, TFLOP/s vs the BF16 MFMA peak), ``quantizer`` (BF16 -> NVFP4 of a
+32B-shaped layer, GB/s at 4.5625 B/element), ``roofline`` (the W4A16 decode
+GEMM calls: bytes / measured duration) and ``cpu_baseline`` (the CPU oracle on
+a bounded sample of the same decode workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import nvfp4_weight_only_quantize_amd as q  # noqa: E402
+from nvfp4_weight_only_quantize_amd import synth  # noqa: E402
+
+METRIC = "W4A16-NVFP4+LoRA GEMM: decode HBM GB/s (%peak), prefill TFLOPS (%MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+DECODE_MS = (1, 8, 64)
+PREFILL_MS = (2048, 8192)
+RANK, ALPHA = 32, 64
+SIGMA0, SIGMA1, STAGES, EPS = 1e-2, 5e-4, 10, 1e-6
+SEED = 1002
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_bytes(m, n, k, r):
+    return n * k // 2 + n * k // 16 + 4 + 2 * r * (k + n) + 2 * m * (k + n)
+
+
+def gemm_flops(m, n, k, r):
+    return 2 * m * n * k + 2 * m * r * (k + n)
+
+
+def norm_bytes(m, h):
+    return 2 * m * h + 4 * h + 2 * m * h
+
+
+class Proj:
+    """One NVFP4 projection with its LoRA (GPU)."""
+
+    def __init__(self, wq, a, b):
+        self.wq, self.a, self.b = wq, a, b
+
+    def clone(self):
+        return Proj(q.NVFP4Weight(self.wq.packed.clone(), self.wq.scales.clone(),
+                                  self.wq.tensor_scale.clone()), self.a.clone(), self.b.clone())
+
+
+def make_layer(shapes, seed, dev, r=RANK, row_sigma=0.5, outlier_rows=0.0):
+    """Quantize a synthetic BF16 layer on the GPU; returns {name: Proj}."""
+    layer = {}
+    for name in synth.PROJ_ORDER:
+        n, k = shapes[name]
+        w = synth.weight_bf16(n, k, seed=synth.seed_for(seed, name), row_lognormal_sigma=row_sigma,
+                              outlier_row_frac=outlier_rows, device=dev)
+        wq = q.nvfp4_quantize(w)
+        del w
+        a, b = synth.lora_bf16(n, k, r, seed=synth.seed_for(seed, name, "lora"), device=dev)
+        layer[name] = Proj(wq, a, b)
+    return layer
+
+
+class DecodeLayer:
+    """Buffers and the launch sequence of one decode step (7B shapes)."""
+
+    def __init__(self, dev, copies):
+        self.dev = dev
+        self.shapes = synth.QWEN25_7B
+        h, inter = 3584, 18944
+        self.h = h
+        base = make_layer(self.shapes, SEED, dev)
+        self.copies = [base] + [{k: p.clone() for k, p in base.items()} for _ in range(copies - 1)]
+        mmax = max(DECODE_MS)
+        self.h_attn = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "h_attn"), 0.005, device=dev)
+        self.h_mlp = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "h_mlp"), 0.005, device=dev)
+        self.x_o = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "x_o"), 0.005, device=dev)
+        self.x_down = synth.activation_bf16(mmax, inter, synth.seed_for(SEED, "x_down"), 0.005, device=dev)
+        self.w_attn = synth.norm_weight_f32(h, synth.seed_for(SEED, "w_attn"), device=dev)
+        self.w_mlp = synth.norm_weight_f32(h, synth.seed_for(SEED, "w_mlp"), device=dev)
+        self.x_attn = torch.empty((mmax, h), dtype=torch.bfloat16, device=dev)
+        self.x_mlp = torch.empty((mmax, h), dtype=torch.bfloat16, device=dev)
+        self.y = {name: torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+                  for name, (n, _k) in self.shapes.items()}
+        ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.sigmas = [q.aqn_sigma(s, STAGES, SIGMA0, SIGMA1) for s in range(STAGES)]
+
+    def inputs_of(self, name):
+        return {"q": self.x_attn, "k": self.x_attn, "v": self.x_attn, "o": self.x_o,
+                "gate": self.x_mlp, "up": self.x_mlp, "down": self.x_down}[name]
+
+    def gemm(self, name, m, c):
+        p = self.copies[c][name]
+        q.w4a16_lora_gemm(self.inputs_of(name)[:m], p.wq, p.a, p.b, ALPHA / RANK,
+                          out=self.y[name][:m], workspace=self.ws)
+
+    def norm(self, which, m, step):
+        src, w, dst, layer = ((self.h_attn, self.w_attn, self.x_attn, 0) if which == "attn"
+                              else (self.h_mlp, self.w_mlp, self.x_mlp, 1))
+        q.aqn_rmsnorm(src[:m], w, EPS, self.sigmas[step % STAGES], SEED, step, layer,
+                      want_f32=False, y_bf16=dst[:m])
+
+    def step(self, s, on_gemm=None):
+        for mi, m in enumerate(DECODE_MS):
+            c = (len(DECODE_MS) * s + mi) % len(self.copies)
+            self.norm("attn", m, s)
+            for name in ("q", "k", "v", "o"):
+                self._g(name, m, c, on_gemm)
+            self.norm("mlp", m, s)
+            for name in ("gate", "up", "down"):
+                self._g(name, m, c, on_gemm)
+
+    def _g(self, name, m, c, on_gemm):
+        if on_gemm is None:
+            self.gemm(name, m, c)
+        else:
+            on_gemm(name, m, lambda: self.gemm(name, m, c))
+
+    def step_bytes(self):
+        tot = 0
+        for m in DECODE_MS:
+            tot += 2 * norm_bytes(m, self.h)
+            tot += sum(gemm_bytes(m, n, k, RANK) for n, k in self.shapes.values())
+        return tot
+
+
+def time_graph(fn_steps, steps, warmup):
+    """Capture `steps` calls of fn (and `warmup` separately) as HIP graphs;
+    returns ms per step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn_steps(0, 1)  # eager pass: one-time setup (function attributes) before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_warm, g_main = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_warm):
+        fn_steps(0, max(warmup, 1))
+    with torch.cuda.graph(g_main):
+        fn_steps(warmup, steps)
+    g_warm.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    g_main.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, (g_warm, g_main)
+
+
+def per_call_durations(layer: DecodeLayer, reps: int):
+    """Event-timed duration of every W4A16 GEMM call of `reps` steps, enqueued
+    behind a GPU sleep so that host enqueue time does not leak into them."""
+    recs = []
+
+    def on_gemm(name, m, run):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        n, k = layer.shapes[name]
+        recs.append((name, m, gemm_bytes(m, n, k, RANK), e0, e1))
+
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e8))  # keep the GPU busy while the host enqueues
+    for s in range(reps):
+        layer.step(1000 + s, on_gemm)
+    torch.cuda.synchronize()
+    return [(name, m, b, e0.elapsed_time(e1) * 1e-3) for name, m, b, e0, e1 in recs]
+
+
+def check_decode_parity(layer: DecodeLayer):
+    """GPU outputs of the last step vs the CPU oracle at M = 1 (all 7 projections)."""
+    import oracle
+    worst = 0.0
+    for name in synth.PROJ_ORDER:
+        p = layer.copies[0][name]
+        x = synth.bf16_bits(layer.inputs_of(name)[:1])
+        layer.gemm(name, 1, 0)
+        torch.cuda.synchronize()
+        y = layer.y[name][:1].float().cpu().numpy().astype(np.float64)
+        ref = oracle.w4a16_lora_gemm(x, p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
+                                     np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a),
+                                     synth.bf16_bits(p.b), ALPHA / RANK, threads=16)
+        rel = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
+        worst = max(worst, rel)
+    return worst
+
+
+def cpu_baseline(layer: DecodeLayer, budget_s: float):
+    """The CPU oracle on a bounded sample of the decode workload: the seven
+    projections at M = 1 (the whole 7B layer's weights), then M = 8 and 64,
+    while the time budget lasts.  Same algorithmic-bytes accounting as the GPU."""
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    host = {}
+    for name in synth.PROJ_ORDER:
+        p = layer.copies[0][name]
+        host[name] = (p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
+                      np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a), synth.bf16_bits(p.b))
+    xs = {name: synth.bf16_bits(layer.inputs_of(name)[:max(DECODE_MS)]) for name in synth.PROJ_ORDER}
+    done_bytes, t_used, sample = 0, 0.0, []
+    for m in DECODE_MS:
+        for name in synth.PROJ_ORDER:
+            if t_used > budget_s:
+                break
+            n, k = layer.shapes[name]
+            packed, scales, st, a, b = host[name]
+            t0 = time.perf_counter()
+            oracle.w4a16_lora_gemm(xs[name][:m], packed, scales, st, a, b, ALPHA / RANK, threads=threads)
+            t_used += time.perf_counter() - t0
+            done_bytes += gemm_bytes(m, n, k, RANK)
+            sample.append(f"{name}@M={m}")
+    return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle W4A16+LoRA on the 7B layer: {', '.join(sample)} "
+                      f"({done_bytes / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
+
+
+def prefill_leg(dev, reps):
+    shapes = dict(synth.QWEN25_32B)
+    layer = make_layer(shapes, 1004, dev)
+    # fused gate/up: one NVFP4 tensor [2N, K] (its own tensor scale) with a
+    # block-diagonal rank-64 LoRA
+    n, k = shapes["gate"]
+    w = synth.weight_bf16(2 * n, k, seed=synth.seed_for(1004, "gate_up"), row_lognormal_sigma=0.5, device=dev)
+    gu = q.nvfp4_quantize(w)
+    del w
+    a = torch.cat([layer["gate"].a, layer["up"].a], 0)
+    b = torch.zeros((2 * n, 2 * RANK), dtype=torch.bfloat16, device=dev)
+    b[:n, :RANK] = layer["gate"].b
+    b[n:, RANK:] = layer["up"].b
+    projs = {"q": (layer["q"], RANK), "k": (layer["k"], RANK), "v": (layer["v"], RANK),
+             "o": (layer["o"], RANK), "gate_up": (Proj(gu, a, b), 2 * RANK), "down": (layer["down"], RANK)}
+    out = {}
+    for m in PREFILL_MS:
+        xk = {kk: synth.activation_bf16(m, kk, synth.seed_for(1004, "x", m, kk), 0.005, device=dev)
+              for kk in {5120, 27648}}
+        ys = {nm: torch.empty((m, p.wq.shape[0]), dtype=torch.bfloat16, device=dev) for nm, (p, _r) in projs.items()}
+        ws = torch.empty(max(q.w4a16_lora_gemm_workspace_size(m, p.wq.shape[0], p.wq.shape[1], r)
+                             for p, r in projs.values()), dtype=torch.uint8, device=dev)
+
+        def run():
+            for nm, (p, r) in projs.items():
+                q.w4a16_lora_gemm(xk[p.wq.shape[1]], p.wq, p.a, p.b, ALPHA / RANK, out=ys[nm], workspace=ws)
+
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        flops = sum(gemm_flops(m, p.wq.shape[0], p.wq.shape[1], r) for p, r in projs.values())
+        out[f"M={m}"] = {"ms": t * 1e3, "tflops": flops / t / 1e12,
+                         "frac": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        del xk, ys, ws
+    return out
+
+
+def quantizer_leg(dev, reps):
+    shapes = synth.QWEN25_32B
+    ws = torch.empty(q.nvfp4_quantize_workspace_size(1, 16), dtype=torch.uint8, device=dev)
+    ws_in, outs, elems = {}, {}, 0
+    for name in synth.PROJ_ORDER:
+        n, k = shapes[name]
+        ws_in[name] = synth.weight_bf16(n, k, seed=synth.seed_for(1005, name), outlier_row_frac=0.001, device=dev)
+        outs[name] = q.NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                                   torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                                   torch.empty(1, dtype=torch.float32, device=dev))
+        elems += n * k
+
+    def run():
+        for name in synth.PROJ_ORDER:
+            q.nvfp4_quantize(ws_in[name], out=outs[name], workspace=ws, check_finite=False)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    gbs = elems * 4.5625 / t / 1e9
+    return {"workload": "BF16->NVFP4 of one Qwen2.5-32B-shaped layer (7 tensors, 1.09 G elements)",
+            "ms": t * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "whole_model_ms_est": t * 1e3 * 64}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=8, help="cold-weight copies of the layer")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    q.lib()
+
+    log("setting up decode layer ...")
+    layer = DecodeLayer(dev, args.copies)
+    torch.cuda.synchronize()
+
+    def steps_fn(first, count):
+        for s in range(first, first + count):
+            layer.step(s)
+
+    ms_per_step, _graphs = time_graph(steps_fn, args.steps, args.warmup)
+    step_bytes = layer.step_bytes()
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
+
+    calls = per_call_durations(layer, reps=5)
+    tot_b = sum(c[2] for c in calls)
+    tot_t = sum(c[3] for c in calls)
+    per_m = {}
+    for m in DECODE_MS:
+        b = sum(c[2] for c in calls if c[1] == m)
+        t = sum(c[3] for c in calls if c[1] == m)
+        per_m[f"M={m}"] = {"gemm_us": t / 5 * 1e6, "GB/s": b / t / 1e9}
+    per_proj = {}
+    for name in synth.PROJ_ORDER:
+        for m in DECODE_MS:
+            sel = [c for c in calls if c[0] == name and c[1] == m]
+            per_proj[f"{name}@{m}"] = round(sum(c[3] for c in sel) / len(sel) * 1e6, 2)
+    achieved = tot_b / tot_t / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "qerl_w4a16_lora_gemm decode calls (LoRA down-projection + W4A16 kernel)",
+                "avg_call_us": tot_t / len(calls) * 1e6, "avg_call_bytes": tot_b / len(calls)}
+
+    parity = check_decode_parity(layer)
+    result = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen2.5-7B-shaped decoder layer, decode: AQN RMSNorm x2 + "
+                               "q/k/v/o/gate/up/down NVFP4 W4A16 + LoRA r32 (alpha 64), M in {1,8,64}",
+                   "hidden": 3584, "intermediate": 18944, "decode_m": list(DECODE_MS),
+                   "lora_rank": RANK, "cold_weight_copies": args.copies, "hip_graph": True,
+                   "step_bytes": step_bytes},
+        "frac_of_hbm_peak": value / HBM_PEAK_GBS,
+        "roofline": roofline,
+        "decode_per_m": per_m,
+        "decode_call_us": per_proj,
+        "parity_rel_l2_m1": parity,
+    }
+    del _graphs
+    if not args.no_prefill:
+        log("prefill leg ...")
+        result["prefill"] = prefill_leg(dev, reps=3)
+    if not args.no_quantizer:
+        log("quantizer leg ...")
+        result["quantizer"] = quantizer_leg(dev, reps=3)
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        result["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
