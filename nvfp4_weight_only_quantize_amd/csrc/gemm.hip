@@ -612,10 +612,12 @@ hipError_t launch_gemv(const Gemm &g, hipStream_t stream) {
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+    if (m <= kDecodeMaxM) return decode_workspace_bytes(m, n, k, r);
     return (size_t)make_plan(m, n, k, r).bytes;
 }
 
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
+    if (a.m <= kDecodeMaxM) return launch_decode(a, stream);
     const Gemm g{a, make_plan(a.m, a.n, a.k, a.r)};
     if (a.r > 0) {
         const int64_t grid = a.m * a.r;

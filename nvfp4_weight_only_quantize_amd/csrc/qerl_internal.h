@@ -35,6 +35,10 @@ struct GemmArgs {
 };
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
+// decode batches (m <= kDecodeMaxM): HBM-streaming split-K path in decode.hip
+constexpr int64_t kDecodeMaxM = 64;
+size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+hipError_t launch_decode(const GemmArgs &a, hipStream_t stream);
 
 // ---- AQN RMSNorm ----
 struct AqnArgs {

@@ -120,4 +120,5 @@ def test_aqn_argument_errors(kw, status):
 def test_workspace_queries():
     assert q.nvfp4_quantize_workspace_size(27648, 5120) >= 4096
     assert q.w4a16_lora_gemm_workspace_size(64, 3584, 3584, 32) >= 64 * 32 * 4
-    assert q.w4a16_lora_gemm_workspace_size(1, 3584, 3584, 0) == 0  # GEMV path, no LoRA
+    # decode sizes keep FP32 split-K partials: at least one m x n slice
+    assert q.w4a16_lora_gemm_workspace_size(1, 3584, 3584, 0) >= 3584 * 4
