@@ -117,7 +117,7 @@ class DecodeLayer:
         self.y = {name: torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
                   for name, (n, _k) in self.shapes.items()}
         ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.sigmas = [q.aqn_sigma(s, STAGES, SIGMA0, SIGMA1) for s in range(STAGES)]
 
     def inputs_of(self, name):
@@ -274,7 +274,7 @@ def prefill_leg(dev, reps):
         xk = {kk: synth.activation_bf16(m, kk, synth.seed_for(1004, "x", m, kk), 0.005, device=dev)
               for kk in {5120, 27648}}
         ys = {nm: torch.empty((m, p.wq.shape[0]), dtype=torch.bfloat16, device=dev) for nm, (p, _r) in projs.items()}
-        ws = torch.empty(max(q.w4a16_lora_gemm_workspace_size(m, p.wq.shape[0], p.wq.shape[1], r)
+        ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(m, p.wq.shape[0], p.wq.shape[1], r)
                              for p, r in projs.values()), dtype=torch.uint8, device=dev)
 
         def run():

@@ -120,9 +120,17 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
  *   lora_a_bf16   [r, k] contiguous; lora_b_bf16 [n, r] contiguous; both may be
  *                 NULL only when r == 0 (no LoRA)
  *   y_bf16        [m, n], row stride ldy >= n; must not overlap any input
- * Small m takes an HBM-streaming GEMV path (E2M1 decode in registers, wave
- * reductions); larger m a BF16-MFMA path on dequantized tiles with the LoRA
- * product folded into the same accumulation.
+ *   workspace     device memory of at least the size query; its first 64 KiB
+ *                 hold counters that must be zero before the first call that
+ *                 uses this workspace (e.g. allocate it zero-filled).  Every
+ *                 call leaves them zero, so one workspace serves any sequence
+ *                 of calls on one stream; calls that overlap in time must not
+ *                 share a workspace.
+ * m <= 64 takes the decode path: one launch that streams the packed weights
+ * once (E2M1/E4M3 decode in registers, BF16 MFMA), reduces split-K partials
+ * in the last workgroup of each row block and adds the LoRA term there; larger
+ * m takes a BF16-MFMA path on dequantized tiles with the LoRA product folded
+ * into the same accumulation.
  * Requires m, n >= 1, k >= 16, k % 16 == 0, 0 <= r <= QERL_MAX_LORA_RANK,
  * finite lora_scale, workspace_bytes >= the size query.
  */

@@ -167,7 +167,11 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
                     lora_b: torch.Tensor | None = None, lora_scale: float = 0.0,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                     stream=None) -> torch.Tensor:
-    """y [M, N] (BF16) = x [M, K] deq(W)^T + lora_scale (x A^T) B^T."""
+    """y [M, N] (BF16) = x [M, K] deq(W)^T + lora_scale (x A^T) B^T.
+
+    A caller-provided ``workspace`` must be zero-filled before its first use
+    (e.g. ``torch.zeros``); every call leaves its counter region zero again, so
+    one workspace serves any sequence of calls on one stream."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     m, k = x.shape
@@ -190,7 +194,8 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
         raise ValueError("out must be [M, N]")
     need = w4a16_lora_gemm_workspace_size(m, n, k, r)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        # its head holds counters that must start at zero (each call leaves them zero)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qerl_w4a16_lora_gemm(
         _ptr(x), m, k, _rows(x, "x"), _ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n,

@@ -11,9 +11,11 @@
 // (Salmon, Moraes, Dror, Shaw, SC'11) with key (seed, layer) and counter
 // (c/4, step, 0, 0), then Box-Muller (1958) on word pairs (r0, r1), (r2, r3).
 //
-// Launch: a grid of up to 512 workgroups; each first builds the noisy weight
-// for all h channels in LDS (so the noise is computed once per workgroup, not
-// once per row), then normalizes rows m = blockIdx.x, + gridDim.x, ...
+// Launch: a 2-D grid.  blockIdx.x picks 1024 channels (4 per thread: one
+// Philox block), blockIdx.y a group of kRows rows.  Every workgroup reads the
+// whole of its rows for the sum of squares (L2-resident, a few KB per row),
+// so no workgroup waits for another and the noise of a channel is drawn by
+// kRows-row groups only.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -21,7 +23,9 @@ namespace qerl {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxGrid = 512;
+constexpr int kChanPerWg = 4 * kThreads;
+constexpr int kRows = 4;           // rows per workgroup
+constexpr int kMaxRowGroups = 8192;
 
 struct U64x4 { uint64_t v[4]; };
 
@@ -53,40 +57,87 @@ __device__ __forceinline__ void box_muller(uint64_t ra, uint64_t rb, float &z0, 
     z1 = rad * s;
 }
 
+// VEC: x rows 16-byte aligned (x % 16 == 0, ldx % 8 == 0, h % 8 == 0) and
+// outputs vector-aligned (y_f32 % 16, y_bf16 % 8, ldy % 4 == 0).
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
-    extern __shared__ float s_w[];  // [h] noisy weight
-    __shared__ float s_red[4];
-    const int tid = threadIdx.x;
-    for (int64_t g = tid; g * 4 < a.h; g += kThreads) {
+    __shared__ float s_red[kRows][4];
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + tid;  // Philox block: channels 4g .. 4g+3
+    const int64_t c0 = 4 * g;
+    float wn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c0 < a.h) {
         const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
         float z[4];
         box_muller(r.v[0], r.v[1], z[0], z[1]);
         box_muller(r.v[2], r.v[3], z[2], z[3]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t c = g * 4 + i;
-            if (c < a.h) {
-                const float wn = __builtin_fmaf(a.sigma, z[i], a.weight[c]);
-                s_w[c] = wn;
-                if (blockIdx.x == 0 && a.noisy_out) a.noisy_out[c] = wn;
+        for (int i = 0; i < 4; ++i)
+            if (c0 + i < a.h) {
+                wn[i] = __builtin_fmaf(a.sigma, z[i], a.weight[c0 + i]);
+                if (blockIdx.y == 0 && a.noisy_out) a.noisy_out[c0 + i] = wn[i];
+            }
+    }
+    const float inv_h = 1.0f / (float)a.h;
+    for (int64_t rg = blockIdx.y; rg * kRows < a.m; rg += gridDim.y) {
+        const int64_t row0 = rg * kRows;
+        float ss[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            ss[i] = 0.0f;
+            if (row0 + i >= a.m) continue;
+            const uint16_t *xr = a.x + (row0 + i) * a.ldx;
+            if (VEC) {
+                for (int64_t p = tid; p * 8 < a.h; p += kThreads) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(xr + p * 8);
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float lo = bf16lo_to_f32(w4[j]), hi = bf16hi_to_f32(w4[j]);
+                        ss[i] = __builtin_fmaf(lo, lo, ss[i]);
+                        ss[i] = __builtin_fmaf(hi, hi, ss[i]);
+                    }
+                }
+            } else {
+                for (int64_t c = tid; c < a.h; c += kThreads) {
+                    const float v = bf16lo_to_f32(xr[c]);
+                    ss[i] = __builtin_fmaf(v, v, ss[i]);
+                }
             }
         }
-    }
-    __syncthreads();
-    const float inv_h = 1.0f / (float)a.h;
-    for (int64_t row = blockIdx.x; row < a.m; row += gridDim.x) {
-        const uint16_t *xr = a.x + row * a.ldx;
-        float ss = 0.0f;
-        for (int64_t c = tid; c < a.h; c += kThreads) {
-            const float v = bf16lo_to_f32(xr[c]);
-            ss = __builtin_fmaf(v, v, ss);
-        }
-        ss = block_sum_256(ss, s_red);
-        const float inv = 1.0f / sqrtf(ss * inv_h + a.eps);
-        for (int64_t c = tid; c < a.h; c += kThreads) {
-            const float y = bf16lo_to_f32(xr[c]) * inv * s_w[c];
-            if (a.y_f32) a.y_f32[row * a.ldy + c] = y;
-            if (a.y_bf16) a.y_bf16[row * a.ldy + c] = f32_to_bf16_bits(y);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) ss[i] = wave_sum(ss[i]);
+        __syncthreads();  // s_red may still be read for the previous row group
+        if ((tid & 63) == 0)
+#pragma unroll
+            for (int i = 0; i < kRows; ++i) s_red[i][wave] = ss[i];
+        __syncthreads();
+        if (c0 >= a.h) continue;
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            const int64_t row = row0 + i;
+            if (row >= a.m) break;
+            const float tot = (s_red[i][0] + s_red[i][1]) + (s_red[i][2] + s_red[i][3]);
+            const float inv = 1.0f / sqrtf(tot * inv_h + a.eps);
+            const uint16_t *xr = a.x + row * a.ldx;
+            if (VEC) {
+                const uint2 xv = *reinterpret_cast<const uint2 *>(xr + c0);
+                const float y0 = bf16lo_to_f32(xv.x) * inv * wn[0], y1 = bf16hi_to_f32(xv.x) * inv * wn[1];
+                const float y2 = bf16lo_to_f32(xv.y) * inv * wn[2], y3 = bf16hi_to_f32(xv.y) * inv * wn[3];
+                if (a.y_f32) *reinterpret_cast<float4 *>(a.y_f32 + row * a.ldy + c0) = make_float4(y0, y1, y2, y3);
+                if (a.y_bf16)
+                    *reinterpret_cast<uint2 *>(a.y_bf16 + row * a.ldy + c0) =
+                        make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t c = c0 + j;
+                    if (c >= a.h) break;
+                    const float y = bf16lo_to_f32(xr[c]) * inv * wn[j];
+                    if (a.y_f32) a.y_f32[row * a.ldy + c] = y;
+                    if (a.y_bf16) a.y_bf16[row * a.ldy + c] = f32_to_bf16_bits(y);
+                }
+            }
         }
     }
 }
@@ -94,14 +145,15 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
 }  // namespace
 
 hipError_t launch_aqn_rmsnorm(const AqnArgs &a, hipStream_t stream) {
-    // widths up to 16384 channels keep the noisy weight in 64 KiB of LDS
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(aqn_rmsnorm_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-        16384 * (int)sizeof(float));
-    if (attr != hipSuccess) return attr;
-    const int grid = (int)(a.m < kMaxGrid ? a.m : kMaxGrid);
-    const size_t lds = (size_t)a.h * sizeof(float);
-    hipLaunchKernelGGL(aqn_rmsnorm_kernel, dim3(grid), dim3(kThreads), lds, stream, a);
+    const bool vec = ((uintptr_t)a.x & 15u) == 0 && a.ldx % 8 == 0 && a.h % 8 == 0 &&
+                     ((uintptr_t)a.y_f32 & 15u) == 0 && ((uintptr_t)a.y_bf16 & 7u) == 0 && a.ldy % 4 == 0;
+    const int64_t row_groups = (a.m + kRows - 1) / kRows;
+    const dim3 grid((unsigned)((a.h + kChanPerWg - 1) / kChanPerWg),
+                    (unsigned)(row_groups < kMaxRowGroups ? row_groups : kMaxRowGroups));
+    if (vec)
+        hipLaunchKernelGGL(aqn_rmsnorm_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(aqn_rmsnorm_kernel<false>, grid, dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
 // decode.hip -- W4A16 (NVFP4 weight x BF16 activation) + LoRA for decode
-// batches, 1 <= m <= 64, on gfx950.
+// batches, 1 <= m <= 64, on gfx950.  One launch per call.
 //
 //   y[m, n] = s_t * sum_k x[m,k] e2m1(q[n,k]) e4m3(sb[n,k/16])
 //           + lora_scale * sum_j t[m,j] B[n,j],        t = x A^T
@@ -9,22 +9,35 @@
 // (Low-Rank Adaptation)" and "Implementation and Practical Details").
 //
 // Decode is bound by the bytes of the packed weights (0.5625 B per weight),
-// which are read exactly once.  Two launches, no inter-workgroup waiting:
+// which are read exactly once.  Work units are (block of 64*NW weight rows) x
+// (slice of K); each of the 4 waves of a unit owns 16*NW rows.
 //
-//  stream_kernel  work units = (block of 64*NW weight rows) x (slice of K).
-//                 Each of the 4 waves owns 16*NW rows and streams them over
-//                 the slice in 128-element chunks (64 packed bytes + 8 scale
-//                 bytes per row), keeping kDepth chunks in flight in a
-//                 register ring.  The x columns of the slice pass through a
-//                 double-buffered LDS segment shared by the 4 waves; LDS reads
-//                 are counted separately from global loads, so waiting for x
-//                 never waits for the weight prefetch.  Weights are decoded to
-//                 exact BF16 (e2m1 * e4m3) and multiplied on the 16x16x32 BF16
-//                 MFMA; each unit writes FP32 partial sums of its slice.
-//                 Extra "producer" workgroups of the same launch compute the
-//                 LoRA down-projection t = x A^T in FP32.
-//  finish_kernel  y = bf16(s_t * sum over slices of the partials (in slice
-//                 order: deterministic) + lora_scale * t B^T).
+//  * Weights stream in 128-element chunks (per row 64 packed bytes) through a
+//    ring of D chunks per wave.  Every load of the steady state is
+//    unconditional, which keeps the compiler's in-order wait counts exact.
+//  * The E4M3 scales of the unit are staged into LDS once with wide loads
+//    (per-lane 2-byte global loads would double the memory instructions).
+//  * x passes through a double-buffered LDS window of W chunks, loaded one
+//    window ahead; LDS reads are counted apart from global loads.
+//  * Weights are decoded to exact BF16 (e2m1 * e4m3 has <= 6 significant
+//    bits) and multiplied on the 16x16x32 BF16 MFMA in FP32.
+//  * LoRA: "producer" workgroups at the head of the grid compute partial sums
+//    of t = x A^T over slices of K (MFMA) and publish them with device-coherent
+//    stores; the epilogue adds lora_scale * t B^T on the MFMA with t split
+//    into BF16 hi + lo halves (relative error ~2^-16).
+//  * m <= 16, one launch: every unit but the last of its row block stores its
+//    FP32 partial tile (coherent stores) and bumps a counter; the last to
+//    arrive sums all partials in slice order (deterministic), waits until the
+//    producers have all published (they are dispatched before every consumer,
+//    so the wait is short; it is bounded all the same), sums their t partials
+//    in producer order and writes the output.
+//  * 16 < m <= 64, two launches: partial tiles are larger, so every unit
+//    stores its tile and finish_kernel sums them (in slice order) in parallel
+//    over the outputs; the last producer sums t, which finish_kernel reads
+//    after the kernel boundary.
+//
+// Counters live in the first kGemmCtrBytes of the workspace: they must be zero
+// before the first call, and every call leaves them zero.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -33,59 +46,136 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreadsD = kWaves * 64;
-constexpr int64_t kChunkK = 128;   // K elements per chunk
-constexpr int kDepth = 4;          // chunks in flight per wave
-constexpr int kXPad = 8;           // LDS row padding of the staged x (BF16 elements)
-constexpr int64_t kLdsBudget = 64 * 1024 - 1024;  // dynamic LDS for x (static LDS stays below 1 KB)
-constexpr int64_t kTargetUnits = 640;
-constexpr int kProdMG = 2;         // activation rows per LoRA producer workgroup
-constexpr int kMaxRank = 128;      // LoRA rank limit of the C ABI
+constexpr int64_t kChunkK = 128;          // K elements per chunk
+constexpr int kXPad = 8;                  // BF16 padding per staged x row
+constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
+constexpr int64_t kXBudget = 36 * 1024;   // LDS for a unit's x slice (m <= 16)
+constexpr int64_t kLdsLimit = 63 * 1024;
+constexpr int64_t kProdChunks = 8;        // K chunks per LoRA producer
+constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
+constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
+constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr int64_t kTargetUnits = 256;
+
+// counter words at the head of the workspace
+constexpr int kCtrProd = 0, kCtrDone = 2, kCtrRow = 4;
+constexpr int64_t kMaxRowBlocks = kGemmCtrBytes / 4 - kCtrRow;
 
 struct DecodePlan {
-    int mt, nw;
-    int64_t rows_per_unit, row_blocks, slices, kslice;
-    int64_t units, producers;
-    int64_t part_off, t_off, bytes, lds_bytes;
+    int mt, nw, px;
+    int64_t rows_per_unit, row_blocks;
+    int64_t chunks, full_chunks;   // chunks of K (the last may be partial), full chunks
+    int64_t cps, slices, units;    // chunks per slice (a multiple of 4/nw)
+    int64_t producers, jt, rp;     // LoRA producers, 16-wide rank tiles, rank padded to 32
+    int64_t xpitch, sc_pitch;      // LDS pitches: BF16 elements per x row, bytes per scale row
+    int64_t sc_lds_off, lds_bytes;
+    int64_t part_off, tpart_off, t_off, bytes;
 };
 
-// The whole x slice of a unit is staged in LDS once, so its K extent is
-// bounded by the LDS budget: m * (kslice + pad) * 2 bytes <= kLdsBudget.
+__host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-    p.nw = p.mt;  // x fragments are reused over nw column groups
+    p.nw = p.mt;
+    const int64_t win = 4 / p.mt;  // chunks per x window (16 KB of LDS at m = 16 mt)
     p.rows_per_unit = 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
-    const int64_t chunks = (k + kChunkK - 1) / kChunkK;
-    int64_t max_chunks = (kLdsBudget / (2 * m) - kXPad) / kChunkK;  // LDS bound on the slice
-    if (max_chunks < 1) max_chunks = 1;
-    // split K so the grid covers the chip, keeping FP32 partials small next to
-    // the weights where the LDS bound allows it (S * m * n * 4 <= weight bytes / 4)
-    int64_t s = (kTargetUnits + p.row_blocks - 1) / p.row_blocks;
-    int64_t s_cap = (k * 9) / (256 * m);
+    if (p.row_blocks > kMaxRowBlocks) p.row_blocks = 0;  // one counter per row block: rejected at launch
+    p.chunks = (k + kChunkK - 1) / kChunkK;
+    p.full_chunks = k / kChunkK;
+    // x window (16 < m): 8-element pieces per thread
+    const int64_t px = (m * win * kChunkK / 8 + kThreadsD - 1) / kThreadsD;
+    p.px = px <= 1 ? 1 : (px <= 2 ? 2 : 4);
+    // slices: cover the chip, keep the FP32 partials below the weight bytes
+    // and the staged scales within their LDS budget
+    int64_t s = p.row_blocks > 0 ? (kTargetUnits + p.row_blocks - 1) / p.row_blocks : 1;
+    int64_t s_cap = (k * 9) / (64 * m);
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
-    const int64_t s_min = (chunks + max_chunks - 1) / max_chunks;
-    if (s < s_min) s = s_min;
-    if (s > chunks) s = chunks;
     if (s < 1) s = 1;
-    p.kslice = (chunks + s - 1) / s * kChunkK;
-    p.slices = (k + p.kslice - 1) / p.kslice;
+    int64_t cps = (p.chunks + s - 1) / s;
+    cps = (cps + win - 1) / win * win;
+    int64_t cps_max = kScBudget * 16 / (p.rows_per_unit * kChunkK) / win * win;
+    if (p.mt == 1) {  // the unit's whole x slice stays in LDS
+        const int64_t x_max = (kXBudget / (2 * m) - kXPad) / kChunkK / win * win;
+        if (cps_max > x_max) cps_max = x_max;
+    }
+    if (cps > cps_max) cps = cps_max;
+    if (cps < win) cps = win;
+    p.cps = cps;
+    p.slices = (p.chunks + cps - 1) / cps;
     p.units = p.row_blocks * p.slices;
-    p.producers = r > 0 ? (int64_t)r * ((m + kProdMG - 1) / kProdMG) : 0;
-    p.part_off = 0;
-    p.t_off = (p.slices * m * n * 4 + 255) & ~(int64_t)255;
-    p.bytes = p.t_off + ((m * (int64_t)r * 4 + 255) & ~(int64_t)255);
-    p.lds_bytes = m * (p.kslice + kXPad) * 2;
+    p.jt = (r + 15) / 16;
+    p.rp = (r + 31) / 32 * 32;
+    p.producers = r > 0 ? (p.chunks + kProdChunks - 1) / kProdChunks : 0;
+    // LDS: x double buffer, then the scales (rows an odd multiple of 16 bytes
+    // apart, so the 16 rows a wave reads fall in distinct banks)
+    p.xpitch = (p.mt == 1 ? cps : win) * kChunkK + kXPad;
+    const int64_t x_bytes = (p.mt == 1 ? 1 : 2) * m * p.xpitch * 2;
+    int64_t scp = (cps * 8 + 15) / 16;
+    if (scp % 2 == 0) ++scp;
+    p.sc_pitch = scp * 16;
+    p.sc_lds_off = (x_bytes + 15) / 16 * 16;
+    int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
+    const int64_t epi = p.mt == 1 ? 16 * p.rp * 2 * 2 : 0;  // t hi/lo in the one-launch epilogue
+    const int64_t prod = (int64_t)p.mt * p.jt * 64 * 16;  // producer wave reduction
+    if (lds < epi) lds = epi;
+    if (lds < prod) lds = prod;
+    p.lds_bytes = lds;
+    // workspace after the counters: partial tiles, producer partials, t
+    const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
+    p.part_off = kGemmCtrBytes;
+    p.tpart_off = align256(p.part_off + (p.slices > 1 || p.mt > 1 ? p.units * tile : 0));
+    p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
+    p.bytes = align256(p.t_off + m * (int64_t)r * 4);
     return p;
 }
 
 struct Decode {
     GemmArgs a;
     DecodePlan p;
-    __device__ float *partials() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
+    __device__ uint32_t *ctr() const { return static_cast<uint32_t *>(a.workspace); }
+    __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
+    __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
     __device__ float *t32() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.t_off); }
 };
+
+// ---- device-coherent access: agent scope, no cache write-back or invalidate ----
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSc1 = 16;  // cache-policy bit: coherent at device scope
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void store_f4_coherent(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
+    i32x4_t b;
+    __builtin_memcpy(&b, &v, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, kSc1);
+}
+__device__ __forceinline__ f32x4_t load_f4_coherent(__amdgpu_buffer_rsrc_t r, int off) {
+    const i32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
+    f32x4_t v;
+    __builtin_memcpy(&v, &b, 16);
+    return v;
+}
+__device__ __forceinline__ void store_f32_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_f32_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_add(uint32_t *c, uint32_t v) {
+    return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_load(uint32_t *c) {
+    return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ctr_store(uint32_t *c, uint32_t v) {
+    __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// every global store and load this wave issued has completed
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8_d(const uint4 &u) {
     bf16x8_t v;
@@ -101,131 +191,273 @@ __device__ __forceinline__ bf16x8_t dequant8_d(uint32_t q, float s) {
                                   pack_bf16x2(f2.x * s, f2.y * s), pack_bf16x2(f3.x * s, f3.y * s)));
 }
 
-// One full chunk of the weights for lane (lr, lq) of column group g: row n,
-// elements 128c + 32lq .. +32 (16 packed bytes, 2 scale bytes).  Rows past n
-// are clamped (their outputs are discarded), so the loads carry no branch and
-// the compiler's in-order wait counting stays exact.  K32: k % 32 == 0, so
-// packed rows are 16-byte and scale rows 2-byte aligned.
+// ---------------------------------------------------------------------------
+// LoRA producers: t = x A^T
+// ---------------------------------------------------------------------------
+// Producer p covers chunks [8p, 8p + 8) of K for all rows and ranks; its 4
+// waves take interleaved 32-element steps.  A lane supplies x row
+// 16*mt + (lane % 16) and A row 16*jt + (lane % 16), 8 elements at
+// 8*(lane / 16) of the step, so MFMA tile (mt, jt) holds
+// t[16 mt + 4 (lane/16) + v][16 jt + lane % 16] in element v.
+template <int MT>
+__device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
+    const GemmArgs &a = d.a;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int JT = (int)d.p.jt;
+    const int64_t kb = p * kProdChunks * kChunkK;
+    const int64_t ke = kb + kProdChunks * kChunkK < a.k ? kb + kProdChunks * kChunkK : a.k;
+    const uint16_t *xrow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int64_t m = 16 * mt + lr < a.m ? 16 * mt + lr : a.m - 1;
+        xrow[mt] = a.x + m * a.ldx;
+    }
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
+    for (int jg = 0; jg < JT; jg += kProdTiles) {  // rank tiles jg, jg + 1
+        f32x4_t acc[MT][kProdTiles];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < kProdTiles; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        // a wave's steps (32 elements each, every 4th of the range) in groups
+        // of PS, all loads of a group issued before its products: the
+        // producers sit on the path to every epilogue, so they must not wait
+        // on memory once per step
+        constexpr int PS = MT == 1 ? 8 : 4;
+        for (int64_t k0 = kb + 32 * wave; k0 < ke; k0 += 4 * 32 * PS) {
+            uint4 xv[PS][MT], av[PS][kProdTiles];
+#pragma unroll
+            for (int u = 0; u < PS; ++u) {
+                const int64_t kk = k0 + 128 * u + 8 * lq;
+                const int64_t kc = kk < ke ? kk : ke - 8;  // k % 16 == 0: a piece never straddles the end
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4 *>(xrow[mt] + kc);
+#pragma unroll
+                for (int jj = 0; jj < kProdTiles; ++jj) {
+                    const int jr = 16 * (jg + jj) + lr;
+                    const int64_t j = jr < a.r ? jr : a.r - 1;
+                    av[u][jj] = *reinterpret_cast<const uint4 *>(a.lora_a + j * a.k + kc);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < PS; ++u) {
+                const bool kin = k0 + 128 * u + 8 * lq < ke;
+                bf16x8_t xa[MT];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) xa[mt] = as_bf16x8_d(kin ? xv[u][mt] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                for (int jj = 0; jj < kProdTiles; ++jj) {
+                    const bool jin = kin && 16 * (jg + jj) + lr < a.r;
+                    const bf16x8_t b = as_bf16x8_d(jin ? av[u][jj] : make_uint4(0, 0, 0, 0));
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt)
+                        acc[mt][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][jj], 0, 0, 0);
+                }
+            }
+        }
+        // the waves add their tiles in the order 0, 1, 2, 3 through LDS
+        for (int w = 0; w < kWaves; ++w) {
+            if (wave == w) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                    for (int jj = 0; jj < kProdTiles; ++jj)
+                        if (jg + jj < JT) {
+                            f32x4_t *slot = red + (mt * JT + jg + jj) * 64 + lane;
+                            if (w > 0) acc[mt][jj] = *slot + acc[mt][jj];
+                            *slot = acc[mt][jj];
+                        }
+            }
+            __syncthreads();
+        }
+    }
+    // wave 0 publishes the workgroup's sum
+    const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
+    if (wave == 0) {
+        const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + p * tile_floats);
+        for (int i = 0; i < MT * JT; ++i) store_f4_coherent(rs, (i * 64 + lane) * 16, red[i * 64 + lane]);
+        wait_vm();
+    }
+    __shared__ uint32_t s_last;
+    __syncthreads();
+    if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
+    __syncthreads();
+    if (MT == 1 || !s_last) return;  // m <= 16: the consumers sum the partials
+    // 16 < m: the last producer sums the partials in producer order into t [m, r]
+    if (wave == 0) {
+        for (int i = 0; i < MT * JT; ++i) {
+            f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t q = 0; q < d.p.producers; ++q) {
+                const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + q * tile_floats);
+                s = s + load_f4_coherent(rs, (i * 64 + lane) * 16);
+            }
+            const int mt = i / JT, jt = i - mt * JT;
+            const int64_t j = 16 * jt + lr;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t m = 16 * mt + 4 * lq + v;
+                if (m < a.m && j < a.r) d.t32()[m * a.r + j] = s[v];
+            }
+        }
+    }
+    if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// The streaming kernel
+// ---------------------------------------------------------------------------
+// One full chunk of the weights for lane (lr, lq) of row group g: row n,
+// elements 128c + 32lq .. +32 (16 packed bytes).  Rows past n are clamped
+// (their outputs are discarded).  K32: k % 32 == 0, packed rows 16-byte aligned.
 template <int NW, bool K32>
-__device__ __forceinline__ void load_chunk_full(const GemmArgs &a, int64_t n0, int64_t c, int lr, int lq,
-                                                uint4 (&w)[NW], uint32_t (&sc)[NW]) {
+__device__ __forceinline__ void load_chunk(const GemmArgs &a, int64_t n0, int64_t c, int lr, int lq, uint4 (&w)[NW]) {
     const int64_t e0 = c * kChunkK + 32 * lq;
 #pragma unroll
     for (int g = 0; g < NW; ++g) {
         int64_t n = n0 + 16 * g + lr;
         n = n < a.n ? n : a.n - 1;
         const uint8_t *prow = a.packed + n * (a.k >> 1) + (e0 >> 1);
-        const uint8_t *srow = a.scales + n * (a.k >> 4) + (e0 >> 4);
         if (K32) {
             w[g] = *reinterpret_cast<const uint4 *>(prow);
-            sc[g] = *reinterpret_cast<const uint16_t *>(srow);
         } else {
             const uint2 lo = reinterpret_cast<const uint2 *>(prow)[0];
             const uint2 hi = reinterpret_cast<const uint2 *>(prow)[1];
             w[g] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            sc[g] = (uint32_t)srow[0] | ((uint32_t)srow[1] << 8);
         }
     }
 }
 
-// The last chunk of a row when k % 128 != 0 (k % 16 == 0): elements past k
-// read as zero.
+// The partial last chunk (k % 128 != 0): elements past k read as zero.
 template <int NW>
 __device__ __forceinline__ void load_chunk_tail(const GemmArgs &a, int64_t n0, int64_t c, int lr, int lq,
-                                                uint4 (&w)[NW], uint32_t (&sc)[NW]) {
+                                                uint4 (&w)[NW]) {
     const int64_t e0 = c * kChunkK + 32 * lq;
 #pragma unroll
     for (int g = 0; g < NW; ++g) {
         int64_t n = n0 + 16 * g + lr;
         n = n < a.n ? n : a.n - 1;
         const uint8_t *prow = a.packed + n * (a.k >> 1) + (e0 >> 1);
-        const uint8_t *srow = a.scales + n * (a.k >> 4) + (e0 >> 4);
         w[g] = make_uint4(0, 0, 0, 0);
-        sc[g] = 0;
         if (e0 + 16 <= a.k) {
             const uint2 lo = *reinterpret_cast<const uint2 *>(prow);
             w[g].x = lo.x;
             w[g].y = lo.y;
-            sc[g] = srow[0];
             if (e0 + 32 <= a.k) {
                 const uint2 hi = reinterpret_cast<const uint2 *>(prow)[1];
                 w[g].z = hi.x;
                 w[g].w = hi.y;
-                sc[g] |= (uint32_t)srow[1] << 8;
             }
         }
     }
 }
 
-// LoRA down-projection for rows [m0, m0 + kProdMG) and rank j: the 256 lanes
-// split K, four 16-byte steps in flight per lane.
-__device__ void lora_producer(const Decode &d, int64_t job) {
-    const GemmArgs &a = d.a;
-    const int64_t j = job % a.r;
-    const int64_t m0 = (job / a.r) * kProdMG;
-    const uint16_t *ar = a.lora_a + j * a.k;
-    float acc[kProdMG];
-#pragma unroll
-    for (int i = 0; i < kProdMG; ++i) acc[i] = 0.0f;
-    const uint16_t *xr[kProdMG];
-#pragma unroll
-    for (int i = 0; i < kProdMG; ++i) {
-        const int64_t m = m0 + i < a.m ? m0 + i : a.m - 1;
-        xr[i] = a.x + m * a.ldx;
-    }
-    const int64_t step = (int64_t)kThreadsD * 8;
-    int64_t kk = (int64_t)threadIdx.x * 8;
-    for (; kk + 3 * step < a.k; kk += 4 * step) {
-        uint4 av[4], xv[4][kProdMG];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            av[u] = *reinterpret_cast<const uint4 *>(ar + kk + u * step);
-#pragma unroll
-            for (int i = 0; i < kProdMG; ++i) xv[u][i] = *reinterpret_cast<const uint4 *>(xr[i] + kk + u * step);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int i = 0; i < kProdMG; ++i) {
-                acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u][i].x), as_bf16x2(av[u].x), acc[i], false);
-                acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u][i].y), as_bf16x2(av[u].y), acc[i], false);
-                acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u][i].z), as_bf16x2(av[u].z), acc[i], false);
-                acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u][i].w), as_bf16x2(av[u].w), acc[i], false);
-            }
-    }
-    for (; kk < a.k; kk += step) {  // k % 16 == 0: a vector never straddles the end
-        const uint4 av = *reinterpret_cast<const uint4 *>(ar + kk);
-#pragma unroll
-        for (int i = 0; i < kProdMG; ++i) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(xr[i] + kk);
-            acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.x), as_bf16x2(av.x), acc[i], false);
-            acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.y), as_bf16x2(av.y), acc[i], false);
-            acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.z), as_bf16x2(av.z), acc[i], false);
-            acc[i] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.w), as_bf16x2(av.w), acc[i], false);
-        }
-    }
-    __shared__ float red[kProdMG][4];
-#pragma unroll
-    for (int i = 0; i < kProdMG; ++i) {
-        const float v = wave_sum(acc[i]);
-        if ((threadIdx.x & 63) == 0) red[i][threadIdx.x >> 6] = v;
-    }
-    __syncthreads();
-    if (threadIdx.x < kProdMG && m0 + threadIdx.x < a.m) {
-        const int i = threadIdx.x;
-        d.t32()[(m0 + i) * a.r + j] = (red[i][0] + red[i][1]) + (red[i][2] + red[i][3]);
+// x window: rows [0, m) x columns [k0, k0 + 128 W) as 8-element pieces;
+// thread t takes pieces t, t + 256, ...  Addresses are clamped into x, so every
+// load is unconditional; columns at or past k hold don't-care values, which
+// are only ever multiplied into chunks that are not computed.  Pieces past the
+// last row are loaded from the last row (same columns) and written there too:
+// the same bytes twice, and no branch for the compiler to sink the load into.
+// (Up to four pieces per thread, kept in named registers: an array here ends
+// up in scratch memory.)
+template <int W>
+__device__ __forceinline__ void x_piece(const GemmArgs &a, int i, int64_t &m, int64_t &col) {
+    constexpr int64_t per_row = W * kChunkK / 8;
+    const int64_t piece = threadIdx.x + (int64_t)i * kThreadsD;
+    m = piece / per_row;
+    col = (piece - m * per_row) * 8;
+    m = m < a.m ? m : a.m - 1;
+}
+template <int W>
+__device__ __forceinline__ uint4 load_x_piece(const GemmArgs &a, int64_t k0, int i) {
+    int64_t m, col;
+    x_piece<W>(a, i, m, col);
+    const int64_t kk = k0 + col < a.k ? k0 + col : a.k - 8;
+    return *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + kk);
+}
+template <int W>
+__device__ __forceinline__ void store_x_piece(const GemmArgs &a, uint16_t *buf, int64_t pitch, int i, const uint4 &v) {
+    int64_t m, col;
+    x_piece<W>(a, i, m, col);
+    *reinterpret_cast<uint4 *>(buf + m * pitch + col) = v;
+}
+struct XWin {
+    uint4 p0, p1, p2, p3;
+};
+template <int PX, int W>
+__device__ __forceinline__ void load_x_window(const GemmArgs &a, int64_t k0, XWin &v) {
+    v.p0 = load_x_piece<W>(a, k0, 0);
+    if (PX > 1) v.p1 = load_x_piece<W>(a, k0, 1);
+    if (PX > 2) v.p2 = load_x_piece<W>(a, k0, 2);
+    if (PX > 3) v.p3 = load_x_piece<W>(a, k0, 3);
+}
+template <int PX, int W>
+__device__ __forceinline__ void store_x_window(const GemmArgs &a, uint16_t *buf, int64_t pitch, const XWin &v) {
+    store_x_piece<W>(a, buf, pitch, 0, v.p0);
+    if (PX > 1) store_x_piece<W>(a, buf, pitch, 1, v.p1);
+    if (PX > 2) store_x_piece<W>(a, buf, pitch, 2, v.p2);
+    if (PX > 3) store_x_piece<W>(a, buf, pitch, 3, v.p3);
+}
+
+// m <= 16: the unit's x slice, rows [0, m) x columns [k0, k0 + width), into
+// LDS rows of `pitch` elements; columns at or past k are zero.
+__device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
+    const int64_t per_row = width / 8;
+    for (int64_t i = threadIdx.x; i < a.m * per_row; i += kThreadsD) {
+        const int64_t m = i / per_row, col = (i - m * per_row) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 + col < a.k) v = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
+        *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v;
     }
 }
 
+// Stage the unit's scale bytes: rows [n0, n0 + R) x bytes [b0, b0 + nb) of
+// the [n, k/16] scale matrix into LDS rows of `pitch` bytes.
+__device__ void stage_scales(const GemmArgs &a, uint8_t *sc, int64_t pitch, int64_t n0, int64_t R, int64_t b0,
+                             int64_t nb) {
+    const int64_t row_bytes = a.k >> 4;
+    if (row_bytes % 16 == 0 && b0 % 16 == 0) {
+        // 16-byte pieces; the last may run past nb but not past the row
+        const int64_t pr = (nb + 15) / 16;
+        for (int64_t i = threadIdx.x; i < R * pr; i += kThreadsD) {
+            const int64_t rr = i / pr, pc = i - rr * pr;
+            int64_t n = n0 + rr;
+            n = n < a.n ? n : a.n - 1;
+            const uint4 v = *reinterpret_cast<const uint4 *>(a.scales + n * row_bytes + b0 + 16 * pc);
+            *reinterpret_cast<uint4 *>(sc + rr * pitch + 16 * pc) = v;
+        }
+    } else if (row_bytes % 4 == 0) {  // b0 is a multiple of 8
+        const int64_t pr = (nb + 3) / 4;
+        for (int64_t i = threadIdx.x; i < R * pr; i += kThreadsD) {
+            const int64_t rr = i / pr, pc = i - rr * pr;
+            int64_t n = n0 + rr;
+            n = n < a.n ? n : a.n - 1;
+            const uint32_t v = *reinterpret_cast<const uint32_t *>(a.scales + n * row_bytes + b0 + 4 * pc);
+            *reinterpret_cast<uint32_t *>(sc + rr * pitch + 4 * pc) = v;
+        }
+    } else {
+        for (int64_t i = threadIdx.x; i < R * nb; i += kThreadsD) {
+            const int64_t rr = i / nb, pc = i - rr * nb;
+            int64_t n = n0 + rr;
+            n = n < a.n ? n : a.n - 1;
+            sc[rr * pitch + pc] = a.scales[n * row_bytes + b0 + pc];
+        }
+    }
+}
+
+// One chunk: x fragments from the LDS window, weights from registers.
+// sc_off[g]: LDS byte offset of this lane's scale pair for row group g at the
+// unit's first chunk; cl: chunk index within the unit; col: x column of the
+// chunk within the window.
 template <int MT, int NW>
-__device__ __forceinline__ void mma_chunk_lds(const uint4 (&w)[NW], const uint32_t (&sc)[NW],
-                                              const uint16_t *lds, int64_t base, int64_t pitch, int64_t col,
-                                              int m_last, int lr, int lq, f32x4_t (&acc)[MT][NW]) {
+__device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *sc, const int (&sc_off)[NW],
+                                          int64_t cl, const uint16_t *xb, int64_t pitch, int64_t col, int m_last,
+                                          int lr, int lq, f32x4_t (&acc)[MT][NW]) {
     float sv[NW][2];
 #pragma unroll
-    for (int gi = 0; gi < NW; ++gi) {
-        sv[gi][0] = QERL_E4M3_F32(sc[gi], 0);
-        sv[gi][1] = QERL_E4M3_F32(sc[gi], 1);
+    for (int g = 0; g < NW; ++g) {
+        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sc + sc_off[g] + cl * 8);
+        sv[g][0] = QERL_E4M3_F32(s2, 0);
+        sv[g][1] = QERL_E4M3_F32(s2, 1);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -233,62 +465,91 @@ __device__ __forceinline__ void mma_chunk_lds(const uint4 (&w)[NW], const uint32
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = 16 * mt + lr < m_last ? 16 * mt + lr : m_last;
-            xa[mt] = *reinterpret_cast<const bf16x8_t *>(lds + (base + m * pitch + col + 32 * lq + 8 * j));
+            xa[mt] = *reinterpret_cast<const bf16x8_t *>(xb + (m * pitch + col + 32 * lq + 8 * j));
         }
 #pragma unroll
-        for (int gi = 0; gi < NW; ++gi) {
-            const uint32_t q = j == 0 ? w[gi].x : j == 1 ? w[gi].y : j == 2 ? w[gi].z : w[gi].w;
-            const bf16x8_t b = dequant8_d(q, sv[gi][j >> 1]);
+        for (int g = 0; g < NW; ++g) {
+            const uint32_t q = j == 0 ? w[g].x : j == 1 ? w[g].y : j == 2 ? w[g].z : w[g].w;
+            const bf16x8_t b = dequant8_d(q, sv[g][j >> 1]);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                acc[mt][gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][gi], 0, 0, 0);
+                acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][g], 0, 0, 0);
         }
     }
 }
 
-// Stage x[:, k0 .. kend) of every row into LDS (row pitch kslice + pad;
-// columns past kend as zero).  Thread t moves 16-byte pieces t, t + 256, ...;
-// addresses are clamped into range so every load is unconditional.
-template <int PIECES>
-__device__ __forceinline__ void stage_x(const GemmArgs &a, uint16_t *lds, int64_t k0, int64_t kend,
-                                        int64_t width, int64_t pitch) {
-    const int64_t per_row = width / 8;
-    uint4 v[PIECES];
-#pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-        const int64_t piece = threadIdx.x + (int64_t)i * kThreadsD;
-        const int64_t m = piece / per_row, col = (piece - m * per_row) * 8;
-        const int64_t mm = m < a.m ? m : a.m - 1;
-        const int64_t kk = k0 + col < kend ? k0 + col : kend - 8;
-        v[i] = *reinterpret_cast<const uint4 *>(a.x + mm * a.ldx + kk);
-        if (!(m < a.m && k0 + col < kend)) v[i] = make_uint4(0, 0, 0, 0);
+// Per-unit state of the streaming loop.
+template <int NW>
+struct Unit {
+    const GemmArgs *a;
+    uint16_t *xs;     // x double buffer in LDS
+    const uint8_t *sc;  // staged scales in LDS
+    int64_t xbuf, pitch;
+    int64_t c_begin, c_full_end, c_last, n0;
+    int m_last, lr, lq;
+    int sc_off[NW];
+};
+
+// One x window of W chunks.  The weight ring holds D chunks (D/W windows);
+// RELOAD: refill each consumed slot with the chunk D ahead (the window is
+// full); NEXTX: load the next window's x now and stage it at the end.  Issue
+// order is kept by scheduling barriers: the next window's x first, then each
+// chunk's refill right after the chunk is consumed.
+template <int MT, int NW, int PX, bool K32, int W, int D, int SG, bool RELOAD, bool NEXTX>
+__device__ __forceinline__ void run_window(const Unit<NW> &t, int64_t wi, uint4 (&w)[D][NW], XWin &xv,
+                                           f32x4_t (&acc)[MT][NW]) {
+    const GemmArgs &a = *t.a;
+    const int64_t cw = t.c_begin + wi * W;
+    if (NEXTX) {
+        load_x_window<PX, W>(a, (cw + W) * kChunkK, xv);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    const uint16_t *xb = t.xs + (wi & 1) * t.xbuf;
 #pragma unroll
-    for (int i = 0; i < PIECES; ++i) {
-        const int64_t piece = threadIdx.x + (int64_t)i * kThreadsD;
-        const int64_t m = piece / per_row, col = (piece - m * per_row) * 8;
-        if (m < a.m) *reinterpret_cast<uint4 *>(lds + (m * pitch + col)) = v[i];
+    for (int s = 0; s < W; ++s) {
+        const int64_t c = cw + s;
+        if (RELOAD || c < t.c_full_end)  // uniform; only the compute is guarded
+            mma_chunk<MT, NW>(w[SG * W + s], t.sc, t.sc_off, c - t.c_begin, xb, t.pitch, s * kChunkK, t.m_last, t.lr,
+                              t.lq, acc);
+        if (RELOAD) {
+            load_chunk<NW, K32>(a, t.n0, c + D < t.c_last ? c + D : t.c_last, t.lr, t.lq, w[SG * W + s]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (NEXTX) {
+        store_x_window<PX, W>(a, t.xs + ((wi + 1) & 1) * t.xbuf, t.pitch, xv);
+        __syncthreads();
     }
 }
 
-// PIECES >= ceil(m * kslice / 8 / 256): 16-byte staging pieces per thread
-template <int MT, int NW, int PIECES, bool K32>
+template <int MT, int NW, int PX, bool K32>
 __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
+    constexpr int W = 4 / MT;         // chunks per x window
+    constexpr int D = W < 2 ? 2 : W;  // chunks in the weight ring (D * NW 16-byte loads per lane)
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    if ((int64_t)blockIdx.x < p.producers) {  // LoRA producers go first so they start early
-        lora_producer(d, blockIdx.x);
+    if ((int64_t)blockIdx.x < p.producers) {
+        lora_producer<MT>(d, blockIdx.x, lds);
         return;
     }
-    extern __shared__ __attribute__((aligned(16))) uint16_t xs_lds[];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
+    uint8_t *sc = lds + p.sc_lds_off;
+    const int64_t xbuf = a.m * p.xpitch;  // elements per x buffer
     const int64_t u = blockIdx.x - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
-    const int64_t k_begin = slice * p.kslice;
-    const int64_t k_end = k_begin + p.kslice < a.k ? k_begin + p.kslice : a.k;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lq = lane >> 4;
-    const int64_t n0 = rblk * p.rows_per_unit + (int64_t)wave * 16 * NW;
-    const int64_t pitch = p.kslice + kXPad;
+    const int64_t c_begin = slice * p.cps;
+    const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
+    const int64_t c_full_end = c_end < p.full_chunks ? c_end : p.full_chunks;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t R = p.rows_per_unit;
+    const int64_t n_unit = rblk * R;
+    const int64_t n0 = n_unit + (int64_t)wave * 16 * NW;
     const int m_last = (int)a.m - 1;
+
+    int sc_off[NW];
+#pragma unroll
+    for (int g = 0; g < NW; ++g) sc_off[g] = (int)((wave * 16 * NW + 16 * g + lr) * p.sc_pitch + 2 * lq);
 
     f32x4_t acc[MT][NW];
 #pragma unroll
@@ -296,127 +557,341 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
 #pragma unroll
         for (int j = 0; j < NW; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int64_t c_begin = k_begin / kChunkK;
-    const int64_t c_end = (k_end + kChunkK - 1) / kChunkK;
-    const int64_t full_chunks = a.k / kChunkK;
-    const int64_t c_full_end = c_end < full_chunks ? c_end : full_chunks;
-
-    // ring prologue (chunk indices clamped into the slice's full chunks), then x
-    uint4 w[kDepth][NW];
-    uint32_t sc[kDepth][NW];
-    if (c_full_end > c_begin) {  // uniform
-        const int64_t c_last = c_full_end - 1;
+    const int64_t c_last = c_full_end - 1;  // the unit's last full chunk (< c_begin: none)
+    const int64_t sb0 = c_begin * 8;
+    const int64_t sb1 = c_end * 8 < (a.k >> 4) ? c_end * 8 : (a.k >> 4);
+    if constexpr (MT == 1) {
+        // ---- m <= 16: x and scales of the whole unit resident in LDS; the
+        // weights stream through a ring of D chunks with no barrier ----
+        constexpr int DR = 4;
+        uint4 w[DR][NW];
+        if (c_full_end > c_begin) {
 #pragma unroll
-        for (int s = 0; s < kDepth; ++s) {
-            const int64_t c = c_begin + s < c_last ? c_begin + s : c_last;
-            load_chunk_full<NW, K32>(a, n0, c, lr, lq, w[s], sc[s]);
+            for (int s = 0; s < DR; ++s)
+                load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
         }
-    }
-    stage_x<PIECES>(a, xs_lds, k_begin, k_end, p.kslice, pitch);
-    __syncthreads();
-
-    if (c_full_end > c_begin) {  // uniform
-        const int64_t c_last = c_full_end - 1;
-        for (int64_t c0 = c_begin; c0 < c_full_end; c0 += kDepth) {
+        stage_x_slice(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
+        stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
+        if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
+            const int64_t z0 = (a.k >> 4) - sb0, zn = p.full_chunks * 8 + 8 - (a.k >> 4);
+            for (int64_t i = tid; i < R * zn; i += kThreadsD) sc[(i / zn) * p.sc_pitch + z0 + i % zn] = 0;
+        }
+        __syncthreads();
+        int64_t c = c_begin;
+        for (; c + 2 * DR <= c_full_end; c += DR) {
 #pragma unroll
-            for (int s = 0; s < kDepth; ++s) {
-                const int64_t c = c0 + s;
-                if (c < c_full_end)  // uniform; the compute only, loads stay unconditional
-                    mma_chunk_lds<MT, NW>(w[s], sc[s], xs_lds, 0, pitch, (c - c_begin) * kChunkK, m_last, lr,
-                                          lq, acc);
-                const int64_t cn = c + kDepth < c_last ? c + kDepth : c_last;
-                load_chunk_full<NW, K32>(a, n0, cn, lr, lq, w[s], sc[s]);
+            for (int s = 0; s < DR; ++s) {
+                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                                  m_last, lr, lq, acc);
+                load_chunk<NW, K32>(a, n0, c + s + DR, lr, lq, w[s]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
+#pragma unroll
+            for (int s = 0; s < DR; ++s) {
+                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                                  m_last, lr, lq, acc);
+                load_chunk<NW, K32>(a, n0, c + s + DR < c_last ? c + s + DR : c_last, lr, lq, w[s]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            c += DR;
+        }
+#pragma unroll
+        for (int s = 0; s < DR; ++s)
+            if (c + s < c_full_end)  // uniform
+                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                                  m_last, lr, lq, acc);
+        if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
+            uint4 wt[NW];
+            load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
+            mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
+                              m_last, lr, lq, acc);
+        }
+    } else {
+    // ---- 16 < m: prologue: the weight ring, x window 0, the unit's scales ----
+    uint4 w[D][NW];
+    if (c_full_end > c_begin) {
+#pragma unroll
+        for (int s = 0; s < D; ++s) load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
     }
-    if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
+    XWin xv;
+    load_x_window<PX, W>(a, c_begin * kChunkK, xv);
+    stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
+    store_x_window<PX, W>(a, xs, p.xpitch, xv);
+    __syncthreads();
+
+    // ---- windows: the last RW = D/W of them no longer reload ----
+    Unit<NW> t;
+    t.a = &a;
+    t.xs = xs;
+    t.sc = sc;
+    t.xbuf = xbuf;
+    t.pitch = p.xpitch;
+    t.c_begin = c_begin;
+    t.c_full_end = c_full_end;
+    t.c_last = c_last;
+    t.n0 = n0;
+    t.m_last = m_last;
+    t.lr = lr;
+    t.lq = lq;
+#pragma unroll
+    for (int g = 0; g < NW; ++g) t.sc_off[g] = sc_off[g];
+    constexpr int RW = D / W;
+    const int64_t nwin = (c_full_end - c_begin + W - 1) / W;  // windows holding a full chunk
+    int64_t wi = 0;
+    for (; wi + 2 * RW <= nwin; wi += RW) {
+        run_window<MT, NW, PX, K32, W, D, 0, true, true>(t, wi, w, xv, acc);
+        if (RW == 2) run_window<MT, NW, PX, K32, W, D, 1, true, true>(t, wi + 1, w, xv, acc);
+    }
+    const int64_t rem = nwin - wi;  // RW <= rem < 2 RW, or nwin < RW
+    if (RW == 1) {
+        if (rem == 1) run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi, w, xv, acc);
+    } else if (rem == 3) {
+        run_window<MT, NW, PX, K32, W, D, 0, true, true>(t, wi, w, xv, acc);
+        run_window<MT, NW, PX, K32, W, D, 1, false, true>(t, wi + 1, w, xv, acc);
+        run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi + 2, w, xv, acc);
+    } else if (rem == 2) {
+        run_window<MT, NW, PX, K32, W, D, 0, false, true>(t, wi, w, xv, acc);
+        run_window<MT, NW, PX, K32, W, D, 1, false, false>(t, wi + 1, w, xv, acc);
+    } else if (rem == 1) {
+        run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi, w, xv, acc);
+    }
+    // ---- the partial last chunk of K (k % 128 != 0) ----
+    if (c_end > c_full_end) {
+        uint16_t *xb = xs + (nwin & 1) * xbuf;  // not read by the last window
+        __syncthreads();
+        const int64_t k0 = p.full_chunks * kChunkK;
+        for (int64_t i = tid; i < a.m * (kChunkK / 8); i += kThreadsD) {
+            const int64_t m = i / (kChunkK / 8), col = (i % (kChunkK / 8)) * 8;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (k0 + col < a.k) v = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
+            *reinterpret_cast<uint4 *>(xb + m * p.xpitch + col) = v;
+        }
+        // scale bytes of the chunk past k: zero (the weights there are zero too)
+        const int64_t z0 = (a.k >> 4) - sb0, zn = p.full_chunks * 8 + 8 - (a.k >> 4);
+        for (int64_t i = tid; i < R * zn; i += kThreadsD) sc[(i / zn) * p.sc_pitch + z0 + i % zn] = 0;
         uint4 wt[NW];
-        uint32_t st[NW];
-        load_chunk_tail<NW>(a, n0, full_chunks, lr, lq, wt, st);
-        mma_chunk_lds<MT, NW>(wt, st, xs_lds, 0, pitch, (full_chunks - c_begin) * kChunkK, m_last, lr, lq, acc);
+        load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
+        __syncthreads();
+        mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xb, p.xpitch, 0, m_last, lr, lq, acc);
     }
 
-    // FP32 partial sums of this slice: P[slice][m][n]
-    float *part = d.partials() + slice * a.m * a.n;
+    }
+    const int64_t tile_floats = R * 16 * MT;
+    const int wave_off = wave * MT * NW * 64;  // f32x4 slots before this wave's in a tile
+    if (MT > 1) {
+        // 16 < m: every unit stores its tile; finish_kernel reduces after the
+        // kernel boundary
+        f32x4_t *tile = reinterpret_cast<f32x4_t *>(d.part() + u * tile_floats) + wave_off + lane;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int gi = 0; gi < NW; ++gi)
+            for (int g = 0; g < NW; ++g)
+                if (16 * mt + 4 * lq < a.m) tile[(mt * NW + g) * 64] = acc[mt][g];
+        return;
+    }
+
+    // ---- m <= 16, split K: the last unit of the row block to arrive sums the slices ----
+    __shared__ uint32_t s_flag;
+    if (p.slices > 1) {
+        {
+            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + u * tile_floats);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int g = 0; g < NW; ++g)
+                    if (16 * mt + 4 * lq < a.m)
+                        store_f4_coherent(rs, (wave_off + (mt * NW + g) * 64 + lane) * 16, acc[mt][g]);
+            wait_vm();
+        }
+        __syncthreads();
+        if (tid == 0) s_flag = ctr_add(d.ctr() + kCtrRow + rblk, 1u) == (uint32_t)(p.slices - 1);
+        __syncthreads();
+        if (!s_flag) return;
+        // every slice (this one included) from the partials, in slice order
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int g = 0; g < NW; ++g) acc[mt][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t s = 0; s < p.slices; ++s) {
+            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + (s * p.row_blocks + rblk) * tile_floats);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int g = 0; g < NW; ++g)
+                    if (16 * mt + 4 * lq < a.m)
+                        acc[mt][g] = acc[mt][g] + load_f4_coherent(rs, (wave_off + (mt * NW + g) * 64 + lane) * 16);
+        }
+        if (tid == 0) ctr_store(d.ctr() + kCtrRow + rblk, 0u);
+    }
+
+    // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
+    uint16_t *th = reinterpret_cast<uint16_t *>(lds);
+    uint16_t *tl = th + 16 * MT * p.rp;
+    // B [n, j] for this lane's rows and ranks 8 lq .. 8 lq + 7 of the block jb
+    auto load_b = [&](int g, int64_t jb) -> bf16x8_t {
+        int64_t nb = n0 + 16 * g + lr;
+        nb = nb < a.n ? nb : a.n - 1;
+        const uint16_t *br = a.lora_b + nb * a.r;
+        const int64_t j0 = jb + 8 * lq;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if ((a.r & 7) == 0) {
+            if (j0 < a.r) v = *reinterpret_cast<const uint4 *>(br + j0);
+        } else {
+            uint16_t e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = j0 + i < a.r ? br[j0 + i] : (uint16_t)0;
+            __builtin_memcpy(&v, e, 16);
+        }
+        return as_bf16x8_d(v);
+    };
+    bf16x8_t b0[NW];  // the first rank block, loaded before the wait for t
+    if (a.r > 0)
+#pragma unroll
+        for (int g = 0; g < NW; ++g) b0[g] = load_b(g, 0);
+    if (a.r > 0) {
+        __syncthreads();  // the LDS is reused below
+        if (tid == 0) {
+            uint32_t it = 0;
+            while (ctr_load(d.ctr() + kCtrProd) < (uint32_t)p.producers && ++it < kSpinLimit)
+                __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+        // t = the producers' partials summed in producer order; wave w takes
+        // the tiles i = w, w + 4, ... and writes them as BF16 hi/lo [m][j]
+        const int JT = (int)p.jt;
+        const int64_t ptile = (int64_t)MT * JT * 64 * 4;
+        for (int i = wave; i < MT * JT; i += kWaves) {
+            f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t q = 0; q < p.producers; ++q) {
+                const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + q * ptile);
+                sum = sum + load_f4_coherent(rs, (i * 64 + lane) * 16);
+            }
+            const int mt = i / JT, jt = i - mt * JT;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t off = (16 * mt + 4 * lq + v) * p.rp + 16 * jt + lr;
+                const uint16_t hi = f32_to_bf16_bits(sum[v]);
+                th[off] = hi;
+                tl[off] = f32_to_bf16_bits(sum[v] - __uint_as_float((uint32_t)hi << 16));
+            }
+        }
+        // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
+        for (int64_t i = tid; i < 16 * MT * (p.rp - 16 * JT); i += kThreadsD) {
+            const int64_t m = i / (p.rp - 16 * JT), j = 16 * JT + i % (p.rp - 16 * JT);
+            th[m * p.rp + j] = 0;
+            tl[m * p.rp + j] = 0;
+        }
+        __syncthreads();
+        if (tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
+            ctr_store(d.ctr() + kCtrProd, 0u);
+            ctr_store(d.ctr() + kCtrDone, 0u);
+        }
+    }
+    const float st = *a.tensor_scale, lam = a.lora_scale;
+#pragma unroll
+    for (int g = 0; g < NW; ++g) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4_t l = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t jb = 0; jb < p.rp; jb += 32) {
+                const bf16x8_t bfrag = jb == 0 ? b0[g] : load_b(g, jb);
+                const int64_t off = (16 * mt + lr) * p.rp + jb + 8 * lq;
+                l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(th + off), bfrag, l,
+                                                            0, 0, 0);
+                l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(tl + off), bfrag, l,
+                                                            0, 0, 0);
+            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t m = 16 * mt + 4 * lq + v;
-                const int64_t n = n0 + 16 * gi + lr;
-                if (m < a.m && n < a.n) part[m * a.n + n] = acc[mt][gi][v];
+                const int64_t n = n0 + 16 * g + lr;
+                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[mt][g][v] + lam * l[v]);
             }
+        }
+    }
 }
 
-// y[m, n] = bf16(s_t * sum_s P[s][m][n] + lora_scale * sum_j t[m][j] B[n][j]);
-// one thread per output, partials summed in slice order.
+// 16 < m: y[m, n] = bf16(s_t * sum over slices of the partial tiles (in slice
+// order) + lora_scale * sum_j t[m][j] B[n][j]).  Thread (n, quad) handles the
+// rows 4 quad .. 4 quad + 3 of column n, which one lane of one tile holds as a
+// float4.  Workgroup: 64 columns x 4 quads (16 rows); t of its rows in LDS.
+template <int MT, int NW>
 __global__ __launch_bounds__(256) void finish_kernel(Decode d) {
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t m = blockIdx.y;
-    __shared__ float ts[kMaxRank];
-    for (int j = threadIdx.x; j < a.r; j += 256) ts[j] = d.t32()[m * a.r + j];
+    __shared__ float ts[16][kMaxRank];
+    const int tid = threadIdx.x;
+    const int64_t n = (int64_t)blockIdx.x * 64 + (tid & 63);
+    const int64_t m0 = (int64_t)blockIdx.y * 16;
+    const int64_t quad = blockIdx.y * 4 + (tid >> 6);
+    for (int64_t i = tid; i < 16 * (int64_t)a.r; i += 256) {
+        const int64_t mm = i / a.r, j = i - mm * a.r;
+        ts[mm][j] = m0 + mm < a.m ? d.t32()[(m0 + mm) * a.r + j] : 0.0f;
+    }
     __syncthreads();
-    if (n >= a.n) return;
-    const float *part = d.partials() + m * a.n + n;
-    const int64_t stride = a.m * a.n;
-    float acc = 0.0f;
-    int64_t s = 0;
-    for (; s + 8 <= p.slices; s += 8) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = part[(s + i) * stride];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc += v[i];
-    }
-    for (; s < p.slices; ++s) acc += part[s * stride];
-    float lora = 0.0f;
+    if (n >= a.n || 4 * quad >= a.m) return;
+    const int64_t R = p.rows_per_unit;
+    const int64_t rblk = n / R, rem = n - rblk * R;
+    const int64_t wave = rem / (16 * NW), g = (rem / 16) % NW, lr = rem % 16;
+    const int64_t mt = quad / 4, lq = quad % 4;
+    const int64_t slot = ((wave * MT + mt) * NW + g) * 64 + lq * 16 + lr;
+    const int64_t tile_floats = R * 16 * MT;
+    const float *part = d.part();
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t s = 0; s < p.slices; ++s)
+        acc = acc + *reinterpret_cast<const f32x4_t *>(part + (s * p.row_blocks + rblk) * tile_floats + slot * 4);
+    float lora[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint16_t *br = a.lora_b + n * a.r;
+    const int q0 = (int)(tid >> 6) * 4;  // this thread's first row in ts
+    int j = 0;
     if ((a.r & 7) == 0) {
-        for (int j = 0; j < a.r; j += 8) {
-            const uint4 b = *reinterpret_cast<const uint4 *>(br + j);
-            lora = __builtin_fmaf(ts[j + 0], bf16lo_to_f32(b.x), lora);
-            lora = __builtin_fmaf(ts[j + 1], bf16hi_to_f32(b.x), lora);
-            lora = __builtin_fmaf(ts[j + 2], bf16lo_to_f32(b.y), lora);
-            lora = __builtin_fmaf(ts[j + 3], bf16hi_to_f32(b.y), lora);
-            lora = __builtin_fmaf(ts[j + 4], bf16lo_to_f32(b.z), lora);
-            lora = __builtin_fmaf(ts[j + 5], bf16hi_to_f32(b.z), lora);
-            lora = __builtin_fmaf(ts[j + 6], bf16lo_to_f32(b.w), lora);
-            lora = __builtin_fmaf(ts[j + 7], bf16hi_to_f32(b.w), lora);
+        for (; j < a.r; j += 8) {
+            const uint4 b8 = *reinterpret_cast<const uint4 *>(br + j);
+            const uint32_t bw[4] = {b8.x, b8.y, b8.z, b8.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e], bf16lo_to_f32(bw[e]), lora[v]);
+                    lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e + 1], bf16hi_to_f32(bw[e]), lora[v]);
+                }
         }
-    } else {
-        for (int j = 0; j < a.r; ++j) lora = __builtin_fmaf(ts[j], bf16lo_to_f32(br[j]), lora);
     }
-    a.y[m * a.ldy + n] = f32_to_bf16_bits(*a.tensor_scale * acc + a.lora_scale * lora);
+    for (; j < a.r; ++j) {
+        const float b = bf16lo_to_f32(br[j]);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lora[v] = __builtin_fmaf(ts[q0 + v][j], b, lora[v]);
+    }
+    const float st = *a.tensor_scale, lam = a.lora_scale;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t m = 4 * quad + v;
+        if (m < a.m) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[v] + lam * lora[v]);
+    }
 }
 
-template <int MT, int NW, int PIECES, bool K32>
+template <int MT, int NW, int PX, bool K32>
 hipError_t launch_stream(const Decode &d, hipStream_t stream) {
-    auto kern = stream_kernel<MT, NW, PIECES, K32>;
+    auto kern = stream_kernel<MT, NW, PX, K32>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBudget);
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
     const int64_t grid = d.p.producers + d.p.units;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsD), (size_t)d.p.lds_bytes, stream, d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || MT == 1) return e;
+    const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));
+    hipLaunchKernelGGL((finish_kernel<MT, NW>), fgrid, dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 
-template <int MT, int NW, bool K32>
-hipError_t launch_stream_pieces(const Decode &d, int64_t pieces, hipStream_t stream) {
-    if (pieces <= 2) return launch_stream<MT, NW, 2, K32>(d, stream);
-    if (pieces <= 4) return launch_stream<MT, NW, 4, K32>(d, stream);
-    if (pieces <= 8) return launch_stream<MT, NW, 8, K32>(d, stream);
-    if (pieces <= 16) return launch_stream<MT, NW, 16, K32>(d, stream);
-    return hipErrorInvalidConfiguration;
-}
-
-template <int MT, int NW>
-hipError_t launch_stream_k(const Decode &d, int64_t pieces, hipStream_t stream) {
-    return (d.a.k & 31) == 0 ? launch_stream_pieces<MT, NW, true>(d, pieces, stream)
-                             : launch_stream_pieces<MT, NW, false>(d, pieces, stream);
+template <bool K32>
+hipError_t launch_stream_k(const Decode &d, hipStream_t stream) {
+    if (d.p.mt == 1) return launch_stream<1, 1, 1, K32>(d, stream);
+    if (d.p.mt == 2) return launch_stream<2, 2, 4, K32>(d, stream);
+    return launch_stream<4, 4, 4, K32>(d, stream);
 }
 
 }  // namespace
@@ -427,17 +902,10 @@ size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
 
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
     const Decode d{a, make_decode_plan(a.m, a.n, a.k, a.r)};
-    if (d.p.producers + d.p.units > 0x7FFFFFFF || d.p.lds_bytes > kLdsBudget) return hipErrorInvalidConfiguration;
-    // 16-byte staging pieces per thread for the unit's x slice
-    const int64_t pieces = (a.m * d.p.kslice / 8 + kThreadsD - 1) / kThreadsD;
-    hipError_t e;
-    if (d.p.mt == 1) e = launch_stream_k<1, 1>(d, pieces, stream);
-    else if (d.p.mt == 2) e = launch_stream_k<2, 2>(d, pieces, stream);
-    else e = launch_stream_k<4, 4>(d, pieces, stream);
-    if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)((a.n + 255) / 256), (unsigned)a.m);
-    hipLaunchKernelGGL(finish_kernel, fgrid, dim3(256), 0, stream, d);
-    return hipGetLastError();
+    if (d.p.row_blocks < 1 || d.p.producers + d.p.units > 0x7FFFFFFF || d.p.lds_bytes > kLdsLimit ||
+        d.p.rows_per_unit * 16 * d.p.mt * d.p.units * 4 > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    return (a.k & 31) == 0 ? launch_stream_k<true>(d, stream) : launch_stream_k<false>(d, stream);
 }
 
 }  // namespace qerl

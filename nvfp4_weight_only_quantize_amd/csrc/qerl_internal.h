@@ -34,8 +34,12 @@ struct GemmArgs {
     void *workspace;
 };
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+// Every GEMM workspace starts with this many bytes of counters for the decode
+// path's in-kernel split-K reduction: zero before first use, left zero by
+// every call (the other path never writes them).
+constexpr int64_t kGemmCtrBytes = 64 * 1024;
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
-// decode batches (m <= kDecodeMaxM): HBM-streaming split-K path in decode.hip
+// decode batches (m <= kDecodeMaxM): HBM-streaming path in decode.hip
 constexpr int64_t kDecodeMaxM = 64;
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream);

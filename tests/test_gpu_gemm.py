@@ -49,7 +49,8 @@ def _x(m, k, seed, outliers=0.005):
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16, 33, 64, 100, 256])
 @pytest.mark.parametrize("nkr", [(96, 256, 16), (77, 512, 32), (130, 1024, 8), (64, 48, 4),
-                                 (33, 80, 0), (200, 2048, 64)])
+                                 (33, 80, 0), (200, 2048, 64), (5, 128, 4), (300, 1040, 24),
+                                 (1000, 3600, 32)])
 def test_small_shapes(m, nkr):
     n, k, r = nkr
     L = Layer(n, k, r, seed=100 + n + k + r)
@@ -161,3 +162,27 @@ def test_gpu_quantizer_feeds_gemm():
     packed, scales, s_t = oracle.nvfp4_quantize(synth.bf16_bits(w))
     ref = oracle.w4a16_lora_gemm(x, packed, scales, s_t, synth.bf16_bits(a), synth.bf16_bits(b), 2.0)
     assert_gemm_close(bf16_to_f64(y), ref, "quantize->gemm")
+
+
+def test_shared_workspace_sequence_is_deterministic():
+    """One zero-filled workspace serves a mixed sequence of calls (decode with and
+    without split K and LoRA, and the large-m path); each output equals the one
+    from a fresh workspace bit for bit, and the counter region ends zero."""
+    cases = [(1, 3584, 3584, 32), (8, 512, 3584, 32), (64, 18944 // 4, 3584, 32), (33, 1000, 3600, 24),
+             (1, 3584, 18944 // 2, 0), (100, 512, 1024, 16), (16, 77, 512, 8), (64, 3584, 3584, 32)]
+    layers, xs = [], []
+    for i, (m, n, k, r) in enumerate(cases):
+        layers.append(Layer(n, k, r, seed=900 + i))
+        xs.append(bits_to_gpu(_x(m, k, seed=950 + i)))
+    need = max(q.w4a16_lora_gemm_workspace_size(m, n, k, r) for m, n, k, r in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    fresh = [q.w4a16_lora_gemm(x, L.wq, L.a, L.b, L.lam) for x, L in zip(xs, layers)]
+    for _ in range(3):
+        for i, (x, L) in enumerate(zip(xs, layers)):
+            y = q.w4a16_lora_gemm(x, L.wq, L.a, L.b, L.lam, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, fresh[i]), f"case {cases[i]}"
+    assert int(torch.count_nonzero(ws[:64 * 1024])) == 0
+    for i in (0, 3):
+        m, n, k, r = cases[i]
+        assert_gemm_close(bf16_to_f64(fresh[i]), layers[i].ref(synth.bf16_bits(xs[i].cpu())), f"case {cases[i]}")
