@@ -50,6 +50,7 @@ constexpr int64_t kChunkK = 128;          // K elements per chunk
 constexpr int kXPad = 8;                  // BF16 padding per staged x row
 constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
 constexpr int64_t kXBudget = 36 * 1024;   // LDS for a unit's x slice (m <= 16)
+constexpr int kXPieces = (int)(kXBudget / 16 / 256);  // 16-byte x pieces per thread when staging it
 constexpr int64_t kLdsLimit = 63 * 1024;
 constexpr int64_t kProdChunks = 8;        // K chunks per LoRA producer
 constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
@@ -399,14 +400,43 @@ __device__ __forceinline__ void store_x_window(const GemmArgs &a, uint16_t *buf,
 }
 
 // m <= 16: the unit's x slice, rows [0, m) x columns [k0, k0 + width), into
-// LDS rows of `pitch` elements; columns at or past k are zero.
+// LDS rows of `pitch` elements; columns at or past k are zero.  All loads of a
+// thread are issued before the first LDS write.
 __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
-    const int64_t per_row = width / 8;
-    for (int64_t i = threadIdx.x; i < a.m * per_row; i += kThreadsD) {
+    const int64_t per_row = width / 8, total = a.m * per_row;  // total <= kXPieces * kThreadsD
+    uint4 v[kXPieces];
+#pragma unroll
+    for (int u = 0; u < kXPieces; ++u) {
+        const int64_t i = threadIdx.x + (int64_t)u * kThreadsD;
         const int64_t m = i / per_row, col = (i - m * per_row) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (k0 + col < a.k) v = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
-        *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (i < total && k0 + col < a.k) v[u] = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
+    }
+#pragma unroll
+    for (int u = 0; u < kXPieces; ++u) {
+        const int64_t i = threadIdx.x + (int64_t)u * kThreadsD;
+        const int64_t m = i / per_row, col = (i - m * per_row) * 8;
+        if (i < total) *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v[u];
+    }
+}
+
+// Copy `total` items from global to LDS, kBatch per thread in flight: a plain
+// loop would wait for every load before issuing the next.
+constexpr int kBatch = 8;
+template <typename T, typename Src, typename Dst>
+__device__ __forceinline__ void batched_copy(int64_t total, Src src, Dst dst) {
+    for (int64_t base = threadIdx.x; base < total; base += kBatch * kThreadsD) {
+        T v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = base + (int64_t)u * kThreadsD;
+            if (i < total) v[u] = src(i);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = base + (int64_t)u * kThreadsD;
+            if (i < total) dst(i, v[u]);
+        }
     }
 }
 
@@ -415,32 +445,43 @@ __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, in
 __device__ void stage_scales(const GemmArgs &a, uint8_t *sc, int64_t pitch, int64_t n0, int64_t R, int64_t b0,
                              int64_t nb) {
     const int64_t row_bytes = a.k >> 4;
+    auto row_of = [&](int64_t rr) { return n0 + rr < a.n ? n0 + rr : a.n - 1; };
     if (row_bytes % 16 == 0 && b0 % 16 == 0) {
         // 16-byte pieces; the last may run past nb but not past the row
         const int64_t pr = (nb + 15) / 16;
-        for (int64_t i = threadIdx.x; i < R * pr; i += kThreadsD) {
-            const int64_t rr = i / pr, pc = i - rr * pr;
-            int64_t n = n0 + rr;
-            n = n < a.n ? n : a.n - 1;
-            const uint4 v = *reinterpret_cast<const uint4 *>(a.scales + n * row_bytes + b0 + 16 * pc);
-            *reinterpret_cast<uint4 *>(sc + rr * pitch + 16 * pc) = v;
-        }
+        batched_copy<uint4>(
+            R * pr,
+            [&](int64_t i) {
+                const int64_t rr = i / pr, pc = i - rr * pr;
+                return *reinterpret_cast<const uint4 *>(a.scales + row_of(rr) * row_bytes + b0 + 16 * pc);
+            },
+            [&](int64_t i, const uint4 &v) {
+                const int64_t rr = i / pr, pc = i - rr * pr;
+                *reinterpret_cast<uint4 *>(sc + rr * pitch + 16 * pc) = v;
+            });
     } else if (row_bytes % 4 == 0) {  // b0 is a multiple of 8
         const int64_t pr = (nb + 3) / 4;
-        for (int64_t i = threadIdx.x; i < R * pr; i += kThreadsD) {
-            const int64_t rr = i / pr, pc = i - rr * pr;
-            int64_t n = n0 + rr;
-            n = n < a.n ? n : a.n - 1;
-            const uint32_t v = *reinterpret_cast<const uint32_t *>(a.scales + n * row_bytes + b0 + 4 * pc);
-            *reinterpret_cast<uint32_t *>(sc + rr * pitch + 4 * pc) = v;
-        }
+        batched_copy<uint32_t>(
+            R * pr,
+            [&](int64_t i) {
+                const int64_t rr = i / pr, pc = i - rr * pr;
+                return *reinterpret_cast<const uint32_t *>(a.scales + row_of(rr) * row_bytes + b0 + 4 * pc);
+            },
+            [&](int64_t i, const uint32_t &v) {
+                const int64_t rr = i / pr, pc = i - rr * pr;
+                *reinterpret_cast<uint32_t *>(sc + rr * pitch + 4 * pc) = v;
+            });
     } else {
-        for (int64_t i = threadIdx.x; i < R * nb; i += kThreadsD) {
-            const int64_t rr = i / nb, pc = i - rr * nb;
-            int64_t n = n0 + rr;
-            n = n < a.n ? n : a.n - 1;
-            sc[rr * pitch + pc] = a.scales[n * row_bytes + b0 + pc];
-        }
+        batched_copy<uint8_t>(
+            R * nb,
+            [&](int64_t i) {
+                const int64_t rr = i / nb, pc = i - rr * nb;
+                return a.scales[row_of(rr) * row_bytes + b0 + pc];
+            },
+            [&](int64_t i, const uint8_t &v) {
+                const int64_t rr = i / nb, pc = i - rr * nb;
+                sc[rr * pitch + pc] = v;
+            });
     }
 }
 
@@ -714,14 +755,19 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int g = 0; g < NW; ++g) acc[mt][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t s = 0; s < p.slices; ++s) {
-            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + (s * p.row_blocks + rblk) * tile_floats);
+        if (4 * lq < a.m) {  // MT == 1 here: one tile per lane, kBatch slices in flight
+            for (int64_t s0 = 0; s0 < p.slices; s0 += kBatch) {
+                f32x4_t v[kBatch];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+                for (int u = 0; u < kBatch; ++u) {
+                    const int64_t s = s0 + u < p.slices ? s0 + u : p.slices - 1;
+                    v[u] = load_f4_coherent(coherent_rsrc(d.part() + (s * p.row_blocks + rblk) * tile_floats),
+                                            (wave_off + lane) * 16);
+                }
 #pragma unroll
-                for (int g = 0; g < NW; ++g)
-                    if (16 * mt + 4 * lq < a.m)
-                        acc[mt][g] = acc[mt][g] + load_f4_coherent(rs, (wave_off + (mt * NW + g) * 64 + lane) * 16);
+                for (int u = 0; u < kBatch; ++u)
+                    if (s0 + u < p.slices) acc[0][0] = acc[0][0] + v[u];
+            }
         }
         if (tid == 0) ctr_store(d.ctr() + kCtrRow + rblk, 0u);
     }
@@ -764,9 +810,16 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         const int64_t ptile = (int64_t)MT * JT * 64 * 4;
         for (int i = wave; i < MT * JT; i += kWaves) {
             f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t q = 0; q < p.producers; ++q) {
-                const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + q * ptile);
-                sum = sum + load_f4_coherent(rs, (i * 64 + lane) * 16);
+            for (int64_t q0 = 0; q0 < p.producers; q0 += kBatch) {  // kBatch producers in flight, summed in order
+                f32x4_t v[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int64_t q = q0 + u < p.producers ? q0 + u : p.producers - 1;
+                    v[u] = load_f4_coherent(coherent_rsrc(d.tpart() + q * ptile), (i * 64 + lane) * 16);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u)
+                    if (q0 + u < p.producers) sum = sum + v[u];
             }
             const int mt = i / JT, jt = i - mt * JT;
 #pragma unroll
@@ -840,8 +893,17 @@ __global__ __launch_bounds__(256) void finish_kernel(Decode d) {
     const int64_t tile_floats = R * 16 * MT;
     const float *part = d.part();
     f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t s = 0; s < p.slices; ++s)
-        acc = acc + *reinterpret_cast<const f32x4_t *>(part + (s * p.row_blocks + rblk) * tile_floats + slot * 4);
+    for (int64_t s0 = 0; s0 < p.slices; s0 += kBatch) {  // kBatch slices in flight, summed in order
+        f32x4_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t s = s0 + u < p.slices ? s0 + u : p.slices - 1;
+            v[u] = *reinterpret_cast<const f32x4_t *>(part + (s * p.row_blocks + rblk) * tile_floats + slot * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (s0 + u < p.slices) acc = acc + v[u];
+    }
     float lora[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const uint16_t *br = a.lora_b + n * a.r;
     const int q0 = (int)(tid >> 6) * 4;  // this thread's first row in ts
