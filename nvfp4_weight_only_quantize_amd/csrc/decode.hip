@@ -52,8 +52,9 @@ constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
 constexpr int64_t kXBudget = 36 * 1024;   // LDS for a unit's x slice (m <= 16)
 constexpr int kXPieces = (int)(kXBudget / 16 / 256);  // 16-byte x pieces per thread when staging it
 constexpr int64_t kLdsLimit = 63 * 1024;
-constexpr int64_t kProdChunks = 8;        // K chunks per LoRA producer
+constexpr int64_t kProdChunks = 4;        // K chunks per LoRA producer
 constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
+constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int64_t kTargetUnits = 256;
@@ -120,7 +121,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.sc_lds_off = (x_bytes + 15) / 16 * 16;
     int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
     const int64_t epi = p.mt == 1 ? 16 * p.rp * 2 * 2 : 0;  // t hi/lo in the one-launch epilogue
-    const int64_t prod = (int64_t)p.mt * p.jt * 64 * 16;  // producer wave reduction
+    const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16;  // producer wave reduction
     if (lds < epi) lds = epi;
     if (lds < prod) lds = prod;
     p.lds_bytes = lds;
@@ -207,98 +208,91 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     const int JT = (int)d.p.jt;
     const int64_t kb = p * kProdChunks * kChunkK;
     const int64_t ke = kb + kProdChunks * kChunkK < a.k ? kb + kProdChunks * kChunkK : a.k;
-    const uint16_t *xrow[MT];
-#pragma unroll
+    const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
+    const __amdgpu_buffer_rsrc_t rs_own = coherent_rsrc(d.tpart() + p * tile_floats);
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
+    // one m-tile and two rank tiles at a time, so the producer path never
+    // needs more registers than the streaming path; each wave's steps (32
+    // elements, every 4th of the range) in groups of PS with all loads of a
+    // group issued before its products
+    constexpr int PS = 4;
     for (int mt = 0; mt < MT; ++mt) {
-        const int64_t m = 16 * mt + lr < a.m ? 16 * mt + lr : a.m - 1;
-        xrow[mt] = a.x + m * a.ldx;
-    }
-    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);
-    for (int jg = 0; jg < JT; jg += kProdTiles) {  // rank tiles jg, jg + 1
-        f32x4_t acc[MT][kProdTiles];
+        const int64_t mrow = 16 * mt + lr < a.m ? 16 * mt + lr : a.m - 1;
+        const uint16_t *xrow = a.x + mrow * a.ldx;
+        for (int jg = 0; jg < JT; jg += kProdTiles) {
+            f32x4_t acc[kProdTiles];
 #pragma unroll
-        for (int i = 0; i < MT; ++i)
+            for (int j = 0; j < kProdTiles; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t k0 = kb + 32 * wave; k0 < ke; k0 += 4 * 32 * PS) {
+                uint4 xv[PS], av[PS][kProdTiles];
 #pragma unroll
-            for (int j = 0; j < kProdTiles; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        // a wave's steps (32 elements each, every 4th of the range) in groups
-        // of PS, all loads of a group issued before its products: the
-        // producers sit on the path to every epilogue, so they must not wait
-        // on memory once per step
-        constexpr int PS = MT == 1 ? 8 : 4;
-        for (int64_t k0 = kb + 32 * wave; k0 < ke; k0 += 4 * 32 * PS) {
-            uint4 xv[PS][MT], av[PS][kProdTiles];
+                for (int u = 0; u < PS; ++u) {
+                    const int64_t kk = k0 + 128 * u + 8 * lq;
+                    const int64_t kc = kk < ke ? kk : ke - 8;  // k % 16 == 0: a piece never straddles the end
+                    xv[u] = *reinterpret_cast<const uint4 *>(xrow + kc);
 #pragma unroll
-            for (int u = 0; u < PS; ++u) {
-                const int64_t kk = k0 + 128 * u + 8 * lq;
-                const int64_t kc = kk < ke ? kk : ke - 8;  // k % 16 == 0: a piece never straddles the end
+                    for (int jj = 0; jj < kProdTiles; ++jj) {
+                        const int jr = 16 * (jg + jj) + lr;
+                        const int64_t j = jr < a.r ? jr : a.r - 1;
+                        av[u][jj] = *reinterpret_cast<const uint4 *>(a.lora_a + j * a.k + kc);
+                    }
+                }
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xv[u][mt] = *reinterpret_cast<const uint4 *>(xrow[mt] + kc);
+                for (int u = 0; u < PS; ++u) {
+                    const bool kin = k0 + 128 * u + 8 * lq < ke;
+                    const bf16x8_t xa = as_bf16x8_d(kin ? xv[u] : make_uint4(0, 0, 0, 0));
 #pragma unroll
-                for (int jj = 0; jj < kProdTiles; ++jj) {
-                    const int jr = 16 * (jg + jj) + lr;
-                    const int64_t j = jr < a.r ? jr : a.r - 1;
-                    av[u][jj] = *reinterpret_cast<const uint4 *>(a.lora_a + j * a.k + kc);
+                    for (int jj = 0; jj < kProdTiles; ++jj) {
+                        const bool jin = kin && 16 * (jg + jj) + lr < a.r;
+                        acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            xa, as_bf16x8_d(jin ? av[u][jj] : make_uint4(0, 0, 0, 0)), acc[jj], 0, 0, 0);
+                    }
                 }
             }
+            // the four waves' tiles, summed in wave order by wave 0 and published
 #pragma unroll
-            for (int u = 0; u < PS; ++u) {
-                const bool kin = k0 + 128 * u + 8 * lq < ke;
-                bf16x8_t xa[MT];
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) xa[mt] = as_bf16x8_d(kin ? xv[u][mt] : make_uint4(0, 0, 0, 0));
+            for (int jj = 0; jj < kProdTiles; ++jj) red[(wave * kProdTiles + jj) * 64 + lane] = acc[jj];
+            __syncthreads();
+            if (wave == 0) {
 #pragma unroll
                 for (int jj = 0; jj < kProdTiles; ++jj) {
-                    const bool jin = kin && 16 * (jg + jj) + lr < a.r;
-                    const bf16x8_t b = as_bf16x8_d(jin ? av[u][jj] : make_uint4(0, 0, 0, 0));
+                    if (jg + jj >= JT) continue;
+                    f32x4_t t = red[jj * 64 + lane];
 #pragma unroll
-                    for (int mt = 0; mt < MT; ++mt)
-                        acc[mt][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][jj], 0, 0, 0);
+                    for (int w = 1; w < kWaves; ++w) t = t + red[(w * kProdTiles + jj) * 64 + lane];
+                    store_f4_coherent(rs_own, ((mt * JT + jg + jj) * 64 + lane) * 16, t);
                 }
-            }
-        }
-        // the waves add their tiles in the order 0, 1, 2, 3 through LDS
-        for (int w = 0; w < kWaves; ++w) {
-            if (wave == w) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                    for (int jj = 0; jj < kProdTiles; ++jj)
-                        if (jg + jj < JT) {
-                            f32x4_t *slot = red + (mt * JT + jg + jj) * 64 + lane;
-                            if (w > 0) acc[mt][jj] = *slot + acc[mt][jj];
-                            *slot = acc[mt][jj];
-                        }
             }
             __syncthreads();
         }
     }
-    // wave 0 publishes the workgroup's sum
-    const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
-    if (wave == 0) {
-        const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + p * tile_floats);
-        for (int i = 0; i < MT * JT; ++i) store_f4_coherent(rs, (i * 64 + lane) * 16, red[i * 64 + lane]);
-        wait_vm();
-    }
+    if (wave == 0) wait_vm();
     __shared__ uint32_t s_last;
     __syncthreads();
     if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
     __syncthreads();
     if (MT == 1 || !s_last) return;  // m <= 16: the consumers sum the partials
-    // 16 < m: the last producer sums the partials in producer order into t [m, r]
-    if (wave == 0) {
-        for (int i = 0; i < MT * JT; ++i) {
-            f32x4_t s = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t q = 0; q < d.p.producers; ++q) {
-                const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.tpart() + q * tile_floats);
-                s = s + load_f4_coherent(rs, (i * 64 + lane) * 16);
-            }
-            const int mt = i / JT, jt = i - mt * JT;
-            const int64_t j = 16 * jt + lr;
+    // 16 < m: the last producer sums the partials in producer order into t [m, r];
+    // tile i goes to wave i % 4, kBatch producers in flight
+    for (int i = wave; i < MT * JT; i += kWaves) {
+        f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t q0 = 0; q0 < d.p.producers; q0 += kBatch) {
+            f32x4_t v[kBatch];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = 16 * mt + 4 * lq + v;
-                if (m < a.m && j < a.r) d.t32()[m * a.r + j] = s[v];
+            for (int u = 0; u < kBatch; ++u) {
+                const int64_t q = q0 + u < d.p.producers ? q0 + u : d.p.producers - 1;
+                v[u] = load_f4_coherent(coherent_rsrc(d.tpart() + q * tile_floats), (i * 64 + lane) * 16);
             }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (q0 + u < d.p.producers) sum = sum + v[u];
+        }
+        const int mt = i / JT, jt = i - mt * JT;
+        const int64_t j = 16 * jt + lr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = 16 * mt + 4 * lq + v;
+            if (m < a.m && j < a.r) d.t32()[m * a.r + j] = sum[v];
         }
     }
     if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);
@@ -422,7 +416,6 @@ __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, in
 
 // Copy `total` items from global to LDS, kBatch per thread in flight: a plain
 // loop would wait for every load before issuing the next.
-constexpr int kBatch = 8;
 template <typename T, typename Src, typename Dst>
 __device__ __forceinline__ void batched_copy(int64_t total, Src src, Dst dst) {
     for (int64_t base = threadIdx.x; base < total; base += kBatch * kThreadsD) {
@@ -488,33 +481,32 @@ __device__ void stage_scales(const GemmArgs &a, uint8_t *sc, int64_t pitch, int6
 // One chunk: x fragments from the LDS window, weights from registers.
 // sc_off[g]: LDS byte offset of this lane's scale pair for row group g at the
 // unit's first chunk; cl: chunk index within the unit; col: x column of the
-// chunk within the window.
+// chunk within the window.  The x fragments of the chunk are read once and
+// reused over the row groups; each row group's weights are decoded just
+// before use, which bounds the registers of the larger tiles.
 template <int MT, int NW>
 __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *sc, const int (&sc_off)[NW],
                                           int64_t cl, const uint16_t *xb, int64_t pitch, int64_t col, int m_last,
                                           int lr, int lq, f32x4_t (&acc)[MT][NW]) {
-    float sv[NW][2];
+    bf16x8_t xa[4][MT];
 #pragma unroll
-    for (int g = 0; g < NW; ++g) {
-        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sc + sc_off[g] + cl * 8);
-        sv[g][0] = QERL_E4M3_F32(s2, 0);
-        sv[g][1] = QERL_E4M3_F32(s2, 1);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        bf16x8_t xa[MT];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             const int m = 16 * mt + lr < m_last ? 16 * mt + lr : m_last;
-            xa[mt] = *reinterpret_cast<const bf16x8_t *>(xb + (m * pitch + col + 32 * lq + 8 * j));
+            xa[j][mt] = *reinterpret_cast<const bf16x8_t *>(xb + (m * pitch + col + 32 * lq + 8 * j));
         }
 #pragma unroll
-        for (int g = 0; g < NW; ++g) {
+    for (int g = 0; g < NW; ++g) {
+        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sc + sc_off[g] + cl * 8);
+        const float sv0 = QERL_E4M3_F32(s2, 0), sv1 = QERL_E4M3_F32(s2, 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
             const uint32_t q = j == 0 ? w[g].x : j == 1 ? w[g].y : j == 2 ? w[g].z : w[g].w;
-            const bf16x8_t b = dequant8_d(q, sv[g][j >> 1]);
+            const bf16x8_t b = dequant8_d(q, j < 2 ? sv0 : sv1);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[mt], b, acc[mt][g], 0, 0, 0);
+                acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][mt], b, acc[mt][g], 0, 0, 0);
         }
     }
 }
