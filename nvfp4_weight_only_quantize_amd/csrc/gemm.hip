@@ -14,9 +14,10 @@
 //   prologue_kernel  t = x A^T in FP32, pre-multiplied by lora_scale / s_t and
 //                    split into BF16 hi + lo halves, so that the LoRA product
 //                    becomes 2r extra K columns of the same MFMA accumulation.
-//   tiled_kernel     64x64 output tiles, x and dequantized weight tiles
-//                    (e2m1 * e4m3 is exact in BF16) staged in LDS, BF16 MFMA
-//                    16x16x32 with FP32 accumulation; s_t applied once.
+//   prefill_kernel   256 x 128 output tiles, x and dequantized weight tiles
+//                    (e2m1 * e4m3 is exact in BF16) double-buffered in LDS,
+//                    BF16 MFMA 16x16x32 with FP32 accumulation; s_t applied
+//                    once.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -103,46 +104,20 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path
+// MFMA path (m > 64)
 // ---------------------------------------------------------------------------
-constexpr int BM = 64, BN = 64, BK = 32, LDS_PITCH = BK + 8;  // pitch in BF16 elements
+// Workgroup tile 256 (rows of x) x 128 (weight rows), K in steps of 32; four
+// waves, each a 128 x 64 sub-tile (8 x 4 MFMA 16x16x32 tiles, 128 FP32
+// accumulators per lane).  x and dequantized weight tiles are double-buffered
+// in LDS; the global loads of step s+1 are in flight while step s multiplies.
+// The LoRA product rides along as 2r extra K columns (t hi/lo x B twice).
+constexpr int PBM = 256, PBN = 128, PBK = 32, PPITCH = PBK + 8;  // LDS row pitch in BF16 elements
+constexpr int PA_STAGE = PBM * PPITCH, PB_STAGE = PBN * PPITCH;  // elements per LDS stage
 
-// Fill one 8-element (16-byte) piece of the weight tile: row n, columns
-// [kk, kk + 8) of the main range (dequantized e2m1 * e4m3, exact in BF16) or
-// of the LoRA range (B[n, j] for j = kk mod r, which pairs with the hi and lo
-// halves of the scaled t).
-__device__ __forceinline__ uint4 load_w_piece(const GemmArgs &a, int64_t n, int64_t kk, int64_t klora) {
-    uint4 o = make_uint4(0, 0, 0, 0);
-    if (n >= a.n) return o;
-    if (kk < a.k) {
-        const uint32_t q = *reinterpret_cast<const uint32_t *>(a.packed + n * (a.k >> 1) + (kk >> 1));
-        const float sc = QERL_E4M3_F32(a.scales[n * (a.k >> 4) + (kk >> 4)], 0);
-        const f32x2_t f0 = QERL_FP4_PAIR_F32(q, 0), f1 = QERL_FP4_PAIR_F32(q, 1);
-        const f32x2_t f2 = QERL_FP4_PAIR_F32(q, 2), f3 = QERL_FP4_PAIR_F32(q, 3);
-        o.x = pack_bf16x2(f0.x * sc, f0.y * sc);
-        o.y = pack_bf16x2(f1.x * sc, f1.y * sc);
-        o.z = pack_bf16x2(f2.x * sc, f2.y * sc);
-        o.w = pack_bf16x2(f3.x * sc, f3.y * sc);
-        return o;
-    }
-    const int64_t j0 = kk - a.k;  // column inside the LoRA range [0, 2r)
-    if (j0 >= klora) return o;
-    uint16_t e[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t j = j0 + i;
-        e[i] = j < klora ? a.lora_b[n * a.r + (j < a.r ? j : j - a.r)] : (uint16_t)0;
-    }
-    o.x = e[0] | ((uint32_t)e[1] << 16);
-    o.y = e[2] | ((uint32_t)e[3] << 16);
-    o.z = e[4] | ((uint32_t)e[5] << 16);
-    o.w = e[6] | ((uint32_t)e[7] << 16);
-    return o;
-}
-
-// 8 activations of row m at column kk (main range from x, LoRA range from the
-// split t in the workspace, row stride 2r).
-__device__ __forceinline__ uint4 load_x_piece(const Gemm &g, int64_t m, int64_t kk, int64_t klora) {
+// 8 elements of the extended K range [0, k + 2r) for x row m at column kk:
+// x itself, then the BF16 hi/lo halves of t * lora_scale / s_t; zero past
+// the end and for rows past m.
+__device__ __forceinline__ uint4 x_piece_ext(const Gemm &g, int64_t m, int64_t kk, int64_t klora) {
     const GemmArgs &a = g.a;
     uint4 o = make_uint4(0, 0, 0, 0);
     if (m >= a.m) return o;
@@ -153,59 +128,165 @@ __device__ __forceinline__ uint4 load_x_piece(const Gemm &g, int64_t m, int64_t 
     uint16_t e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) e[i] = (j0 + i < klora) ? t16[j0 + i] : (uint16_t)0;
-    o.x = e[0] | ((uint32_t)e[1] << 16);
-    o.y = e[2] | ((uint32_t)e[3] << 16);
-    o.z = e[4] | ((uint32_t)e[5] << 16);
-    o.w = e[6] | ((uint32_t)e[7] << 16);
+    __builtin_memcpy(&o, e, 16);
     return o;
 }
 
-__global__ __launch_bounds__(kThreads) void tiled_kernel(Gemm g) {
+// 16 weights of row n at columns [kk, kk + 16) of the extended K range:
+// dequantized NVFP4 (exact in BF16), then B [n, j] for j = column - k mod r;
+// zero past the end and for rows past n.
+__device__ __forceinline__ void w_piece_ext(const GemmArgs &a, int64_t n, int64_t kk, int64_t klora, uint4 &lo,
+                                            uint4 &hi) {
+    lo = hi = make_uint4(0, 0, 0, 0);
+    if (n >= a.n) return;
+    if (kk < a.k) {  // k % 16 == 0: a 16-element block is inside or outside
+        const uint2 q = *reinterpret_cast<const uint2 *>(a.packed + n * (a.k >> 1) + (kk >> 1));
+        const float sc = QERL_E4M3_F32(a.scales[n * (a.k >> 4) + (kk >> 4)], 0);
+        const f32x2_t f0 = QERL_FP4_PAIR_F32(q.x, 0), f1 = QERL_FP4_PAIR_F32(q.x, 1);
+        const f32x2_t f2 = QERL_FP4_PAIR_F32(q.x, 2), f3 = QERL_FP4_PAIR_F32(q.x, 3);
+        const f32x2_t f4 = QERL_FP4_PAIR_F32(q.y, 0), f5 = QERL_FP4_PAIR_F32(q.y, 1);
+        const f32x2_t f6 = QERL_FP4_PAIR_F32(q.y, 2), f7 = QERL_FP4_PAIR_F32(q.y, 3);
+        lo = make_uint4(pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
+                        pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc));
+        hi = make_uint4(pack_bf16x2(f4.x * sc, f4.y * sc), pack_bf16x2(f5.x * sc, f5.y * sc),
+                        pack_bf16x2(f6.x * sc, f6.y * sc), pack_bf16x2(f7.x * sc, f7.y * sc));
+        return;
+    }
+    const int64_t j0 = kk - a.k;
+    uint16_t e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int64_t j = j0 + i;
+        e[i] = j < klora ? a.lora_b[n * a.r + (j < a.r ? j : j - a.r)] : (uint16_t)0;
+    }
+    __builtin_memcpy(&lo, e, 16);
+    __builtin_memcpy(&hi, e + 8, 16);
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
     const GemmArgs &a = g.a;
-    __shared__ __attribute__((aligned(16))) uint16_t sx[BM * LDS_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t sw[BN * LDS_PITCH];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int64_t tiles_n = (a.n + BN - 1) / BN;
-    const int64_t tile = blockIdx.x;
-    const int64_t m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    extern __shared__ __attribute__((aligned(16))) uint16_t plds[];
+    uint16_t *sa = plds;                   // [2][PBM][PPITCH]
+    uint16_t *sb = plds + 2 * PA_STAGE;    // [2][PBN][PPITCH]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
+    // contiguous range of tiles (n fastest), so the workgroups sharing an x
+    // row block also share that XCD's L2
+    const int64_t tiles_n = (a.n + PBN - 1) / PBN, tiles = tiles_n * ((a.m + PBM - 1) / PBM);
+    const int64_t b = blockIdx.x, x8 = b % 8, q8 = tiles / 8, r8 = tiles % 8;
+    const int64_t tile = x8 * q8 + (x8 < r8 ? x8 : r8) + b / 8;
+    const int64_t m0 = (tile / tiles_n) * PBM, n0 = (tile % tiles_n) * PBN;
+    const int wm = wave >> 1, wn = wave & 1;
     const int64_t klora = 2 * (int64_t)a.r;
     const int64_t ktot = a.k + klora;
-    f32x4_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t steps = (ktot + PBK - 1) / PBK;
+    const bool fast_k = (a.k & 31) == 0;
 
-    const int lr = tid >> 2, lc = (tid & 3) * 8;  // loader: row and 8-column piece
-    for (int64_t k0 = 0; k0 < ktot; k0 += BK) {
-        *reinterpret_cast<uint4 *>(&sx[lr * LDS_PITCH + lc]) = load_x_piece(g, m0 + lr, k0 + lc, klora);
-        *reinterpret_cast<uint4 *>(&sw[lr * LDS_PITCH + lc]) = load_w_piece(a, n0 + lr, k0 + lc, klora);
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // this thread's loads: x rows tid/4 + 64u, 8-column piece tid % 4; weight
+    // row tid / 2, 16-column half tid % 2
+    const int xr = tid >> 2, xc = (tid & 3) * 8;
+    const int wr = tid >> 1, wc = (tid & 1) * 16;
+    const int64_t wn_row = n0 + wr < a.n ? n0 + wr : a.n - 1;
+    // x rows past m are clamped (their outputs are discarded); named
+    // registers, not arrays (an array here ends up in scratch memory)
+    auto xrow = [&](int u) {
+        const int64_t m = m0 + xr + 64 * u < a.m ? m0 + xr + 64 * u : a.m - 1;
+        return a.x + m * a.ldx + xc;
+    };
+    const uint16_t *xr0 = xrow(0), *xr1 = xrow(1), *xr2 = xrow(2), *xr3 = xrow(3);
+    const uint8_t *wq_row = a.packed + wn_row * (a.k >> 1) + (wc >> 1);
+    const uint8_t *ws_row = a.scales + wn_row * (a.k >> 4) + (wc >> 4);
+
+    // compute one K step from LDS buffer buf
+    auto mma_step = [&](int buf) {
+        const uint16_t *pa = sa + buf * PA_STAGE + (wm * 128 + lr) * PPITCH + 8 * lq;
+        const uint16_t *pb = sb + buf * PB_STAGE + (wn * 64 + lr) * PPITCH + 8 * lq;
+        bf16x8_t bf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const bf16x8_t *>(pb + 16 * j * PPITCH);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(pa + 16 * i * PPITCH);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // ---- the main K range in full 32-column steps (k % 32 == 0): plain
+    // vector loads of step s+1 in flight while step s multiplies ----
+    const int64_t fast_steps = fast_k ? a.k / PBK : 0;
+    uint4 xp0, xp1, xp2, xp3;
+    uint2 wq;
+    uint32_t wsb;
+    auto issue = [&](int64_t s) {
+        const int64_t k0 = s * PBK;
+        xp0 = *reinterpret_cast<const uint4 *>(xr0 + k0);
+        xp1 = *reinterpret_cast<const uint4 *>(xr1 + k0);
+        xp2 = *reinterpret_cast<const uint4 *>(xr2 + k0);
+        xp3 = *reinterpret_cast<const uint4 *>(xr3 + k0);
+        wq = *reinterpret_cast<const uint2 *>(wq_row + (k0 >> 1));
+        wsb = ws_row[k0 >> 4];
+    };
+    auto commit = [&](int buf) {
+        uint16_t *pa = sa + buf * PA_STAGE + xr * PPITCH + xc, *pb = sb + buf * PB_STAGE;
+        *reinterpret_cast<uint4 *>(pa) = xp0;
+        *reinterpret_cast<uint4 *>(pa + 64 * PPITCH) = xp1;
+        *reinterpret_cast<uint4 *>(pa + 128 * PPITCH) = xp2;
+        *reinterpret_cast<uint4 *>(pa + 192 * PPITCH) = xp3;
+        const float sc = QERL_E4M3_F32(wsb, 0);
+        const f32x2_t f0 = QERL_FP4_PAIR_F32(wq.x, 0), f1 = QERL_FP4_PAIR_F32(wq.x, 1);
+        const f32x2_t f2 = QERL_FP4_PAIR_F32(wq.x, 2), f3 = QERL_FP4_PAIR_F32(wq.x, 3);
+        const f32x2_t f4 = QERL_FP4_PAIR_F32(wq.y, 0), f5 = QERL_FP4_PAIR_F32(wq.y, 1);
+        const f32x2_t f6 = QERL_FP4_PAIR_F32(wq.y, 2), f7 = QERL_FP4_PAIR_F32(wq.y, 3);
+        *reinterpret_cast<uint4 *>(pb + wr * PPITCH + wc) =
+            make_uint4(pack_bf16x2(f0.x * sc, f0.y * sc), pack_bf16x2(f1.x * sc, f1.y * sc),
+                       pack_bf16x2(f2.x * sc, f2.y * sc), pack_bf16x2(f3.x * sc, f3.y * sc));
+        *reinterpret_cast<uint4 *>(pb + wr * PPITCH + wc + 8) =
+            make_uint4(pack_bf16x2(f4.x * sc, f4.y * sc), pack_bf16x2(f5.x * sc, f5.y * sc),
+                       pack_bf16x2(f6.x * sc, f6.y * sc), pack_bf16x2(f7.x * sc, f7.y * sc));
+    };
+    if (fast_steps > 0) {
+        issue(0);
+        commit(0);
         __syncthreads();
-        bf16x8_t af[2], bfr[2];
+        for (int64_t s = 0; s < fast_steps; ++s) {
+            const int buf = (int)(s & 1);
+            if (s + 1 < fast_steps) issue(s + 1);  // uniform
+            mma_step(buf);
+            if (s + 1 < fast_steps) commit(buf ^ 1);
+            __syncthreads();
+        }
+    }
+    // ---- the rest: a partial last K step and the LoRA columns, one buffer ----
+    for (int64_t s = fast_steps; s < steps; ++s) {
+        const int64_t k0 = s * PBK;
+        uint4 lo, hi;
+        w_piece_ext(a, n0 + wr, k0 + wc, klora, lo, hi);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            af[i] = *reinterpret_cast<const bf16x8_t *>(&sx[(wm + 16 * i + (lane & 15)) * LDS_PITCH + 8 * (lane >> 4)]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            bfr[j] = *reinterpret_cast<const bf16x8_t *>(&sw[(wn + 16 * j + (lane & 15)) * LDS_PITCH + 8 * (lane >> 4)]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<uint4 *>(sa + (xr + 64 * u) * PPITCH + xc) = x_piece_ext(g, m0 + xr + 64 * u, k0 + xc, klora);
+        *reinterpret_cast<uint4 *>(sb + wr * PPITCH + wc) = lo;
+        *reinterpret_cast<uint4 *>(sb + wr * PPITCH + wc + 8) = hi;
+        __syncthreads();
+        mma_step(0);
         __syncthreads();
     }
-    const float st = *a.tensor_scale;
+    const float st_scale = *a.tensor_scale;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int64_t m = m0 + wm + 16 * i + 4 * (lane >> 4) + v;
-                const int64_t n = n0 + wn + 16 * j + (lane & 15);
-                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[i][j][v]);
+                const int64_t m = m0 + wm * 128 + 16 * i + 4 * lq + v;
+                const int64_t n = n0 + wn * 64 + 16 * j + lr;
+                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st_scale * acc[i][j][v]);
             }
 }
 
@@ -226,9 +307,13 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t tiles = ((a.n + BN - 1) / BN) * ((a.m + BM - 1) / BM);
+    const int64_t tiles = ((a.n + PBN - 1) / PBN) * ((a.m + PBM - 1) / PBM);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(tiled_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
+    const size_t lds = (size_t)(2 * PA_STAGE + 2 * PB_STAGE) * 2;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(prefill_kernel),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)tiles), dim3(256), lds, stream, g);
     return hipGetLastError();
 }
 
