@@ -144,7 +144,6 @@ struct Decode {
 };
 
 // ---- device-coherent access: agent scope, no cache write-back or invalidate ----
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kSc1 = 16;  // cache-policy bit: coherent at device scope
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base) {
