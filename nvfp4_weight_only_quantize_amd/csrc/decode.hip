@@ -39,6 +39,7 @@
 // Counters live in the first kGemmCtrBytes of the workspace: they must be zero
 // before the first call, and every call leaves them zero.
 #include "device_common.h"
+#include "mfma_tile.h"
 #include "qerl_internal.h"
 
 namespace qerl {
@@ -50,7 +51,6 @@ constexpr int64_t kChunkK = 128;          // K elements per chunk
 constexpr int kXPad = 8;                  // BF16 padding per staged x row
 constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
 constexpr int64_t kXBudget = 36 * 1024;   // LDS for a unit's x slice (m <= 16)
-constexpr int kXPieces = (int)(kXBudget / 16 / 256);  // 16-byte x pieces per thread when staging it
 constexpr int64_t kLdsLimit = 63 * 1024;
 constexpr int64_t kProdChunks = 4;        // K chunks per LoRA producer
 constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
@@ -79,56 +79,62 @@ __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(in
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-    p.nw = p.mt;
-    const int64_t win = 4 / p.mt;  // chunks per x window (16 KB of LDS at m = 16 mt)
+    p.nw = p.mt == 1 ? 1 : 4;  // 16 < m: MFMA units of 256 weight rows
     p.rows_per_unit = 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
     if (p.row_blocks > kMaxRowBlocks) p.row_blocks = 0;  // one counter per row block: rejected at launch
     p.chunks = (k + kChunkK - 1) / kChunkK;
     p.full_chunks = k / kChunkK;
-    // x window (16 < m): 8-element pieces per thread
-    const int64_t px = (m * win * kChunkK / 8 + kThreadsD - 1) / kThreadsD;
-    p.px = px <= 1 ? 1 : (px <= 2 ? 2 : 4);
+    p.px = 1;
+    p.jt = (r + 15) / 16;
+    p.rp = (r + 31) / 32 * 32;
+    p.producers = r > 0 ? (p.chunks + kProdChunks - 1) / kProdChunks : 0;
     // slices: cover the chip, keep the FP32 partials below the weight bytes
-    // and the staged scales within their LDS budget
     int64_t s = p.row_blocks > 0 ? (kTargetUnits + p.row_blocks - 1) / p.row_blocks : 1;
     int64_t s_cap = (k * 9) / (64 * m);
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
     if (s < 1) s = 1;
+    const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
+    if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
+        p.cps = (p.chunks + s - 1) / s;
+        p.slices = (p.chunks + p.cps - 1) / p.cps;
+        p.units = p.row_blocks * p.slices;
+        p.part_off = kGemmCtrBytes;
+        p.tpart_off = align256(p.part_off + p.units * tile);
+        p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
+        p.bytes = align256(p.t_off + m * (int64_t)r * 4);
+        return p;
+    }
+    // m <= 16: stream_kernel, the unit's x slice and scales resident in LDS
+    const int64_t win = 4;  // chunks per slice are a multiple of this
     int64_t cps = (p.chunks + s - 1) / s;
     cps = (cps + win - 1) / win * win;
     int64_t cps_max = kScBudget * 16 / (p.rows_per_unit * kChunkK) / win * win;
-    if (p.mt == 1) {  // the unit's whole x slice stays in LDS
-        const int64_t x_max = (kXBudget / (2 * m) - kXPad) / kChunkK / win * win;
-        if (cps_max > x_max) cps_max = x_max;
-    }
+    const int64_t x_max = (kXBudget / (2 * m) - kXPad) / kChunkK / win * win;
+    if (cps_max > x_max) cps_max = x_max;
     if (cps > cps_max) cps = cps_max;
     if (cps < win) cps = win;
     p.cps = cps;
     p.slices = (p.chunks + cps - 1) / cps;
     p.units = p.row_blocks * p.slices;
-    p.jt = (r + 15) / 16;
-    p.rp = (r + 31) / 32 * 32;
-    p.producers = r > 0 ? (p.chunks + kProdChunks - 1) / kProdChunks : 0;
-    // LDS: x double buffer, then the scales (rows an odd multiple of 16 bytes
+    // LDS: the x slice, then the scales (rows an odd multiple of 16 bytes
     // apart, so the 16 rows a wave reads fall in distinct banks)
-    p.xpitch = (p.mt == 1 ? cps : win) * kChunkK + kXPad;
-    const int64_t x_bytes = (p.mt == 1 ? 1 : 2) * m * p.xpitch * 2;
+    p.xpitch = cps * kChunkK + kXPad;
+    const int64_t x_bytes = m * p.xpitch * 2;
     int64_t scp = (cps * 8 + 15) / 16;
     if (scp % 2 == 0) ++scp;
     p.sc_pitch = scp * 16;
     p.sc_lds_off = (x_bytes + 15) / 16 * 16;
     int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
-    const int64_t epi = p.mt == 1 ? 16 * p.rp * 2 * 2 : 0;  // t hi/lo in the one-launch epilogue
+    const int64_t epi = 16 * p.rp * 2 * 2;  // t hi/lo in the one-launch epilogue
     const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16;  // producer wave reduction
     if (lds < epi) lds = epi;
     if (lds < prod) lds = prod;
     p.lds_bytes = lds;
     // workspace after the counters: partial tiles, producer partials, t
-    const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     p.part_off = kGemmCtrBytes;
-    p.tpart_off = align256(p.part_off + (p.slices > 1 || p.mt > 1 ? p.units * tile : 0));
+    p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
     p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
     p.bytes = align256(p.t_off + m * (int64_t)r * 4);
     return p;
@@ -345,74 +351,6 @@ __device__ __forceinline__ void load_chunk_tail(const GemmArgs &a, int64_t n0, i
     }
 }
 
-// x window: rows [0, m) x columns [k0, k0 + 128 W) as 8-element pieces;
-// thread t takes pieces t, t + 256, ...  Addresses are clamped into x, so every
-// load is unconditional; columns at or past k hold don't-care values, which
-// are only ever multiplied into chunks that are not computed.  Pieces past the
-// last row are loaded from the last row (same columns) and written there too:
-// the same bytes twice, and no branch for the compiler to sink the load into.
-// (Up to four pieces per thread, kept in named registers: an array here ends
-// up in scratch memory.)
-template <int W>
-__device__ __forceinline__ void x_piece(const GemmArgs &a, int i, int64_t &m, int64_t &col) {
-    constexpr int64_t per_row = W * kChunkK / 8;
-    const int64_t piece = threadIdx.x + (int64_t)i * kThreadsD;
-    m = piece / per_row;
-    col = (piece - m * per_row) * 8;
-    m = m < a.m ? m : a.m - 1;
-}
-template <int W>
-__device__ __forceinline__ uint4 load_x_piece(const GemmArgs &a, int64_t k0, int i) {
-    int64_t m, col;
-    x_piece<W>(a, i, m, col);
-    const int64_t kk = k0 + col < a.k ? k0 + col : a.k - 8;
-    return *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + kk);
-}
-template <int W>
-__device__ __forceinline__ void store_x_piece(const GemmArgs &a, uint16_t *buf, int64_t pitch, int i, const uint4 &v) {
-    int64_t m, col;
-    x_piece<W>(a, i, m, col);
-    *reinterpret_cast<uint4 *>(buf + m * pitch + col) = v;
-}
-struct XWin {
-    uint4 p0, p1, p2, p3;
-};
-template <int PX, int W>
-__device__ __forceinline__ void load_x_window(const GemmArgs &a, int64_t k0, XWin &v) {
-    v.p0 = load_x_piece<W>(a, k0, 0);
-    if (PX > 1) v.p1 = load_x_piece<W>(a, k0, 1);
-    if (PX > 2) v.p2 = load_x_piece<W>(a, k0, 2);
-    if (PX > 3) v.p3 = load_x_piece<W>(a, k0, 3);
-}
-template <int PX, int W>
-__device__ __forceinline__ void store_x_window(const GemmArgs &a, uint16_t *buf, int64_t pitch, const XWin &v) {
-    store_x_piece<W>(a, buf, pitch, 0, v.p0);
-    if (PX > 1) store_x_piece<W>(a, buf, pitch, 1, v.p1);
-    if (PX > 2) store_x_piece<W>(a, buf, pitch, 2, v.p2);
-    if (PX > 3) store_x_piece<W>(a, buf, pitch, 3, v.p3);
-}
-
-// m <= 16: the unit's x slice, rows [0, m) x columns [k0, k0 + width), into
-// LDS rows of `pitch` elements; columns at or past k are zero.  All loads of a
-// thread are issued before the first LDS write.
-__device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
-    const int64_t per_row = width / 8, total = a.m * per_row;  // total <= kXPieces * kThreadsD
-    uint4 v[kXPieces];
-#pragma unroll
-    for (int u = 0; u < kXPieces; ++u) {
-        const int64_t i = threadIdx.x + (int64_t)u * kThreadsD;
-        const int64_t m = i / per_row, col = (i - m * per_row) * 8;
-        v[u] = make_uint4(0, 0, 0, 0);
-        if (i < total && k0 + col < a.k) v[u] = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
-    }
-#pragma unroll
-    for (int u = 0; u < kXPieces; ++u) {
-        const int64_t i = threadIdx.x + (int64_t)u * kThreadsD;
-        const int64_t m = i / per_row, col = (i - m * per_row) * 8;
-        if (i < total) *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v[u];
-    }
-}
-
 // Copy `total` items from global to LDS, kBatch per thread in flight: a plain
 // loop would wait for every load before issuing the next.
 template <typename T, typename Src, typename Dst>
@@ -430,6 +368,23 @@ __device__ __forceinline__ void batched_copy(int64_t total, Src src, Dst dst) {
             if (i < total) dst(i, v[u]);
         }
     }
+}
+
+// The unit's x slice, rows [0, m) x columns [k0, k0 + width), into LDS rows
+// of `pitch` elements; columns at or past k are zero.
+__device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
+    const int64_t per_row = width / 8;
+    batched_copy<uint4>(
+        a.m * per_row,
+        [&](int64_t i) {
+            const int64_t m = i / per_row, col = (i - m * per_row) * 8;
+            return k0 + col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col)
+                                  : make_uint4(0, 0, 0, 0);
+        },
+        [&](int64_t i, const uint4 &v) {
+            const int64_t m = i / per_row, col = (i - m * per_row) * 8;
+            *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v;
+        });
 }
 
 // Stage the unit's scale bytes: rows [n0, n0 + R) x bytes [b0, b0 + nb) of
@@ -510,54 +465,9 @@ __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *s
     }
 }
 
-// Per-unit state of the streaming loop.
-template <int NW>
-struct Unit {
-    const GemmArgs *a;
-    uint16_t *xs;     // x double buffer in LDS
-    const uint8_t *sc;  // staged scales in LDS
-    int64_t xbuf, pitch;
-    int64_t c_begin, c_full_end, c_last, n0;
-    int m_last, lr, lq;
-    int sc_off[NW];
-};
-
-// One x window of W chunks.  The weight ring holds D chunks (D/W windows);
-// RELOAD: refill each consumed slot with the chunk D ahead (the window is
-// full); NEXTX: load the next window's x now and stage it at the end.  Issue
-// order is kept by scheduling barriers: the next window's x first, then each
-// chunk's refill right after the chunk is consumed.
-template <int MT, int NW, int PX, bool K32, int W, int D, int SG, bool RELOAD, bool NEXTX>
-__device__ __forceinline__ void run_window(const Unit<NW> &t, int64_t wi, uint4 (&w)[D][NW], XWin &xv,
-                                           f32x4_t (&acc)[MT][NW]) {
-    const GemmArgs &a = *t.a;
-    const int64_t cw = t.c_begin + wi * W;
-    if (NEXTX) {
-        load_x_window<PX, W>(a, (cw + W) * kChunkK, xv);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    const uint16_t *xb = t.xs + (wi & 1) * t.xbuf;
-#pragma unroll
-    for (int s = 0; s < W; ++s) {
-        const int64_t c = cw + s;
-        if (RELOAD || c < t.c_full_end)  // uniform; only the compute is guarded
-            mma_chunk<MT, NW>(w[SG * W + s], t.sc, t.sc_off, c - t.c_begin, xb, t.pitch, s * kChunkK, t.m_last, t.lr,
-                              t.lq, acc);
-        if (RELOAD) {
-            load_chunk<NW, K32>(a, t.n0, c + D < t.c_last ? c + D : t.c_last, t.lr, t.lq, w[SG * W + s]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    if (NEXTX) {
-        store_x_window<PX, W>(a, t.xs + ((wi + 1) & 1) * t.xbuf, t.pitch, xv);
-        __syncthreads();
-    }
-}
-
 template <int MT, int NW, int PX, bool K32>
 __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
-    constexpr int W = 4 / MT;         // chunks per x window
-    constexpr int D = W < 2 ? 2 : W;  // chunks in the weight ring (D * NW 16-byte loads per lane)
+    static_assert(MT == 1 && NW == 1, "m <= 16 only; 16 < m runs mfma_unit_kernel");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
@@ -567,7 +477,6 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
     uint8_t *sc = lds + p.sc_lds_off;
-    const int64_t xbuf = a.m * p.xpitch;  // elements per x buffer
     const int64_t u = blockIdx.x - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
     const int64_t c_begin = slice * p.cps;
@@ -592,138 +501,55 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     const int64_t c_last = c_full_end - 1;  // the unit's last full chunk (< c_begin: none)
     const int64_t sb0 = c_begin * 8;
     const int64_t sb1 = c_end * 8 < (a.k >> 4) ? c_end * 8 : (a.k >> 4);
-    if constexpr (MT == 1) {
-        // ---- m <= 16: x and scales of the whole unit resident in LDS; the
-        // weights stream through a ring of D chunks with no barrier ----
-        constexpr int DR = 4;
-        uint4 w[DR][NW];
-        if (c_full_end > c_begin) {
-#pragma unroll
-            for (int s = 0; s < DR; ++s)
-                load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
-        }
-        stage_x_slice(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
-        stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
-        if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
-            const int64_t z0 = (a.k >> 4) - sb0, zn = p.full_chunks * 8 + 8 - (a.k >> 4);
-            for (int64_t i = tid; i < R * zn; i += kThreadsD) sc[(i / zn) * p.sc_pitch + z0 + i % zn] = 0;
-        }
-        __syncthreads();
-        int64_t c = c_begin;
-        for (; c + 2 * DR <= c_full_end; c += DR) {
-#pragma unroll
-            for (int s = 0; s < DR; ++s) {
-                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                                  m_last, lr, lq, acc);
-                load_chunk<NW, K32>(a, n0, c + s + DR, lr, lq, w[s]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
-#pragma unroll
-            for (int s = 0; s < DR; ++s) {
-                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                                  m_last, lr, lq, acc);
-                load_chunk<NW, K32>(a, n0, c + s + DR < c_last ? c + s + DR : c_last, lr, lq, w[s]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            c += DR;
-        }
-#pragma unroll
-        for (int s = 0; s < DR; ++s)
-            if (c + s < c_full_end)  // uniform
-                mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                                  m_last, lr, lq, acc);
-        if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
-            uint4 wt[NW];
-            load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
-            mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
-                              m_last, lr, lq, acc);
-        }
-    } else {
-    // ---- 16 < m: prologue: the weight ring, x window 0, the unit's scales ----
-    uint4 w[D][NW];
+    // ---- x and scales of the whole unit resident in LDS; the weights
+    // stream through a ring of DR chunks with no barrier ----
+    constexpr int DR = 4;
+    uint4 w[DR][NW];
     if (c_full_end > c_begin) {
 #pragma unroll
-        for (int s = 0; s < D; ++s) load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
+        for (int s = 0; s < DR; ++s)
+            load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
     }
-    XWin xv;
-    load_x_window<PX, W>(a, c_begin * kChunkK, xv);
+    stage_x_slice(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
     stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
-    store_x_window<PX, W>(a, xs, p.xpitch, xv);
-    __syncthreads();
-
-    // ---- windows: the last RW = D/W of them no longer reload ----
-    Unit<NW> t;
-    t.a = &a;
-    t.xs = xs;
-    t.sc = sc;
-    t.xbuf = xbuf;
-    t.pitch = p.xpitch;
-    t.c_begin = c_begin;
-    t.c_full_end = c_full_end;
-    t.c_last = c_last;
-    t.n0 = n0;
-    t.m_last = m_last;
-    t.lr = lr;
-    t.lq = lq;
-#pragma unroll
-    for (int g = 0; g < NW; ++g) t.sc_off[g] = sc_off[g];
-    constexpr int RW = D / W;
-    const int64_t nwin = (c_full_end - c_begin + W - 1) / W;  // windows holding a full chunk
-    int64_t wi = 0;
-    for (; wi + 2 * RW <= nwin; wi += RW) {
-        run_window<MT, NW, PX, K32, W, D, 0, true, true>(t, wi, w, xv, acc);
-        if (RW == 2) run_window<MT, NW, PX, K32, W, D, 1, true, true>(t, wi + 1, w, xv, acc);
-    }
-    const int64_t rem = nwin - wi;  // RW <= rem < 2 RW, or nwin < RW
-    if (RW == 1) {
-        if (rem == 1) run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi, w, xv, acc);
-    } else if (rem == 3) {
-        run_window<MT, NW, PX, K32, W, D, 0, true, true>(t, wi, w, xv, acc);
-        run_window<MT, NW, PX, K32, W, D, 1, false, true>(t, wi + 1, w, xv, acc);
-        run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi + 2, w, xv, acc);
-    } else if (rem == 2) {
-        run_window<MT, NW, PX, K32, W, D, 0, false, true>(t, wi, w, xv, acc);
-        run_window<MT, NW, PX, K32, W, D, 1, false, false>(t, wi + 1, w, xv, acc);
-    } else if (rem == 1) {
-        run_window<MT, NW, PX, K32, W, D, 0, false, false>(t, wi, w, xv, acc);
-    }
-    // ---- the partial last chunk of K (k % 128 != 0) ----
-    if (c_end > c_full_end) {
-        uint16_t *xb = xs + (nwin & 1) * xbuf;  // not read by the last window
-        __syncthreads();
-        const int64_t k0 = p.full_chunks * kChunkK;
-        for (int64_t i = tid; i < a.m * (kChunkK / 8); i += kThreadsD) {
-            const int64_t m = i / (kChunkK / 8), col = (i % (kChunkK / 8)) * 8;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (k0 + col < a.k) v = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col);
-            *reinterpret_cast<uint4 *>(xb + m * p.xpitch + col) = v;
-        }
-        // scale bytes of the chunk past k: zero (the weights there are zero too)
+    if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
         const int64_t z0 = (a.k >> 4) - sb0, zn = p.full_chunks * 8 + 8 - (a.k >> 4);
         for (int64_t i = tid; i < R * zn; i += kThreadsD) sc[(i / zn) * p.sc_pitch + z0 + i % zn] = 0;
+    }
+    __syncthreads();
+    int64_t c = c_begin;
+    for (; c + 2 * DR <= c_full_end; c += DR) {
+#pragma unroll
+        for (int s = 0; s < DR; ++s) {
+            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                              m_last, lr, lq, acc);
+            load_chunk<NW, K32>(a, n0, c + s + DR, lr, lq, w[s]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
+#pragma unroll
+        for (int s = 0; s < DR; ++s) {
+            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                              m_last, lr, lq, acc);
+            load_chunk<NW, K32>(a, n0, c + s + DR < c_last ? c + s + DR : c_last, lr, lq, w[s]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        c += DR;
+    }
+#pragma unroll
+    for (int s = 0; s < DR; ++s)
+        if (c + s < c_full_end)  // uniform
+            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
+                              m_last, lr, lq, acc);
+    if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
         uint4 wt[NW];
         load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
-        __syncthreads();
-        mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xb, p.xpitch, 0, m_last, lr, lq, acc);
-    }
-
+        mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
+                          m_last, lr, lq, acc);
     }
     const int64_t tile_floats = R * 16 * MT;
     const int wave_off = wave * MT * NW * 64;  // f32x4 slots before this wave's in a tile
-    if (MT > 1) {
-        // 16 < m: every unit stores its tile; finish_kernel reduces after the
-        // kernel boundary
-        f32x4_t *tile = reinterpret_cast<f32x4_t *>(d.part() + u * tile_floats) + wave_off + lane;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int g = 0; g < NW; ++g)
-                if (16 * mt + 4 * lq < a.m) tile[(mt * NW + g) * 64] = acc[mt][g];
-        return;
-    }
-
     // ---- m <= 16, split K: the last unit of the row block to arrive sums the slices ----
     __shared__ uint32_t s_flag;
     if (p.slices > 1) {
@@ -925,26 +751,89 @@ __global__ __launch_bounds__(256) void finish_kernel(Decode d) {
     }
 }
 
-template <int MT, int NW, int PX, bool K32>
+// ---------------------------------------------------------------------------
+// 16 < m: MFMA units
+// ---------------------------------------------------------------------------
+// Unit u = (slice of K, block of 256 weight rows) runs the K loops of
+// mfma_tile.h over its chunks with all 16 MT rows of x as the x tile, and
+// stores its FP32 tile where finish_kernel<MT, 4> reads it (f32x4 slot
+// ((wave MT + i) 4 + j) 64 + lane for m-tile i, n-tile j).  Producers of t
+// lead the grid, as in stream_kernel.
+__shared__ __attribute__((aligned(1024))) uint8_t g_dxtile0[64 * kTileRowBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
+
+template <int MT>
+__global__ __launch_bounds__(kThreadsD, 2) void mfma_unit_kernel(Decode d) {
+    const GemmArgs &a = d.a;
+    const DecodePlan &p = d.p;
+    if ((int64_t)blockIdx.x < p.producers) {
+        lora_producer<MT>(d, blockIdx.x, g_dxtile0);
+        return;
+    }
+    const int64_t u = blockIdx.x - p.producers;
+    const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
+    const int64_t c_begin = slice * p.cps;
+    const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
+    const int64_t c_full_end = c_end < p.full_chunks ? c_end : p.full_chunks;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t n0 = rblk * 256, kb = a.k >> 1, ks = a.k >> 4;
+
+    f32x4_t acc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int64_t fast_end = a.ldx <= kTileMaxLdx ? c_full_end : c_begin;
+    mfma_kloop<MT>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k, c_begin, fast_end,
+                   g_dxtile0, g_dxtile1, acc);
+    // the rest of the slice (the partial last chunk of K, or all of it for
+    // very wide x rows)
+    const int64_t nw = n0 + wave * 64 + lr;
+    plain_kloop<MT>(
+        fast_end * kChunkK, c_end * kChunkK < a.k ? c_end * kChunkK : a.k, g_dxtile0,
+        [&](int row, int64_t kk) {
+            uint4 o = make_uint4(0, 0, 0, 0);
+            if (row < a.m && kk < a.k) o = *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + kk);
+            return o;
+        },
+        [&](int j, int64_t kk) {
+            const int64_t n = nw + 16 * j;
+            if (n < a.n && kk < a.k)  // k % 16 == 0: an 8-element piece is inside or outside
+                return dequant8_p(*reinterpret_cast<const uint32_t *>(a.packed + n * kb + (kk >> 1)),
+                                  QERL_E4M3_F32(a.scales[n * ks + (kk >> 4)], 0));
+            return as_bf16x8_d(make_uint4(0, 0, 0, 0));
+        },
+        acc);
+
+    f32x4_t *tile = reinterpret_cast<f32x4_t *>(d.part() + u * (256 * 16 * MT)) + wave * MT * 4 * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (16 * i + 4 * lq < a.m) tile[(i * 4 + j) * 64] = acc[i][j];
+}
+
+template <int MT>
+hipError_t launch_mfma_units(const Decode &d, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_unit_kernel<MT>, dim3((unsigned)(d.p.producers + d.p.units)), dim3(kThreadsD), 0, stream,
+                       d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));
+    hipLaunchKernelGGL((finish_kernel<MT, 4>), fgrid, dim3(256), 0, stream, d);
+    return hipGetLastError();
+}
+
+template <bool K32>
 hipError_t launch_stream(const Decode &d, hipStream_t stream) {
-    auto kern = stream_kernel<MT, NW, PX, K32>;
+    auto kern = stream_kernel<1, 1, 1, K32>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
     const int64_t grid = d.p.producers + d.p.units;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsD), (size_t)d.p.lds_bytes, stream, d);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || MT == 1) return e;
-    const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));
-    hipLaunchKernelGGL((finish_kernel<MT, NW>), fgrid, dim3(256), 0, stream, d);
     return hipGetLastError();
-}
-
-template <bool K32>
-hipError_t launch_stream_k(const Decode &d, hipStream_t stream) {
-    if (d.p.mt == 1) return launch_stream<1, 1, 1, K32>(d, stream);
-    if (d.p.mt == 2) return launch_stream<2, 2, 4, K32>(d, stream);
-    return launch_stream<4, 4, 4, K32>(d, stream);
 }
 
 }  // namespace
@@ -955,10 +844,13 @@ size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
 
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
     const Decode d{a, make_decode_plan(a.m, a.n, a.k, a.r)};
-    if (d.p.row_blocks < 1 || d.p.producers + d.p.units > 0x7FFFFFFF || d.p.lds_bytes > kLdsLimit ||
+    if (d.p.row_blocks < 1 || d.p.producers + d.p.units > 0x7FFFFFFF ||
+        d.p.lds_bytes > kLdsLimit ||
         d.p.rows_per_unit * 16 * d.p.mt * d.p.units * 4 > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    return (a.k & 31) == 0 ? launch_stream_k<true>(d, stream) : launch_stream_k<false>(d, stream);
+    if (d.p.mt == 2) return launch_mfma_units<2>(d, stream);
+    if (d.p.mt == 4) return launch_mfma_units<4>(d, stream);
+    return (a.k & 31) == 0 ? launch_stream<true>(d, stream) : launch_stream<false>(d, stream);
 }
 
 }  // namespace qerl

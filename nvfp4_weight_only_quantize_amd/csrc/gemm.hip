@@ -14,11 +14,12 @@
 //   prologue_kernel  t = x A^T in FP32, pre-multiplied by lora_scale / s_t and
 //                    split into BF16 hi + lo halves, so that the LoRA product
 //                    becomes 2r extra K columns of the same MFMA accumulation.
-//   prefill_kernel   256 x 128 output tiles, x tiles double-buffered in LDS,
-//                    weights decoded to exact BF16 (e2m1 * e4m3) in registers,
-//                    BF16 MFMA 16x16x32 with FP32 accumulation; s_t applied
-//                    once.
+//   prefill_kernel   128 x 256 output tiles over the K loops of mfma_tile.h
+//                    (x by LDS DMA, weights decoded to exact BF16 in
+//                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
+//                    s_t applied once.
 #include "device_common.h"
+#include "mfma_tile.h"
 #include "qerl_internal.h"
 
 namespace qerl {
@@ -106,28 +107,17 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
 // ---------------------------------------------------------------------------
 // MFMA path (m > 64)
 // ---------------------------------------------------------------------------
-// Workgroup tile 128 (rows of x) x 256 (weight rows); four waves side by
-// side along n, each the full 128 x 64 (8 x 4 MFMA 16x16x32 tiles), so no
-// weight fragment is fetched twice.  Each wave decodes its own weight
-// fragments straight from global memory into registers (e2m1 * e4m3 is exact
-// in BF16); x tiles go from global memory to LDS by DMA (buffer loads with
-// the LDS bit), double-buffered in two LDS arrays, and no register holds x in
-// flight.
-//
-// The main loop takes K in blocks of 128 and permutes K inside a block: the
-// sum over K does not depend on its order, so lane quarter q of both operands
-// takes the 32 columns 32q .. 32q+31 -- 16 packed bytes and two scale bytes,
-// one load each -- split over the block's four MFMA steps.  The loads of
-// block s+1 are in flight while block s multiplies.  What is left of K past
-// the last full block, and the LoRA product as 2r extra K columns (t hi/lo x
-// B twice), go through a plain loop of 32 columns a step.
-//
-// LDS x tile: 128 rows of 256 bytes, no padding; 16-byte chunk c of row r
-// holds global chunk c ^ (r % 16), so that the 16 rows one MFMA operand read
-// touches fall in 16 distinct bank groups.
-constexpr int PBM = 128, PBN = 256, PBK = 128;
-constexpr int kXTileBytes = PBM * PBK * 2;
-constexpr int kSlowPitch = 40;  // BF16 elements per row in the plain loop's x tile
+// Workgroup tile 128 (rows of x) x 256 (weight rows): four waves side by
+// side along n, each the full 128 x 64, so no weight fragment is fetched
+// twice.  The main K loop is mfma_kloop (mfma_tile.h); what is left of K past
+// the last full 128-column block, and the LoRA product as 2r extra K columns
+// (t hi/lo x B twice), go through plain_kloop.
+constexpr int PBM = 128, PBN = 256;
+constexpr int kXTileBytes = PBM * kTileRowBytes;
+#ifndef QERL_GROUP_M
+#define QERL_GROUP_M 4
+#endif
+constexpr int64_t kGroupM = QERL_GROUP_M;  // row blocks per group of the tile order
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_xtile0[kXTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_xtile1[kXTileBytes];
@@ -148,17 +138,6 @@ __device__ __forceinline__ uint4 x_piece_ext(const Gemm &g, int64_t m, int64_t k
     for (int i = 0; i < 8; ++i) e[i] = (j0 + i < klora) ? t16[j0 + i] : (uint16_t)0;
     __builtin_memcpy(&o, e, 16);
     return o;
-}
-
-// exact BF16 of e2m1 * e4m3 for the 8 elements of one packed 32-bit word
-__device__ __forceinline__ bf16x8_t dequant8_p(uint32_t q, float s) {
-    const f32x2_t f0 = QERL_FP4_PAIR_F32(q, 0), f1 = QERL_FP4_PAIR_F32(q, 1);
-    const f32x2_t f2 = QERL_FP4_PAIR_F32(q, 2), f3 = QERL_FP4_PAIR_F32(q, 3);
-    const uint4 u = make_uint4(pack_bf16x2(f0.x * s, f0.y * s), pack_bf16x2(f1.x * s, f1.y * s),
-                               pack_bf16x2(f2.x * s, f2.y * s), pack_bf16x2(f3.x * s, f3.y * s));
-    bf16x8_t v;
-    __builtin_memcpy(&v, &u, 16);
-    return v;
 }
 
 // The 8 weights of row n at columns [kk, kk + 8) of the extended K range as
@@ -185,20 +164,21 @@ __device__ __forceinline__ bf16x8_t w_frag_ext(const GemmArgs &a, int64_t n, int
     return v;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
     const GemmArgs &a = g.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-    // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
-    // contiguous range of tiles (n fastest), so the workgroups sharing an x
-    // row block also share that XCD's L2
-    const int64_t tiles_n = (a.n + PBN - 1) / PBN, tiles = tiles_n * ((a.m + PBM - 1) / PBM);
+    // XCD-aware tile order: workgroup b runs on XCD b % 8 and each XCD takes
+    // a contiguous range of the tile order.  That order walks groups of
+    // kGroupM row blocks, n-major inside a group, so the tiles one XCD runs at
+    // a time share kGroupM x slabs and a few weight slabs in its L2 rather
+    // than one x slab and dozens of weight slabs.
+    const int64_t tiles_n = (a.n + PBN - 1) / PBN, tiles_m = (a.m + PBM - 1) / PBM, tiles = tiles_n * tiles_m;
     const int64_t b = blockIdx.x, x8 = b % 8, q8 = tiles / 8, r8 = tiles % 8;
     const int64_t tile = x8 * q8 + (x8 < r8 ? x8 : r8) + b / 8;
-    const int64_t m0 = (tile / tiles_n) * PBM, n0 = (tile % tiles_n) * PBN;
+    const int64_t grp = tile / (kGroupM * tiles_n), in_grp = tile % (kGroupM * tiles_n);
+    const int64_t gm = tiles_m - grp * kGroupM < kGroupM ? tiles_m - grp * kGroupM : kGroupM;  // rows in this group
+    const int64_t m0 = (grp * kGroupM + in_grp % gm) * PBM, n0 = (in_grp / gm) * PBN;
     const int64_t klora = 2 * (int64_t)a.r;
-    const int64_t ktot = a.k + klora;
 
     f32x4_t acc[8][4];
 #pragma unroll
@@ -206,143 +186,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // ---- main K range, 128 columns a block ----
-    // Operands come through buffer loads: one resource per operand for the
-    // whole tile, per-lane 32-bit offsets, the block and the row group in the
-    // uniform offset.  Rows past m or n lie past the resource's end and read
-    // as zeros (their outputs are discarded).  The 32-bit offsets need
-    // 256 * ldx < 2^31; wider rows take the plain loop.
-    const int64_t rows_m = a.m - m0 < PBM ? a.m - m0 : PBM, rows_n = a.n - n0 < PBN ? a.n - n0 : PBN;
-    const int64_t kb = a.k >> 1, ks = a.k >> 4;
-    const int64_t blocks = a.ldx <= ((int64_t)1 << 22) ? a.k / PBK : 0;
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t *>(a.x + m0 * a.ldx), 0, (int)(blocks ? rows_m * a.ldx * 2 : 0), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.packed + n0 * kb), 0, (int)(blocks ? rows_n * kb : 0), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.scales + n0 * ks), 0, (int)(blocks ? rows_n * ks : 0), 0x00020000);
-    // x DMA: instruction v (< 8) of wave w fills LDS bytes [1024 (8w + v), +1024)
-    // = rows 4q .. 4q+3 with q = 8w + v; lane l writes chunk l % 16 of row
-    // 4q + l / 16, i.e. global chunk (l % 16) ^ (row % 16), and row % 16 only
-    // depends on v % 4
-    int xoff[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int row = 4 * (8 * wave + v) + (lane >> 4);
-        xoff[v] = (int)((row * a.ldx + 8 * ((lane & 15) ^ (row & 15))) * 2);
-    }
-    const int xrow16 = (int)(16 * a.ldx * 2);
-    // weight fragments of this lane: rows 64*wave + 16j + lr, columns 32lq ..
-    // 32lq+31 of each block
-    const int wrow = wave * 64 + lr;
-    const int qoff = (int)(wrow * kb + 16 * lq), soff = (int)(wrow * ks + 2 * lq);
-    const int qrow16 = (int)(16 * kb), srow16 = (int)(16 * ks);
-    // A operand of MFMA step t, m-tile i: row 16i + lr, global chunk 4lq + t
-    int aoff[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) aoff[t] = lr * 256 + (((4 * lq + t) ^ lr) << 4);
+    const int64_t blocks = a.ldx <= kTileMaxLdx ? a.k / kTileK : 0;
+    mfma_kloop<8>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1), a.scales + n0 * (a.k >> 4),
+                  a.n - n0, a.k, 0, blocks, g_xtile0, g_xtile1, acc);
+    const int64_t nw = n0 + wave * 64 + lr;
+    plain_kloop<8>(
+        blocks * kTileK, a.k + klora, g_xtile0,
+        [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora); },
+        [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
 
-    auto dma_x = [&](uint8_t *dst, int64_t s) {
-        const int k0 = (int)(s * PBK);
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(dst + 1024 * (8 * wave + v)), 16,
-                                                     xoff[v & 3], 2 * k0 + (v >> 2) * xrow16, 0, 0);
-    };
-    uint4 qn0, qn1, qn2, qn3;
-    uint32_t sn0, sn1, sn2, sn3;
-    auto ldq16 = [&](int j, int kq) {
-        const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, kq + j * qrow16, 0);
-        uint4 o;
-        __builtin_memcpy(&o, &v, 16);
-        return o;
-    };
-    auto lds2 = [&](int j, int kq) { return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, soff, kq + j * srow16, 0); };
-    auto load_w = [&](int64_t s) {
-        const int k0 = (int)(s * PBK);
-        qn0 = ldq16(0, k0 >> 1);
-        qn1 = ldq16(1, k0 >> 1);
-        qn2 = ldq16(2, k0 >> 1);
-        qn3 = ldq16(3, k0 >> 1);
-        sn0 = lds2(0, k0 >> 4);
-        sn1 = lds2(1, k0 >> 4);
-        sn2 = lds2(2, k0 >> 4);
-        sn3 = lds2(3, k0 >> 4);
-    };
-    // one MFMA step over the 8 x 4 tiles; A row 16i + lr at byte pa + 4096 i
-    auto mma_t = [&](const uint8_t *pa, const bf16x8_t &b0, const bf16x8_t &b1, const bf16x8_t &b2,
-                     const bf16x8_t &b3, int pitch_bytes) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(pa + 16 * i * pitch_bytes);
-            acc[i][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b0, acc[i][0], 0, 0, 0);
-            acc[i][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b1, acc[i][1], 0, 0, 0);
-            acc[i][2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b2, acc[i][2], 0, 0, 0);
-            acc[i][3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, b3, acc[i][3], 0, 0, 0);
-        }
-    };
-    uint4 qc0, qc1, qc2, qc3;
-    uint32_t sc0, sc1, sc2, sc3;
-    // block s from LDS tile cur while block s+1 streams into nxt
-    auto block = [&](const uint8_t *cur, uint8_t *nxt, int64_t s) {
-        const bool more = s + 1 < blocks;  // uniform
-        if (more) {
-            dma_x(nxt, s + 1);
-            load_w(s + 1);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool hi = t >= 2;  // scale byte 1 covers the last 16 of the lane's 32 columns
-            const float f0 = hi ? QERL_E4M3_F32(sc0, 1) : QERL_E4M3_F32(sc0, 0);
-            const float f1 = hi ? QERL_E4M3_F32(sc1, 1) : QERL_E4M3_F32(sc1, 0);
-            const float f2 = hi ? QERL_E4M3_F32(sc2, 1) : QERL_E4M3_F32(sc2, 0);
-            const float f3 = hi ? QERL_E4M3_F32(sc3, 1) : QERL_E4M3_F32(sc3, 0);
-            const uint32_t w0 = t == 0 ? qc0.x : t == 1 ? qc0.y : t == 2 ? qc0.z : qc0.w;
-            const uint32_t w1 = t == 0 ? qc1.x : t == 1 ? qc1.y : t == 2 ? qc1.z : qc1.w;
-            const uint32_t w2 = t == 0 ? qc2.x : t == 1 ? qc2.y : t == 2 ? qc2.z : qc2.w;
-            const uint32_t w3 = t == 0 ? qc3.x : t == 1 ? qc3.y : t == 2 ? qc3.z : qc3.w;
-            mma_t(cur + aoff[t], dequant8_p(w0, f0), dequant8_p(w1, f1), dequant8_p(w2, f2), dequant8_p(w3, f3),
-                  256);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (more) {
-            qc0 = qn0; qc1 = qn1; qc2 = qn2; qc3 = qn3;
-            sc0 = sn0; sc1 = sn1; sc2 = sn2; sc3 = sn3;
-        }
-        // this wave's DMA into nxt must land before any wave reads it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-    if (blocks > 0) {
-        dma_x(g_xtile0, 0);
-        load_w(0);
-        qc0 = qn0; qc1 = qn1; qc2 = qn2; qc3 = qn3;
-        sc0 = sn0; sc1 = sn1; sc2 = sn2; sc3 = sn3;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        for (int64_t s = 0; s < blocks; s += 2) {
-            block(g_xtile0, g_xtile1, s);
-            if (s + 1 < blocks) block(g_xtile1, g_xtile0, s + 1);
-        }
-    }
-    // ---- the rest: K past the last full block and the LoRA columns, 32 a
-    // step in natural order (lane quarter q: columns 8q .. 8q+7) ----
-    uint16_t *sx = reinterpret_cast<uint16_t *>(g_xtile0);  // [PBM][kSlowPitch]
-    const int xr2 = tid >> 2, xc2 = (tid & 3) * 8;
-    for (int64_t k0 = blocks * PBK; k0 < ktot; k0 += 32) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<uint4 *>(sx + (xr2 + 64 * u) * kSlowPitch + xc2) =
-                x_piece_ext(g, m0 + xr2 + 64 * u, k0 + xc2, klora);
-        const int64_t kk = k0 + 8 * lq, nw = n0 + wave * 64 + lr;
-        const bf16x8_t b0 = w_frag_ext(a, nw, kk, klora);
-        const bf16x8_t b1 = w_frag_ext(a, nw + 16, kk, klora);
-        const bf16x8_t b2 = w_frag_ext(a, nw + 32, kk, klora);
-        const bf16x8_t b3 = w_frag_ext(a, nw + 48, kk, klora);
-        __syncthreads();
-        mma_t(reinterpret_cast<const uint8_t *>(sx + lr * kSlowPitch + 8 * lq), b0, b1, b2, b3, kSlowPitch * 2);
-        __syncthreads();
-    }
     const float st_scale = *a.tensor_scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
