@@ -117,17 +117,20 @@ class DecodeLayer:
         self.y = {name: torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
                   for name, (n, _k) in self.shapes.items()}
         ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
-        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
+        # one workspace per concurrent GEMM (calls that overlap must not share one)
+        self.ws = [torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev) for _ in range(3)]
+        # side streams for the independent projections (default priority)
+        self.side = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
         self.sigmas = [q.aqn_sigma(s, STAGES, SIGMA0, SIGMA1) for s in range(STAGES)]
 
     def inputs_of(self, name):
         return {"q": self.x_attn, "k": self.x_attn, "v": self.x_attn, "o": self.x_o,
                 "gate": self.x_mlp, "up": self.x_mlp, "down": self.x_down}[name]
 
-    def gemm(self, name, m, c):
+    def gemm(self, name, m, c, slot=0):
         p = self.copies[c][name]
         q.w4a16_lora_gemm(self.inputs_of(name)[:m], p.wq, p.a, p.b, ALPHA / RANK,
-                          out=self.y[name][:m], workspace=self.ws)
+                          out=self.y[name][:m], workspace=self.ws[slot])
 
     def norm(self, which, m, step):
         src, w, dst, layer = ((self.h_attn, self.w_attn, self.x_attn, 0) if which == "attn"
@@ -139,11 +142,35 @@ class DecodeLayer:
         for mi, m in enumerate(DECODE_MS):
             c = (len(DECODE_MS) * s + mi) % len(self.copies)
             self.norm("attn", m, s)
-            for name in ("q", "k", "v", "o"):
-                self._g(name, m, c, on_gemm)
+            if on_gemm is None:
+                # q, k and v read the same normed input and nothing else: they
+                # run side by side; o waits for all three (in a real layer
+                # attention sits in between), as the MLP waits for o
+                self._parallel(("q", "k", "v"), m, c)
+                self.gemm("o", m, c)
+            else:
+                for name in ("q", "k", "v", "o"):
+                    self._g(name, m, c, on_gemm)
             self.norm("mlp", m, s)
-            for name in ("gate", "up", "down"):
-                self._g(name, m, c, on_gemm)
+            if on_gemm is None:
+                self._parallel(("gate", "up"), m, c)  # down waits for both
+                self.gemm("down", m, c)
+            else:
+                for name in ("gate", "up", "down"):
+                    self._g(name, m, c, on_gemm)
+
+    def _parallel(self, names, m, c):
+        """names[0] on the current stream, the rest on side streams, joined
+        back into the current stream; each call has its own workspace."""
+        main = torch.cuda.current_stream()
+        for i, name in enumerate(names[1:]):
+            st = self.side[i]
+            st.wait_stream(main)
+            with torch.cuda.stream(st):
+                self.gemm(name, m, c, slot=i + 1)
+        self.gemm(names[0], m, c, slot=0)
+        for st in self.side[:len(names) - 1]:
+            main.wait_stream(st)
 
     def _g(self, name, m, c, on_gemm):
         if on_gemm is None:
