@@ -47,7 +47,7 @@ def _x(m, k, seed, outliers=0.005):
     return synth.bf16_bits(synth.activation_bf16(m, k, seed=seed, outlier_col_frac=outliers))
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16, 33, 64, 100, 256])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16, 17, 24, 32, 33, 64, 100, 256])
 @pytest.mark.parametrize("nkr", [(96, 256, 16), (77, 512, 32), (130, 1024, 8), (64, 48, 4),
                                  (33, 80, 0), (200, 2048, 64), (5, 128, 4), (300, 1040, 24),
                                  (1000, 3600, 32)])
@@ -59,7 +59,7 @@ def test_small_shapes(m, nkr):
     assert_gemm_close(y, L.ref(x), f"m={m} n={n} k={k} r={r}")
 
 
-@pytest.mark.parametrize("m", [1, 4, 64])
+@pytest.mark.parametrize("m", [1, 4, 20, 64, 200])
 def test_strided_activations_and_output(m):
     n, k, r = 96, 512, 16
     L = Layer(n, k, r, seed=300)
@@ -71,6 +71,22 @@ def test_strided_activations_and_output(m):
     torch.cuda.synchronize()
     assert_gemm_close(bf16_to_f64(yw[:, :n]), L.ref(x), "strided")
     assert torch.all(yw[:, n:] == 7.0)
+
+
+@pytest.mark.parametrize("m", [1, 20, 70])
+def test_very_wide_x_rows(m):
+    """x rows 2^22 + 64 elements apart: past the main loop's 32-bit buffer
+    offsets, so the m > 16 paths take their plain loop for all of K."""
+    n, k, r = 96, 256, 8
+    L = Layer(n, k, r, seed=350)
+    x = _x(m, k, seed=351)
+    ldx = (1 << 22) + 64
+    xw = torch.zeros((m, ldx), dtype=torch.bfloat16, device=dev())
+    xw[:, :k] = bits_to_gpu(x)
+    y = q.w4a16_lora_gemm(xw[:, :k], L.wq, L.a, L.b, L.lam)
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_to_f64(y), L.ref(x), f"wide rows m={m}")
+    del xw
 
 
 @pytest.mark.parametrize("m", [1, 3, 16, 80])
