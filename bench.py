@@ -355,6 +355,139 @@ def quantizer_leg(dev, reps):
             "whole_model_ms_est": t * 1e3 * 64}
 
 
+# ---- roofline of the dominant decode kernel --------------------------------
+# stream_kernel runs every decode call with M <= 16, one launch per call.  Its
+# average launch duration comes from a graph of those calls run one after
+# another (the timed step runs independent projections side by side, where
+# durations overlap; events around single calls add the dispatch overhead).
+ROOFLINE_MS = (1, 8)
+ROOFLINE_KERNEL = "stream_kernel<1, 1, 1, true>"
+KERNEL_SOURCES = ("decode.hip", "mfma_tile.h", "device_common.h", "qerl_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_kernel_7b_m1_m8.md")
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "nvfp4_weight_only_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per stream_kernel launch from the committed counter summary,
+    or None when it is missing or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.strip()[2:].split(": ", 1) for line in fh if line.startswith("- ") and ": " in line)
+    except OSError:
+        return None
+    if kv.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def roofline_leg(layer: DecodeLayer, reps: int = 5):
+    calls = per_call_durations(layer, reps=reps)
+    per_m = {}
+    for m in DECODE_MS:
+        b = sum(c[2] for c in calls if c[1] == m)
+        t = sum(c[3] for c in calls if c[1] == m)
+        per_m[f"M={m}"] = {"gemm_us": t / reps * 1e6, "GB/s": b / t / 1e9}
+    per_proj = {}
+    for name in synth.PROJ_ORDER:
+        for m in DECODE_MS:
+            sel = [c for c in calls if c[0] == name and c[1] == m]
+            per_proj[f"{name}@{m}"] = round(sum(c[3] for c in sel) / len(sel) * 1e6, 2)
+    # the kernel's own launch duration: the M in ROOFLINE_MS calls of `reps`
+    # steps back to back in one graph (cold weights rotate as in the step),
+    # timed with one event pair around the replay
+    def run():
+        for s in range(reps):
+            for mi, m in enumerate(DECODE_MS):
+                if m in ROOFLINE_MS:
+                    c = (len(DECODE_MS) * (1000 + s) + mi) % len(layer.copies)
+                    for name in synth.PROJ_ORDER:
+                        layer.gemm(name, m, c)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    launches = reps * len(ROOFLINE_MS) * len(synth.PROJ_ORDER)
+    b_launch = sum(gemm_bytes(m, *layer.shapes[name], RANK) for m in ROOFLINE_MS
+                   for name in synth.PROJ_ORDER) * reps / launches
+    t_launch = e0.elapsed_time(e1) * 1e-3 / launches
+    del g
+    achieved = b_launch / t_launch / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
+                "kernel": f"{ROOFLINE_KERNEL} (decode W4A16 + LoRA, M in {list(ROOFLINE_MS)}, "
+                          "7 projections of the 7B layer)",
+                "launches": launches, "avg_launch_us": t_launch * 1e6, "avg_launch_bytes": b_launch}
+    return roofline, per_m, per_proj
+
+
+def summarize_profile(trace_dir, fetch_dir, write_dir):
+    """Print the markdown summary of three rocprofv3 runs of `--calls-only
+    --copy-probe`: kernel statistics, and FETCH_SIZE / WRITE_SIZE per dispatch
+    of stream_kernel scaled by what they read for the 256 MiB copy."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    lines = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---:|---:|---:|---:|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        nm = r["Name"].replace("qerl::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"| `{nm[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    ours = [r for r in stats if ROOFLINE_KERNEL in r["Name"]]
+    avg_us = float(ours[0]["AverageNs"]) / 1e3 if ours else float("nan")
+
+    def per_dispatch(d, counter):
+        vals, copy = [], []
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            if ROOFLINE_KERNEL in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+        return sum(vals) / max(len(vals), 1), len(vals), max(copy) if copy else float("nan")
+
+    f_kib, f_n, f_copy = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_kib, w_n, w_copy = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_kib = 256 * 1024  # the probe copies 256 MiB: that many read and written
+    f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
+    hbm = (f_kib * f_scale + w_kib * w_scale) * 1024
+    print("\n".join(lines))
+    print()
+    print(f"- kernel: {ROOFLINE_KERNEL}")
+    print(f"- average_launch_us: {avg_us:.3f}")
+    print(f"- fetch_kib_per_dispatch: {f_kib:.1f} ({f_n} dispatches)")
+    print(f"- write_kib_per_dispatch: {w_kib:.1f} ({w_n} dispatches)")
+    print(f"- copy_probe_fetch_kib: {f_copy:.1f} (256 MiB copy; scale {f_scale:.4f})")
+    print(f"- copy_probe_write_kib: {w_copy:.1f} (256 MiB copy; scale {w_scale:.4f})")
+    print(f"- hbm_bytes_per_launch: {hbm:.0f}")
+    print(f"- sources_sha256: {kernel_sources_sha256()}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,7 +498,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--calls-only", action="store_true",
+                    help="only the per-call roofline leg (for rocprofv3 runs); prints its JSON")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="with --calls-only: also copy 256 MiB device to device (counter scale)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the profile summary of rocprofv3 output directories and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profile(*args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -378,6 +520,16 @@ def main():
     log("setting up decode layer ...")
     layer = DecodeLayer(dev, args.copies)
     torch.cuda.synchronize()
+    if args.calls_only:
+        roofline, per_m, per_proj = roofline_leg(layer)
+        if args.copy_probe:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"roofline": roofline, "decode_per_m": per_m, "decode_call_us": per_proj}), flush=True)
+        return
 
     def steps_fn(first, count):
         for s in range(first, first + count):
@@ -388,24 +540,7 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
 
-    calls = per_call_durations(layer, reps=5)
-    tot_b = sum(c[2] for c in calls)
-    tot_t = sum(c[3] for c in calls)
-    per_m = {}
-    for m in DECODE_MS:
-        b = sum(c[2] for c in calls if c[1] == m)
-        t = sum(c[3] for c in calls if c[1] == m)
-        per_m[f"M={m}"] = {"gemm_us": t / 5 * 1e6, "GB/s": b / t / 1e9}
-    per_proj = {}
-    for name in synth.PROJ_ORDER:
-        for m in DECODE_MS:
-            sel = [c for c in calls if c[0] == name and c[1] == m]
-            per_proj[f"{name}@{m}"] = round(sum(c[3] for c in sel) / len(sel) * 1e6, 2)
-    achieved = tot_b / tot_t / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "kernel": "qerl_w4a16_lora_gemm decode calls (LoRA down-projection + W4A16 kernel)",
-                "avg_call_us": tot_t / len(calls) * 1e6, "avg_call_bytes": tot_b / len(calls)}
+    roofline, per_m, per_proj = roofline_leg(layer)
 
     parity = check_decode_parity(layer)
     result = {
