@@ -367,11 +367,17 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_kernel_7b_m1_m8.md"
 
 
 def kernel_sources_sha256():
+    """Hash of the kernel's sources with comments and blank lines removed
+    (a comment edit does not change the kernel)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "nvfp4_weight_only_quantize_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "nvfp4_weight_only_quantize_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = re.sub(r"//.*", "", line).rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()
 
 

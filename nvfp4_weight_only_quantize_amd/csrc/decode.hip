@@ -1,5 +1,5 @@
 // decode.hip -- W4A16 (NVFP4 weight x BF16 activation) + LoRA for decode
-// batches, 1 <= m <= 64, on gfx950.  One launch per call.
+// batches, 1 <= m <= 64, on gfx950.
 //
 //   y[m, n] = s_t * sum_k x[m,k] e2m1(q[n,k]) e4m3(sb[n,k/16])
 //           + lora_scale * sum_j t[m,j] B[n,j],        t = x A^T
@@ -9,32 +9,35 @@
 // (Low-Rank Adaptation)" and "Implementation and Practical Details").
 //
 // Decode is bound by the bytes of the packed weights (0.5625 B per weight),
-// which are read exactly once.  Work units are (block of 64*NW weight rows) x
-// (slice of K); each of the 4 waves of a unit owns 16*NW rows.
+// which are read exactly once.  Weights are decoded to exact BF16 (e2m1 *
+// e4m3 has <= 6 significant bits) and multiplied on the 16x16x32 BF16 MFMA in
+// FP32; K is permuted inside each 128-element chunk, identically for both
+// operands, so that one 16-byte load gives a lane the packed bytes of four
+// MFMA steps.
 //
-//  * Weights stream in 128-element chunks (per row 64 packed bytes) through a
-//    ring of D chunks per wave.  Every load of the steady state is
-//    unconditional, which keeps the compiler's in-order wait counts exact.
-//  * The E4M3 scales of the unit are staged into LDS once with wide loads
-//    (per-lane 2-byte global loads would double the memory instructions).
-//  * x passes through a double-buffered LDS window of W chunks, loaded one
-//    window ahead; LDS reads are counted apart from global loads.
-//  * Weights are decoded to exact BF16 (e2m1 * e4m3 has <= 6 significant
-//    bits) and multiplied on the 16x16x32 BF16 MFMA in FP32.
+// m <= 16, stream_kernel, one launch per call.  Work units are (64 weight
+// rows) x (slice of K); each of the 4 waves of a unit owns 16 rows.
+//  * The unit's x slice and E4M3 scales are staged into LDS once with batched
+//    wide loads; the weights stream in 128-element chunks (64 packed bytes per
+//    row) through a ring of DR chunks per wave, with no barrier.  Every load
+//    of the steady state is unconditional, which keeps the compiler's
+//    in-order wait counts exact; LDS reads are counted apart from them.
 //  * LoRA: "producer" workgroups at the head of the grid compute partial sums
 //    of t = x A^T over slices of K (MFMA) and publish them with device-coherent
-//    stores; the epilogue adds lora_scale * t B^T on the MFMA with t split
-//    into BF16 hi + lo halves (relative error ~2^-16).
-//  * m <= 16, one launch: every unit but the last of its row block stores its
-//    FP32 partial tile (coherent stores) and bumps a counter; the last to
-//    arrive sums all partials in slice order (deterministic), waits until the
-//    producers have all published (they are dispatched before every consumer,
-//    so the wait is short; it is bounded all the same), sums their t partials
-//    in producer order and writes the output.
-//  * 16 < m <= 64, two launches: partial tiles are larger, so every unit
-//    stores its tile and finish_kernel sums them (in slice order) in parallel
-//    over the outputs; the last producer sums t, which finish_kernel reads
-//    after the kernel boundary.
+//    stores.
+//  * Every unit but the last of its row block stores its FP32 partial tile
+//    (coherent stores) and bumps a counter; the last to arrive sums all
+//    partials in slice order (deterministic), waits until the producers have
+//    all published (they are dispatched before every consumer, so the wait is
+//    short; it is bounded all the same), sums their t partials in producer
+//    order, and adds lora_scale * t B^T on the MFMA with t split into BF16 hi +
+//    lo halves (relative error ~2^-16).
+//
+// 16 < m <= 64, mfma_unit_kernel + finish_kernel, two launches.  Units are
+// (256 weight rows) x (slice of K) running the K loops of mfma_tile.h with all
+// of x as the x tile; every unit stores its FP32 tile and finish_kernel sums
+// them (in slice order) in parallel over the outputs; the last producer sums
+// t, which finish_kernel reads after the kernel boundary.
 //
 // Counters live in the first kGemmCtrBytes of the workspace: they must be zero
 // before the first call, and every call leaves them zero.
