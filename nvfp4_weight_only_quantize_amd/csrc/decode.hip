@@ -50,6 +50,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreadsD = kWaves * 64;
+// waves of a 16 < m unit (64 weight rows each).  Eight waves sharing one x
+// tile, or weights fetched two blocks ahead, were measured slower: the unit is
+// bound by its CU's vector memory path, not by latency.
+constexpr int kUnitWaves = 4;
 constexpr int64_t kChunkK = 128;          // K elements per chunk
 constexpr int kXPad = 8;                  // BF16 padding per staged x row
 constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
@@ -82,7 +86,7 @@ __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(in
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-    p.nw = p.mt == 1 ? 1 : 4;  // 16 < m: MFMA units of 256 weight rows
+    p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
     p.rows_per_unit = 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
     if (p.row_blocks > kMaxRowBlocks) p.row_blocks = 0;  // one counter per row block: rejected at launch
@@ -231,7 +235,9 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
             f32x4_t acc[kProdTiles];
 #pragma unroll
             for (int j = 0; j < kProdTiles; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t k0 = kb + 32 * wave; k0 < ke; k0 += 4 * 32 * PS) {
+            // (in a wider workgroup only the first kWaves waves work; the rest
+            // keep to the barriers)
+            for (int64_t k0 = wave < kWaves ? kb + 32 * wave : ke; k0 < ke; k0 += 4 * 32 * PS) {
                 uint4 xv[PS], av[PS][kProdTiles];
 #pragma unroll
                 for (int u = 0; u < PS; ++u) {
@@ -258,8 +264,9 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
                 }
             }
             // the four waves' tiles, summed in wave order by wave 0 and published
+            if (wave < kWaves)
 #pragma unroll
-            for (int jj = 0; jj < kProdTiles; ++jj) red[(wave * kProdTiles + jj) * 64 + lane] = acc[jj];
+                for (int jj = 0; jj < kProdTiles; ++jj) red[(wave * kProdTiles + jj) * 64 + lane] = acc[jj];
             __syncthreads();
             if (wave == 0) {
 #pragma unroll
@@ -282,7 +289,7 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     if (MT == 1 || !s_last) return;  // m <= 16: the consumers sum the partials
     // 16 < m: the last producer sums the partials in producer order into t [m, r];
     // tile i goes to wave i % 4, kBatch producers in flight
-    for (int i = wave; i < MT * JT; i += kWaves) {
+    for (int i = wave; wave < kWaves && i < MT * JT; i += kWaves) {
         f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         for (int64_t q0 = 0; q0 < d.p.producers; q0 += kBatch) {
             f32x4_t v[kBatch];
@@ -757,29 +764,35 @@ __global__ __launch_bounds__(256) void finish_kernel(Decode d) {
 // ---------------------------------------------------------------------------
 // 16 < m: MFMA units
 // ---------------------------------------------------------------------------
-// Unit u = (slice of K, block of 256 weight rows) runs the K loops of
-// mfma_tile.h over its chunks with all 16 MT rows of x as the x tile, and
-// stores its FP32 tile where finish_kernel<MT, 4> reads it (f32x4 slot
-// ((wave MT + i) 4 + j) 64 + lane for m-tile i, n-tile j).  Producers of t
-// lead the grid, as in stream_kernel.
+// Unit u = (slice of K, block of 64 kUnitWaves weight rows) runs the K loops
+// of mfma_tile.h over its chunks with all 16 MT rows of x as the x tile, so
+// the eight waves share one x tile (x bytes per weight byte halve against
+// four waves).  It stores its FP32 tile where finish_kernel<MT, NW> reads it,
+// NW = 4 kUnitWaves / kWaves n-tiles per wave of a four-wave layout: wave w's
+// n-tile j (unit rows 64w + 16j ..) is n-tile (4w + j) % NW of layout wave
+// w / (kUnitWaves / kWaves), so m-tile i goes to f32x4 slot
+// ((layout wave MT + i) NW + (4w + j) % NW) 64 + lane.  Producers of t lead the grid, as in stream_kernel; only
+// the first four waves of a producer work.
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile0[64 * kTileRowBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
 
 template <int MT>
-__global__ __launch_bounds__(kThreadsD, 2) void mfma_unit_kernel(Decode d) {
+__global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     if ((int64_t)blockIdx.x < p.producers) {
         lora_producer<MT>(d, blockIdx.x, g_dxtile0);
         return;
     }
+    constexpr int NW = 4 * kUnitWaves / kWaves;  // n-tiles per wave of the four-wave tile layout
+    constexpr int kPer = kUnitWaves / kWaves;     // unit waves per layout wave
     const int64_t u = blockIdx.x - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
     const int64_t c_begin = slice * p.cps;
     const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
     const int64_t c_full_end = c_end < p.full_chunks ? c_end : p.full_chunks;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-    const int64_t n0 = rblk * 256, kb = a.k >> 1, ks = a.k >> 4;
+    const int64_t n0 = rblk * p.rows_per_unit, kb = a.k >> 1, ks = a.k >> 4;
 
     f32x4_t acc[MT][4];
 #pragma unroll
@@ -788,12 +801,12 @@ __global__ __launch_bounds__(kThreadsD, 2) void mfma_unit_kernel(Decode d) {
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int64_t fast_end = a.ldx <= kTileMaxLdx ? c_full_end : c_begin;
-    mfma_kloop<MT>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k, c_begin, fast_end,
-                   g_dxtile0, g_dxtile1, acc);
+    mfma_kloop<MT, kUnitWaves>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k, c_begin,
+                               fast_end, g_dxtile0, g_dxtile1, acc);
     // the rest of the slice (the partial last chunk of K, or all of it for
     // very wide x rows)
     const int64_t nw = n0 + wave * 64 + lr;
-    plain_kloop<MT>(
+    plain_kloop<MT, kUnitWaves>(
         fast_end * kChunkK, c_end * kChunkK < a.k ? c_end * kChunkK : a.k, g_dxtile0,
         [&](int row, int64_t kk) {
             uint4 o = make_uint4(0, 0, 0, 0);
@@ -809,22 +822,22 @@ __global__ __launch_bounds__(kThreadsD, 2) void mfma_unit_kernel(Decode d) {
         },
         acc);
 
-    f32x4_t *tile = reinterpret_cast<f32x4_t *>(d.part() + u * (256 * 16 * MT)) + wave * MT * 4 * 64 + lane;
+    f32x4_t *tile = reinterpret_cast<f32x4_t *>(d.part() + u * (p.rows_per_unit * 16 * MT)) + lane;
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (16 * i + 4 * lq < a.m) tile[(i * 4 + j) * 64] = acc[i][j];
+            if (16 * i + 4 * lq < a.m) tile[(((wave / kPer) * MT + i) * NW + (4 * wave + j) % NW) * 64] = acc[i][j];
 }
 
 template <int MT>
 hipError_t launch_mfma_units(const Decode &d, hipStream_t stream) {
-    hipLaunchKernelGGL(mfma_unit_kernel<MT>, dim3((unsigned)(d.p.producers + d.p.units)), dim3(kThreadsD), 0, stream,
-                       d);
+    hipLaunchKernelGGL(mfma_unit_kernel<MT>, dim3((unsigned)(d.p.producers + d.p.units)), dim3(64 * kUnitWaves), 0,
+                       stream, d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));
-    hipLaunchKernelGGL((finish_kernel<MT, 4>), fgrid, dim3(256), 0, stream, d);
+    hipLaunchKernelGGL((finish_kernel<MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, d);
     return hipGetLastError();
 }
 

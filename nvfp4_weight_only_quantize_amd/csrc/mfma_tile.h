@@ -1,9 +1,9 @@
 // mfma_tile.h -- the K loops of the large-m W4A16 GEMM (gemm.hip) on gfx950.
 //
-// A workgroup of four waves owns 256 consecutive weight rows; wave w owns
-// rows 64w .. 64w+63 (four 16-row MFMA n-tiles) against all 16*MTW rows of
-// its x tile (MTW 16-row m-tiles), accumulating in FP32 with BF16 MFMA
-// 16x16x32.  e2m1 * e4m3 is exact in BF16, so the weights are decoded to
+// A workgroup of NWV waves (4 or 8) owns 64 NWV consecutive weight rows;
+// wave w owns rows 64w .. 64w+63 (four 16-row MFMA n-tiles) against all
+// 16*MTW rows of its x tile (MTW 16-row m-tiles), accumulating in FP32 with
+// BF16 MFMA 16x16x32.  e2m1 * e4m3 is exact in BF16, so the weights are decoded to
 // BF16 in registers without rounding; the tensor scale s_t is left to the
 // caller.
 //
@@ -36,6 +36,16 @@ constexpr int kTileRowBytes = kTileK * 2;   // bytes per x row of an LDS tile
 constexpr int kPlainPitch = 40;             // BF16 elements per x row in the plain loop
 constexpr int64_t kTileMaxLdx = (int64_t)1 << 22;  // main loop: 32-bit buffer offsets
 
+// s_waitcnt with only the vector-memory count set (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).  Unlike an
+// inline-asm wait, the compiler's own wait analysis takes this one into
+// account.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // exact BF16 of e2m1 * e4m3 for the 8 elements of one packed 32-bit word
 // (element 2i in the low nibble of byte i)
 __device__ __forceinline__ bf16x8_t dequant8_p(uint32_t q, float s) {
@@ -64,24 +74,27 @@ __device__ __forceinline__ void mfma_step(const uint8_t *pa, int pitch_bytes, co
 
 // Main loop over the full K blocks [b0, b1) (b1 * 128 <= k).
 //   x_tile: row 0 of the x tile; rows at or past x_rows are read as zeros
-//   w_packed, w_scales: row 0 of the workgroup's 256 weight rows; rows at or
-//     past w_rows are read as zeros
+//   w_packed, w_scales: row 0 of the workgroup's 64 NWV weight rows; rows at
+//     or past w_rows are read as zeros
 //   t0, t1: two LDS tiles of 16 * MTW * 256 bytes, distinct arrays
 // Needs ldx <= kTileMaxLdx and uniform arguments; ends with a barrier.
-template <int MTW>
+template <int MTW, int NWV = 4, int WD = 1>
 __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_rows, int64_t ldx,
                                            const uint8_t *w_packed, const uint8_t *w_scales, int64_t w_rows,
                                            int64_t k, int64_t b0, int64_t b1, uint8_t *t0, uint8_t *t1,
                                            f32x4_t (&acc)[MTW][4]) {
     static_assert(MTW == 2 || MTW == 4 || MTW == 8, "x tile of 32, 64 or 128 rows");
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
+    static_assert(4 * MTW % NWV == 0, "whole DMA instructions per wave");
+    static_assert(WD == 1 || WD == 2, "weights one or two blocks ahead");
     if (b0 >= b1) return;
     constexpr int kXRows = 16 * MTW;
-    constexpr int kDma = MTW;  // DMA instructions per wave per block (1 KB = 4 rows each)
+    constexpr int kDma = 4 * MTW / NWV;  // DMA instructions per wave per block (1 KB = 4 rows each)
     // the wave index as a scalar: the DMA's LDS address must be uniform
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15,
               lq = lane >> 4;
     if (x_rows > kXRows) x_rows = kXRows;
-    if (w_rows > 256) w_rows = 256;
+    if (w_rows > 64 * NWV) w_rows = 64 * NWV;
     const int64_t kb = k >> 1, ks = k >> 4;
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(x_tile), 0,
                                                                          (int)(x_rows * ldx * 2), 0x00020000);
@@ -118,71 +131,88 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t *)(dst + 1024 * (kDma * wave + v)), 16,
                                                      xoff[v & 3], 2 * k0 + (v >> 2) * xrow16, 0, 0);
     };
-    uint4 qn0, qn1, qn2, qn3;
-    uint32_t sn0, sn1, sn2, sn3;
     auto ldq16 = [&](int j, int kq) {
         const i32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, kq + j * qrow16, 0);
         uint4 o;
         __builtin_memcpy(&o, &v, 16);
         return o;
     };
-    auto lds2 = [&](int j, int kq) {
-        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, soff, kq + j * srow16, 0);
+    auto lds2 = [&](int j, int kq) { return __builtin_amdgcn_raw_buffer_load_b16(rs, soff, kq + j * srow16, 0); };
+    // the weight fragments of one block: named members (an array of them
+    // ends up in scratch memory), one set per block in flight; the sets
+    // rotate statically over an unrolled loop, since copying a set would
+    // make the compiler wait for the loads that fill it.  The scale pairs stay
+    // 16-bit until used: widened at the loop head, they would be waited for
+    // there.
+    struct WSet {
+        uint4 q0, q1, q2, q3;
+        uint16_t c0, c1, c2, c3;
     };
-    auto load_w = [&](int64_t s) {
+    auto load_w = [&](WSet &w, int64_t s) {
         const int k0 = (int)(s * kTileK);
-        qn0 = ldq16(0, k0 >> 1);
-        qn1 = ldq16(1, k0 >> 1);
-        qn2 = ldq16(2, k0 >> 1);
-        qn3 = ldq16(3, k0 >> 1);
-        sn0 = lds2(0, k0 >> 4);
-        sn1 = lds2(1, k0 >> 4);
-        sn2 = lds2(2, k0 >> 4);
-        sn3 = lds2(3, k0 >> 4);
+        w.q0 = ldq16(0, k0 >> 1);
+        w.q1 = ldq16(1, k0 >> 1);
+        w.q2 = ldq16(2, k0 >> 1);
+        w.q3 = ldq16(3, k0 >> 1);
+        w.c0 = lds2(0, k0 >> 4);
+        w.c1 = lds2(1, k0 >> 4);
+        w.c2 = lds2(2, k0 >> 4);
+        w.c3 = lds2(3, k0 >> 4);
     };
-    uint4 qc0, qc1, qc2, qc3;
-    uint32_t sc0, sc1, sc2, sc3;
-    // block s from LDS tile cur while block s+1 streams into nxt
-    auto block = [&](const uint8_t *cur, uint8_t *nxt, int64_t s) {
-        const bool more = s + 1 < b1;  // uniform
-        if (more) {
-            dma_x(nxt, s + 1);
-            load_w(s + 1);
-        }
+    // block s from LDS tile cur and weight set wc while x of block s+1 streams
+    // into nxt and the weights of block s+WD into wl.  Every block issues its
+    // weight loads (clamped past the end), so the wait at its end always
+    // leaves exactly the 8 loads of block s+WD in flight when WD == 2.
+    auto block = [&](const uint8_t *cur, uint8_t *nxt, const WSet &wc, WSet &wl, int64_t s) {
+        if (s + 1 < b1) dma_x(nxt, s + 1);  // uniform
+        load_w(wl, s + WD < b1 ? s + WD : b1 - 1);
+        if (s < b1) {  // uniform
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bool hi = t >= 2;  // scale byte 1 covers the last 16 of the lane's 32 columns
-            const float f0 = hi ? QERL_E4M3_F32(sc0, 1) : QERL_E4M3_F32(sc0, 0);
-            const float f1 = hi ? QERL_E4M3_F32(sc1, 1) : QERL_E4M3_F32(sc1, 0);
-            const float f2 = hi ? QERL_E4M3_F32(sc2, 1) : QERL_E4M3_F32(sc2, 0);
-            const float f3 = hi ? QERL_E4M3_F32(sc3, 1) : QERL_E4M3_F32(sc3, 0);
-            const uint32_t w0 = t == 0 ? qc0.x : t == 1 ? qc0.y : t == 2 ? qc0.z : qc0.w;
-            const uint32_t w1 = t == 0 ? qc1.x : t == 1 ? qc1.y : t == 2 ? qc1.z : qc1.w;
-            const uint32_t w2 = t == 0 ? qc2.x : t == 1 ? qc2.y : t == 2 ? qc2.z : qc2.w;
-            const uint32_t w3 = t == 0 ? qc3.x : t == 1 ? qc3.y : t == 2 ? qc3.z : qc3.w;
-            mfma_step<MTW>(cur + aoff[t], kTileRowBytes, dequant8_p(w0, f0), dequant8_p(w1, f1), dequant8_p(w2, f2),
-                           dequant8_p(w3, f3), acc);
-            // keep each step's decode next to its MFMAs (hoisting them all
-            // raises register use past the budget)
-            __builtin_amdgcn_sched_barrier(0);
+            for (int t = 0; t < 4; ++t) {
+                const bool hi = t >= 2;  // scale byte 1 covers the last 16 of the lane's 32 columns
+                const float f0 = hi ? QERL_E4M3_F32(wc.c0, 1) : QERL_E4M3_F32(wc.c0, 0);
+                const float f1 = hi ? QERL_E4M3_F32(wc.c1, 1) : QERL_E4M3_F32(wc.c1, 0);
+                const float f2 = hi ? QERL_E4M3_F32(wc.c2, 1) : QERL_E4M3_F32(wc.c2, 0);
+                const float f3 = hi ? QERL_E4M3_F32(wc.c3, 1) : QERL_E4M3_F32(wc.c3, 0);
+                const uint32_t w0 = t == 0 ? wc.q0.x : t == 1 ? wc.q0.y : t == 2 ? wc.q0.z : wc.q0.w;
+                const uint32_t w1 = t == 0 ? wc.q1.x : t == 1 ? wc.q1.y : t == 2 ? wc.q1.z : wc.q1.w;
+                const uint32_t w2 = t == 0 ? wc.q2.x : t == 1 ? wc.q2.y : t == 2 ? wc.q2.z : wc.q2.w;
+                const uint32_t w3 = t == 0 ? wc.q3.x : t == 1 ? wc.q3.y : t == 2 ? wc.q3.z : wc.q3.w;
+                mfma_step<MTW>(cur + aoff[t], kTileRowBytes, dequant8_p(w0, f0), dequant8_p(w1, f1),
+                               dequant8_p(w2, f2), dequant8_p(w3, f3), acc);
+                // keep each step's decode next to its MFMAs (hoisting them all
+                // raises register use past the budget)
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        if (more) {
-            qc0 = qn0; qc1 = qn1; qc2 = qn2; qc3 = qn3;
-            sc0 = sn0; sc1 = sn1; sc2 = sn2; sc3 = sn3;
-        }
-        // this wave's DMA into nxt must land before any wave reads it
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // this wave's DMA into nxt and the weights of block s+1 must land
+        // before the next block; with WD == 2 the loads just issued may not
+        if (WD == 1)
+            wait_vmcnt<0>();
+        else
+            wait_vmcnt<8>();
         __syncthreads();
     };
+    WSet w0, w1, w2;
     dma_x(t0, b0);
-    load_w(b0);
-    qc0 = qn0; qc1 = qn1; qc2 = qn2; qc3 = qn3;
-    sc0 = sn0; sc1 = sn1; sc2 = sn2; sc3 = sn3;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    load_w(w0, b0);
+    if (WD == 2) load_w(w1, b0 + 1 < b1 ? b0 + 1 : b1 - 1);
+    wait_vmcnt<0>();
     __syncthreads();
-    for (int64_t s = b0; s < b1; s += 2) {
-        block(t0, t1, s);
-        if (s + 1 < b1) block(t1, t0, s + 1);
+    if (WD == 1) {
+        for (int64_t s = b0; s < b1; s += 2) {
+            block(t0, t1, w0, w1, s);
+            block(t1, t0, w1, w0, s + 1);
+        }
+    } else {
+        for (int64_t s = b0; s < b1; s += 6) {
+            block(t0, t1, w0, w2, s);
+            block(t1, t0, w1, w0, s + 1);
+            block(t0, t1, w2, w1, s + 2);
+            block(t1, t0, w0, w2, s + 3);
+            block(t0, t1, w1, w0, s + 4);
+            block(t1, t0, w2, w1, s + 5);
+        }
     }
 }
 
@@ -192,13 +222,13 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
 //                  columns kk .. kk+7
 //   tile: LDS of at least 16 * MTW * kPlainPitch * 2 bytes
 // Uniform arguments; ends with a barrier.
-template <int MTW, typename XPiece, typename WFrag>
+template <int MTW, int NWV = 4, typename XPiece, typename WFrag>
 __device__ __forceinline__ void plain_kloop(int64_t k0, int64_t k1, uint8_t *tile, XPiece xpiece, WFrag wfrag,
                                             f32x4_t (&acc)[MTW][4]) {
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     uint16_t *sx = reinterpret_cast<uint16_t *>(tile);  // [16 MTW][kPlainPitch]
     for (int64_t kc = k0; kc < k1; kc += 32) {
-        for (int i = tid; i < 64 * MTW; i += 256) {
+        for (int i = tid; i < 64 * MTW; i += 64 * NWV) {
             const int row = i >> 2, col = (i & 3) * 8;
             *reinterpret_cast<uint4 *>(sx + row * kPlainPitch + col) = xpiece(row, kc + col);
         }
