@@ -11,9 +11,10 @@
 // ("NVFP4 + LoRA summation").
 //
 // Larger m (m > 64; m <= 64 is the decode path of decode.hip):
-//   prologue_kernel  t = x A^T in FP32, pre-multiplied by lora_scale / s_t and
-//                    split into BF16 hi + lo halves, so that the LoRA product
-//                    becomes 2r extra K columns of the same MFMA accumulation.
+//   prologue_kernel  t = x A^T in FP32 (MFMA, 16 rows of x per workgroup),
+//                    pre-multiplied by lora_scale / s_t and split into BF16
+//                    hi + lo halves, so that the LoRA product becomes 2r extra
+//                    K columns of the same MFMA accumulation.
 //   prefill_kernel   128 x 256 output tiles over the K loops of mfma_tile.h
 //                    (x by LDS DMA, weights decoded to exact BF16 in
 //                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
@@ -56,51 +57,81 @@ struct Gemm {
 // ---------------------------------------------------------------------------
 // Prologue: LoRA down-projection t = x A^T
 // ---------------------------------------------------------------------------
-// One workgroup per (row m, rank j); its 256 lanes split K (16 bytes per lane
-// per step, four steps in flight).  Output, with u = t * lora_scale / s_t:
+// One workgroup per 16 rows of x, all ranks: MFMA 16x16x32 with x as the A
+// operand (lane l: row l % 16, columns 8 (l / 16) .. +8 of a 32-column step)
+// and a 16-rank tile of the LoRA A matrix as the B operand, so tile j holds
+// t[m0 + 4 (l / 16) + v][16 j + l % 16] in element v.  The four waves take
+// interleaved 32-column steps, U at a time with every load issued before the
+// products, and are summed in wave order through LDS.  x is read once; the
+// LoRA A matrix is re-read per workgroup from L2.  Output, with
+// u = t * lora_scale / s_t:
 //   t16[m * 2r + j] = bf16(u), t16[m * 2r + r + j] = bf16(u - bf16(u))
+template <int JT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
+    constexpr int U = JT <= 4 ? 4 : 2;  // 32-column steps in flight per wave
     const GemmArgs &a = g.a;
-    const int64_t pair = blockIdx.x;
-    const int64_t m = pair / a.r;
-    const int j = (int)(pair - m * a.r);
-    const uint16_t *xr = a.x + m * a.ldx;
-    const uint16_t *ar = a.lora_a + (int64_t)j * a.k;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int64_t step = (int64_t)kThreads * 8;
-    int64_t kk = (int64_t)threadIdx.x * 8;
-    for (; kk + 3 * step < a.k; kk += 4 * step) {
-        uint4 xv[4], av[4];
+    __shared__ f32x4_t red[4][JT][64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t row = m0 + lr < a.m ? m0 + lr : a.m - 1;  // rows past m: a repeat, not stored
+    const uint16_t *xr = a.x + row * a.ldx;
+    const uint16_t *ar[JT];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            xv[u] = *reinterpret_cast<const uint4 *>(xr + kk + u * step);
-            av[u] = *reinterpret_cast<const uint4 *>(ar + kk + u * step);
+    for (int j = 0; j < JT; ++j) {
+        const int jr = 16 * j + lr;
+        ar[j] = a.lora_a + (int64_t)(jr < a.r ? jr : a.r - 1) * a.k;  // ranks past r: zeroed below
+    }
+    f32x4_t acc[JT];
+#pragma unroll
+    for (int j = 0; j < JT; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t k0 = 32 * wave; k0 < a.k; k0 += 128 * U) {
+        uint4 xv[U], av[U][JT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t kk = k0 + 128 * u + 8 * lq;
+            const bool in = kk < a.k;  // k % 16 == 0: an 8-element piece is inside or outside
+            const int64_t kc = in ? kk : 0;
+            xv[u] = *reinterpret_cast<const uint4 *>(xr + kc);
+#pragma unroll
+            for (int j = 0; j < JT; ++j) av[u][j] = *reinterpret_cast<const uint4 *>(ar[j] + kc);
+            if (!in) {  // past k: zeros on both sides (kc = 0 only keeps the loads in bounds)
+                xv[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < JT; ++j) av[u][j] = make_uint4(0, 0, 0, 0);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            acc[u] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u].x), as_bf16x2(av[u].x), acc[u], false);
-            acc[u] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u].y), as_bf16x2(av[u].y), acc[u], false);
-            acc[u] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u].z), as_bf16x2(av[u].z), acc[u], false);
-            acc[u] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv[u].w), as_bf16x2(av[u].w), acc[u], false);
+        for (int u = 0; u < U; ++u) {
+            bf16x8_t xb;
+            __builtin_memcpy(&xb, &xv[u], 16);
+#pragma unroll
+            for (int j = 0; j < JT; ++j) {
+                uint4 av_in = 16 * j + lr < a.r ? av[u][j] : make_uint4(0, 0, 0, 0);
+                bf16x8_t ab;
+                __builtin_memcpy(&ab, &av_in, 16);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, ab, acc[j], 0, 0, 0);
+            }
         }
     }
-    for (; kk < a.k; kk += step) {  // k % 16 == 0: a vector never straddles the end
-        const uint4 xv = *reinterpret_cast<const uint4 *>(xr + kk);
-        const uint4 av = *reinterpret_cast<const uint4 *>(ar + kk);
-        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.x), as_bf16x2(av.x), acc[0], false);
-        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.y), as_bf16x2(av.y), acc[0], false);
-        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.z), as_bf16x2(av.z), acc[0], false);
-        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(xv.w), as_bf16x2(av.w), acc[0], false);
-    }
-    __shared__ float red[4];
-    const float t = block_sum_256((acc[0] + acc[1]) + (acc[2] + acc[3]), red);
-    if (threadIdx.x == 0) {
-        const float u = t * (a.lora_scale / *a.tensor_scale);
-        const uint16_t hi = f32_to_bf16_bits(u);
-        const uint16_t lo = f32_to_bf16_bits(u - __uint_as_float((uint32_t)hi << 16));
-        uint16_t *t16 = g.t16();
-        t16[m * 2 * a.r + j] = hi;
-        t16[m * 2 * a.r + a.r + j] = lo;
+#pragma unroll
+    for (int j = 0; j < JT; ++j) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    if (wave != 0) return;
+    const float mul = a.lora_scale / *a.tensor_scale;
+    uint16_t *t16 = g.t16();
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
+        const f32x4_t t = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
+        const int jr = 16 * j + lr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + 4 * lq + v;
+            if (m >= a.m || jr >= a.r) continue;
+            const float u = t[v] * mul;
+            const uint16_t hi = f32_to_bf16_bits(u);
+            t16[m * 2 * a.r + jr] = hi;
+            t16[m * 2 * a.r + a.r + jr] = f32_to_bf16_bits(u - __uint_as_float((uint32_t)hi << 16));
+        }
     }
 }
 
@@ -219,9 +250,16 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
     if (a.m <= kDecodeMaxM) return launch_decode(a, stream);
     const Gemm g{a, make_plan(a.m, a.n, a.k, a.r)};
     if (a.r > 0) {
-        const int64_t grid = a.m * a.r;
-        if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(prologue_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, g);
+        const dim3 pgrid((unsigned)((a.m + 15) / 16));
+        const int jt = (a.r + 15) / 16;
+        if (jt <= 1)
+            hipLaunchKernelGGL(prologue_kernel<1>, pgrid, dim3(kThreads), 0, stream, g);
+        else if (jt <= 2)
+            hipLaunchKernelGGL(prologue_kernel<2>, pgrid, dim3(kThreads), 0, stream, g);
+        else if (jt <= 4)
+            hipLaunchKernelGGL(prologue_kernel<4>, pgrid, dim3(kThreads), 0, stream, g);
+        else
+            hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(kThreads), 0, stream, g);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
