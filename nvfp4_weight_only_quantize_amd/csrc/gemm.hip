@@ -18,7 +18,8 @@
 //   prefill_kernel   128 x 256 output tiles over the K loops of mfma_tile.h
 //                    (x by LDS DMA, weights decoded to exact BF16 in
 //                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
-//                    s_t applied once.
+//                    s_t applied once.  Grids of few tiles split K; then
+//   reduce_kernel    sums the FP32 partial outputs in split order.
 #include "device_common.h"
 #include "mfma_tile.h"
 #include "qerl_internal.h"
@@ -32,19 +33,35 @@ constexpr int kThreads = 256;
 // Launch plan and workspace layout
 // ---------------------------------------------------------------------------
 // The workspace starts with the decode path's counter region, which this path
-// never touches, then holds the BF16 hi/lo t [m, 2r].
+// never touches, then holds the BF16 hi/lo t [m, 2r] and, when K is split,
+// the FP32 partial outputs [splits][m][n].
+constexpr int PBM = 128, PBN = 256;   // output tile: rows of x x weight rows
+constexpr int64_t kSplitTiles = 256;  // below this many tiles (fewer than CUs) K is split
+constexpr int64_t kMaxSplits = 16;
+
 struct Plan {
-    int64_t t_off, bytes;
+    int64_t tiles, splits, bps;  // output tiles, K splits, 128-column blocks per split
+    int64_t t_off, part_off, bytes;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
 Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
-    (void)n;
-    (void)k;
     Plan p{};
+    p.tiles = ((m + PBM - 1) / PBM) * ((n + PBN - 1) / PBN);
+    const int64_t blocks = k / 128;
+    p.splits = 1;
+    if (p.tiles < kSplitTiles && blocks >= 8) {
+        int64_t s = (2 * 256 + p.tiles - 1) / p.tiles;  // toward two workgroups per CU
+        if (s > blocks / 4) s = blocks / 4;              // at least four blocks per split
+        if (s > kMaxSplits) s = kMaxSplits;
+        if (s > 1) p.splits = s;
+    }
+    p.bps = (blocks + p.splits - 1) / p.splits;
+    if (p.splits > 1) p.splits = (blocks + p.bps - 1) / p.bps;  // no empty split
     p.t_off = kGemmCtrBytes;
-    p.bytes = p.t_off + align256(m * (int64_t)r * 4);
+    p.part_off = align256(p.t_off + m * (int64_t)r * 4);
+    p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * m * n * 4) : 0);
     return p;
 }
 
@@ -52,6 +69,7 @@ struct Gemm {
     GemmArgs a;
     Plan p;
     __device__ uint16_t *t16() const { return reinterpret_cast<uint16_t *>(static_cast<char *>(a.workspace) + p.t_off); }
+    __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
 };
 
 // ---------------------------------------------------------------------------
@@ -143,7 +161,6 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
 // twice.  The main K loop is mfma_kloop (mfma_tile.h); what is left of K past
 // the last full 128-column block, and the LoRA product as 2r extra K columns
 // (t hi/lo x B twice), go through plain_kloop.
-constexpr int PBM = 128, PBN = 256;
 constexpr int kXTileBytes = PBM * kTileRowBytes;
 #ifndef QERL_GROUP_M
 #define QERL_GROUP_M 4
@@ -195,6 +212,7 @@ __device__ __forceinline__ bf16x8_t w_frag_ext(const GemmArgs &a, int64_t n, int
     return v;
 }
 
+template <bool SPLIT>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
     const GemmArgs &a = g.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -204,7 +222,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
     // a time share kGroupM x slabs and a few weight slabs in its L2 rather
     // than one x slab and dozens of weight slabs.
     const int64_t tiles_n = (a.n + PBN - 1) / PBN, tiles_m = (a.m + PBM - 1) / PBM, tiles = tiles_n * tiles_m;
-    const int64_t b = blockIdx.x, x8 = b % 8, q8 = tiles / 8, r8 = tiles % 8;
+    const int64_t split = SPLIT ? (int64_t)blockIdx.x / tiles : 0;  // K split: blocks [split bps, +bps)
+    const int64_t b = (int64_t)blockIdx.x - split * tiles, x8 = b % 8, q8 = tiles / 8, r8 = tiles % 8;
     const int64_t tile = x8 * q8 + (x8 < r8 ? x8 : r8) + b / 8;
     const int64_t grp = tile / (kGroupM * tiles_n), in_grp = tile % (kGroupM * tiles_n);
     const int64_t gm = tiles_m - grp * kGroupM < kGroupM ? tiles_m - grp * kGroupM : kGroupM;  // rows in this group
@@ -217,15 +236,36 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+    const Plan &p = g.p;
+    const bool last = !SPLIT || split == p.splits - 1;
     const int64_t blocks = a.ldx <= kTileMaxLdx ? a.k / kTileK : 0;
+    const int64_t kb0 = !SPLIT ? 0 : (split * p.bps < blocks ? split * p.bps : blocks);
+    const int64_t kb1 = last ? blocks : (kb0 + p.bps < blocks ? kb0 + p.bps : blocks);
     mfma_kloop<8>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1), a.scales + n0 * (a.k >> 4),
-                  a.n - n0, a.k, 0, blocks, g_xtile0, g_xtile1, acc);
+                  a.n - n0, a.k, kb0, kb1, g_xtile0, g_xtile1, acc);
+    // the last split: the rest of K (and all of it for very wide x rows), then
+    // the LoRA columns
     const int64_t nw = n0 + wave * 64 + lr;
-    plain_kloop<8>(
-        blocks * kTileK, a.k + klora, g_xtile0,
-        [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora); },
-        [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
+    if (last)
+        plain_kloop<8>(
+            blocks * kTileK, a.k + klora, g_xtile0,
+            [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora); },
+            [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
 
+    if (SPLIT) {  // FP32 partial outputs; reduce_kernel finishes
+        float *part = g.part() + split * a.m * a.n;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int64_t m = m0 + 16 * i + 4 * lq + v;
+                    const int64_t n = n0 + wave * 64 + 16 * j + lr;
+                    if (m < a.m && n < a.n) part[m * a.n + n] = acc[i][j][v];
+                }
+        return;
+    }
     const float st_scale = *a.tensor_scale;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -237,6 +277,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
                 const int64_t n = n0 + wave * 64 + 16 * j + lr;
                 if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st_scale * acc[i][j][v]);
             }
+}
+
+template __global__ void prefill_kernel<false>(Gemm);
+template __global__ void prefill_kernel<true>(Gemm);
+
+// y[m, n] = bf16(s_t * sum over splits of the partial outputs, in split order)
+__global__ __launch_bounds__(kThreads) void reduce_kernel(Gemm g) {
+    const GemmArgs &a = g.a;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= a.m * a.n) return;
+    const int64_t m = i / a.n, n = i - m * a.n;
+    const float *part = g.part();
+    const int64_t plane = a.m * a.n;
+    float v[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) v[s] = s < g.p.splits ? part[s * plane + i] : 0.0f;
+    float acc = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s)
+        if (s < g.p.splits) acc += v[s];
+    a.y[m * a.ldy + n] = f32_to_bf16_bits(*a.tensor_scale * acc);
 }
 
 }  // namespace
@@ -263,9 +324,17 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t tiles = ((a.n + PBN - 1) / PBN) * ((a.m + PBM - 1) / PBM);
-    if (tiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, g);
+    const int64_t grid = g.p.tiles * g.p.splits;
+    if (grid > 0x7FFFFFFF || a.m * a.n > 0x7FFFFFFFll * kThreads) return hipErrorInvalidConfiguration;
+    if (g.p.splits == 1) {
+        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, g);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((a.m * a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, g);
     return hipGetLastError();
 }
 
