@@ -50,7 +50,7 @@ def _x(m, k, seed, outliers=0.005):
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16, 17, 24, 32, 33, 64, 100, 256])
 @pytest.mark.parametrize("nkr", [(96, 256, 16), (77, 512, 32), (130, 1024, 8), (64, 48, 4),
                                  (33, 80, 0), (200, 2048, 64), (5, 128, 4), (300, 1040, 24),
-                                 (1000, 3600, 32)])
+                                 (1000, 3600, 32), (256, 1024, 128)])
 def test_small_shapes(m, nkr):
     n, k, r = nkr
     L = Layer(n, k, r, seed=100 + n + k + r)
