@@ -24,14 +24,16 @@
 //    in-order wait counts exact; LDS reads are counted apart from them.
 //  * LoRA: "producer" workgroups at the head of the grid compute partial sums
 //    of t = x A^T over slices of K (MFMA) and publish them with device-coherent
-//    stores.
+//    stores; the last producer to finish sums them in producer order and
+//    publishes t once, as BF16 hi + lo halves (relative error ~2^-16) in the
+//    layout the epilogue multiplies, behind a ready flag.
 //  * Every unit but the last of its row block stores its FP32 partial tile
-//    (coherent stores) and bumps a counter; the last to arrive sums all
-//    partials in slice order (deterministic), waits until the producers have
-//    all published (they are dispatched before every consumer, so the wait is
-//    short; it is bounded all the same), sums their t partials in producer
-//    order, and adds lora_scale * t B^T on the MFMA with t split into BF16 hi +
-//    lo halves (relative error ~2^-16).
+//    (coherent stores) and bumps a counter.  The last to arrive (every unit,
+//    when K is not split) loads all partial tiles and t in one batch -- the
+//    ready flag was read while its last chunks multiplied, so as a rule no
+//    round trip of its own is spent on t (the wait for it is bounded all the
+//    same) -- sums the partials in slice order (deterministic), and adds
+//    lora_scale * t B^T on the MFMA.
 //
 // 16 < m <= 64, mfma_unit_kernel + finish_kernel, two launches.  Units are
 // (256 weight rows) x (slice of K) running the K loops of mfma_tile.h with all
@@ -64,10 +66,17 @@ constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr int64_t kTargetUnits = 256;
+#ifndef QERL_TARGET_UNITS
+#define QERL_TARGET_UNITS 256
+#endif
+constexpr int64_t kTargetUnits = QERL_TARGET_UNITS;
+#ifndef QERL_RING
+#define QERL_RING 4
+#endif
+constexpr int kRing = QERL_RING;  // weight chunks in flight per wave (m <= 16)
 
 // counter words at the head of the workspace
-constexpr int kCtrProd = 0, kCtrDone = 2, kCtrRow = 4;
+constexpr int kCtrProd = 0, kCtrTReady = 1, kCtrDone = 2, kCtrRow = 4;
 constexpr int64_t kMaxRowBlocks = kGemmCtrBytes / 4 - kCtrRow;
 
 struct DecodePlan {
@@ -134,7 +143,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.sc_pitch = scp * 16;
     p.sc_lds_off = (x_bytes + 15) / 16 * 16;
     int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
-    const int64_t epi = 16 * p.rp * 2 * 2;  // t hi/lo in the one-launch epilogue
+    const int64_t epi = 16 * p.rp * 2 * 2;  // t16 in the one-launch epilogue
     const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16;  // producer wave reduction
     if (lds < epi) lds = epi;
     if (lds < prod) lds = prod;
@@ -143,7 +152,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.part_off = kGemmCtrBytes;
     p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
     p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
-    p.bytes = align256(p.t_off + m * (int64_t)r * 4);
+    p.bytes = align256(p.t_off + 2 * 16 * p.rp * 2);  // t16: BF16 hi/lo [2][16][rp]
     return p;
 }
 
@@ -166,6 +175,12 @@ __device__ __forceinline__ void store_f4_coherent(__amdgpu_buffer_rsrc_t r, int 
     i32x4_t b;
     __builtin_memcpy(&b, &v, 16);
     __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, kSc1);
+}
+__device__ __forceinline__ void store_u16_coherent(__amdgpu_buffer_rsrc_t r, int off, uint16_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kSc1);
+}
+__device__ __forceinline__ i32x4_t load_i4_coherent(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
 }
 __device__ __forceinline__ f32x4_t load_f4_coherent(__amdgpu_buffer_rsrc_t r, int off) {
     const i32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
@@ -286,9 +301,14 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     __syncthreads();
     if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
     __syncthreads();
-    if (MT == 1 || !s_last) return;  // m <= 16: the consumers sum the partials
-    // 16 < m: the last producer sums the partials in producer order into t [m, r];
-    // tile i goes to wave i % 4, kBatch producers in flight
+    if (!s_last) return;
+    if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);  // every producer has counted
+    // The last producer sums the partials in producer order (tile i goes to
+    // wave i % 4, kBatch producers in flight).  16 < m: into t [m, r] in FP32,
+    // read after the kernel boundary.  m <= 16: into t16 [2][16][rp], the BF16
+    // hi and lo halves of t in the layout the consumers' epilogue multiplies,
+    // published to this launch's consumers by the ready flag.
+    const __amdgpu_buffer_rsrc_t rt = coherent_rsrc(d.t32());
     for (int i = wave; wave < kWaves && i < MT * JT; i += kWaves) {
         f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         for (int64_t q0 = 0; q0 < d.p.producers; q0 += kBatch) {
@@ -307,10 +327,28 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int64_t m = 16 * mt + 4 * lq + v;
-            if (m < a.m && j < a.r) d.t32()[m * a.r + j] = sum[v];
+            if (MT == 1) {  // all 16 rows (rows past m repeat row m - 1 and are never output)
+                const uint16_t hi = f32_to_bf16_bits(sum[v]);
+                const int off = (int)((m * d.p.rp + j) * 2);
+                store_u16_coherent(rt, off, hi);
+                store_u16_coherent(rt, off + (int)(16 * d.p.rp * 2),
+                                   f32_to_bf16_bits(sum[v] - __uint_as_float((uint32_t)hi << 16)));
+            } else if (m < a.m && j < a.r) {
+                d.t32()[m * a.r + j] = sum[v];
+            }
         }
     }
-    if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);
+    if (MT == 1) {
+        // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
+        const int pad = (int)(d.p.rp - 16 * JT);
+        for (int i = tid; i < 2 * 16 * pad; i += kThreadsD) {
+            const int h = i / (16 * pad), m = (i / pad) % 16, j = 16 * JT + i % pad;
+            store_u16_coherent(rt, (int)(((h * 16 + m) * d.p.rp + j) * 2), 0);
+        }
+        wait_vm();
+        __syncthreads();
+        if (tid == 0) ctr_store(d.ctr() + kCtrTReady, 1u);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -361,40 +399,46 @@ __device__ __forceinline__ void load_chunk_tail(const GemmArgs &a, int64_t n0, i
     }
 }
 
-// Copy `total` items from global to LDS, kBatch per thread in flight: a plain
-// loop would wait for every load before issuing the next.
+// Copy a rows x per_row grid of items from global to LDS, kBatch per thread
+// in flight (a plain loop would wait for every load before issuing the next).
+// Item i = thread + kThreadsD * step is (i / per_row, i % per_row); the pair
+// is advanced by the block's stride instead of dividing per item, in 32 bits.
 template <typename T, typename Src, typename Dst>
-__device__ __forceinline__ void batched_copy(int64_t total, Src src, Dst dst) {
-    for (int64_t base = threadIdx.x; base < total; base += kBatch * kThreadsD) {
+__device__ __forceinline__ void batched_copy_2d(int rows, int per_row, Src src, Dst dst) {
+    const int total = rows * per_row;
+    const int dr = kThreadsD / per_row, dc = kThreadsD - dr * per_row;
+    int r = (int)threadIdx.x / per_row, c = (int)threadIdx.x - r * per_row;
+    for (int base = threadIdx.x; base < total; base += kBatch * kThreadsD) {
         T v[kBatch];
+        int rr[kBatch], cc[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int64_t i = base + (int64_t)u * kThreadsD;
-            if (i < total) v[u] = src(i);
+            rr[u] = r;
+            cc[u] = c;
+            if (base + u * kThreadsD < total) v[u] = src(r, c);
+            r += dr;
+            c += dc;
+            if (c >= per_row) {
+                c -= per_row;
+                ++r;
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t i = base + (int64_t)u * kThreadsD;
-            if (i < total) dst(i, v[u]);
-        }
+        for (int u = 0; u < kBatch; ++u)
+            if (base + u * kThreadsD < total) dst(rr[u], cc[u], v[u]);
     }
 }
 
 // The unit's x slice, rows [0, m) x columns [k0, k0 + width), into LDS rows
 // of `pitch` elements; columns at or past k are zero.
 __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
-    const int64_t per_row = width / 8;
-    batched_copy<uint4>(
-        a.m * per_row,
-        [&](int64_t i) {
-            const int64_t m = i / per_row, col = (i - m * per_row) * 8;
-            return k0 + col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + k0 + col)
-                                  : make_uint4(0, 0, 0, 0);
+    batched_copy_2d<uint4>(
+        (int)a.m, (int)(width / 8),
+        [&](int m, int pc) {
+            const int64_t col = k0 + 8 * pc;
+            return col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col) : make_uint4(0, 0, 0, 0);
         },
-        [&](int64_t i, const uint4 &v) {
-            const int64_t m = i / per_row, col = (i - m * per_row) * 8;
-            *reinterpret_cast<uint4 *>(xs + m * pitch + col) = v;
-        });
+        [&](int m, int pc, const uint4 &v) { *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = v; });
 }
 
 // Stage the unit's scale bytes: rows [n0, n0 + R) x bytes [b0, b0 + nb) of
@@ -402,43 +446,26 @@ __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, in
 __device__ void stage_scales(const GemmArgs &a, uint8_t *sc, int64_t pitch, int64_t n0, int64_t R, int64_t b0,
                              int64_t nb) {
     const int64_t row_bytes = a.k >> 4;
-    auto row_of = [&](int64_t rr) { return n0 + rr < a.n ? n0 + rr : a.n - 1; };
+    auto row_of = [&](int rr) { return n0 + rr < a.n ? n0 + rr : a.n - 1; };
     if (row_bytes % 16 == 0 && b0 % 16 == 0) {
         // 16-byte pieces; the last may run past nb but not past the row
-        const int64_t pr = (nb + 15) / 16;
-        batched_copy<uint4>(
-            R * pr,
-            [&](int64_t i) {
-                const int64_t rr = i / pr, pc = i - rr * pr;
+        batched_copy_2d<uint4>(
+            (int)R, (int)((nb + 15) / 16),
+            [&](int rr, int pc) {
                 return *reinterpret_cast<const uint4 *>(a.scales + row_of(rr) * row_bytes + b0 + 16 * pc);
             },
-            [&](int64_t i, const uint4 &v) {
-                const int64_t rr = i / pr, pc = i - rr * pr;
-                *reinterpret_cast<uint4 *>(sc + rr * pitch + 16 * pc) = v;
-            });
+            [&](int rr, int pc, const uint4 &v) { *reinterpret_cast<uint4 *>(sc + rr * pitch + 16 * pc) = v; });
     } else if (row_bytes % 4 == 0) {  // b0 is a multiple of 8
-        const int64_t pr = (nb + 3) / 4;
-        batched_copy<uint32_t>(
-            R * pr,
-            [&](int64_t i) {
-                const int64_t rr = i / pr, pc = i - rr * pr;
+        batched_copy_2d<uint32_t>(
+            (int)R, (int)((nb + 3) / 4),
+            [&](int rr, int pc) {
                 return *reinterpret_cast<const uint32_t *>(a.scales + row_of(rr) * row_bytes + b0 + 4 * pc);
             },
-            [&](int64_t i, const uint32_t &v) {
-                const int64_t rr = i / pr, pc = i - rr * pr;
-                *reinterpret_cast<uint32_t *>(sc + rr * pitch + 4 * pc) = v;
-            });
+            [&](int rr, int pc, const uint32_t &v) { *reinterpret_cast<uint32_t *>(sc + rr * pitch + 4 * pc) = v; });
     } else {
-        batched_copy<uint8_t>(
-            R * nb,
-            [&](int64_t i) {
-                const int64_t rr = i / nb, pc = i - rr * nb;
-                return a.scales[row_of(rr) * row_bytes + b0 + pc];
-            },
-            [&](int64_t i, const uint8_t &v) {
-                const int64_t rr = i / nb, pc = i - rr * nb;
-                sc[rr * pitch + pc] = v;
-            });
+        batched_copy_2d<uint8_t>(
+            (int)R, (int)nb, [&](int rr, int pc) { return a.scales[row_of(rr) * row_bytes + b0 + pc]; },
+            [&](int rr, int pc, const uint8_t &v) { sc[rr * pitch + pc] = v; });
     }
 }
 
@@ -475,13 +502,15 @@ __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *s
     }
 }
 
-template <int MT, int NW, int PX, bool K32>
+// K32: k % 32 == 0; SPLIT: K is split over several units per row block
+// (slices > 1); LORA: r > 0.
+template <bool K32, bool SPLIT, bool LORA>
 __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
-    static_assert(MT == 1 && NW == 1, "m <= 16 only; 16 < m runs mfma_unit_kernel");
+    constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    if ((int64_t)blockIdx.x < p.producers) {
+    if (LORA && (int64_t)blockIdx.x < p.producers) {
         lora_producer<MT>(d, blockIdx.x, lds);
         return;
     }
@@ -513,7 +542,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     const int64_t sb1 = c_end * 8 < (a.k >> 4) ? c_end * 8 : (a.k >> 4);
     // ---- x and scales of the whole unit resident in LDS; the weights
     // stream through a ring of DR chunks with no barrier ----
-    constexpr int DR = 4;
+    constexpr int DR = kRing;
     uint4 w[DR][NW];
     if (c_full_end > c_begin) {
 #pragma unroll
@@ -523,8 +552,9 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     stage_x_slice(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
     stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
     if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
-        const int64_t z0 = (a.k >> 4) - sb0, zn = p.full_chunks * 8 + 8 - (a.k >> 4);
-        for (int64_t i = tid; i < R * zn; i += kThreadsD) sc[(i / zn) * p.sc_pitch + z0 + i % zn] = 0;
+        const int z0 = (int)((a.k >> 4) - sb0), zn = (int)(p.full_chunks * 8 + 8 - (a.k >> 4));  // zn < 8
+        for (int rr = tid >> 3; rr < R; rr += kThreadsD / 8)
+            if ((tid & 7) < zn) sc[rr * p.sc_pitch + z0 + (tid & 7)] = 0;
     }
     __syncthreads();
     int64_t c = c_begin;
@@ -547,6 +577,11 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         }
         c += DR;
     }
+    // Whether t is published, read while the last chunks multiply: the
+    // producers lead the grid and are done by now as a rule, so t can be
+    // loaded without a round trip of its own.
+    uint32_t t_seen = 0;
+    if (LORA && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
 #pragma unroll
     for (int s = 0; s < DR; ++s)
         if (c + s < c_full_end)  // uniform
@@ -558,50 +593,8 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
                           m_last, lr, lq, acc);
     }
-    const int64_t tile_floats = R * 16 * MT;
-    const int wave_off = wave * MT * NW * 64;  // f32x4 slots before this wave's in a tile
-    // ---- m <= 16, split K: the last unit of the row block to arrive sums the slices ----
-    __shared__ uint32_t s_flag;
-    if (p.slices > 1) {
-        {
-            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + u * tile_floats);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int g = 0; g < NW; ++g)
-                    if (16 * mt + 4 * lq < a.m)
-                        store_f4_coherent(rs, (wave_off + (mt * NW + g) * 64 + lane) * 16, acc[mt][g]);
-            wait_vm();
-        }
-        __syncthreads();
-        if (tid == 0) s_flag = ctr_add(d.ctr() + kCtrRow + rblk, 1u) == (uint32_t)(p.slices - 1);
-        __syncthreads();
-        if (!s_flag) return;
-        // every slice (this one included) from the partials, in slice order
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int g = 0; g < NW; ++g) acc[mt][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        if (4 * lq < a.m) {  // MT == 1 here: one tile per lane, kBatch slices in flight
-            for (int64_t s0 = 0; s0 < p.slices; s0 += kBatch) {
-                f32x4_t v[kBatch];
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int64_t s = s0 + u < p.slices ? s0 + u : p.slices - 1;
-                    v[u] = load_f4_coherent(coherent_rsrc(d.part() + (s * p.row_blocks + rblk) * tile_floats),
-                                            (wave_off + lane) * 16);
-                }
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u)
-                    if (s0 + u < p.slices) acc[0][0] = acc[0][0] + v[u];
-            }
-        }
-        if (tid == 0) ctr_store(d.ctr() + kCtrRow + rblk, 0u);
-    }
-
-    // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
-    uint16_t *th = reinterpret_cast<uint16_t *>(lds);
-    uint16_t *tl = th + 16 * MT * p.rp;
+    const int64_t tile_floats = R * 16;
+    const int wave_off = wave * 64;  // f32x4 slots before this wave's in a tile
     // B [n, j] for this lane's rows and ranks 8 lq .. 8 lq + 7 of the block jb
     auto load_b = [&](int g, int64_t jb) -> bf16x8_t {
         int64_t nb = n0 + 16 * g + lr;
@@ -619,55 +612,90 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         }
         return as_bf16x8_d(v);
     };
-    bf16x8_t b0[NW];  // the first rank block, loaded before the wait for t
-    if (a.r > 0)
+    bf16x8_t b0[NW];  // the first rank block (read-only input: loaded early)
+    if (LORA)
 #pragma unroll
         for (int g = 0; g < NW; ++g) b0[g] = load_b(g, 0);
-    if (a.r > 0) {
-        __syncthreads();  // the LDS is reused below
+    __shared__ uint32_t s_flag, s_ready;
+    // ---- split K: the last unit of the row block to arrive sums the slices ----
+    if (SPLIT) {
+        {
+            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + u * tile_floats);
+            if (4 * lq < a.m) store_f4_coherent(rs, (wave_off + lane) * 16, acc[0][0]);
+            wait_vm();
+        }
+        if (tid == 0) s_ready = t_seen;
+        __syncthreads();
+        if (tid == 0) s_flag = ctr_add(d.ctr() + kCtrRow + rblk, 1u) == (uint32_t)(p.slices - 1);
+        __syncthreads();
+        if (!s_flag) return;
+        if (tid == 0) ctr_store(d.ctr() + kCtrRow + rblk, 0u);
+    } else {
+        if (tid == 0) s_ready = t_seen;
+        __syncthreads();
+    }
+    if (LORA && !s_ready) {  // uniform; rare: wait for the last producer
         if (tid == 0) {
             uint32_t it = 0;
-            while (ctr_load(d.ctr() + kCtrProd) < (uint32_t)p.producers && ++it < kSpinLimit)
-                __builtin_amdgcn_s_sleep(2);
+            while (ctr_load(d.ctr() + kCtrTReady) == 0 && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
         }
         __syncthreads();
-        // t = the producers' partials summed in producer order; wave w takes
-        // the tiles i = w, w + 4, ... and writes them as BF16 hi/lo [m][j]
-        const int JT = (int)p.jt;
-        const int64_t ptile = (int64_t)MT * JT * 64 * 4;
-        for (int i = wave; i < MT * JT; i += kWaves) {
-            f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t q0 = 0; q0 < p.producers; q0 += kBatch) {  // kBatch producers in flight, summed in order
-                f32x4_t v[kBatch];
+    }
+    // The slices' partial tiles and t16 are loaded together (one round trip
+    // in the usual case; more than kRedP slices take more), then summed in
+    // slice order; t16 goes to LDS as it is.
+    constexpr int kRedP = 12;
+    auto part_at = [&](int64_t sl) { return coherent_rsrc(d.part() + (sl * p.row_blocks + rblk) * tile_floats); };
+    const int t_pieces = (int)(16 * p.rp * 2 * 2 / 16);  // 16-byte pieces of t16 (<= 512)
+    // Every load is issued unconditionally; the buffer resources end where
+    // the data does, so a load past the slices or past t16 returns zeros
+    // without a memory access (and with no branch for the compiler to fold
+    // the sums into).
+    f32x4_t pv[kRedP];
+    i32x4_t tq[2];
+    if (SPLIT) {
+        const int64_t sstride = p.row_blocks * tile_floats * 4;  // bytes between slices of a row block
+        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+            d.part() + rblk * tile_floats, 0, (int)(sstride * (p.slices < kRedP ? p.slices : kRedP)), 0x00020000);
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u) {
-                    const int64_t q = q0 + u < p.producers ? q0 + u : p.producers - 1;
-                    v[u] = load_f4_coherent(coherent_rsrc(d.tpart() + q * ptile), (i * 64 + lane) * 16);
-                }
+        for (int v = 0; v < kRedP; ++v)
+            pv[v] = load_f4_coherent(rp, (int)(v * sstride) + (wave_off + lane) * 16);
+    }
+    if (LORA) {
+        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(d.t32(), 0, t_pieces * 16, 0x00020000);
+        tq[0] = load_i4_coherent(rt, tid * 16);
+        tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
+    }
+    // The values are taken here, after every load has been issued: without
+    // this the compiler folds the sums below into the conditional loads and
+    // waits for each load before issuing the next.
+    if (SPLIT)
 #pragma unroll
-                for (int u = 0; u < kBatch; ++u)
-                    if (q0 + u < p.producers) sum = sum + v[u];
+        for (int v = 0; v < kRedP; ++v) asm volatile("" : "+v"(pv[v]));
+    if (LORA) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
+    if (SPLIT) {
+        acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int v = 0; v < kRedP; ++v) acc[0][0] = acc[0][0] + pv[v];  // zeros past the slices
+        for (int64_t s0 = kRedP; s0 < p.slices; s0 += kRedP) {
+#pragma unroll
+            for (int v = 0; v < kRedP; ++v) {
+                const int64_t sl = s0 + v < p.slices ? s0 + v : p.slices - 1;
+                pv[v] = load_f4_coherent(part_at(sl), (wave_off + lane) * 16);
             }
-            const int mt = i / JT, jt = i - mt * JT;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t off = (16 * mt + 4 * lq + v) * p.rp + 16 * jt + lr;
-                const uint16_t hi = f32_to_bf16_bits(sum[v]);
-                th[off] = hi;
-                tl[off] = f32_to_bf16_bits(sum[v] - __uint_as_float((uint32_t)hi << 16));
-            }
+            for (int v = 0; v < kRedP; ++v)
+                if (s0 + v < p.slices) acc[0][0] = acc[0][0] + pv[v];
         }
-        // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
-        for (int64_t i = tid; i < 16 * MT * (p.rp - 16 * JT); i += kThreadsD) {
-            const int64_t m = i / (p.rp - 16 * JT), j = 16 * JT + i % (p.rp - 16 * JT);
-            th[m * p.rp + j] = 0;
-            tl[m * p.rp + j] = 0;
-        }
+    }
+
+    // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
+    uint16_t *th = reinterpret_cast<uint16_t *>(lds);  // t16 [2][16][rp]: hi, then lo
+    uint16_t *tl = th + 16 * p.rp;
+    if (LORA) {  // (the pieces past t16 were loaded as zeros and are not stored)
+        if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
+        if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
         __syncthreads();
-        if (tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
-            ctr_store(d.ctr() + kCtrProd, 0u);
-            ctr_store(d.ctr() + kCtrDone, 0u);
-        }
     }
     const float st = *a.tensor_scale, lam = a.lora_scale;
 #pragma unroll
@@ -690,6 +718,12 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
                 if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[mt][g][v] + lam * l[v]);
             }
         }
+    }
+    // this row block is done with t16; the last one clears the ready flag
+    // and this count for the next call
+    if (LORA && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
+        ctr_store(d.ctr() + kCtrTReady, 0u);
+        ctr_store(d.ctr() + kCtrDone, 0u);
     }
 }
 
@@ -841,15 +875,22 @@ hipError_t launch_mfma_units(const Decode &d, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <bool K32>
+template <bool K32, bool SPLIT, bool LORA>
 hipError_t launch_stream(const Decode &d, hipStream_t stream) {
-    auto kern = stream_kernel<1, 1, 1, K32>;
+    auto kern = stream_kernel<K32, SPLIT, LORA>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
     const int64_t grid = d.p.producers + d.p.units;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsD), (size_t)d.p.lds_bytes, stream, d);
     return hipGetLastError();
+}
+
+template <bool K32>
+hipError_t launch_stream(const Decode &d, hipStream_t stream) {
+    const bool split = d.p.slices > 1, lora = d.a.r > 0;
+    if (split) return lora ? launch_stream<K32, true, true>(d, stream) : launch_stream<K32, true, false>(d, stream);
+    return lora ? launch_stream<K32, false, true>(d, stream) : launch_stream<K32, false, false>(d, stream);
 }
 
 }  // namespace

@@ -167,21 +167,40 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
         if (s + 1 < b1) dma_x(nxt, s + 1);  // uniform
         load_w(wl, s + WD < b1 ? s + WD : b1 - 1);
         if (s < b1) {  // uniform
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            // step t's MFMAs are issued interleaved with the decode of step
+            // t+1: one wave issues in order, so a decode placed wholly before
+            // or after a run of MFMAs would leave one of the two pipes idle
+            auto decode_step = [&](int t, bf16x8_t &d0, bf16x8_t &d1, bf16x8_t &d2, bf16x8_t &d3) {
                 const bool hi = t >= 2;  // scale byte 1 covers the last 16 of the lane's 32 columns
                 const float f0 = hi ? QERL_E4M3_F32(wc.c0, 1) : QERL_E4M3_F32(wc.c0, 0);
                 const float f1 = hi ? QERL_E4M3_F32(wc.c1, 1) : QERL_E4M3_F32(wc.c1, 0);
                 const float f2 = hi ? QERL_E4M3_F32(wc.c2, 1) : QERL_E4M3_F32(wc.c2, 0);
                 const float f3 = hi ? QERL_E4M3_F32(wc.c3, 1) : QERL_E4M3_F32(wc.c3, 0);
-                const uint32_t w0 = t == 0 ? wc.q0.x : t == 1 ? wc.q0.y : t == 2 ? wc.q0.z : wc.q0.w;
-                const uint32_t w1 = t == 0 ? wc.q1.x : t == 1 ? wc.q1.y : t == 2 ? wc.q1.z : wc.q1.w;
-                const uint32_t w2 = t == 0 ? wc.q2.x : t == 1 ? wc.q2.y : t == 2 ? wc.q2.z : wc.q2.w;
-                const uint32_t w3 = t == 0 ? wc.q3.x : t == 1 ? wc.q3.y : t == 2 ? wc.q3.z : wc.q3.w;
-                mfma_step<MTW>(cur + aoff[t], kTileRowBytes, dequant8_p(w0, f0), dequant8_p(w1, f1),
-                               dequant8_p(w2, f2), dequant8_p(w3, f3), acc);
-                // keep each step's decode next to its MFMAs (hoisting them all
-                // raises register use past the budget)
+                d0 = dequant8_p(t == 0 ? wc.q0.x : t == 1 ? wc.q0.y : t == 2 ? wc.q0.z : wc.q0.w, f0);
+                d1 = dequant8_p(t == 0 ? wc.q1.x : t == 1 ? wc.q1.y : t == 2 ? wc.q1.z : wc.q1.w, f1);
+                d2 = dequant8_p(t == 0 ? wc.q2.x : t == 1 ? wc.q2.y : t == 2 ? wc.q2.z : wc.q2.w, f2);
+                d3 = dequant8_p(t == 0 ? wc.q3.x : t == 1 ? wc.q3.y : t == 2 ? wc.q3.z : wc.q3.w, f3);
+            };
+            constexpr int kMf = 4 * MTW;                  // MFMAs per step
+            constexpr int kVa = (68 + kMf - 1) / kMf;     // decode VALU per MFMA slot
+            bf16x8_t e0, e1, e2, e3, o0, o1, o2, o3;      // decoded fragments of even / odd steps
+            decode_step(0, e0, e1, e2, e3);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (t == 0) decode_step(1, o0, o1, o2, o3);
+                if (t == 1) decode_step(2, e0, e1, e2, e3);
+                if (t == 2) decode_step(3, o0, o1, o2, o3);
+                if (t % 2 == 0)
+                    mfma_step<MTW>(cur + aoff[t], kTileRowBytes, e0, e1, e2, e3, acc);
+                else
+                    mfma_step<MTW>(cur + aoff[t], kTileRowBytes, o0, o1, o2, o3, acc);
+                __builtin_amdgcn_sched_group_barrier(0x100, MTW, 0);  // the step's x fragment reads
+#pragma unroll
+                for (int i = 0; i < kMf; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, kVa, 0);  // then a share of the decode
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
