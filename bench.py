@@ -496,6 +496,53 @@ def summarize_profile(trace_dir, fetch_dir, write_dir):
     print(f"- sources_sha256: {kernel_sources_sha256()}")
 
 
+def summarize_prefill_profile(trace_dir, fetch_dir, write_dir, mfma_dir):
+    """Print the markdown summary of four rocprofv3 runs of `--prefill-only`
+    for its dominant launch, prefill_kernel on the fused gate/up GEMM at
+    M = 8192 (the largest grid): duration, MFMA busy cycles and HBM bytes."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    def grid(r):
+        return int(r.get("Grid_Size", 0) or r.get("Grid_Size_X", 0) or 0)
+
+    tr = [r for r in rows(trace_dir, "*kernel_trace.csv") if "prefill_kernel" in r["Kernel_Name"]]
+    top = max(grid(r) for r in tr)
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr if grid(r) == top]
+    m, (n, k) = 8192, synth.QWEN25_32B["gate"]
+    n *= 2
+    flops = gemm_flops(m, n, k, 2 * RANK)
+    avg = sum(durs) / len(durs)
+
+    def counter(d, name):
+        vals = [float(r["Counter_Value"]) for r in rows(d, "*counter_collection.csv")
+                if r["Counter_Name"] == name and "prefill_kernel" in r["Kernel_Name"] and grid(r) == top]
+        return sum(vals) / max(len(vals), 1), len(vals)
+
+    f_kib, f_n = counter(fetch_dir, "FETCH_SIZE")
+    w_kib, w_n = counter(write_dir, "WRITE_SIZE")
+    busy, b_n = counter(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui, _ = counter(mfma_dir, "GRBM_GUI_ACTIVE")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    print(f"- kernel: prefill_kernel, fused gate/up {n} x {k}, M = {m}, LoRA rank {2 * RANK} "
+          f"(grid {top // 256} workgroups, {len(durs)} dispatches)")
+    print(f"- average_launch_us: {avg:.1f}")
+    print(f"- tflops: {flops / (avg * 1e-6) / 1e12:.1f} ({flops / 1e12:.3f} TFLOP per launch)")
+    print(f"- SQ_VALU_MFMA_BUSY_CYCLES: {busy:.4g}; GRBM_GUI_ACTIVE: {gui:.4g} ({b_n} dispatches)")
+    print(f"- mfma_busy_frac: {busy / (gui * cus * 4):.3f} (MFMA busy cycles / (GUI-active cycles x {cus} CUs"
+          f" x 4 SIMDs))")
+    print(f"- fetch_kib_per_dispatch: {f_kib:.1f} ({f_n} dispatches; x 2.0 = bytes read, copy-probe scale)")
+    print(f"- write_kib_per_dispatch: {w_kib:.1f} ({w_n} dispatches)")
+    print(f"- algorithmic_bytes: {n * k * 0.5625 + 2 * m * k + 2 * m * n + 2 * 2 * RANK * (n + k):.0f}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -512,9 +559,16 @@ def main():
                     help="with --calls-only: also copy 256 MiB device to device (counter scale)")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="print the profile summary of rocprofv3 output directories and exit")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the prefill leg (for rocprofv3 runs); prints its JSON")
+    ap.add_argument("--summarize-prefill", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
+                    help="print the prefill profile summary of rocprofv3 output directories and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize_profile(*args.summarize)
+        return
+    if args.summarize_prefill:
+        summarize_prefill_profile(*args.summarize_prefill)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)", file=sys.stderr)
@@ -524,6 +578,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda", 0)
     q.lib()
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(dev, reps=3)}), flush=True)
+        return
 
     log("setting up decode layer ...")
     layer = DecodeLayer(dev, args.copies)

@@ -70,6 +70,7 @@ constexpr uint32_t kSpinLimit = 1u << 20;
 #define QERL_TARGET_UNITS 256
 #endif
 constexpr int64_t kTargetUnits = QERL_TARGET_UNITS;
+constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
 #ifndef QERL_RING
 #define QERL_RING 4
 #endif
@@ -87,6 +88,8 @@ struct DecodePlan {
     int64_t producers, jt, rp;     // LoRA producers, 16-wide rank tiles, rank padded to 32
     int64_t xpitch, sc_pitch;      // LDS pitches: BF16 elements per x row, bytes per scale row
     int64_t sc_lds_off, lds_bytes;
+    int64_t unit_sc_pitch;         // 16 < m: LDS pitch of the unit's scale tile
+    bool unit_sc;                  // 16 < m: scales staged in LDS
     int64_t part_off, tpart_off, t_off, bytes;
 };
 
@@ -116,6 +119,10 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
         p.cps = (p.chunks + s - 1) / s;
         p.slices = (p.chunks + p.cps - 1) / p.cps;
         p.units = p.row_blocks * p.slices;
+        int64_t scp = (p.cps * 8 + 15) / 16;  // rows an odd multiple of 16 bytes apart
+        if (scp % 2 == 0) ++scp;
+        p.unit_sc_pitch = scp * 16;
+        p.unit_sc = p.rows_per_unit * p.unit_sc_pitch <= kUnitScBytes;
         p.part_off = kGemmCtrBytes;
         p.tpart_off = align256(p.part_off + p.units * tile);
         p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
@@ -809,9 +816,14 @@ __global__ __launch_bounds__(256) void finish_kernel(Decode d) {
 // the first four waves of a producer work.
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile0[64 * kTileRowBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
+// the unit's scale bytes (256 rows x its slice), when they fit: 2-byte
+// global loads of 16 rows each cost more of the CU's memory path than the
+// weights they scale
+__shared__ __attribute__((aligned(16))) uint8_t g_dsc[kUnitScBytes];
 
-template <int MT>
+template <int MT, bool SCL>
 __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
+    // SCL: the unit's scales staged in LDS (p.unit_sc)
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     if ((int64_t)blockIdx.x < p.producers) {
@@ -835,8 +847,13 @@ __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int64_t fast_end = a.ldx <= kTileMaxLdx ? c_full_end : c_begin;
-    mfma_kloop<MT, kUnitWaves>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k, c_begin,
-                               fast_end, g_dxtile0, g_dxtile1, acc);
+    static_assert(64 * kUnitWaves == kThreadsD, "the staging helpers assume kThreadsD threads");
+    if (SCL && fast_end > c_begin) {  // (uniform) the slice's full blocks; visible after the barrier
+        stage_scales(a, g_dsc, p.unit_sc_pitch, n0, p.rows_per_unit, c_begin * 8, (fast_end - c_begin) * 8);
+        __syncthreads();
+    }
+    mfma_kloop<MT, kUnitWaves, 1, SCL>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k,
+                                       c_begin, fast_end, g_dxtile0, g_dxtile1, acc, g_dsc, (int)p.unit_sc_pitch);
     // the rest of the slice (the partial last chunk of K, or all of it for
     // very wide x rows)
     const int64_t nw = n0 + wave * 64 + lr;
@@ -866,8 +883,12 @@ __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
 
 template <int MT>
 hipError_t launch_mfma_units(const Decode &d, hipStream_t stream) {
-    hipLaunchKernelGGL(mfma_unit_kernel<MT>, dim3((unsigned)(d.p.producers + d.p.units)), dim3(64 * kUnitWaves), 0,
-                       stream, d);
+    if (d.p.unit_sc)
+        hipLaunchKernelGGL((mfma_unit_kernel<MT, true>), dim3((unsigned)(d.p.producers + d.p.units)),
+                           dim3(64 * kUnitWaves), 0, stream, d);
+    else
+        hipLaunchKernelGGL((mfma_unit_kernel<MT, false>), dim3((unsigned)(d.p.producers + d.p.units)),
+                           dim3(64 * kUnitWaves), 0, stream, d);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));

@@ -77,16 +77,21 @@ __device__ __forceinline__ void mfma_step(const uint8_t *pa, int pitch_bytes, co
 //   w_packed, w_scales: row 0 of the workgroup's 64 NWV weight rows; rows at
 //     or past w_rows are read as zeros
 //   t0, t1: two LDS tiles of 16 * MTW * 256 bytes, distinct arrays
+//   SCL: the scales come from an LDS tile (sc_tile: row r of the workgroup's
+//     rows at sc_tile + r * sc_pitch, the 8 bytes of block b0 + i at 8 i),
+//     staged and made visible by the caller, instead of 2-byte global loads
 // Needs ldx <= kTileMaxLdx and uniform arguments; ends with a barrier.
-template <int MTW, int NWV = 4, int WD = 1>
+template <int MTW, int NWV = 4, int WD = 1, bool SCL = false>
 __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_rows, int64_t ldx,
                                            const uint8_t *w_packed, const uint8_t *w_scales, int64_t w_rows,
                                            int64_t k, int64_t b0, int64_t b1, uint8_t *t0, uint8_t *t1,
-                                           f32x4_t (&acc)[MTW][4]) {
+                                           f32x4_t (&acc)[MTW][4], const uint8_t *sc_tile = nullptr,
+                                           int sc_pitch = 0) {
     static_assert(MTW == 2 || MTW == 4 || MTW == 8, "x tile of 32, 64 or 128 rows");
     static_assert(NWV == 4 || NWV == 8, "four or eight waves");
     static_assert(4 * MTW % NWV == 0, "whole DMA instructions per wave");
     static_assert(WD == 1 || WD == 2, "weights one or two blocks ahead");
+    static_assert(!SCL || WD == 1, "LDS scales with weights one block ahead");
     if (b0 >= b1) return;
     constexpr int kXRows = 16 * MTW;
     constexpr int kDma = 4 * MTW / NWV;  // DMA instructions per wave per block (1 KB = 4 rows each)
@@ -154,10 +159,18 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
         w.q1 = ldq16(1, k0 >> 1);
         w.q2 = ldq16(2, k0 >> 1);
         w.q3 = ldq16(3, k0 >> 1);
-        w.c0 = lds2(0, k0 >> 4);
-        w.c1 = lds2(1, k0 >> 4);
-        w.c2 = lds2(2, k0 >> 4);
-        w.c3 = lds2(3, k0 >> 4);
+        if (SCL) {
+            const uint8_t *sp = sc_tile + wrow * sc_pitch + (int)(s - b0) * 8 + 2 * lq;
+            w.c0 = *reinterpret_cast<const uint16_t *>(sp);
+            w.c1 = *reinterpret_cast<const uint16_t *>(sp + 16 * sc_pitch);
+            w.c2 = *reinterpret_cast<const uint16_t *>(sp + 32 * sc_pitch);
+            w.c3 = *reinterpret_cast<const uint16_t *>(sp + 48 * sc_pitch);
+        } else {
+            w.c0 = lds2(0, k0 >> 4);
+            w.c1 = lds2(1, k0 >> 4);
+            w.c2 = lds2(2, k0 >> 4);
+            w.c3 = lds2(3, k0 >> 4);
+        }
     };
     // block s from LDS tile cur and weight set wc while x of block s+1 streams
     // into nxt and the weights of block s+WD into wl.  Every block issues its
