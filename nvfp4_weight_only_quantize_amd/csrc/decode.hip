@@ -66,10 +66,6 @@ constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr uint32_t kSpinLimit = 1u << 20;
-#ifndef QERL_TARGET_UNITS
-#define QERL_TARGET_UNITS 256
-#endif
-constexpr int64_t kTargetUnits = QERL_TARGET_UNITS;
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
 #ifndef QERL_RING
 #define QERL_RING 4
@@ -95,6 +91,18 @@ struct DecodePlan {
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
 
+// compute units of the current device (queried once)
+int64_t cu_count() {
+    static const int64_t cus = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        return (int64_t)v;
+    }();
+    return cus;
+}
+
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
@@ -108,8 +116,10 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.jt = (r + 15) / 16;
     p.rp = (r + 31) / 32 * 32;
     p.producers = r > 0 ? (p.chunks + kProdChunks - 1) / kProdChunks : 0;
-    // slices: cover the chip, keep the FP32 partials below the weight bytes
-    int64_t s = p.row_blocks > 0 ? (kTargetUnits + p.row_blocks - 1) / p.row_blocks : 1;
+    // slices: as many units as compute units without going over (a CU that
+    // runs two units while others run one sets the time), and the FP32
+    // partials below the weight bytes
+    int64_t s = p.row_blocks > 0 ? cu_count() / p.row_blocks : 1;
     int64_t s_cap = (k * 9) / (64 * m);
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
