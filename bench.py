@@ -529,15 +529,19 @@ def summarize_prefill_profile(trace_dir, fetch_dir, write_dir, mfma_dir):
     f_kib, f_n = counter(fetch_dir, "FETCH_SIZE")
     w_kib, w_n = counter(write_dir, "WRITE_SIZE")
     busy, b_n = counter(mfma_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
-    gui, _ = counter(mfma_dir, "GRBM_GUI_ACTIVE")
-    cus = torch.cuda.get_device_properties(0).multi_processor_count if torch.cuda.is_available() else 256
+    gui, _ = counter(mfma_dir, "GRBM_GUI_ACTIVE")  # summed over the 8 XCDs
+    cus, xcds = 256, 8  # MI355X
+    clock_ghz = gui / xcds / (avg * 1e3)
     print(f"- kernel: prefill_kernel, fused gate/up {n} x {k}, M = {m}, LoRA rank {2 * RANK} "
           f"(grid {top // 256} workgroups, {len(durs)} dispatches)")
     print(f"- average_launch_us: {avg:.1f}")
     print(f"- tflops: {flops / (avg * 1e-6) / 1e12:.1f} ({flops / 1e12:.3f} TFLOP per launch)")
     print(f"- SQ_VALU_MFMA_BUSY_CYCLES: {busy:.4g}; GRBM_GUI_ACTIVE: {gui:.4g} ({b_n} dispatches)")
-    print(f"- mfma_busy_frac: {busy / (gui * cus * 4):.3f} (MFMA busy cycles / (GUI-active cycles x {cus} CUs"
-          f" x 4 SIMDs))")
+    print(f"- clock_ghz: {clock_ghz:.2f} (GUI-active cycles per XCD over the traced duration)")
+    print(f"- mfma_busy_frac: {busy / (gui / xcds * cus * 4):.3f} (MFMA busy cycles / (GUI-active cycles per XCD x"
+          f" {cus} CUs x 4 SIMDs))")
+    print(f"- tflops_at_measured_clock_peak_frac: "
+          f"{flops / (avg * 1e-6) / (cus * 4 * 1024 * clock_ghz * 1e9):.3f} (1024 BF16 FLOP per SIMD per cycle)")
     print(f"- fetch_kib_per_dispatch: {f_kib:.1f} ({f_n} dispatches; x 2.0 = bytes read, copy-probe scale)")
     print(f"- write_kib_per_dispatch: {w_kib:.1f} ({w_n} dispatches)")
     print(f"- algorithmic_bytes: {n * k * 0.5625 + 2 * m * k + 2 * m * n + 2 * 2 * RANK * (n + k):.0f}")
