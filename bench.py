@@ -98,8 +98,9 @@ def make_layer(shapes, seed, dev, r=RANK, row_sigma=0.5, outlier_rows=0.0):
 class DecodeLayer:
     """Buffers and the launch sequence of one decode step (7B shapes)."""
 
-    def __init__(self, dev, copies):
+    def __init__(self, dev, copies, side_streams=True):
         self.dev = dev
+        self.side_streams = side_streams
         self.shapes = synth.QWEN25_7B
         h, inter = 3584, 18944
         self.h = h
@@ -142,7 +143,7 @@ class DecodeLayer:
         for mi, m in enumerate(DECODE_MS):
             c = (len(DECODE_MS) * s + mi) % len(self.copies)
             self.norm("attn", m, s)
-            if on_gemm is None:
+            if on_gemm is None and self.side_streams:
                 # q, k and v read the same normed input and nothing else: they
                 # run side by side; o waits for all three (in a real layer
                 # attention sits in between), as the MLP waits for o
@@ -152,7 +153,7 @@ class DecodeLayer:
                 for name in ("q", "k", "v", "o"):
                     self._g(name, m, c, on_gemm)
             self.norm("mlp", m, s)
-            if on_gemm is None:
+            if on_gemm is None and self.side_streams:
                 self._parallel(("gate", "up"), m, c)  # down waits for both
                 self.gemm("down", m, c)
             else:
@@ -279,6 +280,91 @@ def cpu_baseline(layer: DecodeLayer, budget_s: float):
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle W4A16+LoRA on the 7B layer: {', '.join(sample)} "
                       f"({done_bytes / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
+
+
+def _graph_us(fn, reps):
+    """Average microseconds of fn(s) for s < reps, captured as one HIP graph
+    (after one eager pass) and replayed once between two events."""
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(reps):
+            fn(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def bf16_lora_leg(layer: DecodeLayer, reps: int = 5):
+    """The seven 7B projections at each decode M, one after another on one
+    stream, cold weights rotating: this library's W4A16 + LoRA against torch's
+    BF16 GEMM + the same LoRA (hipBLASLt; BF16 weights of the same shapes, one
+    copy per cold copy of the NVFP4 weights).  The pages' comparison is NVFP4
+    rollout against 16-bit LoRA rollout."""
+    dev = layer.dev
+    ncopy = len(layer.copies)
+    dense = []
+    for c in range(ncopy):
+        dense.append({name: (torch.randn(n, k, device=dev, dtype=torch.bfloat16) * 0.02)
+                      for name, (n, k) in layer.shapes.items()})
+    lam = ALPHA / RANK
+    out = {}
+    for m in DECODE_MS:
+        def ours(s, m=m):
+            c = (s * 3 + 1) % ncopy
+            for name in synth.PROJ_ORDER:
+                layer.gemm(name, m, c)
+
+        def torch_bf16(s, m=m):
+            c = (s * 3 + 1) % ncopy
+            for name in synth.PROJ_ORDER:
+                p, x = layer.copies[c][name], layer.inputs_of(name)[:m]
+                y = torch.nn.functional.linear(x, dense[c][name])
+                y.add_(torch.nn.functional.linear(torch.nn.functional.linear(x, p.a), p.b), alpha=lam)
+
+        t_ours, t_bf16 = _graph_us(ours, reps), _graph_us(torch_bf16, reps)
+        out[f"M={m}"] = {"w4a16_lora_us": round(t_ours, 2), "bf16_lora_us": round(t_bf16, 2),
+                         "speedup": round(t_bf16 / t_ours, 3)}
+    del dense
+    torch.cuda.empty_cache()
+    return out
+
+
+def lora_rank_leg(layer: DecodeLayer, ranks=(8, 16, 32, 64, 128), reps: int = 5):
+    """The seven 7B projections at each decode M with LoRA ranks 8..128 (cold
+    NVFP4 weights rotating as in the step; one LoRA per rank and copy)."""
+    dev = layer.dev
+    ncopy = len(layer.copies)
+    out = {}
+    for r in ranks:
+        loras = [{name: synth.lora_bf16(n, k, r, seed=synth.seed_for(SEED, name, "rank", r, c), device=dev)
+                  for name, (n, k) in layer.shapes.items()} for c in range(ncopy)]
+        ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(max(DECODE_MS), n, k, r)
+                             for n, k in layer.shapes.values()), dtype=torch.uint8, device=dev)
+        row = {}
+        for m in DECODE_MS:
+            def fn(s, m=m):
+                c = (s * 3 + 2) % ncopy
+                for name in synth.PROJ_ORDER:
+                    p = layer.copies[c][name]
+                    a, b = loras[c][name]
+                    q.w4a16_lora_gemm(layer.inputs_of(name)[:m], p.wq, a, b, ALPHA / r,
+                                      out=layer.y[name][:m], workspace=ws)
+
+            t = _graph_us(fn, reps)
+            b_m = sum(gemm_bytes(m, *layer.shapes[name], r) for name in synth.PROJ_ORDER)
+            row[f"M={m}"] = {"us": round(t, 2), "GB/s": round(b_m / (t * 1e-6) / 1e9, 1)}
+        out[f"r={r}"] = row
+        del loras, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def prefill_leg(dev, reps):
@@ -553,6 +639,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=8, help="cold-weight copies of the layer")
+    ap.add_argument("--streams", type=int, choices=(1, 3), default=3,
+                    help="3: independent projections side by side on side streams; 1: one stream")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -587,7 +675,7 @@ def main():
         return
 
     log("setting up decode layer ...")
-    layer = DecodeLayer(dev, args.copies)
+    layer = DecodeLayer(dev, args.copies, side_streams=args.streams == 3)
     torch.cuda.synchronize()
     if args.calls_only:
         roofline, per_m, per_proj = roofline_leg(layer)
@@ -612,6 +700,9 @@ def main():
     roofline, per_m, per_proj = roofline_leg(layer)
 
     parity = check_decode_parity(layer)
+    log("BF16 + LoRA comparison and LoRA rank sweep ...")
+    compare = bf16_lora_leg(layer)
+    ranks = lora_rank_leg(layer)
     result = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -620,12 +711,15 @@ def main():
                                "q/k/v/o/gate/up/down NVFP4 W4A16 + LoRA r32 (alpha 64), M in {1,8,64}",
                    "hidden": 3584, "intermediate": 18944, "decode_m": list(DECODE_MS),
                    "lora_rank": RANK, "cold_weight_copies": args.copies, "hip_graph": True,
+                   "streams": args.streams,
                    "step_bytes": step_bytes},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
         "roofline": roofline,
         "decode_per_m": per_m,
         "decode_call_us": per_proj,
         "parity_rel_l2_m1": parity,
+        "bf16_lora_compare": compare,
+        "lora_rank_sweep": ranks,
     }
     del _graphs
     if not args.no_prefill:

@@ -82,6 +82,7 @@ struct DecodePlan {
     int64_t chunks, full_chunks;   // chunks of K (the last may be partial), full chunks
     int64_t cps, slices, units;    // chunks per slice (a multiple of 4/nw)
     int64_t producers, jt, rp;     // LoRA producers, 16-wide rank tiles, rank padded to 32
+    int64_t prod_kr, prod_groups;  // producers: K ranges x (m-tile, rank-tile pair) groups
     int64_t xpitch, sc_pitch;      // LDS pitches: BF16 elements per x row, bytes per scale row
     int64_t sc_lds_off, lds_bytes;
     int64_t unit_sc_pitch;         // 16 < m: LDS pitch of the unit's scale tile
@@ -115,7 +116,9 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.px = 1;
     p.jt = (r + 15) / 16;
     p.rp = (r + 31) / 32 * 32;
-    p.producers = r > 0 ? (p.chunks + kProdChunks - 1) / kProdChunks : 0;
+    p.prod_kr = (p.chunks + kProdChunks - 1) / kProdChunks;
+    p.prod_groups = p.mt * ((p.jt + kProdTiles - 1) / kProdTiles);
+    p.producers = r > 0 ? p.prod_kr * p.prod_groups : 0;
     // slices: as many units as compute units without going over (a CU that
     // runs two units while others run one sets the time), and the FP32
     // partials below the weight bytes
@@ -135,7 +138,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
         p.unit_sc = p.rows_per_unit * p.unit_sc_pitch <= kUnitScBytes;
         p.part_off = kGemmCtrBytes;
         p.tpart_off = align256(p.part_off + p.units * tile);
-        p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
+        p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
         p.bytes = align256(p.t_off + m * (int64_t)r * 4);
         return p;
     }
@@ -168,7 +171,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     // workspace after the counters: partial tiles, producer partials, t
     p.part_off = kGemmCtrBytes;
     p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
-    p.t_off = align256(p.tpart_off + p.producers * (int64_t)p.mt * p.jt * 64 * 16);
+    p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
     p.bytes = align256(p.t_off + 2 * 16 * p.rp * 2);  // t16: BF16 hi/lo [2][16][rp]
     return p;
 }
@@ -240,8 +243,10 @@ __device__ __forceinline__ bf16x8_t dequant8_d(uint32_t q, float s) {
 // ---------------------------------------------------------------------------
 // LoRA producers: t = x A^T
 // ---------------------------------------------------------------------------
-// Producer p covers chunks [8p, 8p + 8) of K for all rows and ranks; its 4
-// waves take interleaved 32-element steps.  A lane supplies x row
+// Producer p covers one range of kProdChunks chunks of K for one 16-row
+// m-tile and kProdTiles 16-rank tiles (the producers of a launch enumerate
+// K ranges x m-tiles x rank-tile groups); its 4 waves take interleaved
+// 32-element steps.  A lane supplies x row
 // 16*mt + (lane % 16) and A row 16*jt + (lane % 16), 8 elements at
 // 8*(lane / 16) of the step, so MFMA tile (mt, jt) holds
 // t[16 mt + 4 (lane/16) + v][16 jt + lane % 16] in element v.
@@ -249,21 +254,26 @@ template <int MT>
 __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     const GemmArgs &a = d.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-    const int JT = (int)d.p.jt;
-    const int64_t kb = p * kProdChunks * kChunkK;
+    const int JT = (int)d.p.jt, JG = (JT + kProdTiles - 1) / kProdTiles;
+    // producer p: K range kr, m-tile mt, rank tiles jg .. jg + kProdTiles - 1
+    // (one pass each, so that no producer runs all m-tiles and ranks in turn)
+    const int64_t kr = p / d.p.prod_groups;
+    const int grp = (int)(p - kr * d.p.prod_groups);
+    const int64_t kb = kr * kProdChunks * kChunkK;
     const int64_t ke = kb + kProdChunks * kChunkK < a.k ? kb + kProdChunks * kChunkK : a.k;
     const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
-    const __amdgpu_buffer_rsrc_t rs_own = coherent_rsrc(d.tpart() + p * tile_floats);
+    const __amdgpu_buffer_rsrc_t rs_own = coherent_rsrc(d.tpart() + kr * tile_floats);
     f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
-    // one m-tile and two rank tiles at a time, so the producer path never
-    // needs more registers than the streaming path; each wave's steps (32
-    // elements, every 4th of the range) in groups of PS with all loads of a
-    // group issued before its products
+    // one m-tile and two rank tiles, so the producer path never needs more
+    // registers than the streaming path; each wave's steps (32 elements,
+    // every 4th of the range) in groups of PS with all loads of a group
+    // issued before its products
     constexpr int PS = 4;
-    for (int mt = 0; mt < MT; ++mt) {
+    {
+        const int mt = grp / JG, jg = (grp - mt * JG) * kProdTiles;
         const int64_t mrow = 16 * mt + lr < a.m ? 16 * mt + lr : a.m - 1;
         const uint16_t *xrow = a.x + mrow * a.ldx;
-        for (int jg = 0; jg < JT; jg += kProdTiles) {
+        {
             f32x4_t acc[kProdTiles];
 #pragma unroll
             for (int j = 0; j < kProdTiles; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -320,24 +330,24 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     __syncthreads();
     if (!s_last) return;
     if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);  // every producer has counted
-    // The last producer sums the partials in producer order (tile i goes to
-    // wave i % 4, kBatch producers in flight).  16 < m: into t [m, r] in FP32,
+    // The last producer sums the partials in K-range order (tile i goes to
+    // wave i % 4, kBatch ranges in flight).  16 < m: into t [m, r] in FP32,
     // read after the kernel boundary.  m <= 16: into t16 [2][16][rp], the BF16
     // hi and lo halves of t in the layout the consumers' epilogue multiplies,
     // published to this launch's consumers by the ready flag.
     const __amdgpu_buffer_rsrc_t rt = coherent_rsrc(d.t32());
     for (int i = wave; wave < kWaves && i < MT * JT; i += kWaves) {
         f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t q0 = 0; q0 < d.p.producers; q0 += kBatch) {
+        for (int64_t q0 = 0; q0 < d.p.prod_kr; q0 += kBatch) {
             f32x4_t v[kBatch];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int64_t q = q0 + u < d.p.producers ? q0 + u : d.p.producers - 1;
+                const int64_t q = q0 + u < d.p.prod_kr ? q0 + u : d.p.prod_kr - 1;
                 v[u] = load_f4_coherent(coherent_rsrc(d.tpart() + q * tile_floats), (i * 64 + lane) * 16);
             }
 #pragma unroll
             for (int u = 0; u < kBatch; ++u)
-                if (q0 + u < d.p.producers) sum = sum + v[u];
+                if (q0 + u < d.p.prod_kr) sum = sum + v[u];
         }
         const int mt = i / JT, jt = i - mt * JT;
         const int64_t j = 16 * jt + lr;

@@ -35,7 +35,11 @@ constexpr int kThreads = 256;
 // The workspace starts with the decode path's counter region, which this path
 // never touches, then holds the BF16 hi/lo t [m, 2r] and, when K is split,
 // the FP32 partial outputs [splits][m][n].
-constexpr int PBM = 128, PBN = 256;   // output tile: rows of x x weight rows
+#ifndef QERL_PF_WAVES
+#define QERL_PF_WAVES 4
+#endif
+constexpr int kPfWaves = QERL_PF_WAVES;  // waves of a prefill workgroup, 64 weight rows each
+constexpr int PBM = 128, PBN = 64 * kPfWaves;  // output tile: rows of x x weight rows
 constexpr int64_t kSplitTiles = 256;  // below this many tiles (fewer than CUs) K is split
 constexpr int64_t kMaxSplits = 16;
 
@@ -52,7 +56,7 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     const int64_t blocks = k / 128;
     p.splits = 1;
     if (p.tiles < kSplitTiles && blocks >= 8) {
-        int64_t s = (2 * 256 + p.tiles - 1) / p.tiles;  // toward two workgroups per CU
+        int64_t s = ((8 / kPfWaves) * 256 + p.tiles - 1) / p.tiles;  // toward 8 waves per CU
         if (s > blocks / 4) s = blocks / 4;              // at least four blocks per split
         if (s > kMaxSplits) s = kMaxSplits;
         if (s > 1) p.splits = s;
@@ -213,7 +217,7 @@ __device__ __forceinline__ bf16x8_t w_frag_ext(const GemmArgs &a, int64_t n, int
 }
 
 template <bool SPLIT>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
+__global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Gemm g) {
     const GemmArgs &a = g.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     // XCD-aware tile order: workgroup b runs on XCD b % 8 and each XCD takes
@@ -241,13 +245,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(Gemm g) {
     const int64_t blocks = a.ldx <= kTileMaxLdx ? a.k / kTileK : 0;
     const int64_t kb0 = !SPLIT ? 0 : (split * p.bps < blocks ? split * p.bps : blocks);
     const int64_t kb1 = last ? blocks : (kb0 + p.bps < blocks ? kb0 + p.bps : blocks);
-    mfma_kloop<8>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1), a.scales + n0 * (a.k >> 4),
+    mfma_kloop<8, kPfWaves>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1), a.scales + n0 * (a.k >> 4),
                   a.n - n0, a.k, kb0, kb1, g_xtile0, g_xtile1, acc);
     // the last split: the rest of K (and all of it for very wide x rows), then
     // the LoRA columns
     const int64_t nw = n0 + wave * 64 + lr;
     if (last)
-        plain_kloop<8>(
+        plain_kloop<8, kPfWaves>(
             blocks * kTileK, a.k + klora, g_xtile0,
             [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora); },
             [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
@@ -327,10 +331,10 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
     const int64_t grid = g.p.tiles * g.p.splits;
     if (grid > 0x7FFFFFFF || a.m * a.n > 0x7FFFFFFFll * kThreads) return hipErrorInvalidConfiguration;
     if (g.p.splits == 1) {
-        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, g);
+        hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream, g);
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((a.m * a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,

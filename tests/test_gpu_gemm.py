@@ -122,6 +122,19 @@ def test_config2_7b_layer(proj):
         assert_gemm_close(y if rows is None else y[rows], ref, f"{proj} m={m}")
 
 
+@pytest.mark.parametrize("r", [8, 128])
+def test_7b_lora_rank_sweep_ends(r):
+    # the ends of the bench's LoRA-rank sweep at the 7B up projection
+    n, k = synth.QWEN25_7B["up"]
+    L = Layer(n, k, r, seed=synth.seed_for(1005, "up", r), lora_scale=64 / r)
+    for m in (1, 8, 64):
+        x = _x(m, k, seed=synth.seed_for(1005, "x", m))
+        y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+        rows = None if m <= 8 else [0, 17, 63]
+        ref = L.ref(x, rows=rows)
+        assert_gemm_close(y if rows is None else y[rows], ref, f"up r={r} m={m}")
+
+
 @pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
 def test_config3_32b_batched_decode(proj):
     n, k = synth.QWEN25_32B[proj]
