@@ -98,9 +98,9 @@ def make_layer(shapes, seed, dev, r=RANK, row_sigma=0.5, outlier_rows=0.0):
 class DecodeLayer:
     """Buffers and the launch sequence of one decode step (7B shapes)."""
 
-    def __init__(self, dev, copies, side_streams=True):
+    def __init__(self, dev, copies, launch="fused"):
         self.dev = dev
-        self.side_streams = side_streams
+        self.launch = launch
         self.shapes = synth.QWEN25_7B
         h, inter = 3584, 18944
         self.h = h
@@ -118,6 +118,10 @@ class DecodeLayer:
         self.y = {name: torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
                   for name, (n, _k) in self.shapes.items()}
         ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
+        for group in (("q", "k", "v"), ("gate", "up")):
+            for m in DECODE_MS:
+                ws = max(ws, q.w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1],
+                                                                    [(self.shapes[g][0], RANK) for g in group]))
         # one workspace per concurrent GEMM (calls that overlap must not share one)
         self.ws = [torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev) for _ in range(3)]
         # side streams for the independent projections (default priority)
@@ -133,6 +137,12 @@ class DecodeLayer:
         q.w4a16_lora_gemm(self.inputs_of(name)[:m], p.wq, p.a, p.b, ALPHA / RANK,
                           out=self.y[name][:m], workspace=self.ws[slot])
 
+    def gemm_multi(self, names, m, c):
+        """The projections `names` (same input) in one multi-segment call."""
+        segs = [(self.copies[c][n].wq, self.copies[c][n].a, self.copies[c][n].b, ALPHA / RANK) for n in names]
+        q.w4a16_lora_gemm_multi(self.inputs_of(names[0])[:m], segs, outs=[self.y[n][:m] for n in names],
+                                workspace=self.ws[0])
+
     def norm(self, which, m, step):
         src, w, dst, layer = ((self.h_attn, self.w_attn, self.x_attn, 0) if which == "attn"
                               else (self.h_mlp, self.w_mlp, self.x_mlp, 1))
@@ -143,18 +153,25 @@ class DecodeLayer:
         for mi, m in enumerate(DECODE_MS):
             c = (len(DECODE_MS) * s + mi) % len(self.copies)
             self.norm("attn", m, s)
-            if on_gemm is None and self.side_streams:
-                # q, k and v read the same normed input and nothing else: they
-                # run side by side; o waits for all three (in a real layer
-                # attention sits in between), as the MLP waits for o
-                self._parallel(("q", "k", "v"), m, c)
+            if on_gemm is None and self.launch != "serial":
+                # q, k and v read the same normed input and nothing else: one
+                # multi-segment call (or side by side on side streams); o
+                # waits for all three (in a real layer attention sits in
+                # between), as the MLP waits for o
+                if self.launch == "fused":
+                    self.gemm_multi(("q", "k", "v"), m, c)
+                else:
+                    self._parallel(("q", "k", "v"), m, c)
                 self.gemm("o", m, c)
             else:
                 for name in ("q", "k", "v", "o"):
                     self._g(name, m, c, on_gemm)
             self.norm("mlp", m, s)
-            if on_gemm is None and self.side_streams:
-                self._parallel(("gate", "up"), m, c)  # down waits for both
+            if on_gemm is None and self.launch != "serial":
+                if self.launch == "fused":
+                    self.gemm_multi(("gate", "up"), m, c)
+                else:
+                    self._parallel(("gate", "up"), m, c)  # down waits for both
                 self.gemm("down", m, c)
             else:
                 for name in ("gate", "up", "down"):
@@ -639,8 +656,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=8, help="cold-weight copies of the layer")
-    ap.add_argument("--streams", type=int, choices=(1, 3), default=3,
-                    help="3: independent projections side by side on side streams; 1: one stream")
+    ap.add_argument("--launch", choices=("fused", "streams", "serial"), default="fused",
+                    help="q/k/v and gate/up: one multi-segment call each (fused), side by side on side "
+                         "streams (streams), or one call after another on one stream (serial)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -675,7 +693,7 @@ def main():
         return
 
     log("setting up decode layer ...")
-    layer = DecodeLayer(dev, args.copies, side_streams=args.streams == 3)
+    layer = DecodeLayer(dev, args.copies, launch=args.launch)
     torch.cuda.synchronize()
     if args.calls_only:
         roofline, per_m, per_proj = roofline_leg(layer)
@@ -711,7 +729,7 @@ def main():
                                "q/k/v/o/gate/up/down NVFP4 W4A16 + LoRA r32 (alpha 64), M in {1,8,64}",
                    "hidden": 3584, "intermediate": 18944, "decode_m": list(DECODE_MS),
                    "lora_rank": RANK, "cold_weight_copies": args.copies, "hip_graph": True,
-                   "streams": args.streams,
+                   "launch": args.launch,
                    "step_bytes": step_bytes},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
         "roofline": roofline,

@@ -65,6 +65,7 @@ typedef enum qerl_status {
 #define QERL_SCALE_RNE 1u      /* nearest E4M3 value, ties to the even code */
 
 #define QERL_MAX_LORA_RANK 128
+#define QERL_MAX_SEGMENTS 4    /* projections of one qerl_w4a16_lora_gemm_multi call */
 #define QERL_MAX_NORM_WIDTH 16384
 
 /* ----------------------------------------------------------------------- */
@@ -120,12 +121,14 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
  *   lora_a_bf16   [r, k] contiguous; lora_b_bf16 [n, r] contiguous; both may be
  *                 NULL only when r == 0 (no LoRA)
  *   y_bf16        [m, n], row stride ldy >= n; must not overlap any input
- *   workspace     device memory of at least the size query; its first 64 KiB
- *                 hold counters that must be zero before the first call that
- *                 uses this workspace (e.g. allocate it zero-filled).  Every
- *                 call leaves them zero, so one workspace serves any sequence
- *                 of calls on one stream; calls that overlap in time must not
- *                 share a workspace.
+ *   workspace     device memory of at least the size query; its first 256
+ *                 KiB hold counters (64 KiB per projection of a multi call,
+ *                 the same places for every call) that must be zero before the
+ *                 first call that uses this workspace (e.g. allocate it
+ *                 zero-filled).  Every call leaves them zero, so one workspace
+ *                 serves any sequence of calls -- qerl_w4a16_lora_gemm and
+ *                 qerl_w4a16_lora_gemm_multi, any shapes -- on one stream;
+ *                 calls that overlap in time must not share a workspace.
  * m <= 64 takes the decode path: one launch that streams the packed weights
  * once (E2M1/E4M3 decode in registers, BF16 MFMA), reduces split-K partials
  * in the last workgroup of each row block and adds the LoRA term there; larger
@@ -140,6 +143,51 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
                                  const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
                                  float lora_scale, void *y_bf16, int64_t ldy,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One projection of qerl_w4a16_lora_gemm_multi: every field as the argument
+ * of the same name of qerl_w4a16_lora_gemm (device pointers; y_bf16 [m, n]
+ * with row stride ldy).
+ */
+typedef struct {
+    const uint8_t *packed;
+    const uint8_t *scales;
+    const float *tensor_scale;
+    int64_t n;
+    const void *lora_a_bf16;
+    const void *lora_b_bf16;
+    int32_t r;
+    float lora_scale;
+    void *y_bf16;
+    int64_t ldy;
+} qerl_gemm_segment;
+
+/* Bytes of device workspace qerl_w4a16_lora_gemm_multi needs (reads n and r
+ * of segs[0 .. nseg)). */
+size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qerl_gemm_segment *segs,
+                                                 int32_t nseg);
+
+/*
+ * Several projections of the same activations in one call: for each segment
+ * i < nseg (1 <= nseg <= QERL_MAX_SEGMENTS), exactly what qerl_w4a16_lora_gemm
+ * computes for x and segs[i] -- each with its own weight, tensor scale, LoRA
+ * and output.  The operation is the layer of qerl_w4a16_lora_gemm (README
+ * "Acknowledgement"; bitsofall "LoRA (Low-Rank Adaptation)"), applied to the
+ * projections that read one normed input (q/k/v, gate/up).  For m <= 64 the
+ * segments share one launch (so a decode step spends one launch, not one per
+ * projection, on them); the K split is chosen for all segments together, so
+ * the FP32 summation order, and with it the last bit of y, can differ from
+ * separate calls.  Larger m runs the segments one after another.
+ *   segs          host array of nseg segments, read during the call only
+ *   workspace     as for qerl_w4a16_lora_gemm (the same 256 KiB counter
+ *                 head, zero before the first use; every call leaves it zero),
+ *                 of at least the size query
+ * Requires the conditions of qerl_w4a16_lora_gemm for every segment, outputs
+ * that overlap neither each other nor any input.
+ */
+qerl_status qerl_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                       const qerl_gemm_segment *segs, int32_t nseg, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* ----------------------------------------------------------------------- */
 /* AQN RMSNorm                                                               */

@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.qerl_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, P, i64, P, P, i32, f32, P, i64,
                                        P, sz, P]
     L.qerl_w4a16_lora_gemm.restype = ctypes.c_int
+    L.qerl_w4a16_lora_gemm_multi_workspace_size.argtypes = [i64, i64, ctypes.POINTER(GemmSegment), i32]
+    L.qerl_w4a16_lora_gemm_multi_workspace_size.restype = sz
+    L.qerl_w4a16_lora_gemm_multi.argtypes = [P, i64, i64, i64, ctypes.POINTER(GemmSegment), i32, P, sz, P]
+    L.qerl_w4a16_lora_gemm_multi.restype = ctypes.c_int
     L.qerl_aqn_sigma.argtypes = [i32, i32, f32, f32]
     L.qerl_aqn_sigma.restype = f32
     L.qerl_aqn_rmsnorm.argtypes = [P, i64, i64, i64, P, f32, f32, u64, u64, u32, P, P, i64, P, P]
@@ -202,6 +206,71 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
         _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out), _rows(out, "out"),
         _ptr(workspace), ws_bytes, _stream(stream, dev)))
     return out
+
+
+class GemmSegment(ctypes.Structure):
+    """qerl_gemm_segment of include/qerl.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("lora_a_bf16", ctypes.c_void_p), ("lora_b_bf16", ctypes.c_void_p),
+                ("r", ctypes.c_int32), ("lora_scale", ctypes.c_float), ("y_bf16", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64)]
+
+
+MAX_SEGMENTS = 4  # QERL_MAX_SEGMENTS
+
+
+def _segments(x, segments, outs):
+    """ctypes array of the segments (wq, lora_a, lora_b, lora_scale) with outputs."""
+    dev = x.device
+    m, k = x.shape
+    arr = (GemmSegment * len(segments))()
+    for i, ((wq, a, b, lam), out) in enumerate(zip(segments, outs)):
+        n, kw = wq.shape
+        if kw != k:
+            raise ValueError(f"segment {i}: x has K={k} but the weight has K={kw}")
+        r = 0
+        if a is not None or b is not None:
+            _need(a, "lora_a", torch.bfloat16, 2, dev)
+            _need(b, "lora_b", torch.bfloat16, 2, dev)
+            r = a.size(0)
+            if tuple(a.shape) != (r, k) or tuple(b.shape) != (n, r) or not (a.is_contiguous() and b.is_contiguous()):
+                raise ValueError(f"segment {i}: LoRA must be contiguous A [r, K] and B [N, r]")
+        _need(out, "out", torch.bfloat16, 2, dev)
+        if tuple(out.shape) != (m, n):
+            raise ValueError(f"segment {i}: out must be [M, N]")
+        arr[i] = GemmSegment(_ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n, _ptr(a), _ptr(b), r,
+                             float(lam), _ptr(out), _rows(out, "out"))
+    return arr
+
+
+def w4a16_lora_gemm_multi_workspace_size(m: int, k: int, shapes) -> int:
+    """shapes: (n, r) per segment."""
+    arr = (GemmSegment * len(shapes))()
+    for i, (n, r) in enumerate(shapes):
+        arr[i].n, arr[i].r = int(n), int(r)
+    return int(lib().qerl_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(shapes)))
+
+
+def w4a16_lora_gemm_multi(x: torch.Tensor, segments, outs=None, workspace: torch.Tensor | None = None,
+                          stream=None):
+    """Several projections of x in one call: segments is a list of
+    (wq, lora_a, lora_b, lora_scale) (LoRA None for none); returns the outputs
+    (given in ``outs`` or allocated).  For M <= 64 they share one launch."""
+    _need(x, "x", torch.bfloat16, 2)
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError(f"1 to {MAX_SEGMENTS} segments")
+    dev = x.device
+    m, k = x.shape
+    if outs is None:
+        outs = [torch.empty((m, wq.shape[0]), dtype=torch.bfloat16, device=dev) for wq, *_ in segments]
+    arr = _segments(x, segments, outs)
+    need = int(lib().qerl_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(segments)))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qerl_w4a16_lora_gemm_multi(_ptr(x), m, k, _rows(x, "x"), arr, len(segments), _ptr(workspace),
+                                            ws_bytes, _stream(stream, dev)))
+    return outs
 
 
 # -------------------------------------------------------------------- AQN --

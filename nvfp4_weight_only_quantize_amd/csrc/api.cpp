@@ -87,6 +87,57 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
     return qerl::gemm_workspace_bytes(m, n, k, r);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the single and multi-segment GEMM calls; fills *a.
+qerl_status check_gemm(const char *what, const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                       const uint8_t *packed, const uint8_t *scales, const float *tensor_scale, int64_t n,
+                       const void *lora_a_bf16, const void *lora_b_bf16, int32_t r, float lora_scale,
+                       void *y_bf16, int64_t ldy, qerl::GemmArgs *a) {
+    if (!x_bf16 || !packed || !scales || !tensor_scale || !y_bf16)
+        return fail(QERL_ERR_NULL, "%s: x, packed, scales, tensor_scale and y are required", what);
+    if (r < 0 || r > QERL_MAX_LORA_RANK)
+        return fail(QERL_ERR_ARG, "%s: LoRA rank %d outside [0, %d]", what, r, QERL_MAX_LORA_RANK);
+    if (r > 0 && (!lora_a_bf16 || !lora_b_bf16))
+        return fail(QERL_ERR_NULL, "%s: lora_a and lora_b are required when r > 0", what);
+    if (!isfinite(lora_scale)) return fail(QERL_ERR_ARG, "%s: lora_scale must be finite", what);
+    if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || ldx < k || ldy < n || m > kMaxElems / k ||
+        n > kMaxElems / k || m > kMaxElems / ldy || ldx > kMaxElems || m > ((int64_t)1 << 24) ||
+        n > ((int64_t)1 << 28))
+        return fail(QERL_ERR_SHAPE, "%s: need m, n >= 1, k >= 16, k %% 16 == 0, ldx >= k, "
+                    "ldy >= n (got m=%lld n=%lld k=%lld ldx=%lld ldy=%lld)", what, (long long)m,
+                    (long long)n, (long long)k, (long long)ldx, (long long)ldy);
+    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(scales) || ((uintptr_t)y_bf16 & 1u) ||
+        ((uintptr_t)tensor_scale & 3u) || ldx % 8 != 0 ||
+        (r > 0 && (!aligned16(lora_a_bf16) || !aligned16(lora_b_bf16))))
+        return fail(QERL_ERR_ALIGN, "%s: x, packed, scales, lora_a, lora_b must be 16-byte "
+                    "aligned, y 2-byte aligned, ldx %% 8 == 0", what);
+    a->x = static_cast<const uint16_t *>(x_bf16);
+    a->m = m;
+    a->k = k;
+    a->ldx = ldx;
+    a->packed = packed;
+    a->scales = scales;
+    a->tensor_scale = tensor_scale;
+    a->n = n;
+    a->lora_a = static_cast<const uint16_t *>(lora_a_bf16);
+    a->lora_b = static_cast<const uint16_t *>(lora_b_bf16);
+    a->r = r;
+    a->lora_scale = lora_scale;
+    a->y = static_cast<uint16_t *>(y_bf16);
+    a->ldy = ldy;
+    a->workspace = nullptr;
+    return QERL_OK;
+}
+
+static_assert(QERL_MAX_SEGMENTS == 4, "the header's segment limit is the launcher's");
+
+}  // namespace
+
+extern "C" {
+
 qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
                                  const uint8_t *packed, const uint8_t *scales,
                                  const float *tensor_scale, int64_t n,
@@ -94,47 +145,60 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
                                  float lora_scale, void *y_bf16, int64_t ldy,
                                  void *workspace, size_t workspace_bytes, void *stream) {
     g_last_error[0] = '\0';
-    if (!x_bf16 || !packed || !scales || !tensor_scale || !y_bf16)
-        return fail(QERL_ERR_NULL, "w4a16_lora_gemm: x, packed, scales, tensor_scale and y are required");
-    if (r < 0 || r > QERL_MAX_LORA_RANK)
-        return fail(QERL_ERR_ARG, "w4a16_lora_gemm: LoRA rank %d outside [0, %d]", r, QERL_MAX_LORA_RANK);
-    if (r > 0 && (!lora_a_bf16 || !lora_b_bf16))
-        return fail(QERL_ERR_NULL, "w4a16_lora_gemm: lora_a and lora_b are required when r > 0");
-    if (!isfinite(lora_scale)) return fail(QERL_ERR_ARG, "w4a16_lora_gemm: lora_scale must be finite");
-    if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || ldx < k || ldy < n || m > kMaxElems / k ||
-        n > kMaxElems / k || m > kMaxElems / ldy || ldx > kMaxElems || m > ((int64_t)1 << 24) ||
-        n > ((int64_t)1 << 28))
-        return fail(QERL_ERR_SHAPE, "w4a16_lora_gemm: need m, n >= 1, k >= 16, k %% 16 == 0, ldx >= k, "
-                    "ldy >= n (got m=%lld n=%lld k=%lld ldx=%lld ldy=%lld)", (long long)m,
-                    (long long)n, (long long)k, (long long)ldx, (long long)ldy);
-    if (!aligned16(x_bf16) || !aligned16(packed) || !aligned16(scales) || ((uintptr_t)y_bf16 & 1u) ||
-        ((uintptr_t)tensor_scale & 3u) || ldx % 8 != 0 ||
-        (r > 0 && (!aligned16(lora_a_bf16) || !aligned16(lora_b_bf16))))
-        return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm: x, packed, scales, lora_a, lora_b must be 16-byte "
-                    "aligned, y 2-byte aligned, ldx %% 8 == 0");
+    qerl::GemmArgs a;
+    const qerl_status st = check_gemm("w4a16_lora_gemm", x_bf16, m, k, ldx, packed, scales, tensor_scale, n,
+                                      lora_a_bf16, lora_b_bf16, r, lora_scale, y_bf16, ldy, &a);
+    if (st != QERL_OK) return st;
     const size_t need = qerl::gemm_workspace_bytes(m, n, k, r);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm: workspace of %zu bytes needed", need);
     if (workspace && !aligned16(workspace))
         return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm: workspace must be 16-byte aligned");
-    qerl::GemmArgs a;
-    a.x = static_cast<const uint16_t *>(x_bf16);
-    a.m = m;
-    a.k = k;
-    a.ldx = ldx;
-    a.packed = packed;
-    a.scales = scales;
-    a.tensor_scale = tensor_scale;
-    a.n = n;
-    a.lora_a = static_cast<const uint16_t *>(lora_a_bf16);
-    a.lora_b = static_cast<const uint16_t *>(lora_b_bf16);
-    a.r = r;
-    a.lora_scale = lora_scale;
-    a.y = static_cast<uint16_t *>(y_bf16);
-    a.ldy = ldy;
     a.workspace = workspace;
     return hip_status(qerl::launch_w4a16_lora_gemm(a, static_cast<hipStream_t>(stream)),
                       "w4a16_lora_gemm launch");
+}
+
+size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qerl_gemm_segment *segs,
+                                                 int32_t nseg) {
+    if (!segs || nseg < 1 || nseg > QERL_MAX_SEGMENTS) return 0;
+    int64_t n[QERL_MAX_SEGMENTS];
+    int r[QERL_MAX_SEGMENTS];
+    for (int i = 0; i < nseg; ++i) {
+        n[i] = segs[i].n;
+        r[i] = segs[i].r;
+    }
+    return qerl::gemm_multi_workspace_bytes(m, k, n, r, nseg);
+}
+
+qerl_status qerl_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                       const qerl_gemm_segment *segs, int32_t nseg, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!segs) return fail(QERL_ERR_NULL, "w4a16_lora_gemm_multi: segs is required");
+    if (nseg < 1 || nseg > QERL_MAX_SEGMENTS)
+        return fail(QERL_ERR_ARG, "w4a16_lora_gemm_multi: nseg %d outside [1, %d]", nseg, QERL_MAX_SEGMENTS);
+    qerl::GemmArgs a[QERL_MAX_SEGMENTS];
+    int64_t n[QERL_MAX_SEGMENTS];
+    int r[QERL_MAX_SEGMENTS];
+    char what[48];
+    for (int i = 0; i < nseg; ++i) {
+        snprintf(what, sizeof what, "w4a16_lora_gemm_multi segment %d", i);
+        const qerl_gemm_segment &g = segs[i];
+        const qerl_status st = check_gemm(what, x_bf16, m, k, ldx, g.packed, g.scales, g.tensor_scale, g.n,
+                                          g.lora_a_bf16, g.lora_b_bf16, g.r, g.lora_scale, g.y_bf16, g.ldy, &a[i]);
+        if (st != QERL_OK) return st;
+        n[i] = g.n;
+        r[i] = g.r;
+    }
+    const size_t need = qerl::gemm_multi_workspace_bytes(m, k, n, r, nseg);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm_multi: workspace of %zu bytes needed", need);
+    if (workspace && !aligned16(workspace))
+        return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm_multi: workspace must be 16-byte aligned");
+    for (int i = 0; i < nseg; ++i) a[i].workspace = workspace;
+    return hip_status(qerl::launch_w4a16_lora_gemm_multi(a, nseg, static_cast<hipStream_t>(stream)),
+                      "w4a16_lora_gemm_multi launch");
 }
 
 float qerl_aqn_sigma(int32_t stage, int32_t num_stages, float sigma_start, float sigma_end) {

@@ -74,7 +74,7 @@ constexpr int kRing = QERL_RING;  // weight chunks in flight per wave (m <= 16)
 
 // counter words at the head of the workspace
 constexpr int kCtrProd = 0, kCtrTReady = 1, kCtrDone = 2, kCtrRow = 4;
-constexpr int64_t kMaxRowBlocks = kGemmCtrBytes / 4 - kCtrRow;
+constexpr int64_t kMaxRowBlocks = kSegCtrBytes / 4 - kCtrRow;
 
 struct DecodePlan {
     int mt, nw, px;
@@ -104,7 +104,9 @@ int64_t cu_count() {
     return cus;
 }
 
-DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
+// slice_rows: the row blocks the CUs are shared by (a multi-segment launch
+// passes the total over its segments, so every segment gets the same slices)
+DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slice_rows = 0) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
@@ -122,7 +124,8 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     // slices: as many units as compute units without going over (a CU that
     // runs two units while others run one sets the time), and the FP32
     // partials below the weight bytes
-    int64_t s = p.row_blocks > 0 ? cu_count() / p.row_blocks : 1;
+    if (slice_rows < p.row_blocks) slice_rows = p.row_blocks;
+    int64_t s = slice_rows > 0 ? cu_count() / slice_rows : 1;
     int64_t s_cap = (k * 9) / (64 * m);
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
@@ -136,7 +139,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
         if (scp % 2 == 0) ++scp;
         p.unit_sc_pitch = scp * 16;
         p.unit_sc = p.rows_per_unit * p.unit_sc_pitch <= kUnitScBytes;
-        p.part_off = kGemmCtrBytes;
+        p.part_off = 0;  // offsets from the segment's data (after the counter head)
         p.tpart_off = align256(p.part_off + p.units * tile);
         p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
         p.bytes = align256(p.t_off + m * (int64_t)r * 4);
@@ -169,7 +172,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
     if (lds < prod) lds = prod;
     p.lds_bytes = lds;
     // workspace after the counters: partial tiles, producer partials, t
-    p.part_off = kGemmCtrBytes;
+    p.part_off = 0;  // offsets from the segment's data (after the counter head)
     p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
     p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
     p.bytes = align256(p.t_off + 2 * 16 * p.rp * 2);  // t16: BF16 hi/lo [2][16][rp]
@@ -177,13 +180,38 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r) {
 }
 
 struct Decode {
-    GemmArgs a;
+    GemmArgs a;      // a.workspace: this segment's data region
     DecodePlan p;
-    __device__ uint32_t *ctr() const { return static_cast<uint32_t *>(a.workspace); }
+    uint32_t *ctrs;  // this segment's counters in the workspace head
+    __device__ uint32_t *ctr() const { return ctrs; }
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
     __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
     __device__ float *t32() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.t_off); }
 };
+
+// One launch over up to kMaxSegments GEMMs that share x (m, k, ldx): segment
+// i owns the workgroups [start[i], start[i + 1]) of the main kernel and
+// [fstart[i], fstart[i + 1]) of finish_kernel's columns; each has its own
+// workspace region (counters first).
+constexpr int kMaxSegments = QERL_MAX_SEGMENTS;
+static_assert(kMaxSegments * kSegCtrBytes == kGemmCtrBytes, "one counter block per segment");
+struct DecodeSet {
+    Decode seg[kMaxSegments];
+    int64_t start[kMaxSegments + 1];
+    int64_t fstart[kMaxSegments + 1];
+    int nseg;
+};
+
+// the segment of this workgroup along x, and the workgroup's index in it
+__device__ __forceinline__ const Decode &pick_segment(const DecodeSet &ds, const int64_t (&first)[kMaxSegments + 1],
+                                                      int64_t &bx) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < kMaxSegments; ++j)
+        if (j < ds.nseg && (int64_t)blockIdx.x >= first[j]) i = j;
+    bx = (int64_t)blockIdx.x - first[i];
+    return ds.seg[i];
+}
 
 // ---- device-coherent access: agent scope, no cache write-back or invalidate ----
 constexpr int kSc1 = 16;  // cache-policy bit: coherent at device scope
@@ -532,18 +560,21 @@ __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *s
 // K32: k % 32 == 0; SPLIT: K is split over several units per row block
 // (slices > 1); LORA: r > 0.
 template <bool K32, bool SPLIT, bool LORA>
-__global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
+__global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSet ds) {
     constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    int64_t bx;
+    const Decode &d = pick_segment(ds, ds.start, bx);
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    if (LORA && (int64_t)blockIdx.x < p.producers) {
-        lora_producer<MT>(d, blockIdx.x, lds);
+    const bool lora = LORA && a.r > 0;  // (segments of one launch may differ)
+    if (lora && bx < p.producers) {
+        lora_producer<MT>(d, bx, lds);
         return;
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
     uint8_t *sc = lds + p.sc_lds_off;
-    const int64_t u = blockIdx.x - p.producers;
+    const int64_t u = bx - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
     const int64_t c_begin = slice * p.cps;
     const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
@@ -608,7 +639,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     // producers lead the grid and are done by now as a rule, so t can be
     // loaded without a round trip of its own.
     uint32_t t_seen = 0;
-    if (LORA && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
+    if (lora && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
 #pragma unroll
     for (int s = 0; s < DR; ++s)
         if (c + s < c_full_end)  // uniform
@@ -640,7 +671,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         return as_bf16x8_d(v);
     };
     bf16x8_t b0[NW];  // the first rank block (read-only input: loaded early)
-    if (LORA)
+    if (lora)
 #pragma unroll
         for (int g = 0; g < NW; ++g) b0[g] = load_b(g, 0);
     __shared__ uint32_t s_flag, s_ready;
@@ -661,7 +692,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         if (tid == 0) s_ready = t_seen;
         __syncthreads();
     }
-    if (LORA && !s_ready) {  // uniform; rare: wait for the last producer
+    if (lora && !s_ready) {  // uniform; rare: wait for the last producer
         if (tid == 0) {
             uint32_t it = 0;
             while (ctr_load(d.ctr() + kCtrTReady) == 0 && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
@@ -688,7 +719,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
         for (int v = 0; v < kRedP; ++v)
             pv[v] = load_f4_coherent(rp, (int)(v * sstride) + (wave_off + lane) * 16);
     }
-    if (LORA) {
+    if (lora) {
         const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(d.t32(), 0, t_pieces * 16, 0x00020000);
         tq[0] = load_i4_coherent(rt, tid * 16);
         tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
@@ -699,7 +730,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     if (SPLIT)
 #pragma unroll
         for (int v = 0; v < kRedP; ++v) asm volatile("" : "+v"(pv[v]));
-    if (LORA) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
+    if (lora) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
     if (SPLIT) {
         acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -719,7 +750,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
     uint16_t *th = reinterpret_cast<uint16_t *>(lds);  // t16 [2][16][rp]: hi, then lo
     uint16_t *tl = th + 16 * p.rp;
-    if (LORA) {  // (the pieces past t16 were loaded as zeros and are not stored)
+    if (lora) {  // (the pieces past t16 were loaded as zeros and are not stored)
         if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
         if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
         __syncthreads();
@@ -748,7 +779,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
     }
     // this row block is done with t16; the last one clears the ready flag
     // and this count for the next call
-    if (LORA && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
+    if (lora && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
         ctr_store(d.ctr() + kCtrTReady, 0u);
         ctr_store(d.ctr() + kCtrDone, 0u);
     }
@@ -759,12 +790,14 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(Decode d) {
 // rows 4 quad .. 4 quad + 3 of column n, which one lane of one tile holds as a
 // float4.  Workgroup: 64 columns x 4 quads (16 rows); t of its rows in LDS.
 template <int MT, int NW>
-__global__ __launch_bounds__(256) void finish_kernel(Decode d) {
+__global__ __launch_bounds__(256) void finish_kernel(DecodeSet ds) {
+    int64_t bx;
+    const Decode &d = pick_segment(ds, ds.fstart, bx);
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     __shared__ float ts[16][kMaxRank];
     const int tid = threadIdx.x;
-    const int64_t n = (int64_t)blockIdx.x * 64 + (tid & 63);
+    const int64_t n = bx * 64 + (tid & 63);
     const int64_t m0 = (int64_t)blockIdx.y * 16;
     const int64_t quad = blockIdx.y * 4 + (tid >> 6);
     for (int64_t i = tid; i < 16 * (int64_t)a.r; i += 256) {
@@ -842,17 +875,19 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
 __shared__ __attribute__((aligned(16))) uint8_t g_dsc[kUnitScBytes];
 
 template <int MT, bool SCL>
-__global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
+__global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(DecodeSet ds) {
     // SCL: the unit's scales staged in LDS (p.unit_sc)
+    int64_t bx;
+    const Decode &d = pick_segment(ds, ds.start, bx);
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    if ((int64_t)blockIdx.x < p.producers) {
-        lora_producer<MT>(d, blockIdx.x, g_dxtile0);
+    if (bx < p.producers) {
+        lora_producer<MT>(d, bx, g_dxtile0);
         return;
     }
     constexpr int NW = 4 * kUnitWaves / kWaves;  // n-tiles per wave of the four-wave tile layout
     constexpr int kPer = kUnitWaves / kWaves;     // unit waves per layout wave
-    const int64_t u = blockIdx.x - p.producers;
+    const int64_t u = bx - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
     const int64_t c_begin = slice * p.cps;
     const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
@@ -902,53 +937,102 @@ __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(Decode d) {
 }
 
 template <int MT>
-hipError_t launch_mfma_units(const Decode &d, hipStream_t stream) {
+hipError_t launch_mfma_units(const DecodeSet &ds, hipStream_t stream) {
+    const Decode &d = ds.seg[0];  // the unit shape and scale staging are shared by the segments
+    const dim3 grid((unsigned)ds.start[ds.nseg]);
     if (d.p.unit_sc)
-        hipLaunchKernelGGL((mfma_unit_kernel<MT, true>), dim3((unsigned)(d.p.producers + d.p.units)),
-                           dim3(64 * kUnitWaves), 0, stream, d);
+        hipLaunchKernelGGL((mfma_unit_kernel<MT, true>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
     else
-        hipLaunchKernelGGL((mfma_unit_kernel<MT, false>), dim3((unsigned)(d.p.producers + d.p.units)),
-                           dim3(64 * kUnitWaves), 0, stream, d);
+        hipLaunchKernelGGL((mfma_unit_kernel<MT, false>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)((d.a.n + 63) / 64), (unsigned)((d.a.m + 15) / 16));
-    hipLaunchKernelGGL((finish_kernel<MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, d);
+    const dim3 fgrid((unsigned)ds.fstart[ds.nseg], (unsigned)((d.a.m + 15) / 16));
+    hipLaunchKernelGGL((finish_kernel<MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, ds);
     return hipGetLastError();
 }
 
 template <bool K32, bool SPLIT, bool LORA>
-hipError_t launch_stream(const Decode &d, hipStream_t stream) {
+hipError_t launch_stream(const DecodeSet &ds, int64_t lds_bytes, hipStream_t stream) {
     auto kern = stream_kernel<K32, SPLIT, LORA>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
-    const int64_t grid = d.p.producers + d.p.units;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreadsD), (size_t)d.p.lds_bytes, stream, d);
+    hipLaunchKernelGGL(kern, dim3((unsigned)ds.start[ds.nseg]), dim3(kThreadsD), (size_t)lds_bytes, stream, ds);
     return hipGetLastError();
 }
 
 template <bool K32>
-hipError_t launch_stream(const Decode &d, hipStream_t stream) {
-    const bool split = d.p.slices > 1, lora = d.a.r > 0;
-    if (split) return lora ? launch_stream<K32, true, true>(d, stream) : launch_stream<K32, true, false>(d, stream);
-    return lora ? launch_stream<K32, false, true>(d, stream) : launch_stream<K32, false, false>(d, stream);
+hipError_t launch_stream(const DecodeSet &ds, int64_t lds_bytes, bool lora, hipStream_t stream) {
+    const bool split = ds.seg[0].p.slices > 1;  // the same for every segment
+    if (split)
+        return lora ? launch_stream<K32, true, true>(ds, lds_bytes, stream)
+                    : launch_stream<K32, true, false>(ds, lds_bytes, stream);
+    return lora ? launch_stream<K32, false, true>(ds, lds_bytes, stream)
+                : launch_stream<K32, false, false>(ds, lds_bytes, stream);
+}
+
+// the plans of a launch over segs[0 .. nseg) (shared x), slices shared
+DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
+    DecodeSet ds{};
+    ds.nseg = nseg;
+    int64_t rows = 0;
+    for (int i = 0; i < nseg; ++i) rows += make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r).row_blocks;
+    ds.start[0] = ds.fstart[0] = 0;
+    char *base = static_cast<char *>(segs[0].workspace);  // one workspace for the launch
+    int64_t data = kGemmCtrBytes;
+    for (int i = 0; i < nseg; ++i) {
+        ds.seg[i].a = segs[i];
+        ds.seg[i].p = make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, rows);
+        ds.seg[i].ctrs = reinterpret_cast<uint32_t *>(base + i * kSegCtrBytes);
+        ds.seg[i].a.workspace = base + data;
+        data += align256(ds.seg[i].p.bytes);
+        ds.start[i + 1] = ds.start[i] + ds.seg[i].p.producers + ds.seg[i].p.units;
+        ds.fstart[i + 1] = ds.fstart[i] + (segs[i].n + 63) / 64;
+    }
+    for (int i = nseg + 1; i <= kMaxSegments; ++i) ds.start[i] = ds.fstart[i] = ds.start[nseg];
+    return ds;
+}
+
+hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
+    int64_t lds = 0;
+    bool lora = false;
+    for (int i = 0; i < ds.nseg; ++i) {
+        const Decode &d = ds.seg[i];
+        if (d.p.row_blocks < 1 || d.p.lds_bytes > kLdsLimit ||
+            d.p.rows_per_unit * 16 * d.p.mt * d.p.units * 4 > 0x7FFFFFFF)
+            return hipErrorInvalidConfiguration;
+        if (d.p.slices != ds.seg[0].p.slices || d.p.unit_sc != ds.seg[0].p.unit_sc) return hipErrorInvalidConfiguration;
+        lds = d.p.lds_bytes > lds ? d.p.lds_bytes : lds;
+        lora = lora || d.a.r > 0;
+    }
+    if (ds.start[ds.nseg] > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    const Decode &d0 = ds.seg[0];
+    if (d0.p.mt == 2) return launch_mfma_units<2>(ds, stream);
+    if (d0.p.mt == 4) return launch_mfma_units<4>(ds, stream);
+    return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, stream) : launch_stream<false>(ds, lds, lora, stream);
 }
 
 }  // namespace
 
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
-    return (size_t)make_decode_plan(m, n, k, r).bytes;
+    return (size_t)(kGemmCtrBytes + make_decode_plan(m, n, k, r).bytes);
 }
 
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
-    const Decode d{a, make_decode_plan(a.m, a.n, a.k, a.r)};
-    if (d.p.row_blocks < 1 || d.p.producers + d.p.units > 0x7FFFFFFF ||
-        d.p.lds_bytes > kLdsLimit ||
-        d.p.rows_per_unit * 16 * d.p.mt * d.p.units * 4 > 0x7FFFFFFF)
-        return hipErrorInvalidConfiguration;
-    if (d.p.mt == 2) return launch_mfma_units<2>(d, stream);
-    if (d.p.mt == 4) return launch_mfma_units<4>(d, stream);
-    return (a.k & 31) == 0 ? launch_stream<true>(d, stream) : launch_stream<false>(d, stream);
+    return launch_decode_set(make_decode_set(&a, 1), stream);
+}
+
+size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg) {
+    int64_t rows = 0;
+    for (int j = 0; j < nseg; ++j) rows += make_decode_plan(m, n[j], k, r[j]).row_blocks;
+    int64_t bytes = kGemmCtrBytes;
+    for (int j = 0; j < nseg; ++j) bytes += align256(make_decode_plan(m, n[j], k, r[j], rows).bytes);
+    return (size_t)bytes;
+}
+
+hipError_t launch_decode_multi(const GemmArgs *segs, int nseg, hipStream_t stream) {
+    if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
+    return launch_decode_set(make_decode_set(segs, nseg), stream);
 }
 
 }  // namespace qerl

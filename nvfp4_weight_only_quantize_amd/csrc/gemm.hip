@@ -311,6 +311,27 @@ size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
     return (size_t)make_plan(m, n, k, r).bytes;
 }
 
+size_t gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg) {
+    if (m > kDecodeMaxM) {  // one segment after another, each with the whole workspace
+        size_t b = 0;
+        for (int j = 0; j < nseg; ++j) {
+            const size_t bj = gemm_workspace_bytes(m, n[j], k, r[j]);
+            b = bj > b ? bj : b;
+        }
+        return b;
+    }
+    return decode_multi_workspace_bytes(m, k, n, r, nseg);
+}
+
+hipError_t launch_w4a16_lora_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream) {
+    if (segs[0].m <= kDecodeMaxM) return launch_decode_multi(segs, nseg, stream);
+    for (int i = 0; i < nseg; ++i) {  // large m: the launches are large already
+        const hipError_t e = launch_w4a16_lora_gemm(segs[i], stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
     if (a.m <= kDecodeMaxM) return launch_decode(a, stream);
     const Gemm g{a, make_plan(a.m, a.n, a.k, a.r)};

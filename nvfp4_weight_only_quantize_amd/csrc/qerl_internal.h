@@ -34,15 +34,25 @@ struct GemmArgs {
     void *workspace;
 };
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
-// Every GEMM workspace starts with this many bytes of counters for the decode
-// path's in-kernel split-K reduction: zero before first use, left zero by
-// every call (the other path never writes them).
-constexpr int64_t kGemmCtrBytes = 64 * 1024;
+// Every GEMM workspace starts with the counters of the decode path's in-kernel
+// reductions: kSegCtrBytes for each of up to QERL_MAX_SEGMENTS projections of
+// one call, at fixed places, so that any sequence of calls (single or multi,
+// any shapes) on one workspace finds them zero; every call leaves them zero
+// and nothing else is stored there.  A call's data follow the counters.
+#define QERL_MAX_SEGMENTS 4
+constexpr int64_t kSegCtrBytes = 64 * 1024;
+constexpr int64_t kGemmCtrBytes = QERL_MAX_SEGMENTS * kSegCtrBytes;
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
 // decode batches (m <= kDecodeMaxM): HBM-streaming path in decode.hip
 constexpr int64_t kDecodeMaxM = 64;
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream);
+// Several GEMMs sharing x (m, k, ldx) in one launch: segs[i] differ only in
+// the weight, LoRA and output fields and all carry the same workspace.
+size_t gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
+hipError_t launch_w4a16_lora_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
+size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
+hipError_t launch_decode_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
 
 // ---- AQN RMSNorm ----
 struct AqnArgs {

@@ -122,3 +122,39 @@ def test_workspace_queries():
     assert q.w4a16_lora_gemm_workspace_size(64, 3584, 3584, 32) >= 64 * 32 * 4
     # decode sizes keep FP32 split-K partials: at least one m x n slice
     assert q.w4a16_lora_gemm_workspace_size(1, 3584, 3584, 0) >= 3584 * 4
+
+
+def _multi(nseg=3, segs_kw=None, **kw):
+    a = dict(x=FAKE, m=2, k=64, ldx=64, ws=FAKE, ws_bytes=1 << 24, stream=None, segs=True)
+    a.update(kw)
+    arr = (q.GemmSegment * max(nseg, 1))()
+    for i in range(max(nseg, 1)):
+        s = dict(packed=FAKE, scales=FAKE, ts=FAKE, n=32 + 16 * i, A=FAKE, B=FAKE, r=4, lam=2.0, y=FAKE, ldy=64)
+        s.update((segs_kw or {}).get(i, {}))
+        arr[i] = q.GemmSegment(s["packed"], s["scales"], s["ts"], s["n"], s["A"], s["B"], s["r"], s["lam"],
+                               s["y"], s["ldy"])
+    return q.lib().qerl_w4a16_lora_gemm_multi(P(a["x"]), a["m"], a["k"], a["ldx"], arr if a["segs"] else None,
+                                              nseg, P(a["ws"]), a["ws_bytes"], P(a["stream"]))
+
+
+@pytest.mark.parametrize("nseg,segs_kw,kw,status", [
+    (3, None, dict(segs=False), 1), (0, None, {}, 4), (5, None, {}, 4), (3, None, dict(x=None), 1),
+    (3, {1: dict(y=None)}, {}, 1), (3, {2: dict(r=200)}, {}, 4), (3, {0: dict(n=0)}, {}, 2),
+    (3, {1: dict(A=FAKE + 4)}, {}, 3), (3, {2: dict(ldy=8)}, {}, 2), (2, None, dict(k=40, ldx=40), 2),
+    (3, None, dict(ws=None), 5), (3, None, dict(ws_bytes=64), 5), (3, None, dict(ws=FAKE + 8), 3),
+])
+def test_gemm_multi_argument_errors(nseg, segs_kw, kw, status):
+    assert _multi(nseg, segs_kw, **kw) == status
+    assert q.lib().qerl_last_error()
+
+
+def test_gemm_multi_workspace_query():
+    shapes = [(3584, 32), (512, 32), (512, 32)]
+    # decode sizes: one region per segment (each with its own counters)
+    for m in (1, 8, 64):
+        total = q.w4a16_lora_gemm_multi_workspace_size(m, 3584, shapes)
+        assert total >= 3 * 64 * 1024
+    # large m runs the segments in turn over one region: the largest single need
+    big = q.w4a16_lora_gemm_multi_workspace_size(100, 3584, shapes)
+    assert big == max(q.w4a16_lora_gemm_workspace_size(100, n, 3584, r) for n, r in shapes)
+    assert q.lib().qerl_w4a16_lora_gemm_multi_workspace_size(1, 3584, None, 3) == 0

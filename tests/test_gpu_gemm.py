@@ -211,7 +211,7 @@ def test_shared_workspace_sequence_is_deterministic():
             y = q.w4a16_lora_gemm(x, L.wq, L.a, L.b, L.lam, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(y, fresh[i]), f"case {cases[i]}"
-    assert int(torch.count_nonzero(ws[:64 * 1024])) == 0
+    assert int(torch.count_nonzero(ws[:256 * 1024])) == 0  # the counter head
     for i in (0, 3):
         m, n, k, r = cases[i]
         assert_gemm_close(bf16_to_f64(fresh[i]), layers[i].ref(synth.bf16_bits(xs[i].cpu())), f"case {cases[i]}")
