@@ -189,29 +189,21 @@ struct Decode {
     __device__ float *t32() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.t_off); }
 };
 
-// One launch over up to kMaxSegments GEMMs that share x (m, k, ldx): segment
-// i owns the workgroups [start[i], start[i + 1]) of the main kernel and
-// [fstart[i], fstart[i + 1]) of finish_kernel's columns; each has its own
-// workspace region (counters first).
+// One launch over up to kMaxSegments GEMMs that share x (m, k, ldx): the
+// segment is a grid dimension (y for the main kernels, z for finish_kernel),
+// so a workgroup reads its segment's fields without first reading a table;
+// the grid is as wide as the widest segment and the surplus workgroups of
+// the others exit at once.  Each segment has its own counters and data.
+// A one-segment launch takes a one-segment set, so its kernel arguments stay
+// as small as one plan.
 constexpr int kMaxSegments = QERL_MAX_SEGMENTS;
 static_assert(kMaxSegments * kSegCtrBytes == kGemmCtrBytes, "one counter block per segment");
-struct DecodeSet {
-    Decode seg[kMaxSegments];
-    int64_t start[kMaxSegments + 1];
-    int64_t fstart[kMaxSegments + 1];
+template <int NS>
+struct DecodeSetN {
+    Decode seg[NS];
     int nseg;
 };
-
-// the segment of this workgroup along x, and the workgroup's index in it
-__device__ __forceinline__ const Decode &pick_segment(const DecodeSet &ds, const int64_t (&first)[kMaxSegments + 1],
-                                                      int64_t &bx) {
-    int i = 0;
-#pragma unroll
-    for (int j = 1; j < kMaxSegments; ++j)
-        if (j < ds.nseg && (int64_t)blockIdx.x >= first[j]) i = j;
-    bx = (int64_t)blockIdx.x - first[i];
-    return ds.seg[i];
-}
+using DecodeSet = DecodeSetN<kMaxSegments>;
 
 // ---- device-coherent access: agent scope, no cache write-back or invalidate ----
 constexpr int kSc1 = 16;  // cache-policy bit: coherent at device scope
@@ -559,15 +551,17 @@ __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *s
 
 // K32: k % 32 == 0; SPLIT: K is split over several units per row block
 // (slices > 1); LORA: r > 0.
-template <bool K32, bool SPLIT, bool LORA>
-__global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSet ds) {
+template <int NS, bool K32, bool SPLIT, bool LORA>
+__global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    int64_t bx;
-    const Decode &d = pick_segment(ds, ds.start, bx);
+    const Decode &d = ds.seg[NS == 1 ? 0u : blockIdx.y];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
-    const bool lora = LORA && a.r > 0;  // (segments of one launch may differ)
+    const int64_t bx = blockIdx.x;
+    if (NS > 1 && bx >= p.producers + p.units) return;  // past a narrower segment
+    // (segments of one launch may differ; a one-segment launch has LORA == (r > 0))
+    const bool lora = LORA && (NS == 1 || a.r > 0);
     if (lora && bx < p.producers) {
         lora_producer<MT>(d, bx, lds);
         return;
@@ -789,12 +783,13 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSet ds) {
 // order) + lora_scale * sum_j t[m][j] B[n][j]).  Thread (n, quad) handles the
 // rows 4 quad .. 4 quad + 3 of column n, which one lane of one tile holds as a
 // float4.  Workgroup: 64 columns x 4 quads (16 rows); t of its rows in LDS.
-template <int MT, int NW>
-__global__ __launch_bounds__(256) void finish_kernel(DecodeSet ds) {
-    int64_t bx;
-    const Decode &d = pick_segment(ds, ds.fstart, bx);
+template <int NS, int MT, int NW>
+__global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
+    const Decode &d = ds.seg[NS == 1 ? 0u : blockIdx.z];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
+    const int64_t bx = blockIdx.x;
+    if (NS > 1 && bx * 64 >= a.n) return;  // past a narrower segment
     __shared__ float ts[16][kMaxRank];
     const int tid = threadIdx.x;
     const int64_t n = bx * 64 + (tid & 63);
@@ -874,11 +869,10 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
 // weights they scale
 __shared__ __attribute__((aligned(16))) uint8_t g_dsc[kUnitScBytes];
 
+// one workgroup of mfma_unit_kernel: a LoRA producer or a unit
+// SCL: the unit's scales staged in LDS (p.unit_sc)
 template <int MT, bool SCL>
-__global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(DecodeSet ds) {
-    // SCL: the unit's scales staged in LDS (p.unit_sc)
-    int64_t bx;
-    const Decode &d = pick_segment(ds, ds.start, bx);
+__device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     if (bx < p.producers) {
@@ -936,33 +930,51 @@ __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(DecodeSet ds
             if (16 * i + 4 * lq < a.m) tile[(((wave / kPer) * MT + i) * NW + (4 * wave + j) % NW) * 64] = acc[i][j];
 }
 
-template <int MT>
-hipError_t launch_mfma_units(const DecodeSet &ds, hipStream_t stream) {
+template <int NS, int MT, bool SCL>
+__global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(DecodeSetN<NS> ds) {
+    const Decode &d = ds.seg[NS == 1 ? 0u : blockIdx.y];
+    if (NS > 1 && (int64_t)blockIdx.x >= d.p.producers + d.p.units) return;  // past a narrower segment
+    mfma_unit<MT, SCL>(d, blockIdx.x);
+}
+
+template <int MT, int NS>
+hipError_t launch_mfma_units(const DecodeSetN<NS> &ds, hipStream_t stream) {
     const Decode &d = ds.seg[0];  // the unit shape and scale staging are shared by the segments
-    const dim3 grid((unsigned)ds.start[ds.nseg]);
+    int64_t blocks = 0, fblocks = 0;
+    for (int i = 0; i < ds.nseg; ++i) {
+        const int64_t b = ds.seg[i].p.producers + ds.seg[i].p.units, f = (ds.seg[i].a.n + 63) / 64;
+        blocks = b > blocks ? b : blocks;
+        fblocks = f > fblocks ? f : fblocks;
+    }
+    const dim3 grid((unsigned)blocks, (unsigned)ds.nseg);
     if (d.p.unit_sc)
-        hipLaunchKernelGGL((mfma_unit_kernel<MT, true>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
+        hipLaunchKernelGGL((mfma_unit_kernel<NS, MT, true>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
     else
-        hipLaunchKernelGGL((mfma_unit_kernel<MT, false>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
+        hipLaunchKernelGGL((mfma_unit_kernel<NS, MT, false>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)ds.fstart[ds.nseg], (unsigned)((d.a.m + 15) / 16));
-    hipLaunchKernelGGL((finish_kernel<MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, ds);
+    const dim3 fgrid((unsigned)fblocks, (unsigned)((d.a.m + 15) / 16), (unsigned)ds.nseg);
+    hipLaunchKernelGGL((finish_kernel<NS, MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, ds);
     return hipGetLastError();
 }
 
-template <bool K32, bool SPLIT, bool LORA>
-hipError_t launch_stream(const DecodeSet &ds, int64_t lds_bytes, hipStream_t stream) {
-    auto kern = stream_kernel<K32, SPLIT, LORA>;
+template <bool K32, bool SPLIT, bool LORA, int NS>
+hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_t stream) {
+    auto kern = stream_kernel<NS, K32, SPLIT, LORA>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(kern, dim3((unsigned)ds.start[ds.nseg]), dim3(kThreadsD), (size_t)lds_bytes, stream, ds);
+    int64_t blocks = 0;
+    for (int i = 0; i < ds.nseg; ++i) {
+        const int64_t b = ds.seg[i].p.producers + ds.seg[i].p.units;
+        blocks = b > blocks ? b : blocks;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ds.nseg), dim3(kThreadsD), (size_t)lds_bytes, stream, ds);
     return hipGetLastError();
 }
 
-template <bool K32>
-hipError_t launch_stream(const DecodeSet &ds, int64_t lds_bytes, bool lora, hipStream_t stream) {
+template <bool K32, int NS>
+hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, bool lora, hipStream_t stream) {
     const bool split = ds.seg[0].p.slices > 1;  // the same for every segment
     if (split)
         return lora ? launch_stream<K32, true, true>(ds, lds_bytes, stream)
@@ -977,7 +989,6 @@ DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
     ds.nseg = nseg;
     int64_t rows = 0;
     for (int i = 0; i < nseg; ++i) rows += make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r).row_blocks;
-    ds.start[0] = ds.fstart[0] = 0;
     char *base = static_cast<char *>(segs[0].workspace);  // one workspace for the launch
     int64_t data = kGemmCtrBytes;
     for (int i = 0; i < nseg; ++i) {
@@ -986,11 +997,16 @@ DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
         ds.seg[i].ctrs = reinterpret_cast<uint32_t *>(base + i * kSegCtrBytes);
         ds.seg[i].a.workspace = base + data;
         data += align256(ds.seg[i].p.bytes);
-        ds.start[i + 1] = ds.start[i] + ds.seg[i].p.producers + ds.seg[i].p.units;
-        ds.fstart[i + 1] = ds.fstart[i] + (segs[i].n + 63) / 64;
     }
-    for (int i = nseg + 1; i <= kMaxSegments; ++i) ds.start[i] = ds.fstart[i] = ds.start[nseg];
     return ds;
+}
+
+template <int NS>
+hipError_t launch_checked(const DecodeSetN<NS> &ds, int64_t lds, bool lora, hipStream_t stream) {
+    const Decode &d0 = ds.seg[0];
+    if (d0.p.mt == 2) return launch_mfma_units<2>(ds, stream);
+    if (d0.p.mt == 4) return launch_mfma_units<4>(ds, stream);
+    return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, stream) : launch_stream<false>(ds, lds, lora, stream);
 }
 
 hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
@@ -1005,11 +1021,10 @@ hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
         lds = d.p.lds_bytes > lds ? d.p.lds_bytes : lds;
         lora = lora || d.a.r > 0;
     }
-    if (ds.start[ds.nseg] > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    const Decode &d0 = ds.seg[0];
-    if (d0.p.mt == 2) return launch_mfma_units<2>(ds, stream);
-    if (d0.p.mt == 4) return launch_mfma_units<4>(ds, stream);
-    return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, stream) : launch_stream<false>(ds, lds, lora, stream);
+    for (int i = 0; i < ds.nseg; ++i)
+        if (ds.seg[i].p.producers + ds.seg[i].p.units > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    if (ds.nseg == 1) return launch_checked(DecodeSetN<1>{{ds.seg[0]}, 1}, lds, lora, stream);
+    return launch_checked(ds, lds, lora, stream);
 }
 
 }  // namespace
