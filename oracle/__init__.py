@@ -72,6 +72,8 @@ def _load():
     lib.oracle_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, flt, i64, P, P, i32, flt,
                                            P, i64, P, i32]
     lib.oracle_w4a16_lora_gemm.restype = i32
+    lib.oracle_w4a16_lora_gemm_f64.argtypes = lib.oracle_w4a16_lora_gemm.argtypes
+    lib.oracle_w4a16_lora_gemm_f64.restype = i32
     lib.oracle_aqn_sigma.argtypes = [i32, i32, dbl, dbl]
     lib.oracle_aqn_sigma.restype = dbl
     lib.oracle_philox4x64_10.argtypes = [P, P, P]
@@ -147,9 +149,13 @@ def nvfp4_quantize(w_bits, flags: int = SCALE_ROUND_UP, tensor_scale_in: float |
 
 # ------------------------------------------------------------ W4A16 GEMM --
 def w4a16_lora_gemm(x_bits, packed, scales, s_t, lora_a_bits=None, lora_b_bits=None,
-                    lora_scale: float = 0.0, rows=None, threads: int = 0) -> np.ndarray:
-    """fp64 y[rows, N] = x w^T + lora_scale (x A^T) B^T with w dequantized exactly."""
-    x = np.ascontiguousarray(_bits16(x_bits))
+                    lora_scale: float = 0.0, rows=None, threads: int = 0, x_f64=None) -> np.ndarray:
+    """fp64 y[rows, N] = x w^T + lora_scale (x A^T) B^T with w dequantized exactly.
+    x is BF16 bits, or (x_bits None) the fp64 activations x_f64."""
+    if x_bits is None:
+        x = np.ascontiguousarray(np.asarray(x_f64, dtype=np.float64))
+    else:
+        x = np.ascontiguousarray(_bits16(x_bits))
     m, k = x.shape
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     scales = np.ascontiguousarray(scales, dtype=np.uint8)
@@ -170,7 +176,8 @@ def w4a16_lora_gemm(x_bits, packed, scales, s_t, lora_a_bits=None, lora_b_bits=N
         rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         nrows = rows_arr.shape[0]
     y = np.zeros((nrows, n), dtype=np.float64)
-    rc = _load().oracle_w4a16_lora_gemm(
+    fn = _load().oracle_w4a16_lora_gemm if x_bits is not None else _load().oracle_w4a16_lora_gemm_f64
+    rc = fn(
         _ptr(x), m, k, k, _ptr(packed), _ptr(scales), float(s_t), n,
         None if a is None else _ptr(a), None if b is None else _ptr(b), r, float(lora_scale),
         None if rows_arr is None else _ptr(rows_arr), nrows, _ptr(y), int(threads))
@@ -208,6 +215,15 @@ def rmsnorm(x_bits, w_eff, eps: float) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_rmsnorm rejected its arguments")
     return y
+
+
+def rmsnorm_w4a16_lora_gemm(x_bits, norm_weight, eps: float, packed, scales, s_t, lora_a_bits=None,
+                            lora_b_bits=None, lora_scale: float = 0.0, rows=None, threads: int = 0) -> np.ndarray:
+    """fp64 y = W4A16+LoRA layer of RMSNorm(x) with scale vector norm_weight:
+    the norm's fp64 output, unrounded, is the layer's input."""
+    xn = rmsnorm(x_bits, norm_weight, eps)
+    return w4a16_lora_gemm(None, packed, scales, s_t, lora_a_bits, lora_b_bits, lora_scale, rows=rows,
+                           threads=threads, x_f64=xn)
 
 
 def aqn_rmsnorm(x_bits, weight, eps: float, sigma: float, seed: int, step: int, layer: int):

@@ -277,12 +277,19 @@ int oracle_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
 /* ------------------------------------------------------------------------ */
 /* y[m, n] = sum_k x[m,k] * what[n,k]  +  lora_scale * sum_j t[m,j] * B[n,j],
  * t[m, j] = sum_k x[m,k] * A[j,k],  what = e2m1 * e4m3 * s_t (exact in fp64).
- * x is [M, K] bf16 (row stride ldx), A is [r, K] bf16, B is [N, r] bf16.
+ * x is [M, K] bf16 (row stride ldx) -- or fp64 for oracle_w4a16_lora_gemm_f64,
+ * the same definition on activations given in fp64 (the output of a norm
+ * before any rounding) --, A is [r, K] bf16, B is [N, r] bf16.
  * The layer has no bias.  Only the rows listed in rows[] (or all rows when
  * rows is NULL) are evaluated; y is [nrows, N] fp64.                        */
 
+/* x[m, kk]: the fp64 activations when given, else the BF16 ones */
+static double x_elem(const uint16_t *xb, const double *xd, int64_t ldx, int64_t m, int64_t kk) {
+    return xd ? xd[m * ldx + kk] : oracle_bf16_decode(xb[m * ldx + kk]);
+}
+
 typedef struct {
-    const uint16_t *x; int64_t k, ldx;
+    const uint16_t *x; const double *xd; int64_t k, ldx;
     const uint8_t *packed, *scales; double s_t; int64_t n;
     const uint16_t *b; int r; double lora_scale;
     const int64_t *rows; int64_t nrows;
@@ -304,9 +311,8 @@ static void gemm_cols(void *p, int64_t n0, int64_t n1) {
         }
         for (int64_t i = 0; i < c->nrows; ++i) {
             int64_t m = c->rows ? c->rows[i] : i;
-            const uint16_t *xr = c->x + m * c->ldx;
             double acc = 0.0;
-            for (int64_t kk = 0; kk < c->k; ++kk) acc += oracle_bf16_decode(xr[kk]) * wrow[kk];
+            for (int64_t kk = 0; kk < c->k; ++kk) acc += x_elem(c->x, c->xd, c->ldx, m, kk) * wrow[kk];
             double lora = 0.0;
             for (int j = 0; j < c->r; ++j)
                 lora += c->t[i * c->r + j] * oracle_bf16_decode(c->b[n * c->r + j]);
@@ -316,11 +322,11 @@ static void gemm_cols(void *p, int64_t n0, int64_t n1) {
     free(wrow);
 }
 
-int oracle_w4a16_lora_gemm(const uint16_t *x, int64_t m, int64_t k, int64_t ldx,
-                           const uint8_t *packed, const uint8_t *scales, float s_t, int64_t n,
-                           const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
-                           const int64_t *rows, int64_t nrows, double *y, int threads) {
-    if (!x || !packed || !scales || !y || m <= 0 || n <= 0 || k <= 0 || k % 16 || ldx < k || r < 0)
+static int gemm_impl(const uint16_t *x, const double *xd, int64_t m, int64_t k, int64_t ldx,
+                     const uint8_t *packed, const uint8_t *scales, float s_t, int64_t n,
+                     const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
+                     const int64_t *rows, int64_t nrows, double *y, int threads) {
+    if ((!x && !xd) || !packed || !scales || !y || m <= 0 || n <= 0 || k <= 0 || k % 16 || ldx < k || r < 0)
         return -1;
     if (r > 0 && (!lora_a || !lora_b)) return -1;
     if (!rows) nrows = m;
@@ -335,15 +341,33 @@ int oracle_w4a16_lora_gemm(const uint16_t *x, int64_t m, int64_t k, int64_t ldx,
         for (int j = 0; j < r; ++j) {
             double acc = 0.0;
             for (int64_t kk = 0; kk < k; ++kk)
-                acc += oracle_bf16_decode(x[mm * ldx + kk]) * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
+                acc += x_elem(x, xd, ldx, mm, kk) * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
             t[i * r + j] = acc;
         }
     }
-    gemm_ctx c = {x, k, ldx, packed, scales, (double)s_t, n, lora_b, r, (double)lora_scale,
+    gemm_ctx c = {x, xd, k, ldx, packed, scales, (double)s_t, n, lora_b, r, (double)lora_scale,
                   rows, nrows, t, y};
     parallel_range(threads, n, gemm_cols, &c);
     free(t);
     return 0;
+}
+
+int oracle_w4a16_lora_gemm(const uint16_t *x, int64_t m, int64_t k, int64_t ldx,
+                           const uint8_t *packed, const uint8_t *scales, float s_t, int64_t n,
+                           const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
+                           const int64_t *rows, int64_t nrows, double *y, int threads) {
+    if (!x) return -1;
+    return gemm_impl(x, NULL, m, k, ldx, packed, scales, s_t, n, lora_a, lora_b, r, lora_scale, rows, nrows, y,
+                     threads);
+}
+
+int oracle_w4a16_lora_gemm_f64(const double *x, int64_t m, int64_t k, int64_t ldx,
+                               const uint8_t *packed, const uint8_t *scales, float s_t, int64_t n,
+                               const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
+                               const int64_t *rows, int64_t nrows, double *y, int threads) {
+    if (!x) return -1;
+    return gemm_impl(NULL, x, m, k, ldx, packed, scales, s_t, n, lora_a, lora_b, r, lora_scale, rows, nrows, y,
+                     threads);
 }
 
 /* ------------------------------------------------------------------------ */

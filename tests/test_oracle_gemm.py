@@ -139,3 +139,44 @@ def test_block_diagonal_lora_equals_two_separate_loras():
     u = oracle.w4a16_lora_gemm(x, packed[n:], scales[n:], s_t, au, bu, lam)
     sep = np.concatenate([g, u], axis=1)
     np.testing.assert_allclose(fused, sep, rtol=1e-12, atol=1e-14 * np.abs(base).max())
+
+
+# ---- fp64 activations and the RMSNorm + layer composite ----
+@pytest.mark.parametrize("shape", [(3, 40, 256, 8), (16, 64, 512, 0)])
+def test_fp64_activations_match_torch_float64(shape):
+    # activations that are not BF16 values (a norm's output before rounding)
+    m, n, k, r = shape
+    _, packed, scales, s_t, a, b = _layer(1, n, k, r, seed=61 + k)
+    x = np.random.default_rng(62).standard_normal((m, k)) * np.exp(np.random.default_rng(63).standard_normal(k))
+    y = oracle.w4a16_lora_gemm(None, packed, scales, s_t, a, b, 1.5, threads=2, x_f64=x)
+    xd = torch.from_numpy(x)
+    ref = xd @ torch.from_numpy(dequant_f64(packed, scales, s_t)).T
+    if r:
+        ref = ref + 1.5 * ((xd @ torch.from_numpy(bf16_bits_to_f64(a)).T) @ torch.from_numpy(bf16_bits_to_f64(b)).T)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-10, atol=1e-12 * np.abs(ref.numpy()).max())
+
+
+def test_rmsnorm_layer_composite_matches_torch():
+    # RMSNorm (torch's rms_norm in fp64, scale vector w) followed by the layer
+    # (torch fp64 matmul on the independent dequantization)
+    m, n, k, r = 5, 48, 256, 16
+    x, packed, scales, s_t, a, b = _layer(m, n, k, r, seed=71, x_outliers=0.01)
+    w = (1.0 + 0.1 * np.random.default_rng(72).standard_normal(k)).astype(np.float32)
+    y = oracle.rmsnorm_w4a16_lora_gemm(x, w, 1e-6, packed, scales, s_t, a, b, 2.0)
+    xn = torch.nn.functional.rms_norm(torch.from_numpy(bf16_bits_to_f64(x)), (k,),
+                                      weight=torch.from_numpy(w.astype(np.float64)), eps=1e-6)
+    ref = xn @ torch.from_numpy(dequant_f64(packed, scales, s_t)).T
+    ref = ref + 2.0 * ((xn @ torch.from_numpy(bf16_bits_to_f64(a)).T) @ torch.from_numpy(bf16_bits_to_f64(b)).T)
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-9, atol=1e-12 * np.abs(ref.numpy()).max())
+
+
+def test_rmsnorm_layer_composite_row_scale_invariance():
+    # RMSNorm makes each output row invariant under scaling its input row by 2^j
+    m, n, k, r = 3, 32, 128, 4
+    x, packed, scales, s_t, a, b = _layer(m, n, k, r, seed=81)
+    w = np.linspace(0.5, 1.5, k).astype(np.float32)
+    y = oracle.rmsnorm_w4a16_lora_gemm(x, w, 1e-30, packed, scales, s_t, a, b, 2.0)
+    xs = bf16_bits_to_f64(x) * np.array([[4.0], [0.25], [1.0]])
+    xs_bits = synth.bf16_bits(torch.from_numpy(xs).to(torch.bfloat16))
+    y2 = oracle.rmsnorm_w4a16_lora_gemm(xs_bits, w, 1e-30, packed, scales, s_t, a, b, 2.0)
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-14 * np.abs(y).max())
