@@ -189,6 +189,39 @@ qerl_status qerl_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k,
                                        const qerl_gemm_segment *segs, int32_t nseg, void *workspace,
                                        size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace qerl_rmsnorm_w4a16_lora_gemm_multi needs (reads
+ * n and r of segs[0 .. nseg)). */
+size_t qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qerl_gemm_segment *segs,
+                                                         int32_t nseg);
+
+/*
+ * An RMSNorm and the projections that read its output, in one call: with
+ *   xn[i, c] = x[i, c] / sqrt(mean_c x[i, c]^2 + eps) * norm_weight[c]
+ * each segment i < nseg gets what qerl_w4a16_lora_gemm computes for xn and
+ * segs[i].  This is the norm of qerl_aqn_rmsnorm with its scale vector given:
+ * AQN's noise lives in the norm's scale parameters (dataforcee page; 1kpapers
+ * "Summary"), one vector per (seed, step, layer), so norm_weight is the
+ * vector qerl_aqn_noisy_weight returns for the current noise stage (or the
+ * plain weight for sigma = 0), drawn once per step rather than once per call.
+ * For m <= 16 and k % 32 == 0 the norm runs inside the decode launch: each row's
+ * 1 / rms is a factor of its whole output row, so the product takes
+ * bf16(x * norm_weight) and the FP32 result is scaled by 1 / rms in the
+ * epilogue (the LoRA term likewise).  Otherwise the norm is a launch of its
+ * own writing BF16 xn (as qerl_aqn_rmsnorm's y_bf16) into the workspace,
+ * followed by qerl_w4a16_lora_gemm_multi on it.  The two roundings differ in
+ * the last bits of y, within the GEMM's tolerance.
+ *   x_bf16        [m, k] (row stride ldx): the norm's input
+ *   norm_weight   FP32 [k], 16-byte aligned
+ *   segs, workspace as for qerl_w4a16_lora_gemm_multi (the same 256 KiB
+ *                 counter head), workspace of at least the size query
+ * Requires the conditions of qerl_w4a16_lora_gemm_multi, k <=
+ * QERL_MAX_NORM_WIDTH, eps > 0 and finite.
+ */
+qerl_status qerl_rmsnorm_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                               const float *norm_weight, float eps,
+                                               const qerl_gemm_segment *segs, int32_t nseg,
+                                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* ----------------------------------------------------------------------- */
 /* AQN RMSNorm                                                               */
 /* ----------------------------------------------------------------------- */
@@ -223,6 +256,18 @@ qerl_status qerl_aqn_rmsnorm(const void *x_bf16, int64_t m, int64_t h, int64_t l
                              uint64_t seed, uint64_t step, uint32_t layer_id,
                              float *y_f32, void *y_bf16, int64_t ldy,
                              float *noisy_weight_out, void *stream);
+
+/*
+ * The AQN scale vector alone: noisy_weight_out[c] = weight[c] + sigma * z[c],
+ * with z exactly as qerl_aqn_rmsnorm draws it (the same seed, step and
+ * layer_id give the vector that call multiplies by, bit for bit).  For
+ * qerl_rmsnorm_w4a16_lora_gemm_multi, which takes the vector as its norm
+ * weight.
+ *   weight, noisy_weight_out  FP32 [h] device arrays (may be the same array)
+ * Requires 1 <= h <= QERL_MAX_NORM_WIDTH, sigma >= 0 and finite.
+ */
+qerl_status qerl_aqn_noisy_weight(const float *weight, int64_t h, float sigma, uint64_t seed, uint64_t step,
+                                  uint32_t layer_id, float *noisy_weight_out, void *stream);
 
 /* ----------------------------------------------------------------------- */
 /* diagnostics                                                               */

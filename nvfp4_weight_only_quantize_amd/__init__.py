@@ -66,6 +66,13 @@ def lib() -> ctypes.CDLL:
     L.qerl_w4a16_lora_gemm_multi_workspace_size.restype = sz
     L.qerl_w4a16_lora_gemm_multi.argtypes = [P, i64, i64, i64, ctypes.POINTER(GemmSegment), i32, P, sz, P]
     L.qerl_w4a16_lora_gemm_multi.restype = ctypes.c_int
+    L.qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size.argtypes = [i64, i64, ctypes.POINTER(GemmSegment), i32]
+    L.qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size.restype = sz
+    L.qerl_rmsnorm_w4a16_lora_gemm_multi.argtypes = [P, i64, i64, i64, P, f32, ctypes.POINTER(GemmSegment), i32,
+                                                     P, sz, P]
+    L.qerl_rmsnorm_w4a16_lora_gemm_multi.restype = ctypes.c_int
+    L.qerl_aqn_noisy_weight.argtypes = [P, i64, f32, u64, u64, u32, P, P]
+    L.qerl_aqn_noisy_weight.restype = ctypes.c_int
     L.qerl_aqn_sigma.argtypes = [i32, i32, f32, f32]
     L.qerl_aqn_sigma.restype = f32
     L.qerl_aqn_rmsnorm.argtypes = [P, i64, i64, i64, P, f32, f32, u64, u64, u32, P, P, i64, P, P]
@@ -273,7 +280,58 @@ def w4a16_lora_gemm_multi(x: torch.Tensor, segments, outs=None, workspace: torch
     return outs
 
 
+def rmsnorm_w4a16_lora_gemm_multi_workspace_size(m: int, k: int, shapes) -> int:
+    """shapes: (n, r) per segment."""
+    arr = (GemmSegment * len(shapes))()
+    for i, (n, r) in enumerate(shapes):
+        arr[i].n, arr[i].r = int(n), int(r)
+    return int(lib().qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(shapes)))
+
+
+def rmsnorm_w4a16_lora_gemm_multi(x: torch.Tensor, norm_weight: torch.Tensor, eps: float, segments, outs=None,
+                                  workspace: torch.Tensor | None = None, stream=None):
+    """RMSNorm of x with scale vector norm_weight (FP32 [K]; the AQN noisy
+    weight) and then the projections of w4a16_lora_gemm_multi on the normed
+    rows, in one call (for M <= 16 and K % 32 == 0 one launch)."""
+    _need(x, "x", torch.bfloat16, 2)
+    if not 1 <= len(segments) <= MAX_SEGMENTS:
+        raise ValueError(f"1 to {MAX_SEGMENTS} segments")
+    dev = x.device
+    m, k = x.shape
+    _need(norm_weight, "norm_weight", torch.float32, 1, dev)
+    if norm_weight.numel() != k or not norm_weight.is_contiguous():
+        raise ValueError("norm_weight must be a contiguous [K] tensor")
+    if outs is None:
+        outs = [torch.empty((m, wq.shape[0]), dtype=torch.bfloat16, device=dev) for wq, *_ in segments]
+    arr = _segments(x, segments, outs)
+    need = int(lib().qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(segments)))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qerl_rmsnorm_w4a16_lora_gemm_multi(_ptr(x), m, k, _rows(x, "x"), _ptr(norm_weight), float(eps), arr,
+                                                    len(segments), _ptr(workspace), ws_bytes, _stream(stream, dev)))
+    return outs
+
+
 # -------------------------------------------------------------------- AQN --
+def aqn_noisy_weight(weight: torch.Tensor, sigma: float, seed: int = 0, step: int = 0, layer_id: int = 0,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """w + sigma z, the scale vector aqn_rmsnorm multiplies by for the same
+    (seed, step, layer_id)."""
+    _need(weight, "weight", torch.float32, 1)
+    dev = weight.device
+    if not weight.is_contiguous():
+        raise ValueError("weight must be contiguous")
+    if out is None:
+        out = torch.empty_like(weight)
+    _need(out, "out", torch.float32, 1, dev)
+    if out.numel() != weight.numel() or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like weight")
+    _check(lib().qerl_aqn_noisy_weight(_ptr(weight), weight.numel(), float(sigma), int(seed) & (2 ** 64 - 1),
+                                       int(step) & (2 ** 64 - 1), int(layer_id) & 0xFFFFFFFF, _ptr(out),
+                                       _stream(stream, dev)))
+    return out
+
 def aqn_sigma(stage: int, num_stages: int, sigma_start: float, sigma_end: float) -> float:
     return float(lib().qerl_aqn_sigma(int(stage), int(num_stages), float(sigma_start),
                                       float(sigma_end)))

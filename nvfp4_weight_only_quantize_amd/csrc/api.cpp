@@ -201,6 +201,80 @@ qerl_status qerl_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k,
                       "w4a16_lora_gemm_multi launch");
 }
 
+size_t qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qerl_gemm_segment *segs,
+                                                         int32_t nseg) {
+    if (!segs || nseg < 1 || nseg > QERL_MAX_SEGMENTS) return 0;
+    int64_t n[QERL_MAX_SEGMENTS];
+    int r[QERL_MAX_SEGMENTS];
+    for (int i = 0; i < nseg; ++i) {
+        n[i] = segs[i].n;
+        r[i] = segs[i].r;
+    }
+    return qerl::norm_gemm_multi_workspace_bytes(m, k, n, r, nseg);
+}
+
+qerl_status qerl_rmsnorm_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                               const float *norm_weight, float eps,
+                                               const qerl_gemm_segment *segs, int32_t nseg,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!segs || !norm_weight) return fail(QERL_ERR_NULL, "rmsnorm_w4a16_lora_gemm_multi: segs and norm_weight are required");
+    if (nseg < 1 || nseg > QERL_MAX_SEGMENTS)
+        return fail(QERL_ERR_ARG, "rmsnorm_w4a16_lora_gemm_multi: nseg %d outside [1, %d]", nseg, QERL_MAX_SEGMENTS);
+    if (!(eps > 0.0f) || !isfinite(eps))
+        return fail(QERL_ERR_ARG, "rmsnorm_w4a16_lora_gemm_multi: eps must be positive and finite");
+    if (k > QERL_MAX_NORM_WIDTH)
+        return fail(QERL_ERR_SHAPE, "rmsnorm_w4a16_lora_gemm_multi: k=%lld above %d", (long long)k, QERL_MAX_NORM_WIDTH);
+    if (!aligned16(norm_weight))
+        return fail(QERL_ERR_ALIGN, "rmsnorm_w4a16_lora_gemm_multi: norm_weight must be 16-byte aligned");
+    qerl::GemmArgs a[QERL_MAX_SEGMENTS];
+    int64_t n[QERL_MAX_SEGMENTS];
+    int r[QERL_MAX_SEGMENTS];
+    char what[56];
+    for (int i = 0; i < nseg; ++i) {
+        snprintf(what, sizeof what, "rmsnorm_w4a16_lora_gemm_multi segment %d", i);
+        const qerl_gemm_segment &g = segs[i];
+        const qerl_status st = check_gemm(what, x_bf16, m, k, ldx, g.packed, g.scales, g.tensor_scale, g.n,
+                                          g.lora_a_bf16, g.lora_b_bf16, g.r, g.lora_scale, g.y_bf16, g.ldy, &a[i]);
+        if (st != QERL_OK) return st;
+        n[i] = g.n;
+        r[i] = g.r;
+    }
+    const size_t need = qerl::norm_gemm_multi_workspace_bytes(m, k, n, r, nseg);
+    if (!workspace || workspace_bytes < need)
+        return fail(QERL_ERR_WORKSPACE, "rmsnorm_w4a16_lora_gemm_multi: workspace of %zu bytes needed", need);
+    if (!aligned16(workspace))
+        return fail(QERL_ERR_ALIGN, "rmsnorm_w4a16_lora_gemm_multi: workspace must be 16-byte aligned");
+    for (int i = 0; i < nseg; ++i) {
+        a[i].workspace = workspace;
+        a[i].norm_w = norm_weight;
+        a[i].norm_eps = eps;
+    }
+    return hip_status(qerl::launch_norm_gemm_multi(a, nseg, static_cast<hipStream_t>(stream)),
+                      "rmsnorm_w4a16_lora_gemm_multi launch");
+}
+
+qerl_status qerl_aqn_noisy_weight(const float *weight, int64_t h, float sigma, uint64_t seed, uint64_t step,
+                                  uint32_t layer_id, float *noisy_weight_out, void *stream) {
+    g_last_error[0] = '\0';
+    if (!weight || !noisy_weight_out) return fail(QERL_ERR_NULL, "aqn_noisy_weight: weight and noisy_weight_out are required");
+    if (h < 1 || h > QERL_MAX_NORM_WIDTH)
+        return fail(QERL_ERR_SHAPE, "aqn_noisy_weight: need 1 <= h <= %d (got %lld)", QERL_MAX_NORM_WIDTH, (long long)h);
+    if (((uintptr_t)weight & 3u) || ((uintptr_t)noisy_weight_out & 3u))
+        return fail(QERL_ERR_ALIGN, "aqn_noisy_weight: pointers must be 4-byte aligned");
+    if (!(sigma >= 0.0f) || !isfinite(sigma))
+        return fail(QERL_ERR_ARG, "aqn_noisy_weight: sigma must be non-negative and finite");
+    qerl::AqnArgs a{};
+    a.h = h;
+    a.weight = weight;
+    a.sigma = sigma;
+    a.seed = seed;
+    a.step = step;
+    a.layer = layer_id;
+    a.noisy_out = noisy_weight_out;
+    return hip_status(qerl::launch_aqn_noisy_weight(a, static_cast<hipStream_t>(stream)), "aqn_noisy_weight launch");
+}
+
 float qerl_aqn_sigma(int32_t stage, int32_t num_stages, float sigma_start, float sigma_end) {
     if (!(sigma_start > 0.0f) || !(sigma_end > 0.0f) || !isfinite(sigma_start) || !isfinite(sigma_end))
         return NAN;

@@ -142,7 +142,29 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
     }
 }
 
+// w + sigma z alone: the scale vector every norm call of one (seed, step,
+// layer) uses, for callers that apply it themselves (the RMSNorm prologue of
+// the decode GEMM).  Thread g draws channels 4g .. 4g + 3, as above.
+__global__ __launch_bounds__(kThreads) void aqn_noisy_weight_kernel(AqnArgs a) {
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t c0 = 4 * g;
+    if (c0 >= a.h) return;
+    const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
+    float z[4];
+    box_muller(r.v[0], r.v[1], z[0], z[1]);
+    box_muller(r.v[2], r.v[3], z[2], z[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (c0 + i < a.h) a.noisy_out[c0 + i] = __builtin_fmaf(a.sigma, z[i], a.weight[c0 + i]);
+}
+
 }  // namespace
+
+hipError_t launch_aqn_noisy_weight(const AqnArgs &a, hipStream_t stream) {
+    const int64_t blocks = (a.h + kChanPerWg - 1) / kChanPerWg;
+    hipLaunchKernelGGL(aqn_noisy_weight_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_aqn_rmsnorm(const AqnArgs &a, hipStream_t stream) {
     const bool vec = ((uintptr_t)a.x & 15u) == 0 && a.ldx % 8 == 0 && a.h % 8 == 0 &&

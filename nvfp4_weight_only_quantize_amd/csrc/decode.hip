@@ -88,6 +88,10 @@ struct DecodePlan {
     int64_t unit_sc_pitch;         // 16 < m: LDS pitch of the unit's scale tile
     bool unit_sc;                  // 16 < m: scales staged in LDS
     int64_t part_off, tpart_off, t_off, bytes;
+    // RMSNorm prologue (m <= 16): the producers' per-K-range sums of squares
+    // [prod_kr][16] at ss_off, and the rows' 1 / rms [16] after t16 at inv_off
+    bool norm;
+    int64_t ss_off, inv_off;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -106,7 +110,9 @@ int64_t cu_count() {
 
 // slice_rows: the row blocks the CUs are shared by (a multi-segment launch
 // passes the total over its segments, so every segment gets the same slices)
-DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slice_rows = 0) {
+// norm: an RMSNorm prologue (m <= 16 only): producers run even without LoRA
+// and also sum the squares of x.
+DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slice_rows = 0, bool norm = false) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
@@ -120,7 +126,9 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.rp = (r + 31) / 32 * 32;
     p.prod_kr = (p.chunks + kProdChunks - 1) / kProdChunks;
     p.prod_groups = p.mt * ((p.jt + kProdTiles - 1) / kProdTiles);
-    p.producers = r > 0 ? p.prod_kr * p.prod_groups : 0;
+    p.norm = norm && p.mt == 1;
+    if (p.norm && p.prod_groups < 1) p.prod_groups = 1;  // sums of squares only
+    p.producers = (r > 0 || p.norm) ? p.prod_kr * p.prod_groups : 0;
     // slices: as many units as compute units without going over (a CU that
     // runs two units while others run one sets the time), and the FP32
     // partials below the weight bytes
@@ -130,6 +138,9 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
     if (s < 1) s = 1;
+#ifdef VAR_SMIN
+    if (m <= 16 && s < VAR_SMIN) s = VAR_SMIN;
+#endif
     const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
         p.cps = (p.chunks + s - 1) / s;
@@ -167,15 +178,17 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.sc_lds_off = (x_bytes + 15) / 16 * 16;
     int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
     const int64_t epi = 16 * p.rp * 2 * 2;  // t16 in the one-launch epilogue
-    const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16;  // producer wave reduction
+    const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16 + kWaves * 16 * 4;  // producer wave reductions
     if (lds < epi) lds = epi;
     if (lds < prod) lds = prod;
     p.lds_bytes = lds;
     // workspace after the counters: partial tiles, producer partials, t
     p.part_off = 0;  // offsets from the segment's data (after the counter head)
     p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
-    p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
-    p.bytes = align256(p.t_off + 2 * 16 * p.rp * 2);  // t16: BF16 hi/lo [2][16][rp]
+    p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
+    p.t_off = align256(p.ss_off + (p.norm ? p.prod_kr * 16 * 4 : 0));
+    p.inv_off = p.t_off + 2 * 16 * p.rp * 2;  // after t16: BF16 hi/lo [2][16][rp]
+    p.bytes = align256(p.inv_off + (p.norm ? 16 * 4 : 0));
     return p;
 }
 
@@ -187,6 +200,8 @@ struct Decode {
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
     __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
     __device__ float *t32() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.t_off); }
+    __device__ float *ssp() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.ss_off); }
+    __device__ float *inv() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.inv_off); }
 };
 
 // One launch over up to kMaxSegments GEMMs that share x (m, k, ldx): the
@@ -270,11 +285,16 @@ __device__ __forceinline__ bf16x8_t dequant8_d(uint32_t q, float s) {
 // 16*mt + (lane % 16) and A row 16*jt + (lane % 16), 8 elements at
 // 8*(lane / 16) of the step, so MFMA tile (mt, jt) holds
 // t[16 mt + 4 (lane/16) + v][16 jt + lane % 16] in element v.
-template <int MT>
+// NORM (m <= 16): x enters as bf16(x * norm_w) and the first group of each K
+// range also sums the squares of x over the range; the last producer turns
+// the sums into 1 / rms per row, scales t by it and publishes both.
+template <int MT, bool NORM = false>
 __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
+    static_assert(!NORM || MT == 1, "the norm prologue is for m <= 16");
     const GemmArgs &a = d.a;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int JT = (int)d.p.jt, JG = (JT + kProdTiles - 1) / kProdTiles;
+    const int JGd = JG > 0 ? JG : 1;  // (r == 0 with the norm: one group, no rank tiles)
     // producer p: K range kr, m-tile mt, rank tiles jg .. jg + kProdTiles - 1
     // (one pass each, so that no producer runs all m-tiles and ranks in turn)
     const int64_t kr = p / d.p.prod_groups;
@@ -284,15 +304,18 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
     const __amdgpu_buffer_rsrc_t rs_own = coherent_rsrc(d.tpart() + kr * tile_floats);
     f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
+    float *red_ss = reinterpret_cast<float *>(lds + kWaves * kProdTiles * 64 * 16);  // [wave][16]
     // one m-tile and two rank tiles, so the producer path never needs more
     // registers than the streaming path; each wave's steps (32 elements,
     // every 4th of the range) in groups of PS with all loads of a group
     // issued before its products
     constexpr int PS = 4;
     {
-        const int mt = grp / JG, jg = (grp - mt * JG) * kProdTiles;
+        const int mt = grp / JGd, jg = (grp - mt * JGd) * kProdTiles;
+        const bool sum_sq = NORM && grp == 0;  // (uniform)
         const int64_t mrow = 16 * mt + lr < a.m ? 16 * mt + lr : a.m - 1;
         const uint16_t *xrow = a.x + mrow * a.ldx;
+        float ss = 0.0f;
         {
             f32x4_t acc[kProdTiles];
 #pragma unroll
@@ -301,22 +324,42 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
             // keep to the barriers)
             for (int64_t k0 = wave < kWaves ? kb + 32 * wave : ke; k0 < ke; k0 += 4 * 32 * PS) {
                 uint4 xv[PS], av[PS][kProdTiles];
+                float4 nv[PS][2];
 #pragma unroll
                 for (int u = 0; u < PS; ++u) {
                     const int64_t kk = k0 + 128 * u + 8 * lq;
                     const int64_t kc = kk < ke ? kk : ke - 8;  // k % 16 == 0: a piece never straddles the end
                     xv[u] = *reinterpret_cast<const uint4 *>(xrow + kc);
+                    if (NORM) {
+                        nv[u][0] = *reinterpret_cast<const float4 *>(a.norm_w + kc);
+                        nv[u][1] = *reinterpret_cast<const float4 *>(a.norm_w + kc + 4);
+                    }
 #pragma unroll
                     for (int jj = 0; jj < kProdTiles; ++jj) {
-                        const int jr = 16 * (jg + jj) + lr;
-                        const int64_t j = jr < a.r ? jr : a.r - 1;
-                        av[u][jj] = *reinterpret_cast<const uint4 *>(a.lora_a + j * a.k + kc);
+                        av[u][jj] = make_uint4(0, 0, 0, 0);
+                        if (jg + jj < JT) {  // (uniform)
+                            const int jr = 16 * (jg + jj) + lr;
+                            const int64_t j = jr < a.r ? jr : a.r - 1;
+                            av[u][jj] = *reinterpret_cast<const uint4 *>(a.lora_a + j * a.k + kc);
+                        }
                     }
                 }
 #pragma unroll
                 for (int u = 0; u < PS; ++u) {
                     const bool kin = k0 + 128 * u + 8 * lq < ke;
-                    const bf16x8_t xa = as_bf16x8_d(kin ? xv[u] : make_uint4(0, 0, 0, 0));
+                    uint4 xu = kin ? xv[u] : make_uint4(0, 0, 0, 0);
+                    if (NORM) {
+                        const float xf[8] = {bf16lo_to_f32(xu.x), bf16hi_to_f32(xu.x), bf16lo_to_f32(xu.y),
+                                             bf16hi_to_f32(xu.y), bf16lo_to_f32(xu.z), bf16hi_to_f32(xu.z),
+                                             bf16lo_to_f32(xu.w), bf16hi_to_f32(xu.w)};
+                        if (sum_sq)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(xf[e], xf[e], ss);
+                        const float4 n0 = nv[u][0], n1 = nv[u][1];
+                        xu = make_uint4(pack_bf16x2(xf[0] * n0.x, xf[1] * n0.y), pack_bf16x2(xf[2] * n0.z, xf[3] * n0.w),
+                                        pack_bf16x2(xf[4] * n1.x, xf[5] * n1.y), pack_bf16x2(xf[6] * n1.z, xf[7] * n1.w));
+                    }
+                    const bf16x8_t xa = as_bf16x8_d(xu);
 #pragma unroll
                     for (int jj = 0; jj < kProdTiles; ++jj) {
                         const bool jin = kin && 16 * (jg + jj) + lr < a.r;
@@ -329,6 +372,11 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
             if (wave < kWaves)
 #pragma unroll
                 for (int jj = 0; jj < kProdTiles; ++jj) red[(wave * kProdTiles + jj) * 64 + lane] = acc[jj];
+            if (NORM && sum_sq) {  // a row's squares: its 4 lanes in each wave, then the waves
+                ss += __shfl_xor(ss, 16, 64);
+                ss += __shfl_xor(ss, 32, 64);
+                if (wave < kWaves && lq == 0) red_ss[wave * 16 + lr] = ss;
+            }
             __syncthreads();
             if (wave == 0) {
 #pragma unroll
@@ -339,17 +387,34 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
                     for (int w = 1; w < kWaves; ++w) t = t + red[(w * kProdTiles + jj) * 64 + lane];
                     store_f4_coherent(rs_own, ((mt * JT + jg + jj) * 64 + lane) * 16, t);
                 }
+                if (NORM && sum_sq && lane < 16) {
+                    float tot = red_ss[lane];
+#pragma unroll
+                    for (int w = 1; w < kWaves; ++w) tot += red_ss[w * 16 + lane];
+                    store_f32_coherent(d.ssp() + kr * 16 + lane, tot);
+                }
             }
             __syncthreads();
         }
     }
     if (wave == 0) wait_vm();
     __shared__ uint32_t s_last;
+    __shared__ float s_inv[16];
     __syncthreads();
     if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
     __syncthreads();
     if (!s_last) return;
     if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);  // every producer has counted
+    if (NORM) {  // 1 / rms of the 16 rows (rows past m repeat row m - 1), sums in K-range order
+        if (tid < 16) {
+            float tot = 0.0f;
+            for (int64_t q = 0; q < d.p.prod_kr; ++q) tot += load_f32_coherent(d.ssp() + q * 16 + tid);
+            const float inv = 1.0f / sqrtf(tot * (1.0f / (float)a.k) + a.norm_eps);
+            s_inv[tid] = inv;
+            store_f32_coherent(d.inv() + tid, inv);
+        }
+        __syncthreads();
+    }
     // The last producer sums the partials in K-range order (tile i goes to
     // wave i % 4, kBatch ranges in flight).  16 < m: into t [m, r] in FP32,
     // read after the kernel boundary.  m <= 16: into t16 [2][16][rp], the BF16
@@ -375,11 +440,12 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
         for (int v = 0; v < 4; ++v) {
             const int64_t m = 16 * mt + 4 * lq + v;
             if (MT == 1) {  // all 16 rows (rows past m repeat row m - 1 and are never output)
-                const uint16_t hi = f32_to_bf16_bits(sum[v]);
+                const float tv = NORM ? sum[v] * s_inv[m] : sum[v];
+                const uint16_t hi = f32_to_bf16_bits(tv);
                 const int off = (int)((m * d.p.rp + j) * 2);
                 store_u16_coherent(rt, off, hi);
                 store_u16_coherent(rt, off + (int)(16 * d.p.rp * 2),
-                                   f32_to_bf16_bits(sum[v] - __uint_as_float((uint32_t)hi << 16)));
+                                   f32_to_bf16_bits(tv - __uint_as_float((uint32_t)hi << 16)));
             } else if (m < a.m && j < a.r) {
                 d.t32()[m * a.r + j] = sum[v];
             }
@@ -477,15 +543,45 @@ __device__ __forceinline__ void batched_copy_2d(int rows, int per_row, Src src, 
 }
 
 // The unit's x slice, rows [0, m) x columns [k0, k0 + width), into LDS rows
-// of `pitch` elements; columns at or past k are zero.
+// of `pitch` elements; columns at or past k are zero.  NORM: each element
+// enters as bf16(x * norm_w[column]) (the row's 1 / rms is applied in the
+// epilogue).
+struct XNormItem {
+    uint4 x;
+    float4 w0, w1;
+};
+template <bool NORM>
 __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
-    batched_copy_2d<uint4>(
+    if (!NORM) {
+        batched_copy_2d<uint4>(
+            (int)a.m, (int)(width / 8),
+            [&](int m, int pc) {
+                const int64_t col = k0 + 8 * pc;
+                return col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col) : make_uint4(0, 0, 0, 0);
+            },
+            [&](int m, int pc, const uint4 &v) { *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = v; });
+        return;
+    }
+    batched_copy_2d<XNormItem>(
         (int)a.m, (int)(width / 8),
         [&](int m, int pc) {
             const int64_t col = k0 + 8 * pc;
-            return col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col) : make_uint4(0, 0, 0, 0);
+            XNormItem it{make_uint4(0, 0, 0, 0), make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+            if (col < a.k) {
+                it.x = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col);
+                it.w0 = *reinterpret_cast<const float4 *>(a.norm_w + col);
+                it.w1 = *reinterpret_cast<const float4 *>(a.norm_w + col + 4);
+            }
+            return it;
         },
-        [&](int m, int pc, const uint4 &v) { *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = v; });
+        [&](int m, int pc, const XNormItem &it) {
+            const uint4 v = it.x;
+            const uint4 o = make_uint4(pack_bf16x2(bf16lo_to_f32(v.x) * it.w0.x, bf16hi_to_f32(v.x) * it.w0.y),
+                                       pack_bf16x2(bf16lo_to_f32(v.y) * it.w0.z, bf16hi_to_f32(v.y) * it.w0.w),
+                                       pack_bf16x2(bf16lo_to_f32(v.z) * it.w1.x, bf16hi_to_f32(v.z) * it.w1.y),
+                                       pack_bf16x2(bf16lo_to_f32(v.w) * it.w1.z, bf16hi_to_f32(v.w) * it.w1.w));
+            *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = o;
+        });
 }
 
 // Stage the unit's scale bytes: rows [n0, n0 + R) x bytes [b0, b0 + nb) of
@@ -551,7 +647,7 @@ __device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *s
 
 // K32: k % 32 == 0; SPLIT: K is split over several units per row block
 // (slices > 1); LORA: r > 0.
-template <int NS, bool K32, bool SPLIT, bool LORA>
+template <int NS, bool K32, bool SPLIT, bool LORA, bool NORM>
 __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -562,8 +658,9 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     if (NS > 1 && bx >= p.producers + p.units) return;  // past a narrower segment
     // (segments of one launch may differ; a one-segment launch has LORA == (r > 0))
     const bool lora = LORA && (NS == 1 || a.r > 0);
-    if (lora && bx < p.producers) {
-        lora_producer<MT>(d, bx, lds);
+    const bool wait_t = lora || NORM;  // producers publish t and / or 1 / rms behind the ready flag
+    if (wait_t && bx < p.producers) {
+        lora_producer<MT, NORM>(d, bx, lds);
         return;
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
@@ -596,13 +693,19 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // stream through a ring of DR chunks with no barrier ----
     constexpr int DR = kRing;
     uint4 w[DR][NW];
+#ifdef VAR_NOLOOP
+    if (false) {
+#else
     if (c_full_end > c_begin) {
+#endif
 #pragma unroll
         for (int s = 0; s < DR; ++s)
             load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
     }
-    stage_x_slice(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
+#ifndef VAR_NOSTAGE
+    stage_x_slice<NORM>(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
     stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
+#endif
     if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
         const int z0 = (int)((a.k >> 4) - sb0), zn = (int)(p.full_chunks * 8 + 8 - (a.k >> 4));  // zn < 8
         for (int rr = tid >> 3; rr < R; rr += kThreadsD / 8)
@@ -610,6 +713,9 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     }
     __syncthreads();
     int64_t c = c_begin;
+#ifdef VAR_NOLOOP
+    if (false)
+#endif
     for (; c + 2 * DR <= c_full_end; c += DR) {
 #pragma unroll
         for (int s = 0; s < DR; ++s) {
@@ -619,6 +725,9 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+#ifdef VAR_NOLOOP
+    if (false)
+#endif
     if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
 #pragma unroll
         for (int s = 0; s < DR; ++s) {
@@ -633,13 +742,17 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // producers lead the grid and are done by now as a rule, so t can be
     // loaded without a round trip of its own.
     uint32_t t_seen = 0;
-    if (lora && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
+    if (wait_t && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
+#ifndef VAR_NOLOOP
 #pragma unroll
     for (int s = 0; s < DR; ++s)
         if (c + s < c_full_end)  // uniform
             mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
                               m_last, lr, lq, acc);
     if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
+#else
+    if (false) {
+#endif
         uint4 wt[NW];
         load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
         mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
@@ -686,7 +799,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
         if (tid == 0) s_ready = t_seen;
         __syncthreads();
     }
-    if (lora && !s_ready) {  // uniform; rare: wait for the last producer
+    if (wait_t && !s_ready) {  // uniform; rare: wait for the last producer
         if (tid == 0) {
             uint32_t it = 0;
             while (ctr_load(d.ctr() + kCtrTReady) == 0 && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
@@ -704,7 +817,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // without a memory access (and with no branch for the compiler to fold
     // the sums into).
     f32x4_t pv[kRedP];
-    i32x4_t tq[2];
+    i32x4_t tq[2], iq;
     if (SPLIT) {
         const int64_t sstride = p.row_blocks * tile_floats * 4;  // bytes between slices of a row block
         const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
@@ -718,6 +831,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
         tq[0] = load_i4_coherent(rt, tid * 16);
         tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
     }
+    if (NORM) iq = load_i4_coherent(coherent_rsrc(d.inv()), (tid & 3) * 16);  // 1 / rms of the 16 rows
     // The values are taken here, after every load has been issued: without
     // this the compiler folds the sums below into the conditional loads and
     // waits for each load before issuing the next.
@@ -725,6 +839,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
 #pragma unroll
         for (int v = 0; v < kRedP; ++v) asm volatile("" : "+v"(pv[v]));
     if (lora) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
+    if (NORM) asm volatile("" : "+v"(iq));
     if (SPLIT) {
         acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -744,11 +859,13 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
     uint16_t *th = reinterpret_cast<uint16_t *>(lds);  // t16 [2][16][rp]: hi, then lo
     uint16_t *tl = th + 16 * p.rp;
+    __shared__ __attribute__((aligned(16))) float s_inv[16];
     if (lora) {  // (the pieces past t16 were loaded as zeros and are not stored)
         if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
         if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
-        __syncthreads();
     }
+    if (NORM && tid < 4) reinterpret_cast<i32x4_t *>(s_inv)[tid] = iq;
+    if (wait_t) __syncthreads();
     const float st = *a.tensor_scale, lam = a.lora_scale;
 #pragma unroll
     for (int g = 0; g < NW; ++g) {
@@ -767,13 +884,14 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
             for (int v = 0; v < 4; ++v) {
                 const int64_t m = 16 * mt + 4 * lq + v;
                 const int64_t n = n0 + 16 * g + lr;
-                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[mt][g][v] + lam * l[v]);
+                const float base = NORM ? st * s_inv[m] * acc[mt][g][v] : st * acc[mt][g][v];
+                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(base + lam * l[v]);
             }
         }
     }
     // this row block is done with t16; the last one clears the ready flag
     // and this count for the next call
-    if (lora && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
+    if (wait_t && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
         ctr_store(d.ctr() + kCtrTReady, 0u);
         ctr_store(d.ctr() + kCtrDone, 0u);
     }
@@ -958,9 +1076,9 @@ hipError_t launch_mfma_units(const DecodeSetN<NS> &ds, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <bool K32, bool SPLIT, bool LORA, int NS>
+template <bool K32, bool SPLIT, bool LORA, bool NORM, int NS>
 hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_t stream) {
-    auto kern = stream_kernel<NS, K32, SPLIT, LORA>;
+    auto kern = stream_kernel<NS, K32, SPLIT, LORA, NORM>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
@@ -976,24 +1094,37 @@ hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_
 template <bool K32, int NS>
 hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, bool lora, hipStream_t stream) {
     const bool split = ds.seg[0].p.slices > 1;  // the same for every segment
+    if (ds.seg[0].p.norm) {  // the norm prologue: k % 32 == 0 only (checked by the caller)
+        if constexpr (K32) {
+            if (split)
+                return lora ? launch_stream<K32, true, true, true>(ds, lds_bytes, stream)
+                            : launch_stream<K32, true, false, true>(ds, lds_bytes, stream);
+            return lora ? launch_stream<K32, false, true, true>(ds, lds_bytes, stream)
+                        : launch_stream<K32, false, false, true>(ds, lds_bytes, stream);
+        } else {
+            return hipErrorInvalidValue;
+        }
+    }
     if (split)
-        return lora ? launch_stream<K32, true, true>(ds, lds_bytes, stream)
-                    : launch_stream<K32, true, false>(ds, lds_bytes, stream);
-    return lora ? launch_stream<K32, false, true>(ds, lds_bytes, stream)
-                : launch_stream<K32, false, false>(ds, lds_bytes, stream);
+        return lora ? launch_stream<K32, true, true, false>(ds, lds_bytes, stream)
+                    : launch_stream<K32, true, false, false>(ds, lds_bytes, stream);
+    return lora ? launch_stream<K32, false, true, false>(ds, lds_bytes, stream)
+                : launch_stream<K32, false, false, false>(ds, lds_bytes, stream);
 }
 
 // the plans of a launch over segs[0 .. nseg) (shared x), slices shared
 DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
     DecodeSet ds{};
     ds.nseg = nseg;
+    const bool norm = segs[0].norm_w != nullptr;
     int64_t rows = 0;
-    for (int i = 0; i < nseg; ++i) rows += make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r).row_blocks;
+    for (int i = 0; i < nseg; ++i)
+        rows += make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, 0, norm).row_blocks;
     char *base = static_cast<char *>(segs[0].workspace);  // one workspace for the launch
     int64_t data = kGemmCtrBytes;
     for (int i = 0; i < nseg; ++i) {
         ds.seg[i].a = segs[i];
-        ds.seg[i].p = make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, rows);
+        ds.seg[i].p = make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, rows, norm);
         ds.seg[i].ctrs = reinterpret_cast<uint32_t *>(base + i * kSegCtrBytes);
         ds.seg[i].a.workspace = base + data;
         data += align256(ds.seg[i].p.bytes);
@@ -1017,7 +1148,9 @@ hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
         if (d.p.row_blocks < 1 || d.p.lds_bytes > kLdsLimit ||
             d.p.rows_per_unit * 16 * d.p.mt * d.p.units * 4 > 0x7FFFFFFF)
             return hipErrorInvalidConfiguration;
-        if (d.p.slices != ds.seg[0].p.slices || d.p.unit_sc != ds.seg[0].p.unit_sc) return hipErrorInvalidConfiguration;
+        if (d.p.slices != ds.seg[0].p.slices || d.p.unit_sc != ds.seg[0].p.unit_sc || d.p.norm != ds.seg[0].p.norm ||
+            (d.a.norm_w != nullptr) != d.p.norm)
+            return hipErrorInvalidConfiguration;
         lds = d.p.lds_bytes > lds ? d.p.lds_bytes : lds;
         lora = lora || d.a.r > 0;
     }
@@ -1037,11 +1170,11 @@ hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
     return launch_decode_set(make_decode_set(&a, 1), stream);
 }
 
-size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg) {
+size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm) {
     int64_t rows = 0;
-    for (int j = 0; j < nseg; ++j) rows += make_decode_plan(m, n[j], k, r[j]).row_blocks;
+    for (int j = 0; j < nseg; ++j) rows += make_decode_plan(m, n[j], k, r[j], 0, norm).row_blocks;
     int64_t bytes = kGemmCtrBytes;
-    for (int j = 0; j < nseg; ++j) bytes += align256(make_decode_plan(m, n[j], k, r[j], rows).bytes);
+    for (int j = 0; j < nseg; ++j) bytes += align256(make_decode_plan(m, n[j], k, r[j], rows, norm).bytes);
     return (size_t)bytes;
 }
 

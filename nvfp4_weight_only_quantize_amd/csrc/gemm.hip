@@ -332,6 +332,49 @@ hipError_t launch_w4a16_lora_gemm_multi(const GemmArgs *segs, int nseg, hipStrea
     return hipSuccess;
 }
 
+// RMSNorm + GEMMs: fused into the decode launch (the producers also sum the
+// squares of x, the units stage bf16(x * norm_w), the epilogue applies 1 / rms)
+// when m <= kNormFuseMaxM and k % 32 == 0; otherwise the norm is a launch of
+// its own into the workspace, after the GEMM's part of it.
+static bool norm_fused(int64_t m, int64_t k) { return m <= kNormFuseMaxM && k % 32 == 0; }
+
+size_t norm_gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg) {
+    if (norm_fused(m, k)) return decode_multi_workspace_bytes(m, k, n, r, nseg, true);
+    return (size_t)align256((int64_t)gemm_multi_workspace_bytes(m, k, n, r, nseg)) + (size_t)align256(m * k * 2);
+}
+
+hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream) {
+    const GemmArgs &a = segs[0];
+    if (norm_fused(a.m, a.k)) return launch_decode_multi(segs, nseg, stream);
+    int64_t n[QERL_MAX_SEGMENTS];
+    int r[QERL_MAX_SEGMENTS];
+    for (int i = 0; i < nseg; ++i) {
+        n[i] = segs[i].n;
+        r[i] = segs[i].r;
+    }
+    uint16_t *xn = reinterpret_cast<uint16_t *>(static_cast<char *>(a.workspace) +
+                                                align256((int64_t)gemm_multi_workspace_bytes(a.m, a.k, n, r, nseg)));
+    AqnArgs na{};  // sigma 0: the plain RMSNorm with scale vector norm_w
+    na.x = a.x;
+    na.m = a.m;
+    na.h = a.k;
+    na.ldx = a.ldx;
+    na.weight = a.norm_w;
+    na.eps = a.norm_eps;
+    na.y_bf16 = xn;
+    na.ldy = a.k;
+    hipError_t e = launch_aqn_rmsnorm(na, stream);
+    if (e != hipSuccess) return e;
+    GemmArgs g[QERL_MAX_SEGMENTS];
+    for (int i = 0; i < nseg; ++i) {
+        g[i] = segs[i];
+        g[i].x = xn;
+        g[i].ldx = a.k;
+        g[i].norm_w = nullptr;
+    }
+    return launch_w4a16_lora_gemm_multi(g, nseg, stream);
+}
+
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
     if (a.m <= kDecodeMaxM) return launch_decode(a, stream);
     const Gemm g{a, make_plan(a.m, a.n, a.k, a.r)};

@@ -32,6 +32,11 @@ struct GemmArgs {
     uint16_t *y;
     int64_t ldy;
     void *workspace;
+    // RMSNorm prologue (decode path, m <= 16): x is the norm's input and each
+    // row is normed with scale vector norm_w [k] and norm_eps before the
+    // product; nullptr: x is used as it is
+    const float *norm_w = nullptr;
+    float norm_eps = 0.0f;
 };
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 // Every GEMM workspace starts with the counters of the decode path's in-kernel
@@ -51,8 +56,15 @@ hipError_t launch_decode(const GemmArgs &a, hipStream_t stream);
 // the weight, LoRA and output fields and all carry the same workspace.
 size_t gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
 hipError_t launch_w4a16_lora_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
-size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
+size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg,
+                                    bool norm = false);
 hipError_t launch_decode_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
+// RMSNorm + GEMMs: the norm fused into the decode launch when m <= kNormFuseMaxM
+// and k % 32 == 0 (segs carry norm_w), else a norm launch into the workspace
+// and then launch_w4a16_lora_gemm_multi
+constexpr int64_t kNormFuseMaxM = 16;
+size_t norm_gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
+hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
 
 // ---- AQN RMSNorm ----
 struct AqnArgs {
@@ -68,5 +80,7 @@ struct AqnArgs {
     float *noisy_out;
 };
 hipError_t launch_aqn_rmsnorm(const AqnArgs &a, hipStream_t stream);
+// w + sigma z alone (a.x, a.m and the outputs unused; a.noisy_out required)
+hipError_t launch_aqn_noisy_weight(const AqnArgs &a, hipStream_t stream);
 
 }  // namespace qerl

@@ -158,3 +158,53 @@ def test_gemm_multi_workspace_query():
     big = q.w4a16_lora_gemm_multi_workspace_size(100, 3584, shapes)
     assert big == max(q.w4a16_lora_gemm_workspace_size(100, n, 3584, r) for n, r in shapes)
     assert q.lib().qerl_w4a16_lora_gemm_multi_workspace_size(1, 3584, None, 3) == 0
+
+
+def _norm_multi(nseg=2, segs_kw=None, **kw):
+    a = dict(x=FAKE, m=2, k=64, ldx=64, nw=FAKE, eps=1e-6, ws=FAKE, ws_bytes=1 << 24, stream=None, segs=True)
+    a.update(kw)
+    arr = (q.GemmSegment * max(nseg, 1))()
+    for i in range(max(nseg, 1)):
+        s = dict(packed=FAKE, scales=FAKE, ts=FAKE, n=32 + 16 * i, A=FAKE, B=FAKE, r=4, lam=2.0, y=FAKE, ldy=64)
+        s.update((segs_kw or {}).get(i, {}))
+        arr[i] = q.GemmSegment(s["packed"], s["scales"], s["ts"], s["n"], s["A"], s["B"], s["r"], s["lam"],
+                               s["y"], s["ldy"])
+    return q.lib().qerl_rmsnorm_w4a16_lora_gemm_multi(P(a["x"]), a["m"], a["k"], a["ldx"], P(a["nw"]), a["eps"],
+                                                      arr if a["segs"] else None, nseg, P(a["ws"]), a["ws_bytes"],
+                                                      P(a["stream"]))
+
+
+@pytest.mark.parametrize("nseg,segs_kw,kw,status", [
+    (2, None, dict(segs=False), 1), (2, None, dict(nw=None), 1), (0, None, {}, 4), (5, None, {}, 4),
+    (2, None, dict(eps=0.0), 4), (2, None, dict(eps=float("nan")), 4), (2, None, dict(nw=FAKE + 4), 3),
+    (2, None, dict(k=16400, ldx=16400), 2), (2, None, dict(x=None), 1), (2, {1: dict(r=-1)}, {}, 4),
+    (2, {0: dict(n=0)}, {}, 2), (2, None, dict(ws=None), 5), (2, None, dict(ws_bytes=64), 5),
+    (2, None, dict(ws=FAKE + 8), 3),
+])
+def test_norm_gemm_multi_argument_errors(nseg, segs_kw, kw, status):
+    assert _norm_multi(nseg, segs_kw, **kw) == status
+    assert q.lib().qerl_last_error()
+
+
+def test_norm_gemm_multi_workspace_query():
+    shapes = [(3584, 32), (512, 32), (512, 0)]
+    # fused (m <= 16, k % 32 == 0): the decode regions plus the producers' sums of squares
+    for m in (1, 8, 16):
+        fused = q.rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, 3584, shapes)
+        assert fused >= q.w4a16_lora_gemm_multi_workspace_size(m, 3584, shapes)
+    # otherwise the GEMM's workspace, then room for the normed rows
+    for m, k in ((24, 3584), (100, 3584), (4, 3600)):
+        plain = q.w4a16_lora_gemm_multi_workspace_size(m, k, shapes)
+        assert q.rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, k, shapes) >= plain + m * k * 2
+    assert q.lib().qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(1, 3584, None, 2) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(out=None), 1), (dict(h=0), 2), (dict(h=16385), 2), (dict(w=FAKE + 2), 3),
+    (dict(out=FAKE + 1), 3), (dict(sigma=-1.0), 4), (dict(sigma=float("inf")), 4),
+])
+def test_aqn_noisy_weight_argument_errors(kw, status):
+    a = dict(w=FAKE, h=64, sigma=1e-2, seed=1, step=0, layer=0, out=FAKE, stream=None)
+    a.update(kw)
+    assert q.lib().qerl_aqn_noisy_weight(P(a["w"]), a["h"], a["sigma"], a["seed"], a["step"], a["layer"],
+                                         P(a["out"]), P(a["stream"])) == status
