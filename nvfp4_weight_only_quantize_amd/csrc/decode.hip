@@ -138,9 +138,6 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     if (s_cap < 1) s_cap = 1;
     if (s > s_cap) s = s_cap;
     if (s < 1) s = 1;
-#ifdef VAR_SMIN
-    if (m <= 16 && s < VAR_SMIN) s = VAR_SMIN;
-#endif
     const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
         p.cps = (p.chunks + s - 1) / s;
@@ -693,19 +690,13 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // stream through a ring of DR chunks with no barrier ----
     constexpr int DR = kRing;
     uint4 w[DR][NW];
-#ifdef VAR_NOLOOP
-    if (false) {
-#else
     if (c_full_end > c_begin) {
-#endif
 #pragma unroll
         for (int s = 0; s < DR; ++s)
             load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
     }
-#ifndef VAR_NOSTAGE
     stage_x_slice<NORM>(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
     stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
-#endif
     if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
         const int z0 = (int)((a.k >> 4) - sb0), zn = (int)(p.full_chunks * 8 + 8 - (a.k >> 4));  // zn < 8
         for (int rr = tid >> 3; rr < R; rr += kThreadsD / 8)
@@ -713,9 +704,6 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     }
     __syncthreads();
     int64_t c = c_begin;
-#ifdef VAR_NOLOOP
-    if (false)
-#endif
     for (; c + 2 * DR <= c_full_end; c += DR) {
 #pragma unroll
         for (int s = 0; s < DR; ++s) {
@@ -725,9 +713,6 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-#ifdef VAR_NOLOOP
-    if (false)
-#endif
     if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
 #pragma unroll
         for (int s = 0; s < DR; ++s) {
@@ -743,16 +728,12 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // loaded without a round trip of its own.
     uint32_t t_seen = 0;
     if (wait_t && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
-#ifndef VAR_NOLOOP
 #pragma unroll
     for (int s = 0; s < DR; ++s)
         if (c + s < c_full_end)  // uniform
             mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
                               m_last, lr, lq, acc);
     if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
-#else
-    if (false) {
-#endif
         uint4 wt[NW];
         load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
         mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
