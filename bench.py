@@ -9,8 +9,10 @@ every operation of the hot path, at each decode batch M in {1, 8, 64}:
     AQN RMSNorm (MLP)        -> gate, up
     down                     (synthetic activation as input)
 
-The sigma of the AQN noise follows the exponential schedule 1e-2 -> 5e-4 over
-10 stages (stage = step mod 10).  Weights are cold: 8 copies of the layer's
+The AQN noise is that of one RL step (sigma of stage 3 of the exponential
+schedule 1e-2 -> 5e-4 over 10 stages): drawn once, as every decode step of a
+rollout uses the same noisy norm weight.  By default each norm runs inside the
+call of the projections that read it (qerl_rmsnorm_w4a16_lora_gemm_multi).  Weights are cold: 8 copies of the layer's
 NVFP4 weights and LoRA (~1.1 GB, far above the 256 MB Infinity Cache) rotate
 so that no weight is re-read from cache.  The steps run as one captured HIP
 graph (the decode loop is launch-bound otherwise).
@@ -51,6 +53,7 @@ DECODE_MS = (1, 8, 64)
 PREFILL_MS = (2048, 8192)
 RANK, ALPHA = 32, 64
 SIGMA0, SIGMA1, STAGES, EPS = 1e-2, 5e-4, 10, 1e-6
+RL_STEP = 3  # the RL step (noise stage) the decode steps belong to
 SEED = 1002
 
 
@@ -120,13 +123,22 @@ class DecodeLayer:
         ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
         for group in (("q", "k", "v"), ("gate", "up")):
             for m in DECODE_MS:
-                ws = max(ws, q.w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1],
-                                                                    [(self.shapes[g][0], RANK) for g in group]))
+                shp = [(self.shapes[g][0], RANK) for g in group]
+                ws = max(ws, q.w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1], shp),
+                         q.rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1], shp))
         # one workspace per concurrent GEMM (calls that overlap must not share one)
         self.ws = [torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev) for _ in range(3)]
         # side streams for the independent projections (default priority)
         self.side = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
-        self.sigmas = [q.aqn_sigma(s, STAGES, SIGMA0, SIGMA1) for s in range(STAGES)]
+        # AQN: the noise of one RL step is drawn once and every decode step of
+        # the rollout reuses it (the fused launches take the noisy weight; the
+        # standalone norm redraws the same vector on each call)
+        self.sigma = q.aqn_sigma(RL_STEP, STAGES, SIGMA0, SIGMA1)
+        self.wn_attn = q.aqn_noisy_weight(self.w_attn, self.sigma, SEED, RL_STEP, 0)
+        self.wn_mlp = q.aqn_noisy_weight(self.w_mlp, self.sigma, SEED, RL_STEP, 1)
+        # the normed rows, for the calls that take them from the standalone norm
+        self.norm("attn", mmax)
+        self.norm("mlp", mmax)
 
     def inputs_of(self, name):
         return {"q": self.x_attn, "k": self.x_attn, "v": self.x_attn, "o": self.x_o,
@@ -137,39 +149,43 @@ class DecodeLayer:
         q.w4a16_lora_gemm(self.inputs_of(name)[:m], p.wq, p.a, p.b, ALPHA / RANK,
                           out=self.y[name][:m], workspace=self.ws[slot])
 
-    def gemm_multi(self, names, m, c):
-        """The projections `names` (same input) in one multi-segment call."""
+    def norm_gemm_multi(self, which, names, m, c):
+        """The AQN RMSNorm `which` and the projections `names` that read its
+        output, in one call."""
+        src, wn = (self.h_attn, self.wn_attn) if which == "attn" else (self.h_mlp, self.wn_mlp)
         segs = [(self.copies[c][n].wq, self.copies[c][n].a, self.copies[c][n].b, ALPHA / RANK) for n in names]
-        q.w4a16_lora_gemm_multi(self.inputs_of(names[0])[:m], segs, outs=[self.y[n][:m] for n in names],
-                                workspace=self.ws[0])
+        q.rmsnorm_w4a16_lora_gemm_multi(src[:m], wn, EPS, segs, outs=[self.y[n][:m] for n in names],
+                                        workspace=self.ws[0])
 
-    def norm(self, which, m, step):
+    def norm(self, which, m):
         src, w, dst, layer = ((self.h_attn, self.w_attn, self.x_attn, 0) if which == "attn"
                               else (self.h_mlp, self.w_mlp, self.x_mlp, 1))
-        q.aqn_rmsnorm(src[:m], w, EPS, self.sigmas[step % STAGES], SEED, step, layer,
-                      want_f32=False, y_bf16=dst[:m])
+        q.aqn_rmsnorm(src[:m], w, EPS, self.sigma, SEED, RL_STEP, layer, want_f32=False, y_bf16=dst[:m])
 
     def step(self, s, on_gemm=None):
         for mi, m in enumerate(DECODE_MS):
             c = (len(DECODE_MS) * s + mi) % len(self.copies)
-            self.norm("attn", m, s)
+            fused = on_gemm is None and self.launch == "fused"
+            if not fused:
+                self.norm("attn", m)
             if on_gemm is None and self.launch != "serial":
                 # q, k and v read the same normed input and nothing else: one
-                # multi-segment call (or side by side on side streams); o
-                # waits for all three (in a real layer attention sits in
-                # between), as the MLP waits for o
-                if self.launch == "fused":
-                    self.gemm_multi(("q", "k", "v"), m, c)
+                # call with the norm (or side by side on side streams after
+                # it); o waits for all three (in a real layer attention sits
+                # in between), as the MLP waits for o
+                if fused:
+                    self.norm_gemm_multi("attn", ("q", "k", "v"), m, c)
                 else:
                     self._parallel(("q", "k", "v"), m, c)
                 self.gemm("o", m, c)
             else:
                 for name in ("q", "k", "v", "o"):
                     self._g(name, m, c, on_gemm)
-            self.norm("mlp", m, s)
+            if not fused:
+                self.norm("mlp", m)
             if on_gemm is None and self.launch != "serial":
-                if self.launch == "fused":
-                    self.gemm_multi(("gate", "up"), m, c)
+                if fused:
+                    self.norm_gemm_multi("mlp", ("gate", "up"), m, c)
                 else:
                     self._parallel(("gate", "up"), m, c)  # down waits for both
                 self.gemm("down", m, c)
@@ -253,9 +269,24 @@ def per_call_durations(layer: DecodeLayer, reps: int):
 
 
 def check_decode_parity(layer: DecodeLayer):
-    """GPU outputs of the last step vs the CPU oracle at M = 1 (all 7 projections)."""
+    """GPU outputs vs the CPU oracle at M = 1: the five projections behind a
+    norm through the fused norm call (oracle: RMSNorm then the layer), and
+    all seven projections as single calls."""
     import oracle
     worst = 0.0
+    for which, names in (("attn", ("q", "k", "v")), ("mlp", ("gate", "up"))):
+        layer.norm_gemm_multi(which, names, 1, 0)
+        torch.cuda.synchronize()
+        src, wn = (layer.h_attn, layer.wn_attn) if which == "attn" else (layer.h_mlp, layer.wn_mlp)
+        x = synth.bf16_bits(src[:1])
+        for name in names:
+            p = layer.copies[0][name]
+            y = layer.y[name][:1].float().cpu().numpy().astype(np.float64)
+            ref = oracle.rmsnorm_w4a16_lora_gemm(x, wn.cpu().numpy(), EPS, p.wq.packed.cpu().numpy(),
+                                                 p.wq.scales.cpu().numpy(), np.float32(p.wq.tensor_scale.item()),
+                                                 synth.bf16_bits(p.a), synth.bf16_bits(p.b), ALPHA / RANK,
+                                                 threads=16)
+            worst = max(worst, float(np.linalg.norm(y - ref) / np.linalg.norm(ref)))
     for name in synth.PROJ_ORDER:
         p = layer.copies[0][name]
         x = synth.bf16_bits(layer.inputs_of(name)[:1])
