@@ -59,8 +59,8 @@ constexpr int kUnitWaves = 4;
 constexpr int64_t kChunkK = 128;          // K elements per chunk
 constexpr int kXPad = 8;                  // BF16 padding per staged x row
 constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
-constexpr int64_t kXBudget = 36 * 1024;   // LDS for a unit's x slice (m <= 16)
-constexpr int64_t kLdsLimit = 63 * 1024;
+constexpr int64_t kXBudget = 96 * 1024;   // LDS for a unit's x slice (m <= 16)
+constexpr int64_t kLdsLimit = 140 * 1024;  // of the 160 KiB a gfx950 workgroup may hold
 constexpr int64_t kProdChunks = 4;        // K chunks per LoRA producer
 constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
