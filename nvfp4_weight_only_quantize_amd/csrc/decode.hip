@@ -67,6 +67,7 @@ constexpr int kBatch = 8;                // loads in flight per thread in reduct
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
+constexpr int64_t kUnitMinChunks = 8;        // 16 < m: K chunks per unit the split may go down to
 #ifndef QERL_RING
 #define QERL_RING 4
 #endif
@@ -140,6 +141,11 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     if (s < 1) s = 1;
     const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
+        // fewer row blocks than CUs split K as above; more keep at least
+        // kUnitMinChunks chunks per unit but still split K (several units
+        // per CU keep more loads in flight than one long unit)
+        const int64_t s_work = p.chunks / kUnitMinChunks;
+        if (s < s_work) s = s_work < s_cap ? s_work : s_cap;
         p.cps = (p.chunks + s - 1) / s;
         p.slices = (p.chunks + p.cps - 1) / p.cps;
         p.units = p.row_blocks * p.slices;
