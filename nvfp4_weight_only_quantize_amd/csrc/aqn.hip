@@ -67,10 +67,12 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
     const int64_t c0 = 4 * g;
     float wn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (c0 < a.h) {
-        const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
-        float z[4];
-        box_muller(r.v[0], r.v[1], z[0], z[1]);
-        box_muller(r.v[2], r.v[3], z[2], z[3]);
+        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sigma == 0: no noise to draw (w + 0 z is w)
+        if (a.sigma != 0.0f) {
+            const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
+            box_muller(r.v[0], r.v[1], z[0], z[1]);
+            box_muller(r.v[2], r.v[3], z[2], z[3]);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (c0 + i < a.h) {

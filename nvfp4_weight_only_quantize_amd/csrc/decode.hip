@@ -68,6 +68,8 @@ constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr uint32_t kSpinLimit = 1u << 20;
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
 constexpr int64_t kUnitMinChunks = 8;        // 16 < m: K chunks per unit the split may go down to
+constexpr int64_t kDirectMaxKr = 8;          // m <= 16: most producer K ranges the epilogue sums itself
+constexpr int64_t kDirectMaxCps = 12;        // ... in units of at most this many chunks
 #ifndef QERL_RING
 #define QERL_RING 4
 #endif
@@ -93,6 +95,9 @@ struct DecodePlan {
     // [prod_kr][16] at ss_off, and the rows' 1 / rms [16] after t16 at inv_off
     bool norm;
     int64_t ss_off, inv_off;
+    // m <= 16 with few producer K ranges (and r <= 64): the epilogue sums the
+    // producers' partial tiles itself, so t costs no last-producer stage
+    bool direct;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -171,6 +176,9 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.cps = cps;
     p.slices = (p.chunks + cps - 1) / cps;
     p.units = p.row_blocks * p.slices;
+    // short units reach their epilogue before a last-producer stage could
+    // publish t: those sum the producers' partials themselves
+    p.direct = p.producers > 0 && p.prod_kr <= kDirectMaxKr && p.jt <= 4 && p.cps <= kDirectMaxCps;
     // LDS: the x slice, then the scales (rows an odd multiple of 16 bytes
     // apart, so the 16 rows a wave reads fall in distinct banks)
     p.xpitch = cps * kChunkK + kXPad;
@@ -406,7 +414,7 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     __syncthreads();
     if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
     __syncthreads();
-    if (!s_last) return;
+    if (!s_last || d.p.direct) return;  // direct: the consumers read the count and the partials
     if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);  // every producer has counted
     if (NORM) {  // 1 / rms of the 16 rows (rows past m repeat row m - 1), sums in K-range order
         if (tid < 16) {
@@ -733,7 +741,11 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // producers lead the grid and are done by now as a rule, so t can be
     // loaded without a round trip of its own.
     uint32_t t_seen = 0;
-    if (wait_t && tid == 0) t_seen = ctr_load(d.ctr() + kCtrTReady);
+    // (direct: ready once every producer has counted; else the ready flag)
+    const bool direct = wait_t && p.direct;
+    uint32_t *ready_ctr = d.ctr() + (direct ? kCtrProd : kCtrTReady);
+    const uint32_t ready_at = direct ? (uint32_t)p.producers : 1u;
+    if (wait_t && tid == 0) t_seen = ctr_load(ready_ctr) >= ready_at;
 #pragma unroll
     for (int s = 0; s < DR; ++s)
         if (c + s < c_full_end)  // uniform
@@ -789,7 +801,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     if (wait_t && !s_ready) {  // uniform; rare: wait for the last producer
         if (tid == 0) {
             uint32_t it = 0;
-            while (ctr_load(d.ctr() + kCtrTReady) == 0 && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
+            while (ctr_load(ready_ctr) < ready_at && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
         }
         __syncthreads();
     }
@@ -805,6 +817,8 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // the sums into).
     f32x4_t pv[kRedP];
     i32x4_t tq[2], iq;
+    f32x4_t dq[kDirectMaxKr];  // direct: tile (wave) of each K range's partial t
+    float sq[kDirectMaxKr];    // direct + NORM: row (tid < 16) of each K range's sum of squares
     if (SPLIT) {
         const int64_t sstride = p.row_blocks * tile_floats * 4;  // bytes between slices of a row block
         const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
@@ -813,20 +827,47 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
         for (int v = 0; v < kRedP; ++v)
             pv[v] = load_f4_coherent(rp, (int)(v * sstride) + (wave_off + lane) * 16);
     }
-    if (lora) {
-        const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(d.t32(), 0, t_pieces * 16, 0x00020000);
-        tq[0] = load_i4_coherent(rt, tid * 16);
-        tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
+    const int64_t ptile = (int64_t)p.jt * 64 * 4;  // floats of one K range's partial tiles
+    if (direct) {
+        if (lora && wave < p.jt) {  // (uniform) tile `wave`, K ranges past prod_kr read as zeros
+            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+                d.tpart(), 0, (int)(p.prod_kr * ptile * 4), 0x00020000);
+#pragma unroll
+            for (int q = 0; q < kDirectMaxKr; ++q)
+                dq[q] = load_f4_coherent(rq, (int)((q * ptile + (wave * 64 + lane) * 4) * 4));
+        }
+        if (NORM) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                d.ssp(), 0, (int)(p.prod_kr * 16 * 4), 0x00020000);
+#pragma unroll
+            for (int q = 0; q < kDirectMaxKr; ++q)
+                sq[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 16 + (tid & 15)) * 4, 0, kSc1));
+        }
+    } else {
+        if (lora) {
+            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(d.t32(), 0, t_pieces * 16, 0x00020000);
+            tq[0] = load_i4_coherent(rt, tid * 16);
+            tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
+        }
+        if (NORM) iq = load_i4_coherent(coherent_rsrc(d.inv()), (tid & 3) * 16);  // 1 / rms of the 16 rows
     }
-    if (NORM) iq = load_i4_coherent(coherent_rsrc(d.inv()), (tid & 3) * 16);  // 1 / rms of the 16 rows
     // The values are taken here, after every load has been issued: without
     // this the compiler folds the sums below into the conditional loads and
     // waits for each load before issuing the next.
     if (SPLIT)
 #pragma unroll
         for (int v = 0; v < kRedP; ++v) asm volatile("" : "+v"(pv[v]));
-    if (lora) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
-    if (NORM) asm volatile("" : "+v"(iq));
+    if (direct) {
+        if (lora && wave < p.jt)
+#pragma unroll
+            for (int q = 0; q < kDirectMaxKr; ++q) asm volatile("" : "+v"(dq[q]));
+        if (NORM)
+#pragma unroll
+            for (int q = 0; q < kDirectMaxKr; ++q) asm volatile("" : "+v"(sq[q]));
+    } else {
+        if (lora) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
+        if (NORM) asm volatile("" : "+v"(iq));
+    }
     if (SPLIT) {
         acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -847,11 +888,47 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     uint16_t *th = reinterpret_cast<uint16_t *>(lds);  // t16 [2][16][rp]: hi, then lo
     uint16_t *tl = th + 16 * p.rp;
     __shared__ __attribute__((aligned(16))) float s_inv[16];
-    if (lora) {  // (the pieces past t16 were loaded as zeros and are not stored)
-        if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
-        if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
+    if (direct) {
+        // t = the K ranges' partial tiles summed in K-range order (scaled by
+        // 1 / rms with the norm), into LDS as BF16 hi + lo in the t16 layout
+        if (NORM) {
+            if (tid < 16) {
+                float tot = 0.0f;
+#pragma unroll
+                for (int q = 0; q < kDirectMaxKr; ++q) tot += sq[q];  // zeros past prod_kr
+                s_inv[tid] = 1.0f / sqrtf(tot * (1.0f / (float)a.k) + a.norm_eps);
+            }
+            __syncthreads();
+        }
+        if (lora) {
+            if (wave < p.jt) {
+                f32x4_t t = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int q = 0; q < kDirectMaxKr; ++q) t = t + dq[q];
+                const int64_t j = 16 * wave + lr;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 4 * lq + v;
+                    const float tv = NORM ? t[v] * s_inv[m] : t[v];
+                    const uint16_t hi = f32_to_bf16_bits(tv);
+                    th[m * p.rp + j] = hi;
+                    tl[m * p.rp + j] = f32_to_bf16_bits(tv - __uint_as_float((uint32_t)hi << 16));
+                }
+            }
+            // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
+            const int pad = (int)(p.rp - 16 * p.jt);
+            for (int i = tid; i < 2 * 16 * pad; i += kThreadsD) {
+                const int h = i / (16 * pad), m = (i / pad) % 16, j = 16 * (int)p.jt + i % pad;
+                th[(h * 16 + m) * p.rp + j] = 0;
+            }
+        }
+    } else {
+        if (lora) {  // (the pieces past t16 were loaded as zeros and are not stored)
+            if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
+            if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
+        }
+        if (NORM && tid < 4) reinterpret_cast<i32x4_t *>(s_inv)[tid] = iq;
     }
-    if (NORM && tid < 4) reinterpret_cast<i32x4_t *>(s_inv)[tid] = iq;
     if (wait_t) __syncthreads();
     const float st = *a.tensor_scale, lam = a.lora_scale;
 #pragma unroll
@@ -879,7 +956,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // this row block is done with t16; the last one clears the ready flag
     // and this count for the next call
     if (wait_t && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
-        ctr_store(d.ctr() + kCtrTReady, 0u);
+        ctr_store(ready_ctr, 0u);  // (direct: the producers' count)
         ctr_store(d.ctr() + kCtrDone, 0u);
     }
 }
