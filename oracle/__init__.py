@@ -72,6 +72,14 @@ def _load():
     lib.oracle_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, flt, i64, P, P, i32, flt,
                                            P, i64, P, i32]
     lib.oracle_w4a16_lora_gemm.restype = i32
+    lib.oracle_nvfp4_quantize_sr.argtypes = [P, i64, i64, i64, P, u32, u64, P, P, P, i32]
+    lib.oracle_nvfp4_quantize_sr.restype = i32
+    lib.oracle_sr_uniform.argtypes = [u64, i64]
+    lib.oracle_sr_uniform.restype = dbl
+    lib.oracle_e2m1_sr_mag.argtypes = [dbl, dbl, dbl]
+    lib.oracle_e2m1_sr_mag.restype = i32
+    lib.oracle_mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P]
+    lib.oracle_mxfp4_quantize.restype = i32
     lib.oracle_w4a16_lora_gemm_f64.argtypes = lib.oracle_w4a16_lora_gemm.argtypes
     lib.oracle_w4a16_lora_gemm_f64.restype = i32
     lib.oracle_aqn_sigma.argtypes = [i32, i32, dbl, dbl]
@@ -125,8 +133,9 @@ def e2m1_code(w: float, S: float) -> int:
 
 # -------------------------------------------------------------- quantizer --
 def nvfp4_quantize(w_bits, flags: int = SCALE_ROUND_UP, tensor_scale_in: float | None = None,
-                   threads: int = 0):
-    """BF16 [N, K] bit patterns -> (packed u8 [N, K/2], scales u8 [N, K/16], s_t float32)."""
+                   threads: int = 0, stochastic_seed: int | None = None):
+    """BF16 [N, K] bit patterns -> (packed u8 [N, K/2], scales u8 [N, K/16], s_t float32).
+    stochastic_seed: stochastic element rounding with that seed (else nearest-even)."""
     w = _bits16(w_bits)
     if w.ndim != 2:
         raise ValueError("w must be 2-D")
@@ -139,12 +148,38 @@ def nvfp4_quantize(w_bits, flags: int = SCALE_ROUND_UP, tensor_scale_in: float |
     scales = np.zeros((n, k // 16), dtype=np.uint8)
     s_out = np.zeros(1, dtype=np.float32)
     s_in = None if tensor_scale_in is None else np.array([tensor_scale_in], dtype=np.float32)
-    rc = _load().oracle_nvfp4_quantize(_ptr(w), n, k, ldw, None if s_in is None else _ptr(s_in),
-                                       int(flags), _ptr(packed), _ptr(scales), _ptr(s_out),
-                                       int(threads))
+    if stochastic_seed is None:
+        rc = _load().oracle_nvfp4_quantize(_ptr(w), n, k, ldw, None if s_in is None else _ptr(s_in),
+                                           int(flags), _ptr(packed), _ptr(scales), _ptr(s_out),
+                                           int(threads))
+    else:
+        rc = _load().oracle_nvfp4_quantize_sr(_ptr(w), n, k, ldw, None if s_in is None else _ptr(s_in),
+                                              int(flags), int(stochastic_seed) & (2 ** 64 - 1), _ptr(packed),
+                                              _ptr(scales), _ptr(s_out), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_nvfp4_quantize rejected its arguments (rc={rc})")
     return packed, scales, np.float32(s_out[0])
+
+
+def sr_uniform(seed: int, e: int) -> float:
+    """The uniform in [0, 1) that stochastic rounding draws for element e."""
+    return float(_load().oracle_sr_uniform(int(seed) & (2 ** 64 - 1), int(e)))
+
+
+def e2m1_sr_mag(aw: float, S: float, u: float) -> int:
+    return int(_load().oracle_e2m1_sr_mag(float(aw), float(S), float(u)))
+
+
+def mxfp4_quantize(w_bits):
+    """BF16 [N, K] bit patterns (K % 32 == 0) -> (packed u8 [N, K/2], E8M0 scales u8 [N, K/32])."""
+    w = np.ascontiguousarray(_bits16(w_bits))
+    n, k = w.shape
+    packed = np.zeros((n, k // 2), dtype=np.uint8)
+    scales = np.zeros((n, k // 32), dtype=np.uint8)
+    rc = _load().oracle_mxfp4_quantize(_ptr(w), n, k, k, _ptr(packed), _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"oracle_mxfp4_quantize rejected its arguments (rc={rc})")
+    return packed, scales
 
 
 # ------------------------------------------------------------ W4A16 GEMM --

@@ -211,7 +211,12 @@ typedef struct {
     const uint16_t *w; int64_t n, k, ldw;
     uint8_t *packed, *scales;
     double s_t; unsigned flags;
+    int stochastic; uint64_t seed;   /* element rounding: stochastic (see below) */
 } quant_ctx;
+
+static double sr_uniform(uint64_t seed, int64_t e);
+static int e2m1_sr_mag(double aw, double S, double u);
+void oracle_philox4x64_10(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]);
 
 static void quant_rows(void *p, int64_t r0, int64_t r1) {
     quant_ctx *c = (quant_ctx *)p;
@@ -234,7 +239,10 @@ static void quant_rows(void *p, int64_t r0, int64_t r1) {
                     uint16_t bits = wr[b * 16 + i + h];
                     double v = oracle_bf16_decode(bits);
                     int sign = (bits >> 15) & 1;              /* signbit(w) */
-                    code[h] = (sign << 3) | e2m1_rne_mag(fabs(v), S);
+                    int mag = c->stochastic
+                                  ? e2m1_sr_mag(fabs(v), S, sr_uniform(c->seed, row * c->k + b * 16 + i + h))
+                                  : e2m1_rne_mag(fabs(v), S);
+                    code[h] = (sign << 3) | mag;
                 }
                 c->packed[row * (c->k / 2) + (b * 16 + i) / 2] =
                     (uint8_t)(code[0] | (code[1] << 4));
@@ -244,10 +252,9 @@ static void quant_rows(void *p, int64_t r0, int64_t r1) {
 }
 
 /* returns 0 on success, -1 on bad arguments */
-int oracle_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
-                          const float *s_t_in, unsigned flags,
-                          uint8_t *packed, uint8_t *scales, float *s_t_out,
-                          int threads) {
+static int quantize_impl(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
+                         const float *s_t_in, unsigned flags, int stochastic, uint64_t seed,
+                         uint8_t *packed, uint8_t *scales, float *s_t_out, int threads) {
     if (!w || !packed || !scales || !s_t_out || n <= 0 || k <= 0 || k % 16 || ldw < k)
         return -1;
     float s_t;
@@ -267,8 +274,106 @@ int oracle_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
         s_t = (amax == 0.0f) ? 1.0f : amax / 2688.0f;
     }
     *s_t_out = s_t;
-    quant_ctx c = {w, n, k, ldw, packed, scales, (double)s_t, flags};
+    quant_ctx c = {w, n, k, ldw, packed, scales, (double)s_t, flags, stochastic, seed};
     parallel_range(threads, n, quant_rows, &c);
+    return 0;
+}
+
+int oracle_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
+                          const float *s_t_in, unsigned flags,
+                          uint8_t *packed, uint8_t *scales, float *s_t_out,
+                          int threads) {
+    return quantize_impl(w, n, k, ldw, s_t_in, flags, 0, 0, packed, scales, s_t_out, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stochastic element rounding ([BoA-NVFP4]: the FP4 training work it cites   */
+/* pairs 16-value blocks with stochastic rounding)                           */
+/* ------------------------------------------------------------------------ */
+/* Reading (self-defined stream, the pages name the method only): with
+ * lo <= |w|/S < hi the neighbouring E2M1 grid points, the element rounds up to
+ * hi with probability (|w|/S - lo) / (hi - lo), else down to lo, so that the
+ * expected dequantized value is w.  Values at or above 6 S saturate to 6; grid
+ * values stay.  The uniform of element e (row-major index row * k + col) is
+ * u = (r >> 40) * 2^-24 for word e % 4 of Philox4x64-10 with key (seed, 0)
+ * and counter (e / 4, 0, 1, 0).  Rounding up <=> u * (hi - lo) * S < |w| - lo * S,
+ * evaluated exactly in fp64: (hi - lo) is a power of two, u has 24
+ * significant bits and S = E4M3 * s_t at most 28; |w| - lo * S is exact by
+ * Sterbenz's lemma (lo * S <= |w| < hi * S <= 2 lo * S when lo > 0).        */
+static double sr_uniform(uint64_t seed, int64_t e) {
+    const uint64_t ctr[4] = {(uint64_t)e / 4, 0, 1, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t r[4];
+    oracle_philox4x64_10(ctr, key, r);
+    return (double)(r[e % 4] >> 40) * 0x1p-24;
+}
+
+static int e2m1_sr_mag(double aw, double S, double u) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    if (S == 0.0) return 0;
+    int lo = 0;
+    for (int i = 1; i < 8; ++i)
+        if (grid[i] * S <= aw) lo = i;
+    if (lo == 7) return 7;
+    return u * (grid[lo + 1] - grid[lo]) * S < aw - grid[lo] * S ? lo + 1 : lo;
+}
+
+/* exposed for the tests: the uniform element e draws, and the magnitude code
+ * of |w| in a block of scale S given that uniform */
+double oracle_sr_uniform(uint64_t seed, int64_t e) { return sr_uniform(seed, e); }
+int oracle_e2m1_sr_mag(double aw, double S, double u) { return e2m1_sr_mag(aw, S, u); }
+
+int oracle_nvfp4_quantize_sr(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
+                             const float *s_t_in, unsigned flags, uint64_t seed,
+                             uint8_t *packed, uint8_t *scales, float *s_t_out, int threads) {
+    return quantize_impl(w, n, k, ldw, s_t_in, flags, 1, seed, packed, scales, s_t_out, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* MXFP4 (OCP MX v1.0): blocks of 32 along K, one E8M0 scale each             */
+/* ------------------------------------------------------------------------ */
+/* [BoA-NVFP4] contrasts NVFP4's 16-value blocks with MXFP4's 32.
+ * [OCP-MX] conversion: X = 2^(floor(log2(amax_b)) - emax) with emax = 2 for
+ * E2M1, stored as the E8M0 byte floor(log2(amax_b)) - 2 + 127 (clamped to
+ * [0, 254]; an all-zero block gets byte 0); elements round to nearest-even on
+ * the E2M1 grid of |w| / X, saturating at 6, sign = signbit(w).  A block with
+ * a non-finite element gets the NaN byte 0xFF and unspecified elements.
+ * Layout as NVFP4: packed[n, k/2] (even element in the low nibble),
+ * scales[n, k/32].                                                          */
+int oracle_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
+                          uint8_t *packed, uint8_t *scales) {
+    if (!w || !packed || !scales || n <= 0 || k <= 0 || k % 32 || ldw < k) return -1;
+    for (int64_t row = 0; row < n; ++row) {
+        const uint16_t *wr = w + row * ldw;
+        for (int64_t b = 0; b < k / 32; ++b) {
+            double amax = 0.0;
+            int finite = 1;
+            for (int i = 0; i < 32; ++i) {
+                double v = oracle_bf16_decode(wr[b * 32 + i]);
+                if (!isfinite(v)) finite = 0;
+                else if (fabs(v) > amax) amax = fabs(v);
+            }
+            if (!finite) { scales[row * (k / 32) + b] = 0xFF; continue; }
+            int code = 0;
+            if (amax > 0.0) {
+                int ex;
+                frexp(amax, &ex);          /* amax = f * 2^ex, f in [0.5, 1): floor(log2) = ex - 1 */
+                code = (ex - 1) - 2 + 127;
+                if (code < 0) code = 0;
+                if (code > 254) code = 254;
+            }
+            scales[row * (k / 32) + b] = (uint8_t)code;
+            double X = ldexp(1.0, code - 127);
+            for (int i = 0; i < 32; i += 2) {
+                int c2[2];
+                for (int h = 0; h < 2; ++h) {
+                    uint16_t bits = wr[b * 32 + i + h];
+                    c2[h] = (((bits >> 15) & 1) << 3) | e2m1_rne_mag(fabs(oracle_bf16_decode(bits)), X);
+                }
+                packed[row * (k / 2) + (b * 32 + i) / 2] = (uint8_t)(c2[0] | (c2[1] << 4));
+            }
+        }
+    }
     return 0;
 }
 
