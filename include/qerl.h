@@ -102,6 +102,40 @@ qerl_status qerl_nvfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_
                                 const float *tensor_scale_in, uint32_t flags,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * qerl_nvfp4_quantize with stochastic rounding of the elements (the FP4
+ * training work that the bitsofall page's "NVFP4: NVIDIA's FP4 Format"
+ * section cites pairs 16-value blocks with stochastic rounding): s_t and the
+ * block scales are exactly those of qerl_nvfp4_quantize with the same flags;
+ * each element goes to one of the two E2M1 grid points lo <= |w|/S < hi
+ * around it (S = E4M3(sb) s_t), to hi with probability (|w|/S - lo)/(hi - lo),
+ * so its expected dequantized value is w (values at or above 6 S take 6, grid
+ * values stay).  The uniform of element e = row * k + col is u = (r >> 40) 2^-24
+ * for word e % 4 of Philox4x64-10 (Salmon et al., SC'11) with key (seed, 0)
+ * and counter (e / 4, 0, 1, 0); up <=> u (hi - lo) S < |w| - lo S, decided
+ * exactly.  Same arguments, workspace and errors as qerl_nvfp4_quantize.
+ */
+qerl_status qerl_nvfp4_quantize_stochastic(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                           uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                           const float *tensor_scale_in, uint32_t flags, uint64_t seed,
+                                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * BF16 -> MXFP4 (OCP Microscaling Formats v1.0: E2M1 elements, one E8M0 scale
+ * per 32 elements along k), the coarser sibling format the bitsofall page
+ * ("NVFP4: NVIDIA's FP4 Format") contrasts with NVFP4's 16-value blocks:
+ *   scale byte = floor(log2 amax_b) - 2 + 127 clamped to [0, 254] (0 for an
+ *                all-zero block; 0xFF, with zero codes, for a block holding
+ *                Inf or NaN); X = 2^(byte - 127)
+ *   code       = signbit(w) << 3 | RNE of |w| / X onto the E2M1 grid,
+ *                saturating at 6
+ * Outputs: packed uint8 [n, k/2] (nibble order as qerl_nvfp4_quantize), scales
+ * uint8 [n, k/32].  One pass, no workspace.  Requires n >= 1, k >= 32,
+ * k % 32 == 0, ldw >= k, 16-byte aligned w/packed and ldw % 8 == 0.
+ */
+qerl_status qerl_mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                uint8_t *packed, uint8_t *scales, void *stream);
+
 /* ----------------------------------------------------------------------- */
 /* W4A16 (NVFP4 weight x BF16 activation) linear layer with LoRA epilogue   */
 /* ----------------------------------------------------------------------- */

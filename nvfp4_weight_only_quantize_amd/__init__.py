@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
     L.qerl_nvfp4_quantize_workspace_size.restype = sz
     L.qerl_nvfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P, P, u32, P, sz, P]
     L.qerl_nvfp4_quantize.restype = ctypes.c_int
+    L.qerl_nvfp4_quantize_stochastic.argtypes = [P, i64, i64, i64, P, P, P, P, u32, u64, P, sz, P]
+    L.qerl_nvfp4_quantize_stochastic.restype = ctypes.c_int
+    L.qerl_mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P]
+    L.qerl_mxfp4_quantize.restype = ctypes.c_int
     L.qerl_w4a16_lora_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
     L.qerl_w4a16_lora_gemm_workspace_size.restype = sz
     L.qerl_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, P, i64, P, P, i32, f32, P, i64,
@@ -143,11 +147,12 @@ def nvfp4_quantize_workspace_size(n: int, k: int) -> int:
 
 def nvfp4_quantize(w: torch.Tensor, flags: int = SCALE_ROUND_UP, tensor_scale_in=None,
                    out: NVFP4Weight | None = None, workspace: torch.Tensor | None = None,
-                   stream=None, check_finite: bool = True) -> NVFP4Weight:
+                   stream=None, check_finite: bool = True, stochastic_seed: int | None = None) -> NVFP4Weight:
     """Quantize a BF16 [N, K] GPU tensor to NVFP4 (K % 16 == 0).
 
     ``check_finite`` synchronizes and raises if the tensor held a NaN/Inf (the
-    library reports it in-band as a NaN tensor scale)."""
+    library reports it in-band as a NaN tensor scale).  ``stochastic_seed``:
+    stochastic element rounding with that seed (qerl_nvfp4_quantize_stochastic)."""
     _need(w, "w", torch.bfloat16, 2)
     n, k = w.shape
     ldw = _rows(w, "w")
@@ -161,12 +166,30 @@ def nvfp4_quantize(w: torch.Tensor, flags: int = SCALE_ROUND_UP, tensor_scale_in
     if workspace is None and tensor_scale_in is None:
         workspace = torch.empty(nvfp4_quantize_workspace_size(n, k), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().qerl_nvfp4_quantize(_ptr(w), n, k, ldw, _ptr(out.packed), _ptr(out.scales),
-                                     _ptr(out.tensor_scale), _ptr(tensor_scale_in), int(flags),
-                                     _ptr(workspace), ws_bytes, _stream(stream, dev)))
+    if stochastic_seed is None:
+        _check(lib().qerl_nvfp4_quantize(_ptr(w), n, k, ldw, _ptr(out.packed), _ptr(out.scales),
+                                         _ptr(out.tensor_scale), _ptr(tensor_scale_in), int(flags),
+                                         _ptr(workspace), ws_bytes, _stream(stream, dev)))
+    else:
+        _check(lib().qerl_nvfp4_quantize_stochastic(_ptr(w), n, k, ldw, _ptr(out.packed), _ptr(out.scales),
+                                                    _ptr(out.tensor_scale), _ptr(tensor_scale_in), int(flags),
+                                                    int(stochastic_seed) & (2 ** 64 - 1), _ptr(workspace),
+                                                    ws_bytes, _stream(stream, dev)))
     if check_finite and not torch.isfinite(out.tensor_scale).all().item():
         raise QerlError(4, "weight tensor holds a NaN or Inf (tensor scale is NaN)")
     return out
+
+
+def mxfp4_quantize(w: torch.Tensor, stream=None):
+    """BF16 [N, K] GPU tensor (K % 32 == 0) -> (packed u8 [N, K/2], E8M0 scales u8 [N, K/32])."""
+    _need(w, "w", torch.bfloat16, 2)
+    n, k = w.shape
+    dev = w.device
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, max(k // 32, 0)), dtype=torch.uint8, device=dev)
+    _check(lib().qerl_mxfp4_quantize(_ptr(w), n, k, _rows(w, "w"), _ptr(packed), _ptr(scales),
+                                     _stream(stream, dev)))
+    return packed, scales
 
 
 # --------------------------------------------------------- W4A16 + LoRA ----

@@ -58,28 +58,64 @@ size_t qerl_nvfp4_quantize_workspace_size(int64_t n, int64_t k) {
     return qerl::quantize_workspace_bytes(n, k);
 }
 
+static qerl_status quantize_common(const char *what, const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                   uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                   const float *tensor_scale_in, uint32_t flags, void *workspace,
+                                   size_t workspace_bytes, void *stream, bool stochastic, uint64_t seed);
+
 qerl_status qerl_nvfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
                                 uint8_t *packed, uint8_t *scales, float *tensor_scale,
                                 const float *tensor_scale_in, uint32_t flags,
                                 void *workspace, size_t workspace_bytes, void *stream) {
+    return quantize_common("nvfp4_quantize", w_bf16, n, k, ldw, packed, scales, tensor_scale, tensor_scale_in,
+                           flags, workspace, workspace_bytes, stream, false, 0);
+}
+
+qerl_status qerl_nvfp4_quantize_stochastic(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                           uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                           const float *tensor_scale_in, uint32_t flags, uint64_t seed,
+                                           void *workspace, size_t workspace_bytes, void *stream) {
+    return quantize_common("nvfp4_quantize_stochastic", w_bf16, n, k, ldw, packed, scales, tensor_scale,
+                           tensor_scale_in, flags, workspace, workspace_bytes, stream, true, seed);
+}
+
+qerl_status qerl_mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw, uint8_t *packed,
+                                uint8_t *scales, void *stream) {
+    g_last_error[0] = '\0';
+    if (!w_bf16 || !packed || !scales) return fail(QERL_ERR_NULL, "mxfp4_quantize: w, packed and scales are required");
+    if (n < 1 || k < 32 || k % 32 != 0 || ldw < k || n > kMaxElems / k || ldw > kMaxElems)
+        return fail(QERL_ERR_SHAPE, "mxfp4_quantize: need n >= 1, k >= 32, k %% 32 == 0, ldw >= k "
+                    "(got n=%lld k=%lld ldw=%lld)", (long long)n, (long long)k, (long long)ldw);
+    if (!aligned16(w_bf16) || !aligned16(packed) || ldw % 8 != 0)
+        return fail(QERL_ERR_ALIGN, "mxfp4_quantize: w and packed must be 16-byte aligned and ldw %% 8 == 0");
+    return hip_status(qerl::launch_mxfp4_quantize(static_cast<const uint16_t *>(w_bf16), n, k, ldw, packed, scales,
+                                                  static_cast<hipStream_t>(stream)),
+                      "mxfp4_quantize launch");
+}
+
+static qerl_status quantize_common(const char *what, const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
+                                   uint8_t *packed, uint8_t *scales, float *tensor_scale,
+                                   const float *tensor_scale_in, uint32_t flags, void *workspace,
+                                   size_t workspace_bytes, void *stream, bool stochastic, uint64_t seed) {
     g_last_error[0] = '\0';
     if (!w_bf16 || !packed || !scales || !tensor_scale)
-        return fail(QERL_ERR_NULL, "nvfp4_quantize: w, packed, scales and tensor_scale are required");
+        return fail(QERL_ERR_NULL, "%s: w, packed, scales and tensor_scale are required", what);
     if (n < 1 || k < 16 || k % 16 != 0 || ldw < k || n > kMaxElems / k || ldw > kMaxElems)
-        return fail(QERL_ERR_SHAPE, "nvfp4_quantize: need n >= 1, k >= 16, k %% 16 == 0, ldw >= k "
-                    "(got n=%lld k=%lld ldw=%lld)", (long long)n, (long long)k, (long long)ldw);
+        return fail(QERL_ERR_SHAPE, "%s: need n >= 1, k >= 16, k %% 16 == 0, ldw >= k "
+                    "(got n=%lld k=%lld ldw=%lld)", what, (long long)n, (long long)k, (long long)ldw);
     if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(scales) || ldw % 8 != 0 ||
         ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)tensor_scale_in & 3u))
-        return fail(QERL_ERR_ALIGN, "nvfp4_quantize: pointers must be 16-byte aligned and ldw %% 8 == 0");
-    if (flags & ~1u) return fail(QERL_ERR_ARG, "nvfp4_quantize: unknown flag bits 0x%x", flags);
+        return fail(QERL_ERR_ALIGN, "%s: pointers must be 16-byte aligned and ldw %% 8 == 0", what);
+    if (flags & ~1u) return fail(QERL_ERR_ARG, "%s: unknown flag bits 0x%x", what, flags);
     if (!tensor_scale_in && (!workspace || workspace_bytes < qerl::quantize_workspace_bytes(n, k)))
-        return fail(QERL_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed",
-                    qerl::quantize_workspace_bytes(n, k));
+        return fail(QERL_ERR_WORKSPACE, "%s: workspace of %zu bytes needed",
+                    what, qerl::quantize_workspace_bytes(n, k));
     if (workspace && !aligned16(workspace))
-        return fail(QERL_ERR_ALIGN, "nvfp4_quantize: workspace must be 16-byte aligned");
+        return fail(QERL_ERR_ALIGN, "%s: workspace must be 16-byte aligned", what);
     return hip_status(qerl::launch_nvfp4_quantize(static_cast<const uint16_t *>(w_bf16), n, k, ldw,
                                                   packed, scales, tensor_scale, tensor_scale_in,
-                                                  flags, workspace, static_cast<hipStream_t>(stream)),
+                                                  flags, workspace, static_cast<hipStream_t>(stream),
+                                                  stochastic, seed),
                       "nvfp4_quantize launch");
 }
 

@@ -73,4 +73,23 @@ __device__ __forceinline__ float block_sum_256(float v, float *scratch /* >= 4 f
     return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
 }
 
+// Counter-based Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): round
+// multipliers and key increments (Weyl sequence constants) as published.
+struct U64x4 { uint64_t v[4]; };
+__device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                               uint64_t k0, uint64_t k1) {
+    constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull, kMul1 = 0xCA5A826395121157ull;
+    constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull, kWeyl1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint64_t hi0 = __umul64hi(kMul0, c0), lo0 = kMul0 * c0;
+        const uint64_t hi1 = __umul64hi(kMul1, c2), lo1 = kMul1 * c2;
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        k0 += kWeyl0;
+        k1 += kWeyl1;
+    }
+    return U64x4{{c0, c1, c2, c3}};
+}
+
 }  // namespace qerl

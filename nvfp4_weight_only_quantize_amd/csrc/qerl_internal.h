@@ -12,10 +12,14 @@ namespace qerl {
 // ---- quantizer ----
 constexpr int kAmaxMaxBlocks = 1024;  // per-workgroup partial maxima kept in the workspace
 size_t quantize_workspace_bytes(int64_t n, int64_t k);
+// stochastic: stochastic element rounding with stream `seed`
 hipError_t launch_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
                                  uint8_t *packed, uint8_t *scales, float *tensor_scale,
                                  const float *tensor_scale_in, uint32_t flags, void *workspace,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool stochastic = false, uint64_t seed = 0);
+// BF16 -> MXFP4 (k % 32 == 0): packed [n, k/2], E8M0 scales [n, k/32]; no workspace
+hipError_t launch_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw, uint8_t *packed,
+                                 uint8_t *scales, hipStream_t stream);
 
 // ---- W4A16 + LoRA ----
 struct GemmArgs {

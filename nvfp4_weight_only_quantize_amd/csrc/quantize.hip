@@ -137,6 +137,30 @@ __device__ __forceinline__ uint32_t e2m1_mag_f64(float a, const float (&ce)[7], 
     return mag;
 }
 
+// Stochastic rounding of |w| (a) in a block of scale S = e * s_t: between the
+// neighbouring grid points lo <= a / S < hi, up with probability
+// (a / S - lo) / (hi - lo): up <=> u (hi - lo) S < a - lo S, where u is the
+// element's 24-bit uniform.  Exact in double: S has at most 28 significant
+// bits, (hi - lo) is a power of two, and a - lo S is exact (lo S <= a < 2 lo S
+// when lo > 0).  Values at or above 6 S take 6.
+__device__ __forceinline__ uint32_t e2m1_mag_sr(float a, float e, float st, uint32_t u24) {
+    const double S = (double)e * (double)st, d = (double)a;
+    constexpr double g[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    uint32_t lo = 0;
+#pragma unroll
+    for (int i = 1; i < 8; ++i) lo += g[i] * S <= d;
+    if (lo == 7) return 7;
+    double glo = 0.0, gap = 0.5;
+#pragma unroll
+    for (int i = 1; i < 7; ++i)
+        if (lo == (uint32_t)i) {
+            glo = g[i];
+            gap = g[i + 1] - g[i];
+        }
+    const double u = (double)u24 * 0x1p-24;
+    return lo + (u * (gap * S) < d - glo * S ? 1u : 0u);
+}
+
 struct EncodeParams {
     const uint16_t *w;
     int64_t n, k, ldw;
@@ -147,8 +171,13 @@ struct EncodeParams {
     const uint32_t *partial;
     int num_partials;
     uint32_t flags;
+    uint64_t seed;  // SR: the stochastic-rounding stream
 };
 
+// SR: stochastic element rounding; the uniform of element e (row-major index
+// row * k + col) is the top 24 bits of word e % 4 of Philox4x64-10 with key
+// (seed, 0) and counter (e / 4, 0, 1, 0).
+template <bool SR>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
     __shared__ float s_st;
     if (threadIdx.x < kWave) {
@@ -193,7 +222,25 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
         const int sb = rne ? scale_code_rne(amax_b, st) : scale_code_round_up(amax_b, st);
         const float e = e4m3_value(sb);
         uint32_t lo = 0, hi = 0;
-        if (e != 0.0f) {
+        if (SR && e != 0.0f) {
+            const int64_t row = b / bpr;
+            const uint64_t e0 = (uint64_t)(row * p.k + (b - row * bpr) * 16);  // a multiple of 16
+            uint32_t u[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const U64x4 r = philox4x64_10(e0 / 4 + q, 0, 1, 0, p.seed, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[4 * q + i] = (uint32_t)(r.v[i] >> 40);
+            }
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
+                const float a = __uint_as_float((bits & 0x7FFFu) << 16);
+                const uint32_t code = e2m1_mag_sr(a, e, st, u[j]) | ((bits >> 12) & 8u);
+                if (j < 8) lo |= code << (4 * j);
+                else hi |= code << (4 * (j - 8));
+            }
+        } else if (e != 0.0f) {
             const float ce[7] = {0.25f * e, 0.75f * e, 1.25f * e, 1.75f * e,
                                  2.5f * e,  3.5f * e,  5.0f * e};
 #pragma unroll
@@ -237,7 +284,7 @@ size_t quantize_workspace_bytes(int64_t, int64_t) { return kAmaxMaxBlocks * size
 hipError_t launch_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
                                  uint8_t *packed, uint8_t *scales, float *tensor_scale,
                                  const float *tensor_scale_in, uint32_t flags, void *workspace,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool stochastic, uint64_t seed) {
     uint32_t *partial = static_cast<uint32_t *>(workspace);
     int g1 = 0;
     if (!tensor_scale_in) {
@@ -248,12 +295,93 @@ hipError_t launch_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    EncodeParams p{w, n, k, ldw, packed, scales, tensor_scale, tensor_scale_in, partial, g1, flags};
+    EncodeParams p{w, n, k, ldw, packed, scales, tensor_scale, tensor_scale_in, partial, g1, flags, seed};
     const int64_t blocks16 = n * (k >> 4);
     const int64_t want = (blocks16 + kThreads - 1) / kThreads;
     const int64_t cap = (int64_t)num_cus() * 16;
     const int g2 = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL(encode_kernel, dim3(g2), dim3(kThreads), 0, stream, p);
+    if (stochastic)
+        hipLaunchKernelGGL(encode_kernel<true>, dim3(g2), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(encode_kernel<false>, dim3(g2), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ---- MXFP4 (OCP MX v1.0): 32-element blocks along K, E8M0 scale ----
+// One thread per block: 64 B in, 16 B of codes and 1 scale byte out.  The
+// scale is 2^(floor(log2 amax) - 2) (E8M0 byte clamped to [0, 254], 0 for an
+// all-zero block, 0xFF for a block with Inf/NaN and zero codes); |w| / X is
+// exact (X a power of two) and rounds to nearest-even on the E2M1 grid with
+// the midpoint comparisons of the NVFP4 encoder, saturating at 6.
+__global__ __launch_bounds__(kThreads) void mxfp4_encode_kernel(const uint16_t *__restrict__ w, int64_t n,
+                                                                int64_t k, int64_t ldw, uint8_t *__restrict__ packed,
+                                                                uint8_t *__restrict__ scales) {
+    const int64_t bpr = k >> 5, total = n * bpr;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < total; b += stride) {
+        const int64_t row = b / bpr;
+        const uint4 *src = reinterpret_cast<const uint4 *>(w + row * ldw + (b - row * bpr) * 32);
+        const uint4 v[4] = {src[0], src[1], src[2], src[3]};
+        const uint32_t am = max(max(absmax_vec(v[0]), absmax_vec(v[1])), max(absmax_vec(v[2]), absmax_vec(v[3])));
+        uint4 out = make_uint4(0, 0, 0, 0);
+        uint32_t code = 0;
+        if (am >= 0x7F80u) {
+            code = 0xFF;
+        } else if (am != 0) {
+            const int ef = (int)(am >> 7);  // BF16 exponent field
+            const int fl = ef > 0 ? ef - 127 : (31 - __builtin_clz(am & 0x7Fu)) - 133;  // floor(log2 amax)
+            int c = fl - 2 + 127;
+            c = c < 0 ? 0 : (c > 254 ? 254 : c);
+            code = (uint32_t)c;
+            // 1 / X = 2^(127 - c), a normal float for c <= 253 (BF16 amax gives c <= 252)
+            const float r = c <= 253 ? __uint_as_float((uint32_t)(254 - c) << 23) : 0x1p-127f;
+            uint32_t wd[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wd[4 * q] = v[q].x;
+                wd[4 * q + 1] = v[q].y;
+                wd[4 * q + 2] = v[q].z;
+                wd[4 * q + 3] = v[q].w;
+            }
+            uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
+                const float a = __uint_as_float((bits & 0x7FFFu) << 16) * r;  // |w| / X, exact
+                uint32_t mag = 0;
+                mag += a > 0.25f;
+                mag += a >= 0.75f;
+                mag += a > 1.25f;
+                mag += a >= 1.75f;
+                mag += a > 2.5f;
+                mag += a >= 3.5f;
+                mag += a > 5.0f;
+                o[j >> 3] |= (mag | ((bits >> 12) & 8u)) << (4 * (j & 7));
+            }
+            out = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {  // all zero: signed zero codes
+            uint32_t o[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const uint4 q = v[j >> 3];
+                const uint32_t word = ((j >> 1) & 3) == 0 ? q.x : ((j >> 1) & 3) == 1 ? q.y : ((j >> 1) & 3) == 2 ? q.z : q.w;
+                const uint32_t bits = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+                o[j >> 3] |= ((bits >> 12) & 8u) << (4 * (j & 7));
+            }
+            out = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        reinterpret_cast<uint4 *>(packed + row * (k >> 1))[b - row * bpr] = out;
+        scales[b] = (uint8_t)code;
+    }
+}
+
+hipError_t launch_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw, uint8_t *packed,
+                                 uint8_t *scales, hipStream_t stream) {
+    const int64_t blocks32 = n * (k >> 5);
+    const int64_t want = (blocks32 + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)num_cus() * 16;
+    const int g = (int)(want < cap ? (want < 1 ? 1 : want) : cap);
+    hipLaunchKernelGGL(mxfp4_encode_kernel, dim3(g), dim3(kThreads), 0, stream, w, n, k, ldw, packed, scales);
     return hipGetLastError();
 }
 

@@ -208,3 +208,28 @@ def test_aqn_noisy_weight_argument_errors(kw, status):
     a.update(kw)
     assert q.lib().qerl_aqn_noisy_weight(P(a["w"]), a["h"], a["sigma"], a["seed"], a["step"], a["layer"],
                                          P(a["out"]), P(a["stream"])) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(packed=None), 1), (dict(scales=None), 1), (dict(n=0), 2), (dict(k=48, ldw=48), 2),
+    (dict(k=16, ldw=16), 2), (dict(ldw=32), 2), (dict(w=FAKE + 2), 3), (dict(packed=FAKE + 8), 3),
+    (dict(ldw=68), 3),
+])
+def test_mxfp4_argument_errors(kw, status):
+    a = dict(w=FAKE, n=4, k=64, ldw=64, packed=FAKE, scales=FAKE, stream=None)
+    a.update(kw)
+    assert q.lib().qerl_mxfp4_quantize(P(a["w"]), a["n"], a["k"], a["ldw"], P(a["packed"]), P(a["scales"]),
+                                       P(a["stream"])) == status
+    assert q.lib().qerl_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(w=None), 1), (dict(n=0), 2), (dict(k=24, ldw=24), 2), (dict(flags=4), 4), (dict(ws=None), 5),
+])
+def test_quantize_stochastic_argument_errors(kw, status):
+    a = dict(w=FAKE, n=4, k=64, ldw=64, packed=FAKE, scales=FAKE, ts=FAKE, flags=0, seed=1, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    assert q.lib().qerl_nvfp4_quantize_stochastic(P(a["w"]), a["n"], a["k"], a["ldw"], P(a["packed"]),
+                                                  P(a["scales"]), P(a["ts"]), None, a["flags"], a["seed"],
+                                                  P(a["ws"]), a["wsb"], None) == status
+    assert b"nvfp4_quantize_stochastic" in q.lib().qerl_last_error()
