@@ -489,6 +489,72 @@ def quantizer_leg(dev, reps):
             "whole_model_ms_est": t * 1e3 * 64}
 
 
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _dequant_codes(packed):
+    """E2M1 values of the codes in packed [N, K/2] (torch, on the GPU)."""
+    lut = torch.tensor(list(E2M1_GRID) + [-v for v in E2M1_GRID], dtype=torch.float32, device=packed.device)
+    lo, hi = (packed & 15).long(), (packed >> 4).long()
+    return torch.stack((lut[lo], lut[hi]), dim=-1).reshape(packed.shape[0], -1)
+
+
+def quantizer_variants_leg(dev, reps):
+    """The quantizer variants the NVFP4 section names: stochastic element
+    rounding and MXFP4 (block 32, E8M0 scales), timed on the 32B layer like
+    the deterministic quantizer, and the relative L2 error of each format's
+    dequantized weights on the 7B layer (the format comparison)."""
+    shapes = synth.QWEN25_32B
+    ws = torch.empty(q.nvfp4_quantize_workspace_size(1, 16), dtype=torch.uint8, device=dev)
+    res = {"workload": "one Qwen2.5-32B-shaped layer (7 tensors, 1.09 G elements); errors on the 7B layer"}
+    ws_in, elems = {}, 0
+    for name in synth.PROJ_ORDER:
+        n, k = shapes[name]
+        ws_in[name] = synth.weight_bf16(n, k, seed=synth.seed_for(1005, name), outlier_row_frac=0.001, device=dev)
+        elems += n * k
+    outs = {name: q.NVFP4Weight(torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev),
+                                torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev),
+                                torch.empty(1, dtype=torch.float32, device=dev)) for name, w in ws_in.items()}
+
+    def timed(run, bytes_per_elem):
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / reps
+        return {"ms": t * 1e3, "GB/s": elems * bytes_per_elem / t / 1e9}
+
+    res["nvfp4_stochastic"] = timed(lambda: [q.nvfp4_quantize(ws_in[nm], out=outs[nm], workspace=ws, check_finite=False,
+                                                              stochastic_seed=7) for nm in synth.PROJ_ORDER], 4.5625)
+    res["mxfp4"] = timed(lambda: [q.mxfp4_quantize(ws_in[nm]) for nm in synth.PROJ_ORDER], 2 + 0.5 + 1 / 32)
+    del ws_in, outs
+    torch.cuda.empty_cache()
+    # format comparison: ||deq(w) - w|| / ||w|| over the 7B layer's weights
+    sq = {"nvfp4": 0.0, "nvfp4_stochastic": 0.0, "mxfp4": 0.0}
+    ref = 0.0
+    for name in synth.PROJ_ORDER:
+        n, k = synth.QWEN25_7B[name]
+        w = synth.weight_bf16(n, k, seed=synth.seed_for(SEED, name), row_lognormal_sigma=0.5, device=dev)
+        wf = w.float()
+        ref += float((wf * wf).sum())
+        for key, seed in (("nvfp4", None), ("nvfp4_stochastic", 11)):
+            wq = q.nvfp4_quantize(w, stochastic_seed=seed)
+            sc = wq.scales.view(torch.float8_e4m3fn).float().repeat_interleave(16, dim=1)
+            d = _dequant_codes(wq.packed) * sc * wq.tensor_scale
+            sq[key] += float(((d - wf) ** 2).sum())
+        mp, ms = q.mxfp4_quantize(w)
+        sc = torch.exp2(ms.float() - 127.0).repeat_interleave(32, dim=1)
+        d = _dequant_codes(mp) * sc
+        sq["mxfp4"] += float(((d - wf) ** 2).sum())
+        del w, wf
+    res["rel_l2_error_7b"] = {key: (v / ref) ** 0.5 for key, v in sq.items()}
+    return res
+
+
 # ---- roofline of the dominant decode kernel --------------------------------
 # stream_kernel runs every decode call with M <= 16, one launch per call.  Its
 # average launch duration comes from a graph of those calls run one after
@@ -777,6 +843,8 @@ def main():
     if not args.no_quantizer:
         log("quantizer leg ...")
         result["quantizer"] = quantizer_leg(dev, reps=3)
+        log("quantizer variants leg ...")
+        result["quantizer_variants"] = quantizer_variants_leg(dev, reps=3)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
