@@ -80,6 +80,8 @@ def _load():
     lib.oracle_e2m1_sr_mag.restype = i32
     lib.oracle_mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P]
     lib.oracle_mxfp4_quantize.restype = i32
+    lib.oracle_w4a16_lora_backward.argtypes = [P, P, i64, i64, i64, P, P, flt, P, P, i32, flt, P, P, P]
+    lib.oracle_w4a16_lora_backward.restype = i32
     lib.oracle_w4a16_lora_gemm_f64.argtypes = lib.oracle_w4a16_lora_gemm.argtypes
     lib.oracle_w4a16_lora_gemm_f64.restype = i32
     lib.oracle_aqn_sigma.argtypes = [i32, i32, dbl, dbl]
@@ -250,6 +252,33 @@ def rmsnorm(x_bits, w_eff, eps: float) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_rmsnorm rejected its arguments")
     return y
+
+
+def w4a16_lora_backward(dy_bits, x_bits, packed, scales, s_t, lora_a_bits=None, lora_b_bits=None,
+                        lora_scale: float = 0.0):
+    """fp64 (dx [M, K], dA [r, K] or None, dB [N, r] or None) of the layer for upstream dy [M, N]."""
+    dy = np.ascontiguousarray(_bits16(dy_bits))
+    x = np.ascontiguousarray(_bits16(x_bits))
+    m, n = dy.shape
+    k = x.shape[1]
+    if x.shape[0] != m or packed.shape != (n, k // 2) or scales.shape != (n, k // 16):
+        raise ValueError("shapes do not match")
+    r = 0
+    a = b = None
+    if lora_a_bits is not None:
+        a = np.ascontiguousarray(_bits16(lora_a_bits))
+        b = np.ascontiguousarray(_bits16(lora_b_bits))
+        r = a.shape[0]
+    dx = np.zeros((m, k))
+    da = np.zeros((r, k)) if r else None
+    db = np.zeros((n, r)) if r else None
+    rc = _load().oracle_w4a16_lora_backward(
+        _ptr(dy), _ptr(x), m, n, k, _ptr(np.ascontiguousarray(packed)), _ptr(np.ascontiguousarray(scales)),
+        float(s_t), None if a is None else _ptr(a), None if b is None else _ptr(b), r, float(lora_scale),
+        _ptr(dx), None if da is None else _ptr(da), None if db is None else _ptr(db))
+    if rc != 0:
+        raise ValueError(f"oracle_w4a16_lora_backward rejected its arguments (rc={rc})")
+    return dx, da, db
 
 
 def rmsnorm_w4a16_lora_gemm(x_bits, norm_weight, eps: float, packed, scales, s_t, lora_a_bits=None,

@@ -476,6 +476,77 @@ int oracle_w4a16_lora_gemm_f64(const double *x, int64_t m, int64_t k, int64_t ld
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward of the layer (the update phase trains the LoRA; W is frozen)     */
+/* ------------------------------------------------------------------------ */
+/* With y = x what^T + lambda t B^T and t = x A^T (forward above), and an
+ * upstream gradient dy [M, N], the chain rule gives (g = dy B, [M, r]):
+ *   dx = dy what + lambda g A          [M, K]
+ *   dA = lambda g^T x                   [r, K]
+ *   dB = lambda dy^T t                  [N, r]
+ * (what is dequantized exactly; W itself gets no gradient, as in the pages'
+ * LoRA training, [BoA-LoRA]).  Any of dx, dA, dB may be NULL.  All fp64.    */
+int oracle_w4a16_lora_backward(const uint16_t *dy, const uint16_t *x, int64_t m, int64_t n, int64_t k,
+                               const uint8_t *packed, const uint8_t *scales, float s_t,
+                               const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
+                               double *dx, double *da, double *db) {
+    if (!dy || !x || !packed || !scales || m <= 0 || n <= 0 || k <= 0 || k % 16 || r < 0) return -1;
+    if (r > 0 && (!lora_a || !lora_b)) return -1;
+    const double lam = (double)lora_scale;
+    double *t = (double *)calloc((size_t)(m * (r > 0 ? r : 1)), sizeof(double));
+    double *g = (double *)calloc((size_t)(m * (r > 0 ? r : 1)), sizeof(double));
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!t || !g || !wrow) { free(t); free(g); free(wrow); return -2; }
+    for (int64_t i = 0; i < m; ++i)
+        for (int j = 0; j < r; ++j) {
+            double at = 0.0, ag = 0.0;
+            for (int64_t kk = 0; kk < k; ++kk)
+                at += oracle_bf16_decode(x[i * k + kk]) * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
+            for (int64_t nn = 0; nn < n; ++nn)
+                ag += oracle_bf16_decode(dy[i * n + nn]) * oracle_bf16_decode(lora_b[nn * r + j]);
+            t[i * r + j] = at;
+            g[i * r + j] = ag;
+        }
+    if (dx) {
+        for (int64_t i = 0; i < m * k; ++i) dx[i] = 0.0;
+        for (int64_t nn = 0; nn < n; ++nn) {
+            for (int64_t kk = 0; kk < k; ++kk) {
+                uint8_t byte = packed[nn * (k / 2) + kk / 2];
+                int code = (kk & 1) ? (byte >> 4) : (byte & 15);
+                wrow[kk] = oracle_e2m1_decode(code) * oracle_e4m3_decode(scales[nn * (k / 16) + kk / 16]) * (double)s_t;
+            }
+            for (int64_t i = 0; i < m; ++i) {
+                const double d = oracle_bf16_decode(dy[i * n + nn]);
+                for (int64_t kk = 0; kk < k; ++kk) dx[i * k + kk] += d * wrow[kk];
+            }
+        }
+        for (int64_t i = 0; i < m; ++i)
+            for (int64_t kk = 0; kk < k; ++kk) {
+                double acc = 0.0;
+                for (int j = 0; j < r; ++j) acc += g[i * r + j] * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
+                dx[i * k + kk] += lam * acc;
+            }
+    }
+    if (da)
+        for (int j = 0; j < r; ++j)
+            for (int64_t kk = 0; kk < k; ++kk) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < m; ++i) acc += g[i * r + j] * oracle_bf16_decode(x[i * k + kk]);
+                da[(int64_t)j * k + kk] = lam * acc;
+            }
+    if (db)
+        for (int64_t nn = 0; nn < n; ++nn)
+            for (int j = 0; j < r; ++j) {
+                double acc = 0.0;
+                for (int64_t i = 0; i < m; ++i) acc += oracle_bf16_decode(dy[i * n + nn]) * t[i * r + j];
+                db[nn * r + j] = lam * acc;
+            }
+    free(t);
+    free(g);
+    free(wrow);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* AQN: schedule, Philox4x64-10 noise, noisy RMSNorm                         */
 /* ------------------------------------------------------------------------ */
 
