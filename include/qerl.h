@@ -257,6 +257,42 @@ qerl_status qerl_rmsnorm_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, in
                                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* ----------------------------------------------------------------------- */
+/* Backward of the layer (update phase: LoRA trained, NVFP4 base frozen)    */
+/* ----------------------------------------------------------------------- */
+/* Bytes of device workspace qerl_w4a16_lora_backward needs. */
+size_t qerl_w4a16_lora_backward_workspace_size(int64_t m, int64_t n, int64_t k, int32_t r);
+
+/*
+ * Gradients of the layer of qerl_w4a16_lora_gemm, y = x what^T +
+ * lora_scale (x A^T) B^T, for an upstream gradient dy: only the low-rank
+ * matrices train, the NVFP4 weight stays frozen (bitsofall page, "LoRA
+ * (Low-Rank Adaptation)"; the rollout kernel's layer, README
+ * "Acknowledgement").  With t = x A^T and g = dy B ([m, r], FP32):
+ *   dx = dy what + lora_scale g A       BF16 [m, k] (RNE of the FP32 sum)
+ *   dA = lora_scale g^T x               FP32 [r, k]
+ *   dB = lora_scale dy^T t              FP32 [n, r]
+ * what is dequantized exactly (e2m1 * e4m3 * s_t) inside the kernel; nothing
+ * is re-laid out.
+ *   dy_bf16      [m, n], row stride ldy; x_bf16 [m, k], row stride ldx (the
+ *                forward input, for dA and dB)
+ *   packed, scales, tensor_scale, lora_a_bf16, lora_b_bf16, r, lora_scale
+ *                as for qerl_w4a16_lora_gemm
+ *   dx_bf16      nullable; [m, k] with row stride lddx
+ *   da_f32, db_f32  nullable; contiguous; ignored when r == 0
+ *   workspace    device memory of at least the size query (t, g and partial
+ *                sums; no state is kept)
+ * Requires m, n >= 1, k >= 16, k % 16 == 0, 0 <= r <= QERL_MAX_LORA_RANK,
+ * ldy >= n, ldx >= k, lddx >= k, finite lora_scale, 16-byte aligned dy, x,
+ * packed and lora_a with ldx % 8 == 0 (ldy any), 2-byte aligned dx.
+ */
+qerl_status qerl_w4a16_lora_backward(const void *dy_bf16, int64_t m, int64_t n, int64_t ldy,
+                                     const void *x_bf16, int64_t k, int64_t ldx,
+                                     const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                     const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                     float lora_scale, void *dx_bf16, int64_t lddx, float *da_f32,
+                                     float *db_f32, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ----------------------------------------------------------------------- */
 /* AQN RMSNorm                                                               */
 /* ----------------------------------------------------------------------- */
 /*

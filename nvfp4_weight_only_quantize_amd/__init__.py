@@ -77,6 +77,11 @@ def lib() -> ctypes.CDLL:
     L.qerl_rmsnorm_w4a16_lora_gemm_multi.restype = ctypes.c_int
     L.qerl_aqn_noisy_weight.argtypes = [P, i64, f32, u64, u64, u32, P, P]
     L.qerl_aqn_noisy_weight.restype = ctypes.c_int
+    L.qerl_w4a16_lora_backward_workspace_size.argtypes = [i64, i64, i64, i32]
+    L.qerl_w4a16_lora_backward_workspace_size.restype = sz
+    L.qerl_w4a16_lora_backward.argtypes = [P, i64, i64, i64, P, i64, i64, P, P, P, P, P, i32, f32, P, i64, P, P,
+                                           P, sz, P]
+    L.qerl_w4a16_lora_backward.restype = ctypes.c_int
     L.qerl_aqn_sigma.argtypes = [i32, i32, f32, f32]
     L.qerl_aqn_sigma.restype = f32
     L.qerl_aqn_rmsnorm.argtypes = [P, i64, i64, i64, P, f32, f32, u64, u64, u32, P, P, i64, P, P]
@@ -334,6 +339,43 @@ def rmsnorm_w4a16_lora_gemm_multi(x: torch.Tensor, norm_weight: torch.Tensor, ep
     _check(lib().qerl_rmsnorm_w4a16_lora_gemm_multi(_ptr(x), m, k, _rows(x, "x"), _ptr(norm_weight), float(eps), arr,
                                                     len(segments), _ptr(workspace), ws_bytes, _stream(stream, dev)))
     return outs
+
+
+def w4a16_lora_backward_workspace_size(m: int, n: int, k: int, r: int) -> int:
+    return int(lib().qerl_w4a16_lora_backward_workspace_size(m, n, k, r))
+
+
+def w4a16_lora_backward(dy: torch.Tensor, x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | None = None,
+                        lora_b: torch.Tensor | None = None, lora_scale: float = 0.0, want_dx: bool = True,
+                        want_lora: bool = True, workspace: torch.Tensor | None = None, stream=None):
+    """Gradients of the layer for upstream dy [M, N]: returns (dx BF16 [M, K] or
+    None, dA FP32 [r, K] or None, dB FP32 [N, r] or None)."""
+    _need(dy, "dy", torch.bfloat16, 2)
+    dev = dy.device
+    _need(x, "x", torch.bfloat16, 2, dev)
+    m, n = dy.shape
+    k = x.shape[1]
+    if x.shape[0] != m or tuple(wq.shape) != (n, k):
+        raise ValueError("dy [M, N], x [M, K] and the weight [N, K] must agree")
+    r = 0
+    if lora_a is not None or lora_b is not None:
+        _need(lora_a, "lora_a", torch.bfloat16, 2, dev)
+        _need(lora_b, "lora_b", torch.bfloat16, 2, dev)
+        r = lora_a.size(0)
+        if tuple(lora_a.shape) != (r, k) or tuple(lora_b.shape) != (n, r):
+            raise ValueError("LoRA must be A [r, K] and B [N, r]")
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if want_dx else None
+    da = torch.empty((r, k), dtype=torch.float32, device=dev) if (want_lora and r) else None
+    db = torch.empty((n, r), dtype=torch.float32, device=dev) if (want_lora and r) else None
+    need = w4a16_lora_backward_workspace_size(m, n, k, r)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().qerl_w4a16_lora_backward(_ptr(dy), m, n, _rows(dy, "dy"), _ptr(x), k, _rows(x, "x"),
+                                          _ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), _ptr(lora_a),
+                                          _ptr(lora_b), r, float(lora_scale), _ptr(dx), k, _ptr(da), _ptr(db),
+                                          _ptr(workspace), ws_bytes, _stream(stream, dev)))
+    return dx, da, db
 
 
 # -------------------------------------------------------------------- AQN --

@@ -311,6 +311,62 @@ qerl_status qerl_aqn_noisy_weight(const float *weight, int64_t h, float sigma, u
     return hip_status(qerl::launch_aqn_noisy_weight(a, static_cast<hipStream_t>(stream)), "aqn_noisy_weight launch");
 }
 
+size_t qerl_w4a16_lora_backward_workspace_size(int64_t m, int64_t n, int64_t k, int32_t r) {
+    if (m < 1 || n < 1 || k < 1 || r < 0) return 0;
+    return qerl::backward_workspace_bytes(m, n, k, r);
+}
+
+qerl_status qerl_w4a16_lora_backward(const void *dy_bf16, int64_t m, int64_t n, int64_t ldy,
+                                     const void *x_bf16, int64_t k, int64_t ldx,
+                                     const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                     const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                     float lora_scale, void *dx_bf16, int64_t lddx, float *da_f32,
+                                     float *db_f32, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    if (!dy_bf16 || !x_bf16 || !packed || !scales || !tensor_scale)
+        return fail(QERL_ERR_NULL, "w4a16_lora_backward: dy, x, packed, scales and tensor_scale are required");
+    if (r < 0 || r > QERL_MAX_LORA_RANK)
+        return fail(QERL_ERR_ARG, "w4a16_lora_backward: LoRA rank %d outside [0, %d]", r, QERL_MAX_LORA_RANK);
+    if (r > 0 && (!lora_a_bf16 || !lora_b_bf16))
+        return fail(QERL_ERR_NULL, "w4a16_lora_backward: lora_a and lora_b are required when r > 0");
+    if (!isfinite(lora_scale)) return fail(QERL_ERR_ARG, "w4a16_lora_backward: lora_scale must be finite");
+    if (m < 1 || n < 1 || k < 16 || k % 16 != 0 || ldy < n || ldx < k || (dx_bf16 && lddx < k) ||
+        m > kMaxElems / k || m > kMaxElems / ldy || m > kMaxElems / ldx || n > kMaxElems / k ||
+        (dx_bf16 && m > kMaxElems / lddx) || m > ((int64_t)1 << 22) * 64)
+        return fail(QERL_ERR_SHAPE, "w4a16_lora_backward: need m, n >= 1, k >= 16, k %% 16 == 0, ldy >= n, "
+                    "ldx >= k, lddx >= k (got m=%lld n=%lld k=%lld)", (long long)m, (long long)n, (long long)k);
+    if (!aligned16(dy_bf16) || !aligned16(x_bf16) || !aligned16(packed) || ldx % 8 != 0 ||
+        ((uintptr_t)dx_bf16 & 1u) || ((uintptr_t)tensor_scale & 3u) || ((uintptr_t)da_f32 & 3u) ||
+        ((uintptr_t)db_f32 & 3u) || (r > 0 && (!aligned16(lora_a_bf16) || ((uintptr_t)lora_b_bf16 & 1u))))
+        return fail(QERL_ERR_ALIGN, "w4a16_lora_backward: dy, x, packed, lora_a must be 16-byte aligned, "
+                    "ldx %% 8 == 0");
+    const size_t need = qerl::backward_workspace_bytes(m, n, k, r);
+    if (!workspace || workspace_bytes < need)
+        return fail(QERL_ERR_WORKSPACE, "w4a16_lora_backward: workspace of %zu bytes needed", need);
+    if (!aligned16(workspace)) return fail(QERL_ERR_ALIGN, "w4a16_lora_backward: workspace must be 16-byte aligned");
+    qerl::BackwardArgs b{};
+    b.dy = static_cast<const uint16_t *>(dy_bf16);
+    b.x = static_cast<const uint16_t *>(x_bf16);
+    b.m = m;
+    b.n = n;
+    b.k = k;
+    b.ldy = ldy;
+    b.ldx = ldx;
+    b.packed = packed;
+    b.scales = scales;
+    b.tensor_scale = tensor_scale;
+    b.lora_a = static_cast<const uint16_t *>(lora_a_bf16);
+    b.lora_b = static_cast<const uint16_t *>(lora_b_bf16);
+    b.r = r;
+    b.lora_scale = lora_scale;
+    b.dx = static_cast<uint16_t *>(dx_bf16);
+    b.lddx = lddx;
+    b.da = r > 0 ? da_f32 : nullptr;
+    b.db = r > 0 ? db_f32 : nullptr;
+    b.workspace = workspace;
+    return hip_status(qerl::launch_backward(b, static_cast<hipStream_t>(stream)), "w4a16_lora_backward launch");
+}
+
 float qerl_aqn_sigma(int32_t stage, int32_t num_stages, float sigma_start, float sigma_end) {
     if (!(sigma_start > 0.0f) || !(sigma_end > 0.0f) || !isfinite(sigma_start) || !isfinite(sigma_end))
         return NAN;

@@ -1,0 +1,319 @@
+// backward.hip -- backward of the W4A16 + LoRA layer for gfx950.
+//
+// The update phase trains the low-rank matrices with the NVFP4 base frozen
+// ("QeRL: NVFP4-Quantized Reinforcement Learning -- Redefining Efficiency in
+// AI Training and Inference", "LoRA (Low-Rank Adaptation)").  For
+//   y = x what^T + lambda (x A^T) B^T,   t = x A^T,   g = dy B   ([M, r])
+// the gradients are
+//   dx = dy what + lambda g A   [M, K]  BF16   dx_kernel
+//   dA = lambda g^T x           [r, K]  FP32   skinny products
+//   dB = lambda dy^T t          [N, r]  FP32   skinny products
+//
+// dx contracts over N, along which the packed weight is strided: a workgroup
+// owns a 64 x 128 tile of dx and walks N in steps of 32 rows, decoding each
+// 32 x 128 weight block (exact BF16 e2m1 * e4m3) into LDS transposed, so that
+// every MFMA B fragment (8 consecutive n of one column) is one 16-byte LDS
+// read.  The LoRA term continues the same accumulation: the ranks act as 2r
+// more rows, A as their weights and g * lambda / s_t split into BF16 hi + lo
+// as their activations; s_t is applied once at the end.
+//
+// t, g, dA and dB are products with one side of width r <= 128: each is
+// computed in FP32 on the VALU over q-chunks of 512 (a grid over output rows
+// and chunks), and the chunks' partial sums are added in chunk order.
+#include "device_common.h"
+#include "qerl_internal.h"
+
+namespace qerl {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---- skinny products ------------------------------------------------------
+// part[c][p][j] = sum over q in chunk c of L(p, q) R(q, j), j < r.
+// L(p, q) = L[p * lsp + q * lsq], R(q, j) = R[q * rsq + j * rsj].
+constexpr int kSkP = 16;      // output rows per workgroup
+constexpr int kSkQ = 64;      // q per LDS step
+constexpr int kSkChunk = 512; // q per workgroup
+struct Skinny {
+    const void *L;
+    int64_t lsp, lsq;
+    const void *R;
+    int64_t rsq, rsj;
+    int64_t P, Q;
+    int r;
+    float *part;  // [chunks][P][r]
+};
+
+template <typename T>
+__device__ __forceinline__ float ld_f32(const void *base, int64_t i) {
+    if constexpr (sizeof(T) == 2) {
+        return bf16lo_to_f32(static_cast<const uint16_t *>(base)[i]);
+    } else {
+        return static_cast<const float *>(base)[i];
+    }
+}
+
+template <typename LT, typename RT>
+__global__ __launch_bounds__(kThreads) void skinny_kernel(Skinny s) {
+    __shared__ float ls[kSkQ][kSkP + 1];
+    __shared__ float rs[kSkQ][kMaxRankBwd + 1];
+    const int tid = threadIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.x * kSkP;
+    const int64_t c = blockIdx.y;
+    const int64_t q_begin = c * kSkChunk, q_end = q_begin + kSkChunk < s.Q ? q_begin + kSkChunk : s.Q;
+    // thread -> output row p0 + (tid % 16), ranks j = tid / 16 + 16 u
+    const int pl = tid % kSkP, jl = tid / kSkP;
+    constexpr int kJ = kMaxRankBwd / (kThreads / kSkP);  // ranks per thread (8)
+    float acc[kJ];
+#pragma unroll
+    for (int u = 0; u < kJ; ++u) acc[u] = 0.0f;
+    for (int64_t q0 = q_begin; q0 < q_end; q0 += kSkQ) {
+        __syncthreads();  // the previous step's tiles have been read
+        for (int e = tid; e < kSkQ * kSkP; e += kThreads) {
+            // consecutive threads along whichever L index is contiguous
+            const int qq = s.lsq == 1 ? e % kSkQ : e / kSkP;
+            const int pp = s.lsq == 1 ? e / kSkQ : e % kSkP;
+            const int64_t p = p0 + pp, q = q0 + qq;
+            ls[qq][pp] = (p < s.P && q < q_end) ? ld_f32<LT>(s.L, p * s.lsp + q * s.lsq) : 0.0f;
+        }
+        for (int e = tid; e < kSkQ * s.r; e += kThreads) {
+            const int qq = s.rsj == 1 ? e / s.r : e % kSkQ;
+            const int jj = s.rsj == 1 ? e % s.r : e / kSkQ;
+            const int64_t q = q0 + qq;
+            rs[qq][jj] = q < q_end ? ld_f32<RT>(s.R, q * s.rsq + jj * s.rsj) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int qq = 0; qq < kSkQ; ++qq) {
+            const float l = ls[qq][pl];
+#pragma unroll
+            for (int u = 0; u < kJ; ++u) acc[u] = __builtin_fmaf(l, rs[qq][jl + 16 * u], acc[u]);
+        }
+    }
+    const int64_t p = p0 + pl;
+    if (p < s.P)
+#pragma unroll
+        for (int u = 0; u < kJ; ++u) {
+            const int j = jl + 16 * u;
+            if (j < s.r) s.part[(c * s.P + p) * s.r + j] = acc[u];
+        }
+}
+
+// out[p * osp + j * osj] = scale * sum over chunks (in order) of part[c][p][j]
+__global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float *part, int64_t chunks, int64_t P, int r,
+                                                                 float scale, float *out, int64_t osp, int64_t osj) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= P * r) return;
+    const int64_t p = i / r, j = i - p * r;
+    float acc = 0.0f;
+    for (int64_t c = 0; c < chunks; ++c) acc += part[c * P * r + i];
+    out[p * osp + j * osj] = scale * acc;
+}
+
+// ---- dx = dy what + lambda g A ---------------------------------------------
+constexpr int kBM = 64, kBK = 128, kBN = 32;
+constexpr int kTPitch = kBN + 8;  // BF16 elements per transposed LDS row (16-byte aligned rows)
+
+struct DxArgs {
+    const uint16_t *dy;
+    int64_t m, n, ldy;
+    const uint8_t *packed;
+    const uint8_t *scales;
+    const float *tensor_scale;
+    int64_t k;
+    const uint16_t *lora_a;
+    int r;
+    float lora_scale;
+    const float *g;  // [m, r] FP32
+    uint16_t *dx;
+    int64_t lddx;
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8_b(const uint4 &u) {
+    bf16x8_t v;
+    __builtin_memcpy(&v, &u, 16);
+    return v;
+}
+
+// 8 BF16 of dy row `row`, columns c0 .. c0 + 7 (zeros past m or n)
+__device__ __forceinline__ uint4 load_dy8(const DxArgs &a, int64_t row, int64_t c0) {
+    if (row >= a.m || c0 >= a.n) return make_uint4(0, 0, 0, 0);
+    const uint16_t *p = a.dy + row * a.ldy + c0;
+    if (c0 + 8 <= a.n && (a.ldy & 7) == 0) return *reinterpret_cast<const uint4 *>(p);
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = c0 + i < a.n ? p[i] : (uint16_t)0;
+    uint4 v;
+    __builtin_memcpy(&v, e, 16);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t tt[kBK * kTPitch];  // tile^T: [kk][n]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t i0 = (int64_t)blockIdx.y * kBM, kk0 = (int64_t)blockIdx.x * kBK;
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // the decode share of a thread: weight row nl (of the 32), 16 columns at 16 seg
+    const int nl = tid >> 3, seg = tid & 7;
+    const int64_t kcol = kk0 + 16 * seg;
+    auto mfma_step = [&](const uint4 (&af)[4]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(tt + (32 * wave + 16 * j + lr) * kTPitch + 8 * lq);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_b(af[i]), b, acc[i][j], 0, 0, 0);
+        }
+    };
+    for (int64_t n0 = 0; n0 < a.n; n0 += kBN) {
+        // A fragments: dy rows i0 + 16 i + lr, columns n0 + 8 lq .. + 8
+        uint4 af[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = load_dy8(a, i0 + 16 * i + lr, n0 + 8 * lq);
+        // this thread's 16 weights, decoded exactly (e2m1 * e4m3; s_t at the end)
+        const int64_t nrow = n0 + nl;
+        uint32_t w16[8];
+        if (nrow < a.n && kcol < a.k) {
+            const uint2 q = *reinterpret_cast<const uint2 *>(a.packed + nrow * (a.k >> 1) + (kcol >> 1));
+            const float sc = QERL_E4M3_F32(a.scales[nrow * (a.k >> 4) + (kcol >> 4)], 0);
+            const uint32_t qq[2] = {q.x, q.y};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x2_t f0 = QERL_FP4_PAIR_F32(qq[h], 0), f1 = QERL_FP4_PAIR_F32(qq[h], 1);
+                const f32x2_t f2 = QERL_FP4_PAIR_F32(qq[h], 2), f3 = QERL_FP4_PAIR_F32(qq[h], 3);
+                w16[4 * h] = pack_bf16x2(f0.x * sc, f0.y * sc);
+                w16[4 * h + 1] = pack_bf16x2(f1.x * sc, f1.y * sc);
+                w16[4 * h + 2] = pack_bf16x2(f2.x * sc, f2.y * sc);
+                w16[4 * h + 3] = pack_bf16x2(f3.x * sc, f3.y * sc);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w16[e] = 0;
+        }
+        __syncthreads();  // the previous block's tile has been read
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tt[(16 * seg + 2 * e) * kTPitch + nl] = (uint16_t)(w16[e] & 0xFFFFu);
+            tt[(16 * seg + 2 * e + 1) * kTPitch + nl] = (uint16_t)(w16[e] >> 16);
+        }
+        __syncthreads();
+        mfma_step(af);
+    }
+    // LoRA: ranks as 2r more rows (hi, lo) with weights A and activations
+    // g * lambda / s_t
+    const float st = *a.tensor_scale;
+    const float gs = a.lora_scale / st;
+    for (int64_t j0 = 0; j0 < a.r; j0 += kBN) {
+        // A rows j0 + nl, 16 columns at kcol (BF16 as they are)
+        uint4 av[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+        if (j0 + nl < a.r && kcol < a.k) {
+            const uint4 *pa = reinterpret_cast<const uint4 *>(a.lora_a + (j0 + nl) * a.k + kcol);
+            av[0] = pa[0];
+            av[1] = pa[1];
+        }
+        uint4 ah[4], al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row = i0 + 16 * i + lr;
+            float gv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t j = j0 + 8 * lq + e;
+                gv[e] = (row < a.m && j < a.r) ? a.g[row * a.r + j] * gs : 0.0f;
+            }
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hw[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+                lw[e] = pack_bf16x2(gv[2 * e] - bf16lo_to_f32(hw[e]), gv[2 * e + 1] - bf16hi_to_f32(hw[e]));
+            }
+            ah[i] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            al[i] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        __syncthreads();
+        const uint32_t aw[8] = {av[0].x, av[0].y, av[0].z, av[0].w, av[1].x, av[1].y, av[1].z, av[1].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            tt[(16 * seg + 2 * e) * kTPitch + nl] = (uint16_t)(aw[e] & 0xFFFFu);
+            tt[(16 * seg + 2 * e + 1) * kTPitch + nl] = (uint16_t)(aw[e] >> 16);
+        }
+        __syncthreads();
+        mfma_step(ah);
+        mfma_step(al);
+    }
+    // dx[i][kk] = bf16(s_t * acc): lane holds rows 4 lq + v of column lr
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = i0 + 16 * i + 4 * lq + v, col = kk0 + 32 * wave + 16 * j + lr;
+                if (row < a.m && col < a.k) a.dx[row * a.lddx + col] = f32_to_bf16_bits(st * acc[i][j][v]);
+            }
+}
+
+int64_t chunks_of(int64_t q) { return (q + kSkChunk - 1) / kSkChunk; }
+
+template <typename LT, typename RT>
+hipError_t skinny(const Skinny &s, float scale, float *out, int64_t osp, int64_t osj, hipStream_t stream) {
+    const dim3 grid((unsigned)((s.P + kSkP - 1) / kSkP), (unsigned)chunks_of(s.Q));
+    hipLaunchKernelGGL((skinny_kernel<LT, RT>), grid, dim3(kThreads), 0, stream, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = s.P * s.r;
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       stream, s.part, chunks_of(s.Q), s.P, s.r, scale, out, osp, osj);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+    // t and g [m, r], then the largest skinny partials (one product at a time)
+    int64_t part = 0;
+    const int64_t cand[4] = {chunks_of(k) * m * r, chunks_of(n) * m * r, chunks_of(m) * k * r, chunks_of(m) * n * r};
+    for (int64_t c : cand) part = c > part ? c : part;
+    return (size_t)(2 * m * r + part) * 4 + 256;
+}
+
+hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
+    float *t = static_cast<float *>(b.workspace);
+    float *g = t + b.m * b.r;
+    float *part = g + b.m * b.r;
+    hipError_t e = hipSuccess;
+    if (b.r > 0) {
+        // t = x A^T: L(p=i, q=kk) = x[i][kk], R(q=kk, j) = A[j][kk]
+        e = skinny<uint16_t, uint16_t>(Skinny{b.x, b.ldx, 1, b.lora_a, 1, b.k, b.m, b.k, b.r, part}, 1.0f, t, b.r, 1,
+                                       stream);
+        if (e != hipSuccess) return e;
+        // g = dy B: L(p=i, q=n) = dy[i][n], R(q=n, j) = B[n][j]
+        e = skinny<uint16_t, uint16_t>(Skinny{b.dy, b.ldy, 1, b.lora_b, b.r, 1, b.m, b.n, b.r, part}, 1.0f, g, b.r, 1,
+                                       stream);
+        if (e != hipSuccess) return e;
+        if (b.da) {  // dA[j][kk] = lambda sum_i g[i][j] x[i][kk]: L(p=kk, q=i) = x[i][kk], R(q=i, j) = g[i][j]
+            e = skinny<uint16_t, float>(Skinny{b.x, 1, b.ldx, g, b.r, 1, b.k, b.m, b.r, part}, b.lora_scale, b.da, 1,
+                                        b.k, stream);
+            if (e != hipSuccess) return e;
+        }
+        if (b.db) {  // dB[n][j] = lambda sum_i dy[i][n] t[i][j]
+            e = skinny<uint16_t, float>(Skinny{b.dy, 1, b.ldy, t, b.r, 1, b.n, b.m, b.r, part}, b.lora_scale, b.db,
+                                        b.r, 1, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    if (b.dx) {
+        const DxArgs d{b.dy, b.m, b.n, b.ldy, b.packed, b.scales, b.tensor_scale, b.k, b.lora_a, b.r, b.lora_scale,
+                       g, b.dx, b.lddx};
+        const dim3 grid((unsigned)((b.k + kBK - 1) / kBK), (unsigned)((b.m + kBM - 1) / kBM));
+        hipLaunchKernelGGL(dx_kernel, grid, dim3(kThreads), 0, stream, d);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace qerl

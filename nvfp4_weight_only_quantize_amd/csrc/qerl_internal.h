@@ -70,6 +70,28 @@ constexpr int64_t kNormFuseMaxM = 16;
 size_t norm_gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
 hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
 
+// ---- backward of the layer (LoRA trained, W frozen) ----
+constexpr int kMaxRankBwd = 128;  // QERL_MAX_LORA_RANK
+struct BackwardArgs {
+    const uint16_t *dy;  // [m, n], row stride ldy
+    const uint16_t *x;   // [m, k], row stride ldx
+    int64_t m, n, k, ldy, ldx;
+    const uint8_t *packed;
+    const uint8_t *scales;
+    const float *tensor_scale;
+    const uint16_t *lora_a;  // [r, k]
+    const uint16_t *lora_b;  // [n, r]
+    int r;
+    float lora_scale;
+    uint16_t *dx;  // [m, k], row stride lddx (nullable)
+    int64_t lddx;
+    float *da;  // [r, k] (nullable)
+    float *db;  // [n, r] (nullable)
+    void *workspace;
+};
+size_t backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream);
+
 // ---- AQN RMSNorm ----
 struct AqnArgs {
     const uint16_t *x;

@@ -233,3 +233,25 @@ def test_quantize_stochastic_argument_errors(kw, status):
                                                   P(a["scales"]), P(a["ts"]), None, a["flags"], a["seed"],
                                                   P(a["ws"]), a["wsb"], None) == status
     assert b"nvfp4_quantize_stochastic" in q.lib().qerl_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dy=None), 1), (dict(x=None), 1), (dict(A=None), 1), (dict(r=200), 4), (dict(lam=float("inf")), 4),
+    (dict(m=0), 2), (dict(k=40, ldx=40, lddx=40), 2), (dict(ldy=16), 2), (dict(lddx=8), 2),
+    (dict(dy=FAKE + 2), 3), (dict(x=FAKE + 4), 3), (dict(ldx=68), 3), (dict(dx=FAKE + 1), 3),
+    (dict(ws=None), 5), (dict(wsb=16), 5), (dict(ws=FAKE + 8), 3),
+])
+def test_backward_argument_errors(kw, status):
+    a = dict(dy=FAKE, m=4, n=32, ldy=32, x=FAKE, k=64, ldx=64, packed=FAKE, scales=FAKE, ts=FAKE, A=FAKE, B=FAKE,
+             r=8, lam=2.0, dx=FAKE, lddx=64, da=FAKE, db=FAKE, ws=FAKE, wsb=1 << 24)
+    a.update(kw)
+    assert q.lib().qerl_w4a16_lora_backward(P(a["dy"]), a["m"], a["n"], a["ldy"], P(a["x"]), a["k"], a["ldx"],
+                                            P(a["packed"]), P(a["scales"]), P(a["ts"]), P(a["A"]), P(a["B"]),
+                                            a["r"], a["lam"], P(a["dx"]), a["lddx"], P(a["da"]), P(a["db"]),
+                                            P(a["ws"]), a["wsb"], None) == status
+    assert q.lib().qerl_last_error()
+
+
+def test_backward_workspace_query():
+    assert q.w4a16_lora_backward_workspace_size(2048, 5120, 5120, 32) >= 2 * 2048 * 32 * 4
+    assert q.w4a16_lora_backward_workspace_size(0, 5120, 5120, 32) == 0
