@@ -489,6 +489,47 @@ def quantizer_leg(dev, reps):
             "whole_model_ms_est": t * 1e3 * 64}
 
 
+def backward_leg(dev, reps, m=2048):
+    """The update phase's backward of the 7B layer's seven projections at M
+    tokens (LoRA r = 32 trained, NVFP4 base frozen): dx, dA and dB per
+    projection, timed in one graph.  FLOPs per projection: 2 M N K (dy what)
+    + 2 M r (N + K) (t and g) + 2 M r K (g A) + 2 M r (K + N) (dA, dB)."""
+    layer = make_layer(synth.QWEN25_7B, SEED, dev)
+    xs = {name: synth.activation_bf16(m, k, synth.seed_for(SEED, "bx", name), 0.005, device=dev)
+          for name, (n, k) in synth.QWEN25_7B.items()}
+    dys = {name: synth.activation_bf16(m, n, synth.seed_for(SEED, "bdy", name), 0.0, device=dev)
+           for name, (n, k) in synth.QWEN25_7B.items()}
+    ws = torch.empty(max(q.w4a16_lora_backward_workspace_size(m, n, k, RANK) for n, k in synth.QWEN25_7B.values()),
+                     dtype=torch.uint8, device=dev)
+    flops = 0
+    for name, (n, k) in synth.QWEN25_7B.items():
+        flops += 2 * m * n * k + 2 * m * RANK * (n + k) + 2 * m * RANK * k + 2 * m * RANK * (k + n)
+
+    def run():
+        for name in synth.PROJ_ORDER:
+            p = layer[name]
+            q.w4a16_lora_backward(dys[name], xs[name], p.wq, p.a, p.b, ALPHA / RANK, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del g
+    tf = flops / t / 1e12
+    return {"workload": f"backward (dx, dA, dB) of the Qwen2.5-7B-shaped layer's 7 projections, M = {m} tokens, "
+                        f"LoRA r = {RANK}", "ms": t * 1e3, "tflops": tf, "frac": tf / BF16_MFMA_PEAK_TFLOPS}
+
+
 E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 
@@ -760,6 +801,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calls-only", action="store_true",
                     help="only the per-call roofline leg (for rocprofv3 runs); prints its JSON")
     ap.add_argument("--copy-probe", action="store_true",
@@ -845,6 +887,9 @@ def main():
         result["quantizer"] = quantizer_leg(dev, reps=3)
         log("quantizer variants leg ...")
         result["quantizer_variants"] = quantizer_variants_leg(dev, reps=3)
+    if not args.no_backward:
+        log("backward leg ...")
+        result["backward"] = backward_leg(dev, reps=3)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
