@@ -18,8 +18,9 @@
 // as their activations; s_t is applied once at the end.
 //
 // t, g, dA and dB are products with one side of width r <= 128: each is
-// computed in FP32 on the VALU over q-chunks of 512 (a grid over output rows
-// and chunks), and the chunks' partial sums are added in chunk order.
+// computed in FP32 on the VALU, one output row per thread, over q-chunks (a
+// grid over output rows and chunks), and the chunks' partial sums are added
+// in chunk order.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -31,9 +32,14 @@ constexpr int kThreads = 256;
 // ---- skinny products ------------------------------------------------------
 // part[c][p][j] = sum over q in chunk c of L(p, q) R(q, j), j < r.
 // L(p, q) = L[p * lsp + q * lsq], R(q, j) = R[q * rsq + j * rsj].
-constexpr int kSkP = 16;      // output rows per workgroup
-constexpr int kSkQ = 64;      // q per LDS step
-constexpr int kSkChunk = 512; // q per workgroup
+// One thread per output row p and 32 ranks at a time (one pass per group of
+// 32): the chunk's R values for the group sit in LDS (every thread reads the
+// same R[q][..], a broadcast) and the thread streams its L(p, q) -- 8 q per
+// 16-byte load when L is contiguous along q, else one load per q coalesced
+// across the threads' consecutive p.
+constexpr int kSkP = 256;     // output rows per workgroup (one per thread)
+constexpr int kSkJ = 32;      // ranks per pass
+constexpr int kSkMaxChunk = 512;
 struct Skinny {
     const void *L;
     int64_t lsp, lsq;
@@ -41,7 +47,8 @@ struct Skinny {
     int64_t rsq, rsj;
     int64_t P, Q;
     int r;
-    float *part;  // [chunks][P][r]
+    int64_t chunk;  // q per workgroup (a multiple of 8, <= kSkMaxChunk)
+    float *part;    // [chunks][P][r]
 };
 
 template <typename T>
@@ -55,48 +62,56 @@ __device__ __forceinline__ float ld_f32(const void *base, int64_t i) {
 
 template <typename LT, typename RT>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(Skinny s) {
-    __shared__ float ls[kSkQ][kSkP + 1];
-    __shared__ float rs[kSkQ][kMaxRankBwd + 1];
+    __shared__ __attribute__((aligned(16))) float rs[kSkMaxChunk][kSkJ];
     const int tid = threadIdx.x;
-    const int64_t p0 = (int64_t)blockIdx.x * kSkP;
+    const int64_t p = (int64_t)blockIdx.x * kSkP + tid;
     const int64_t c = blockIdx.y;
-    const int64_t q_begin = c * kSkChunk, q_end = q_begin + kSkChunk < s.Q ? q_begin + kSkChunk : s.Q;
-    // thread -> output row p0 + (tid % 16), ranks j = tid / 16 + 16 u
-    const int pl = tid % kSkP, jl = tid / kSkP;
-    constexpr int kJ = kMaxRankBwd / (kThreads / kSkP);  // ranks per thread (8)
-    float acc[kJ];
-#pragma unroll
-    for (int u = 0; u < kJ; ++u) acc[u] = 0.0f;
-    for (int64_t q0 = q_begin; q0 < q_end; q0 += kSkQ) {
-        __syncthreads();  // the previous step's tiles have been read
-        for (int e = tid; e < kSkQ * kSkP; e += kThreads) {
-            // consecutive threads along whichever L index is contiguous
-            const int qq = s.lsq == 1 ? e % kSkQ : e / kSkP;
-            const int pp = s.lsq == 1 ? e / kSkQ : e % kSkP;
-            const int64_t p = p0 + pp, q = q0 + qq;
-            ls[qq][pp] = (p < s.P && q < q_end) ? ld_f32<LT>(s.L, p * s.lsp + q * s.lsq) : 0.0f;
-        }
-        for (int e = tid; e < kSkQ * s.r; e += kThreads) {
-            const int qq = s.rsj == 1 ? e / s.r : e % kSkQ;
-            const int jj = s.rsj == 1 ? e % s.r : e / kSkQ;
-            const int64_t q = q0 + qq;
-            rs[qq][jj] = q < q_end ? ld_f32<RT>(s.R, q * s.rsq + jj * s.rsj) : 0.0f;
+    const int64_t q_begin = c * s.chunk, q_end = q_begin + s.chunk < s.Q ? q_begin + s.chunk : s.Q;
+    const int nq = (int)(q_end - q_begin);
+    const bool vec = sizeof(LT) == 2 && s.lsq == 1 && (s.lsp & 7) == 0;  // 8 BF16 of a row per load
+    for (int j0 = 0; j0 < s.r; j0 += kSkJ) {
+        const int nj = s.r - j0 < kSkJ ? s.r - j0 : kSkJ;
+        __syncthreads();  // the previous pass's R values have been read
+        for (int e = tid; e < nq * kSkJ; e += kThreads) {
+            const int qq = s.rsj == 1 ? e / kSkJ : e % nq;
+            const int jj = s.rsj == 1 ? e % kSkJ : e / nq;
+            rs[qq][jj] = jj < nj ? ld_f32<RT>(s.R, (q_begin + qq) * s.rsq + (j0 + jj) * s.rsj) : 0.0f;
         }
         __syncthreads();
+        if (p >= s.P) continue;
+        float acc[kSkJ];
+#pragma unroll
+        for (int u = 0; u < kSkJ; ++u) acc[u] = 0.0f;
+        auto fma_row = [&](int qq, float l) {
+            const f32x4_t *rq = reinterpret_cast<const f32x4_t *>(rs[qq]);
+#pragma unroll
+            for (int u = 0; u < kSkJ / 4; ++u) {
+                const f32x4_t rv = rq[u];
+                acc[4 * u] = __builtin_fmaf(l, rv[0], acc[4 * u]);
+                acc[4 * u + 1] = __builtin_fmaf(l, rv[1], acc[4 * u + 1]);
+                acc[4 * u + 2] = __builtin_fmaf(l, rv[2], acc[4 * u + 2]);
+                acc[4 * u + 3] = __builtin_fmaf(l, rv[3], acc[4 * u + 3]);
+            }
+        };
+        if (vec) {
+            const uint16_t *lrow = static_cast<const uint16_t *>(s.L) + p * s.lsp + q_begin;
+            int qq = 0;
+            for (; qq + 8 <= nq; qq += 8) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(lrow + qq);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    fma_row(qq + 2 * h, bf16lo_to_f32(w4[h]));
+                    fma_row(qq + 2 * h + 1, bf16hi_to_f32(w4[h]));
+                }
+            }
+            for (; qq < nq; ++qq) fma_row(qq, bf16lo_to_f32(lrow[qq]));
+        } else {
 #pragma unroll 4
-        for (int qq = 0; qq < kSkQ; ++qq) {
-            const float l = ls[qq][pl];
-#pragma unroll
-            for (int u = 0; u < kJ; ++u) acc[u] = __builtin_fmaf(l, rs[qq][jl + 16 * u], acc[u]);
+            for (int qq = 0; qq < nq; ++qq) fma_row(qq, ld_f32<LT>(s.L, p * s.lsp + (q_begin + qq) * s.lsq));
         }
+        for (int u = 0; u < nj; ++u) s.part[(c * s.P + p) * s.r + j0 + u] = acc[u];
     }
-    const int64_t p = p0 + pl;
-    if (p < s.P)
-#pragma unroll
-        for (int u = 0; u < kJ; ++u) {
-            const int j = jl + 16 * u;
-            if (j < s.r) s.part[(c * s.P + p) * s.r + j] = acc[u];
-        }
 }
 
 // out[p * osp + j * osj] = scale * sum over chunks (in order) of part[c][p][j]
@@ -257,17 +272,30 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
             }
 }
 
-int64_t chunks_of(int64_t q) { return (q + kSkChunk - 1) / kSkChunk; }
+// q per workgroup: enough chunks that the grid covers the GPU about twice
+// (at least 64 q each, a multiple of 8, at most kSkMaxChunk)
+int64_t chunk_of(int64_t P, int64_t Q) {
+    const int64_t pblocks = (P + kSkP - 1) / kSkP;
+    int64_t want = (512 + pblocks - 1) / pblocks;  // chunks wanted
+    int64_t ch = (Q + want - 1) / want;
+    ch = (ch + 7) / 8 * 8;
+    if (ch < 64) ch = 64;
+    if (ch > kSkMaxChunk) ch = kSkMaxChunk;
+    return ch;
+}
+int64_t chunks_of(int64_t P, int64_t Q) { return (Q + chunk_of(P, Q) - 1) / chunk_of(P, Q); }
 
 template <typename LT, typename RT>
-hipError_t skinny(const Skinny &s, float scale, float *out, int64_t osp, int64_t osj, hipStream_t stream) {
-    const dim3 grid((unsigned)((s.P + kSkP - 1) / kSkP), (unsigned)chunks_of(s.Q));
+hipError_t skinny(Skinny s, float scale, float *out, int64_t osp, int64_t osj, hipStream_t stream) {
+    s.chunk = chunk_of(s.P, s.Q);
+    const int64_t chunks = chunks_of(s.P, s.Q);
+    const dim3 grid((unsigned)((s.P + kSkP - 1) / kSkP), (unsigned)chunks);
     hipLaunchKernelGGL((skinny_kernel<LT, RT>), grid, dim3(kThreads), 0, stream, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = s.P * s.r;
     hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, s.part, chunks_of(s.Q), s.P, s.r, scale, out, osp, osj);
+                       stream, s.part, chunks, s.P, s.r, scale, out, osp, osj);
     return hipGetLastError();
 }
 
@@ -276,7 +304,8 @@ hipError_t skinny(const Skinny &s, float scale, float *out, int64_t osp, int64_t
 size_t backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
     // t and g [m, r], then the largest skinny partials (one product at a time)
     int64_t part = 0;
-    const int64_t cand[4] = {chunks_of(k) * m * r, chunks_of(n) * m * r, chunks_of(m) * k * r, chunks_of(m) * n * r};
+    const int64_t cand[4] = {chunks_of(m, k) * m * r, chunks_of(m, n) * m * r, chunks_of(k, m) * k * r,
+                             chunks_of(n, m) * n * r};
     for (int64_t c : cand) part = c > part ? c : part;
     return (size_t)(2 * m * r + part) * 4 + 256;
 }
@@ -288,20 +317,20 @@ hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (b.r > 0) {
         // t = x A^T: L(p=i, q=kk) = x[i][kk], R(q=kk, j) = A[j][kk]
-        e = skinny<uint16_t, uint16_t>(Skinny{b.x, b.ldx, 1, b.lora_a, 1, b.k, b.m, b.k, b.r, part}, 1.0f, t, b.r, 1,
+        e = skinny<uint16_t, uint16_t>(Skinny{b.x, b.ldx, 1, b.lora_a, 1, b.k, b.m, b.k, b.r, 0, part}, 1.0f, t, b.r, 1,
                                        stream);
         if (e != hipSuccess) return e;
         // g = dy B: L(p=i, q=n) = dy[i][n], R(q=n, j) = B[n][j]
-        e = skinny<uint16_t, uint16_t>(Skinny{b.dy, b.ldy, 1, b.lora_b, b.r, 1, b.m, b.n, b.r, part}, 1.0f, g, b.r, 1,
+        e = skinny<uint16_t, uint16_t>(Skinny{b.dy, b.ldy, 1, b.lora_b, b.r, 1, b.m, b.n, b.r, 0, part}, 1.0f, g, b.r, 1,
                                        stream);
         if (e != hipSuccess) return e;
         if (b.da) {  // dA[j][kk] = lambda sum_i g[i][j] x[i][kk]: L(p=kk, q=i) = x[i][kk], R(q=i, j) = g[i][j]
-            e = skinny<uint16_t, float>(Skinny{b.x, 1, b.ldx, g, b.r, 1, b.k, b.m, b.r, part}, b.lora_scale, b.da, 1,
+            e = skinny<uint16_t, float>(Skinny{b.x, 1, b.ldx, g, b.r, 1, b.k, b.m, b.r, 0, part}, b.lora_scale, b.da, 1,
                                         b.k, stream);
             if (e != hipSuccess) return e;
         }
         if (b.db) {  // dB[n][j] = lambda sum_i dy[i][n] t[i][j]
-            e = skinny<uint16_t, float>(Skinny{b.dy, 1, b.ldy, t, b.r, 1, b.n, b.m, b.r, part}, b.lora_scale, b.db,
+            e = skinny<uint16_t, float>(Skinny{b.dy, 1, b.ldy, t, b.r, 1, b.n, b.m, b.r, 0, part}, b.lora_scale, b.db,
                                         b.r, 1, stream);
             if (e != hipSuccess) return e;
         }
