@@ -10,10 +10,11 @@
 //   dB = lambda dy^T t          [N, r]  FP32   skinny products
 //
 // dx contracts over N, along which the packed weight is strided: a workgroup
-// owns a 64 x 128 tile of dx and walks N in steps of 32 rows, decoding each
-// 32 x 128 weight block (exact BF16 e2m1 * e4m3) into LDS transposed, so that
+// owns a 64 x 128 tile of dx and walks N in steps of 64 rows, decoding each
+// 64 x 128 weight block (exact BF16 e2m1 * e4m3) into LDS transposed, so that
 // every MFMA B fragment (8 consecutive n of one column) is one 16-byte LDS
-// read.  The LoRA term continues the same accumulation: the ranks act as 2r
+// read; the tile is double-buffered (the next block is decoded while this
+// one multiplies), one barrier per step.  The LoRA term continues the same accumulation: the ranks act as 2r
 // more rows, A as their weights and g * lambda / s_t split into BF16 hi + lo
 // as their activations; s_t is applied once at the end.
 //
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float *pa
 }
 
 // ---- dx = dy what + lambda g A ---------------------------------------------
-constexpr int kBM = 64, kBK = 128, kBN = 32;
+constexpr int kBM = 64, kBK = 128, kBN = 64;  // dx tile (rows x columns), N per step
 constexpr int kTPitch = kBN + 8;  // BF16 elements per transposed LDS row (16-byte aligned rows)
 
 struct DxArgs {
@@ -163,8 +164,50 @@ __device__ __forceinline__ uint4 load_dy8(const DxArgs &a, int64_t row, int64_t 
     return v;
 }
 
+// The 32 weights of row nrow, columns kcol .. kcol + 31 (two 16-blocks), as
+// packed bytes and their two scale bytes (zeros past n or k)
+struct WPiece {
+    uint4 q;
+    uint32_t s0, s1;
+};
+__device__ __forceinline__ WPiece load_wpiece(const DxArgs &a, int64_t nrow, int64_t kcol) {
+    WPiece w{make_uint4(0, 0, 0, 0), 0, 0};
+    if (nrow < a.n && kcol < a.k) {
+        const uint8_t *pr = a.packed + nrow * (a.k >> 1) + (kcol >> 1);
+        const uint8_t *sr = a.scales + nrow * (a.k >> 4) + (kcol >> 4);
+        // rows start 8-byte aligned (k % 16 == 0), 16-byte aligned when k % 32 == 0
+        const uint2 h0 = *reinterpret_cast<const uint2 *>(pr);
+        w.q.x = h0.x;
+        w.q.y = h0.y;
+        w.s0 = sr[0];
+        if (kcol + 32 <= a.k) {  // (else the last 16-block of a row with k % 32 == 16)
+            const uint2 h1 = reinterpret_cast<const uint2 *>(pr)[1];
+            w.q.z = h1.x;
+            w.q.w = h1.y;
+            w.s1 = sr[1];
+        }
+    }
+    return w;
+}
+
+// decode (exact BF16 e2m1 * e4m3) and store transposed: column kl + e of the
+// tile gets row nl
+__device__ __forceinline__ void store_wpiece(uint16_t *t, const WPiece &w, int nl, int kl) {
+    const float s0 = QERL_E4M3_F32(w.s0, 0), s1 = QERL_E4M3_F32(w.s1, 0);
+    const uint32_t qq[4] = {w.q.x, w.q.y, w.q.z, w.q.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        const float sc = h < 2 ? s0 : s1;
+        const f32x2_t f0 = QERL_FP4_PAIR_F32(qq[h], 0), f1 = QERL_FP4_PAIR_F32(qq[h], 1);
+        const f32x2_t f2 = QERL_FP4_PAIR_F32(qq[h], 2), f3 = QERL_FP4_PAIR_F32(qq[h], 3);
+        const float v[8] = {f0.x, f0.y, f1.x, f1.y, f2.x, f2.y, f3.x, f3.y};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[(kl + 8 * h + e) * kTPitch + nl] = f32_to_bf16_bits(v[e] * sc);
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t tt[kBK * kTPitch];  // tile^T: [kk][n]
+    __shared__ __attribute__((aligned(16))) uint16_t tt[2][kBK * kTPitch];  // tile^T: [kk][n], double-buffered
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int64_t i0 = (int64_t)blockIdx.y * kBM, kk0 = (int64_t)blockIdx.x * kBK;
     f32x4_t acc[4][2];
@@ -172,93 +215,93 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // the decode share of a thread: weight row nl (of the 32), 16 columns at 16 seg
-    const int nl = tid >> 3, seg = tid & 7;
-    const int64_t kcol = kk0 + 16 * seg;
-    auto mfma_step = [&](const uint4 (&af)[4]) {
+    // a thread's decode share per step: weight row nl (of 64), 32 columns at 32 seg
+    const int nl = tid >> 2, seg = tid & 3;
+    const int64_t kcol = kk0 + 32 * seg;
+    auto mfma_k32 = [&](const uint16_t *t, int koff, const uint4 (&af)[4]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(tt + (32 * wave + 16 * j + lr) * kTPitch + 8 * lq);
+            const bf16x8_t b =
+                *reinterpret_cast<const bf16x8_t *>(t + (32 * wave + 16 * j + lr) * kTPitch + koff + 8 * lq);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_b(af[i]), b, acc[i][j], 0, 0, 0);
         }
     };
-    for (int64_t n0 = 0; n0 < a.n; n0 += kBN) {
-        // A fragments: dy rows i0 + 16 i + lr, columns n0 + 8 lq .. + 8
-        uint4 af[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = load_dy8(a, i0 + 16 * i + lr, n0 + 8 * lq);
-        // this thread's 16 weights, decoded exactly (e2m1 * e4m3; s_t at the end)
-        const int64_t nrow = n0 + nl;
-        uint32_t w16[8];
-        if (nrow < a.n && kcol < a.k) {
-            const uint2 q = *reinterpret_cast<const uint2 *>(a.packed + nrow * (a.k >> 1) + (kcol >> 1));
-            const float sc = QERL_E4M3_F32(a.scales[nrow * (a.k >> 4) + (kcol >> 4)], 0);
-            const uint32_t qq[2] = {q.x, q.y};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const f32x2_t f0 = QERL_FP4_PAIR_F32(qq[h], 0), f1 = QERL_FP4_PAIR_F32(qq[h], 1);
-                const f32x2_t f2 = QERL_FP4_PAIR_F32(qq[h], 2), f3 = QERL_FP4_PAIR_F32(qq[h], 3);
-                w16[4 * h] = pack_bf16x2(f0.x * sc, f0.y * sc);
-                w16[4 * h + 1] = pack_bf16x2(f1.x * sc, f1.y * sc);
-                w16[4 * h + 2] = pack_bf16x2(f2.x * sc, f2.y * sc);
-                w16[4 * h + 3] = pack_bf16x2(f3.x * sc, f3.y * sc);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) w16[e] = 0;
-        }
-        __syncthreads();  // the previous block's tile has been read
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            tt[(16 * seg + 2 * e) * kTPitch + nl] = (uint16_t)(w16[e] & 0xFFFFu);
-            tt[(16 * seg + 2 * e + 1) * kTPitch + nl] = (uint16_t)(w16[e] >> 16);
-        }
+    const int64_t steps = (a.n + kBN - 1) / kBN;
+    if (steps > 0) {
+        store_wpiece(tt[0], load_wpiece(a, nl, kcol), nl, 32 * seg);
         __syncthreads();
-        mfma_step(af);
+    }
+    for (int64_t s = 0; s < steps; ++s) {
+        const int64_t n0 = s * kBN;
+        // A fragments of this step (dy rows i0 + 16 i + lr, two 32-column halves)
+        // and the next step's weights, all issued before the products
+        uint4 af[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[h][i] = load_dy8(a, i0 + 16 * i + lr, n0 + 32 * h + 8 * lq);
+        const bool more = s + 1 < steps;
+        WPiece nxt{make_uint4(0, 0, 0, 0), 0, 0};
+        if (more) nxt = load_wpiece(a, n0 + kBN + nl, kcol);
+        const uint16_t *cur = tt[s & 1];
+        mfma_k32(cur, 0, af[0]);
+        mfma_k32(cur, 32, af[1]);
+        if (more) store_wpiece(tt[(s + 1) & 1], nxt, nl, 32 * seg);
+        __syncthreads();  // next tile written; this one read by every wave
     }
     // LoRA: ranks as 2r more rows (hi, lo) with weights A and activations
-    // g * lambda / s_t
+    // g * lambda / s_t, 64 ranks per step (rows of the tile past r are zero)
     const float st = *a.tensor_scale;
     const float gs = a.lora_scale / st;
     for (int64_t j0 = 0; j0 < a.r; j0 += kBN) {
-        // A rows j0 + nl, 16 columns at kcol (BF16 as they are)
-        uint4 av[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+        // A row j0 + nl, 32 columns at kcol (BF16 as it is), transposed into the tile
+        uint4 av[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                       make_uint4(0, 0, 0, 0)};
         if (j0 + nl < a.r && kcol < a.k) {
             const uint4 *pa = reinterpret_cast<const uint4 *>(a.lora_a + (j0 + nl) * a.k + kcol);
             av[0] = pa[0];
             av[1] = pa[1];
+            if (kcol + 32 <= a.k) {
+                av[2] = pa[2];
+                av[3] = pa[3];
+            }
         }
-        uint4 ah[4], al[4];
+        uint16_t *t = tt[0];
+        const uint32_t aw[16] = {av[0].x, av[0].y, av[0].z, av[0].w, av[1].x, av[1].y, av[1].z, av[1].w,
+                                 av[2].x, av[2].y, av[2].z, av[2].w, av[3].x, av[3].y, av[3].z, av[3].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row = i0 + 16 * i + lr;
-            float gv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int64_t j = j0 + 8 * lq + e;
-                gv[e] = (row < a.m && j < a.r) ? a.g[row * a.r + j] * gs : 0.0f;
-            }
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hw[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
-                lw[e] = pack_bf16x2(gv[2 * e] - bf16lo_to_f32(hw[e]), gv[2 * e + 1] - bf16hi_to_f32(hw[e]));
-            }
-            ah[i] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            al[i] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        for (int e = 0; e < 16; ++e) {
+            t[(32 * seg + 2 * e) * kTPitch + nl] = (uint16_t)(aw[e] & 0xFFFFu);
+            t[(32 * seg + 2 * e + 1) * kTPitch + nl] = (uint16_t)(aw[e] >> 16);
         }
         __syncthreads();
-        const uint32_t aw[8] = {av[0].x, av[0].y, av[0].z, av[0].w, av[1].x, av[1].y, av[1].z, av[1].w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            tt[(16 * seg + 2 * e) * kTPitch + nl] = (uint16_t)(aw[e] & 0xFFFFu);
-            tt[(16 * seg + 2 * e + 1) * kTPitch + nl] = (uint16_t)(aw[e] >> 16);
+        for (int h = 0; h < 2; ++h) {
+            uint4 ah[4], al[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = i0 + 16 * i + lr;
+                float gv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int64_t j = j0 + 32 * h + 8 * lq + e;
+                    gv[e] = (row < a.m && j < a.r) ? a.g[row * a.r + j] * gs : 0.0f;
+                }
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    hw[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+                    lw[e] = pack_bf16x2(gv[2 * e] - bf16lo_to_f32(hw[e]), gv[2 * e + 1] - bf16hi_to_f32(hw[e]));
+                }
+                ah[i] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                al[i] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            }
+            mfma_k32(t, 32 * h, ah);
+            mfma_k32(t, 32 * h, al);
         }
-        __syncthreads();
-        mfma_step(ah);
-        mfma_step(al);
+        __syncthreads();  // the tile is read before the next ranks overwrite it
     }
     // dx[i][kk] = bf16(s_t * acc): lane holds rows 4 lq + v of column lr
 #pragma unroll
