@@ -10,7 +10,7 @@
 //   dB = lambda dy^T t          [N, r]  FP32   skinny products
 //
 // dx contracts over N, along which the packed weight is strided: a workgroup
-// owns a 64 x 128 tile of dx and walks N in steps of 64 rows, decoding each
+// owns a 128 x 128 tile of dx and walks N in steps of 64 rows, decoding each
 // 64 x 128 weight block (exact BF16 e2m1 * e4m3) into LDS transposed, so that
 // every MFMA B fragment (8 consecutive n of one column) is one 16-byte LDS
 // read; the tile is double-buffered (the next block is decoded while this
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float *pa
 }
 
 // ---- dx = dy what + lambda g A ---------------------------------------------
-constexpr int kBM = 64, kBK = 128, kBN = 64;  // dx tile (rows x columns), N per step
+constexpr int kMT = 8;  // 16-row m-tiles per workgroup
+constexpr int kBM = 16 * kMT, kBK = 128, kBN = 64;  // dx tile (rows x columns), N per step
 constexpr int kTPitch = kBN + 8;  // BF16 elements per transposed LDS row (16-byte aligned rows)
 
 struct DxArgs {
@@ -210,21 +211,21 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tt[2][kBK * kTPitch];  // tile^T: [kk][n], double-buffered
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int64_t i0 = (int64_t)blockIdx.y * kBM, kk0 = (int64_t)blockIdx.x * kBK;
-    f32x4_t acc[4][2];
+    f32x4_t acc[kMT][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // a thread's decode share per step: weight row nl (of 64), 32 columns at 32 seg
     const int nl = tid >> 2, seg = tid & 3;
     const int64_t kcol = kk0 + 32 * seg;
-    auto mfma_k32 = [&](const uint16_t *t, int koff, const uint4 (&af)[4]) {
+    auto mfma_k32 = [&](const uint16_t *t, int koff, const uint4 (&af)[kMT]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const bf16x8_t b =
                 *reinterpret_cast<const bf16x8_t *>(t + (32 * wave + 16 * j + lr) * kTPitch + koff + 8 * lq);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kMT; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_b(af[i]), b, acc[i][j], 0, 0, 0);
         }
     };
@@ -237,11 +238,11 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
         const int64_t n0 = s * kBN;
         // A fragments of this step (dy rows i0 + 16 i + lr, two 32-column halves)
         // and the next step's weights, all issued before the products
-        uint4 af[2][4];
+        uint4 af[2][kMT];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[h][i] = load_dy8(a, i0 + 16 * i + lr, n0 + 32 * h + 8 * lq);
+            for (int i = 0; i < kMT; ++i) af[h][i] = load_dy8(a, i0 + 16 * i + lr, n0 + 32 * h + 8 * lq);
         const bool more = s + 1 < steps;
         WPiece nxt{make_uint4(0, 0, 0, 0), 0, 0};
         if (more) nxt = load_wpiece(a, n0 + kBN + nl, kcol);
@@ -279,9 +280,9 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint4 ah[4], al[4];
+            uint4 ah[kMT], al[kMT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < kMT; ++i) {
                 const int64_t row = i0 + 16 * i + lr;
                 float gv[8];
 #pragma unroll
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     }
     // dx[i][kk] = bf16(s_t * acc): lane holds rows 4 lq + v of column lr
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
