@@ -211,24 +211,26 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tt[2][kBK * kTPitch];  // tile^T: [kk][n], double-buffered
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int64_t i0 = (int64_t)blockIdx.y * kBM, kk0 = (int64_t)blockIdx.x * kBK;
-    f32x4_t acc[kMT][2];
+    // wave w: m-tiles kMW w .. kMW w + kMW - 1 (its own dy rows) x all 8 column tiles
+    constexpr int kMW = kMT / 4, kNT = kBK / 16;
+    f32x4_t acc[kMW][kNT];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j = 0; j < kNT; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // a thread's decode share per step: weight row nl (of 64), 32 columns at 32 seg
     const int nl = tid >> 2, seg = tid & 3;
     const int64_t kcol = kk0 + 32 * seg;
-    auto mfma_k32 = [&](const uint16_t *t, int koff, const uint4 (&af)[kMT]) {
+    auto mfma_k32 = [&](const uint16_t *t, int koff, const uint4 (&af)[kMW]) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const bf16x8_t b =
-                *reinterpret_cast<const bf16x8_t *>(t + (32 * wave + 16 * j + lr) * kTPitch + koff + 8 * lq);
+        for (int j = 0; j < kNT; ++j) {
+            const bf16x8_t b = *reinterpret_cast<const bf16x8_t *>(t + (16 * j + lr) * kTPitch + koff + 8 * lq);
 #pragma unroll
-            for (int i = 0; i < kMT; ++i)
+            for (int i = 0; i < kMW; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_b(af[i]), b, acc[i][j], 0, 0, 0);
         }
     };
+    const int64_t mrow0 = i0 + 16 * kMW * wave;  // this wave's first dy row
     const int64_t steps = (a.n + kBN - 1) / kBN;
     if (steps > 0) {
         store_wpiece(tt[0], load_wpiece(a, nl, kcol), nl, 32 * seg);
@@ -238,11 +240,11 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
         const int64_t n0 = s * kBN;
         // A fragments of this step (dy rows i0 + 16 i + lr, two 32-column halves)
         // and the next step's weights, all issued before the products
-        uint4 af[2][kMT];
+        uint4 af[2][kMW];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) af[h][i] = load_dy8(a, i0 + 16 * i + lr, n0 + 32 * h + 8 * lq);
+            for (int i = 0; i < kMW; ++i) af[h][i] = load_dy8(a, mrow0 + 16 * i + lr, n0 + 32 * h + 8 * lq);
         const bool more = s + 1 < steps;
         WPiece nxt{make_uint4(0, 0, 0, 0), 0, 0};
         if (more) nxt = load_wpiece(a, n0 + kBN + nl, kcol);
@@ -280,10 +282,10 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
         __syncthreads();
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint4 ah[kMT], al[kMT];
+            uint4 ah[kMW], al[kMW];
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) {
-                const int64_t row = i0 + 16 * i + lr;
+            for (int i = 0; i < kMW; ++i) {
+                const int64_t row = mrow0 + 16 * i + lr;
                 float gv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -306,12 +308,12 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     }
     // dx[i][kk] = bf16(s_t * acc): lane holds rows 4 lq + v of column lr
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int64_t row = i0 + 16 * i + 4 * lq + v, col = kk0 + 32 * wave + 16 * j + lr;
+                const int64_t row = mrow0 + 16 * i + 4 * lq + v, col = kk0 + 16 * j + lr;
                 if (row < a.m && col < a.k) a.dx[row * a.lddx + col] = f32_to_bf16_bits(st * acc[i][j][v]);
             }
 }
