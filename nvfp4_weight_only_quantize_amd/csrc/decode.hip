@@ -26,7 +26,10 @@
 //    of t = x A^T over slices of K (MFMA) and publish them with device-coherent
 //    stores; the last producer to finish sums them in producer order and
 //    publishes t once, as BF16 hi + lo halves (relative error ~2^-16) in the
-//    layout the epilogue multiplies, behind a ready flag.
+//    layout the epilogue multiplies, behind a ready flag.  Short units with
+//    few producers ("direct") instead wait for the producers' count and sum
+//    their partials themselves, which takes the last-producer stage off the
+//    chain.
 //  * Every unit but the last of its row block stores its FP32 partial tile
 //    (coherent stores) and bumps a counter.  The last to arrive (every unit,
 //    when K is not split) loads all partial tiles and t in one batch -- the
@@ -34,6 +37,12 @@
 //    round trip of its own is spent on t (the wait for it is bounded all the
 //    same) -- sums the partials in slice order (deterministic), and adds
 //    lora_scale * t B^T on the MFMA.
+//  * NORM (an RMSNorm of x fused in front): the units stage bf16(x * norm_w),
+//    the producers also sum x^2 per K range, and 1 / rms scales t and the
+//    output row in the epilogue (a row's 1 / rms factors out of the product).
+//  * Several projections of one x (q/k/v, gate/up) share a launch: the
+//    segment is a grid dimension; a one-segment launch is its own
+//    instantiation with a one-plan argument.
 //
 // 16 < m <= 64, mfma_unit_kernel + finish_kernel, two launches.  Units are
 // (256 weight rows) x (slice of K) running the K loops of mfma_tile.h with all
