@@ -18,10 +18,11 @@
 // more rows, A as their weights and g * lambda / s_t split into BF16 hi + lo
 // as their activations; s_t is applied once at the end.
 //
-// t, g, dA and dB are products with one side of width r <= 128: each is
-// computed in FP32 on the VALU, one output row per thread, over q-chunks (a
-// grid over output rows and chunks), and the chunks' partial sums are added
-// in chunk order.
+// t and g (contractions over K and N, both operands contiguous along them,
+// B transposed first) run on the MFMA over chunks of 1024; dA and dB
+// (contractions over M, along which x and dy are strided) are FP32 VALU
+// products, one output row per thread.  Chunks' partial sums are added in
+// chunk order.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -126,6 +127,87 @@ __global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float *pa
     out[p * osp + j * osj] = scale * acc;
 }
 
+// ---- rank products on the MFMA: part[c][i][j] = sum over q in chunk c of
+// L[i][q] R[j][q], with both L [M, Q] and R [r, Q] contiguous along q (t = x A^T
+// with R = A; g = dy B with R = B^T formed first).  A workgroup takes 16 rows
+// of L and every rank; its 4 waves take interleaved 32-column steps of the
+// chunk and their tiles are summed in wave order through LDS.
+constexpr int kRpChunk = 1024;
+__device__ __forceinline__ bf16x8_t as_bf16x8_b(const uint4 &u) {
+    bf16x8_t v;
+    __builtin_memcpy(&v, &u, 16);
+    return v;
+}
+struct RankProd {
+    const uint16_t *L;
+    int64_t ldl;
+    const uint16_t *R;
+    int64_t ldr;
+    int64_t M, Q;
+    int r;
+    float *part;  // [chunks][M][r]
+};
+
+// 8 BF16 of row `row` at columns q .. q + 7 (zeros past rows or Q)
+__device__ __forceinline__ uint4 load_row8(const uint16_t *base, int64_t ld, int64_t rows, int64_t row, int64_t Q,
+                                           int64_t q) {
+    if (row >= rows || q >= Q) return make_uint4(0, 0, 0, 0);
+    const uint16_t *p = base + row * ld + q;
+    if (q + 8 <= Q && (ld & 7) == 0) return *reinterpret_cast<const uint4 *>(p);
+    uint16_t e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e[i] = q + i < Q ? p[i] : (uint16_t)0;
+    uint4 v;
+    __builtin_memcpy(&v, e, 16);
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void rank_prod_kernel(RankProd a) {
+    constexpr int JT = kMaxRankBwd / 16;
+    __shared__ f32x4_t red[4][JT][64];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t i0 = (int64_t)blockIdx.x * 16, c = blockIdx.y;
+    const int64_t q0 = c * kRpChunk, q1 = q0 + kRpChunk < a.Q ? q0 + kRpChunk : a.Q;
+    const int jt_n = (a.r + 15) / 16;
+    f32x4_t acc[JT];
+#pragma unroll
+    for (int j = 0; j < JT; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t q = q0 + 32 * wave; q < q1; q += 128) {
+        const uint4 af = load_row8(a.L, a.ldl, a.M, i0 + lr, q1, q + 8 * lq);
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+            if (j >= jt_n) break;  // (uniform)
+            const uint4 bf = load_row8(a.R, a.ldr, a.r, 16 * j + lr, q1, q + 8 * lq);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8_b(af), as_bf16x8_b(bf), acc[j], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < JT; ++j)
+        if (j < jt_n) red[wave][j][lane] = acc[j];
+    __syncthreads();
+    // tile j, lane l: rows 4 (l / 16) + v, rank 16 j + l % 16; one wave per tile group
+    for (int j = wave; j < jt_n; j += 4) {
+        f32x4_t t = red[0][j][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t = t + red[w][j][lane];
+        const int64_t jj = 16 * j + lr;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t i = i0 + 4 * lq + v;
+            if (i < a.M && jj < a.r) a.part[(c * a.M + i) * a.r + jj] = t[v];
+        }
+    }
+}
+
+// B [n, r] -> B^T [r, ldt] (BF16, rows padded to ldt >= n with zeros)
+__global__ __launch_bounds__(kThreads) void transpose_b_kernel(const uint16_t *b, int64_t n, int r, uint16_t *bt,
+                                                               int64_t ldt) {
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= (int64_t)r * ldt) return;
+    const int64_t j = i / ldt, nn = i - j * ldt;
+    bt[i] = nn < n ? b[nn * r + j] : (uint16_t)0;
+}
+
 // ---- dx = dy what + lambda g A ---------------------------------------------
 constexpr int kMT = 8;  // 16-row m-tiles per workgroup
 constexpr int kBM = 16 * kMT, kBK = 128, kBN = 64;  // dx tile (rows x columns), N per step
@@ -145,12 +227,6 @@ struct DxArgs {
     uint16_t *dx;
     int64_t lddx;
 };
-
-__device__ __forceinline__ bf16x8_t as_bf16x8_b(const uint4 &u) {
-    bf16x8_t v;
-    __builtin_memcpy(&v, &u, 16);
-    return v;
-}
 
 // 8 BF16 of dy row `row`, columns c0 .. c0 + 7 (zeros past m or n)
 __device__ __forceinline__ uint4 load_dy8(const DxArgs &a, int64_t row, int64_t c0) {
@@ -350,10 +426,11 @@ hipError_t skinny(Skinny s, float scale, float *out, int64_t osp, int64_t osj, h
 size_t backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
     // t and g [m, r], then the largest skinny partials (one product at a time)
     int64_t part = 0;
-    const int64_t cand[4] = {chunks_of(m, k) * m * r, chunks_of(m, n) * m * r, chunks_of(k, m) * k * r,
-                             chunks_of(n, m) * n * r};
+    const int64_t rp_k = (k + kRpChunk - 1) / kRpChunk, rp_n = (n + kRpChunk - 1) / kRpChunk;
+    const int64_t cand[4] = {rp_k * m * r, rp_n * m * r, chunks_of(k, m) * k * r, chunks_of(n, m) * n * r};
     for (int64_t c : cand) part = c > part ? c : part;
-    return (size_t)(2 * m * r + part) * 4 + 256;
+    const int64_t ldt = (n + 7) / 8 * 8;  // B^T rows, 16-byte aligned
+    return (size_t)(2 * m * r + part) * 4 + (size_t)(r * ldt) * 2 + 512;
 }
 
 hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
@@ -362,13 +439,37 @@ hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
     float *part = g + b.m * b.r;
     hipError_t e = hipSuccess;
     if (b.r > 0) {
-        // t = x A^T: L(p=i, q=kk) = x[i][kk], R(q=kk, j) = A[j][kk]
-        e = skinny<uint16_t, uint16_t>(Skinny{b.x, b.ldx, 1, b.lora_a, 1, b.k, b.m, b.k, b.r, 0, part}, 1.0f, t, b.r, 1,
-                                       stream);
+        int64_t part_floats = 0;
+        {
+            const int64_t rp_k = (b.k + kRpChunk - 1) / kRpChunk, rp_n = (b.n + kRpChunk - 1) / kRpChunk;
+            const int64_t cand[4] = {rp_k * b.m * b.r, rp_n * b.m * b.r, chunks_of(b.k, b.m) * b.k * b.r,
+                                     chunks_of(b.n, b.m) * b.n * b.r};
+            for (int64_t c : cand) part_floats = c > part_floats ? c : part_floats;
+        }
+        const int64_t ldt = (b.n + 7) / 8 * 8;
+        // B^T after t, g and the partials, 256-byte aligned from the (16-byte aligned) workspace
+        uint16_t *bt = reinterpret_cast<uint16_t *>(static_cast<char *>(b.workspace) +
+                                                    (((2 * b.m * b.r + part_floats) * 4 + 255) & ~(int64_t)255));
+        auto rank_prod = [&](const uint16_t *L, int64_t ldl, const uint16_t *R, int64_t ldr, int64_t Q, float *out) {
+            const int64_t chunks = (Q + kRpChunk - 1) / kRpChunk;
+            hipLaunchKernelGGL(rank_prod_kernel, dim3((unsigned)((b.m + 15) / 16), (unsigned)chunks), dim3(kThreads),
+                               0, stream, RankProd{L, ldl, R, ldr, b.m, Q, b.r, part});
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            const int64_t total = b.m * b.r;
+            hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                               dim3(kThreads), 0, stream, part, chunks, b.m, b.r, 1.0f, out, (int64_t)b.r, (int64_t)1);
+            return hipGetLastError();
+        };
+        // t = x A^T (A rows contiguous along k)
+        e = rank_prod(b.x, b.ldx, b.lora_a, b.k, b.k, t);
         if (e != hipSuccess) return e;
-        // g = dy B: L(p=i, q=n) = dy[i][n], R(q=n, j) = B[n][j]
-        e = skinny<uint16_t, uint16_t>(Skinny{b.dy, b.ldy, 1, b.lora_b, b.r, 1, b.m, b.n, b.r, 0, part}, 1.0f, g, b.r, 1,
-                                       stream);
+        // g = dy B = dy (B^T)^T: B^T formed first, rows padded to a multiple of 8
+        hipLaunchKernelGGL(transpose_b_kernel, dim3((unsigned)((b.r * ldt + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, b.lora_b, b.n, b.r, bt, ldt);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = rank_prod(b.dy, b.ldy, bt, ldt, b.n, g);
         if (e != hipSuccess) return e;
         if (b.da) {  // dA[j][kk] = lambda sum_i g[i][j] x[i][kk]: L(p=kk, q=i) = x[i][kk], R(q=i, j) = g[i][j]
             e = skinny<uint16_t, float>(Skinny{b.x, 1, b.ldx, g, b.r, 1, b.k, b.m, b.r, 0, part}, b.lora_scale, b.da, 1,

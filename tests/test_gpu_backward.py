@@ -57,7 +57,8 @@ def _check(m, n, k, r, seed, lam=2.0, strided=False):
 
 
 @pytest.mark.parametrize("mnkr", [(1, 16, 32, 4), (5, 40, 64, 8), (64, 96, 256, 16), (100, 130, 528, 32),
-                                  (3, 33, 80, 0), (17, 256, 1024, 128), (128, 512, 1024, 32), (65, 64, 144, 24)])
+                                  (3, 33, 80, 0), (17, 256, 1024, 128), (128, 512, 1024, 32), (65, 64, 144, 24),
+                                  (9, 37, 96, 5), (33, 2050, 2064, 3)])
 def test_backward_small(mnkr):
     m, n, k, r = mnkr
     _check(m, n, k, r, seed=5000 + m + n + k + r)
