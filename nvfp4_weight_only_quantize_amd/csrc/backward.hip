@@ -6,8 +6,8 @@
 //   y = x what^T + lambda (x A^T) B^T,   t = x A^T,   g = dy B   ([M, r])
 // the gradients are
 //   dx = dy what + lambda g A   [M, K]  BF16   dx_kernel
-//   dA = lambda g^T x           [r, K]  FP32   skinny products
-//   dB = lambda dy^T t          [N, r]  FP32   skinny products
+//   dA = lambda g^T x           [r, K]  FP32   mprod_kernel
+//   dB = lambda dy^T t          [N, r]  FP32   mprod_kernel
 //
 // dx contracts over N, along which the packed weight is strided: a workgroup
 // owns a 128 x 128 tile of dx and walks N in steps of 64 rows, decoding each
@@ -19,9 +19,9 @@
 // as their activations; s_t is applied once at the end.
 //
 // t and g (contractions over K and N, both operands contiguous along them,
-// B transposed first) run on the MFMA over chunks of 1024; dA and dB
-// (contractions over M, along which x and dy are strided) are FP32 VALU
-// products, one output row per thread.  Chunks' partial sums are added in
+// B transposed first) and dA, dB (contractions over M, along which x and dy
+// are strided: transposed LDS tiles, the FP32 side as BF16 hi + lo) run on the
+// MFMA over chunks of the contraction; the chunks' partial sums are added in
 // chunk order.
 #include "device_common.h"
 #include "qerl_internal.h"
@@ -31,93 +31,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ---- skinny products ------------------------------------------------------
-// part[c][p][j] = sum over q in chunk c of L(p, q) R(q, j), j < r.
-// L(p, q) = L[p * lsp + q * lsq], R(q, j) = R[q * rsq + j * rsj].
-// One thread per output row p and 32 ranks at a time (one pass per group of
-// 32): the chunk's R values for the group sit in LDS (every thread reads the
-// same R[q][..], a broadcast) and the thread streams its L(p, q) -- 8 q per
-// 16-byte load when L is contiguous along q, else one load per q coalesced
-// across the threads' consecutive p.
-constexpr int kSkP = 256;     // output rows per workgroup (one per thread)
-constexpr int kSkJ = 32;      // ranks per pass
-constexpr int kSkMaxChunk = 512;
-struct Skinny {
-    const void *L;
-    int64_t lsp, lsq;
-    const void *R;
-    int64_t rsq, rsj;
-    int64_t P, Q;
-    int r;
-    int64_t chunk;  // q per workgroup (a multiple of 8, <= kSkMaxChunk)
-    float *part;    // [chunks][P][r]
-};
-
-template <typename T>
-__device__ __forceinline__ float ld_f32(const void *base, int64_t i) {
-    if constexpr (sizeof(T) == 2) {
-        return bf16lo_to_f32(static_cast<const uint16_t *>(base)[i]);
-    } else {
-        return static_cast<const float *>(base)[i];
-    }
-}
-
-template <typename LT, typename RT>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(Skinny s) {
-    __shared__ __attribute__((aligned(16))) float rs[kSkMaxChunk][kSkJ];
-    const int tid = threadIdx.x;
-    const int64_t p = (int64_t)blockIdx.x * kSkP + tid;
-    const int64_t c = blockIdx.y;
-    const int64_t q_begin = c * s.chunk, q_end = q_begin + s.chunk < s.Q ? q_begin + s.chunk : s.Q;
-    const int nq = (int)(q_end - q_begin);
-    const bool vec = sizeof(LT) == 2 && s.lsq == 1 && (s.lsp & 7) == 0;  // 8 BF16 of a row per load
-    for (int j0 = 0; j0 < s.r; j0 += kSkJ) {
-        const int nj = s.r - j0 < kSkJ ? s.r - j0 : kSkJ;
-        __syncthreads();  // the previous pass's R values have been read
-        for (int e = tid; e < nq * kSkJ; e += kThreads) {
-            const int qq = s.rsj == 1 ? e / kSkJ : e % nq;
-            const int jj = s.rsj == 1 ? e % kSkJ : e / nq;
-            rs[qq][jj] = jj < nj ? ld_f32<RT>(s.R, (q_begin + qq) * s.rsq + (j0 + jj) * s.rsj) : 0.0f;
-        }
-        __syncthreads();
-        if (p >= s.P) continue;
-        float acc[kSkJ];
-#pragma unroll
-        for (int u = 0; u < kSkJ; ++u) acc[u] = 0.0f;
-        auto fma_row = [&](int qq, float l) {
-            const f32x4_t *rq = reinterpret_cast<const f32x4_t *>(rs[qq]);
-#pragma unroll
-            for (int u = 0; u < kSkJ / 4; ++u) {
-                const f32x4_t rv = rq[u];
-                acc[4 * u] = __builtin_fmaf(l, rv[0], acc[4 * u]);
-                acc[4 * u + 1] = __builtin_fmaf(l, rv[1], acc[4 * u + 1]);
-                acc[4 * u + 2] = __builtin_fmaf(l, rv[2], acc[4 * u + 2]);
-                acc[4 * u + 3] = __builtin_fmaf(l, rv[3], acc[4 * u + 3]);
-            }
-        };
-        if (vec) {
-            const uint16_t *lrow = static_cast<const uint16_t *>(s.L) + p * s.lsp + q_begin;
-            int qq = 0;
-            for (; qq + 8 <= nq; qq += 8) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(lrow + qq);
-                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    fma_row(qq + 2 * h, bf16lo_to_f32(w4[h]));
-                    fma_row(qq + 2 * h + 1, bf16hi_to_f32(w4[h]));
-                }
-            }
-            for (; qq < nq; ++qq) fma_row(qq, bf16lo_to_f32(lrow[qq]));
-        } else {
-#pragma unroll 4
-            for (int qq = 0; qq < nq; ++qq) fma_row(qq, ld_f32<LT>(s.L, p * s.lsp + (q_begin + qq) * s.lsq));
-        }
-        for (int u = 0; u < nj; ++u) s.part[(c * s.P + p) * s.r + j0 + u] = acc[u];
-    }
-}
-
 // out[p * osp + j * osj] = scale * sum over chunks (in order) of part[c][p][j]
-__global__ __launch_bounds__(kThreads) void skinny_reduce_kernel(const float *part, int64_t chunks, int64_t P, int r,
+__global__ __launch_bounds__(kThreads) void chunk_reduce_kernel(const float *part, int64_t chunks, int64_t P, int r,
                                                                  float scale, float *out, int64_t osp, int64_t osj) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (i >= P * r) return;
@@ -197,6 +112,103 @@ __global__ __launch_bounds__(kThreads) void rank_prod_kernel(RankProd a) {
             if (i < a.M && jj < a.r) a.part[(c * a.M + i) * a.r + jj] = t[v];
         }
     }
+}
+
+// ---- products over M on the MFMA: part[c][p][j] = sum over m in chunk c of
+// X[m][p] Y[m][j], X BF16 [M, P] (row stride ldx), Y FP32 [M, r] (dA with
+// X = x, Y = g; dB with X = dy, Y = t).  Both are strided along M, the
+// contraction: each 32-row step stages X's 128 columns and Y transposed into
+// LDS (Y as BF16 hi + lo, two MFMAs), so every fragment is one 16-byte read.
+// A workgroup covers 128 values of p x every rank over one chunk of M.
+constexpr int kMpChunk = 512, kMpP = 128, kMpStep = 32;
+constexpr int kMpPitch = kMpStep + 8;  // BF16 per transposed LDS row
+struct MProd {
+    const uint16_t *X;
+    int64_t ldx;
+    const float *Y;
+    int64_t M, P;
+    int r;
+    float *part;  // [chunks][P][r]
+};
+
+__global__ __launch_bounds__(kThreads) void mprod_kernel(MProd a) {
+    constexpr int JT = kMaxRankBwd / 16;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[kMpP * kMpPitch];           // [p][m]
+    __shared__ __attribute__((aligned(16))) uint16_t yt[2][kMaxRankBwd * kMpPitch];  // hi, lo: [j][m]
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int64_t p0 = (int64_t)blockIdx.x * kMpP, c = blockIdx.y;
+    const int64_t m0 = c * kMpChunk, m1 = m0 + kMpChunk < a.M ? m0 + kMpChunk : a.M;
+    const int jt_n = (a.r + 15) / 16;
+    // wave w: p-tiles 2 w, 2 w + 1 x every rank tile
+    f32x4_t acc[2][JT];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < JT; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t ms = m0; ms < m1; ms += kMpStep) {
+        __syncthreads();  // the previous step's tiles have been read
+        // X rows ms .. ms + 31, columns p0 .. p0 + 127 -> xt[p][m]: a thread
+        // takes one row and 16 columns (two 8-column loads)
+        {
+            const int ml = tid >> 3, pc = 16 * (tid & 7);
+            const int64_t mm = ms + ml;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t pp = p0 + pc + 8 * h;
+                uint16_t e[8];
+                if (mm < m1 && pp + 8 <= a.P && (a.ldx & 7) == 0) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(a.X + mm * a.ldx + pp);
+                    __builtin_memcpy(e, &v, 16);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) e[i] = (mm < m1 && pp + i < a.P) ? a.X[mm * a.ldx + pp + i] : (uint16_t)0;
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xt[(pc + 8 * h + i) * kMpPitch + ml] = e[i];
+            }
+        }
+        // Y rows ms .. ms + 31, all ranks -> yt[hi/lo][j][m]
+        for (int e = tid; e < kMpStep * a.r; e += kThreads) {
+            const int ml = e / a.r, j = e - ml * a.r;
+            const int64_t mm = ms + ml;
+            const float v = mm < m1 ? a.Y[mm * a.r + j] : 0.0f;
+            const uint16_t hi = f32_to_bf16_bits(v);
+            yt[0][j * kMpPitch + ml] = hi;
+            yt[1][j * kMpPitch + ml] = f32_to_bf16_bits(v - __uint_as_float((uint32_t)hi << 16));
+        }
+        // ranks past r (to the tile edge) are zero
+        for (int e = tid; e < kMpStep * (16 * jt_n - a.r); e += kThreads) {
+            const int ml = e % kMpStep, j = a.r + e / kMpStep;
+            yt[0][j * kMpPitch + ml] = 0;
+            yt[1][j * kMpPitch + ml] = 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t *>(xt + (32 * wave + 16 * i + lr) * kMpPitch + 8 * lq);
+#pragma unroll
+            for (int j = 0; j < JT; ++j) {
+                if (j >= jt_n) break;  // (uniform)
+                const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(yt[0] + (16 * j + lr) * kMpPitch + 8 * lq);
+                const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(yt[1] + (16 * j + lr) * kMpPitch + 8 * lq);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bh, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bl, acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+    // tile (i, j), lane l: p = p0 + 32 w + 16 i + 4 (l / 16) + v, rank 16 j + l % 16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < JT; ++j) {
+            if (j >= jt_n) break;
+            const int64_t jj = 16 * j + lr;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t pp = p0 + 32 * wave + 16 * i + 4 * lq + v;
+                if (pp < a.P && jj < a.r) a.part[(c * a.P + pp) * a.r + jj] = acc[i][j][v];
+            }
+        }
 }
 
 // B [n, r] -> B^T [r, ldt] (BF16, rows padded to ldt >= n with zeros)
@@ -394,40 +406,14 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
             }
 }
 
-// q per workgroup: enough chunks that the grid covers the GPU about twice
-// (at least 64 q each, a multiple of 8, at most kSkMaxChunk)
-int64_t chunk_of(int64_t P, int64_t Q) {
-    const int64_t pblocks = (P + kSkP - 1) / kSkP;
-    int64_t want = (512 + pblocks - 1) / pblocks;  // chunks wanted
-    int64_t ch = (Q + want - 1) / want;
-    ch = (ch + 7) / 8 * 8;
-    if (ch < 64) ch = 64;
-    if (ch > kSkMaxChunk) ch = kSkMaxChunk;
-    return ch;
-}
-int64_t chunks_of(int64_t P, int64_t Q) { return (Q + chunk_of(P, Q) - 1) / chunk_of(P, Q); }
-
-template <typename LT, typename RT>
-hipError_t skinny(Skinny s, float scale, float *out, int64_t osp, int64_t osj, hipStream_t stream) {
-    s.chunk = chunk_of(s.P, s.Q);
-    const int64_t chunks = chunks_of(s.P, s.Q);
-    const dim3 grid((unsigned)((s.P + kSkP - 1) / kSkP), (unsigned)chunks);
-    hipLaunchKernelGGL((skinny_kernel<LT, RT>), grid, dim3(kThreads), 0, stream, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t total = s.P * s.r;
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, s.part, chunks, s.P, s.r, scale, out, osp, osj);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 size_t backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
-    // t and g [m, r], then the largest skinny partials (one product at a time)
+    // t and g [m, r], then the largest chunk partials (one product at a time)
     int64_t part = 0;
     const int64_t rp_k = (k + kRpChunk - 1) / kRpChunk, rp_n = (n + kRpChunk - 1) / kRpChunk;
-    const int64_t cand[4] = {rp_k * m * r, rp_n * m * r, chunks_of(k, m) * k * r, chunks_of(n, m) * n * r};
+    const int64_t mp = (m + kMpChunk - 1) / kMpChunk;
+    const int64_t cand[4] = {rp_k * m * r, rp_n * m * r, mp * k * r, mp * n * r};
     for (int64_t c : cand) part = c > part ? c : part;
     const int64_t ldt = (n + 7) / 8 * 8;  // B^T rows, 16-byte aligned
     return (size_t)(2 * m * r + part) * 4 + (size_t)(r * ldt) * 2 + 512;
@@ -442,8 +428,8 @@ hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
         int64_t part_floats = 0;
         {
             const int64_t rp_k = (b.k + kRpChunk - 1) / kRpChunk, rp_n = (b.n + kRpChunk - 1) / kRpChunk;
-            const int64_t cand[4] = {rp_k * b.m * b.r, rp_n * b.m * b.r, chunks_of(b.k, b.m) * b.k * b.r,
-                                     chunks_of(b.n, b.m) * b.n * b.r};
+            const int64_t mp = (b.m + kMpChunk - 1) / kMpChunk;
+            const int64_t cand[4] = {rp_k * b.m * b.r, rp_n * b.m * b.r, mp * b.k * b.r, mp * b.n * b.r};
             for (int64_t c : cand) part_floats = c > part_floats ? c : part_floats;
         }
         const int64_t ldt = (b.n + 7) / 8 * 8;
@@ -457,7 +443,7 @@ hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
             const int64_t total = b.m * b.r;
-            hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+            hipLaunchKernelGGL(chunk_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
                                dim3(kThreads), 0, stream, part, chunks, b.m, b.r, 1.0f, out, (int64_t)b.r, (int64_t)1);
             return hipGetLastError();
         };
@@ -471,14 +457,24 @@ hipError_t launch_backward(const BackwardArgs &b, hipStream_t stream) {
         if (e != hipSuccess) return e;
         e = rank_prod(b.dy, b.ldy, bt, ldt, b.n, g);
         if (e != hipSuccess) return e;
-        if (b.da) {  // dA[j][kk] = lambda sum_i g[i][j] x[i][kk]: L(p=kk, q=i) = x[i][kk], R(q=i, j) = g[i][j]
-            e = skinny<uint16_t, float>(Skinny{b.x, 1, b.ldx, g, b.r, 1, b.k, b.m, b.r, 0, part}, b.lora_scale, b.da, 1,
-                                        b.k, stream);
+        auto mprod = [&](const uint16_t *X, int64_t ldx, const float *Y, int64_t P, float *out, int64_t osp,
+                         int64_t osj) {
+            const int64_t chunks = (b.m + kMpChunk - 1) / kMpChunk;
+            hipLaunchKernelGGL(mprod_kernel, dim3((unsigned)((P + kMpP - 1) / kMpP), (unsigned)chunks),
+                               dim3(kThreads), 0, stream, MProd{X, ldx, Y, b.m, P, b.r, part});
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            const int64_t total = P * b.r;
+            hipLaunchKernelGGL(chunk_reduce_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
+                               dim3(kThreads), 0, stream, part, chunks, P, b.r, b.lora_scale, out, osp, osj);
+            return hipGetLastError();
+        };
+        if (b.da) {  // dA[j][kk] = lambda sum_i x[i][kk] g[i][j]
+            e = mprod(b.x, b.ldx, g, b.k, b.da, 1, b.k);
             if (e != hipSuccess) return e;
         }
         if (b.db) {  // dB[n][j] = lambda sum_i dy[i][n] t[i][j]
-            e = skinny<uint16_t, float>(Skinny{b.dy, 1, b.ldy, t, b.r, 1, b.n, b.m, b.r, 0, part}, b.lora_scale, b.db,
-                                        b.r, 1, stream);
+            e = mprod(b.dy, b.ldy, t, b.n, b.db, b.r, 1);
             if (e != hipSuccess) return e;
         }
     }
