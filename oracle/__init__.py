@@ -80,6 +80,10 @@ def _load():
     lib.oracle_e2m1_sr_mag.restype = i32
     lib.oracle_mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P]
     lib.oracle_mxfp4_quantize.restype = i32
+    lib.oracle_bf16_nearest_even.argtypes = [dbl]
+    lib.oracle_bf16_nearest_even.restype = ctypes.c_uint16
+    lib.oracle_nvfp4_dequantize.argtypes = [P, P, flt, i64, i64, P, P]
+    lib.oracle_nvfp4_dequantize.restype = i32
     lib.oracle_w4a16_lora_backward.argtypes = [P, P, i64, i64, i64, P, P, flt, P, P, i32, flt, P, P, P]
     lib.oracle_w4a16_lora_backward.restype = i32
     lib.oracle_w4a16_lora_gemm_f64.argtypes = lib.oracle_w4a16_lora_gemm.argtypes
@@ -182,6 +186,28 @@ def mxfp4_quantize(w_bits):
     if rc != 0:
         raise ValueError(f"oracle_mxfp4_quantize rejected its arguments (rc={rc})")
     return packed, scales
+
+
+def bf16_nearest_even(v: float) -> int:
+    """Bit pattern of the BF16 value nearest to v (ties to the even code)."""
+    return int(_load().oracle_bf16_nearest_even(float(v)))
+
+
+def nvfp4_dequantize(packed, scales, s_t):
+    """(fp64 [N, K] exact values, uint16 [N, K] BF16 bit patterns) of an NVFP4
+    tensor: e2m1 x e4m3 x s_t, rounded once to the nearest BF16 (ties even)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, k = packed.shape[0], packed.shape[1] * 2
+    if scales.shape != (n, k // 16):
+        raise ValueError(f"scales shape {scales.shape} != {(n, k // 16)}")
+    f64 = np.zeros((n, k), dtype=np.float64)
+    bits = np.zeros((n, k), dtype=np.uint16)
+    rc = _load().oracle_nvfp4_dequantize(_ptr(packed), _ptr(scales), float(np.float32(s_t)), n, k, _ptr(f64),
+                                         _ptr(bits))
+    if rc != 0:
+        raise ValueError(f"oracle_nvfp4_dequantize rejected its arguments (rc={rc})")
+    return f64, bits
 
 
 # ------------------------------------------------------------ W4A16 GEMM --

@@ -378,6 +378,62 @@ int oracle_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw,
 }
 
 /* ------------------------------------------------------------------------ */
+/* NVFP4 -> BF16 dequantization                                              */
+/* ------------------------------------------------------------------------ */
+/* The value a stored weight stands for is e2m1(code) * e4m3(block scale) *
+ * s_t (bitsofall page, "NVFP4: NVIDIA's FP4 Format": a 4-bit element, one
+ * E4M3 scale per 16 values, an FP32 tensor scale).  The update phase of QeRL
+ * turns the weights back into 16-bit values before its GEMMs (README "Hints
+ * for QeRL training", item 2; bitsofall page, "Workflow: Rollout, Update,
+ * Quantization"); the BF16 result is that exact product (fp64:
+ * 6 significant bits times 24) rounded to the nearest BF16 value, ties to the
+ * even code.                                                               */
+
+/* The BF16 value of code c (0 <= c <= 0x7F80, sign clear); 0x7F80 counts as
+ * 2^128, the next step past the largest finite value, so that a magnitude
+ * from half a step above that value up rounds to infinity as IEEE 754 says. */
+static double bf16_mag(uint16_t c) {
+    return c == 0x7F80 ? ldexp(1.0, 128) : oracle_bf16_decode(c);
+}
+
+/* Nearest BF16 to v, ties to the even code: the largest magnitude code not
+ * above |v| by bisection over the ordered codes, then the nearer of it and
+ * its successor. */
+uint16_t oracle_bf16_nearest_even(double v) {
+    if (isnan(v)) return 0x7FC0;
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    const double a = fabs(v);
+    if (a >= bf16_mag(0x7F80)) return sign | 0x7F80;
+    uint16_t lo = 0, hi = 0x7F80; /* bf16_mag(lo) <= a < bf16_mag(hi) */
+    while (hi - lo > 1) {
+        const uint16_t mid = (uint16_t)((lo + hi) / 2);
+        if (bf16_mag(mid) <= a) lo = mid; else hi = mid;
+    }
+    const double below = a - bf16_mag(lo), above = bf16_mag(hi) - a;
+    uint16_t c;
+    if (below < above) c = lo;
+    else if (above < below) c = hi;
+    else c = (lo & 1) ? hi : lo;
+    return sign | c;
+}
+
+/* packed [n, k/2] (even element in the low nibble), scales [n, k/16], s_t ->
+ * out_f64 [n, k] (exact values, may be NULL) and out_bf16 [n, k] (may be NULL). */
+int oracle_nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, float s_t, int64_t n, int64_t k,
+                            double *out_f64, uint16_t *out_bf16) {
+    if (n < 0 || k < 0 || k % 16 != 0) return 1;
+    for (int64_t row = 0; row < n; ++row)
+        for (int64_t j = 0; j < k; ++j) {
+            const uint8_t byte = packed[row * (k / 2) + j / 2];
+            const int code = (j % 2 == 0) ? (byte & 15) : (byte >> 4);
+            const double v = oracle_e2m1_decode(code) * oracle_e4m3_decode(scales[row * (k / 16) + j / 16]) * (double)s_t;
+            if (out_f64) out_f64[row * k + j] = v;
+            if (out_bf16) out_bf16[row * k + j] = oracle_bf16_nearest_even(v);
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* W4A16 + LoRA linear layer, fp64                                           */
 /* ------------------------------------------------------------------------ */
 /* y[m, n] = sum_k x[m,k] * what[n,k]  +  lora_scale * sum_j t[m,j] * B[n,j],
