@@ -530,6 +530,69 @@ def backward_leg(dev, reps, m=2048):
                         f"LoRA r = {RANK}", "ms": t * 1e3, "tflops": tf, "frac": tf / BF16_MFMA_PEAK_TFLOPS}
 
 
+def _graph_ms(run, reps):
+    """Milliseconds per run(), captured once as a HIP graph and replayed."""
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps
+
+
+def update_forward_leg(dev, reps, m=2048):
+    """The update phase's forward (the logits pass over the sampled tokens) of
+    the 7B layer's seven projections at M tokens, two ways: the fused W4A16 +
+    LoRA GEMM, and the unfused route the README's training hints describe
+    (each weight dequantized to BF16 by qerl_nvfp4_dequantize, then torch's
+    BF16 GEMM and the LoRA products).  The dequantization alone is reported
+    as HBM bandwidth: per weight element 0.5 B of codes, 1/16 B of scales and
+    2 B of BF16 written."""
+    layer = make_layer(synth.QWEN25_7B, SEED, dev)
+    xs = {name: synth.activation_bf16(m, k, synth.seed_for(SEED, "fx", name), 0.005, device=dev)
+          for name, (n, k) in synth.QWEN25_7B.items()}
+    ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in synth.QWEN25_7B.items()}
+    wbf = {name: torch.empty((n, k), dtype=torch.bfloat16, device=dev) for name, (n, k) in synth.QWEN25_7B.items()}
+    ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(m, n, k, RANK) for n, k in synth.QWEN25_7B.values()),
+                     dtype=torch.uint8, device=dev)
+    lam = ALPHA / RANK
+
+    def fused():
+        for name in synth.PROJ_ORDER:
+            p = layer[name]
+            q.w4a16_lora_gemm(xs[name], p.wq, p.a, p.b, lam, out=ys[name], workspace=ws)
+
+    def dequant():
+        for name in synth.PROJ_ORDER:
+            q.nvfp4_dequantize(layer[name].wq, out=wbf[name])
+
+    def unfused():
+        for name in synth.PROJ_ORDER:
+            p, x = layer[name], xs[name]
+            q.nvfp4_dequantize(p.wq, out=wbf[name])
+            torch.mm(x, wbf[name].t(), out=ys[name])
+            ys[name].add_(torch.nn.functional.linear(torch.nn.functional.linear(x, p.a), p.b), alpha=lam)
+
+    t_fused, t_unfused, t_deq = _graph_ms(fused, reps), _graph_ms(unfused, reps), _graph_ms(dequant, reps)
+    elems = sum(n * k for n, k in synth.QWEN25_7B.values())
+    flops = sum(gemm_flops(m, n, k, RANK) for n, k in synth.QWEN25_7B.values())
+    del layer, xs, ys, wbf, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"forward of the Qwen2.5-7B-shaped layer's 7 projections, M = {m} tokens, LoRA r = {RANK}",
+            "fused_w4a16_lora_ms": round(t_fused, 4), "dequant_then_bf16_ms": round(t_unfused, 4),
+            "speedup": round(t_unfused / t_fused, 3), "fused_tflops": round(flops / t_fused / 1e9, 1),
+            "dequant_ms": round(t_deq, 4), "dequant_gbs": round(elems * (0.5 + 1 / 16 + 2) / t_deq / 1e6, 1)}
+
+
 E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 
 
@@ -888,6 +951,8 @@ def main():
         log("quantizer variants leg ...")
         result["quantizer_variants"] = quantizer_variants_leg(dev, reps=3)
     if not args.no_backward:
+        log("update-phase forward: fused W4A16 + LoRA against dequantize + BF16 GEMM ...")
+        result["update_forward"] = update_forward_leg(dev, reps=3)
         log("backward leg ...")
         result["backward"] = backward_leg(dev, reps=3)
     if not args.no_cpu_baseline:

@@ -136,6 +136,25 @@ qerl_status qerl_nvfp4_quantize_stochastic(const void *w_bf16, int64_t n, int64_
 qerl_status qerl_mxfp4_quantize(const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
                                 uint8_t *packed, uint8_t *scales, void *stream);
 
+/*
+ * NVFP4 -> BF16: out[n, j] = e2m1(code[n, j]) * e4m3(scales[n, j/16]) * s_t,
+ * the value the bitsofall page's "NVFP4: NVIDIA's FP4 Format" gives a stored
+ * weight, rounded once to the nearest BF16 (ties to even; the exact product
+ * is formed first).  This is the dequantization an unfused update-phase
+ * forward performs before 16-bit GEMMs (README "Hints for QeRL training",
+ * item 2; bitsofall "Workflow: Rollout, Update, Quantization");
+ * qerl_w4a16_lora_gemm computes the same layer without it.
+ *   packed        uint8 [n, k/2] as written by qerl_nvfp4_quantize (even
+ *                 element in the low nibble), 8-byte aligned
+ *   scales        uint8 [n, k/16] E4M3 bytes (0x7F / 0xFF, E4M3 NaN, give NaN)
+ *   tensor_scale  device pointer to the FP32 s_t
+ *   out_bf16      [n, k], row stride ldo >= k, ldo % 8 == 0, 16-byte aligned;
+ *                 must not overlap the inputs
+ * Requires n >= 1, k >= 16, k % 16 == 0.  No workspace.
+ */
+qerl_status qerl_nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                  int64_t n, int64_t k, void *out_bf16, int64_t ldo, void *stream);
+
 /* ----------------------------------------------------------------------- */
 /* W4A16 (NVFP4 weight x BF16 activation) linear layer with LoRA epilogue   */
 /* ----------------------------------------------------------------------- */

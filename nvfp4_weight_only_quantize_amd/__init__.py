@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     L.qerl_nvfp4_quantize_stochastic.restype = ctypes.c_int
     L.qerl_mxfp4_quantize.argtypes = [P, i64, i64, i64, P, P, P]
     L.qerl_mxfp4_quantize.restype = ctypes.c_int
+    L.qerl_nvfp4_dequantize.argtypes = [P, P, P, i64, i64, P, i64, P]
+    L.qerl_nvfp4_dequantize.restype = ctypes.c_int
     L.qerl_w4a16_lora_gemm_workspace_size.argtypes = [i64, i64, i64, i32]
     L.qerl_w4a16_lora_gemm_workspace_size.restype = sz
     L.qerl_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, P, i64, P, P, i32, f32, P, i64,
@@ -195,6 +197,20 @@ def mxfp4_quantize(w: torch.Tensor, stream=None):
     _check(lib().qerl_mxfp4_quantize(_ptr(w), n, k, _rows(w, "w"), _ptr(packed), _ptr(scales),
                                      _stream(stream, dev)))
     return packed, scales
+
+
+def nvfp4_dequantize(wq: NVFP4Weight, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """BF16 [N, K] = e2m1 x e4m3 x s_t of an NVFP4 weight, rounded once to BF16."""
+    n, k = wq.shape
+    dev = wq.packed.device
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (n, k):
+        raise ValueError(f"out shape {tuple(out.shape)} != {(n, k)}")
+    _check(lib().qerl_nvfp4_dequantize(_ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n, k, _ptr(out),
+                                       _rows(out, "out"), _stream(stream, dev)))
+    return out
 
 
 # --------------------------------------------------------- W4A16 + LoRA ----

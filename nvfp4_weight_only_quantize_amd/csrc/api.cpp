@@ -58,6 +58,23 @@ size_t qerl_nvfp4_quantize_workspace_size(int64_t n, int64_t k) {
     return qerl::quantize_workspace_bytes(n, k);
 }
 
+qerl_status qerl_nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                  int64_t n, int64_t k, void *out_bf16, int64_t ldo, void *stream) {
+    g_last_error[0] = '\0';
+    if (!packed || !scales || !tensor_scale || !out_bf16)
+        return fail(QERL_ERR_NULL, "nvfp4_dequantize: packed, scales, tensor_scale and out are required");
+    if (n < 1 || k < 16 || k % 16 != 0 || ldo < k || ldo > kMaxElems || n > kMaxElems / ldo)
+        return fail(QERL_ERR_SHAPE, "nvfp4_dequantize: need n >= 1, k >= 16, k %% 16 == 0, ldo >= k "
+                    "(got n=%lld k=%lld ldo=%lld)", (long long)n, (long long)k, (long long)ldo);
+    if (((uintptr_t)packed & 7u) || !aligned16(out_bf16) || ldo % 8 != 0 || ((uintptr_t)tensor_scale & 3u))
+        return fail(QERL_ERR_ALIGN, "nvfp4_dequantize: packed must be 8-byte aligned, out 16-byte aligned with "
+                    "ldo %% 8 == 0");
+    return hip_status(qerl::launch_nvfp4_dequantize(packed, scales, tensor_scale, n, k,
+                                                    static_cast<uint16_t *>(out_bf16), ldo,
+                                                    static_cast<hipStream_t>(stream)),
+                      "nvfp4_dequantize launch");
+}
+
 static qerl_status quantize_common(const char *what, const void *w_bf16, int64_t n, int64_t k, int64_t ldw,
                                    uint8_t *packed, uint8_t *scales, float *tensor_scale,
                                    const float *tensor_scale_in, uint32_t flags, void *workspace,

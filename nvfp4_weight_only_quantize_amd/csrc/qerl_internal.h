@@ -20,6 +20,9 @@ hipError_t launch_nvfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_
 // BF16 -> MXFP4 (k % 32 == 0): packed [n, k/2], E8M0 scales [n, k/32]; no workspace
 hipError_t launch_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_t ldw, uint8_t *packed,
                                  uint8_t *scales, hipStream_t stream);
+// NVFP4 -> BF16 [n, k] (row stride ldo): e2m1 * e4m3 * s_t rounded once to BF16
+hipError_t launch_nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                   int64_t n, int64_t k, uint16_t *out, int64_t ldo, hipStream_t stream);
 
 // ---- W4A16 + LoRA ----
 struct GemmArgs {

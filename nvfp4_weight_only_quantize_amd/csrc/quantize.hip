@@ -385,4 +385,65 @@ hipError_t launch_mxfp4_quantize(const uint16_t *w, int64_t n, int64_t k, int64_
     return hipGetLastError();
 }
 
+namespace {
+
+// ---- NVFP4 -> BF16 ----
+// What an unfused update-phase forward needs before a BF16 GEMM.  One thread
+// per 16-element block: 8 code bytes and 1 scale byte in, 32 B out, coalesced
+// across the wave.  e2m1 * e4m3 is exact in float (<= 6 significant bits) and
+// its product with s_t exact in double (<= 30 bits); that value is rounded
+// once to BF16: to float with round-to-odd (24 bits >= 8 + 2 keeps the later
+// rounding correct), then to BF16 nearest-even.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double v) {
+    if (v != v) return 0x7FC0;
+    float f = (float)v;  // nearest-even
+    uint32_t b = __float_as_uint(f);
+    if ((double)f != v && (b & 0x7F800000u) != 0x7F800000u && (b & 1u) == 0)
+        b = fabs(v) > fabs((double)f) ? b + 1u : b - 1u;  // the odd neighbour on v's side
+    return f32_to_bf16_bits(__uint_as_float(b));
+}
+
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t *__restrict__ packed,
+                                                           const uint8_t *__restrict__ scales,
+                                                           const float *__restrict__ tensor_scale, int64_t n,
+                                                           int64_t k, uint16_t *__restrict__ out, int64_t ldo) {
+    const int64_t bpr = k >> 4, total = n * bpr;
+    const double st = (double)*tensor_scale;
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < total; b += stride) {
+        const int64_t row = b / bpr, col = b - row * bpr;
+        const uint2 c = *reinterpret_cast<const uint2 *>(packed + row * (k >> 1) + col * 8);
+        const double s = (double)QERL_E4M3_F32(scales[b], 0) * st;  // exact: 4 x 24 bits
+        float e[16];
+        const auto p0 = QERL_FP4_PAIR_F32(c.x, 0), p1 = QERL_FP4_PAIR_F32(c.x, 1);
+        const auto p2 = QERL_FP4_PAIR_F32(c.x, 2), p3 = QERL_FP4_PAIR_F32(c.x, 3);
+        const auto p4 = QERL_FP4_PAIR_F32(c.y, 0), p5 = QERL_FP4_PAIR_F32(c.y, 1);
+        const auto p6 = QERL_FP4_PAIR_F32(c.y, 2), p7 = QERL_FP4_PAIR_F32(c.y, 3);
+        e[0] = p0[0], e[1] = p0[1], e[2] = p1[0], e[3] = p1[1], e[4] = p2[0], e[5] = p2[1], e[6] = p3[0];
+        e[7] = p3[1], e[8] = p4[0], e[9] = p4[1], e[10] = p5[0], e[11] = p5[1], e[12] = p6[0], e[13] = p6[1];
+        e[14] = p7[0], e[15] = p7[1];
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            o[i] = (uint32_t)f64_to_bf16_rne((double)e[2 * i] * s) |
+                   ((uint32_t)f64_to_bf16_rne((double)e[2 * i + 1] * s) << 16);
+        uint4 *dst = reinterpret_cast<uint4 *>(out + row * ldo + col * 16);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_nvfp4_dequantize(const uint8_t *packed, const uint8_t *scales, const float *tensor_scale,
+                                   int64_t n, int64_t k, uint16_t *out, int64_t ldo, hipStream_t stream) {
+    const int64_t blocks16 = n * (k >> 4);
+    const int64_t want = (blocks16 + kThreads - 1) / kThreads;
+    const int64_t cap = (int64_t)num_cus() * 16;
+    const int g = (int)(want < cap ? (want < 1 ? 1 : want) : cap);
+    hipLaunchKernelGGL(dequant_kernel, dim3(g), dim3(kThreads), 0, stream, packed, scales, tensor_scale, n, k, out,
+                       ldo);
+    return hipGetLastError();
+}
+
 }  // namespace qerl

@@ -255,3 +255,16 @@ def test_backward_argument_errors(kw, status):
 def test_backward_workspace_query():
     assert q.w4a16_lora_backward_workspace_size(2048, 5120, 5120, 32) >= 2 * 2048 * 32 * 4
     assert q.w4a16_lora_backward_workspace_size(0, 5120, 5120, 32) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(packed=None), 1), (dict(scales=None), 1), (dict(ts=None), 1), (dict(out=None), 1), (dict(n=0), 2),
+    (dict(k=24, ldo=24), 2), (dict(k=0, ldo=16), 2), (dict(ldo=32), 2), (dict(packed=FAKE + 4), 3),
+    (dict(out=FAKE + 8), 3), (dict(ldo=68), 3), (dict(ts=FAKE + 2), 3),
+])
+def test_dequantize_argument_errors(kw, status):
+    a = dict(packed=FAKE, scales=FAKE, ts=FAKE, n=4, k=64, out=FAKE, ldo=64, stream=None)
+    a.update(kw)
+    assert q.lib().qerl_nvfp4_dequantize(P(a["packed"]), P(a["scales"]), P(a["ts"]), a["n"], a["k"], P(a["out"]),
+                                         a["ldo"], P(a["stream"])) == status
+    assert q.lib().qerl_last_error()
