@@ -84,7 +84,7 @@ def _load():
     lib.oracle_bf16_nearest_even.restype = ctypes.c_uint16
     lib.oracle_nvfp4_dequantize.argtypes = [P, P, flt, i64, i64, P, P]
     lib.oracle_nvfp4_dequantize.restype = i32
-    lib.oracle_w4a16_lora_backward.argtypes = [P, P, i64, i64, i64, P, P, flt, P, P, i32, flt, P, P, P]
+    lib.oracle_w4a16_lora_backward.argtypes = [P, P, i64, i64, i64, P, P, flt, P, P, i32, flt, P, P, P, i32]
     lib.oracle_w4a16_lora_backward.restype = i32
     lib.oracle_w4a16_lora_gemm_f64.argtypes = lib.oracle_w4a16_lora_gemm.argtypes
     lib.oracle_w4a16_lora_gemm_f64.restype = i32
@@ -281,8 +281,9 @@ def rmsnorm(x_bits, w_eff, eps: float) -> np.ndarray:
 
 
 def w4a16_lora_backward(dy_bits, x_bits, packed, scales, s_t, lora_a_bits=None, lora_b_bits=None,
-                        lora_scale: float = 0.0):
-    """fp64 (dx [M, K], dA [r, K] or None, dB [N, r] or None) of the layer for upstream dy [M, N]."""
+                        lora_scale: float = 0.0, threads: int = 0):
+    """fp64 (dx [M, K], dA [r, K] or None, dB [N, r] or None) of the layer for upstream dy [M, N].
+    threads: worker threads over independent output rows (0: one per core)."""
     dy = np.ascontiguousarray(_bits16(dy_bits))
     x = np.ascontiguousarray(_bits16(x_bits))
     m, n = dy.shape
@@ -301,7 +302,7 @@ def w4a16_lora_backward(dy_bits, x_bits, packed, scales, s_t, lora_a_bits=None, 
     rc = _load().oracle_w4a16_lora_backward(
         _ptr(dy), _ptr(x), m, n, k, _ptr(np.ascontiguousarray(packed)), _ptr(np.ascontiguousarray(scales)),
         float(s_t), None if a is None else _ptr(a), None if b is None else _ptr(b), r, float(lora_scale),
-        _ptr(dx), None if da is None else _ptr(da), None if db is None else _ptr(db))
+        _ptr(dx), None if da is None else _ptr(da), None if db is None else _ptr(db), int(threads))
     if rc != 0:
         raise ValueError(f"oracle_w4a16_lora_backward rejected its arguments (rc={rc})")
     return dx, da, db

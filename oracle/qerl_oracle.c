@@ -541,64 +541,97 @@ int oracle_w4a16_lora_gemm_f64(const double *x, int64_t m, int64_t k, int64_t ld
  *   dB = lambda dy^T t                  [N, r]
  * (what is dequantized exactly; W itself gets no gradient, as in the pages'
  * LoRA training, [BoA-LoRA]).  Any of dx, dA, dB may be NULL.  All fp64.    */
+typedef struct {
+    const uint16_t *dy, *x; int64_t m, n, k;
+    const uint8_t *packed, *scales; double s_t;
+    const uint16_t *a, *b; int r; double lam;
+    double *t, *g, *dx, *da, *db;
+} bwd_ctx;
+
+/* t[i, :] = x[i, :] A^T and g[i, :] = dy[i, :] B for rows i in [i0, i1) */
+static void bwd_rank_rows(void *p, int64_t i0, int64_t i1) {
+    bwd_ctx *c = (bwd_ctx *)p;
+    for (int64_t i = i0; i < i1; ++i)
+        for (int j = 0; j < c->r; ++j) {
+            double at = 0.0, ag = 0.0;
+            for (int64_t kk = 0; kk < c->k; ++kk)
+                at += oracle_bf16_decode(c->x[i * c->k + kk]) * oracle_bf16_decode(c->a[(int64_t)j * c->k + kk]);
+            for (int64_t nn = 0; nn < c->n; ++nn)
+                ag += oracle_bf16_decode(c->dy[i * c->n + nn]) * oracle_bf16_decode(c->b[nn * c->r + j]);
+            c->t[i * c->r + j] = at;
+            c->g[i * c->r + j] = ag;
+        }
+}
+
+/* dx rows [i0, i1): the sum over nn in ascending order, then the LoRA term */
+static void bwd_dx_rows(void *p, int64_t i0, int64_t i1) {
+    bwd_ctx *c = (bwd_ctx *)p;
+    const int64_t k = c->k;
+    double *wrow = (double *)malloc(sizeof(double) * (size_t)k);
+    if (!wrow) return;
+    for (int64_t i = i0; i < i1; ++i)
+        for (int64_t kk = 0; kk < k; ++kk) c->dx[i * k + kk] = 0.0;
+    for (int64_t nn = 0; nn < c->n; ++nn) {
+        for (int64_t kk = 0; kk < k; ++kk) {
+            uint8_t byte = c->packed[nn * (k / 2) + kk / 2];
+            int code = (kk & 1) ? (byte >> 4) : (byte & 15);
+            wrow[kk] = oracle_e2m1_decode(code) * oracle_e4m3_decode(c->scales[nn * (k / 16) + kk / 16]) * c->s_t;
+        }
+        for (int64_t i = i0; i < i1; ++i) {
+            const double d = oracle_bf16_decode(c->dy[i * c->n + nn]);
+            for (int64_t kk = 0; kk < k; ++kk) c->dx[i * k + kk] += d * wrow[kk];
+        }
+    }
+    for (int64_t i = i0; i < i1; ++i)
+        for (int64_t kk = 0; kk < k; ++kk) {
+            double acc = 0.0;
+            for (int j = 0; j < c->r; ++j) acc += c->g[i * c->r + j] * oracle_bf16_decode(c->a[(int64_t)j * k + kk]);
+            c->dx[i * k + kk] += c->lam * acc;
+        }
+    free(wrow);
+}
+
+/* dA columns [k0, k1) of every rank row: sums over i in ascending order */
+static void bwd_da_cols(void *p, int64_t k0, int64_t k1) {
+    bwd_ctx *c = (bwd_ctx *)p;
+    for (int j = 0; j < c->r; ++j)
+        for (int64_t kk = k0; kk < k1; ++kk) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < c->m; ++i) acc += c->g[i * c->r + j] * oracle_bf16_decode(c->x[i * c->k + kk]);
+            c->da[(int64_t)j * c->k + kk] = c->lam * acc;
+        }
+}
+
+/* dB rows [n0, n1): sums over i in ascending order */
+static void bwd_db_rows(void *p, int64_t n0, int64_t n1) {
+    bwd_ctx *c = (bwd_ctx *)p;
+    for (int64_t nn = n0; nn < n1; ++nn)
+        for (int j = 0; j < c->r; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < c->m; ++i) acc += oracle_bf16_decode(c->dy[i * c->n + nn]) * c->t[i * c->r + j];
+            c->db[nn * c->r + j] = c->lam * acc;
+        }
+}
+
 int oracle_w4a16_lora_backward(const uint16_t *dy, const uint16_t *x, int64_t m, int64_t n, int64_t k,
                                const uint8_t *packed, const uint8_t *scales, float s_t,
                                const uint16_t *lora_a, const uint16_t *lora_b, int r, float lora_scale,
-                               double *dx, double *da, double *db) {
+                               double *dx, double *da, double *db, int threads) {
     if (!dy || !x || !packed || !scales || m <= 0 || n <= 0 || k <= 0 || k % 16 || r < 0) return -1;
     if (r > 0 && (!lora_a || !lora_b)) return -1;
-    const double lam = (double)lora_scale;
     double *t = (double *)calloc((size_t)(m * (r > 0 ? r : 1)), sizeof(double));
     double *g = (double *)calloc((size_t)(m * (r > 0 ? r : 1)), sizeof(double));
-    double *wrow = (double *)malloc(sizeof(double) * (size_t)k);
-    if (!t || !g || !wrow) { free(t); free(g); free(wrow); return -2; }
-    for (int64_t i = 0; i < m; ++i)
-        for (int j = 0; j < r; ++j) {
-            double at = 0.0, ag = 0.0;
-            for (int64_t kk = 0; kk < k; ++kk)
-                at += oracle_bf16_decode(x[i * k + kk]) * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
-            for (int64_t nn = 0; nn < n; ++nn)
-                ag += oracle_bf16_decode(dy[i * n + nn]) * oracle_bf16_decode(lora_b[nn * r + j]);
-            t[i * r + j] = at;
-            g[i * r + j] = ag;
-        }
-    if (dx) {
-        for (int64_t i = 0; i < m * k; ++i) dx[i] = 0.0;
-        for (int64_t nn = 0; nn < n; ++nn) {
-            for (int64_t kk = 0; kk < k; ++kk) {
-                uint8_t byte = packed[nn * (k / 2) + kk / 2];
-                int code = (kk & 1) ? (byte >> 4) : (byte & 15);
-                wrow[kk] = oracle_e2m1_decode(code) * oracle_e4m3_decode(scales[nn * (k / 16) + kk / 16]) * (double)s_t;
-            }
-            for (int64_t i = 0; i < m; ++i) {
-                const double d = oracle_bf16_decode(dy[i * n + nn]);
-                for (int64_t kk = 0; kk < k; ++kk) dx[i * k + kk] += d * wrow[kk];
-            }
-        }
-        for (int64_t i = 0; i < m; ++i)
-            for (int64_t kk = 0; kk < k; ++kk) {
-                double acc = 0.0;
-                for (int j = 0; j < r; ++j) acc += g[i * r + j] * oracle_bf16_decode(lora_a[(int64_t)j * k + kk]);
-                dx[i * k + kk] += lam * acc;
-            }
-    }
-    if (da)
-        for (int j = 0; j < r; ++j)
-            for (int64_t kk = 0; kk < k; ++kk) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < m; ++i) acc += g[i * r + j] * oracle_bf16_decode(x[i * k + kk]);
-                da[(int64_t)j * k + kk] = lam * acc;
-            }
-    if (db)
-        for (int64_t nn = 0; nn < n; ++nn)
-            for (int j = 0; j < r; ++j) {
-                double acc = 0.0;
-                for (int64_t i = 0; i < m; ++i) acc += oracle_bf16_decode(dy[i * n + nn]) * t[i * r + j];
-                db[nn * r + j] = lam * acc;
-            }
+    if (!t || !g) { free(t); free(g); return -2; }
+    bwd_ctx c = {dy, x, m, n, k, packed, scales, (double)s_t, lora_a, lora_b, r, (double)lora_scale,
+                 t, g, dx, da, db};
+    /* each stage splits its independent output rows (or columns) over the
+     * threads; every sum runs in the order the definition writes it */
+    if (r > 0) parallel_range(threads, m, bwd_rank_rows, &c);
+    if (dx) parallel_range(threads, m, bwd_dx_rows, &c);
+    if (da && r > 0) parallel_range(threads, k, bwd_da_cols, &c);
+    if (db && r > 0) parallel_range(threads, n, bwd_db_rows, &c);
     free(t);
     free(g);
-    free(wrow);
     return 0;
 }
 
