@@ -363,9 +363,43 @@ qerl_status qerl_aqn_noisy_weight(const float *weight, int64_t h, float sigma, u
 /* ----------------------------------------------------------------------- */
 /* Static English text for a status code. */
 const char *qerl_status_string(qerl_status status);
-/* Text of the last error on the calling thread ("" if none); valid until the
- * next library call on that thread. */
+/* Text of the last error on the calling thread ("" if none): the argument
+ * check that failed, or the HIP runtime's message for QERL_ERR_HIP; valid
+ * until the next library call on that thread. */
 const char *qerl_last_error(void);
+/* The same text (thread-local); the name the boundary's error convention
+ * uses for launch failures. */
+const char *qerl_last_hip_error(void);
+
+/*
+ * Workspace health of qerl_w4a16_lora_gemm / _multi / qerl_rmsnorm_..._multi.
+ * The decode kernels reduce split-K partials and wait for the LoRA
+ * down-projection through counters in the workspace's first 256 KiB, which
+ * every call leaves zero; a wait inside the kernel is bounded, and one that
+ * gives up writes its row block's outputs as NaN and sets an error word
+ * there.
+ *
+ * qerl_gemm_workspace_check: synchronizes `stream` (every call enqueued on it
+ *   is finished), copies the counter head to the host and returns QERL_OK if
+ *   it is all zero; QERL_ERR_HIP if a bounded wait gave up since the last
+ *   reset; QERL_ERR_WORKSPACE if a counter is not zero (a call did not
+ *   finish, or the workspace was not zero-filled before first use).  The
+ *   text says which, in qerl_last_error().  A diagnostic: it blocks the host.
+ * qerl_gemm_workspace_reset: enqueues, on `stream`, a kernel that zeroes the
+ *   counter head (no memset node, so it may be captured in a graph).
+ * Both need workspace_bytes >= 256 KiB; reset needs a 16-byte aligned pointer.
+ */
+qerl_status qerl_gemm_workspace_check(const void *workspace, size_t workspace_bytes, void *stream);
+qerl_status qerl_gemm_workspace_reset(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test hook, process-wide: while enable != 0, the bounded waits of the decode
+ * kernels (m <= 16 with LoRA or the fused norm) wait for a count that is never
+ * reached and give up after one poll, so the failure report above can be
+ * tested while every kernel still exits normally.  Launches made after the
+ * call see the setting.  Not for production use.
+ */
+void qerl_debug_force_wait_timeout(int enable);
 
 #ifdef __cplusplus
 }

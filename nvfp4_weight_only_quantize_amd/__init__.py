@@ -92,6 +92,14 @@ def lib() -> ctypes.CDLL:
     L.qerl_status_string.restype = ctypes.c_char_p
     L.qerl_last_error.argtypes = []
     L.qerl_last_error.restype = ctypes.c_char_p
+    L.qerl_last_hip_error.argtypes = []
+    L.qerl_last_hip_error.restype = ctypes.c_char_p
+    L.qerl_gemm_workspace_check.argtypes = [P, sz, P]
+    L.qerl_gemm_workspace_check.restype = ctypes.c_int
+    L.qerl_gemm_workspace_reset.argtypes = [P, sz, P]
+    L.qerl_gemm_workspace_reset.restype = ctypes.c_int
+    L.qerl_debug_force_wait_timeout.argtypes = [ctypes.c_int]
+    L.qerl_debug_force_wait_timeout.restype = None
     _lib = L
     return L
 
@@ -145,6 +153,19 @@ class NVFP4Weight:
     @property
     def nbytes(self) -> int:
         return self.packed.numel() + self.scales.numel() + 4
+
+
+def _need_wq(wq: NVFP4Weight, device):
+    """An NVFP4 weight the kernels can read: contiguous uint8 packed [N, K/2]
+    and scales [N, K/16] and one FP32 tensor scale, on `device`."""
+    _need(wq.packed, "packed", torch.uint8, 2, device)
+    _need(wq.scales, "scales", torch.uint8, 2, device)
+    _need(wq.tensor_scale, "tensor_scale", torch.float32, None, device)
+    n, k = wq.shape
+    if tuple(wq.scales.shape) != (n, k // 16) or wq.tensor_scale.numel() != 1:
+        raise ValueError("NVFP4 weight: scales must be [N, K/16] and tensor_scale one element")
+    if not (wq.packed.is_contiguous() and wq.scales.is_contiguous()):
+        raise ValueError("NVFP4 weight: packed and scales must be contiguous")
 
 
 # --------------------------------------------------------------- quantizer --
@@ -203,6 +224,7 @@ def nvfp4_dequantize(wq: NVFP4Weight, out: torch.Tensor | None = None, stream=No
     """BF16 [N, K] = e2m1 x e4m3 x s_t of an NVFP4 weight, rounded once to BF16."""
     n, k = wq.shape
     dev = wq.packed.device
+    _need_wq(wq, dev)
     if out is None:
         out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, 2)
@@ -230,6 +252,7 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     m, k = x.shape
+    _need_wq(wq, dev)
     n, kw = wq.shape
     if kw != k:
         raise ValueError(f"x has K={k} but the weight has K={kw}")
@@ -259,6 +282,25 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
     return out
 
 
+def gemm_workspace_check(workspace: torch.Tensor, stream=None) -> None:
+    """Synchronize the stream and raise QerlError unless the GEMM workspace's
+    counter head is all zero (a bounded wait in the decode kernel gave up, or
+    a call on it did not finish)."""
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib().qerl_gemm_workspace_check(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
+
+
+def gemm_workspace_reset(workspace: torch.Tensor, stream=None) -> None:
+    """Zero the GEMM workspace's counter head (a kernel on the stream)."""
+    _need(workspace, "workspace", torch.uint8, 1)
+    _check(lib().qerl_gemm_workspace_reset(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
+
+
+def _debug_force_wait_timeout(enable: bool) -> None:
+    """Test hook: make every bounded wait of the decode kernels give up."""
+    lib().qerl_debug_force_wait_timeout(1 if enable else 0)
+
+
 class GemmSegment(ctypes.Structure):
     """qerl_gemm_segment of include/qerl.h."""
     _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("tensor_scale", ctypes.c_void_p),
@@ -276,6 +318,7 @@ def _segments(x, segments, outs):
     m, k = x.shape
     arr = (GemmSegment * len(segments))()
     for i, ((wq, a, b, lam), out) in enumerate(zip(segments, outs)):
+        _need_wq(wq, dev)
         n, kw = wq.shape
         if kw != k:
             raise ValueError(f"segment {i}: x has K={k} but the weight has K={kw}")
@@ -371,6 +414,7 @@ def w4a16_lora_backward(dy: torch.Tensor, x: torch.Tensor, wq: NVFP4Weight, lora
     _need(x, "x", torch.bfloat16, 2, dev)
     m, n = dy.shape
     k = x.shape[1]
+    _need_wq(wq, dev)
     if x.shape[0] != m or tuple(wq.shape) != (n, k):
         raise ValueError("dy [M, N], x [M, K] and the weight [N, K] must agree")
     r = 0
@@ -380,6 +424,9 @@ def w4a16_lora_backward(dy: torch.Tensor, x: torch.Tensor, wq: NVFP4Weight, lora
         r = lora_a.size(0)
         if tuple(lora_a.shape) != (r, k) or tuple(lora_b.shape) != (n, r):
             raise ValueError("LoRA must be A [r, K] and B [N, r]")
+        # the kernels index A and B with row strides K and r
+        if not (lora_a.is_contiguous() and lora_b.is_contiguous()):
+            raise ValueError("LoRA matrices must be contiguous")
     dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev) if want_dx else None
     da = torch.empty((r, k), dtype=torch.float32, device=dev) if (want_lora and r) else None
     db = torch.empty((n, r), dtype=torch.float32, device=dev) if (want_lora and r) else None

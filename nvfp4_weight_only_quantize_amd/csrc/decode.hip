@@ -74,7 +74,7 @@ constexpr int64_t kProdChunks = 4;        // K chunks per LoRA producer
 constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
-constexpr uint32_t kSpinLimit = 1u << 20;
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls of the bounded wait for t (2^20 x s_sleep 2)
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
 constexpr int64_t kUnitMinChunks = 8;        // 16 < m: K chunks per unit the split may go down to
 constexpr int64_t kDirectMaxKr = 8;          // m <= 16: most producer K ranges the epilogue sums itself
@@ -84,8 +84,11 @@ constexpr int64_t kDirectMaxCps = 12;        // ... in units of at most this man
 #endif
 constexpr int kRing = QERL_RING;  // weight chunks in flight per wave (m <= 16)
 
-// counter words at the head of the workspace
-constexpr int kCtrProd = 0, kCtrTReady = 1, kCtrDone = 2, kCtrRow = 4;
+// counter words at the head of the workspace; kCtrErr is the segment's error
+// word (kGemmErrWaitTimeout when a bounded wait gave up), read by
+// gemm_workspace_check and cleared by gemm_workspace_reset
+constexpr int kCtrProd = 0, kCtrTReady = 1, kCtrDone = 2, kCtrErr = kGemmCtrErrWord, kCtrRow = 4;
+static_assert(kCtrErr == 3, "the error word sits between the fixed counters and the row counters");
 constexpr int64_t kMaxRowBlocks = kSegCtrBytes / 4 - kCtrRow;
 
 struct DecodePlan {
@@ -107,6 +110,10 @@ struct DecodePlan {
     // m <= 16 with few producer K ranges (and r <= 64): the epilogue sums the
     // producers' partial tiles itself, so t costs no last-producer stage
     bool direct;
+    // the bounded wait for t: polls before giving up, and a count added to
+    // the value waited for (nonzero only when the host forces every such wait
+    // to give up, to test that failure is reported)
+    uint32_t spin_limit, wait_bias;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -142,6 +149,8 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.prod_kr = (p.chunks + kProdChunks - 1) / kProdChunks;
     p.prod_groups = p.mt * ((p.jt + kProdTiles - 1) / kProdTiles);
     p.norm = norm && p.mt == 1;
+    p.spin_limit = g_force_wait_timeout ? 1u : kSpinLimit;
+    p.wait_bias = g_force_wait_timeout ? 1u : 0u;
     if (p.norm && p.prod_groups < 1) p.prod_groups = 1;  // sums of squares only
     p.producers = (r > 0 || p.norm) ? p.prod_kr * p.prod_groups : 0;
     // slices: as many units as compute units without going over (a CU that
@@ -753,7 +762,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     // (direct: ready once every producer has counted; else the ready flag)
     const bool direct = wait_t && p.direct;
     uint32_t *ready_ctr = d.ctr() + (direct ? kCtrProd : kCtrTReady);
-    const uint32_t ready_at = direct ? (uint32_t)p.producers : 1u;
+    const uint32_t ready_at = (direct ? (uint32_t)p.producers : 1u) + p.wait_bias;
     if (wait_t && tid == 0) t_seen = ctr_load(ready_ctr) >= ready_at;
 #pragma unroll
     for (int s = 0; s < DR; ++s)
@@ -789,7 +798,7 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     if (lora)
 #pragma unroll
         for (int g = 0; g < NW; ++g) b0[g] = load_b(g, 0);
-    __shared__ uint32_t s_flag, s_ready;
+    __shared__ uint32_t s_flag, s_ready, s_timeout;
     // ---- split K: the last unit of the row block to arrive sums the slices ----
     if (SPLIT) {
         {
@@ -807,12 +816,19 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
         if (tid == 0) s_ready = t_seen;
         __syncthreads();
     }
+    // A wait that gives up leaves t (or 1 / rms) unknown: the row block's
+    // outputs are written as NaN and the segment's error word is set, which
+    // gemm_workspace_check reports.
+    bool timed_out = false;
     if (wait_t && !s_ready) {  // uniform; rare: wait for the last producer
         if (tid == 0) {
             uint32_t it = 0;
-            while (ctr_load(ready_ctr) < ready_at && ++it < kSpinLimit) __builtin_amdgcn_s_sleep(2);
+            while (ctr_load(ready_ctr) < ready_at && ++it < p.spin_limit) __builtin_amdgcn_s_sleep(2);
+            s_timeout = ctr_load(ready_ctr) < ready_at;
+            if (s_timeout) ctr_store(d.ctr() + kCtrErr, kGemmErrWaitTimeout);
         }
         __syncthreads();
+        timed_out = s_timeout;
     }
     // The slices' partial tiles and t16 are loaded together (one round trip
     // in the usual case; more than kRedP slices take more), then summed in
@@ -958,7 +974,8 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
                 const int64_t m = 16 * mt + 4 * lq + v;
                 const int64_t n = n0 + 16 * g + lr;
                 const float base = NORM ? st * s_inv[m] * acc[mt][g][v] : st * acc[mt][g][v];
-                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(base + lam * l[v]);
+                if (m < a.m && n < a.n)
+                    a.y[m * a.ldy + n] = timed_out ? (uint16_t)0x7FC0 : f32_to_bf16_bits(base + lam * l[v]);
             }
         }
     }
@@ -1233,7 +1250,21 @@ hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
     return launch_checked(ds, lds, lora, stream);
 }
 
+// the counter head of a GEMM workspace to zero, 16 bytes per thread
+__global__ __launch_bounds__(256) void zero_head_kernel(uint4 *head) {
+    head[(int64_t)blockIdx.x * 256 + threadIdx.x] = make_uint4(0, 0, 0, 0);
+}
+static_assert(kGemmCtrBytes % (256 * 16) == 0, "whole workgroups of 16-byte stores");
+
 }  // namespace
+
+std::atomic<int> g_force_wait_timeout{0};
+
+hipError_t launch_gemm_workspace_reset(void *workspace, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_head_kernel, dim3((unsigned)(kGemmCtrBytes / (256 * 16))), dim3(256), 0, stream,
+                       static_cast<uint4 *>(workspace));
+    return hipGetLastError();
+}
 
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
     return (size_t)(kGemmCtrBytes + make_decode_plan(m, n, k, r).bytes);

@@ -268,3 +268,15 @@ def test_dequantize_argument_errors(kw, status):
     assert q.lib().qerl_nvfp4_dequantize(P(a["packed"]), P(a["scales"]), P(a["ts"]), a["n"], a["k"], P(a["out"]),
                                          a["ldo"], P(a["stream"])) == status
     assert q.lib().qerl_last_error()
+
+
+def test_workspace_check_and_reset_argument_errors():
+    L = q.lib()
+    assert L.qerl_gemm_workspace_check(None, 1 << 20, None) == 1
+    assert L.qerl_gemm_workspace_reset(None, 1 << 20, None) == 1
+    # smaller than the 256 KiB counter head (checked before any device access)
+    assert L.qerl_gemm_workspace_check(ctypes.c_void_p(256), 1024, None) == 5
+    assert L.qerl_gemm_workspace_reset(ctypes.c_void_p(256), (256 << 10) - 1, None) == 5
+    assert L.qerl_last_error()
+    assert L.qerl_gemm_workspace_reset(ctypes.c_void_p(264), 256 << 10, None) == 3
+    assert L.qerl_last_hip_error() == L.qerl_last_error()

@@ -44,7 +44,7 @@ def _check(m, n, k, r, seed, lam=2.0, strided=False):
     bg = None if b is None else bits_to_gpu(b)
     dx, da, db = q.w4a16_lora_backward(dyg, xg, wq, ag, bg, lam)
     torch.cuda.synchronize()
-    rdx, rda, rdb = oracle.w4a16_lora_backward(dy, x, packed, scales, s_t, a, b, lam)
+    rdx, rda, rdb = oracle.w4a16_lora_backward(dy, x, packed, scales, s_t, a, b, lam, threads=16)
     what = f"m={m} n={n} k={k} r={r}"
     assert_gemm_close(bf16_to_f64(dx), rdx, "dx " + what)
     if r:
@@ -72,3 +72,31 @@ def test_backward_strided_inputs():
 def test_backward_7b_projection(proj):
     n, k = synth.QWEN25_7B[proj]
     _check(64, n, k, 32, seed=5200 + n)
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "gate", "down"])
+def test_backward_7b_bench_shapes(proj):
+    # the backward leg's shapes (M = 2048 tokens, r = 32), dx, dA and dB in
+    # full: 16 row blocks of dx, four M chunks of the rank products, and the
+    # widest N (gate, 18944) and K (down, 18944) of the layer
+    n, k = synth.QWEN25_7B[proj]
+    _check(2048, n, k, 32, seed=5300 + n + k)
+
+
+def test_backward_many_m_chunks_ragged():
+    # m = 1100: three M chunks of the rank products (the last one partial) and
+    # nine dx row blocks, the last one ragged (7B k/v projection)
+    n, k = synth.QWEN25_7B["k"]
+    _check(1100, n, k, 32, seed=5400)
+
+
+def test_backward_rejects_non_contiguous_lora():
+    n, k, r, m = 64, 256, 16, 8
+    dy, x, packed, scales, s_t, a, b, wq = _case(m, n, k, r, seed=5500)
+    ag, bg = bits_to_gpu(a), bits_to_gpu(b)
+    a_view = ag.t().contiguous().t()  # [r, k] with strides (1, r)
+    b_view = bg.t().contiguous().t()
+    with pytest.raises(ValueError):
+        q.w4a16_lora_backward(bits_to_gpu(dy), bits_to_gpu(x), wq, a_view, bg, 2.0)
+    with pytest.raises(ValueError):
+        q.w4a16_lora_backward(bits_to_gpu(dy), bits_to_gpu(x), wq, ag, b_view, 2.0)
