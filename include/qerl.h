@@ -174,19 +174,14 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
  *   lora_a_bf16   [r, k] contiguous; lora_b_bf16 [n, r] contiguous; both may be
  *                 NULL only when r == 0 (no LoRA)
  *   y_bf16        [m, n], row stride ldy >= n; must not overlap any input
- *   workspace     device memory of at least the size query; its first 256
- *                 KiB hold counters (64 KiB per projection of a multi call,
- *                 the same places for every call) that must be zero before the
- *                 first call that uses this workspace (e.g. allocate it
- *                 zero-filled).  Every call leaves them zero, so one workspace
- *                 serves any sequence of calls -- qerl_w4a16_lora_gemm and
- *                 qerl_w4a16_lora_gemm_multi, any shapes -- on one stream;
- *                 calls that overlap in time must not share a workspace.
- * m <= 64 takes the decode path: one launch that streams the packed weights
- * once (E2M1/E4M3 decode in registers, BF16 MFMA), reduces split-K partials
- * in the last workgroup of each row block and adds the LoRA term there; larger
- * m takes a BF16-MFMA path on dequantized tiles with the LoRA product folded
- * into the same accumulation.
+ *   workspace     device memory of at least the size query (partial sums;
+ *                 no state is kept between calls, nothing needs to be zero);
+ *                 calls that overlap in time must not share a workspace
+ * m <= 64 takes the decode path: a launch that streams the packed weights
+ * once (E2M1/E4M3 decode in registers, BF16 MFMA) and stores partial sums,
+ * and a small launch that adds them in a fixed order with the LoRA term;
+ * larger m takes a BF16-MFMA path on dequantized tiles with the LoRA product
+ * folded into the same accumulation.
  * Requires m, n >= 1, k >= 16, k % 16 == 0, 0 <= r <= QERL_MAX_LORA_RANK,
  * finite lora_scale, workspace_bytes >= the size query.
  */
@@ -227,14 +222,12 @@ size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qer
  * and output.  The operation is the layer of qerl_w4a16_lora_gemm (README
  * "Acknowledgement"; bitsofall "LoRA (Low-Rank Adaptation)"), applied to the
  * projections that read one normed input (q/k/v, gate/up).  For m <= 64 the
- * segments share one launch (so a decode step spends one launch, not one per
- * projection, on them); the K split is chosen for all segments together, so
+ * segments share the launches (so a decode step spends two launches, not two
+ * per projection, on them); the K split is chosen for all segments together, so
  * the FP32 summation order, and with it the last bit of y, can differ from
  * separate calls.  Larger m runs the segments one after another.
  *   segs          host array of nseg segments, read during the call only
- *   workspace     as for qerl_w4a16_lora_gemm (the same 256 KiB counter
- *                 head, zero before the first use; every call leaves it zero),
- *                 of at least the size query
+ *   workspace     as for qerl_w4a16_lora_gemm, of at least the size query
  * Requires the conditions of qerl_w4a16_lora_gemm for every segment, outputs
  * that overlap neither each other nor any input.
  */
@@ -256,17 +249,17 @@ size_t qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, c
  * "Summary"), one vector per (seed, step, layer), so norm_weight is the
  * vector qerl_aqn_noisy_weight returns for the current noise stage (or the
  * plain weight for sigma = 0), drawn once per step rather than once per call.
- * For m <= 16 and k % 32 == 0 the norm runs inside the decode launch: each row's
- * 1 / rms is a factor of its whole output row, so the product takes
- * bf16(x * norm_weight) and the FP32 result is scaled by 1 / rms in the
- * epilogue (the LoRA term likewise).  Otherwise the norm is a launch of its
+ * For m <= 16 and k % 32 == 0 the norm runs inside the decode launches: each
+ * row's 1 / rms is a factor of its whole output row, so the product takes
+ * bf16(x * norm_weight) and the FP32 result is scaled by 1 / rms at the end
+ * (the LoRA term likewise).  Otherwise the norm is a launch of its
  * own writing BF16 xn (as qerl_aqn_rmsnorm's y_bf16) into the workspace,
  * followed by qerl_w4a16_lora_gemm_multi on it.  The two roundings differ in
  * the last bits of y, within the GEMM's tolerance.
  *   x_bf16        [m, k] (row stride ldx): the norm's input
  *   norm_weight   FP32 [k], 16-byte aligned
- *   segs, workspace as for qerl_w4a16_lora_gemm_multi (the same 256 KiB
- *                 counter head), workspace of at least the size query
+ *   segs, workspace as for qerl_w4a16_lora_gemm_multi, workspace of at least
+ *                 the size query
  * Requires the conditions of qerl_w4a16_lora_gemm_multi, k <=
  * QERL_MAX_NORM_WIDTH, eps > 0 and finite.
  */
@@ -367,39 +360,9 @@ const char *qerl_status_string(qerl_status status);
  * check that failed, or the HIP runtime's message for QERL_ERR_HIP; valid
  * until the next library call on that thread. */
 const char *qerl_last_error(void);
-/* The same text (thread-local); the name the boundary's error convention
- * uses for launch failures. */
+/* The same text (thread-local), under the name the boundary's error
+ * convention gives launch failures. */
 const char *qerl_last_hip_error(void);
-
-/*
- * Workspace health of qerl_w4a16_lora_gemm / _multi / qerl_rmsnorm_..._multi.
- * The decode kernels reduce split-K partials and wait for the LoRA
- * down-projection through counters in the workspace's first 256 KiB, which
- * every call leaves zero; a wait inside the kernel is bounded, and one that
- * gives up writes its row block's outputs as NaN and sets an error word
- * there.
- *
- * qerl_gemm_workspace_check: synchronizes `stream` (every call enqueued on it
- *   is finished), copies the counter head to the host and returns QERL_OK if
- *   it is all zero; QERL_ERR_HIP if a bounded wait gave up since the last
- *   reset; QERL_ERR_WORKSPACE if a counter is not zero (a call did not
- *   finish, or the workspace was not zero-filled before first use).  The
- *   text says which, in qerl_last_error().  A diagnostic: it blocks the host.
- * qerl_gemm_workspace_reset: enqueues, on `stream`, a kernel that zeroes the
- *   counter head (no memset node, so it may be captured in a graph).
- * Both need workspace_bytes >= 256 KiB; reset needs a 16-byte aligned pointer.
- */
-qerl_status qerl_gemm_workspace_check(const void *workspace, size_t workspace_bytes, void *stream);
-qerl_status qerl_gemm_workspace_reset(void *workspace, size_t workspace_bytes, void *stream);
-
-/*
- * Test hook, process-wide: while enable != 0, the bounded waits of the decode
- * kernels (m <= 16 with LoRA or the fused norm) wait for a count that is never
- * reached and give up after one poll, so the failure report above can be
- * tested while every kernel still exits normally.  Launches made after the
- * call see the setting.  Not for production use.
- */
-void qerl_debug_force_wait_timeout(int enable);
 
 #ifdef __cplusplus
 }

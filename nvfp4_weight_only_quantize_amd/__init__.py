@@ -94,12 +94,6 @@ def lib() -> ctypes.CDLL:
     L.qerl_last_error.restype = ctypes.c_char_p
     L.qerl_last_hip_error.argtypes = []
     L.qerl_last_hip_error.restype = ctypes.c_char_p
-    L.qerl_gemm_workspace_check.argtypes = [P, sz, P]
-    L.qerl_gemm_workspace_check.restype = ctypes.c_int
-    L.qerl_gemm_workspace_reset.argtypes = [P, sz, P]
-    L.qerl_gemm_workspace_reset.restype = ctypes.c_int
-    L.qerl_debug_force_wait_timeout.argtypes = [ctypes.c_int]
-    L.qerl_debug_force_wait_timeout.restype = None
     _lib = L
     return L
 
@@ -246,9 +240,9 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
                     stream=None) -> torch.Tensor:
     """y [M, N] (BF16) = x [M, K] deq(W)^T + lora_scale (x A^T) B^T.
 
-    A caller-provided ``workspace`` must be zero-filled before its first use
-    (e.g. ``torch.zeros``); every call leaves its counter region zero again, so
-    one workspace serves any sequence of calls on one stream."""
+    A caller-provided ``workspace`` (uint8, at least the size query) holds
+    partial sums only: any contents, reusable by any sequence of calls on one
+    stream."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     m, k = x.shape
@@ -272,33 +266,13 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
         raise ValueError("out must be [M, N]")
     need = w4a16_lora_gemm_workspace_size(m, n, k, r)
     if workspace is None and need > 0:
-        # its head holds counters that must start at zero (each call leaves them zero)
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qerl_w4a16_lora_gemm(
         _ptr(x), m, k, _rows(x, "x"), _ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n,
         _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out), _rows(out, "out"),
         _ptr(workspace), ws_bytes, _stream(stream, dev)))
     return out
-
-
-def gemm_workspace_check(workspace: torch.Tensor, stream=None) -> None:
-    """Synchronize the stream and raise QerlError unless the GEMM workspace's
-    counter head is all zero (a bounded wait in the decode kernel gave up, or
-    a call on it did not finish)."""
-    _need(workspace, "workspace", torch.uint8, 1)
-    _check(lib().qerl_gemm_workspace_check(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
-
-
-def gemm_workspace_reset(workspace: torch.Tensor, stream=None) -> None:
-    """Zero the GEMM workspace's counter head (a kernel on the stream)."""
-    _need(workspace, "workspace", torch.uint8, 1)
-    _check(lib().qerl_gemm_workspace_reset(_ptr(workspace), workspace.numel(), _stream(stream, workspace.device)))
-
-
-def _debug_force_wait_timeout(enable: bool) -> None:
-    """Test hook: make every bounded wait of the decode kernels give up."""
-    lib().qerl_debug_force_wait_timeout(1 if enable else 0)
 
 
 class GemmSegment(ctypes.Structure):
@@ -360,7 +334,7 @@ def w4a16_lora_gemm_multi(x: torch.Tensor, segments, outs=None, workspace: torch
     arr = _segments(x, segments, outs)
     need = int(lib().qerl_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(segments)))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qerl_w4a16_lora_gemm_multi(_ptr(x), m, k, _rows(x, "x"), arr, len(segments), _ptr(workspace),
                                             ws_bytes, _stream(stream, dev)))
@@ -393,7 +367,7 @@ def rmsnorm_w4a16_lora_gemm_multi(x: torch.Tensor, norm_weight: torch.Tensor, ep
     arr = _segments(x, segments, outs)
     need = int(lib().qerl_rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, k, arr, len(segments)))
     if workspace is None and need > 0:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().qerl_rmsnorm_w4a16_lora_gemm_multi(_ptr(x), m, k, _rows(x, "x"), _ptr(norm_weight), float(eps), arr,
                                                     len(segments), _ptr(workspace), ws_bytes, _stream(stream, dev)))

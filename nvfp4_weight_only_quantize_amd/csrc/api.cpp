@@ -57,60 +57,6 @@ const char *qerl_last_error(void) { return g_last_error; }
 
 const char *qerl_last_hip_error(void) { return g_last_error; }
 
-void qerl_debug_force_wait_timeout(int enable) { qerl::g_force_wait_timeout = enable ? 1 : 0; }
-
-qerl_status qerl_gemm_workspace_check(const void *workspace, size_t workspace_bytes, void *stream) {
-    g_last_error[0] = '\0';
-    if (!workspace) return fail(QERL_ERR_NULL, "gemm_workspace_check: workspace is required");
-    if (workspace_bytes < (size_t)qerl::kGemmCtrBytes)
-        return fail(QERL_ERR_WORKSPACE, "gemm_workspace_check: a GEMM workspace holds at least %lld bytes",
-                    (long long)qerl::kGemmCtrBytes);
-    static_assert(qerl::kGemmCtrBytes % 4 == 0, "whole words");
-    const size_t words = (size_t)qerl::kGemmCtrBytes / 4;
-    uint32_t *head = static_cast<uint32_t *>(malloc((size_t)qerl::kGemmCtrBytes));
-    if (!head) return fail(QERL_ERR_HIP, "gemm_workspace_check: no host memory for the counter head");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(head, workspace, (size_t)qerl::kGemmCtrBytes, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e != hipSuccess) {
-        free(head);
-        return hip_status(e, "gemm_workspace_check: reading the counter head");
-    }
-    const size_t seg_words = (size_t)qerl::kSegCtrBytes / 4;
-    int timeouts = 0;
-    size_t busy = 0, first_busy = words;
-    for (size_t i = 0; i < words; ++i) {
-        if (!head[i]) continue;
-        if (i % seg_words == (size_t)qerl::kGemmCtrErrWord) {
-            ++timeouts;
-        } else {
-            ++busy;
-            if (first_busy == words) first_busy = i;
-        }
-    }
-    free(head);
-    if (timeouts)
-        return fail(QERL_ERR_HIP, "gemm_workspace_check: a bounded wait in the decode kernel gave up in %d "
-                    "segment(s); the affected outputs were written as NaN (clear with qerl_gemm_workspace_reset)",
-                    timeouts);
-    if (busy)
-        return fail(QERL_ERR_WORKSPACE, "gemm_workspace_check: %zu counter word(s) are not zero (first: word %zu); "
-                    "a call on this workspace did not finish, or it was not zero-filled before first use "
-                    "(clear with qerl_gemm_workspace_reset)", busy, first_busy);
-    return QERL_OK;
-}
-
-qerl_status qerl_gemm_workspace_reset(void *workspace, size_t workspace_bytes, void *stream) {
-    g_last_error[0] = '\0';
-    if (!workspace) return fail(QERL_ERR_NULL, "gemm_workspace_reset: workspace is required");
-    if (workspace_bytes < (size_t)qerl::kGemmCtrBytes)
-        return fail(QERL_ERR_WORKSPACE, "gemm_workspace_reset: a GEMM workspace holds at least %lld bytes",
-                    (long long)qerl::kGemmCtrBytes);
-    if (!aligned16(workspace)) return fail(QERL_ERR_ALIGN, "gemm_workspace_reset: workspace must be 16-byte aligned");
-    return hip_status(qerl::launch_gemm_workspace_reset(workspace, static_cast<hipStream_t>(stream)),
-                      "gemm_workspace_reset launch");
-}
-
 size_t qerl_nvfp4_quantize_workspace_size(int64_t n, int64_t k) {
     return qerl::quantize_workspace_bytes(n, k);
 }

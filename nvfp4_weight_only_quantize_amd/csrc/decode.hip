@@ -10,48 +10,30 @@
 //
 // Decode is bound by the bytes of the packed weights (0.5625 B per weight),
 // which are read exactly once.  Weights are decoded to exact BF16 (e2m1 *
-// e4m3 has <= 6 significant bits) and multiplied on the 16x16x32 BF16 MFMA in
-// FP32; K is permuted inside each 128-element chunk, identically for both
-// operands, so that one 16-byte load gives a lane the packed bytes of four
-// MFMA steps.
+// e4m3 has <= 6 significant bits) and multiplied on the BF16 MFMA in FP32.
 //
-// m <= 16, stream_kernel, one launch per call.  Work units are (64 weight
-// rows) x (slice of K); each of the 4 waves of a unit owns 16 rows.
-//  * The unit's x slice and E4M3 scales are staged into LDS once with batched
-//    wide loads; the weights stream in 128-element chunks (64 packed bytes per
-//    row) through a ring of DR chunks per wave, with no barrier.  Every load
-//    of the steady state is unconditional, which keeps the compiler's
-//    in-order wait counts exact; LDS reads are counted apart from them.
-//  * LoRA: "producer" workgroups at the head of the grid compute partial sums
-//    of t = x A^T over slices of K (MFMA) and publish them with device-coherent
-//    stores; the last producer to finish sums them in producer order and
-//    publishes t once, as BF16 hi + lo halves (relative error ~2^-16) in the
-//    layout the epilogue multiplies, behind a ready flag.  Short units with
-//    few producers ("direct") instead wait for the producers' count and sum
-//    their partials themselves, which takes the last-producer stage off the
-//    chain.
-//  * Every unit but the last of its row block stores its FP32 partial tile
-//    (coherent stores) and bumps a counter.  The last to arrive (every unit,
-//    when K is not split) loads all partial tiles and t in one batch -- the
-//    ready flag was read while its last chunks multiplied, so as a rule no
-//    round trip of its own is spent on t (the wait for it is bounded all the
-//    same) -- sums the partials in slice order (deterministic), and adds
-//    lora_scale * t B^T on the MFMA.
-//  * NORM (an RMSNorm of x fused in front): the units stage bf16(x * norm_w),
-//    the producers also sum x^2 per K range, and 1 / rms scales t and the
-//    output row in the epilogue (a row's 1 / rms factors out of the product).
-//  * Several projections of one x (q/k/v, gate/up) share a launch: the
-//    segment is a grid dimension; a one-segment launch is its own
-//    instantiation with a one-plan argument.
+// Two launches per call, with no counter, flag or wait between workgroups:
+//  * the main kernel: "producer" workgroups at the head of the grid compute
+//    partial sums of t = x A^T over ranges of K (and, with the fused RMSNorm,
+//    of x^2), and "units" stream a block of weight rows over a slice of K;
+//    every workgroup stores its FP32 partial tile and exits.
+//  * finish_kernel sums the producers' partial tiles (into t, K-range order)
+//    and the units' partial tiles (slice order) -- deterministic -- and writes
+//    y = bf16(inv_rms * (s_t * acc + lora_scale * t B^T)).
+// A call with a single slice, no LoRA and no norm writes y from the units.
 //
-// 16 < m <= 64, mfma_unit_kernel + finish_kernel, two launches.  Units are
-// (256 weight rows) x (slice of K) running the K loops of mfma_tile.h with all
-// of x as the x tile; every unit stores its FP32 tile and finish_kernel sums
-// them (in slice order) in parallel over the outputs; the last producer sums
-// t, which finish_kernel reads after the kernel boundary.
+// m <= 16, stream_kernel.  Units are 64 weight rows x one K slice; each of the
+// 4 waves owns 16 rows.  The unit's x slice is staged into LDS (bf16(x *
+// norm_w) with the norm); the weights stream in the span layout (below), one
+// group of loads in flight per wave, and latency is covered by several
+// resident units per CU (registers are capped for that).
 //
-// Counters live in the first kGemmCtrBytes of the workspace: they must be zero
-// before the first call, and every call leaves them zero.
+// 16 < m <= 64, mfma_unit_kernel.  Units are (256 weight rows) x (slice of K)
+// running the K loops of mfma_tile.h with all of x as the x tile.
+//
+// Several projections of one x (q/k/v, gate/up) share a launch: the segment
+// is a grid dimension; a one-segment launch is its own instantiation with a
+// one-plan argument.
 #include "device_common.h"
 #include "mfma_tile.h"
 #include "qerl_internal.h"
@@ -67,53 +49,54 @@ constexpr int kThreadsD = kWaves * 64;
 constexpr int kUnitWaves = 4;
 constexpr int64_t kChunkK = 128;          // K elements per chunk
 constexpr int kXPad = 8;                  // BF16 padding per staged x row
-constexpr int64_t kScBudget = 24 * 1024;  // LDS for the unit's scales
-constexpr int64_t kXBudget = 96 * 1024;   // LDS for a unit's x slice (m <= 16)
+constexpr int64_t kGroupK = 4 * kChunkK;  // m <= 16: K elements of one span group (four chunks)
+#ifndef QERL_XSLICE_KB
+#define QERL_XSLICE_KB 36
+#endif
+#ifndef QERL_UNITS_PER_CU
+#define QERL_UNITS_PER_CU 4
+#endif
+#ifndef QERL_STREAM_WAVES_PER_SIMD
+#define QERL_STREAM_WAVES_PER_SIMD 6
+#endif
+constexpr int64_t kXSliceBudget = QERL_XSLICE_KB * 1024;  // m <= 16: LDS for a unit's x slice, so that several units share a CU
+constexpr int64_t kUnitsPerCu = QERL_UNITS_PER_CU;        // m <= 16: units per compute unit the K split aims for
 constexpr int64_t kLdsLimit = 140 * 1024;  // of the 160 KiB a gfx950 workgroup may hold
-constexpr int64_t kProdChunks = 4;        // K chunks per LoRA producer
-constexpr int kProdTiles = 2;            // rank tiles a producer accumulates at once
+constexpr int64_t kProdChunks = 4;        // least K chunks per LoRA producer
+constexpr int64_t kMaxProdRanges = 8;     // K ranges of the producers, at most (finish_kernel sums them in one batch)
+constexpr int kProdTiles = 1;             // rank tiles a producer accumulates
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
-constexpr uint32_t kSpinLimit = 1u << 20;  // polls of the bounded wait for t (2^20 x s_sleep 2)
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
-constexpr int64_t kUnitMinChunks = 8;        // 16 < m: K chunks per unit the split may go down to
-constexpr int64_t kDirectMaxKr = 8;          // m <= 16: most producer K ranges the epilogue sums itself
-constexpr int64_t kDirectMaxCps = 12;        // ... in units of at most this many chunks
-#ifndef QERL_RING
-#define QERL_RING 4
+#ifndef QERL_MFMA_MIN_CHUNKS
+#define QERL_MFMA_MIN_CHUNKS 8
 #endif
-constexpr int kRing = QERL_RING;  // weight chunks in flight per wave (m <= 16)
-
-// counter words at the head of the workspace; kCtrErr is the segment's error
-// word (kGemmErrWaitTimeout when a bounded wait gave up), read by
-// gemm_workspace_check and cleared by gemm_workspace_reset
-constexpr int kCtrProd = 0, kCtrTReady = 1, kCtrDone = 2, kCtrErr = kGemmCtrErrWord, kCtrRow = 4;
-static_assert(kCtrErr == 3, "the error word sits between the fixed counters and the row counters");
-constexpr int64_t kMaxRowBlocks = kSegCtrBytes / 4 - kCtrRow;
+#ifndef QERL_MFMA_UNITS_PER_CU
+#define QERL_MFMA_UNITS_PER_CU 1
+#endif
+constexpr int64_t kUnitMinChunks = QERL_MFMA_MIN_CHUNKS;      // 16 < m: K chunks per unit the split may go down to
+constexpr int64_t kMfmaUnitsPerCu = QERL_MFMA_UNITS_PER_CU;  // 16 < m: units per CU the K split aims for
+constexpr int64_t kMaxRowBlocks = (int64_t)1 << 24;  // row blocks of one call (grid x stays in range)
 
 struct DecodePlan {
     int mt, nw, px;
     int64_t rows_per_unit, row_blocks;
     int64_t chunks, full_chunks;   // chunks of K (the last may be partial), full chunks
     int64_t cps, slices, units;    // chunks per slice (a multiple of 4/nw)
-    int64_t producers, jt, rp;     // LoRA producers, 16-wide rank tiles, rank padded to 32
-    int64_t prod_kr, prod_groups;  // producers: K ranges x (m-tile, rank-tile pair) groups
-    int64_t xpitch, sc_pitch;      // LDS pitches: BF16 elements per x row, bytes per scale row
-    int64_t sc_lds_off, lds_bytes;
+    int64_t producers, jt;         // LoRA producers, 16-wide rank tiles
+    int64_t prod_kr, prod_groups;  // producers: K ranges x (m-tile, rank-tile group) groups
+    int64_t prod_chunks;           // K chunks of one producer range
+    int64_t xpitch, lds_bytes;     // m <= 16: BF16 elements per LDS x row; dynamic LDS bytes
     int64_t unit_sc_pitch;         // 16 < m: LDS pitch of the unit's scale tile
     bool unit_sc;                  // 16 < m: scales staged in LDS
-    int64_t part_off, tpart_off, t_off, bytes;
-    // RMSNorm prologue (m <= 16): the producers' per-K-range sums of squares
-    // [prod_kr][16] at ss_off, and the rows' 1 / rms [16] after t16 at inv_off
+    // workspace offsets from the segment's data: the units' partial tiles,
+    // the producers' partial tiles of t, their sums of squares
+    int64_t part_off, tpart_off, ss_off, bytes;
+    // RMSNorm prologue (m <= 16): the producers also sum x^2 per K range,
+    // [prod_kr][16] at ss_off
     bool norm;
-    int64_t ss_off, inv_off;
-    // m <= 16 with few producer K ranges (and r <= 64): the epilogue sums the
-    // producers' partial tiles itself, so t costs no last-producer stage
-    bool direct;
-    // the bounded wait for t: polls before giving up, and a count added to
-    // the value waited for (nonzero only when the host forces every such wait
-    // to give up, to test that failure is reported)
-    uint32_t spin_limit, wait_bias;
+    // the units write y themselves (one slice, no LoRA, no norm)
+    bool direct_out;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -145,12 +128,11 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.full_chunks = k / kChunkK;
     p.px = 1;
     p.jt = (r + 15) / 16;
-    p.rp = (r + 31) / 32 * 32;
-    p.prod_kr = (p.chunks + kProdChunks - 1) / kProdChunks;
+    p.prod_chunks = (p.chunks + kMaxProdRanges - 1) / kMaxProdRanges;
+    if (p.prod_chunks < kProdChunks) p.prod_chunks = kProdChunks;
+    p.prod_kr = (p.chunks + p.prod_chunks - 1) / p.prod_chunks;
     p.prod_groups = p.mt * ((p.jt + kProdTiles - 1) / kProdTiles);
     p.norm = norm && p.mt == 1;
-    p.spin_limit = g_force_wait_timeout ? 1u : kSpinLimit;
-    p.wait_bias = g_force_wait_timeout ? 1u : 0u;
     if (p.norm && p.prod_groups < 1) p.prod_groups = 1;  // sums of squares only
     p.producers = (r > 0 || p.norm) ? p.prod_kr * p.prod_groups : 0;
     // slices: as many units as compute units without going over (a CU that
@@ -169,6 +151,10 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
         // per CU keep more loads in flight than one long unit)
         const int64_t s_work = p.chunks / kUnitMinChunks;
         if (s < s_work) s = s_work < s_cap ? s_work : s_cap;
+        const int64_t s_occ = (cu_count() * kMfmaUnitsPerCu + slice_rows - 1) / slice_rows;
+        const int64_t s_most = p.chunks / 2 < s_cap ? p.chunks / 2 : s_cap;  // at least two chunks per unit
+        if (s < s_occ) s = s_occ < s_most ? s_occ : s_most;
+        if (s < 1) s = 1;
         p.cps = (p.chunks + s - 1) / s;
         p.slices = (p.chunks + p.cps - 1) / p.cps;
         p.units = p.row_blocks * p.slices;
@@ -176,119 +162,69 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
         if (scp % 2 == 0) ++scp;
         p.unit_sc_pitch = scp * 16;
         p.unit_sc = p.rows_per_unit * p.unit_sc_pitch <= kUnitScBytes;
-        p.part_off = 0;  // offsets from the segment's data (after the counter head)
+        p.part_off = 0;
         p.tpart_off = align256(p.part_off + p.units * tile);
-        p.t_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
-        p.bytes = align256(p.t_off + m * (int64_t)r * 4);
+        p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
+        p.bytes = p.ss_off;
         return p;
     }
-    // m <= 16: stream_kernel, the unit's x slice and scales resident in LDS
-    const int64_t win = 4;  // chunks per slice are a multiple of this
-    int64_t cps = (p.chunks + s - 1) / s;
-    cps = (cps + win - 1) / win * win;
-    int64_t cps_max = kScBudget * 16 / (p.rows_per_unit * kChunkK) / win * win;
-    const int64_t x_max = (kXBudget / (2 * m) - kXPad) / kChunkK / win * win;
-    if (cps_max > x_max) cps_max = x_max;
-    if (cps > cps_max) cps = cps_max;
-    if (cps < win) cps = win;
+    // m <= 16: stream_kernel.  K is cut into slices of whole 512-element
+    // groups (the span layout of the main loop) so that there are about
+    // kUnitsPerCu units per compute unit: a unit's loads are in flight only
+    // while it waits for them, so memory-level parallelism comes from several
+    // resident units per CU.  The x slice (the unit's only LDS besides the
+    // epilogue and producer scratch) is bounded so that they fit together.
+    const int64_t groups = (p.chunks + 3) / 4;  // the last one may be short
+    int64_t sl = (cu_count() * kUnitsPerCu + slice_rows - 1) / slice_rows;
+    if (sl > s_cap) sl = s_cap;
+    if (sl > groups) sl = groups;
+    if (sl < 1) sl = 1;
+    int64_t gps = (groups + sl - 1) / sl;
+    const int64_t g_max = (kXSliceBudget / (2 * m) - kXPad) / kGroupK;
+    if (gps > g_max) gps = g_max;
+    if (gps < 1) gps = 1;
+    const int64_t cps = gps * 4;
     p.cps = cps;
     p.slices = (p.chunks + cps - 1) / cps;
     p.units = p.row_blocks * p.slices;
-    // short units reach their epilogue before a last-producer stage could
-    // publish t: those sum the producers' partials themselves
-    p.direct = p.producers > 0 && p.prod_kr <= kDirectMaxKr && p.jt <= 4 && p.cps <= kDirectMaxCps;
-    // LDS: the x slice, then the scales (rows an odd multiple of 16 bytes
-    // apart, so the 16 rows a wave reads fall in distinct banks)
+    p.direct_out = r == 0 && !p.norm && p.slices == 1;
     p.xpitch = cps * kChunkK + kXPad;
-    const int64_t x_bytes = m * p.xpitch * 2;
-    int64_t scp = (cps * 8 + 15) / 16;
-    if (scp % 2 == 0) ++scp;
-    p.sc_pitch = scp * 16;
-    p.sc_lds_off = (x_bytes + 15) / 16 * 16;
-    int64_t lds = p.sc_lds_off + p.rows_per_unit * p.sc_pitch;
-    const int64_t epi = 16 * p.rp * 2 * 2;  // t16 in the one-launch epilogue
+    int64_t lds = m * p.xpitch * 2;
     const int64_t prod = (int64_t)kWaves * kProdTiles * 64 * 16 + kWaves * 16 * 4;  // producer wave reductions
-    if (lds < epi) lds = epi;
     if (lds < prod) lds = prod;
     p.lds_bytes = lds;
-    // workspace after the counters: partial tiles, producer partials, t
-    p.part_off = 0;  // offsets from the segment's data (after the counter head)
-    p.tpart_off = align256(p.part_off + (p.slices > 1 ? p.units * tile : 0));
+    // workspace: the units' partial tiles (every unit has one: a launch over
+    // several segments writes y from the units only if every segment can),
+    // the producers' partial tiles of t, their sums of squares
+    p.part_off = 0;
+    p.tpart_off = align256(p.part_off + p.units * tile);
     p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
-    p.t_off = align256(p.ss_off + (p.norm ? p.prod_kr * 16 * 4 : 0));
-    p.inv_off = p.t_off + 2 * 16 * p.rp * 2;  // after t16: BF16 hi/lo [2][16][rp]
-    p.bytes = align256(p.inv_off + (p.norm ? 16 * 4 : 0));
+    p.bytes = align256(p.ss_off + (p.norm ? p.prod_kr * 16 * 4 : 0));
     return p;
 }
 
 struct Decode {
-    GemmArgs a;      // a.workspace: this segment's data region
+    GemmArgs a;  // a.workspace: this segment's data region
     DecodePlan p;
-    uint32_t *ctrs;  // this segment's counters in the workspace head
-    __device__ uint32_t *ctr() const { return ctrs; }
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
     __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
-    __device__ float *t32() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.t_off); }
     __device__ float *ssp() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.ss_off); }
-    __device__ float *inv() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.inv_off); }
 };
 
 // One launch over up to kMaxSegments GEMMs that share x (m, k, ldx): the
 // segment is a grid dimension (y for the main kernels, z for finish_kernel),
 // so a workgroup reads its segment's fields without first reading a table;
 // the grid is as wide as the widest segment and the surplus workgroups of
-// the others exit at once.  Each segment has its own counters and data.
+// the others exit at once.  Each segment has its own workspace region.
 // A one-segment launch takes a one-segment set, so its kernel arguments stay
 // as small as one plan.
 constexpr int kMaxSegments = QERL_MAX_SEGMENTS;
-static_assert(kMaxSegments * kSegCtrBytes == kGemmCtrBytes, "one counter block per segment");
 template <int NS>
 struct DecodeSetN {
     Decode seg[NS];
     int nseg;
 };
 using DecodeSet = DecodeSetN<kMaxSegments>;
-
-// ---- device-coherent access: agent scope, no cache write-back or invalidate ----
-constexpr int kSc1 = 16;  // cache-policy bit: coherent at device scope
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void *base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7FFFFFFF, 0x00020000);
-}
-__device__ __forceinline__ void store_f4_coherent(__amdgpu_buffer_rsrc_t r, int off, f32x4_t v) {
-    i32x4_t b;
-    __builtin_memcpy(&b, &v, 16);
-    __builtin_amdgcn_raw_buffer_store_b128(b, r, off, 0, kSc1);
-}
-__device__ __forceinline__ void store_u16_coherent(__amdgpu_buffer_rsrc_t r, int off, uint16_t v) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kSc1);
-}
-__device__ __forceinline__ i32x4_t load_i4_coherent(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
-}
-__device__ __forceinline__ f32x4_t load_f4_coherent(__amdgpu_buffer_rsrc_t r, int off) {
-    const i32x4_t b = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1);
-    f32x4_t v;
-    __builtin_memcpy(&v, &b, 16);
-    return v;
-}
-__device__ __forceinline__ void store_f32_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_f32_coherent(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ctr_add(uint32_t *c, uint32_t v) {
-    return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ctr_load(uint32_t *c) {
-    return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void ctr_store(uint32_t *c, uint32_t v) {
-    __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// every global store and load this wave issued has completed
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8_d(const uint4 &u) {
     bf16x8_t v;
@@ -307,16 +243,15 @@ __device__ __forceinline__ bf16x8_t dequant8_d(uint32_t q, float s) {
 // ---------------------------------------------------------------------------
 // LoRA producers: t = x A^T
 // ---------------------------------------------------------------------------
-// Producer p covers one range of kProdChunks chunks of K for one 16-row
+// Producer p covers one range of prod_chunks chunks of K for one 16-row
 // m-tile and kProdTiles 16-rank tiles (the producers of a launch enumerate
 // K ranges x m-tiles x rank-tile groups); its 4 waves take interleaved
-// 32-element steps.  A lane supplies x row
-// 16*mt + (lane % 16) and A row 16*jt + (lane % 16), 8 elements at
-// 8*(lane / 16) of the step, so MFMA tile (mt, jt) holds
-// t[16 mt + 4 (lane/16) + v][16 jt + lane % 16] in element v.
+// 32-element steps.  A lane supplies x row 16*mt + (lane % 16) and A row
+// 16*jt + (lane % 16), 8 elements at 8*(lane / 16) of the step, so MFMA tile
+// (mt, jt) holds t[16 mt + 4 (lane/16) + v][16 jt + lane % 16] in element v.
+// The range's tiles go to the workspace; finish_kernel sums the ranges.
 // NORM (m <= 16): x enters as bf16(x * norm_w) and the first group of each K
-// range also sums the squares of x over the range; the last producer turns
-// the sums into 1 / rms per row, scales t by it and publishes both.
+// range also stores the sums of the squares of x over the range.
 template <int MT, bool NORM = false>
 __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     static_assert(!NORM || MT == 1, "the norm prologue is for m <= 16");
@@ -328,17 +263,17 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     // (one pass each, so that no producer runs all m-tiles and ranks in turn)
     const int64_t kr = p / d.p.prod_groups;
     const int grp = (int)(p - kr * d.p.prod_groups);
-    const int64_t kb = kr * kProdChunks * kChunkK;
-    const int64_t ke = kb + kProdChunks * kChunkK < a.k ? kb + kProdChunks * kChunkK : a.k;
+    const int64_t kb = kr * d.p.prod_chunks * kChunkK;
+    const int64_t ke = kb + d.p.prod_chunks * kChunkK < a.k ? kb + d.p.prod_chunks * kChunkK : a.k;
     const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
-    const __amdgpu_buffer_rsrc_t rs_own = coherent_rsrc(d.tpart() + kr * tile_floats);
+    f32x4_t *own = reinterpret_cast<f32x4_t *>(d.tpart() + kr * tile_floats);  // this K range's tiles
     f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
     float *red_ss = reinterpret_cast<float *>(lds + kWaves * kProdTiles * 64 * 16);  // [wave][16]
     // one m-tile and two rank tiles, so the producer path never needs more
     // registers than the streaming path; each wave's steps (32 elements,
     // every 4th of the range) in groups of PS with all loads of a group
     // issued before its products
-    constexpr int PS = 4;
+    constexpr int PS = 2;
     {
         const int mt = grp / JGd, jg = (grp - mt * JGd) * kProdTiles;
         const bool sum_sq = NORM && grp == 0;  // (uniform)
@@ -397,7 +332,8 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
                     }
                 }
             }
-            // the four waves' tiles, summed in wave order by wave 0 and published
+            // the four waves' tiles, summed in wave order by wave 0 and stored;
+            // finish_kernel reads them after the kernel boundary
             if (wave < kWaves)
 #pragma unroll
                 for (int jj = 0; jj < kProdTiles; ++jj) red[(wave * kProdTiles + jj) * 64 + lane] = acc[jj];
@@ -414,82 +350,16 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
                     f32x4_t t = red[jj * 64 + lane];
 #pragma unroll
                     for (int w = 1; w < kWaves; ++w) t = t + red[(w * kProdTiles + jj) * 64 + lane];
-                    store_f4_coherent(rs_own, ((mt * JT + jg + jj) * 64 + lane) * 16, t);
+                    own[(mt * JT + jg + jj) * 64 + lane] = t;
                 }
                 if (NORM && sum_sq && lane < 16) {
                     float tot = red_ss[lane];
 #pragma unroll
                     for (int w = 1; w < kWaves; ++w) tot += red_ss[w * 16 + lane];
-                    store_f32_coherent(d.ssp() + kr * 16 + lane, tot);
+                    d.ssp()[kr * 16 + lane] = tot;
                 }
             }
-            __syncthreads();
         }
-    }
-    if (wave == 0) wait_vm();
-    __shared__ uint32_t s_last;
-    __shared__ float s_inv[16];
-    __syncthreads();
-    if (tid == 0) s_last = ctr_add(d.ctr() + kCtrProd, 1u) == (uint32_t)(d.p.producers - 1);
-    __syncthreads();
-    if (!s_last || d.p.direct) return;  // direct: the consumers read the count and the partials
-    if (tid == 0) ctr_store(d.ctr() + kCtrProd, 0u);  // every producer has counted
-    if (NORM) {  // 1 / rms of the 16 rows (rows past m repeat row m - 1), sums in K-range order
-        if (tid < 16) {
-            float tot = 0.0f;
-            for (int64_t q = 0; q < d.p.prod_kr; ++q) tot += load_f32_coherent(d.ssp() + q * 16 + tid);
-            const float inv = 1.0f / sqrtf(tot * (1.0f / (float)a.k) + a.norm_eps);
-            s_inv[tid] = inv;
-            store_f32_coherent(d.inv() + tid, inv);
-        }
-        __syncthreads();
-    }
-    // The last producer sums the partials in K-range order (tile i goes to
-    // wave i % 4, kBatch ranges in flight).  16 < m: into t [m, r] in FP32,
-    // read after the kernel boundary.  m <= 16: into t16 [2][16][rp], the BF16
-    // hi and lo halves of t in the layout the consumers' epilogue multiplies,
-    // published to this launch's consumers by the ready flag.
-    const __amdgpu_buffer_rsrc_t rt = coherent_rsrc(d.t32());
-    for (int i = wave; wave < kWaves && i < MT * JT; i += kWaves) {
-        f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int64_t q0 = 0; q0 < d.p.prod_kr; q0 += kBatch) {
-            f32x4_t v[kBatch];
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int64_t q = q0 + u < d.p.prod_kr ? q0 + u : d.p.prod_kr - 1;
-                v[u] = load_f4_coherent(coherent_rsrc(d.tpart() + q * tile_floats), (i * 64 + lane) * 16);
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u)
-                if (q0 + u < d.p.prod_kr) sum = sum + v[u];
-        }
-        const int mt = i / JT, jt = i - mt * JT;
-        const int64_t j = 16 * jt + lr;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int64_t m = 16 * mt + 4 * lq + v;
-            if (MT == 1) {  // all 16 rows (rows past m repeat row m - 1 and are never output)
-                const float tv = NORM ? sum[v] * s_inv[m] : sum[v];
-                const uint16_t hi = f32_to_bf16_bits(tv);
-                const int off = (int)((m * d.p.rp + j) * 2);
-                store_u16_coherent(rt, off, hi);
-                store_u16_coherent(rt, off + (int)(16 * d.p.rp * 2),
-                                   f32_to_bf16_bits(tv - __uint_as_float((uint32_t)hi << 16)));
-            } else if (m < a.m && j < a.r) {
-                d.t32()[m * a.r + j] = sum[v];
-            }
-        }
-    }
-    if (MT == 1) {
-        // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
-        const int pad = (int)(d.p.rp - 16 * JT);
-        for (int i = tid; i < 2 * 16 * pad; i += kThreadsD) {
-            const int h = i / (16 * pad), m = (i / pad) % 16, j = 16 * JT + i % pad;
-            store_u16_coherent(rt, (int)(((h * 16 + m) * d.p.rp + j) * 2), 0);
-        }
-        wait_vm();
-        __syncthreads();
-        if (tid == 0) ctr_store(d.ctr() + kCtrTReady, 1u);
     }
 }
 
@@ -575,42 +445,41 @@ __device__ __forceinline__ void batched_copy_2d(int rows, int per_row, Src src, 
 // of `pitch` elements; columns at or past k are zero.  NORM: each element
 // enters as bf16(x * norm_w[column]) (the row's 1 / rms is applied in the
 // epilogue).
-struct XNormItem {
-    uint4 x;
-    float4 w0, w1;
-};
 template <bool NORM>
 __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
-    if (!NORM) {
-        batched_copy_2d<uint4>(
-            (int)a.m, (int)(width / 8),
-            [&](int m, int pc) {
-                const int64_t col = k0 + 8 * pc;
-                return col < a.k ? *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col) : make_uint4(0, 0, 0, 0);
-            },
-            [&](int m, int pc, const uint4 &v) { *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = v; });
-        return;
-    }
-    batched_copy_2d<XNormItem>(
-        (int)a.m, (int)(width / 8),
-        [&](int m, int pc) {
+    // 8-element pieces i = row * per_row + piece, kStage per thread in flight
+    // (every load of a round issued before its stores)
+    constexpr int kStage = 4;
+    const int per_row = (int)(width / 8), total = (int)a.m * per_row;
+    for (int base = threadIdx.x; base < total; base += kStage * kThreadsD) {
+        uint4 v[kStage];
+        float4 w0[kStage], w1[kStage];
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = base + u * kThreadsD;
+            const int row = i / per_row, pc = i - row * per_row;
             const int64_t col = k0 + 8 * pc;
-            XNormItem it{make_uint4(0, 0, 0, 0), make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-            if (col < a.k) {
-                it.x = *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + col);
-                it.w0 = *reinterpret_cast<const float4 *>(a.norm_w + col);
-                it.w1 = *reinterpret_cast<const float4 *>(a.norm_w + col + 4);
+            const bool in = i < total && col < a.k;  // k % 16 == 0: a piece is inside or outside
+            v[u] = in ? *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + col) : make_uint4(0, 0, 0, 0);
+            if (NORM) {
+                w0[u] = in ? *reinterpret_cast<const float4 *>(a.norm_w + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+                w1[u] = in ? *reinterpret_cast<const float4 *>(a.norm_w + col + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            return it;
-        },
-        [&](int m, int pc, const XNormItem &it) {
-            const uint4 v = it.x;
-            const uint4 o = make_uint4(pack_bf16x2(bf16lo_to_f32(v.x) * it.w0.x, bf16hi_to_f32(v.x) * it.w0.y),
-                                       pack_bf16x2(bf16lo_to_f32(v.y) * it.w0.z, bf16hi_to_f32(v.y) * it.w0.w),
-                                       pack_bf16x2(bf16lo_to_f32(v.z) * it.w1.x, bf16hi_to_f32(v.z) * it.w1.y),
-                                       pack_bf16x2(bf16lo_to_f32(v.w) * it.w1.z, bf16hi_to_f32(v.w) * it.w1.w));
-            *reinterpret_cast<uint4 *>(xs + m * pitch + 8 * pc) = o;
-        });
+        }
+#pragma unroll
+        for (int u = 0; u < kStage; ++u) {
+            const int i = base + u * kThreadsD;
+            if (i >= total) break;
+            const int row = i / per_row, pc = i - row * per_row;
+            uint4 o = v[u];
+            if (NORM)
+                o = make_uint4(pack_bf16x2(bf16lo_to_f32(o.x) * w0[u].x, bf16hi_to_f32(o.x) * w0[u].y),
+                               pack_bf16x2(bf16lo_to_f32(o.y) * w0[u].z, bf16hi_to_f32(o.y) * w0[u].w),
+                               pack_bf16x2(bf16lo_to_f32(o.z) * w1[u].x, bf16hi_to_f32(o.z) * w1[u].y),
+                               pack_bf16x2(bf16lo_to_f32(o.w) * w1[u].z, bf16hi_to_f32(o.w) * w1[u].w));
+            *reinterpret_cast<uint4 *>(xs + row * pitch + 8 * pc) = o;
+        }
+    }
 }
 
 // Stage the unit's scale bytes: rows [n0, n0 + R) x bytes [b0, b0 + nb) of
@@ -641,43 +510,82 @@ __device__ void stage_scales(const GemmArgs &a, uint8_t *sc, int64_t pitch, int6
     }
 }
 
-// One chunk: x fragments from the LDS window, weights from registers.
-// sc_off[g]: LDS byte offset of this lane's scale pair for row group g at the
-// unit's first chunk; cl: chunk index within the unit; col: x column of the
-// chunk within the window.  The x fragments of the chunk are read once and
-// reused over the row groups; each row group's weights are decoded just
-// before use, which bounds the registers of the larger tiles.
-template <int MT, int NW>
-__device__ __forceinline__ void mma_chunk(const uint4 (&w)[NW], const uint8_t *sc, const int (&sc_off)[NW],
-                                          int64_t cl, const uint16_t *xb, int64_t pitch, int64_t col, int m_last,
-                                          int lr, int lq, f32x4_t (&acc)[MT][NW]) {
-    bf16x8_t xa[4][MT];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const int m = 16 * mt + lr < m_last ? 16 * mt + lr : m_last;
-            xa[j][mt] = *reinterpret_cast<const bf16x8_t *>(xb + (m * pitch + col + 32 * lq + 8 * j));
-        }
-#pragma unroll
-    for (int g = 0; g < NW; ++g) {
-        const uint32_t s2 = *reinterpret_cast<const uint16_t *>(sc + sc_off[g] + cl * 8);
-        const float sv0 = QERL_E4M3_F32(s2, 0), sv1 = QERL_E4M3_F32(s2, 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t q = j == 0 ? w[g].x : j == 1 ? w[g].y : j == 2 ? w[g].z : w[g].w;
-            const bf16x8_t b = dequant8_d(q, j < 2 ? sv0 : sv1);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-                acc[mt][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j][mt], b, acc[mt][g], 0, 0, 0);
-        }
-    }
+// ---- m <= 16 main loop: the span layout ----
+// A 512-element group of K is permuted identically on both MFMA operands:
+// lane quarter q takes elements 128 q .. 128 q + 127 of the group, i.e. 64
+// contiguous packed bytes (four 16-byte loads) and the 8 scale bytes of its 8
+// blocks (one 8-byte load), spread over the group's 16 MFMA steps (8 elements
+// each).  Against one 16-byte code load and one 2-byte scale load per
+// 128-element chunk, that is 5 loads instead of 8 per 512 elements, and scale
+// loads 8 bytes wide: measured on gfx950 this layout streams a 38 MB weight at
+// 3.8-4.0 TB/s where the chunk layout reaches 2.2 TB/s.
+struct SpanGroup {
+    uint4 q0, q1, q2, q3;  // packed codes: 32 elements each
+    uint2 sc;              // E4M3 scales of the 8 blocks
+};
+
+__device__ __forceinline__ SpanGroup load_span_group(const uint8_t *prow, const uint8_t *srow, int64_t g, int lq) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(prow + g * (kGroupK / 2) + 64 * lq);
+    SpanGroup v;
+    v.q0 = q[0];
+    v.q1 = q[1];
+    v.q2 = q[2];
+    v.q3 = q[3];
+    v.sc = *reinterpret_cast<const uint2 *>(srow + g * (kGroupK / 16) + 8 * lq);
+    return v;
 }
 
-// K32: k % 32 == 0; SPLIT: K is split over several units per row block
-// (slices > 1); LORA: r > 0.
-template <int NS, bool K32, bool SPLIT, bool LORA, bool NORM>
-__global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
+// 16-byte piece of codes `q` (blocks b0, b1 of scale word `sw`, bytes B0 and
+// B0 + 1) against the x elements at xp .. xp + 31
+template <int B0>
+__device__ __forceinline__ void mma_piece(const uint4 &q, uint32_t sw, const uint16_t *xp, f32x4_t &acc) {
+    const float s0 = QERL_E4M3_F32(sw, B0), s1 = QERL_E4M3_F32(sw, B0 + 1);
+    const bf16x8_t x0 = *reinterpret_cast<const bf16x8_t *>(xp), x1 = *reinterpret_cast<const bf16x8_t *>(xp + 8);
+    const bf16x8_t x2 = *reinterpret_cast<const bf16x8_t *>(xp + 16), x3 = *reinterpret_cast<const bf16x8_t *>(xp + 24);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, dequant8_d(q.x, s0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, dequant8_d(q.y, s0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x2, dequant8_d(q.z, s1), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x3, dequant8_d(q.w, s1), acc, 0, 0, 0);
+}
+
+// One group: xg is this lane's x row at element 128 lq of the group
+// (the scheduling barriers keep the compiler from hoisting all 16 x
+// fragments of a group, which would cost 64 registers and with them resident
+// waves)
+__device__ __forceinline__ void mma_span_group(const SpanGroup &v, const uint16_t *xg, f32x4_t &acc) {
+    mma_piece<0>(v.q0, v.sc.x, xg, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_piece<2>(v.q1, v.sc.x, xg + 32, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_piece<0>(v.q2, v.sc.y, xg + 64, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_piece<2>(v.q3, v.sc.y, xg + 96, acc);
+}
+
+// The scale bytes b, b + 1 of a row holding nb of them (bytes past nb read
+// as zero).  ALIGNED: nb even and b even, so one 16-bit load.
+template <bool ALIGNED>
+__device__ __forceinline__ uint32_t load_scale_pair(const uint8_t *srow, int64_t b, int64_t nb) {
+    if (ALIGNED) return *reinterpret_cast<const uint16_t *>(srow + b);
+    const uint32_t lo = b < nb ? srow[b] : 0u, hi = b + 1 < nb ? srow[b + 1] : 0u;
+    return lo | hi << 8;
+}
+
+// One 128-element chunk in the chunk layout (lane quarter q: elements 32 q ..
+// 32 q + 31; scale pair s2): xp is this lane's x row at element 32 q of it
+__device__ __forceinline__ void mma_chunk_sc(const uint4 &w, uint32_t s2, const uint16_t *xp, f32x4_t &acc) {
+    mma_piece<0>(w, s2, xp, acc);
+}
+
+// K32: k % 32 == 0; DIRECT: the units write y (every segment has one slice,
+// no LoRA, no norm), else each stores its FP32 partial tile for
+// finish_kernel; LORA: some segment has r > 0; NORM: the RMSNorm in front.
+template <int NS, bool K32, bool DIRECT, bool LORA, bool NORM>
+// Registers are capped so that QERL_STREAM_WAVES_PER_SIMD waves fit each SIMD
+// (the main loop needs about 60; the producer and epilogue paths would take
+// more and are allowed to spill a little).
+__global__ __launch_bounds__(kThreadsD) __attribute__((amdgpu_waves_per_eu(QERL_STREAM_WAVES_PER_SIMD, 8)))
+void stream_kernel(DecodeSetN<NS> ds) {
     constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const Decode &d = ds.seg[NS == 1 ? 0u : blockIdx.y];
@@ -685,18 +593,14 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     const DecodePlan &p = d.p;
     const int64_t bx = blockIdx.x;
     if (NS > 1 && bx >= p.producers + p.units) return;  // past a narrower segment
-    // (segments of one launch may differ; a one-segment launch has LORA == (r > 0))
-    const bool lora = LORA && (NS == 1 || a.r > 0);
-    const bool wait_t = lora || NORM;  // producers publish t and / or 1 / rms behind the ready flag
-    if (wait_t && bx < p.producers) {
+    if ((LORA || NORM) && bx < p.producers) {  // (a segment without LoRA or norm has none)
         lora_producer<MT, NORM>(d, bx, lds);
         return;
     }
     uint16_t *xs = reinterpret_cast<uint16_t *>(lds);
-    uint8_t *sc = lds + p.sc_lds_off;
     const int64_t u = bx - p.producers;
     const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
-    const int64_t c_begin = slice * p.cps;
+    const int64_t c_begin = slice * p.cps;  // a multiple of 4 chunks
     const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
     const int64_t c_full_end = c_end < p.full_chunks ? c_end : p.full_chunks;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -705,356 +609,220 @@ __global__ __launch_bounds__(kThreadsD) void stream_kernel(DecodeSetN<NS> ds) {
     const int64_t n0 = n_unit + (int64_t)wave * 16 * NW;
     const int m_last = (int)a.m - 1;
 
-    int sc_off[NW];
-#pragma unroll
-    for (int g = 0; g < NW; ++g) sc_off[g] = (int)((wave * 16 * NW + 16 * g + lr) * p.sc_pitch + 2 * lq);
-
     f32x4_t acc[MT][NW];
-#pragma unroll
-    for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NW; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int64_t c_last = c_full_end - 1;  // the unit's last full chunk (< c_begin: none)
-    const int64_t sb0 = c_begin * 8;
-    const int64_t sb1 = c_end * 8 < (a.k >> 4) ? c_end * 8 : (a.k >> 4);
-    // ---- x and scales of the whole unit resident in LDS; the weights
-    // stream through a ring of DR chunks with no barrier ----
-    constexpr int DR = kRing;
-    uint4 w[DR][NW];
-    if (c_full_end > c_begin) {
-#pragma unroll
-        for (int s = 0; s < DR; ++s)
-            load_chunk<NW, K32>(a, n0, c_begin + s < c_last ? c_begin + s : c_last, lr, lq, w[s]);
-    }
+    acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's weight row (rows past n repeat row n - 1; their outputs are
+    // discarded) and x row (rows past m repeat row m - 1)
+    const int64_t nrow = n0 + lr < a.n ? n0 + lr : a.n - 1;
+    const uint8_t *prow = a.packed + nrow * (a.k >> 1);
+    const uint8_t *srow = a.scales + nrow * (a.k >> 4);
+    const uint16_t *xrow = xs + (lr < m_last ? lr : m_last) * p.xpitch;
+    // whole 512-element groups of the slice in the span layout (k % 128 == 0
+    // keeps their 16-byte code and 8-byte scale loads aligned); the other
+    // chunks, if any, in the chunk layout
+    const int64_t ng = (a.k & 127) == 0 ? (c_full_end - c_begin) / 4 : 0;
+    // ---- the first group's loads travel while the x slice is staged ----
+    SpanGroup cur;
+    if (ng > 0) cur = load_span_group(prow, srow, c_begin / 4, lq);
     stage_x_slice<NORM>(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
-    stage_scales(a, sc, p.sc_pitch, n_unit, R, sb0, sb1 - sb0);
-    if (c_end > c_full_end) {  // scale bytes of the partial last chunk past k: zero
-        const int z0 = (int)((a.k >> 4) - sb0), zn = (int)(p.full_chunks * 8 + 8 - (a.k >> 4));  // zn < 8
-        for (int rr = tid >> 3; rr < R; rr += kThreadsD / 8)
-            if ((tid & 7) < zn) sc[rr * p.sc_pitch + z0 + (tid & 7)] = 0;
-    }
     __syncthreads();
-    int64_t c = c_begin;
-    for (; c + 2 * DR <= c_full_end; c += DR) {
-#pragma unroll
-        for (int s = 0; s < DR; ++s) {
-            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                              m_last, lr, lq, acc);
-            load_chunk<NW, K32>(a, n0, c + s + DR, lr, lq, w[s]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    // One group in flight per wave: latency is covered by the other resident
+    // units and waves (registers kept low for that), not by a deeper ring.
+    for (int64_t gl = 0; gl < ng; ++gl) {
+        if (gl > 0) cur = load_span_group(prow, srow, c_begin / 4 + gl, lq);
+        mma_span_group(cur, xrow + gl * kGroupK + 128 * lq, acc[0][0]);
     }
-    if (c_full_end - c > DR) {  // DR < rest < 2 DR: one more reloading round (clamped)
-#pragma unroll
-        for (int s = 0; s < DR; ++s) {
-            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                              m_last, lr, lq, acc);
-            load_chunk<NW, K32>(a, n0, c + s + DR < c_last ? c + s + DR : c_last, lr, lq, w[s]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        c += DR;
+    // the remaining full chunks (k % 512 != 0 or k % 128 != 0), chunk layout
+    for (int64_t c = c_begin + 4 * ng; c < c_full_end; ++c) {
+        uint4 w[NW];
+        load_chunk<NW, K32>(a, n0, c, lr, lq, w);
+        const uint32_t s2 = load_scale_pair<K32>(srow, c * 8 + 2 * lq, a.k >> 4);
+        mma_chunk_sc(w[0], s2, xrow + (c - c_begin) * kChunkK + 32 * lq, acc[0][0]);
     }
-    // Whether t is published, read while the last chunks multiply: the
-    // producers lead the grid and are done by now as a rule, so t can be
-    // loaded without a round trip of its own.
-    uint32_t t_seen = 0;
-    // (direct: ready once every producer has counted; else the ready flag)
-    const bool direct = wait_t && p.direct;
-    uint32_t *ready_ctr = d.ctr() + (direct ? kCtrProd : kCtrTReady);
-    const uint32_t ready_at = (direct ? (uint32_t)p.producers : 1u) + p.wait_bias;
-    if (wait_t && tid == 0) t_seen = ctr_load(ready_ctr) >= ready_at;
-#pragma unroll
-    for (int s = 0; s < DR; ++s)
-        if (c + s < c_full_end)  // uniform
-            mma_chunk<MT, NW>(w[s], sc, sc_off, c + s - c_begin, xs, p.xpitch, (c + s - c_begin) * kChunkK,
-                              m_last, lr, lq, acc);
-    if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0)
+    if (c_end > c_full_end) {  // the partial last chunk of K (k % 128 != 0): zeros past k
         uint4 wt[NW];
         load_chunk_tail<NW>(a, n0, p.full_chunks, lr, lq, wt);
-        mma_chunk<MT, NW>(wt, sc, sc_off, p.full_chunks - c_begin, xs, p.xpitch, (p.full_chunks - c_begin) * kChunkK,
-                          m_last, lr, lq, acc);
+        const uint32_t s2 = load_scale_pair<false>(srow, p.full_chunks * 8 + 2 * lq, a.k >> 4);
+        mma_chunk_sc(wt[0], s2, xrow + (p.full_chunks - c_begin) * kChunkK + 32 * lq, acc[0][0]);
     }
-    const int64_t tile_floats = R * 16;
-    const int wave_off = wave * 64;  // f32x4 slots before this wave's in a tile
-    // B [n, j] for this lane's rows and ranks 8 lq .. 8 lq + 7 of the block jb
-    auto load_b = [&](int g, int64_t jb) -> bf16x8_t {
-        int64_t nb = n0 + 16 * g + lr;
-        nb = nb < a.n ? nb : a.n - 1;
-        const uint16_t *br = a.lora_b + nb * a.r;
-        const int64_t j0 = jb + 8 * lq;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if ((a.r & 7) == 0) {
-            if (j0 < a.r) v = *reinterpret_cast<const uint4 *>(br + j0);
-        } else {
-            uint16_t e[8];
+    // Lane (lr, lq) holds rows 4 lq .. 4 lq + 3 of column n0 + lr.
+    if (DIRECT) {
+        const float st = *a.tensor_scale;
+        const int64_t n = n0 + lr;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = j0 + i < a.r ? br[j0 + i] : (uint16_t)0;
-            __builtin_memcpy(&v, e, 16);
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = 4 * lq + v;
+            if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[0][0][v]);
         }
-        return as_bf16x8_d(v);
-    };
-    bf16x8_t b0[NW];  // the first rank block (read-only input: loaded early)
-    if (lora)
-#pragma unroll
-        for (int g = 0; g < NW; ++g) b0[g] = load_b(g, 0);
-    __shared__ uint32_t s_flag, s_ready, s_timeout;
-    // ---- split K: the last unit of the row block to arrive sums the slices ----
-    if (SPLIT) {
-        {
-            const __amdgpu_buffer_rsrc_t rs = coherent_rsrc(d.part() + u * tile_floats);
-            if (4 * lq < a.m) store_f4_coherent(rs, (wave_off + lane) * 16, acc[0][0]);
-            wait_vm();
-        }
-        if (tid == 0) s_ready = t_seen;
-        __syncthreads();
-        if (tid == 0) s_flag = ctr_add(d.ctr() + kCtrRow + rblk, 1u) == (uint32_t)(p.slices - 1);
-        __syncthreads();
-        if (!s_flag) return;
-        if (tid == 0) ctr_store(d.ctr() + kCtrRow + rblk, 0u);
-    } else {
-        if (tid == 0) s_ready = t_seen;
-        __syncthreads();
-    }
-    // A wait that gives up leaves t (or 1 / rms) unknown: the row block's
-    // outputs are written as NaN and the segment's error word is set, which
-    // gemm_workspace_check reports.
-    bool timed_out = false;
-    if (wait_t && !s_ready) {  // uniform; rare: wait for the last producer
-        if (tid == 0) {
-            uint32_t it = 0;
-            while (ctr_load(ready_ctr) < ready_at && ++it < p.spin_limit) __builtin_amdgcn_s_sleep(2);
-            s_timeout = ctr_load(ready_ctr) < ready_at;
-            if (s_timeout) ctr_store(d.ctr() + kCtrErr, kGemmErrWaitTimeout);
-        }
-        __syncthreads();
-        timed_out = s_timeout;
-    }
-    // The slices' partial tiles and t16 are loaded together (one round trip
-    // in the usual case; more than kRedP slices take more), then summed in
-    // slice order; t16 goes to LDS as it is.
-    constexpr int kRedP = 12;
-    auto part_at = [&](int64_t sl) { return coherent_rsrc(d.part() + (sl * p.row_blocks + rblk) * tile_floats); };
-    const int t_pieces = (int)(16 * p.rp * 2 * 2 / 16);  // 16-byte pieces of t16 (<= 512)
-    // Every load is issued unconditionally; the buffer resources end where
-    // the data does, so a load past the slices or past t16 returns zeros
-    // without a memory access (and with no branch for the compiler to fold
-    // the sums into).
-    f32x4_t pv[kRedP];
-    i32x4_t tq[2], iq;
-    f32x4_t dq[kDirectMaxKr];  // direct: tile (wave) of each K range's partial t
-    float sq[kDirectMaxKr];    // direct + NORM: row (tid < 16) of each K range's sum of squares
-    if (SPLIT) {
-        const int64_t sstride = p.row_blocks * tile_floats * 4;  // bytes between slices of a row block
-        const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
-            d.part() + rblk * tile_floats, 0, (int)(sstride * (p.slices < kRedP ? p.slices : kRedP)), 0x00020000);
-#pragma unroll
-        for (int v = 0; v < kRedP; ++v)
-            pv[v] = load_f4_coherent(rp, (int)(v * sstride) + (wave_off + lane) * 16);
-    }
-    const int64_t ptile = (int64_t)p.jt * 64 * 4;  // floats of one K range's partial tiles
-    if (direct) {
-        if (lora && wave < p.jt) {  // (uniform) tile `wave`, K ranges past prod_kr read as zeros
-            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-                d.tpart(), 0, (int)(p.prod_kr * ptile * 4), 0x00020000);
-#pragma unroll
-            for (int q = 0; q < kDirectMaxKr; ++q)
-                dq[q] = load_f4_coherent(rq, (int)((q * ptile + (wave * 64 + lane) * 4) * 4));
-        }
-        if (NORM) {
-            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                d.ssp(), 0, (int)(p.prod_kr * 16 * 4), 0x00020000);
-#pragma unroll
-            for (int q = 0; q < kDirectMaxKr; ++q)
-                sq[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (q * 16 + (tid & 15)) * 4, 0, kSc1));
-        }
-    } else {
-        if (lora) {
-            const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(d.t32(), 0, t_pieces * 16, 0x00020000);
-            tq[0] = load_i4_coherent(rt, tid * 16);
-            tq[1] = load_i4_coherent(rt, (tid + kThreadsD) * 16);
-        }
-        if (NORM) iq = load_i4_coherent(coherent_rsrc(d.inv()), (tid & 3) * 16);  // 1 / rms of the 16 rows
-    }
-    // The values are taken here, after every load has been issued: without
-    // this the compiler folds the sums below into the conditional loads and
-    // waits for each load before issuing the next.
-    if (SPLIT)
-#pragma unroll
-        for (int v = 0; v < kRedP; ++v) asm volatile("" : "+v"(pv[v]));
-    if (direct) {
-        if (lora && wave < p.jt)
-#pragma unroll
-            for (int q = 0; q < kDirectMaxKr; ++q) asm volatile("" : "+v"(dq[q]));
-        if (NORM)
-#pragma unroll
-            for (int q = 0; q < kDirectMaxKr; ++q) asm volatile("" : "+v"(sq[q]));
-    } else {
-        if (lora) asm volatile("" : "+v"(tq[0]), "+v"(tq[1]));
-        if (NORM) asm volatile("" : "+v"(iq));
-    }
-    if (SPLIT) {
-        acc[0][0] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int v = 0; v < kRedP; ++v) acc[0][0] = acc[0][0] + pv[v];  // zeros past the slices
-        for (int64_t s0 = kRedP; s0 < p.slices; s0 += kRedP) {
-#pragma unroll
-            for (int v = 0; v < kRedP; ++v) {
-                const int64_t sl = s0 + v < p.slices ? s0 + v : p.slices - 1;
-                pv[v] = load_f4_coherent(part_at(sl), (wave_off + lane) * 16);
-            }
-#pragma unroll
-            for (int v = 0; v < kRedP; ++v)
-                if (s0 + v < p.slices) acc[0][0] = acc[0][0] + pv[v];
-        }
-    }
-
-    // ---- LoRA epilogue (lora_scale * t B^T on the MFMA, t as BF16 hi + lo) and output ----
-    uint16_t *th = reinterpret_cast<uint16_t *>(lds);  // t16 [2][16][rp]: hi, then lo
-    uint16_t *tl = th + 16 * p.rp;
-    __shared__ __attribute__((aligned(16))) float s_inv[16];
-    if (direct) {
-        // t = the K ranges' partial tiles summed in K-range order (scaled by
-        // 1 / rms with the norm), into LDS as BF16 hi + lo in the t16 layout
-        if (NORM) {
-            if (tid < 16) {
-                float tot = 0.0f;
-#pragma unroll
-                for (int q = 0; q < kDirectMaxKr; ++q) tot += sq[q];  // zeros past prod_kr
-                s_inv[tid] = 1.0f / sqrtf(tot * (1.0f / (float)a.k) + a.norm_eps);
-            }
-            __syncthreads();
-        }
-        if (lora) {
-            if (wave < p.jt) {
-                f32x4_t t = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int q = 0; q < kDirectMaxKr; ++q) t = t + dq[q];
-                const int64_t j = 16 * wave + lr;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int m = 4 * lq + v;
-                    const float tv = NORM ? t[v] * s_inv[m] : t[v];
-                    const uint16_t hi = f32_to_bf16_bits(tv);
-                    th[m * p.rp + j] = hi;
-                    tl[m * p.rp + j] = f32_to_bf16_bits(tv - __uint_as_float((uint32_t)hi << 16));
-                }
-            }
-            // rank columns past the tiles (r rounded up to 16 vs to 32) are zero
-            const int pad = (int)(p.rp - 16 * p.jt);
-            for (int i = tid; i < 2 * 16 * pad; i += kThreadsD) {
-                const int h = i / (16 * pad), m = (i / pad) % 16, j = 16 * (int)p.jt + i % pad;
-                th[(h * 16 + m) * p.rp + j] = 0;
-            }
-        }
-    } else {
-        if (lora) {  // (the pieces past t16 were loaded as zeros and are not stored)
-            if (tid < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid] = tq[0];
-            if (tid + kThreadsD < t_pieces) reinterpret_cast<i32x4_t *>(th)[tid + kThreadsD] = tq[1];
-        }
-        if (NORM && tid < 4) reinterpret_cast<i32x4_t *>(s_inv)[tid] = iq;
-    }
-    if (wait_t) __syncthreads();
-    const float st = *a.tensor_scale, lam = a.lora_scale;
-#pragma unroll
-    for (int g = 0; g < NW; ++g) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            f32x4_t l = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int64_t jb = 0; jb < p.rp; jb += 32) {
-                const bf16x8_t bfrag = jb == 0 ? b0[g] : load_b(g, jb);
-                const int64_t off = (16 * mt + lr) * p.rp + jb + 8 * lq;
-                l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(th + off), bfrag, l,
-                                                            0, 0, 0);
-                l = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8_t *>(tl + off), bfrag, l,
-                                                            0, 0, 0);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = 16 * mt + 4 * lq + v;
-                const int64_t n = n0 + 16 * g + lr;
-                const float base = NORM ? st * s_inv[m] * acc[mt][g][v] : st * acc[mt][g][v];
-                if (m < a.m && n < a.n)
-                    a.y[m * a.ldy + n] = timed_out ? (uint16_t)0x7FC0 : f32_to_bf16_bits(base + lam * l[v]);
-            }
-        }
-    }
-    // this row block is done with t16; the last one clears the ready flag
-    // and this count for the next call
-    if (wait_t && tid == 0 && ctr_add(d.ctr() + kCtrDone, 1u) == (uint32_t)(p.row_blocks - 1)) {
-        ctr_store(ready_ctr, 0u);  // (direct: the producers' count)
-        ctr_store(d.ctr() + kCtrDone, 0u);
+    } else if (4 * lq < a.m) {  // this unit's FP32 tile, slot wave * 64 + lane
+        reinterpret_cast<f32x4_t *>(d.part() + u * (R * 16))[wave * 64 + lane] = acc[0][0];
     }
 }
 
-// 16 < m: y[m, n] = bf16(s_t * sum over slices of the partial tiles (in slice
-// order) + lora_scale * sum_j t[m][j] B[n][j]).  Thread (n, quad) handles the
-// rows 4 quad .. 4 quad + 3 of column n, which one lane of one tile holds as a
-// float4.  Workgroup: 64 columns x 4 quads (16 rows); t of its rows in LDS.
-template <int NS, int MT, int NW>
+// ---------------------------------------------------------------------------
+// finish_kernel: y from the partial tiles of the main kernel
+// ---------------------------------------------------------------------------
+// Workgroup: 64 columns x one 16-row m-tile of one segment, 256 threads, one
+// round trip of loads (every load a thread needs is issued before any is
+// used), then two LDS stages; every sum runs in the same order on every call.
+//  * t of the m-tile's rows: the producers' tiles summed over the K ranges
+//    (at most kMaxProdRanges).  Each (rank tile, lane) item has P threads
+//    that sum contiguous runs of K ranges, added in order through LDS.
+//  * NORM: the rows' 1 / rms from the producers' sums of squares (K-range
+//    order), as the standalone norm forms it.
+//  * Output (n, quad) -- rows 4 quad .. 4 quad + 3 of column n, which one
+//    lane of one unit tile holds as a float4 -- takes 4 / Q threads (Q quads
+//    in the tile): thread part p sums its run of slices in order and its run
+//    of ranks of the LoRA dot; the parts are added in order.
+//  y = bf16(inv (s_t acc + lora_scale t B[n]^T)).
+template <int NS, int MT, int NW, bool NORM>
 __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
+    constexpr int kFinS = 8, kFinB = 4, kFinT = 8;  // loads of each kind issued at once
     const Decode &d = ds.seg[NS == 1 ? 0u : blockIdx.z];
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     const int64_t bx = blockIdx.x;
     if (NS > 1 && bx * 64 >= a.n) return;  // past a narrower segment
     __shared__ float ts[16][kMaxRank];
-    const int tid = threadIdx.x;
-    const int64_t n = bx * 64 + (tid & 63);
-    const int64_t m0 = (int64_t)blockIdx.y * 16;
-    const int64_t quad = blockIdx.y * 4 + (tid >> 6);
-    for (int64_t i = tid; i < 16 * (int64_t)a.r; i += 256) {
-        const int64_t mm = i / a.r, j = i - mm * a.r;
-        ts[mm][j] = m0 + mm < a.m ? d.t32()[(m0 + mm) * a.r + j] : 0.0f;
-    }
-    __syncthreads();
-    if (n >= a.n || 4 * quad >= a.m) return;
+    __shared__ f32x4_t tred[512];
+    __shared__ f32x4_t ored[2][256];
+    __shared__ float s_inv[16];
+    const int tid = threadIdx.x, col = tid & 63, h = tid >> 6;
+    const int mt = (int)blockIdx.y;
+    const int64_t rows = a.m - 16 * (int64_t)mt < 16 ? a.m - 16 * (int64_t)mt : 16;
+    const int Q = (int)((rows + 3) / 4), P = Q == 1 ? 4 : (Q == 2 ? 2 : 1);
+    const int quad_l = h % Q, part = h / Q;  // part < P, except the idle h = 3 when Q = 3
+    const int64_t n = bx * 64 + col, quad = (int64_t)mt * 4 + quad_l;
+    const bool out = n < a.n && part < P;
+    // this output's place in the units' tiles
     const int64_t R = p.rows_per_unit;
-    const int64_t rblk = n / R, rem = n - rblk * R;
+    const int64_t nc = n < a.n ? n : a.n - 1;
+    const int64_t rblk = nc / R, rem = nc - rblk * R;
     const int64_t wave = rem / (16 * NW), g = (rem / 16) % NW, lr = rem % 16;
-    const int64_t mt = quad / 4, lq = quad % 4;
+    const int64_t lq = quad % 4;
     const int64_t slot = ((wave * MT + mt) * NW + g) * 64 + lq * 16 + lr;
     const int64_t tile_floats = R * 16 * MT;
-    const float *part = d.part();
+    const float *part_base = d.part() + rblk * tile_floats + slot * 4;
+    const int64_t sstride = p.row_blocks * tile_floats;  // floats between slices
+    const int pp = part < P ? part : 0;
+    const int64_t s0 = p.slices * pp / P, s1 = p.slices * (pp + 1) / P;
+    // ---- issue: this part's slice tiles, its ranks of B[n], its share of t ----
+    f32x4_t pv[kFinS];
+#pragma unroll
+    for (int u = 0; u < kFinS; ++u) {
+        const int64_t sl = s0 + u < s1 ? s0 + u : (s1 > s0 ? s1 - 1 : s0);
+        pv[u] = *reinterpret_cast<const f32x4_t *>(part_base + sl * sstride);
+    }
+    const bool r8 = (a.r & 7) == 0;
+    const int units8 = a.r / 8;  // 8-rank pieces of B (r % 8 == 0)
+    const int b0 = r8 ? units8 * pp / P : 0, b1 = r8 ? units8 * (pp + 1) / P : 0;
+    const uint16_t *br = a.lora_b + nc * a.r;
+    uint4 bq[kFinB];
+#pragma unroll
+    for (int u = 0; u < kFinB; ++u)
+        bq[u] = b0 + u < b1 ? *reinterpret_cast<const uint4 *>(br + 8 * (b0 + u)) : make_uint4(0, 0, 0, 0);
+    const int JT = (int)p.jt, items = JT * 64, PT = items >= 256 ? 1 : 256 / items;
+    const f32x4_t *tp = reinterpret_cast<const f32x4_t *>(d.tpart()) + ((int64_t)mt * JT) * 64;
+    const int64_t kstride = (int64_t)MT * JT * 64;  // f32x4 between K ranges
+    // (r <= 64: one (item, run) per thread; larger ranks take a second one)
+    auto t_run = [&](int w, int64_t &kr0, int64_t &kr1) {
+        const int q = w / items;
+        kr0 = p.prod_kr * q / PT;
+        kr1 = p.prod_kr * (q + 1) / PT;
+    };
+    f32x4_t tv[kFinT];
+    const bool t_mine = a.r > 0 && tid < items * PT;
+    int64_t kr0 = 0, kr1 = 0;
+    if (t_mine) {
+        t_run(tid, kr0, kr1);
+        const f32x4_t *src = tp + tid % items;
+#pragma unroll
+        for (int u = 0; u < kFinT; ++u) tv[u] = src[(kr0 + u < kr1 ? kr0 + u : (kr1 > kr0 ? kr1 - 1 : kr0)) * kstride];
+    }
+    float ssv[kMaxProdRanges];
+    if (NORM && tid < 16)
+#pragma unroll
+        for (int q = 0; q < kMaxProdRanges; ++q) ssv[q] = q < p.prod_kr ? d.ssp()[q * 16 + tid] : 0.0f;
+    // ---- t and 1 / rms ----
+    if (t_mine) {
+        f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int u = 0; u < kFinT; ++u)
+            if (kr0 + u < kr1) sum = sum + tv[u];
+        for (int64_t k0 = kr0 + kFinT; k0 < kr1; ++k0)  // (more ranges than kFinT: never with the plan's bound)
+            sum = sum + tp[tid % items + k0 * kstride];
+        tred[tid] = sum;  // = tred[q * items + item]
+    }
+    for (int w = tid + 256; a.r > 0 && w < items * PT; w += 256) {  // r > 64
+        int64_t k0, k1;
+        t_run(w, k0, k1);
+        f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int64_t k = k0; k < k1; ++k) sum = sum + tp[w % items + k * kstride];
+        tred[w] = sum;
+    }
+    if (NORM && tid < 16) {
+        float tot = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kMaxProdRanges; ++q) tot += ssv[q];  // zeros past prod_kr
+        s_inv[tid] = 1.0f / sqrtf(tot * (1.0f / (float)a.k) + a.norm_eps);
+    }
+    __syncthreads();
+    if (a.r > 0) {
+        for (int item = tid; item < items; item += 256) {
+            f32x4_t t = tred[item];
+            for (int q = 1; q < PT; ++q) t = t + tred[q * items + item];
+            // tile jt, lane l: t[4 (l / 16) + v][16 jt + l % 16]
+            const int jt = item / 64, l = item % 64, j = 16 * jt + (l & 15);
+            if (j < a.r)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ts[4 * (l >> 4) + v][j] = t[v];
+        }
+        __syncthreads();
+    }
+    // ---- this part's slices and ranks ----
     f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t s0 = 0; s0 < p.slices; s0 += kBatch) {  // kBatch slices in flight, summed in order
-        f32x4_t v[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int64_t s = s0 + u < p.slices ? s0 + u : p.slices - 1;
-            v[u] = *reinterpret_cast<const f32x4_t *>(part + (s * p.row_blocks + rblk) * tile_floats + slot * 4);
+    for (int u = 0; u < kFinS; ++u)
+        if (s0 + u < s1) acc = acc + pv[u];
+    for (int64_t sl = s0 + kFinS; sl < s1; ++sl) acc = acc + *reinterpret_cast<const f32x4_t *>(part_base + sl * sstride);
+    f32x4_t lora = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int q0 = quad_l * 4;  // this output's first row in ts
+    auto dot8 = [&](const uint4 &b8, int j) {
+        const uint32_t bw[4] = {b8.x, b8.y, b8.z, b8.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e], bf16lo_to_f32(bw[e]), lora[v]);
+                lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e + 1], bf16hi_to_f32(bw[e]), lora[v]);
+            }
+    };
+    if (r8) {
+#pragma unroll
+        for (int u = 0; u < kFinB; ++u)
+            if (b0 + u < b1) dot8(bq[u], 8 * (b0 + u));
+        for (int u = b0 + kFinB; u < b1; ++u) dot8(*reinterpret_cast<const uint4 *>(br + 8 * u), 8 * u);
+    } else if (pp == 0) {  // r % 8 != 0: the first part takes every rank
+        for (int j = 0; j < a.r; ++j) {
+            const float b = bf16lo_to_f32(br[j]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) lora[v] = __builtin_fmaf(ts[q0 + v][j], b, lora[v]);
         }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u)
-            if (s0 + u < p.slices) acc = acc + v[u];
     }
-    float lora[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint16_t *br = a.lora_b + n * a.r;
-    const int q0 = (int)(tid >> 6) * 4;  // this thread's first row in ts
-    int j = 0;
-    if ((a.r & 7) == 0) {
-        for (; j < a.r; j += 8) {
-            const uint4 b8 = *reinterpret_cast<const uint4 *>(br + j);
-            const uint32_t bw[4] = {b8.x, b8.y, b8.z, b8.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e], bf16lo_to_f32(bw[e]), lora[v]);
-                    lora[v] = __builtin_fmaf(ts[q0 + v][j + 2 * e + 1], bf16hi_to_f32(bw[e]), lora[v]);
-                }
-        }
-    }
-    for (; j < a.r; ++j) {
-        const float b = bf16lo_to_f32(br[j]);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) lora[v] = __builtin_fmaf(ts[q0 + v][j], b, lora[v]);
+    ored[0][tid] = acc;
+    ored[1][tid] = lora;
+    __syncthreads();
+    if (!out || part != 0) return;
+    for (int q = 1; q < P; ++q) {  // the parts in order
+        acc = acc + ored[0][(q * Q + quad_l) * 64 + col];
+        lora = lora + ored[1][(q * Q + quad_l) * 64 + col];
     }
     const float st = *a.tensor_scale, lam = a.lora_scale;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int64_t m = 4 * quad + v;
-        if (m < a.m) a.y[m * a.ldy + n] = f32_to_bf16_bits(st * acc[v] + lam * lora[v]);
+        const float y = st * acc[v] + lam * lora[v];
+        if (m < a.m) a.y[m * a.ldy + n] = f32_to_bf16_bits(NORM ? s_inv[q0 + v] * y : y);
     }
 }
 
@@ -1145,30 +913,40 @@ __global__ __launch_bounds__(64 * kUnitWaves) void mfma_unit_kernel(DecodeSetN<N
     mfma_unit<MT, SCL>(d, blockIdx.x);
 }
 
+// the finish launch: (column blocks of the widest segment) x m-tiles x segments
+template <int NS, int MT, int NW, bool NORM>
+hipError_t launch_finish(const DecodeSetN<NS> &ds, hipStream_t stream) {
+    int64_t fblocks = 0;
+    for (int i = 0; i < ds.nseg; ++i) {
+        const int64_t f = (ds.seg[i].a.n + 63) / 64;
+        fblocks = f > fblocks ? f : fblocks;
+    }
+    const dim3 fgrid((unsigned)fblocks, (unsigned)((ds.seg[0].a.m + 15) / 16), (unsigned)ds.nseg);
+    hipLaunchKernelGGL((finish_kernel<NS, MT, NW, NORM>), fgrid, dim3(256), 0, stream, ds);
+    return hipGetLastError();
+}
+
 template <int MT, int NS>
 hipError_t launch_mfma_units(const DecodeSetN<NS> &ds, hipStream_t stream) {
     const Decode &d = ds.seg[0];  // the unit shape and scale staging are shared by the segments
-    int64_t blocks = 0, fblocks = 0;
+    int64_t blocks = 0;
     for (int i = 0; i < ds.nseg; ++i) {
-        const int64_t b = ds.seg[i].p.producers + ds.seg[i].p.units, f = (ds.seg[i].a.n + 63) / 64;
+        const int64_t b = ds.seg[i].p.producers + ds.seg[i].p.units;
         blocks = b > blocks ? b : blocks;
-        fblocks = f > fblocks ? f : fblocks;
     }
     const dim3 grid((unsigned)blocks, (unsigned)ds.nseg);
     if (d.p.unit_sc)
         hipLaunchKernelGGL((mfma_unit_kernel<NS, MT, true>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
     else
         hipLaunchKernelGGL((mfma_unit_kernel<NS, MT, false>), grid, dim3(64 * kUnitWaves), 0, stream, ds);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 fgrid((unsigned)fblocks, (unsigned)((d.a.m + 15) / 16), (unsigned)ds.nseg);
-    hipLaunchKernelGGL((finish_kernel<NS, MT, 4 * kUnitWaves / kWaves>), fgrid, dim3(256), 0, stream, ds);
-    return hipGetLastError();
+    return launch_finish<NS, MT, 4 * kUnitWaves / kWaves, false>(ds, stream);
 }
 
-template <bool K32, bool SPLIT, bool LORA, bool NORM, int NS>
+template <bool K32, bool DIRECT, bool LORA, bool NORM, int NS>
 hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_t stream) {
-    auto kern = stream_kernel<NS, K32, SPLIT, LORA, NORM>;
+    auto kern = stream_kernel<NS, K32, DIRECT, LORA, NORM>;
     static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
     if (attr != hipSuccess) return attr;
@@ -1178,26 +956,22 @@ hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_
         blocks = b > blocks ? b : blocks;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ds.nseg), dim3(kThreadsD), (size_t)lds_bytes, stream, ds);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (DIRECT || e != hipSuccess) return e;
+    return launch_finish<NS, 1, 1, NORM>(ds, stream);
 }
 
 template <bool K32, int NS>
-hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, bool lora, hipStream_t stream) {
-    const bool split = ds.seg[0].p.slices > 1;  // the same for every segment
+hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, bool lora, bool direct, hipStream_t stream) {
     if (ds.seg[0].p.norm) {  // the norm prologue: k % 32 == 0 only (checked by the caller)
         if constexpr (K32) {
-            if (split)
-                return lora ? launch_stream<K32, true, true, true>(ds, lds_bytes, stream)
-                            : launch_stream<K32, true, false, true>(ds, lds_bytes, stream);
             return lora ? launch_stream<K32, false, true, true>(ds, lds_bytes, stream)
                         : launch_stream<K32, false, false, true>(ds, lds_bytes, stream);
         } else {
             return hipErrorInvalidValue;
         }
     }
-    if (split)
-        return lora ? launch_stream<K32, true, true, false>(ds, lds_bytes, stream)
-                    : launch_stream<K32, true, false, false>(ds, lds_bytes, stream);
+    if (direct) return launch_stream<K32, true, false, false>(ds, lds_bytes, stream);
     return lora ? launch_stream<K32, false, true, false>(ds, lds_bytes, stream)
                 : launch_stream<K32, false, false, false>(ds, lds_bytes, stream);
 }
@@ -1211,11 +985,10 @@ DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
     for (int i = 0; i < nseg; ++i)
         rows += make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, 0, norm).row_blocks;
     char *base = static_cast<char *>(segs[0].workspace);  // one workspace for the launch
-    int64_t data = kGemmCtrBytes;
+    int64_t data = 0;
     for (int i = 0; i < nseg; ++i) {
         ds.seg[i].a = segs[i];
         ds.seg[i].p = make_decode_plan(segs[i].m, segs[i].n, segs[i].k, segs[i].r, rows, norm);
-        ds.seg[i].ctrs = reinterpret_cast<uint32_t *>(base + i * kSegCtrBytes);
         ds.seg[i].a.workspace = base + data;
         data += align256(ds.seg[i].p.bytes);
     }
@@ -1223,16 +996,17 @@ DecodeSet make_decode_set(const GemmArgs *segs, int nseg) {
 }
 
 template <int NS>
-hipError_t launch_checked(const DecodeSetN<NS> &ds, int64_t lds, bool lora, hipStream_t stream) {
+hipError_t launch_checked(const DecodeSetN<NS> &ds, int64_t lds, bool lora, bool direct, hipStream_t stream) {
     const Decode &d0 = ds.seg[0];
     if (d0.p.mt == 2) return launch_mfma_units<2>(ds, stream);
     if (d0.p.mt == 4) return launch_mfma_units<4>(ds, stream);
-    return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, stream) : launch_stream<false>(ds, lds, lora, stream);
+    return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, direct, stream)
+                              : launch_stream<false>(ds, lds, lora, direct, stream);
 }
 
 hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
     int64_t lds = 0;
-    bool lora = false;
+    bool lora = false, direct = true;
     for (int i = 0; i < ds.nseg; ++i) {
         const Decode &d = ds.seg[i];
         if (d.p.row_blocks < 1 || d.p.lds_bytes > kLdsLimit ||
@@ -1243,31 +1017,18 @@ hipError_t launch_decode_set(const DecodeSet &ds, hipStream_t stream) {
             return hipErrorInvalidConfiguration;
         lds = d.p.lds_bytes > lds ? d.p.lds_bytes : lds;
         lora = lora || d.a.r > 0;
+        direct = direct && d.p.direct_out;
     }
     for (int i = 0; i < ds.nseg; ++i)
         if (ds.seg[i].p.producers + ds.seg[i].p.units > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    if (ds.nseg == 1) return launch_checked(DecodeSetN<1>{{ds.seg[0]}, 1}, lds, lora, stream);
-    return launch_checked(ds, lds, lora, stream);
+    if (ds.nseg == 1) return launch_checked(DecodeSetN<1>{{ds.seg[0]}, 1}, lds, lora, direct, stream);
+    return launch_checked(ds, lds, lora, direct, stream);
 }
-
-// the counter head of a GEMM workspace to zero, 16 bytes per thread
-__global__ __launch_bounds__(256) void zero_head_kernel(uint4 *head) {
-    head[(int64_t)blockIdx.x * 256 + threadIdx.x] = make_uint4(0, 0, 0, 0);
-}
-static_assert(kGemmCtrBytes % (256 * 16) == 0, "whole workgroups of 16-byte stores");
 
 }  // namespace
 
-std::atomic<int> g_force_wait_timeout{0};
-
-hipError_t launch_gemm_workspace_reset(void *workspace, hipStream_t stream) {
-    hipLaunchKernelGGL(zero_head_kernel, dim3((unsigned)(kGemmCtrBytes / (256 * 16))), dim3(256), 0, stream,
-                       static_cast<uint4 *>(workspace));
-    return hipGetLastError();
-}
-
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
-    return (size_t)(kGemmCtrBytes + make_decode_plan(m, n, k, r).bytes);
+    return (size_t)align256(make_decode_plan(m, n, k, r).bytes);
 }
 
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
@@ -1277,7 +1038,7 @@ hipError_t launch_decode(const GemmArgs &a, hipStream_t stream) {
 size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm) {
     int64_t rows = 0;
     for (int j = 0; j < nseg; ++j) rows += make_decode_plan(m, n[j], k, r[j], 0, norm).row_blocks;
-    int64_t bytes = kGemmCtrBytes;
+    int64_t bytes = 0;
     for (int j = 0; j < nseg; ++j) bytes += align256(make_decode_plan(m, n[j], k, r[j], rows, norm).bytes);
     return (size_t)bytes;
 }

@@ -32,9 +32,8 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // Launch plan and workspace layout
 // ---------------------------------------------------------------------------
-// The workspace starts with the decode path's counter region, which this path
-// never touches, then holds the BF16 hi/lo t [m, 2r] and, when K is split,
-// the FP32 partial outputs [splits][m][n].
+// The workspace holds the BF16 hi/lo t [m, 2r] and, when K is split, the
+// FP32 partial outputs [splits][m][n].
 #ifndef QERL_PF_WAVES
 #define QERL_PF_WAVES 4
 #endif
@@ -63,7 +62,7 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     }
     p.bps = (blocks + p.splits - 1) / p.splits;
     if (p.splits > 1) p.splits = (blocks + p.bps - 1) / p.bps;  // no empty split
-    p.t_off = kGemmCtrBytes;
+    p.t_off = 0;
     p.part_off = align256(p.t_off + m * (int64_t)r * 4);
     p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * m * n * 4) : 0);
     return p;

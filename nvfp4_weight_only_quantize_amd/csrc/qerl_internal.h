@@ -7,8 +7,6 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include <atomic>
-
 namespace qerl {
 
 // ---- quantizer ----
@@ -48,26 +46,7 @@ struct GemmArgs {
     float norm_eps = 0.0f;
 };
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
-// Every GEMM workspace starts with the counters of the decode path's in-kernel
-// reductions: kSegCtrBytes for each of up to QERL_MAX_SEGMENTS projections of
-// one call, at fixed places, so that any sequence of calls (single or multi,
-// any shapes) on one workspace finds them zero; every call leaves them zero
-// and nothing else is stored there.  A call's data follow the counters.
 #define QERL_MAX_SEGMENTS 4
-constexpr int64_t kSegCtrBytes = 64 * 1024;
-constexpr int64_t kGemmCtrBytes = QERL_MAX_SEGMENTS * kSegCtrBytes;
-// Word kGemmCtrErrWord of each segment's counter block is its error word:
-// kGemmErrWaitTimeout after a bounded in-kernel wait gave up (that row
-// block's outputs are then NaN).  Every other word is a counter.
-constexpr int kGemmCtrErrWord = 3;
-constexpr uint32_t kGemmErrWaitTimeout = 1u;
-// Test hook: while set, the decode kernels' bounded waits wait for a count
-// that is never reached and give up after one poll, so the error path runs
-// with every kernel still exiting normally (set by qerl_debug_force_wait_timeout).
-extern std::atomic<int> g_force_wait_timeout;
-// Zero the counter head of a GEMM workspace (a fill kernel: no memset node
-// ends up in a captured graph).
-hipError_t launch_gemm_workspace_reset(void *workspace, hipStream_t stream);
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
 // decode batches (m <= kDecodeMaxM): HBM-streaming path in decode.hip
 constexpr int64_t kDecodeMaxM = 64;

@@ -227,9 +227,9 @@ def test_gpu_quantizer_feeds_gemm():
 
 
 def test_shared_workspace_sequence_is_deterministic():
-    """One zero-filled workspace serves a mixed sequence of calls (decode with and
-    without split K and LoRA, and the large-m path); each output equals the one
-    from a fresh workspace bit for bit, and the counter region ends zero."""
+    """One workspace, filled with garbage first, serves a mixed sequence of
+    calls (decode with and without split K and LoRA, and the large-m path);
+    each output equals the one from a fresh workspace bit for bit."""
     cases = [(1, 3584, 3584, 32), (8, 512, 3584, 32), (64, 18944 // 4, 3584, 32), (33, 1000, 3600, 24),
              (1, 3584, 18944 // 2, 0), (100, 512, 1024, 16), (16, 77, 512, 8), (64, 3584, 3584, 32)]
     layers, xs = [], []
@@ -237,55 +237,13 @@ def test_shared_workspace_sequence_is_deterministic():
         layers.append(Layer(n, k, r, seed=900 + i))
         xs.append(bits_to_gpu(_x(m, k, seed=950 + i)))
     need = max(q.w4a16_lora_gemm_workspace_size(m, n, k, r) for m, n, k, r in cases)
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev())
     fresh = [q.w4a16_lora_gemm(x, L.wq, L.a, L.b, L.lam) for x, L in zip(xs, layers)]
     for _ in range(3):
         for i, (x, L) in enumerate(zip(xs, layers)):
             y = q.w4a16_lora_gemm(x, L.wq, L.a, L.b, L.lam, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(y, fresh[i]), f"case {cases[i]}"
-    assert int(torch.count_nonzero(ws[:256 * 1024])) == 0  # the counter head
     for i in (0, 3):
         m, n, k, r = cases[i]
         assert_gemm_close(bf16_to_f64(fresh[i]), layers[i].ref(synth.bf16_bits(xs[i].cpu())), f"case {cases[i]}")
-
-
-def test_wait_timeout_is_reported_and_cleared():
-    """A bounded wait that gives up (forced from the host: the kernels wait for
-    a count that never comes, one poll) writes NaN outputs and sets the error
-    word; the workspace check reports it, the reset clears it, and the next
-    call is correct again."""
-    n, k, r = 512, 3584, 32
-    L = Layer(n, k, r, seed=980)
-    x = _x(1, k, seed=981)
-    ws = torch.zeros(q.w4a16_lora_gemm_workspace_size(1, n, k, r), dtype=torch.uint8, device=dev())
-    q.gemm_workspace_check(ws)  # a fresh zero-filled workspace is healthy
-    q._debug_force_wait_timeout(True)
-    try:
-        y = q.w4a16_lora_gemm(bits_to_gpu(x), L.wq, L.a, L.b, L.lam, workspace=ws)
-        torch.cuda.synchronize()
-    finally:
-        q._debug_force_wait_timeout(False)
-    assert torch.isnan(y.float()).all()
-    with pytest.raises(q.QerlError) as err:
-        q.gemm_workspace_check(ws)
-    assert err.value.status == 6 and "gave up" in str(err.value)
-    q.gemm_workspace_reset(ws)
-    q.gemm_workspace_check(ws)
-    y = q.w4a16_lora_gemm(bits_to_gpu(x), L.wq, L.a, L.b, L.lam, workspace=ws)
-    torch.cuda.synchronize()
-    assert_gemm_close(bf16_to_f64(y), L.ref(x), "after reset")
-    q.gemm_workspace_check(ws)
-
-
-def test_workspace_check_sees_nonzero_counters():
-    n, k, r = 96, 256, 16
-    ws = torch.zeros(q.w4a16_lora_gemm_workspace_size(1, n, k, r), dtype=torch.uint8, device=dev())
-    ws[4 * 10] = 1  # a row counter left behind
-    with pytest.raises(q.QerlError) as err:
-        q.gemm_workspace_check(ws)
-    assert err.value.status == 5
-    q.gemm_workspace_reset(ws)
-    torch.cuda.synchronize()
-    assert int(torch.count_nonzero(ws[:256 * 1024])) == 0
-    q.gemm_workspace_check(ws)

@@ -51,16 +51,15 @@ def test_multi_mixed_ranks_and_widths(m):
 
 
 def test_multi_shared_workspace_is_repeatable():
-    # one zero-filled workspace over a sequence of multi and single calls of
-    # different shapes: every repeat is bit-identical to the first, and the
-    # counter head (256 KiB: one 64 KiB block per segment) ends zero
+    # one workspace (any contents) over a sequence of multi and single calls
+    # of different shapes: every repeat is bit-identical to the first
     k = 3584
     qkv = [Layer(synth.QWEN25_7B[p][0], k, 32, seed=synth.seed_for(1008, p)) for p in ("q", "k", "v")]
     gu = [Layer(synth.QWEN25_7B[p][0], k, 32, seed=synth.seed_for(1008, p)) for p in ("gate", "up")]
     cases = [(1, qkv), (8, gu), (64, qkv), (3, gu)]
     need = max(max(q.w4a16_lora_gemm_multi_workspace_size(m, k, [(L.n, L.r) for L in ls]),
                    q.w4a16_lora_gemm_workspace_size(m, qkv[0].n, k, 32)) for m, ls in cases)
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=dev())  # any contents
     xs = {m: bits_to_gpu(_x(m, k, seed=1300 + m)) for m, _ in cases}
     first = None
     for rep in range(3):
@@ -75,4 +74,3 @@ def test_multi_shared_workspace_is_repeatable():
             for a, b in zip(first, got):
                 for ya, yb in zip(a, b):
                     assert torch.equal(ya, yb)
-    assert int(ws.view(torch.int32)[:65536].abs().sum()) == 0

@@ -124,14 +124,14 @@ def test_noisy_weight_matches_oracle_and_the_norm():
 
 def test_norm_shared_workspace_is_repeatable():
     # fused-norm calls, plain multi calls and single calls of several shapes on
-    # one zero-filled workspace: every repeat is bit-identical, the head ends zero
+    # one workspace (any contents): every repeat is bit-identical
     k = 3584
     qkv = [Layer(synth.QWEN25_7B[p][0], k, 32, seed=synth.seed_for(1019, p)) for p in ("q", "k", "v")]
     gu = [Layer(synth.QWEN25_7B[p][0], k, 32, seed=synth.seed_for(1019, p)) for p in ("gate", "up")]
     cases = [(1, qkv), (8, gu), (16, qkv), (24, gu), (3, gu)]
     need = max(max(q.rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, k, [(L.n, L.r) for L in ls]),
                    q.w4a16_lora_gemm_multi_workspace_size(m, k, [(L.n, L.r) for L in ls])) for m, ls in cases)
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    ws = torch.full((need,), 0x5A, dtype=torch.uint8, device=dev())  # any contents
     _, wn = _noisy(k, 2900)
     wg = torch.from_numpy(wn).to(dev())
     xs = {m: bits_to_gpu(_x(m, k, seed=3000 + m)) for m, _ in cases}
@@ -149,4 +149,3 @@ def test_norm_shared_workspace_is_repeatable():
             for a, b in zip(first, got):
                 for ya, yb in zip(a, b):
                     assert torch.equal(ya, yb)
-    assert int(ws.view(torch.int32)[:65536].abs().sum()) == 0
