@@ -1,32 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of the QeRL rollout-phase linear layer on one MI355X.
 
-One *step* is the decode pass of a Qwen2.5-7B-shaped decoder layer through
-every operation of the hot path, at each decode batch M in {1, 8, 64}:
+One *step* is the decode pass of two synthetic decoder layers through every
+operation of the hot path:
 
-    AQN RMSNorm (attention)  -> q, k, v   (NVFP4 W4A16 + LoRA r=32, alpha=64)
-    o                        (synthetic attention output as input)
-    AQN RMSNorm (MLP)        -> gate, up
-    down                     (synthetic activation as input)
+  * a Qwen2.5-7B-shaped layer at decode batch M in {1, 8, 64}, and
+  * a Qwen2.5-32B-shaped layer at batched-rollout M in {16, 64},
+
+each as  AQN RMSNorm -> q|k|v,  o,  AQN RMSNorm -> gate|up,  down  (NVFP4
+W4A16 + LoRA r=32, alpha=64 on all seven projections; o and down take
+synthetic inputs, where attention and the MLP activation would sit).
 
 The AQN noise is that of one RL step (sigma of stage 3 of the exponential
 schedule 1e-2 -> 5e-4 over 10 stages): drawn once, as every decode step of a
-rollout uses the same noisy norm weight.  By default each norm runs inside the
-call of the projections that read it (qerl_rmsnorm_w4a16_lora_gemm_multi).  Weights are cold: 8 copies of the layer's
-NVFP4 weights and LoRA (~1.1 GB, far above the 256 MB Infinity Cache) rotate
-so that no weight is re-read from cache.  The steps run as one captured HIP
-graph (the decode loop is launch-bound otherwise).
+rollout uses the same noisy norm weight; each norm runs inside the call of the
+projections that read it (qerl_rmsnorm_w4a16_lora_gemm_multi).  Weights are
+cold: rotating copies of each layer's NVFP4 weights and LoRA (about 1.1 GB per
+layer, far above the 256 MB Infinity Cache) so that no weight is re-read from
+cache.  The steps run as one captured HIP graph.
 
 ``value`` = algorithmic bytes of a step / wall time of a step (GB/s), inputs
 resident in HBM.  Algorithmic bytes per projection call:
     N*K/2 + N*K/16 + 4 (NVFP4 weight) + 2*r*(K + N) (LoRA) + 2*M*(K + N) (x, y)
-and per norm call: 2*M*H (x) + 4*H (weight) + 2*M*H (BF16 out).
+and per norm: 2*M*H (x) + 4*H (weight) + 2*M*H (BF16 out).
 
-Extra legs in the same JSON line: ``prefill`` (32B-shaped layer, M in {2048,
-8192}, TFLOP/s vs the BF16 MFMA peak), ``quantizer`` (BF16 -> NVFP4 of a
-32B-shaped layer, GB/s at 4.5625 B/element), ``roofline`` (the W4A16 decode
-GEMM calls: bytes / measured duration) and ``cpu_baseline`` (the CPU oracle on
-a bounded sample of the same decode workload).
+Other legs in the same JSON line: ``roofline`` (the decode GEMM call class
+with the larger share of the step), ``decode_32b_large_m`` (the 32B layer at
+M 128 and 256, past the ridge: both roofline fractions), ``prefill`` (32B
+layer, M in {2048, 8192}, TFLOP/s), ``quantizer`` (one 32B layer; the whole
+64-layer 32B model streamed layer by layer; the 2048 x 2048 single layer),
+``single_layer_2048`` (the W4A16 + LoRA GEMM of that layer at M = 1),
+``aqn_rmsnorm`` (the norm alone), ``cpu_baseline`` (the CPU oracle on a
+bounded sample of the decode workload) and the comparison and update-phase
+legs.
 """
 from __future__ import annotations
 
@@ -49,12 +55,18 @@ from nvfp4_weight_only_quantize_amd import synth  # noqa: E402
 METRIC = "W4A16-NVFP4+LoRA GEMM: decode HBM GB/s (%peak), prefill TFLOPS (%MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-DECODE_MS = (1, 8, 64)
 PREFILL_MS = (2048, 8192)
 RANK, ALPHA = 32, 64
 SIGMA0, SIGMA1, STAGES, EPS = 1e-2, 5e-4, 10, 1e-6
 RL_STEP = 3  # the RL step (noise stage) the decode steps belong to
 SEED = 1002
+
+# the decoder layers of a step: shapes, hidden and intermediate widths,
+# decode batches, master seed, cold copies
+LAYER_7B = dict(name="qwen2.5-7b", shapes=synth.QWEN25_7B, hidden=3584, inter=18944, ms=(1, 8, 64), seed=1002,
+                copies=8)
+LAYER_32B = dict(name="qwen2.5-32b", shapes=synth.QWEN25_32B, hidden=5120, inter=27648, ms=(16, 64), seed=1003,
+                 copies=4)
 
 
 def log(*a):
@@ -71,6 +83,12 @@ def gemm_flops(m, n, k, r):
 
 def norm_bytes(m, h):
     return 2 * m * h + 4 * h + 2 * m * h
+
+
+def pct(v, lo, hi):
+    """(p10, p50, p90) of a list."""
+    a = np.sort(np.asarray(v, dtype=np.float64))
+    return tuple(float(np.percentile(a, x)) for x in (lo, 50, hi))
 
 
 class Proj:
@@ -99,44 +117,43 @@ def make_layer(shapes, seed, dev, r=RANK, row_sigma=0.5, outlier_rows=0.0):
 
 
 class DecodeLayer:
-    """Buffers and the launch sequence of one decode step (7B shapes)."""
+    """Buffers and the launch sequence of one decoder layer's decode pass."""
 
-    def __init__(self, dev, copies, launch="fused"):
-        self.dev = dev
-        self.launch = launch
-        self.shapes = synth.QWEN25_7B
-        h, inter = 3584, 18944
+    def __init__(self, cfg, dev, copies=None, launch="fused"):
+        self.cfg, self.dev, self.launch = cfg, dev, launch
+        self.shapes, self.ms = cfg["shapes"], cfg["ms"]
+        h, inter, seed = cfg["hidden"], cfg["inter"], cfg["seed"]
         self.h = h
-        base = make_layer(self.shapes, SEED, dev)
-        self.copies = [base] + [{k: p.clone() for k, p in base.items()} for _ in range(copies - 1)]
-        mmax = max(DECODE_MS)
-        self.h_attn = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "h_attn"), 0.005, device=dev)
-        self.h_mlp = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "h_mlp"), 0.005, device=dev)
-        self.x_o = synth.activation_bf16(mmax, h, synth.seed_for(SEED, "x_o"), 0.005, device=dev)
-        self.x_down = synth.activation_bf16(mmax, inter, synth.seed_for(SEED, "x_down"), 0.005, device=dev)
-        self.w_attn = synth.norm_weight_f32(h, synth.seed_for(SEED, "w_attn"), device=dev)
-        self.w_mlp = synth.norm_weight_f32(h, synth.seed_for(SEED, "w_mlp"), device=dev)
+        base = make_layer(self.shapes, seed, dev)
+        ncopy = copies or cfg["copies"]
+        self.copies = [base] + [{k: p.clone() for k, p in base.items()} for _ in range(ncopy - 1)]
+        mmax = max(self.ms)
+        self.h_attn = synth.activation_bf16(mmax, h, synth.seed_for(seed, "h_attn"), 0.005, device=dev)
+        self.h_mlp = synth.activation_bf16(mmax, h, synth.seed_for(seed, "h_mlp"), 0.005, device=dev)
+        self.x_o = synth.activation_bf16(mmax, h, synth.seed_for(seed, "x_o"), 0.005, device=dev)
+        self.x_down = synth.activation_bf16(mmax, inter, synth.seed_for(seed, "x_down"), 0.005, device=dev)
+        self.w_attn = synth.norm_weight_f32(h, synth.seed_for(seed, "w_attn"), device=dev)
+        self.w_mlp = synth.norm_weight_f32(h, synth.seed_for(seed, "w_mlp"), device=dev)
         self.x_attn = torch.empty((mmax, h), dtype=torch.bfloat16, device=dev)
         self.x_mlp = torch.empty((mmax, h), dtype=torch.bfloat16, device=dev)
         self.y = {name: torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
                   for name, (n, _k) in self.shapes.items()}
-        ws = max(q.w4a16_lora_gemm_workspace_size(mmax, n, k, RANK) for n, k in self.shapes.values())
+        ws = max(q.w4a16_lora_gemm_workspace_size(m, n, k, RANK) for n, k in self.shapes.values() for m in self.ms)
         for group in (("q", "k", "v"), ("gate", "up")):
-            for m in DECODE_MS:
+            for m in self.ms:
                 shp = [(self.shapes[g][0], RANK) for g in group]
                 ws = max(ws, q.w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1], shp),
                          q.rmsnorm_w4a16_lora_gemm_multi_workspace_size(m, self.shapes[group[0]][1], shp))
         # one workspace per concurrent GEMM (calls that overlap must not share one)
-        self.ws = [torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev) for _ in range(3)]
+        self.ws = [torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) for _ in range(3)]
         # side streams for the independent projections (default priority)
         self.side = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
         # AQN: the noise of one RL step is drawn once and every decode step of
         # the rollout reuses it (the fused launches take the noisy weight; the
         # standalone norm redraws the same vector on each call)
         self.sigma = q.aqn_sigma(RL_STEP, STAGES, SIGMA0, SIGMA1)
-        self.wn_attn = q.aqn_noisy_weight(self.w_attn, self.sigma, SEED, RL_STEP, 0)
-        self.wn_mlp = q.aqn_noisy_weight(self.w_mlp, self.sigma, SEED, RL_STEP, 1)
-        # the normed rows, for the calls that take them from the standalone norm
+        self.wn_attn = q.aqn_noisy_weight(self.w_attn, self.sigma, seed, RL_STEP, 0)
+        self.wn_mlp = q.aqn_noisy_weight(self.w_mlp, self.sigma, seed, RL_STEP, 1)
         self.norm("attn", mmax)
         self.norm("mlp", mmax)
 
@@ -160,38 +177,43 @@ class DecodeLayer:
     def norm(self, which, m):
         src, w, dst, layer = ((self.h_attn, self.w_attn, self.x_attn, 0) if which == "attn"
                               else (self.h_mlp, self.w_mlp, self.x_mlp, 1))
-        q.aqn_rmsnorm(src[:m], w, EPS, self.sigma, SEED, RL_STEP, layer, want_f32=False, y_bf16=dst[:m])
+        q.aqn_rmsnorm(src[:m], w, EPS, self.sigma, self.cfg["seed"], RL_STEP, layer, want_f32=False,
+                      y_bf16=dst[:m])
+
+    def step_m(self, s, m, mi, on_gemm=None):
+        """The layer's decode pass at batch m (copy chosen by step s)."""
+        c = (len(self.ms) * s + mi) % len(self.copies)
+        fused = on_gemm is None and self.launch == "fused"
+        if not fused:
+            self.norm("attn", m)
+        if on_gemm is None and self.launch != "serial":
+            # q, k and v read the same normed input and nothing else: one call
+            # with the norm (or side by side on side streams after it); o
+            # waits for all three (in a real layer attention sits in between),
+            # as the MLP waits for o
+            if fused:
+                self.norm_gemm_multi("attn", ("q", "k", "v"), m, c)
+            else:
+                self._parallel(("q", "k", "v"), m, c)
+            self.gemm("o", m, c)
+        else:
+            for name in ("q", "k", "v", "o"):
+                self._g(name, m, c, on_gemm)
+        if not fused:
+            self.norm("mlp", m)
+        if on_gemm is None and self.launch != "serial":
+            if fused:
+                self.norm_gemm_multi("mlp", ("gate", "up"), m, c)
+            else:
+                self._parallel(("gate", "up"), m, c)  # down waits for both
+            self.gemm("down", m, c)
+        else:
+            for name in ("gate", "up", "down"):
+                self._g(name, m, c, on_gemm)
 
     def step(self, s, on_gemm=None):
-        for mi, m in enumerate(DECODE_MS):
-            c = (len(DECODE_MS) * s + mi) % len(self.copies)
-            fused = on_gemm is None and self.launch == "fused"
-            if not fused:
-                self.norm("attn", m)
-            if on_gemm is None and self.launch != "serial":
-                # q, k and v read the same normed input and nothing else: one
-                # call with the norm (or side by side on side streams after
-                # it); o waits for all three (in a real layer attention sits
-                # in between), as the MLP waits for o
-                if fused:
-                    self.norm_gemm_multi("attn", ("q", "k", "v"), m, c)
-                else:
-                    self._parallel(("q", "k", "v"), m, c)
-                self.gemm("o", m, c)
-            else:
-                for name in ("q", "k", "v", "o"):
-                    self._g(name, m, c, on_gemm)
-            if not fused:
-                self.norm("mlp", m)
-            if on_gemm is None and self.launch != "serial":
-                if fused:
-                    self.norm_gemm_multi("mlp", ("gate", "up"), m, c)
-                else:
-                    self._parallel(("gate", "up"), m, c)  # down waits for both
-                self.gemm("down", m, c)
-            else:
-                for name in ("gate", "up", "down"):
-                    self._g(name, m, c, on_gemm)
+        for mi, m in enumerate(self.ms):
+            self.step_m(s, m, mi, on_gemm)
 
     def _parallel(self, names, m, c):
         """names[0] on the current stream, the rest on side streams, joined
@@ -212,17 +234,16 @@ class DecodeLayer:
         else:
             on_gemm(name, m, lambda: self.gemm(name, m, c))
 
+    def bytes_m(self, m):
+        return 2 * norm_bytes(m, self.h) + sum(gemm_bytes(m, n, k, RANK) for n, k in self.shapes.values())
+
     def step_bytes(self):
-        tot = 0
-        for m in DECODE_MS:
-            tot += 2 * norm_bytes(m, self.h)
-            tot += sum(gemm_bytes(m, n, k, RANK) for n, k in self.shapes.values())
-        return tot
+        return sum(self.bytes_m(m) for m in self.ms)
 
 
 def time_graph(fn_steps, steps, warmup):
     """Capture `steps` calls of fn (and `warmup` separately) as HIP graphs;
-    returns ms per step."""
+    returns ms per step and the graphs."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -246,88 +267,112 @@ def time_graph(fn_steps, steps, warmup):
     return t0.elapsed_time(t1) / steps, (g_warm, g_main)
 
 
-def per_call_durations(layer: DecodeLayer, reps: int):
-    """Event-timed duration of every W4A16 GEMM call of `reps` steps, enqueued
-    behind a GPU sleep so that host enqueue time does not leak into them."""
-    recs = []
-
-    def on_gemm(name, m, run):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
+def replay_percentiles(fn, reps=120, warm=20):
+    """fn() captured as one graph and replayed reps times, an event pair
+    around each replay: (p10, p50, p90) in microseconds."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in evs:
         e0.record()
-        run()
+        g.replay()
         e1.record()
-        n, k = layer.shapes[name]
-        recs.append((name, m, gemm_bytes(m, n, k, RANK), e0, e1))
-
     torch.cuda.synchronize()
-    torch.cuda._sleep(int(2e8))  # keep the GPU busy while the host enqueues
-    for s in range(reps):
-        layer.step(1000 + s, on_gemm)
-    torch.cuda.synchronize()
-    return [(name, m, b, e0.elapsed_time(e1) * 1e-3) for name, m, b, e0, e1 in recs]
+    del g
+    return pct([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs], 10, 90)
 
 
-def check_decode_parity(layer: DecodeLayer):
-    """GPU outputs vs the CPU oracle at M = 1: the five projections behind a
-    norm through the fused norm call (oracle: RMSNorm then the layer), and
-    all seven projections as single calls."""
+def check_decode_parity(layers):
+    """GPU outputs vs the CPU oracle: for each layer at its smallest M, the
+    five projections behind a norm through the fused norm call (oracle:
+    RMSNorm then the layer), and o and down as single calls.  Worst relative
+    L2 error."""
     import oracle
     worst = 0.0
-    for which, names in (("attn", ("q", "k", "v")), ("mlp", ("gate", "up"))):
-        layer.norm_gemm_multi(which, names, 1, 0)
-        torch.cuda.synchronize()
-        src, wn = (layer.h_attn, layer.wn_attn) if which == "attn" else (layer.h_mlp, layer.wn_mlp)
-        x = synth.bf16_bits(src[:1])
-        for name in names:
+    for layer in layers:
+        m = min(layer.ms)
+        for which, names in (("attn", ("q", "k", "v")), ("mlp", ("gate", "up"))):
+            layer.norm_gemm_multi(which, names, m, 0)
+            torch.cuda.synchronize()
+            src, wn = (layer.h_attn, layer.wn_attn) if which == "attn" else (layer.h_mlp, layer.wn_mlp)
+            x = synth.bf16_bits(src[:m])
+            for name in names:
+                p = layer.copies[0][name]
+                y = layer.y[name][:m].float().cpu().numpy().astype(np.float64)
+                ref = oracle.rmsnorm_w4a16_lora_gemm(x, wn.cpu().numpy(), EPS, p.wq.packed.cpu().numpy(),
+                                                     p.wq.scales.cpu().numpy(), np.float32(p.wq.tensor_scale.item()),
+                                                     synth.bf16_bits(p.a), synth.bf16_bits(p.b), ALPHA / RANK,
+                                                     threads=16)
+                worst = max(worst, float(np.linalg.norm(y - ref) / np.linalg.norm(ref)))
+        for name in ("o", "down"):
             p = layer.copies[0][name]
-            y = layer.y[name][:1].float().cpu().numpy().astype(np.float64)
-            ref = oracle.rmsnorm_w4a16_lora_gemm(x, wn.cpu().numpy(), EPS, p.wq.packed.cpu().numpy(),
-                                                 p.wq.scales.cpu().numpy(), np.float32(p.wq.tensor_scale.item()),
-                                                 synth.bf16_bits(p.a), synth.bf16_bits(p.b), ALPHA / RANK,
-                                                 threads=16)
+            x = synth.bf16_bits(layer.inputs_of(name)[:m])
+            layer.gemm(name, m, 0)
+            torch.cuda.synchronize()
+            y = layer.y[name][:m].float().cpu().numpy().astype(np.float64)
+            ref = oracle.w4a16_lora_gemm(x, p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
+                                         np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a),
+                                         synth.bf16_bits(p.b), ALPHA / RANK, threads=16)
             worst = max(worst, float(np.linalg.norm(y - ref) / np.linalg.norm(ref)))
-    for name in synth.PROJ_ORDER:
-        p = layer.copies[0][name]
-        x = synth.bf16_bits(layer.inputs_of(name)[:1])
-        layer.gemm(name, 1, 0)
-        torch.cuda.synchronize()
-        y = layer.y[name][:1].float().cpu().numpy().astype(np.float64)
-        ref = oracle.w4a16_lora_gemm(x, p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
-                                     np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a),
-                                     synth.bf16_bits(p.b), ALPHA / RANK, threads=16)
-        rel = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
-        worst = max(worst, rel)
     return worst
 
 
-def cpu_baseline(layer: DecodeLayer, budget_s: float):
-    """The CPU oracle on a bounded sample of the decode workload: the seven
-    projections at M = 1 (the whole 7B layer's weights), then M = 8 and 64,
-    while the time budget lasts.  Same algorithmic-bytes accounting as the GPU."""
+def host_cpu():
+    """(threads the oracle may use here, CPU model name)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    # a GPU box's share of the host is 16 threads, whatever the affinity mask shows
+    return min(16, avail), model
+
+
+def cpu_baseline(layers, budget_s: float):
+    """The CPU oracle on the decode step's projections: the 7B layer's seven
+    at M = 1, 8, 64, then the 32B layer's at M = 16, 64 (one whole step of
+    GEMM work), stopping early once the time budget is spent.  Same
+    algorithmic-bytes accounting as the GPU."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
-    host = {}
-    for name in synth.PROJ_ORDER:
-        p = layer.copies[0][name]
-        host[name] = (p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
-                      np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a), synth.bf16_bits(p.b))
-    xs = {name: synth.bf16_bits(layer.inputs_of(name)[:max(DECODE_MS)]) for name in synth.PROJ_ORDER}
+    threads, model = host_cpu()
     done_bytes, t_used, sample = 0, 0.0, []
-    for m in DECODE_MS:
+    for L in layers:
+        host = {}
         for name in synth.PROJ_ORDER:
-            if t_used > budget_s:
-                break
-            n, k = layer.shapes[name]
-            packed, scales, st, a, b = host[name]
-            t0 = time.perf_counter()
-            oracle.w4a16_lora_gemm(xs[name][:m], packed, scales, st, a, b, ALPHA / RANK, threads=threads)
-            t_used += time.perf_counter() - t0
-            done_bytes += gemm_bytes(m, n, k, RANK)
-            sample.append(f"{name}@M={m}")
+            p = L.copies[0][name]
+            host[name] = (p.wq.packed.cpu().numpy(), p.wq.scales.cpu().numpy(),
+                          np.float32(p.wq.tensor_scale.item()), synth.bf16_bits(p.a), synth.bf16_bits(p.b))
+        xs = {name: synth.bf16_bits(L.inputs_of(name)[:max(L.ms)]) for name in synth.PROJ_ORDER}
+        for m in L.ms:
+            for name in synth.PROJ_ORDER:
+                if t_used > budget_s:
+                    break
+                n, k = L.shapes[name]
+                packed, scales, st, a, b = host[name]
+                t0 = time.perf_counter()
+                oracle.w4a16_lora_gemm(xs[name][:m], packed, scales, st, a, b, ALPHA / RANK, threads=threads)
+                t_used += time.perf_counter() - t0
+                done_bytes += gemm_bytes(m, n, k, RANK)
+                sample.append(f"{L.cfg['name']} {name}@M={m}")
+        del host, xs
     return {"value": done_bytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"fp64 oracle W4A16+LoRA on the 7B layer: {', '.join(sample)} "
-                      f"({done_bytes / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
+            "cpu_model": model,
+            "sample": f"fp64 oracle W4A16+LoRA, {len(sample)} projection calls of the step ({sample[0]} .. "
+                      f"{sample[-1]}; {done_bytes / 1e6:.1f} MB algorithmic, {t_used:.1f} s)"}
 
 
 def _graph_us(fn, reps):
@@ -364,7 +409,7 @@ def bf16_lora_leg(layer: DecodeLayer, reps: int = 5):
                       for name, (n, k) in layer.shapes.items()})
     lam = ALPHA / RANK
     out = {}
-    for m in DECODE_MS:
+    for m in layer.ms:
         def ours(s, m=m):
             c = (s * 3 + 1) % ncopy
             for name in synth.PROJ_ORDER:
@@ -394,10 +439,10 @@ def lora_rank_leg(layer: DecodeLayer, ranks=(8, 16, 32, 64, 128), reps: int = 5)
     for r in ranks:
         loras = [{name: synth.lora_bf16(n, k, r, seed=synth.seed_for(SEED, name, "rank", r, c), device=dev)
                   for name, (n, k) in layer.shapes.items()} for c in range(ncopy)]
-        ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(max(DECODE_MS), n, k, r)
+        ws = torch.empty(max(q.w4a16_lora_gemm_workspace_size(max(layer.ms), n, k, r)
                              for n, k in layer.shapes.values()), dtype=torch.uint8, device=dev)
         row = {}
-        for m in DECODE_MS:
+        for m in layer.ms:
             def fn(s, m=m):
                 c = (s * 3 + 2) % ncopy
                 for name in synth.PROJ_ORDER:
@@ -430,12 +475,12 @@ def prefill_leg(dev, reps):
     b[n:, RANK:] = layer["up"].b
     projs = {"q": (layer["q"], RANK), "k": (layer["k"], RANK), "v": (layer["v"], RANK),
              "o": (layer["o"], RANK), "gate_up": (Proj(gu, a, b), 2 * RANK), "down": (layer["down"], RANK)}
-    out = {}
+    out, tot_flops, tot_t = {}, 0, 0.0
     for m in PREFILL_MS:
         xk = {kk: synth.activation_bf16(m, kk, synth.seed_for(1004, "x", m, kk), 0.005, device=dev)
               for kk in {5120, 27648}}
         ys = {nm: torch.empty((m, p.wq.shape[0]), dtype=torch.bfloat16, device=dev) for nm, (p, _r) in projs.items()}
-        ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(m, p.wq.shape[0], p.wq.shape[1], r)
+        ws = torch.empty(max(q.w4a16_lora_gemm_workspace_size(m, p.wq.shape[0], p.wq.shape[1], r)
                              for p, r in projs.values()), dtype=torch.uint8, device=dev)
 
         def run():
@@ -454,7 +499,14 @@ def prefill_leg(dev, reps):
         flops = sum(gemm_flops(m, p.wq.shape[0], p.wq.shape[1], r) for p, r in projs.values())
         out[f"M={m}"] = {"ms": t * 1e3, "tflops": flops / t / 1e12,
                          "frac": flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS}
+        tot_flops += flops
+        tot_t += t
         del xk, ys, ws
+    # the layer aggregate over both M: sum of flops / sum of time
+    out.update({"value": tot_flops / tot_t / 1e12, "unit": "TFLOP/s",
+                "frac": tot_flops / tot_t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                "workload": "Qwen2.5-32B-shaped layer, q/k/v/o, fused gate|up [55296, 5120] (rank-64 "
+                            "block-diagonal LoRA) and down, NVFP4 W4A16 + LoRA, M in {2048, 8192}"})
     return out
 
 
@@ -484,9 +536,148 @@ def quantizer_leg(dev, reps):
     torch.cuda.synchronize()
     t = e0.elapsed_time(e1) * 1e-3 / reps
     gbs = elems * 4.5625 / t / 1e9
-    return {"workload": "BF16->NVFP4 of one Qwen2.5-32B-shaped layer (7 tensors, 1.09 G elements)",
-            "ms": t * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
-            "whole_model_ms_est": t * 1e3 * 64}
+    return {"workload": f"BF16->NVFP4 of one Qwen2.5-32B-shaped layer (7 tensors, {elems / 1e9:.3f} G elements)",
+            "ms": t * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}
+
+
+def model_quantizer_leg(dev, layers=64, verify_layers=(0, 37), verify=True):
+    """The whole 64-layer Qwen2.5-32B-shaped weight set quantized layer by
+    layer: each layer's seven BF16 tensors are generated on the GPU (W ~ N(0,
+    0.02^2), 0.1% outlier rows x20), quantized into the resident NVFP4 model,
+    and freed.  GPU time = the quantize calls of every layer, event-timed per
+    layer; the whole pass (generation included) is timed too.  A seeded
+    sample of layers is compared bit for bit with the CPU oracle.  Memory: the
+    quantized model (plus the BF16 embedding and lm_head of 152064 x 5120,
+    kept in 16 bits) against the all-BF16 model."""
+    shapes = synth.QWEN25_32B
+    ws = torch.empty(q.nvfp4_quantize_workspace_size(1, 16), dtype=torch.uint8, device=dev)
+    model, evs, checks = [], [], []
+    elems = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for li in range(layers):
+        ws_in = {}
+        for name in synth.PROJ_ORDER:
+            n, k = shapes[name]
+            ws_in[name] = synth.weight_bf16(n, k, seed=synth.seed_for(1005, li, name), outlier_row_frac=0.001,
+                                            device=dev)
+        outs = {name: q.NVFP4Weight(torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev),
+                                    torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev),
+                                    torch.empty(1, dtype=torch.float32, device=dev)) for name, w in ws_in.items()}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for name in synth.PROJ_ORDER:
+            q.nvfp4_quantize(ws_in[name], out=outs[name], workspace=ws, check_finite=False)
+        e1.record()
+        evs.append((e0, e1))
+        elems += sum(w.numel() for w in ws_in.values())
+        if verify and li in verify_layers:
+            checks.append((li, {name: synth.bf16_bits(w) for name, w in ws_in.items()}))
+        model.append(outs)
+        del ws_in
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_q = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e-3
+    bad = []
+    if verify:
+        import oracle
+        threads, _ = host_cpu()
+        for li, bits in checks:
+            for name in synth.PROJ_ORDER:
+                op, osc, ot = oracle.nvfp4_quantize(bits[name], threads=threads)
+                g = model[li][name]
+                if not (np.array_equal(g.packed.cpu().numpy(), op) and np.array_equal(g.scales.cpu().numpy(), osc)
+                        and np.float32(g.tensor_scale.item()) == ot):
+                    bad.append(f"layer {li} {name}")
+    emb = 2 * 152064 * 5120  # embedding and lm_head elements, kept BF16
+    q_bytes = sum(w.nbytes for L in model for w in L.values())
+    ratio = (q_bytes + 2 * emb) / (2 * elems + 2 * emb)
+    del model
+    torch.cuda.empty_cache()
+    gbs = elems * 4.5625 / t_q / 1e9
+    return {"workload": f"whole Qwen2.5-32B-shaped model: {layers} layers x 7 tensors, {elems / 1e9:.2f} G elements "
+                        "(62.4 GB BF16), generated, quantized and freed layer by layer",
+            "quantize_ms": t_q * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "wall_s_with_generation": wall, "nvfp4_bytes": q_bytes,
+            "memory_ratio_vs_bf16": ratio, "memory_ratio_note": "NVFP4 layers + BF16 embedding and lm_head over "
+                                                               "the all-BF16 model",
+            "verified_layers": [li for li, _ in checks], "verify_mismatches": bad}
+
+
+def single_layer_leg(dev, copies=128, reps=20):
+    """The smallest instance: W [2048, 2048] (N(0, 0.02^2)), LoRA r = 16,
+    alpha = 32, x [1, 2048].  The quantizer (GB/s at 4.5625 B/element) and
+    the W4A16 + LoRA GEMM at M = 1 (GB/s of its algorithmic bytes), each over
+    `copies` rotating cold copies in one graph."""
+    n = k = 2048
+    r = 16
+    ws_q = torch.empty(q.nvfp4_quantize_workspace_size(n, k), dtype=torch.uint8, device=dev)
+    ws_in = [synth.weight_bf16(n, k, seed=synth.seed_for(1001, "w", c), device=dev) for c in range(copies)]
+    outs = [q.NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                          torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                          torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(copies)]
+
+    def quant():
+        for c in range(copies):
+            q.nvfp4_quantize(ws_in[c], out=outs[c], workspace=ws_q, check_finite=False)
+
+    tq = _graph_ms(quant, 3) * 1e-3 / copies
+    del ws_in
+    a, b = synth.lora_bf16(n, k, r, seed=synth.seed_for(1001, "lora"), device=dev)
+    loras = [(a.clone(), b.clone()) for _ in range(copies)]
+    x = synth.activation_bf16(1, k, synth.seed_for(1001, "x"), device=dev)
+    y = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    ws_g = torch.empty(q.w4a16_lora_gemm_workspace_size(1, n, k, r), dtype=torch.uint8, device=dev)
+
+    def gemm():
+        for c in range(copies):
+            q.w4a16_lora_gemm(x, outs[c], loras[c][0], loras[c][1], 32 / r, out=y, workspace=ws_g)
+
+    tg = _graph_ms(gemm, reps) * 1e-3 / copies
+    p10, p50, p90 = replay_percentiles(lambda: q.w4a16_lora_gemm(x, outs[0], loras[0][0], loras[0][1], 32 / r,
+                                                                 out=y, workspace=ws_g))
+    gb = gemm_bytes(1, n, k, r)
+    del outs, loras
+    return {"workload": "W [2048, 2048] NVFP4, LoRA r = 16 (alpha 32), x [1, 2048]",
+            "quantizer_us": tq * 1e6, "quantizer_GB/s": n * k * 4.5625 / tq / 1e9,
+            "gemm_us": tg * 1e6, "gemm_GB/s": gb / tg / 1e9, "gemm_frac": gb / tg / 1e9 / HBM_PEAK_GBS,
+            "gemm_single_call_us_p10_p50_p90": [p10, p50, p90],
+            "note": "cold: rotating copies; a 2.5 MB call is bound by launch and ramp, not bandwidth"}
+
+
+def aqn_leg(dev):
+    """AQN RMSNorm on its own (qerl_aqn_rmsnorm: noise drawn, scale vector
+    w + sigma z, BF16 output): bytes 2 M H (x) + 4 H (weight) + 2 M H (y)."""
+    out = {}
+    sigma = q.aqn_sigma(RL_STEP, STAGES, SIGMA0, SIGMA1)
+    for m, h in ((1, 3584), (8192, 5120)):
+        x = synth.activation_bf16(m, h, synth.seed_for(1006, "x", m), 0.005, device=dev)
+        w = synth.norm_weight_f32(h, synth.seed_for(1006, "w", h), device=dev)
+        y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
+        t = _graph_ms(lambda: q.aqn_rmsnorm(x, w, EPS, sigma, SEED, RL_STEP, 0, want_f32=False, y_bf16=y), 50)
+        b = norm_bytes(m, h)
+        out[f"M={m},H={h}"] = {"us": t * 1e3, "bytes": b, "GB/s": b / (t * 1e-3) / 1e9,
+                               "frac": b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+def decode_large_m_leg(dev, ms=(128, 256), copies=4, reps=5):
+    """The 32B layer's batched rollout past the ridge (M 128 and 256): the
+    same step as the decode layers (norm + q|k|v, o, norm + gate|up, down),
+    cold copies, one graph.  Both roofline fractions and T_roof / T."""
+    layer = DecodeLayer(dict(LAYER_32B, ms=tuple(ms)), dev, copies=copies)
+    out = {}
+    for mi, m in enumerate(ms):
+        t = _graph_ms(lambda: [layer.step_m(s, m, mi) for s in range(reps)], 3) * 1e-3 / reps
+        b = layer.bytes_m(m)
+        f = sum(gemm_flops(m, n, k, RANK) for n, k in layer.shapes.values())
+        t_roof = max(b / (HBM_PEAK_GBS * 1e9), f / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        out[f"M={m}"] = {"us": t * 1e6, "GB/s": b / t / 1e9, "hbm_frac": b / t / 1e9 / HBM_PEAK_GBS,
+                         "tflops": f / t / 1e12, "mfma_frac": f / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                         "t_roof_us": t_roof * 1e6, "t_roof_over_t": t_roof / t}
+    del layer
+    torch.cuda.empty_cache()
+    return out
 
 
 def backward_leg(dev, reps, m=2048):
@@ -562,7 +753,7 @@ def update_forward_leg(dev, reps, m=2048):
           for name, (n, k) in synth.QWEN25_7B.items()}
     ys = {name: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for name, (n, k) in synth.QWEN25_7B.items()}
     wbf = {name: torch.empty((n, k), dtype=torch.bfloat16, device=dev) for name, (n, k) in synth.QWEN25_7B.items()}
-    ws = torch.zeros(max(q.w4a16_lora_gemm_workspace_size(m, n, k, RANK) for n, k in synth.QWEN25_7B.values()),
+    ws = torch.empty(max(q.w4a16_lora_gemm_workspace_size(m, n, k, RANK) for n, k in synth.QWEN25_7B.values()),
                      dtype=torch.uint8, device=dev)
     lam = ALPHA / RANK
 
@@ -610,7 +801,7 @@ def quantizer_variants_leg(dev, reps):
     dequantized weights on the 7B layer (the format comparison)."""
     shapes = synth.QWEN25_32B
     ws = torch.empty(q.nvfp4_quantize_workspace_size(1, 16), dtype=torch.uint8, device=dev)
-    res = {"workload": "one Qwen2.5-32B-shaped layer (7 tensors, 1.09 G elements); errors on the 7B layer"}
+    res = {"workload": "one Qwen2.5-32B-shaped layer (7 tensors, 0.488 G elements); errors on the 7B layer"}
     ws_in, elems = {}, 0
     for name in synth.PROJ_ORDER:
         n, k = shapes[name]
@@ -660,24 +851,30 @@ def quantizer_variants_leg(dev, reps):
 
 
 # ---- roofline of the dominant decode kernel --------------------------------
-# stream_kernel runs every decode call with M <= 16, one launch per call.  Its
-# average launch duration comes from a graph of those calls run one after
-# another (the timed step runs independent projections side by side, where
-# durations overlap; events around single calls add the dispatch overhead).
-ROOFLINE_MS = (1, 8)
-# (every instantiation: with and without a split of K, with LoRA)
-ROOFLINE_KERNEL = "stream_kernel<"
-KERNEL_SOURCES = ("decode.hip", "mfma_tile.h", "device_common.h", "qerl_internal.h")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_stream_kernel_7b_m1_m8.md")
+# A decode GEMM call is two launches: the streaming kernel (stream_kernel for
+# M <= 16, mfma_unit_kernel for 16 < M <= 64) and finish_kernel, which sums the
+# partial tiles and adds the LoRA term.  The unit of the roofline is one call
+# (its algorithmic bytes over its duration); the class whose calls take the
+# larger share of the step is reported, the other beside it.  Durations come
+# from a graph of the step's calls of that class run back to back (cold
+# copies rotating), timed with one event pair around the replay.
+ROOFLINE_CLASSES = {
+    "stream": dict(max_m=16, kernels=("stream_kernel<", "finish_kernel<"),
+                   file="decode_stream_kernel_m1_m16.md",
+                   sources=("decode.hip", "device_common.h", "qerl_internal.h")),
+    "mfma": dict(max_m=64, kernels=("mfma_unit_kernel<", "finish_kernel<", "aqn_rmsnorm_kernel"),
+                 file="decode_mfma_unit_kernel_m64.md",
+                 sources=("decode.hip", "mfma_tile.h", "device_common.h", "qerl_internal.h", "aqn.hip")),
+}
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(sources):
     """Hash of the kernel's sources with comments and blank lines removed
     (a comment edit does not change the kernel)."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "nvfp4_weight_only_quantize_amd", "csrc", f)) as fh:
             for line in fh:
                 code = re.sub(r"//.*", "", line).rstrip()
@@ -686,74 +883,67 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per stream_kernel launch from the committed counter summary,
-    or None when it is missing or the kernel sources changed since."""
+def recorded_traffic(cls):
+    """HBM bytes per call from the committed counter summary of the class, or
+    None when it is missing or the kernel sources changed since."""
+    c = ROOFLINE_CLASSES[cls]
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(os.path.join(ROOT, "profiles", c["file"])) as fh:
             kv = dict(line.strip()[2:].split(": ", 1) for line in fh if line.startswith("- ") and ": " in line)
     except OSError:
         return None
-    if kv.get("sources_sha256") != kernel_sources_sha256():
+    if kv.get("sources_sha256") != kernel_sources_sha256(c["sources"]):
         return None
-    return float(kv["hbm_bytes_per_launch"])
+    return float(kv["hbm_bytes_per_call"])
 
 
-def roofline_leg(layer: DecodeLayer, reps: int = 5):
-    calls = per_call_durations(layer, reps=reps)
-    per_m = {}
-    for m in DECODE_MS:
-        b = sum(c[2] for c in calls if c[1] == m)
-        t = sum(c[3] for c in calls if c[1] == m)
-        per_m[f"M={m}"] = {"gemm_us": t / reps * 1e6, "GB/s": b / t / 1e9}
-    per_proj = {}
-    for name in synth.PROJ_ORDER:
-        for m in DECODE_MS:
-            sel = [c for c in calls if c[0] == name and c[1] == m]
-            per_proj[f"{name}@{m}"] = round(sum(c[3] for c in sel) / len(sel) * 1e6, 2)
-    # the kernel's own launch duration: the M in ROOFLINE_MS calls of `reps`
-    # steps back to back in one graph (cold weights rotate as in the step),
-    # timed with one event pair around the replay
-    def run():
-        for s in range(reps):
-            for mi, m in enumerate(DECODE_MS):
-                if m in ROOFLINE_MS:
-                    c = (len(DECODE_MS) * (1000 + s) + mi) % len(layer.copies)
-                    for name in synth.PROJ_ORDER:
-                        layer.gemm(name, m, c)
-
-    run()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run()
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    launches = reps * len(ROOFLINE_MS) * len(synth.PROJ_ORDER)
-    b_launch = sum(gemm_bytes(m, *layer.shapes[name], RANK) for m in ROOFLINE_MS
-                   for name in synth.PROJ_ORDER) * reps / launches
-    t_launch = e0.elapsed_time(e1) * 1e-3 / launches
-    del g
-    achieved = b_launch / t_launch / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                "kernel": f"stream_kernel (decode W4A16 + LoRA, M in {list(ROOFLINE_MS)}, "
-                          "7 projections of the 7B layer)",
-                "launches": launches, "avg_launch_us": t_launch * 1e6, "avg_launch_bytes": b_launch}
-    return roofline, per_m, per_proj
+def class_calls(layers, cls):
+    """(layer, m, mi) of the step whose calls fall in the class."""
+    lo = 0 if cls == "stream" else 16
+    hi = ROOFLINE_CLASSES[cls]["max_m"]
+    return [(L, m, mi) for L in layers for mi, m in enumerate(L.ms) if lo < m <= hi]
 
 
-def summarize_profile(trace_dir, fetch_dir, write_dir):
+def roofline_leg(layers, reps=5, classes=ROOFLINE_CLASSES):
+    """Per call class: algorithmic bytes per call over the average call
+    duration.  Returns (the class with the larger share of the step, the
+    others)."""
+    res = {}
+    for cls in classes:
+        sel = class_calls(layers, cls)
+        if not sel:
+            continue
+
+        def run(sel=sel):
+            for s in range(reps):
+                for L, m, mi in sel:
+                    L.step_m(1000 + s, m, mi)
+
+        t = _graph_ms(run, 1) * 1e-3
+        ncalls = 4 * len(sel) * reps  # four calls per layer step: norm+q|k|v, o, norm+gate|up, down
+        b = sum(L.bytes_m(m) for L, m, _ in sel) * reps
+        b_call, t_call = b / ncalls, t / ncalls
+        achieved = b_call / t_call / 1e9
+        res[cls] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(cls),
+                    "kernel": f"decode GEMM call ({' + '.join(k.rstrip('<') for k in ROOFLINE_CLASSES[cls]['kernels'])}"
+                              f"), M in {sorted({m for _, m, _ in sel})}, layers "
+                              f"{sorted({L.cfg['name'] for L, _, _ in sel})}",
+                    "calls": ncalls, "avg_call_us": t_call * 1e6, "avg_call_bytes": b_call,
+                    "class_step_us": t / reps * 1e6}
+    dom = max(res, key=lambda c: res[c]["class_step_us"])
+    other = {c: v for c, v in res.items() if c != dom}
+    return res[dom], other
+
+
+def summarize_profile(cls, trace_dir, fetch_dir, write_dir):
     """Print the markdown summary of three rocprofv3 runs of `--calls-only
-    --copy-probe`: kernel statistics, and FETCH_SIZE / WRITE_SIZE per dispatch
-    of stream_kernel scaled by what they read for the 256 MiB copy."""
+    CLASS --copy-probe`: kernel statistics of the class's kernels, the
+    per-call sum of their durations, and FETCH_SIZE / WRITE_SIZE per call
+    scaled by what the counters read for the 256 MiB copy."""
     import csv
     import glob
+    c = ROOFLINE_CLASSES[cls]
 
     def rows(d, pat):
         out = []
@@ -762,42 +952,46 @@ def summarize_profile(trace_dir, fetch_dir, write_dir):
                 out += list(csv.DictReader(fh))
         return out
 
+    def ours(name):
+        return any(k in name for k in c["kernels"])
+
     stats = rows(trace_dir, "*kernel_stats.csv")
     lines = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---:|---:|---:|---:|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:10]:
         nm = r["Name"].replace("qerl::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
-        lines.append(f"| `{nm[:80]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        lines.append(f"| `{nm[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
-    ours = [r for r in stats if ROOFLINE_KERNEL in r["Name"]]
-    calls = sum(int(r["Calls"]) for r in ours)
-    avg_us = sum(float(r["TotalDurationNs"]) for r in ours) / calls / 1e3 if calls else float("nan")
+    mine = [r for r in stats if ours(r["Name"])]
+    calls = sum(int(r["Calls"]) for r in mine if "finish_kernel" in r["Name"])
+    tot_ns = sum(float(r["TotalDurationNs"]) for r in mine)
+    per_call_us = tot_ns / calls / 1e3 if calls else float("nan")
 
-    def per_dispatch(d, counter):
-        vals, copy = [], []
+    def per_call(d, counter):
+        vals, copy = 0.0, []
         for r in rows(d, "*counter_collection.csv"):
             if r["Counter_Name"] != counter:
                 continue
-            if ROOFLINE_KERNEL in r["Kernel_Name"]:
-                vals.append(float(r["Counter_Value"]))
+            if ours(r["Kernel_Name"]):
+                vals += float(r["Counter_Value"])
             elif "copyBuffer" in r["Kernel_Name"]:
                 copy.append(float(r["Counter_Value"]))
-        return sum(vals) / max(len(vals), 1), len(vals), max(copy) if copy else float("nan")
+        return vals / max(calls, 1), max(copy) if copy else float("nan")
 
-    f_kib, f_n, f_copy = per_dispatch(fetch_dir, "FETCH_SIZE")
-    w_kib, w_n, w_copy = per_dispatch(write_dir, "WRITE_SIZE")
+    f_kib, f_copy = per_call(fetch_dir, "FETCH_SIZE")
+    w_kib, w_copy = per_call(write_dir, "WRITE_SIZE")
     copy_kib = 256 * 1024  # the probe copies 256 MiB: that many read and written
     f_scale, w_scale = copy_kib / f_copy, copy_kib / w_copy
     hbm = (f_kib * f_scale + w_kib * w_scale) * 1024
     print("\n".join(lines))
     print()
-    print(f"- kernel: stream_kernel (all instantiations, {calls} dispatches)")
-    print(f"- average_launch_us: {avg_us:.3f}")
-    print(f"- fetch_kib_per_dispatch: {f_kib:.1f} ({f_n} dispatches)")
-    print(f"- write_kib_per_dispatch: {w_kib:.1f} ({w_n} dispatches)")
+    print(f"- class: {cls} ({', '.join(k.rstrip('<') for k in c['kernels'])}; {calls} calls)")
+    print(f"- kernel_us_per_call: {per_call_us:.3f} (sum of the class's kernel durations / calls)")
+    print(f"- fetch_kib_per_call: {f_kib:.1f}")
+    print(f"- write_kib_per_call: {w_kib:.1f}")
     print(f"- copy_probe_fetch_kib: {f_copy:.1f} (256 MiB copy; scale {f_scale:.4f})")
     print(f"- copy_probe_write_kib: {w_copy:.1f} (256 MiB copy; scale {w_scale:.4f})")
-    print(f"- hbm_bytes_per_launch: {hbm:.0f}")
-    print(f"- sources_sha256: {kernel_sources_sha256()}")
+    print(f"- hbm_bytes_per_call: {hbm:.0f}")
+    print(f"- sources_sha256: {kernel_sources_sha256(c['sources'])}")
 
 
 def summarize_prefill_profile(trace_dir, fetch_dir, write_dir, mfma_dir):
@@ -851,25 +1045,43 @@ def summarize_prefill_profile(trace_dir, fetch_dir, write_dir, mfma_dir):
     print(f"- algorithmic_bytes: {n * k * 0.5625 + 2 * m * k + 2 * m * n + 2 * 2 * RANK * (n + k):.0f}")
 
 
+def decode_breakdown(layers, reps=4):
+    """Per layer and M: the step's four calls (norm + q|k|v, o, norm +
+    gate|up, down) over `reps` rotating cold copies, replayed as one graph
+    120 times; p10 / p50 / p90 of the per-pass time and GB/s at the median."""
+    out = {}
+    for L in layers:
+        for mi, m in enumerate(L.ms):
+            p10, p50, p90 = replay_percentiles(lambda L=L, m=m, mi=mi: [L.step_m(s, m, mi) for s in range(reps)])
+            b = L.bytes_m(m)
+            out[f"{L.cfg['name']} M={m}"] = {"us_p10_p50_p90": [round(p10 / reps, 2), round(p50 / reps, 2),
+                                                                round(p90 / reps, 2)],
+                                             "bytes": b, "GB/s_p50": round(b / (p50 / reps * 1e-6) / 1e9, 1),
+                                             "frac_p50": round(b / (p50 / reps * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=8, help="cold-weight copies of the layer")
     ap.add_argument("--launch", choices=("fused", "streams", "serial"), default="fused",
-                    help="q/k/v and gate/up: one multi-segment call each (fused), side by side on side "
-                         "streams (streams), or one call after another on one stream (serial)")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+                    help="q/k/v and gate/up: one multi-segment call each with its norm (fused), side by side "
+                         "on side streams after a standalone norm (streams), or one call after another on one "
+                         "stream (serial)")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--calls-only", action="store_true",
-                    help="only the per-call roofline leg (for rocprofv3 runs); prints its JSON")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the comparison, rank-sweep, single-layer, norm and large-M legs")
+    ap.add_argument("--calls-only", choices=tuple(ROOFLINE_CLASSES),
+                    help="only the roofline leg of this call class (for rocprofv3 runs); prints its JSON")
     ap.add_argument("--copy-probe", action="store_true",
                     help="with --calls-only: also copy 256 MiB device to device (counter scale)")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize", nargs=4, metavar=("CLASS", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="print the profile summary of rocprofv3 output directories and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill leg (for rocprofv3 runs); prints its JSON")
@@ -883,7 +1095,7 @@ def main():
         summarize_prefill_profile(*args.summarize_prefill)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (pass --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path here (pass --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -894,70 +1106,85 @@ def main():
         print(json.dumps({"prefill": prefill_leg(dev, reps=3)}), flush=True)
         return
 
-    log("setting up decode layer ...")
-    layer = DecodeLayer(dev, args.copies, launch=args.launch)
+    log("setting up the decode layers ...")
+    layers = [DecodeLayer(LAYER_7B, dev, launch=args.launch), DecodeLayer(LAYER_32B, dev, launch=args.launch)]
     torch.cuda.synchronize()
     if args.calls_only:
-        roofline, per_m, per_proj = roofline_leg(layer)
+        sel = {args.calls_only: ROOFLINE_CLASSES[args.calls_only]}
+        roofline, other = roofline_leg(layers, classes=sel)
         if args.copy_probe:
             src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
             dst = torch.empty_like(src)
             for _ in range(3):
                 dst.copy_(src)
             torch.cuda.synchronize()
-        print(json.dumps({"roofline": roofline, "decode_per_m": per_m, "decode_call_us": per_proj}), flush=True)
+        print(json.dumps({"roofline": roofline}), flush=True)
         return
 
     def steps_fn(first, count):
         for s in range(first, first + count):
-            layer.step(s)
+            for L in layers:
+                L.step(s)
 
     ms_per_step, _graphs = time_graph(steps_fn, args.steps, args.warmup)
-    step_bytes = layer.step_bytes()
+    del _graphs
+    step_bytes = sum(L.step_bytes() for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s")
-
-    roofline, per_m, per_proj = roofline_leg(layer)
-
-    parity = check_decode_parity(layer)
-    log("BF16 + LoRA comparison and LoRA rank sweep ...")
-    compare = bf16_lora_leg(layer)
-    ranks = lora_rank_leg(layer)
+    p10, p50, p90 = replay_percentiles(lambda: steps_fn(0, 4))
+    roofline, roofline_other = roofline_leg(layers)
+    breakdown = decode_breakdown(layers)
+    log("parity against the oracle ...")
+    parity = check_decode_parity(layers)
     result = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Qwen2.5-7B-shaped decoder layer, decode: AQN RMSNorm x2 + "
-                               "q/k/v/o/gate/up/down NVFP4 W4A16 + LoRA r32 (alpha 64), M in {1,8,64}",
-                   "hidden": 3584, "intermediate": 18944, "decode_m": list(DECODE_MS),
-                   "lora_rank": RANK, "cold_weight_copies": args.copies, "hip_graph": True,
-                   "launch": args.launch,
-                   "step_bytes": step_bytes},
+        "config": {"workload": "decode of a Qwen2.5-7B-shaped layer at M in {1, 8, 64} and a Qwen2.5-32B-shaped "
+                               "layer at M in {16, 64}: AQN RMSNorm + q|k|v, o, AQN RMSNorm + gate|up, down, "
+                               "NVFP4 W4A16 + LoRA r32 (alpha 64) on all seven projections",
+                   "layers": [{"name": L.cfg["name"], "hidden": L.cfg["hidden"], "intermediate": L.cfg["inter"],
+                               "decode_m": list(L.ms), "cold_weight_copies": len(L.copies)} for L in layers],
+                   "lora_rank": RANK, "hip_graph": True, "launch": args.launch, "step_bytes": step_bytes},
         "frac_of_hbm_peak": value / HBM_PEAK_GBS,
+        "step_us_p10_p50_p90": [round(p10 / 4, 2), round(p50 / 4, 2), round(p90 / 4, 2)],
         "roofline": roofline,
-        "decode_per_m": per_m,
-        "decode_call_us": per_proj,
-        "parity_rel_l2_m1": parity,
-        "bf16_lora_compare": compare,
-        "lora_rank_sweep": ranks,
+        "roofline_secondary": roofline_other,
+        "decode_breakdown": breakdown,
+        "parity_rel_l2_smallest_m": parity,
     }
-    del _graphs
+    if not args.no_extras:
+        log("BF16 + LoRA comparison and LoRA rank sweep ...")
+        result["bf16_lora_compare_7b"] = bf16_lora_leg(layers[0])
+        result["lora_rank_sweep_7b"] = lora_rank_leg(layers[0])
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        cpu = cpu_baseline(layers, args.cpu_budget)
+    del layers
+    torch.cuda.empty_cache()
+    if not args.no_extras:
+        log("32B layer at M 128 and 256 ...")
+        result["decode_32b_large_m"] = decode_large_m_leg(dev)
+        log("single 2048 x 2048 layer ...")
+        result["single_layer_2048"] = single_layer_leg(dev)
+        log("AQN RMSNorm alone ...")
+        result["aqn_rmsnorm"] = aqn_leg(dev)
     if not args.no_prefill:
         log("prefill leg ...")
         result["prefill"] = prefill_leg(dev, reps=3)
     if not args.no_quantizer:
-        log("quantizer leg ...")
-        result["quantizer"] = quantizer_leg(dev, reps=3)
-        log("quantizer variants leg ...")
-        result["quantizer_variants"] = quantizer_variants_leg(dev, reps=3)
+        log("quantizer legs ...")
+        result["quantizer"] = {"layer_32b": quantizer_leg(dev, reps=3),
+                               "model_32b": model_quantizer_leg(dev),
+                               "variants": quantizer_variants_leg(dev, reps=3)}
     if not args.no_backward:
         log("update-phase forward: fused W4A16 + LoRA against dequantize + BF16 GEMM ...")
         result["update_forward"] = update_forward_leg(dev, reps=3)
         log("backward leg ...")
         result["backward"] = backward_leg(dev, reps=3)
-    if not args.no_cpu_baseline:
-        log("cpu baseline ...")
-        result["cpu_baseline"] = cpu_baseline(layer, args.cpu_budget)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
