@@ -67,6 +67,8 @@ typedef enum qerl_status {
 #define QERL_MAX_LORA_RANK 128
 #define QERL_MAX_SEGMENTS 4    /* projections of one qerl_w4a16_lora_gemm_multi call */
 #define QERL_MAX_NORM_WIDTH 16384
+/* bytes of the per-device static scratch behind qerl_w4a16_lora_gemm_noalloc */
+#define QERL_NOALLOC_SCRATCH_BYTES ((size_t)48 << 20)
 
 /* ----------------------------------------------------------------------- */
 /* BF16 -> NVFP4 quantizer                                                   */
@@ -191,6 +193,32 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
                                  const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
                                  float lora_scale, void *y_bf16, int64_t ldy,
                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the layer of
+ * qerl_w4a16_lora_gemm (same arguments, same kernels, same results) with no
+ * workspace argument.  Its partial sums go to a static device array of
+ * QERL_NOALLOC_SCRATCH_BYTES (48 MiB) that the library's code object holds
+ * on each device it runs on, for the life of the process; its device address
+ * is looked up once per device on the first call there.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   Returns QERL_ERR_WORKSPACE, before enqueueing anything, when
+ *   qerl_w4a16_lora_gemm_workspace_size(m, n, k, r) exceeds the scratch (48
+ *   MiB covers the decode path, m <= 64, at r <= 128 for weights of up to
+ *   27648 x 5120 and 5120 x 27648, the largest projections of a 32B-class
+ *   decoder layer).
+ *   Every call on one device shares that device's scratch, which keeps the
+ *   last call's partial sums (nothing in it needs to start at zero): calls
+ *   that may overlap in time on one device -- on different streams, or from
+ *   different threads without ordering -- race and give wrong results.
+ *   Stream-ordered calls on one stream are safe.
+ */
+qerl_status qerl_w4a16_lora_gemm_noalloc(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                         const uint8_t *packed, const uint8_t *scales,
+                                         const float *tensor_scale, int64_t n,
+                                         const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                         float lora_scale, void *y_bf16, int64_t ldy, void *stream);
 
 /*
  * One projection of qerl_w4a16_lora_gemm_multi: every field as the argument

@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
     L.qerl_w4a16_lora_gemm.argtypes = [P, i64, i64, i64, P, P, P, i64, P, P, i32, f32, P, i64,
                                        P, sz, P]
     L.qerl_w4a16_lora_gemm.restype = ctypes.c_int
+    L.qerl_w4a16_lora_gemm_noalloc.argtypes = [P, i64, i64, i64, P, P, P, i64, P, P, i32, f32, P, i64, P]
+    L.qerl_w4a16_lora_gemm_noalloc.restype = ctypes.c_int
     L.qerl_w4a16_lora_gemm_multi_workspace_size.argtypes = [i64, i64, ctypes.POINTER(GemmSegment), i32]
     L.qerl_w4a16_lora_gemm_multi_workspace_size.restype = sz
     L.qerl_w4a16_lora_gemm_multi.argtypes = [P, i64, i64, i64, ctypes.POINTER(GemmSegment), i32, P, sz, P]
@@ -234,15 +236,8 @@ def w4a16_lora_gemm_workspace_size(m: int, n: int, k: int, r: int) -> int:
     return int(lib().qerl_w4a16_lora_gemm_workspace_size(m, n, k, r))
 
 
-def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | None = None,
-                    lora_b: torch.Tensor | None = None, lora_scale: float = 0.0,
-                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
-    """y [M, N] (BF16) = x [M, K] deq(W)^T + lora_scale (x A^T) B^T.
-
-    A caller-provided ``workspace`` (uint8, at least the size query) holds
-    partial sums only: any contents, reusable by any sequence of calls on one
-    stream."""
+def _gemm_operands(x, wq, lora_a, lora_b, out):
+    """Checks of the single-projection GEMM's tensors; returns (m, n, k, r, out)."""
     _need(x, "x", torch.bfloat16, 2)
     dev = x.device
     m, k = x.shape
@@ -264,6 +259,20 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
     _need(out, "out", torch.bfloat16, 2, dev)
     if tuple(out.shape) != (m, n):
         raise ValueError("out must be [M, N]")
+    return m, n, k, r, out
+
+
+def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | None = None,
+                    lora_b: torch.Tensor | None = None, lora_scale: float = 0.0,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """y [M, N] (BF16) = x [M, K] deq(W)^T + lora_scale (x A^T) B^T.
+
+    A caller-provided ``workspace`` (uint8, at least the size query) holds
+    partial sums only: any contents, reusable by any sequence of calls on one
+    stream."""
+    m, n, k, r, out = _gemm_operands(x, wq, lora_a, lora_b, out)
+    dev = x.device
     need = w4a16_lora_gemm_workspace_size(m, n, k, r)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -272,6 +281,27 @@ def w4a16_lora_gemm(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | Non
         _ptr(x), m, k, _rows(x, "x"), _ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n,
         _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out), _rows(out, "out"),
         _ptr(workspace), ws_bytes, _stream(stream, dev)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 48 << 20  # QERL_NOALLOC_SCRATCH_BYTES
+
+
+def w4a16_lora_gemm_noalloc(x: torch.Tensor, wq: NVFP4Weight, lora_a: torch.Tensor | None,
+                            lora_b: torch.Tensor | None, lora_scale: float, out: torch.Tensor,
+                            stream=None) -> torch.Tensor:
+    """The layer of w4a16_lora_gemm through qerl_w4a16_lora_gemm_noalloc: no
+    workspace, the partial sums go to the library's static per-device scratch
+    (sizes whose workspace query exceeds NOALLOC_SCRATCH_BYTES are rejected).
+    ``out`` is required so that nothing is allocated here either.  Calls that
+    overlap in time on one device race on the shared scratch."""
+    if out is None:
+        raise ValueError("out is required")
+    m, n, k, r, out = _gemm_operands(x, wq, lora_a, lora_b, out)
+    _check(lib().qerl_w4a16_lora_gemm_noalloc(
+        _ptr(x), m, k, _rows(x, "x"), _ptr(wq.packed), _ptr(wq.scales), _ptr(wq.tensor_scale), n,
+        _ptr(lora_a), _ptr(lora_b), r, float(lora_scale), _ptr(out), _rows(out, "out"),
+        _stream(stream, x.device)))
     return out
 
 

@@ -27,7 +27,7 @@ COMMON = [
 ]
 # exact rounding decisions in the quantizer rely on explicit fmaf only
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "decode.hip", "aqn.hip", "backward.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "decode.hip", "aqn.hip", "backward.hip", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

@@ -215,6 +215,29 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
                       "w4a16_lora_gemm launch");
 }
 
+qerl_status qerl_w4a16_lora_gemm_noalloc(const void *x_bf16, int64_t m, int64_t k, int64_t ldx,
+                                         const uint8_t *packed, const uint8_t *scales,
+                                         const float *tensor_scale, int64_t n,
+                                         const void *lora_a_bf16, const void *lora_b_bf16, int32_t r,
+                                         float lora_scale, void *y_bf16, int64_t ldy, void *stream) {
+    g_last_error[0] = '\0';
+    qerl::GemmArgs a;
+    const qerl_status st = check_gemm("w4a16_lora_gemm_noalloc", x_bf16, m, k, ldx, packed, scales, tensor_scale,
+                                      n, lora_a_bf16, lora_b_bf16, r, lora_scale, y_bf16, ldy, &a);
+    if (st != QERL_OK) return st;
+    const size_t need = qerl::gemm_workspace_bytes(m, n, k, r);
+    if (need > QERL_NOALLOC_SCRATCH_BYTES)
+        return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm_noalloc: m=%lld n=%lld k=%lld r=%d needs %zu bytes of "
+                    "scratch, above the static scratch of %zu bytes (use qerl_w4a16_lora_gemm with a workspace)",
+                    (long long)m, (long long)n, (long long)k, r, need, (size_t)QERL_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    const qerl_status sst = hip_status(qerl::noalloc_scratch(&ws), "w4a16_lora_gemm_noalloc: scratch address");
+    if (sst != QERL_OK) return sst;
+    a.workspace = ws;
+    return hip_status(qerl::launch_w4a16_lora_gemm(a, static_cast<hipStream_t>(stream)),
+                      "w4a16_lora_gemm_noalloc launch");
+}
+
 size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qerl_gemm_segment *segs,
                                                  int32_t nseg) {
     if (!segs || nseg < 1 || nseg > QERL_MAX_SEGMENTS) return 0;

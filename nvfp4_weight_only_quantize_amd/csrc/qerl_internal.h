@@ -48,6 +48,9 @@ struct GemmArgs {
 size_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 #define QERL_MAX_SEGMENTS 4
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
+// device address of the current device's copy of the static scratch array
+// (QERL_NOALLOC_SCRATCH_BYTES), looked up on the first call on each device
+hipError_t noalloc_scratch(void **ptr);
 // decode batches (m <= kDecodeMaxM): HBM-streaming path in decode.hip
 constexpr int64_t kDecodeMaxM = 64;
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);

@@ -275,3 +275,19 @@ def test_last_hip_error_is_the_error_text():
     assert L.qerl_w4a16_lora_gemm(None, 1, 16, 16, None, None, None, 1, None, None, 0, 0.0, None, 1, None, 0,
                                   None) == 1
     assert L.qerl_last_error() and L.qerl_last_hip_error() == L.qerl_last_error()
+
+
+def test_noalloc_gemm_rejects_sizes_above_the_scratch():
+    """Host-side checks of qerl_w4a16_lora_gemm_noalloc: nothing is enqueued
+    (the pointers are never dereferenced)."""
+    L = q.lib()
+    m, n, k, r = 128, 27648, 5120, 32
+    assert L.qerl_w4a16_lora_gemm_workspace_size(m, n, k, r) > q.NOALLOC_SCRATCH_BYTES
+    st = L.qerl_w4a16_lora_gemm_noalloc(P(FAKE), m, k, k, P(FAKE), P(FAKE), P(FAKE), n, P(FAKE), P(FAKE), r, 2.0,
+                                        P(FAKE), n, None)
+    assert st == 5  # QERL_ERR_WORKSPACE
+    assert b"scratch" in L.qerl_last_hip_error()
+    # argument checks come first, as in the workspace call
+    st = L.qerl_w4a16_lora_gemm_noalloc(None, 1, 16, 16, P(FAKE), P(FAKE), P(FAKE), 1, None, None, 0, 0.0,
+                                        P(FAKE), 1, None)
+    assert st == 1  # QERL_ERR_NULL
