@@ -526,18 +526,33 @@ def quantizer_leg(dev, reps):
         for name in synth.PROJ_ORDER:
             q.nvfp4_quantize(ws_in[name], out=outs[name], workspace=ws, check_finite=False)
 
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) * 1e-3 / reps
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    t = timed(run)
     gbs = elems * 4.5625 / t / 1e9
+    # one pass: the tensor scale supplied (each tensor's own, from the run
+    # above), so only the encode pass runs: 2.5625 B per element
+    scales_in = {name: outs[name].tensor_scale.clone() for name in synth.PROJ_ORDER}
+
+    def run_one_pass():
+        for name in synth.PROJ_ORDER:
+            q.nvfp4_quantize(ws_in[name], tensor_scale_in=scales_in[name], out=outs[name], check_finite=False)
+
+    t1 = timed(run_one_pass)
+    gbs1 = elems * 2.5625 / t1 / 1e9
     return {"workload": f"BF16->NVFP4 of one Qwen2.5-32B-shaped layer (7 tensors, {elems / 1e9:.3f} G elements)",
-            "ms": t * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}
+            "ms": t * 1e3, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS,
+            "one_pass_tensor_scale_in": {"ms": t1 * 1e3, "GB/s": gbs1, "frac": gbs1 / HBM_PEAK_GBS,
+                                         "bytes_per_element": 2.5625}}
 
 
 def model_quantizer_leg(dev, layers=64, verify_layers=(0, 37), verify=True):
@@ -1080,11 +1095,14 @@ def main():
     ap.add_argument("--calls-only", choices=tuple(ROOFLINE_CLASSES),
                     help="only the roofline leg of this call class (for rocprofv3 runs); prints its JSON")
     ap.add_argument("--copy-probe", action="store_true",
-                    help="with --calls-only: also copy 256 MiB device to device (counter scale)")
+                    help="with --calls-only or --quantizer-only: also copy 256 MiB device to device "
+                         "(counter scale)")
     ap.add_argument("--summarize", nargs=4, metavar=("CLASS", "TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="print the profile summary of rocprofv3 output directories and exit")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only the prefill leg (for rocprofv3 runs); prints its JSON")
+    ap.add_argument("--quantizer-only", action="store_true",
+                    help="only the one-layer quantizer leg (for rocprofv3 runs); prints its JSON")
     ap.add_argument("--summarize-prefill", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
                     help="print the prefill profile summary of rocprofv3 output directories and exit")
     args = ap.parse_args()
@@ -1104,6 +1122,16 @@ def main():
     q.lib()
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_leg(dev, reps=3)}), flush=True)
+        return
+    if args.quantizer_only:
+        q_res = quantizer_leg(dev, reps=3)
+        if args.copy_probe:
+            src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+        print(json.dumps({"quantizer": q_res}), flush=True)
         return
 
     log("setting up the decode layers ...")

@@ -23,6 +23,20 @@
 // exact difference once, so its sign is exact whenever the difference cannot
 // fall below the float subnormal range -- guaranteed for s_t >= 2^-90 (all
 // operands are then multiples of 2^-133).  Smaller s_t takes a double path.
+//
+// Fast element path (deterministic rounding, s_t in [2^-80, 2^80] with more
+// than 8 significant bits): the hardware FP32 -> E2M1 conversion rounds to
+// nearest-even on the E2M1 grid and saturates at 6 (checked exhaustively over
+// every float in [2^-9, 16) and its negative), so it decides each element
+// from a quotient q ~ w / (e s_t) that is on the same side of every midpoint
+// c as the exact one.  Why that holds: with s_t of more than 8 significant
+// bits, c e s_t has more significant bits than any BF16 |w|, so |w| is never
+// a midpoint exactly, and when |w| != c e s_t the two differ by at least
+// 2^-33 relative (|w| has 8 significant bits, c e s_t at most 33).  q is
+// formed in float-float, q_hi + q_lo with a relative error below 2^-45, from
+// 1 / (e s_t) taken in double; s = fl(q_hi + q_lo) is then on the exact
+// side of every midpoint or equal to one, and an element whose s is equal to
+// one (low 21 mantissa bits zero) is decided again by the comparisons above.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -36,6 +50,26 @@ __device__ __forceinline__ uint32_t absmax_pair(uint32_t w) {
 }
 __device__ __forceinline__ uint32_t absmax_vec(uint4 v) {
     return max(max(absmax_pair(v.x), absmax_pair(v.y)), max(absmax_pair(v.z), absmax_pair(v.w)));
+}
+
+// max of (bits & 0x7FFF) over the 16 BF16 values of two vectors, two at a
+// time in 16-bit halves
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t abs_pair16(uint32_t w) {
+    u16x2_t h;
+    const uint32_t a = w & 0x7FFF7FFFu;
+    __builtin_memcpy(&h, &a, 4);
+    return h;
+}
+__device__ __forceinline__ uint32_t absmax16(uint4 v0, uint4 v1) {
+    u16x2_t m = __builtin_elementwise_max(abs_pair16(v0.x), abs_pair16(v0.y));
+    m = __builtin_elementwise_max(m, abs_pair16(v0.z));
+    m = __builtin_elementwise_max(m, abs_pair16(v0.w));
+    m = __builtin_elementwise_max(m, abs_pair16(v1.x));
+    m = __builtin_elementwise_max(m, abs_pair16(v1.y));
+    m = __builtin_elementwise_max(m, abs_pair16(v1.z));
+    m = __builtin_elementwise_max(m, abs_pair16(v1.w));
+    return max((uint32_t)m.x, (uint32_t)m.y);
 }
 
 __global__ __launch_bounds__(kThreads) void amax_kernel(const uint16_t *__restrict__ w, int64_t n,
@@ -73,6 +107,18 @@ __device__ __forceinline__ float e4m3_value(int c) {
                   : __uint_as_float(((uint32_t)(e + 120) << 23) | ((uint32_t)m << 20));
 }
 
+// 1 / E4M3(c) rounded to double, c = 1 .. 126 (0 for c = 0): a power of two
+// times the rounded inverse of the 3-bit mantissa's significand (normal
+// codes), or 512 / c (subnormal codes); the quotients are compile-time
+// constants.
+__device__ __forceinline__ double e4m3_inverse(int c) {
+    constexpr double kNorm[8] = {8.0 / 8, 8.0 / 9, 8.0 / 10, 8.0 / 11, 8.0 / 12, 8.0 / 13, 8.0 / 14, 8.0 / 15};
+    constexpr double kSub[8] = {0.0, 512.0 / 1, 512.0 / 2, 512.0 / 3, 512.0 / 4, 512.0 / 5, 512.0 / 6, 512.0 / 7};
+    if (c <= 0 || c > 126) return 0.0;
+    const int e = c >> 3, m = c & 7;
+    return e == 0 ? kSub[m] : __builtin_ldexp(kNorm[m], 7 - e);  // E4M3(c) = 2^(e-7) (8 + m) / 8
+}
+
 // Approximate least E4M3 code with value >= t (t >= 0); corrected exactly below.
 __device__ __forceinline__ int e4m3_ceil_code_guess(float t) {
     if (!(t > 0.0f)) return 0;
@@ -85,21 +131,22 @@ __device__ __forceinline__ int e4m3_ceil_code_guess(float t) {
 }
 
 // Least E4M3 code v with E4M3(v) * 6 * s_t >= amax_b (saturating at 448).
-__device__ __forceinline__ int scale_code_round_up(float amax_b, float st) {
+// inv6st ~ 1 / (6 s_t) seeds the search (any approximation is corrected).
+__device__ __forceinline__ int scale_code_round_up(float amax_b, float st, float inv6st) {
     const double s6 = 6.0 * (double)st;  // exact
     const double a = (double)amax_b;
     if (448.0 * s6 < a) return 126;
-    int c = e4m3_ceil_code_guess(amax_b / (6.0f * st));
+    int c = e4m3_ceil_code_guess(amax_b * inv6st);
     while (c > 0 && (double)e4m3_value(c - 1) * s6 >= a) --c;
     while (c < 126 && (double)e4m3_value(c) * s6 < a) ++c;
     return c;
 }
 
 // Nearest E4M3 value to amax_b / (6 s_t), ties to the even code, saturating.
-__device__ __forceinline__ int scale_code_rne(float amax_b, float st) {
+__device__ __forceinline__ int scale_code_rne(float amax_b, float st, float inv6st) {
     const double s6 = 6.0 * (double)st;
     const double a = (double)amax_b;
-    const int hi = scale_code_round_up(amax_b, st);
+    const int hi = scale_code_round_up(amax_b, st, inv6st);
     const double vhi = (double)e4m3_value(hi);
     if (vhi * s6 < a) return 126;
     if (hi == 0 || vhi * s6 == a) return hi;
@@ -107,6 +154,32 @@ __device__ __forceinline__ int scale_code_rne(float amax_b, float st) {
     const double two_a = 2.0 * a, mid = (vlo + vhi) * s6;  // both exact
     if (two_a < mid) return hi - 1;
     if (two_a > mid) return hi;
+    return ((hi - 1) & 1) ? hi : hi - 1;
+}
+
+// The same two decisions in float for s_t >= 2^-90, each comparison the sign
+// of one fma: 6 E4M3(c) and 6 (E4M3(c-1) + E4M3(c)) are exact in float, and
+// fmaf(x, s_t, -amax_b) rounds the exact difference once, so its sign is
+// exact (as for the elements below).  The guess from amax_b * inv6st is
+// within one code of the answer (its relative error, ~2^-22, is far below
+// the 1/15 spacing of E4M3 values), so one step corrects it.
+__device__ __forceinline__ int scale_code_round_up_f32(float amax_b, float st, float inv6st) {
+    int c = e4m3_ceil_code_guess(amax_b * inv6st);
+    if (c > 0 && __builtin_fmaf(6.0f * e4m3_value(c - 1), st, -amax_b) >= 0.0f) --c;
+    else if (c < 126 && __builtin_fmaf(6.0f * e4m3_value(c), st, -amax_b) < 0.0f) ++c;
+    return c;
+}
+
+__device__ __forceinline__ int scale_code_rne_f32(float amax_b, float st, float inv6st) {
+    const int hi = scale_code_round_up_f32(amax_b, st, inv6st);
+    const float vhi = e4m3_value(hi);
+    const float dhi = __builtin_fmaf(6.0f * vhi, st, -amax_b);
+    if (dhi < 0.0f) return 126;  // above 448: saturate
+    if (hi == 0 || dhi == 0.0f) return hi;
+    // 2 amax_b against (vlo + vhi) 6 s_t: the sum of neighbours is exact
+    const float d = __builtin_fmaf(6.0f * (e4m3_value(hi - 1) + vhi), st, -2.0f * amax_b);
+    if (d > 0.0f) return hi - 1;
+    if (d < 0.0f) return hi;
     return ((hi - 1) & 1) ? hi : hi - 1;
 }
 
@@ -177,32 +250,100 @@ struct EncodeParams {
 // SR: stochastic element rounding; the uniform of element e (row-major index
 // row * k + col) is the top 24 bits of word e % 4 of Philox4x64-10 with key
 // (seed, 0) and counter (e / 4, 0, 1, 0).
+// s_t admits the fast element path: in range for the float-float quotient,
+// and more than 8 significant bits (no BF16 value is an exact midpoint)
+__device__ __forceinline__ bool fast_path_scale(float st) {
+    if (!(st >= 0x1p-80f && st <= 0x1p80f)) return false;
+    const uint32_t sig = (__float_as_uint(st) & 0x7FFFFFu) | 0x800000u;  // normal: 24-bit significand
+    return __builtin_ctz(sig) < 16;  // odd part of at least 9 bits
+}
+
+// q ~ f / (e s_t) as fl(q_hi + q_lo): r_hi + r_lo ~ 1 / (e s_t)
+__device__ __forceinline__ float fast_quotient(float f, float rh, float rl) {
+    const float qh = f * rh;
+    const float t = __builtin_fmaf(f, rh, -qh);  // the product's rounding error, exact
+    const float ql = __builtin_fmaf(f, rl, t);
+    return qh + ql;
+}
+
+// s is E2M1-grid aligned (a midpoint or grid value: low 21 mantissa bits
+// zero) and non-zero: the hardware's tie rule might not be the exact
+// decision, so the element is decided again by comparisons
+__device__ __forceinline__ uint32_t fast_suspect(float s) {
+    // lowest set bit of the bits of s at 21 .. 30 <=> low 21 bits zero and s
+    // neither +0 (no bit) nor -0 (bit 31); a zero element gives a zero s
+    return (uint32_t)__builtin_ffs((int)__float_as_uint(s)) - 22u <= 9u;
+}
+
+// byte SEL of `old` <- the codes of the two BF16 elements of `word` (low
+// half -> low nibble); bits J and J + 1 of `suspect` flag their quotients
+template <int SEL, int J>
+__device__ __forceinline__ uint32_t fast_pair(uint32_t old, uint32_t word, float rh, float rl, uint32_t &suspect) {
+    const float f0 = __uint_as_float(word << 16), f1 = __uint_as_float(word & 0xFFFF0000u);
+    const float s0 = fast_quotient(f0, rh, rl), s1 = fast_quotient(f1, rh, rl);
+    suspect |= fast_suspect(s0) << J | fast_suspect(s1) << (J + 1);
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, s0, s1, 1.0f, SEL);
+}
+
+// the 32-bit code word of elements J .. J + 7 (4 BF16 words)
+template <int J>
+__device__ __forceinline__ uint32_t fast_codes4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, float rh,
+                                                float rl, uint32_t &suspect) {
+    uint32_t c = fast_pair<0, J>(0u, w0, rh, rl, suspect);
+    c = fast_pair<1, J + 2>(c, w1, rh, rl, suspect);
+    c = fast_pair<2, J + 4>(c, w2, rh, rl, suspect);
+    return fast_pair<3, J + 6>(c, w3, rh, rl, suspect);
+}
+
 template <bool SR>
 __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
     __shared__ float s_st;
-    if (threadIdx.x < kWave) {
+    __shared__ double s_inv_st;
+    __shared__ double s_inv_e[128];  // 1 / E4M3(c), c = 1 .. 126
+    if (!SR && threadIdx.x < 128) s_inv_e[threadIdx.x] = e4m3_inverse((int)threadIdx.x);
+    // the partial maxima: every thread loads its share at once (at most
+    // kAmaxMaxBlocks / kThreads), the waves' maxima meet in LDS
+    __shared__ uint32_t s_red[kThreads / kWave];
+    if (!p.tensor_scale_in) {
+        constexpr int kPer = kAmaxMaxBlocks / kThreads;
+        uint32_t v[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = threadIdx.x + u * kThreads;
+            v[u] = i < p.num_partials ? p.partial[i] : 0u;
+        }
+        uint32_t m = v[0];
+#pragma unroll
+        for (int u = 1; u < kPer; ++u) m = max(m, v[u]);
+        m = wave_max(m);
+        if ((threadIdx.x & (kWave - 1)) == 0) s_red[threadIdx.x / kWave] = m;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
         float st;
         if (p.tensor_scale_in) {
             st = *p.tensor_scale_in;
             if (!(st > 0.0f && st < INFINITY)) st = __builtin_nanf("");
         } else {
-            uint32_t m = 0;
-            for (int i = threadIdx.x; i < p.num_partials; i += kWave) m = max(m, p.partial[i]);
-            m = wave_max(m);
+            uint32_t m = s_red[0];
+#pragma unroll
+            for (int w = 1; w < kThreads / kWave; ++w) m = max(m, s_red[w]);
             if (m >= 0x7F80u) st = __builtin_nanf("");
             else if (m == 0) st = 1.0f;
             else st = (float)((double)__uint_as_float(m << 16) / 2688.0);
         }
-        if (threadIdx.x == 0) {
-            s_st = st;
-            if (blockIdx.x == 0) *p.tensor_scale_out = st;
-        }
+        s_st = st;
+        s_inv_st = 1.0 / (double)st;
+        if (blockIdx.x == 0) *p.tensor_scale_out = st;
     }
     __syncthreads();
     const float st = s_st;
     if (!(st > 0.0f && st < INFINITY)) return;  // non-finite input: outputs unspecified
     const bool fma_exact = st >= 0x1p-90f;
     const bool rne = (p.flags & 1u) != 0;
+    const bool fast = !SR && fast_path_scale(st);
+    const double inv_st = s_inv_st;
+    const float inv6st = (float)(inv_st / 6.0);  // scale-code guesses
     const int64_t bpr = p.k >> 4;
     const int64_t total = p.n * bpr;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -217,9 +358,13 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
         const uint4 v0 = reinterpret_cast<const uint4 *>(src)[0];
         const uint4 v1 = reinterpret_cast<const uint4 *>(src)[1];
         const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const uint32_t am = max(absmax_vec(v0), absmax_vec(v1));
+        const uint32_t am = absmax16(v0, v1);
         const float amax_b = __uint_as_float(am << 16);
-        const int sb = rne ? scale_code_rne(amax_b, st) : scale_code_round_up(amax_b, st);
+        int sb;
+        if (fast)  // (uniform)
+            sb = rne ? scale_code_rne_f32(amax_b, st, inv6st) : scale_code_round_up_f32(amax_b, st, inv6st);
+        else
+            sb = rne ? scale_code_rne(amax_b, st, inv6st) : scale_code_round_up(amax_b, st, inv6st);
         const float e = e4m3_value(sb);
         uint32_t lo = 0, hi = 0;
         if (SR && e != 0.0f) {
@@ -241,16 +386,51 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
                 else hi |= code << (4 * (j - 8));
             }
         } else if (e != 0.0f) {
-            const float ce[7] = {0.25f * e, 0.75f * e, 1.25f * e, 1.75f * e,
-                                 2.5f * e,  3.5f * e,  5.0f * e};
+            bool done = false;
+            if (fast && am < 0x7F80u) {  // (finite block)
+                const double r = inv_st * s_inv_e[sb];
+                const float rh = (float)r, rl = (float)(r - (double)rh);
+                if (amax_b * rh < 0x1p100f) {
+                    uint32_t suspect = 0;  // bit j: element j's quotient fell on an aligned value
+                    lo = fast_codes4<0>(wd[0], wd[1], wd[2], wd[3], rh, rl, suspect);
+                    hi = fast_codes4<8>(wd[4], wd[5], wd[6], wd[7], rh, rl, suspect);
+                    if (suspect) {
+                        // those elements again by the comparisons (the quotient
+                        // lies within 2^-24 of a midpoint whenever |w| / (e s_t)
+                        // is a short binary fraction times fl(s_t) / s_t's exact
+                        // value, which s_t = fl(amax / 2688) makes common)
+                        const float ce[7] = {0.25f * e, 0.75f * e, 1.25f * e, 1.75f * e,
+                                             2.5f * e,  3.5f * e,  5.0f * e};
+                        do {
+                            const int j = __builtin_ctz(suspect);
+                            suspect &= suspect - 1;
+                            const int wi = j >> 1;
+                            const uint32_t word = wi == 0 ? wd[0] : wi == 1 ? wd[1] : wi == 2 ? wd[2] : wi == 3 ? wd[3]
+                                                : wi == 4 ? wd[4] : wi == 5 ? wd[5] : wi == 6 ? wd[6] : wd[7];
+                            const uint32_t bits = (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+                            const float a = __uint_as_float((bits & 0x7FFFu) << 16);
+                            const uint32_t code = e2m1_mag_f32(a, ce, st) | ((bits >> 12) & 8u);
+                            const int sh = 4 * (j & 7);
+                            if (j < 8) lo = (lo & ~(0xFu << sh)) | code << sh;
+                            else hi = (hi & ~(0xFu << sh)) | code << sh;
+                        } while (suspect);
+                    }
+                    done = true;
+                }
+            }
+            if (!done) {
+                lo = hi = 0;
+                const float ce[7] = {0.25f * e, 0.75f * e, 1.25f * e, 1.75f * e,
+                                     2.5f * e,  3.5f * e,  5.0f * e};
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
-                const float a = __uint_as_float((bits & 0x7FFFu) << 16);
-                const uint32_t mag = fma_exact ? e2m1_mag_f32(a, ce, st) : e2m1_mag_f64(a, ce, st);
-                const uint32_t code = mag | ((bits >> 12) & 8u);
-                if (j < 8) lo |= code << (4 * j);
-                else hi |= code << (4 * (j - 8));
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t bits = (j & 1) ? (wd[j >> 1] >> 16) : (wd[j >> 1] & 0xFFFFu);
+                    const float a = __uint_as_float((bits & 0x7FFFu) << 16);
+                    const uint32_t mag = fma_exact ? e2m1_mag_f32(a, ce, st) : e2m1_mag_f64(a, ce, st);
+                    const uint32_t code = mag | ((bits >> 12) & 8u);
+                    if (j < 8) lo |= code << (4 * j);
+                    else hi |= code << (4 * (j - 8));
+                }
             }
         } else {
 #pragma unroll

@@ -123,6 +123,22 @@ def test_supplied_tensor_scale(s_in):
     _compare(bits, 1, s_in=s_in)
 
 
+@pytest.mark.parametrize("num,den", [(1, 3), (1, 7), (5, 21), (3, 7), (1, 21)])
+def test_quotients_next_to_midpoints(num, den):
+    """Elements +-n 2^j (n < 16) with s_t = fl(num / den): many |w| / (e s_t)
+    land within 2^-24 of an E2M1 midpoint (e.g. 3 f / e = 0.75 for s_t ~ 1/3),
+    where only the exact comparison decides the side."""
+    rng = np.random.default_rng(100 * den + num)
+    n = rng.integers(1, 16, size=(64, 256))
+    j = rng.integers(-8, 2, size=(64, 256))
+    sign = rng.choice([-1.0, 1.0], size=(64, 256))
+    vals = (sign * n * np.exp2(j)).astype(np.float32)  # 4-bit significands: exact in BF16
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    s_in = float(np.float32(num / den))
+    _compare(bits, 0, s_in=s_in)
+    _compare(bits, 1, s_in=s_in)
+
+
 def test_invalid_supplied_tensor_scale_gives_nan():
     bits = _dist("normal", 4, 32, 14)
     for s_in in (0.0, -1.0, float("inf"), float("nan")):
