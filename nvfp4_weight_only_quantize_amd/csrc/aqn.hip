@@ -12,11 +12,12 @@
 // (c/4, step, 0, 0), then Box-Muller (1958) on word pairs (r0, r1), (r2, r3).
 //
 // Launch: a 2-D grid.  blockIdx.x picks 1024 channels (4 per thread: one
-// Philox block), blockIdx.y a group of kRows rows.  Every workgroup reads the
-// whole of its rows for the sum of squares (L2-resident, a few KB per row),
-// so no workgroup waits for another and the noise of a channel is drawn by
-// kRows-row groups only.
+// Philox block), blockIdx.y a group of rows (one row for m <= 512, else
+// kRows).  Every workgroup reads the whole of its rows for the sum of squares
+// (L2-resident, a few KB per row), so no workgroup waits for another; the
+// noise of a channel is drawn once per row group.
 #include "device_common.h"
+#include "../../include/qerl.h"
 #include "qerl_internal.h"
 
 namespace qerl {
@@ -24,7 +25,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChanPerWg = 4 * kThreads;
-constexpr int kRows = 4;           // rows per workgroup
+constexpr int kRows = 4;           // rows per workgroup (m > kOneRowMaxM)
+constexpr int64_t kOneRowMaxM = 512;
 constexpr int kMaxRowGroups = 8192;
 
 __device__ __forceinline__ void box_muller(uint64_t ra, uint64_t rb, float &z0, float &z1) {
@@ -39,40 +41,58 @@ __device__ __forceinline__ void box_muller(uint64_t ra, uint64_t rb, float &z0, 
 
 // VEC: x rows 16-byte aligned (x % 16 == 0, ldx % 8 == 0, h % 8 == 0) and
 // outputs vector-aligned (y_f32 % 16, y_bf16 % 8, ldy % 4 == 0).
-template <bool VEC>
+// ROWS: rows per workgroup and row group.  Each row's loads -- its 16-byte
+// pieces for the sum of squares (at most kMaxPieces per thread) and this
+// thread's 4 output channels -- are issued together, and the noise is drawn
+// while they travel, so a row group costs one round trip.
+constexpr int kMaxPieces = (QERL_MAX_NORM_WIDTH / 8 + kThreads - 1) / kThreads;
+template <bool VEC, int ROWS>
 __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
-    __shared__ float s_red[kRows][4];
+    __shared__ float s_red[ROWS][4];
     const int tid = threadIdx.x, wave = tid >> 6;
     const int64_t g = (int64_t)blockIdx.x * kThreads + tid;  // Philox block: channels 4g .. 4g+3
     const int64_t c0 = 4 * g;
-    float wn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (c0 < a.h) {
-        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sigma == 0: no noise to draw (w + 0 z is w)
-        if (a.sigma != 0.0f) {
-            const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
-            box_muller(r.v[0], r.v[1], z[0], z[1]);
-            box_muller(r.v[2], r.v[3], z[2], z[3]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (c0 + i < a.h) {
-                wn[i] = __builtin_fmaf(a.sigma, z[i], a.weight[c0 + i]);
-                if (blockIdx.y == 0 && a.noisy_out) a.noisy_out[c0 + i] = wn[i];
-            }
-    }
     const float inv_h = 1.0f / (float)a.h;
-    for (int64_t rg = blockIdx.y; rg * kRows < a.m; rg += gridDim.y) {
-        const int64_t row0 = rg * kRows;
-        float ss[kRows];
+    bool drawn = false;
+    float wn[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t rg = blockIdx.y; rg * ROWS < a.m; rg += gridDim.y) {
+        const int64_t row0 = rg * ROWS;
+        float ss[ROWS];
+        uint2 xo[ROWS];  // this thread's output channels of each row (VEC)
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
+        for (int i = 0; i < ROWS; ++i) {
             ss[i] = 0.0f;
+            xo[i] = make_uint2(0, 0);
             if (row0 + i >= a.m) continue;
             const uint16_t *xr = a.x + (row0 + i) * a.ldx;
             if (VEC) {
-                for (int64_t p = tid; p * 8 < a.h; p += kThreads) {
-                    const uint4 v = *reinterpret_cast<const uint4 *>(xr + p * 8);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+                uint4 v[kMaxPieces];
+#pragma unroll
+                for (int u = 0; u < kMaxPieces; ++u) {
+                    const int64_t pc = tid + (int64_t)u * kThreads;
+                    v[u] = pc * 8 < a.h ? *reinterpret_cast<const uint4 *>(xr + pc * 8) : make_uint4(0, 0, 0, 0);
+                }
+                if (c0 < a.h) xo[i] = *reinterpret_cast<const uint2 *>(xr + c0);
+                if (!drawn) {  // (first row only) the noise while the loads travel
+                    drawn = true;
+                    if (c0 < a.h) {
+                        float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // sigma == 0: w + 0 z is w
+                        if (a.sigma != 0.0f) {
+                            const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
+                            box_muller(r.v[0], r.v[1], z[0], z[1]);
+                            box_muller(r.v[2], r.v[3], z[2], z[3]);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (c0 + j < a.h) {
+                                wn[j] = __builtin_fmaf(a.sigma, z[j], a.weight[c0 + j]);
+                                if (blockIdx.y == 0 && a.noisy_out) a.noisy_out[c0 + j] = wn[j];
+                            }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kMaxPieces; ++u) {
+                    const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const float lo = bf16lo_to_f32(w4[j]), hi = bf16hi_to_f32(w4[j]);
@@ -87,23 +107,39 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
                 }
             }
         }
+        if (!drawn) {  // (no row drawn the noise yet: the scalar path, or a short row group)
+            drawn = true;
+            if (c0 < a.h) {
+                float z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if (a.sigma != 0.0f) {
+                    const U64x4 r = philox4x64_10((uint64_t)g, a.step, 0, 0, a.seed, (uint64_t)a.layer);
+                    box_muller(r.v[0], r.v[1], z[0], z[1]);
+                    box_muller(r.v[2], r.v[3], z[2], z[3]);
+                }
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) ss[i] = wave_sum(ss[i]);
+                for (int j = 0; j < 4; ++j)
+                    if (c0 + j < a.h) {
+                        wn[j] = __builtin_fmaf(a.sigma, z[j], a.weight[c0 + j]);
+                        if (blockIdx.y == 0 && a.noisy_out) a.noisy_out[c0 + j] = wn[j];
+                    }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ROWS; ++i) ss[i] = wave_sum(ss[i]);
         __syncthreads();  // s_red may still be read for the previous row group
         if ((tid & 63) == 0)
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) s_red[i][wave] = ss[i];
+            for (int i = 0; i < ROWS; ++i) s_red[i][wave] = ss[i];
         __syncthreads();
         if (c0 >= a.h) continue;
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) {
+        for (int i = 0; i < ROWS; ++i) {
             const int64_t row = row0 + i;
             if (row >= a.m) break;
             const float tot = (s_red[i][0] + s_red[i][1]) + (s_red[i][2] + s_red[i][3]);
             const float inv = 1.0f / sqrtf(tot * inv_h + a.eps);
-            const uint16_t *xr = a.x + row * a.ldx;
             if (VEC) {
-                const uint2 xv = *reinterpret_cast<const uint2 *>(xr + c0);
+                const uint2 xv = xo[i];
                 const float y0 = bf16lo_to_f32(xv.x) * inv * wn[0], y1 = bf16hi_to_f32(xv.x) * inv * wn[1];
                 const float y2 = bf16lo_to_f32(xv.y) * inv * wn[2], y3 = bf16hi_to_f32(xv.y) * inv * wn[3];
                 if (a.y_f32) *reinterpret_cast<float4 *>(a.y_f32 + row * a.ldy + c0) = make_float4(y0, y1, y2, y3);
@@ -111,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void aqn_rmsnorm_kernel(AqnArgs a) {
                     *reinterpret_cast<uint2 *>(a.y_bf16 + row * a.ldy + c0) =
                         make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
             } else {
+                const uint16_t *xr = a.x + row * a.ldx;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int64_t c = c0 + j;
@@ -151,13 +188,23 @@ hipError_t launch_aqn_noisy_weight(const AqnArgs &a, hipStream_t stream) {
 hipError_t launch_aqn_rmsnorm(const AqnArgs &a, hipStream_t stream) {
     const bool vec = ((uintptr_t)a.x & 15u) == 0 && a.ldx % 8 == 0 && a.h % 8 == 0 &&
                      ((uintptr_t)a.y_f32 & 15u) == 0 && ((uintptr_t)a.y_bf16 & 7u) == 0 && a.ldy % 4 == 0;
-    const int64_t row_groups = (a.m + kRows - 1) / kRows;
+    // one row per workgroup while that gives few enough workgroups (each
+    // draws its channels' noise once); kRows rows per group above
+    const int rows = a.m <= kOneRowMaxM ? 1 : kRows;
+    const int64_t row_groups = (a.m + rows - 1) / rows;
     const dim3 grid((unsigned)((a.h + kChanPerWg - 1) / kChanPerWg),
                     (unsigned)(row_groups < kMaxRowGroups ? row_groups : kMaxRowGroups));
-    if (vec)
-        hipLaunchKernelGGL(aqn_rmsnorm_kernel<true>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(aqn_rmsnorm_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+    if (vec) {
+        if (rows == 1)
+            hipLaunchKernelGGL((aqn_rmsnorm_kernel<true, 1>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((aqn_rmsnorm_kernel<true, kRows>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (rows == 1)
+            hipLaunchKernelGGL((aqn_rmsnorm_kernel<false, 1>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((aqn_rmsnorm_kernel<false, kRows>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

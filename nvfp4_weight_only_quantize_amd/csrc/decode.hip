@@ -146,10 +146,6 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     if (s < 1) s = 1;
     const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
-#ifdef QERL_MFMA_SPLIT_DIV
-        s = s / QERL_MFMA_SPLIT_DIV;
-        if (s < 1) s = 1;
-#endif
         // fewer row blocks than CUs split K as above; more keep at least
         // kUnitMinChunks chunks per unit but still split K (several units
         // per CU keep more loads in flight than one long unit)
