@@ -346,7 +346,10 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
     // g * lambda / s_t, 64 ranks per step (rows of the tile past r are zero)
     const float st = *a.tensor_scale;
     const float gs = a.lora_scale / st;
-    for (int64_t j0 = 0; j0 < a.r; j0 += kBN) {
+    // lambda / s_t finite and moderate: the ranks ride in the accumulation;
+    // else (tiny s_t) the epilogue adds lambda sum_j g[i, j] A[j, kk] itself
+    const bool fold = __builtin_isfinite(gs) && __builtin_fabsf(gs) <= 0x1p64f;  // (uniform)
+    for (int64_t j0 = 0; fold && j0 < a.r; j0 += kBN) {
         // A row j0 + nl, 32 columns at kcol (BF16 as it is), transposed into the tile
         uint4 av[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
                        make_uint4(0, 0, 0, 0)};
@@ -402,7 +405,16 @@ __global__ __launch_bounds__(kThreads) void dx_kernel(DxArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int64_t row = mrow0 + 16 * i + 4 * lq + v, col = kk0 + 16 * j + lr;
-                if (row < a.m && col < a.k) a.dx[row * a.lddx + col] = f32_to_bf16_bits(st * acc[i][j][v]);
+                if (row < a.m && col < a.k) {
+                    float d = st * acc[i][j][v];
+                    if (!fold) {
+                        float l = 0.0f;
+                        for (int jr = 0; jr < a.r; ++jr)
+                            l = __builtin_fmaf(a.g[row * a.r + jr], bf16lo_to_f32(a.lora_a[jr * a.k + col]), l);
+                        d = __builtin_fmaf(a.lora_scale, l, d);
+                    }
+                    a.dx[row * a.lddx + col] = f32_to_bf16_bits(d);
+                }
             }
 }
 

@@ -75,6 +75,25 @@ struct Gemm {
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
 };
 
+// The LoRA product rides in the MFMA accumulation as t * lora_scale / s_t,
+// which needs that factor finite and moderate; for tiny s_t (a subnormal or
+// a caller's tensor scale far below lora_scale) it is not, and then the
+// prologue stores lora_scale * t in FP32 in the same region, the extra K
+// columns read as zeros, and the epilogue adds sum_j (lora_scale t[m, j])
+// B[n, j] to s_t * acc.  Every kernel decides the same way from the same two
+// floats.
+__device__ __forceinline__ bool lora_fold_ok(float lora_scale, float st) {
+    const float mul = lora_scale / st;
+    return __builtin_isfinite(mul) && __builtin_fabsf(mul) <= 0x1p64f;
+}
+
+// sum_j t32[m, j] B[n, j] in rank order (the unfolded LoRA term)
+__device__ __forceinline__ float lora_term(const GemmArgs &a, const float *t32, int64_t m, int64_t n) {
+    float s = 0.0f;
+    for (int j = 0; j < a.r; ++j) s = __builtin_fmaf(t32[m * a.r + j], bf16lo_to_f32(a.lora_b[n * a.r + j]), s);
+    return s;
+}
+
 // ---------------------------------------------------------------------------
 // Prologue: LoRA down-projection t = x A^T
 // ---------------------------------------------------------------------------
@@ -139,6 +158,7 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
     __syncthreads();
     if (wave != 0) return;
     const float mul = a.lora_scale / *a.tensor_scale;
+    const bool fold = lora_fold_ok(a.lora_scale, *a.tensor_scale);  // (uniform)
     uint16_t *t16 = g.t16();
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
@@ -148,6 +168,10 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
         for (int v = 0; v < 4; ++v) {
             const int64_t m = m0 + 4 * lq + v;
             if (m >= a.m || jr >= a.r) continue;
+            if (!fold) {  // lora_scale * t in FP32, for the epilogue
+                reinterpret_cast<float *>(t16)[m * a.r + jr] = t[v] * a.lora_scale;
+                continue;
+            }
             const float u = t[v] * mul;
             const uint16_t hi = f32_to_bf16_bits(u);
             t16[m * 2 * a.r + jr] = hi;
@@ -176,13 +200,13 @@ __shared__ __attribute__((aligned(1024))) uint8_t g_xtile1[kXTileBytes];
 // 8 elements of the extended K range [0, k + 2r) for x row m at column kk:
 // x itself, then the BF16 hi/lo halves of t * lora_scale / s_t; zero past
 // the end and for rows past m.
-__device__ __forceinline__ uint4 x_piece_ext(const Gemm &g, int64_t m, int64_t kk, int64_t klora) {
+__device__ __forceinline__ uint4 x_piece_ext(const Gemm &g, int64_t m, int64_t kk, int64_t klora, bool fold) {
     const GemmArgs &a = g.a;
     uint4 o = make_uint4(0, 0, 0, 0);
     if (m >= a.m) return o;
     if (kk < a.k) return *reinterpret_cast<const uint4 *>(a.x + m * a.ldx + kk);
     const int64_t j0 = kk - a.k;
-    if (j0 >= klora) return o;
+    if (j0 >= klora || !fold) return o;
     const uint16_t *t16 = g.t16() + m * klora;
     uint16_t e[8];
 #pragma unroll
@@ -232,6 +256,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
     const int64_t gm = tiles_m - grp * kGroupM < kGroupM ? tiles_m - grp * kGroupM : kGroupM;  // rows in this group
     const int64_t m0 = (grp * kGroupM + in_grp % gm) * PBM, n0 = (in_grp / gm) * PBN;
     const int64_t klora = 2 * (int64_t)a.r;
+    const bool fold = a.r == 0 || lora_fold_ok(a.lora_scale, *a.tensor_scale);  // (uniform)
 
     f32x4_t acc[8][4];
 #pragma unroll
@@ -252,7 +277,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
     if (last)
         plain_kloop<8, kPfWaves>(
             blocks * kTileK, a.k + klora, g_xtile0,
-            [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora); },
+            [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora, fold); },
             [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
 
     if (SPLIT) {  // FP32 partial outputs; reduce_kernel finishes
@@ -270,6 +295,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
         return;
     }
     const float st_scale = *a.tensor_scale;
+    const float *t32 = reinterpret_cast<const float *>(g.t16());
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -278,7 +304,11 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
             for (int v = 0; v < 4; ++v) {
                 const int64_t m = m0 + 16 * i + 4 * lq + v;
                 const int64_t n = n0 + wave * 64 + 16 * j + lr;
-                if (m < a.m && n < a.n) a.y[m * a.ldy + n] = f32_to_bf16_bits(st_scale * acc[i][j][v]);
+                if (m < a.m && n < a.n) {
+                    float yv = st_scale * acc[i][j][v];
+                    if (!fold) yv += lora_term(a, t32, m, n);
+                    a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
+                }
             }
 }
 
@@ -300,7 +330,10 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(Gemm g) {
 #pragma unroll
     for (int s = 0; s < kMaxSplits; ++s)
         if (s < g.p.splits) acc += v[s];
-    a.y[m * a.ldy + n] = f32_to_bf16_bits(*a.tensor_scale * acc);
+    float yv = *a.tensor_scale * acc;
+    if (a.r > 0 && !lora_fold_ok(a.lora_scale, *a.tensor_scale))
+        yv += lora_term(a, reinterpret_cast<const float *>(g.t16()), m, n);
+    a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
 }
 
 }  // namespace

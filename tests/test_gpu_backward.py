@@ -30,8 +30,11 @@ def _case(m, n, k, r, seed):
     return dy, x, packed, scales, s_t, a, b, wq
 
 
-def _check(m, n, k, r, seed, lam=2.0, strided=False):
+def _check(m, n, k, r, seed, lam=2.0, strided=False, s_t_override=None):
     dy, x, packed, scales, s_t, a, b, wq = _case(m, n, k, r, seed)
+    if s_t_override is not None:  # the same codes under another tensor scale
+        s_t = np.float32(s_t_override)
+        wq = q.NVFP4Weight(wq.packed, wq.scales, torch.tensor([s_t], dtype=torch.float32, device=dev()))
     dyg, xg = bits_to_gpu(dy), bits_to_gpu(x)
     if strided:
         big = torch.zeros((m, n + 24), dtype=torch.bfloat16, device=dev())
@@ -100,3 +103,12 @@ def test_backward_rejects_non_contiguous_lora():
         q.w4a16_lora_backward(bits_to_gpu(dy), bits_to_gpu(x), wq, a_view, bg, 2.0)
     with pytest.raises(ValueError):
         q.w4a16_lora_backward(bits_to_gpu(dy), bits_to_gpu(x), wq, ag, b_view, 2.0)
+
+
+@pytest.mark.parametrize("s_t", [1e-39, 1e-30, 1e-18])
+def test_backward_tiny_tensor_scale(s_t):
+    """lambda / s_t overflows FP32 (1e-39, a subnormal) or exceeds the folding
+    bound (1e-30): the LoRA term is added outside the accumulation; 1e-18
+    still folds.  dx is then dominated by the LoRA term."""
+    _check(100, 130, 528, 32, seed=5300, s_t_override=s_t)
+    _check(70, 64, 144, 8, seed=5301, s_t_override=s_t)

@@ -247,3 +247,25 @@ def test_shared_workspace_sequence_is_deterministic():
     for i in (0, 3):
         m, n, k, r = cases[i]
         assert_gemm_close(bf16_to_f64(fresh[i]), layers[i].ref(synth.bf16_bits(xs[i].cpu())), f"case {cases[i]}")
+
+
+@pytest.mark.parametrize("s_t", [1e-39, 1e-30, 1e-18])
+@pytest.mark.parametrize("m", [65, 300])
+def test_tiny_tensor_scale(m, s_t):
+    """The prefill path folds lambda / s_t into its accumulation only while
+    that factor is finite and moderate; for a subnormal or tiny s_t the LoRA
+    term is added in the epilogue (split and unsplit K both: 300 x 1000 x 2048
+    splits, 65 x 96 x 256 does not).  Decode (m <= 64) applies s_t apart."""
+    for n, k, r in ((96, 256, 16), (1000, 2048, 32)):
+        L = Layer(n, k, r, seed=900 + n + m)
+        L.s_t = np.float32(s_t)
+        L.wq = q.NVFP4Weight(L.wq.packed, L.wq.scales, torch.tensor([L.s_t], dtype=torch.float32, device=dev()))
+        x = _x(m, k, seed=m + 3 * k)
+        y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+        assert_gemm_close(y, L.ref(x), f"m={m} n={n} k={k} r={r} s_t={s_t}")
+    # decode path, same scales
+    L = Layer(96, 256, 16, seed=990)
+    L.s_t = np.float32(s_t)
+    L.wq = q.NVFP4Weight(L.wq.packed, L.wq.scales, torch.tensor([L.s_t], dtype=torch.float32, device=dev()))
+    x = _x(8, 256, seed=991)
+    assert_gemm_close(bf16_to_f64(L.gpu(bits_to_gpu(x))), L.ref(x), f"decode s_t={s_t}")
