@@ -32,6 +32,18 @@ qerl_status hip_status(hipError_t e, const char *what) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// QERL_DEBUG set (and not "0"): every GEMM call first checks its launch plan's
+// workspace use against the size query on the host (decode_plan_check and
+// the prefill plan's check) and fails with QERL_ERR_WORKSPACE instead of
+// launching a plan that would address past it.
+bool debug_checks() {
+    static const bool on = [] {
+        const char *v = getenv("QERL_DEBUG");
+        return v && *v && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
 // Largest element count a single tensor may have (keeps 64-bit index math far
 // from overflow and every grid dimension in range).
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
@@ -211,6 +223,11 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
     if (workspace && !aligned16(workspace))
         return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm: workspace must be 16-byte aligned");
     a.workspace = workspace;
+    if (debug_checks()) {
+        char msg[200];
+        if (qerl::gemm_plan_check(m, n, k, r, (int64_t)need, msg, sizeof msg))
+            return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm: plan check: %s", msg);
+    }
     return hip_status(qerl::launch_w4a16_lora_gemm(a, static_cast<hipStream_t>(stream)),
                       "w4a16_lora_gemm launch");
 }
@@ -234,6 +251,11 @@ qerl_status qerl_w4a16_lora_gemm_noalloc(const void *x_bf16, int64_t m, int64_t 
     const qerl_status sst = hip_status(qerl::noalloc_scratch(&ws), "w4a16_lora_gemm_noalloc: scratch address");
     if (sst != QERL_OK) return sst;
     a.workspace = ws;
+    if (debug_checks()) {
+        char msg[200];
+        if (qerl::gemm_plan_check(m, n, k, r, (int64_t)need, msg, sizeof msg))
+            return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm_noalloc: plan check: %s", msg);
+    }
     return hip_status(qerl::launch_w4a16_lora_gemm(a, static_cast<hipStream_t>(stream)),
                       "w4a16_lora_gemm_noalloc launch");
 }
@@ -276,6 +298,11 @@ qerl_status qerl_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, int64_t k,
     if (workspace && !aligned16(workspace))
         return fail(QERL_ERR_ALIGN, "w4a16_lora_gemm_multi: workspace must be 16-byte aligned");
     for (int i = 0; i < nseg; ++i) a[i].workspace = workspace;
+    if (debug_checks()) {
+        char msg[200];
+        if (qerl::gemm_multi_plan_check(m, k, n, r, nseg, false, msg, sizeof msg))
+            return fail(QERL_ERR_WORKSPACE, "w4a16_lora_gemm_multi: plan check: %s", msg);
+    }
     return hip_status(qerl::launch_w4a16_lora_gemm_multi(a, nseg, static_cast<hipStream_t>(stream)),
                       "w4a16_lora_gemm_multi launch");
 }
@@ -328,6 +355,11 @@ qerl_status qerl_rmsnorm_w4a16_lora_gemm_multi(const void *x_bf16, int64_t m, in
         a[i].workspace = workspace;
         a[i].norm_w = norm_weight;
         a[i].norm_eps = eps;
+    }
+    if (debug_checks()) {
+        char msg[200];
+        if (qerl::gemm_multi_plan_check(m, k, n, r, nseg, true, msg, sizeof msg))
+            return fail(QERL_ERR_WORKSPACE, "rmsnorm_w4a16_lora_gemm_multi: plan check: %s", msg);
     }
     return hip_status(qerl::launch_norm_gemm_multi(a, nseg, static_cast<hipStream_t>(stream)),
                       "rmsnorm_w4a16_lora_gemm_multi launch");

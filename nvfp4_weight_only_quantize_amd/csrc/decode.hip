@@ -34,6 +34,8 @@
 // Several projections of one x (q/k/v, gate/up) share a launch: the segment
 // is a grid dimension; a one-segment launch is its own instantiation with a
 // one-plan argument.
+#include <stdio.h>
+
 #include "device_common.h"
 #include "mfma_tile.h"
 #include "qerl_internal.h"
@@ -1046,6 +1048,52 @@ size_t decode_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, cons
 hipError_t launch_decode_multi(const GemmArgs *segs, int nseg, hipStream_t stream) {
     if (nseg < 1 || nseg > kMaxSegments) return hipErrorInvalidValue;
     return launch_decode_set(make_decode_set(segs, nseg), stream);
+}
+
+// The furthest workspace byte each kernel of a decode launch addresses,
+// recomputed from the plan fields its indexing uses, against the size query
+// the caller sized the workspace by; and the grid and LDS limits the
+// launcher relies on.
+int decode_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm, char *msg,
+                      size_t len) {
+    auto fail = [&](const char *what, int64_t seg, int64_t a, int64_t b) {
+        snprintf(msg, len, "decode m=%lld k=%lld segment %lld: %s (%lld > %lld)", (long long)m, (long long)k,
+                 (long long)seg, what, (long long)a, (long long)b);
+        return 1;
+    };
+    if (nseg < 1 || nseg > kMaxSegments) return fail("segment count", 0, nseg, kMaxSegments);
+    const int64_t size = nseg == 1 && !norm ? (int64_t)decode_workspace_bytes(m, n[0], k, r[0])
+                                            : (int64_t)decode_multi_workspace_bytes(m, k, n, r, nseg, norm);
+    int64_t rows = 0;
+    for (int j = 0; j < nseg; ++j) rows += make_decode_plan(m, n[j], k, r[j], 0, norm).row_blocks;
+    int64_t off = 0, slices0 = -1;
+    for (int j = 0; j < nseg; ++j) {
+        const DecodePlan p = make_decode_plan(m, n[j], k, r[j], rows, norm);
+        if (p.row_blocks < 1) return fail("no row blocks", j, 1, p.row_blocks);
+        if (slices0 < 0) slices0 = p.slices;
+        if (p.slices != slices0) return fail("slices differ between segments", j, p.slices, slices0);
+        if (p.row_blocks * p.rows_per_unit < n[j]) return fail("rows not covered", j, n[j], p.row_blocks * p.rows_per_unit);
+        if (p.slices * p.cps < p.chunks) return fail("K not covered", j, p.chunks, p.slices * p.cps);
+        const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;  // bytes of one unit's FP32 tile
+        // f32x4 slots a unit writes: stream_kernel wave * 64 + lane; an MFMA
+        // unit ((layout wave MT + i) NW + n-tile) 64 + lane
+        const int64_t slots = p.mt == 1 ? (int64_t)kWaves * 64 : (int64_t)4 * p.mt * p.nw * 64;
+        if (slots * 16 > tile) return fail("unit tile slots", j, slots * 16, tile);
+        if (p.units != p.row_blocks * p.slices) return fail("units", j, p.units, p.row_blocks * p.slices);
+        const int64_t units_end = p.part_off + p.units * tile;  // written by the units, read by finish_kernel
+        if (units_end > p.tpart_off) return fail("unit tiles past their region", j, units_end, p.tpart_off);
+        // producers: f32x4 (mt JT + rank tile) 64 + lane of K range kr < prod_kr
+        const int64_t prod_end = p.tpart_off + (p.producers ? p.prod_kr * p.mt * p.jt * 64 * 16 : 0);
+        if (prod_end > p.ss_off) return fail("producer tiles past their region", j, prod_end, p.ss_off);
+        const int64_t ss_end = p.ss_off + (p.norm && p.producers ? p.prod_kr * 16 * 4 : 0);
+        if (ss_end > p.bytes) return fail("sums of squares past the plan", j, ss_end, p.bytes);
+        if (p.producers && p.prod_kr > kMaxProdRanges) return fail("producer K ranges", j, p.prod_kr, kMaxProdRanges);
+        if (p.producers + p.units > 0x7FFFFFFF) return fail("grid", j, p.producers + p.units, 0x7FFFFFFF);
+        if (p.mt == 1 && p.lds_bytes > kLdsLimit) return fail("LDS", j, p.lds_bytes, kLdsLimit);
+        off += align256(p.bytes);
+        if (off > size) return fail("segment data past the size query", j, off, size);
+    }
+    return 0;
 }
 
 }  // namespace qerl

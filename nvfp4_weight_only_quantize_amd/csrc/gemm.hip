@@ -20,6 +20,8 @@
 //                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
 //                    s_t applied once.  Grids of few tiles split K; then
 //   reduce_kernel    sums the FP32 partial outputs in split order.
+#include <stdio.h>
+
 #include "device_common.h"
 #include "mfma_tile.h"
 #include "qerl_internal.h"
@@ -405,6 +407,44 @@ hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t st
         g[i].norm_w = nullptr;
     }
     return launch_w4a16_lora_gemm_multi(g, nseg, stream);
+}
+
+// The workspace use of one projection's launch against its size query (the
+// decode plan's own check for m <= 64): the prologue's t region [m][r] four
+// bytes each (BF16 hi/lo or FP32), the split partial outputs and their
+// reduction, and the grid limits.
+int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *msg, size_t len) {
+    if (m <= kDecodeMaxM) return decode_plan_check(m, k, &n, &r, 1, false, msg, len);
+    const Plan p = make_plan(m, n, k, r);
+    auto fail = [&](const char *what, int64_t a, int64_t b) {
+        snprintf(msg, len, "prefill m=%lld n=%lld k=%lld r=%d: %s (%lld > %lld)", (long long)m, (long long)n,
+                 (long long)k, r, what, (long long)a, (long long)b);
+        return 1;
+    };
+    if (p.t_off + m * (int64_t)r * 4 > p.part_off) return fail("t region", p.t_off + m * (int64_t)r * 4, p.part_off);
+    const int64_t part_end = p.part_off + (p.splits > 1 ? p.splits * m * n * 4 : 0);
+    if (part_end > size) return fail("partial outputs", part_end, size);
+    if (p.splits > kMaxSplits) return fail("splits", p.splits, kMaxSplits);
+    if (p.splits > 1 && (p.splits - 1) * p.bps >= k / 128) return fail("empty split", (p.splits - 1) * p.bps, k / 128 - 1);
+    if (p.tiles * p.splits > 0x7FFFFFFF) return fail("grid", p.tiles * p.splits, 0x7FFFFFFF);
+    return 0;
+}
+
+int gemm_multi_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm, char *msg,
+                          size_t len) {
+    if (norm ? norm_fused(m, k) : m <= kDecodeMaxM) return decode_plan_check(m, k, n, r, nseg, norm, msg, len);
+    const int64_t size = (int64_t)gemm_multi_workspace_bytes(m, k, n, r, nseg);
+    for (int j = 0; j < nseg; ++j)  // one launch after another, each with the whole workspace
+        if (gemm_plan_check(m, n[j], k, r[j], size, msg, len)) return 1;
+    if (norm) {  // the normed x after the GEMMs' part
+        const int64_t xn_end = align256(size) + m * k * 2, nsize = (int64_t)norm_gemm_multi_workspace_bytes(m, k, n, r, nseg);
+        if (xn_end > nsize) {
+            snprintf(msg, len, "norm m=%lld k=%lld: normed x past the size query (%lld > %lld)", (long long)m,
+                     (long long)k, (long long)xn_end, (long long)nsize);
+            return 1;
+        }
+    }
+    return 0;
 }
 
 hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {

@@ -68,6 +68,15 @@ hipError_t launch_decode_multi(const GemmArgs *segs, int nseg, hipStream_t strea
 constexpr int64_t kNormFuseMaxM = 16;
 size_t norm_gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
 hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
+// Host checks of a launch's workspace use against its size query (0: in
+// bounds; else a message in msg): decode (m <= 64) launches over segments of
+// one x, one projection's launch for a workspace of `size` bytes, and the
+// multi-segment calls with or without the RMSNorm.
+int decode_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm, char *msg,
+                      size_t len);
+int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *msg, size_t len);
+int gemm_multi_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm, char *msg,
+                          size_t len);
 
 // ---- backward of the layer (LoRA trained, W frozen) ----
 constexpr int kMaxRankBwd = 128;  // QERL_MAX_LORA_RANK

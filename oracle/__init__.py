@@ -29,6 +29,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qerl_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libqerl_oracle.so")
+# a separately built copy of the same source (the sanitizer run of the tests)
+_LIB_OVERRIDE = os.environ.get("QERL_ORACLE_LIB")
 
 SCALE_ROUND_UP = 0
 SCALE_RNE = 1
@@ -51,9 +53,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build(force=True)
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i64, i32, u32, u64, dbl, flt = (ctypes.c_int64, ctypes.c_int, ctypes.c_uint,
                                     ctypes.c_uint64, ctypes.c_double, ctypes.c_float)
