@@ -1009,6 +1009,68 @@ def summarize_profile(cls, trace_dir, fetch_dir, write_dir):
     print(f"- sources_sha256: {kernel_sources_sha256(c['sources'])}")
 
 
+def summarize_quantizer_profile(trace_dir, fetch_dir, write_dir):
+    """Print the markdown summary of three rocprofv3 runs of `--quantizer-only
+    --copy-probe` (the 32B layer's seven tensors: amax_kernel then
+    encode_kernel each, two-pass timing then one-pass): kernel statistics,
+    per-layer durations of each pass, and HBM bytes per layer from
+    FETCH_SIZE / WRITE_SIZE scaled by the 256 MiB copy."""
+    import csv
+    import glob
+
+    def rows(d, pat):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", pat), recursive=True):
+            with open(f) as fh:
+                out += list(csv.DictReader(fh))
+        return out
+
+    stats = rows(trace_dir, "*kernel_stats.csv")
+    lines = ["| kernel | calls | average (us) | min (us) | max (us) |", "|---|---:|---:|---:|---:|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:8]:
+        nm = r["Name"].replace("qerl::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+        lines.append(f"| `{nm[:60]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    ours = [r for r in stats if "amax_kernel" in r["Name"] or "encode_kernel<false>" in r["Name"]]
+    amax = [r for r in ours if "amax_kernel" in r["Name"]]
+    enc = [r for r in ours if "encode_kernel" in r["Name"]]
+    layers_amax = sum(int(r["Calls"]) for r in amax) / 7  # two-pass layer quantizations (7 tensors each)
+    layers_enc = sum(int(r["Calls"]) for r in enc) / 7    # every layer quantization, both routes
+    amax_us = sum(float(r["TotalDurationNs"]) for r in amax) / 1e3 / max(layers_amax, 1)
+    enc_us = sum(float(r["TotalDurationNs"]) for r in enc) / 1e3 / max(layers_enc, 1)
+    elems = sum(n * k for n, k in synth.QWEN25_32B.values())
+
+    def per_layer(d, counter):
+        vals, copy = {"amax": 0.0, "encode": 0.0}, []
+        for r in rows(d, "*counter_collection.csv"):
+            if r["Counter_Name"] != counter:
+                continue
+            if "amax_kernel" in r["Kernel_Name"]:
+                vals["amax"] += float(r["Counter_Value"])
+            elif "encode_kernel<false>" in r["Kernel_Name"]:
+                vals["encode"] += float(r["Counter_Value"])
+            elif "copyBuffer" in r["Kernel_Name"]:
+                copy.append(float(r["Counter_Value"]))
+        return vals["amax"] / max(layers_amax, 1), vals["encode"] / max(layers_enc, 1), max(copy) if copy else float("nan")
+
+    fa, fe, f_copy = per_layer(fetch_dir, "FETCH_SIZE")
+    wa, we, w_copy = per_layer(write_dir, "WRITE_SIZE")
+    copy_kib = 256 * 1024
+    fs, ws = copy_kib / f_copy, copy_kib / w_copy
+    print("\n".join(lines))
+    print()
+    print(f"- layer: Qwen2.5-32B-shaped, 7 tensors, {elems / 1e9:.4f} G elements")
+    print(f"- amax_us_per_layer: {amax_us:.1f} (pass 1, {layers_amax:.0f} layers)")
+    print(f"- encode_us_per_layer: {enc_us:.1f} (pass 2, {layers_enc:.0f} layers)")
+    print(f"- two_pass_GB/s: {elems * 4.5625 / ((amax_us + enc_us) * 1e-6) / 1e9:.0f} (4.5625 B per element)")
+    print(f"- one_pass_GB/s: {elems * 2.5625 / (enc_us * 1e-6) / 1e9:.0f} (encode only, 2.5625 B per element)")
+    print(f"- amax_fetch_kib_per_layer: {fa:.0f}; encode_fetch_kib_per_layer: {fe:.0f}")
+    print(f"- amax_write_kib_per_layer: {wa:.0f}; encode_write_kib_per_layer: {we:.0f}")
+    print(f"- copy_probe_fetch_kib: {f_copy:.1f} (scale {fs:.4f}); copy_probe_write_kib: {w_copy:.1f} (scale {ws:.4f})")
+    print(f"- hbm_bytes_per_layer: amax {fa * fs * 1024:.0f}, encode {(fe * fs + we * ws) * 1024:.0f} "
+          f"(algorithmic: amax {2 * elems}, encode {int(2.5625 * elems)})")
+
+
 def summarize_prefill_profile(trace_dir, fetch_dir, write_dir, mfma_dir):
     """Print the markdown summary of four rocprofv3 runs of `--prefill-only`
     for its dominant launch, prefill_kernel on the fused gate/up GEMM at
@@ -1103,6 +1165,8 @@ def main():
                     help="only the prefill leg (for rocprofv3 runs); prints its JSON")
     ap.add_argument("--quantizer-only", action="store_true",
                     help="only the one-layer quantizer leg (for rocprofv3 runs); prints its JSON")
+    ap.add_argument("--summarize-quantizer", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print the quantizer profile summary of rocprofv3 output directories and exit")
     ap.add_argument("--summarize-prefill", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
                     help="print the prefill profile summary of rocprofv3 output directories and exit")
     args = ap.parse_args()
@@ -1111,6 +1175,9 @@ def main():
         return
     if args.summarize_prefill:
         summarize_prefill_profile(*args.summarize_prefill)
+        return
+    if args.summarize_quantizer:
+        summarize_quantizer_profile(*args.summarize_quantizer)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: there is no multi-GPU path here (pass --gpus 1)", file=sys.stderr)
