@@ -42,11 +42,13 @@ constexpr int kThreads = 256;
 constexpr int kPfWaves = QERL_PF_WAVES;  // waves of a prefill workgroup, 64 weight rows each
 constexpr int PBM = 128, PBN = 64 * kPfWaves;  // output tile: rows of x x weight rows
 constexpr int64_t kSplitTiles = 256;  // below this many tiles (fewer than CUs) K is split
+constexpr int64_t kPrologueWgs = 128;  // below this many prologue workgroups its K is split
 constexpr int64_t kMaxSplits = 16;
 
 struct Plan {
     int64_t tiles, splits, bps;  // output tiles, K splits, 128-column blocks per split
-    int64_t t_off, part_off, bytes;
+    int64_t ksplit, kchunk;      // prologue: K ranges (FP32 partial t each when > 1), columns per range
+    int64_t t_off, tpart_off, part_off, bytes;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -64,8 +66,23 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     }
     p.bps = (blocks + p.splits - 1) / p.splits;
     if (p.splits > 1) p.splits = (blocks + p.bps - 1) / p.bps;  // no empty split
+    // the prologue: one workgroup per 16 rows of x; with fewer than
+    // kPrologueWgs of them, K is split too (ranges of at least 512 columns,
+    // a multiple of 128) and t_reduce_kernel adds the ranges' FP32 partials
+    const int64_t row_groups = (m + 15) / 16;
+    p.ksplit = 1;
+    p.kchunk = k;
+    if (r > 0 && row_groups < kPrologueWgs) {
+        int64_t ks = (2 * kPrologueWgs + row_groups - 1) / row_groups;
+        if (ks > k / 512) ks = k / 512;
+        if (ks > 1) {
+            p.kchunk = ((k + ks - 1) / ks + 127) / 128 * 128;
+            p.ksplit = (k + p.kchunk - 1) / p.kchunk;
+        }
+    }
     p.t_off = 0;
-    p.part_off = align256(p.t_off + m * (int64_t)r * 4);
+    p.tpart_off = align256(p.t_off + m * (int64_t)r * 4);
+    p.part_off = align256(p.tpart_off + (p.ksplit > 1 ? p.ksplit * m * (int64_t)r * 4 : 0));
     p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * m * n * 4) : 0);
     return p;
 }
@@ -75,6 +92,7 @@ struct Gemm {
     Plan p;
     __device__ uint16_t *t16() const { return reinterpret_cast<uint16_t *>(static_cast<char *>(a.workspace) + p.t_off); }
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
+    __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
 };
 
 // The LoRA product rides in the MFMA accumulation as t * lora_scale / s_t,
@@ -108,6 +126,22 @@ __device__ __forceinline__ float lora_term(const GemmArgs &a, const float *t32, 
 // LoRA A matrix is re-read per workgroup from L2.  Output, with
 // u = t * lora_scale / s_t:
 //   t16[m * 2r + j] = bf16(u), t16[m * 2r + r + j] = bf16(u - bf16(u))
+// t[m, j] (FP32) into the region the main kernel reads: the BF16 hi/lo halves
+// of t * lora_scale / s_t, or lora_scale * t in FP32 when that factor does
+// not fold (fold and mul as lora_fold_ok and lora_scale / s_t give them)
+__device__ __forceinline__ void store_t(const Gemm &g, int64_t m, int j, float t, bool fold, float mul) {
+    const GemmArgs &a = g.a;
+    uint16_t *t16 = g.t16();
+    if (!fold) {
+        reinterpret_cast<float *>(t16)[m * a.r + j] = t * a.lora_scale;
+        return;
+    }
+    const float u = t * mul;
+    const uint16_t hi = f32_to_bf16_bits(u);
+    t16[m * 2 * a.r + j] = hi;
+    t16[m * 2 * a.r + a.r + j] = f32_to_bf16_bits(u - __uint_as_float((uint32_t)hi << 16));
+}
+
 template <int JT>
 __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
     constexpr int U = JT <= 4 ? 4 : 2;  // 32-column steps in flight per wave
@@ -126,12 +160,15 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
     f32x4_t acc[JT];
 #pragma unroll
     for (int j = 0; j < JT; ++j) acc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t k0 = 32 * wave; k0 < a.k; k0 += 128 * U) {
+    // this workgroup's K range (all of K unless the plan splits it)
+    const int64_t kbeg = (int64_t)blockIdx.y * g.p.kchunk;
+    const int64_t kend = kbeg + g.p.kchunk < a.k ? kbeg + g.p.kchunk : a.k;
+    for (int64_t k0 = kbeg + 32 * wave; k0 < kend; k0 += 128 * U) {
         uint4 xv[U], av[U][JT];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t kk = k0 + 128 * u + 8 * lq;
-            const bool in = kk < a.k;  // k % 16 == 0: an 8-element piece is inside or outside
+            const bool in = kk < kend;  // k % 16 == 0, kchunk % 128 == 0: a piece is inside or outside
             const int64_t kc = in ? kk : 0;
             xv[u] = *reinterpret_cast<const uint4 *>(xr + kc);
 #pragma unroll
@@ -161,7 +198,8 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
     if (wave != 0) return;
     const float mul = a.lora_scale / *a.tensor_scale;
     const bool fold = lora_fold_ok(a.lora_scale, *a.tensor_scale);  // (uniform)
-    uint16_t *t16 = g.t16();
+    const bool split = g.p.ksplit > 1;                               // (uniform)
+    float *tp = g.tpart() + (int64_t)blockIdx.y * a.m * a.r;        // this K range's partial t
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
         const f32x4_t t = ((red[0][j][lane] + red[1][j][lane]) + red[2][j][lane]) + red[3][j][lane];
@@ -170,16 +208,24 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
         for (int v = 0; v < 4; ++v) {
             const int64_t m = m0 + 4 * lq + v;
             if (m >= a.m || jr >= a.r) continue;
-            if (!fold) {  // lora_scale * t in FP32, for the epilogue
-                reinterpret_cast<float *>(t16)[m * a.r + jr] = t[v] * a.lora_scale;
-                continue;
-            }
-            const float u = t[v] * mul;
-            const uint16_t hi = f32_to_bf16_bits(u);
-            t16[m * 2 * a.r + jr] = hi;
-            t16[m * 2 * a.r + a.r + jr] = f32_to_bf16_bits(u - __uint_as_float((uint32_t)hi << 16));
+            if (split)
+                tp[m * a.r + jr] = t[v];
+            else
+                store_t(g, m, jr, t[v], fold, mul);
         }
     }
+}
+
+// K split prologue: t[m, j] = the ranges' partials added in range order
+__global__ __launch_bounds__(kThreads) void t_reduce_kernel(Gemm g) {
+    const GemmArgs &a = g.a;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= a.m * a.r) return;
+    const float *tp = g.tpart();
+    float t = 0.0f;
+    for (int64_t s = 0; s < g.p.ksplit; ++s) t += tp[s * a.m * a.r + i];
+    store_t(g, i / a.r, (int)(i % a.r), t, lora_fold_ok(a.lora_scale, *a.tensor_scale),
+            a.lora_scale / *a.tensor_scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,7 +467,12 @@ int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *
                  (long long)k, r, what, (long long)a, (long long)b);
         return 1;
     };
-    if (p.t_off + m * (int64_t)r * 4 > p.part_off) return fail("t region", p.t_off + m * (int64_t)r * 4, p.part_off);
+    if (p.t_off + m * (int64_t)r * 4 > p.tpart_off) return fail("t region", p.t_off + m * (int64_t)r * 4, p.tpart_off);
+    const int64_t tpart_end = p.tpart_off + (p.ksplit > 1 ? p.ksplit * m * (int64_t)r * 4 : 0);
+    if (tpart_end > p.part_off) return fail("partial t region", tpart_end, p.part_off);
+    if (p.ksplit > 1 && ((p.kchunk % 128) != 0 || (p.ksplit - 1) * p.kchunk >= k))
+        return fail("prologue K ranges", (p.ksplit - 1) * p.kchunk, k - 1);
+    if (p.ksplit > 0xFFFF) return fail("prologue grid", p.ksplit, 0xFFFF);
     const int64_t part_end = p.part_off + (p.splits > 1 ? p.splits * m * n * 4 : 0);
     if (part_end > size) return fail("partial outputs", part_end, size);
     if (p.splits > kMaxSplits) return fail("splits", p.splits, kMaxSplits);
@@ -451,7 +502,7 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
     if (a.m <= kDecodeMaxM) return launch_decode(a, stream);
     const Gemm g{a, make_plan(a.m, a.n, a.k, a.r)};
     if (a.r > 0) {
-        const dim3 pgrid((unsigned)((a.m + 15) / 16));
+        const dim3 pgrid((unsigned)((a.m + 15) / 16), (unsigned)g.p.ksplit);
         const int jt = (a.r + 15) / 16;
         if (jt <= 1)
             hipLaunchKernelGGL(prologue_kernel<1>, pgrid, dim3(kThreads), 0, stream, g);
@@ -463,6 +514,12 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
             hipLaunchKernelGGL(prologue_kernel<8>, pgrid, dim3(kThreads), 0, stream, g);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (g.p.ksplit > 1) {
+            hipLaunchKernelGGL(t_reduce_kernel, dim3((unsigned)((a.m * a.r + kThreads - 1) / kThreads)), dim3(kThreads),
+                               0, stream, g);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     const int64_t grid = g.p.tiles * g.p.splits;
     if (grid > 0x7FFFFFFF || a.m * a.n > 0x7FFFFFFFll * kThreads) return hipErrorInvalidConfiguration;
