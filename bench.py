@@ -241,6 +241,18 @@ class DecodeLayer:
         return sum(self.bytes_m(m) for m in self.ms)
 
 
+def warm_up(run, min_s=0.3):
+    """Repeat run() until at least min_s seconds of it have run, so a leg's
+    timed region does not start on clocks still rising from idle (the first
+    leg of a process measured up to 10% low otherwise)."""
+    t0 = time.perf_counter()
+    while True:
+        run()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= min_s:
+            return
+
+
 def time_graph(fn_steps, steps, warmup):
     """Capture `steps` calls of fn (and `warmup` separately) as HIP graphs;
     returns ms per step and the graphs."""
@@ -487,8 +499,7 @@ def prefill_leg(dev, reps):
             for nm, (p, r) in projs.items():
                 q.w4a16_lora_gemm(xk[p.wq.shape[1]], p.wq, p.a, p.b, ALPHA / RANK, out=ys[nm], workspace=ws)
 
-        run()
-        torch.cuda.synchronize()
+        warm_up(run)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -527,8 +538,7 @@ def quantizer_leg(dev, reps):
             q.nvfp4_quantize(ws_in[name], out=outs[name], workspace=ws, check_finite=False)
 
     def timed(fn):
-        fn()
-        torch.cuda.synchronize()
+        warm_up(fn)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
@@ -721,8 +731,7 @@ def backward_leg(dev, reps, m=2048):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
-    g.replay()
-    torch.cuda.synchronize()
+    warm_up(g.replay)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -743,8 +752,7 @@ def _graph_ms(run, reps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
-    g.replay()
-    torch.cuda.synchronize()
+    warm_up(g.replay)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):

@@ -41,7 +41,13 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kPfWaves = QERL_PF_WAVES;  // waves of a prefill workgroup, 64 weight rows each
 constexpr int PBM = 128, PBN = 64 * kPfWaves;  // output tile: rows of x x weight rows
-constexpr int64_t kSplitTiles = 256;  // below this many tiles (fewer than CUs) K is split
+// below this many tiles K is split, toward kSplitTarget workgroups (three per
+// CU, two resident): a grid of 256-511 tiles leaves a quarter to half of the
+// two-per-CU slots idle, which costs more than the split's FP32 partials (32B
+// layer at M = 2048: q, o and down have 320 tiles; 750 -> 820 TFLOP/s over
+// the layer, M = 8192 and the M = 128 / 256 steps unchanged)
+constexpr int64_t kSplitTiles = 512;
+constexpr int64_t kSplitTarget = 768;
 constexpr int64_t kPrologueWgs = 128;  // below this many prologue workgroups its K is split
 constexpr int64_t kMaxSplits = 16;
 
@@ -59,7 +65,7 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     const int64_t blocks = k / 128;
     p.splits = 1;
     if (p.tiles < kSplitTiles && blocks >= 8) {
-        int64_t s = ((8 / kPfWaves) * 256 + p.tiles - 1) / p.tiles;  // toward 8 waves per CU
+        int64_t s = (kSplitTarget + p.tiles - 1) / p.tiles;
         if (s > blocks / 4) s = blocks / 4;              // at least four blocks per split
         if (s > kMaxSplits) s = kMaxSplits;
         if (s > 1) p.splits = s;
