@@ -242,15 +242,18 @@ class DecodeLayer:
 
 
 def warm_up(run, min_s=0.3):
-    """Repeat run() until at least min_s seconds of it have run, so a leg's
-    timed region does not start on clocks still rising from idle (the first
-    leg of a process measured up to 10% low otherwise)."""
+    """Keep the GPU busy with run() for about min_s seconds before a leg's
+    timed region, so it does not start on clocks still rising from idle (the
+    first leg of a process measured up to 10% low otherwise): one timed run,
+    then enough runs enqueued back to back, one synchronization at the end
+    (a synchronization after every short run leaves the GPU mostly idle)."""
     t0 = time.perf_counter()
-    while True:
+    run()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-5)
+    for _ in range(min(int(min_s / one), 20000)):
         run()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t0 >= min_s:
-            return
+    torch.cuda.synchronize()
 
 
 def time_graph(fn_steps, steps, warmup):
@@ -679,7 +682,9 @@ def aqn_leg(dev):
         x = synth.activation_bf16(m, h, synth.seed_for(1006, "x", m), 0.005, device=dev)
         w = synth.norm_weight_f32(h, synth.seed_for(1006, "w", h), device=dev)
         y = torch.empty((m, h), dtype=torch.bfloat16, device=dev)
-        t = _graph_ms(lambda: q.aqn_rmsnorm(x, w, EPS, sigma, SEED, RL_STEP, 0, want_f32=False, y_bf16=y), 50)
+        calls = 20  # per graph, so the per-call time is not one graph launch
+        t = _graph_ms(lambda: [q.aqn_rmsnorm(x, w, EPS, sigma, SEED, RL_STEP, 0, want_f32=False, y_bf16=y)
+                               for _ in range(calls)], 10) / calls
         b = norm_bytes(m, h)
         out[f"M={m},H={h}"] = {"us": t * 1e3, "bytes": b, "GB/s": b / (t * 1e-3) / 1e9,
                                "frac": b / (t * 1e-3) / 1e9 / HBM_PEAK_GBS}
