@@ -757,7 +757,12 @@ def _graph_ms(run, reps):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
-    warm_up(g.replay)
+    # one warm replay, as the step's own timing does: the call-class and
+    # per-layer figures are compared with that step and with the rocprofv3
+    # traces of the same replays (0.3 s of back-to-back decode replays first
+    # made them about 15% slower)
+    g.replay()
+    torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
