@@ -786,7 +786,16 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
 #pragma unroll
     for (int u = 0; u < kFinS; ++u)
         if (s0 + u < s1) acc = acc + pv[u];
-    for (int64_t sl = s0 + kFinS; sl < s1; ++sl) acc = acc + *reinterpret_cast<const f32x4_t *>(part_base + sl * sstride);
+    constexpr int kFinS2 = 4;  // more slices: this many loads at a time, same order
+    for (int64_t sb = s0 + kFinS; sb < s1; sb += kFinS2) {
+        f32x4_t pw[kFinS2];
+#pragma unroll
+        for (int u = 0; u < kFinS2; ++u)
+            pw[u] = *reinterpret_cast<const f32x4_t *>(part_base + (sb + u < s1 ? sb + u : s1 - 1) * sstride);
+#pragma unroll
+        for (int u = 0; u < kFinS2; ++u)
+            if (sb + u < s1) acc = acc + pw[u];
+    }
     f32x4_t lora = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int q0 = quad_l * 4;  // this output's first row in ts
     auto dot8 = [&](const uint4 &b8, int j) {
