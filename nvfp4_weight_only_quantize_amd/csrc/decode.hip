@@ -22,8 +22,8 @@
 //    y = bf16(inv_rms * (s_t * acc + lora_scale * t B^T)).
 // A call with a single slice, no LoRA and no norm writes y from the units.
 //
-// m <= 16, stream_kernel.  Units are 64 weight rows x one K slice; each of the
-// 4 waves owns 16 rows.  The unit's x slice is staged into LDS (bf16(x *
+// m <= 16, stream_kernel.  Units are 128 weight rows x one K slice; each of
+// the 8 waves owns 16 rows.  The unit's x slice is staged into LDS (bf16(x *
 // norm_w) with the norm); the weights stream in the span layout (below), one
 // group of loads in flight per wave, and latency is covered by several
 // resident units per CU (registers are capped for that).
@@ -45,6 +45,14 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreadsD = kWaves * 64;
+#ifndef QERL_STREAM_UNIT_WAVES
+#define QERL_STREAM_UNIT_WAVES 8
+#endif
+// waves of a stream_kernel unit (16 weight rows each): eight share one staged
+// x slice, half the x bytes per weight byte of four (32B layer at m = 16: 137
+// -> 128 us per decode pass); sixteen were slower
+constexpr int kSW = QERL_STREAM_UNIT_WAVES;
+constexpr int kThreadsS = 64 * kSW;
 // waves of a 16 < m unit (64 weight rows each).  Eight waves sharing one x
 // tile, or weights fetched two blocks ahead, were measured slower: the unit is
 // bound by its CU's vector memory path, not by latency.
@@ -56,7 +64,7 @@ constexpr int64_t kGroupK = 4 * kChunkK;  // m <= 16: K elements of one span gro
 #define QERL_XSLICE_KB 36
 #endif
 #ifndef QERL_UNITS_PER_CU
-#define QERL_UNITS_PER_CU 4
+#define QERL_UNITS_PER_CU 3
 #endif
 #ifndef QERL_STREAM_WAVES_PER_SIMD
 #define QERL_STREAM_WAVES_PER_SIMD 6
@@ -123,7 +131,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
     p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
-    p.rows_per_unit = 16 * kWaves * (int64_t)p.nw;
+    p.rows_per_unit = p.mt == 1 ? 16 * kSW : 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
     if (p.row_blocks > kMaxRowBlocks) p.row_blocks = 0;  // one counter per row block: rejected at launch
     p.chunks = (k + kChunkK - 1) / kChunkK;
@@ -447,18 +455,18 @@ __device__ __forceinline__ void batched_copy_2d(int rows, int per_row, Src src, 
 // of `pitch` elements; columns at or past k are zero.  NORM: each element
 // enters as bf16(x * norm_w[column]) (the row's 1 / rms is applied in the
 // epilogue).
-template <bool NORM>
+template <bool NORM, int NT = kThreadsD>
 __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, int64_t k0, int64_t width) {
     // 8-element pieces i = row * per_row + piece, kStage per thread in flight
     // (every load of a round issued before its stores)
     constexpr int kStage = 4;
     const int per_row = (int)(width / 8), total = (int)a.m * per_row;
-    for (int base = threadIdx.x; base < total; base += kStage * kThreadsD) {
+    for (int base = threadIdx.x; base < total; base += kStage * NT) {
         uint4 v[kStage];
         float4 w0[kStage], w1[kStage];
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
-            const int i = base + u * kThreadsD;
+            const int i = base + u * NT;
             const int row = i / per_row, pc = i - row * per_row;
             const int64_t col = k0 + 8 * pc;
             const bool in = i < total && col < a.k;  // k % 16 == 0: a piece is inside or outside
@@ -470,7 +478,7 @@ __device__ void stage_x_slice(const GemmArgs &a, uint16_t *xs, int64_t pitch, in
         }
 #pragma unroll
         for (int u = 0; u < kStage; ++u) {
-            const int i = base + u * kThreadsD;
+            const int i = base + u * NT;
             if (i >= total) break;
             const int row = i / per_row, pc = i - row * per_row;
             uint4 o = v[u];
@@ -586,7 +594,7 @@ template <int NS, bool K32, bool DIRECT, bool LORA, bool NORM>
 // Registers are capped so that QERL_STREAM_WAVES_PER_SIMD waves fit each SIMD
 // (the main loop needs about 60; the producer and epilogue paths would take
 // more and are allowed to spill a little).
-__global__ __launch_bounds__(kThreadsD) __attribute__((amdgpu_waves_per_eu(QERL_STREAM_WAVES_PER_SIMD, 8)))
+__global__ __launch_bounds__(kThreadsS) __attribute__((amdgpu_waves_per_eu(QERL_STREAM_WAVES_PER_SIMD, 8)))
 void stream_kernel(DecodeSetN<NS> ds) {
     constexpr int MT = 1, NW = 1;  // one 16-row m-tile, one 16-row weight group per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -626,7 +634,7 @@ void stream_kernel(DecodeSetN<NS> ds) {
     // ---- the first group's loads travel while the x slice is staged ----
     SpanGroup cur;
     if (ng > 0) cur = load_span_group(prow, srow, c_begin / 4, lq);
-    stage_x_slice<NORM>(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
+    stage_x_slice<NORM, kThreadsS>(a, xs, p.xpitch, c_begin * kChunkK, (c_end - c_begin) * kChunkK);
     __syncthreads();
     // One group in flight per wave: latency is covered by the other resident
     // units and waves (registers kept low for that), not by a deeper ring.
@@ -966,7 +974,7 @@ hipError_t launch_stream(const DecodeSetN<NS> &ds, int64_t lds_bytes, hipStream_
         const int64_t b = ds.seg[i].p.producers + ds.seg[i].p.units;
         blocks = b > blocks ? b : blocks;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ds.nseg), dim3(kThreadsD), (size_t)lds_bytes, stream, ds);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)ds.nseg), dim3(kThreadsS), (size_t)lds_bytes, stream, ds);
     const hipError_t e = hipGetLastError();
     if (DIRECT || e != hipSuccess) return e;
     return launch_finish<NS, 1, 1, NORM>(ds, stream);
@@ -1086,7 +1094,7 @@ int decode_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int 
         const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;  // bytes of one unit's FP32 tile
         // f32x4 slots a unit writes: stream_kernel wave * 64 + lane; an MFMA
         // unit ((layout wave MT + i) NW + n-tile) 64 + lane
-        const int64_t slots = p.mt == 1 ? (int64_t)kWaves * 64 : (int64_t)4 * p.mt * p.nw * 64;
+        const int64_t slots = p.mt == 1 ? (int64_t)kSW * 64 : (int64_t)4 * p.mt * p.nw * 64;
         if (slots * 16 > tile) return fail("unit tile slots", j, slots * 16, tile);
         if (p.units != p.row_blocks * p.slices) return fail("units", j, p.units, p.row_blocks * p.slices);
         const int64_t units_end = p.part_off + p.units * tile;  // written by the units, read by finish_kernel
