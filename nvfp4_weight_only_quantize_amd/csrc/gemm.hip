@@ -18,7 +18,9 @@
 //   prefill_kernel   128 x 256 output tiles over the K loops of mfma_tile.h
 //                    (x by LDS DMA, weights decoded to exact BF16 in
 //                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
-//                    s_t applied once.  Grids of few tiles split K; then
+//                    s_t applied once; with K a multiple of 256 the scales
+//                    arrive by LDS DMA, four blocks at a time.  Grids of few
+//                    tiles split K (even block counts per split); then
 //   reduce_kernel    sums the FP32 partial outputs in split order.
 #include <stdio.h>
 
@@ -71,6 +73,7 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
         if (s > 1) p.splits = s;
     }
     p.bps = (blocks + p.splits - 1) / p.splits;
+    if (p.splits > 1 && blocks % 2 == 0) p.bps += p.bps & 1;  // even split starts: aligned scale chunks
     if (p.splits > 1) p.splits = (blocks + p.bps - 1) / p.bps;  // no empty split
     // the prologue: one workgroup per 16 rows of x; with fewer than
     // kPrologueWgs of them, K is split too (ranges of at least 512 columns,
@@ -250,6 +253,10 @@ constexpr int64_t kGroupM = QERL_GROUP_M;  // row blocks per group of the tile o
 
 __shared__ __attribute__((aligned(1024))) uint8_t g_xtile0[kXTileBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_xtile1[kXTileBytes];
+// the workgroup's scale bytes of four blocks (64 kPfWaves rows x 32 bytes),
+// two chunks (the main K loop's scales by DMA)
+__shared__ __attribute__((aligned(1024))) uint8_t g_sctile0[64 * kPfWaves * 32];
+__shared__ __attribute__((aligned(1024))) uint8_t g_sctile1[64 * kPfWaves * 32];
 
 // 8 elements of the extended K range [0, k + 2r) for x row m at column kk:
 // x itself, then the BF16 hi/lo halves of t * lora_scale / s_t; zero past
@@ -323,8 +330,13 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
     const int64_t blocks = a.ldx <= kTileMaxLdx ? a.k / kTileK : 0;
     const int64_t kb0 = !SPLIT ? 0 : (split * p.bps < blocks ? split * p.bps : blocks);
     const int64_t kb1 = last ? blocks : (kb0 + p.bps < blocks ? kb0 + p.bps : blocks);
-    mfma_kloop<8, kPfWaves>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1), a.scales + n0 * (a.k >> 4),
-                  a.n - n0, a.k, kb0, kb1, g_xtile0, g_xtile1, acc);
+    if ((a.k & 255) == 0 && (kb0 & 1) == 0)  // (uniform) 16-byte aligned scale chunks: scales by DMA
+        mfma_kloop<8, kPfWaves, 1, false, true>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1),
+                                                a.scales + n0 * (a.k >> 4), a.n - n0, a.k, kb0, kb1, g_xtile0,
+                                                g_xtile1, acc, nullptr, 0, g_sctile0, g_sctile1);
+    else
+        mfma_kloop<8, kPfWaves>(a.x + m0 * a.ldx, a.m - m0, a.ldx, a.packed + n0 * (a.k >> 1),
+                                a.scales + n0 * (a.k >> 4), a.n - n0, a.k, kb0, kb1, g_xtile0, g_xtile1, acc);
     // the last split: the rest of K (and all of it for very wide x rows), then
     // the LoRA columns
     const int64_t nw = n0 + wave * 64 + lr;

@@ -81,12 +81,21 @@ __device__ __forceinline__ void mfma_step(const uint8_t *pa, int pitch_bytes, co
 //     rows at sc_tile + r * sc_pitch, the 8 bytes of block b0 + i at 8 i),
 //     staged and made visible by the caller, instead of 2-byte global loads
 // Needs ldx <= kTileMaxLdx and uniform arguments; ends with a barrier.
-template <int MTW, int NWV = 4, int WD = 1, bool SCL = false>
+//   SCD: the scales travel by DMA in chunks of four blocks (32 contiguous
+//     bytes per weight row) into the LDS tiles sd0, sd1 (64 NWV rows of 32
+//     bytes each), one chunk ahead, and each block reads its pairs from
+//     there: one 16-byte DMA lane per half row instead of a 2-byte load per
+//     lane and block (16 cache lines an instruction).  Needs k % 256 == 0 and
+//     b0 even (16-byte aligned sources); the range check of the buffer
+//     (offset + soffset against its size) zero-fills what a chunk reads past
+//     the last row.
+template <int MTW, int NWV = 4, int WD = 1, bool SCL = false, bool SCD = false>
 __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_rows, int64_t ldx,
                                            const uint8_t *w_packed, const uint8_t *w_scales, int64_t w_rows,
                                            int64_t k, int64_t b0, int64_t b1, uint8_t *t0, uint8_t *t1,
                                            f32x4_t (&acc)[MTW][4], const uint8_t *sc_tile = nullptr,
-                                           int sc_pitch = 0) {
+                                           int sc_pitch = 0, uint8_t *sd0 = nullptr, uint8_t *sd1 = nullptr) {
+    static_assert(!SCD || (WD == 1 && !SCL), "scales by DMA: weights one block ahead, no LDS scale tile");
     static_assert(MTW == 2 || MTW == 4 || MTW == 8, "x tile of 32, 64 or 128 rows");
     static_assert(NWV == 4 || NWV == 8, "four or eight waves");
     static_assert(4 * MTW % NWV == 0, "whole DMA instructions per wave");
@@ -159,7 +168,8 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
         w.q1 = ldq16(1, k0 >> 1);
         w.q2 = ldq16(2, k0 >> 1);
         w.q3 = ldq16(3, k0 >> 1);
-        if (SCL) {
+        if (SCD) {  // the block reads its scale pairs from the DMA'd chunk
+        } else if (SCL) {
             const uint8_t *sp = sc_tile + wrow * sc_pitch + (int)(s - b0) * 8 + 2 * lq;
             w.c0 = *reinterpret_cast<const uint16_t *>(sp);
             w.c1 = *reinterpret_cast<const uint16_t *>(sp + 16 * sc_pitch);
@@ -176,8 +186,31 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
     // into nxt and the weights of block s+WD into wl.  Every block issues its
     // weight loads (clamped past the end), so the wait at its end always
     // leaves exactly the 8 loads of block s+WD in flight when WD == 2.
-    auto block = [&](const uint8_t *cur, uint8_t *nxt, const WSet &wc, WSet &wl, int64_t s) {
+    // SCD chunk DMA, instruction i of wave w: lane l copies half l % 2 of the
+    // 32 bytes of row 64w + 32i + l / 2 (LDS rows of 32 bytes, 1 KB an
+    // instruction)
+    int sdoff = 0;
+    if (SCD) sdoff = (int)(((int64_t)wave * 64 + (lane >> 1)) * ks + 16 * (lane & 1));
+    auto dma_sc = [&](uint8_t *dst, int64_t s) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + 2048 * wave + 1024 * i), 16, sdoff,
+                                                     (int)(8 * s + 32 * i * ks), 0, 0);
+    };
+    // SCD: sdc holds the chunk of block s; when cn, s ends its chunk and the
+    // next chunk goes to sdn (both uniform)
+    auto block = [&](const uint8_t *cur, uint8_t *nxt, const WSet &wc, WSet &wl, int64_t s,
+                     const uint8_t *sdc = nullptr, uint8_t *sdn = nullptr, bool cn = false) {
+        uint16_t c0 = wc.c0, c1 = wc.c1, c2 = wc.c2, c3 = wc.c3;
+        if (SCD && s < b1) {  // uniform: the scale pairs, before any load is issued
+            const uint8_t *sp = sdc + wrow * 32 + (int)((s - b0) & 3) * 8 + 2 * lq;
+            c0 = *reinterpret_cast<const uint16_t *>(sp);
+            c1 = *reinterpret_cast<const uint16_t *>(sp + 16 * 32);
+            c2 = *reinterpret_cast<const uint16_t *>(sp + 32 * 32);
+            c3 = *reinterpret_cast<const uint16_t *>(sp + 48 * 32);
+        }
         if (s + 1 < b1) dma_x(nxt, s + 1);  // uniform
+        if (SCD && cn && s + 1 < b1) dma_sc(sdn, s + 1);
         load_w(wl, s + WD < b1 ? s + WD : b1 - 1);
         if (s < b1) {  // uniform
             // step t's MFMAs are issued interleaved with the decode of step
@@ -185,10 +218,10 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
             // or after a run of MFMAs would leave one of the two pipes idle
             auto decode_step = [&](int t, bf16x8_t &d0, bf16x8_t &d1, bf16x8_t &d2, bf16x8_t &d3) {
                 const bool hi = t >= 2;  // scale byte 1 covers the last 16 of the lane's 32 columns
-                const float f0 = hi ? QERL_E4M3_F32(wc.c0, 1) : QERL_E4M3_F32(wc.c0, 0);
-                const float f1 = hi ? QERL_E4M3_F32(wc.c1, 1) : QERL_E4M3_F32(wc.c1, 0);
-                const float f2 = hi ? QERL_E4M3_F32(wc.c2, 1) : QERL_E4M3_F32(wc.c2, 0);
-                const float f3 = hi ? QERL_E4M3_F32(wc.c3, 1) : QERL_E4M3_F32(wc.c3, 0);
+                const float f0 = hi ? QERL_E4M3_F32(c0, 1) : QERL_E4M3_F32(c0, 0);
+                const float f1 = hi ? QERL_E4M3_F32(c1, 1) : QERL_E4M3_F32(c1, 0);
+                const float f2 = hi ? QERL_E4M3_F32(c2, 1) : QERL_E4M3_F32(c2, 0);
+                const float f3 = hi ? QERL_E4M3_F32(c3, 1) : QERL_E4M3_F32(c3, 0);
                 d0 = dequant8_p(t == 0 ? wc.q0.x : t == 1 ? wc.q0.y : t == 2 ? wc.q0.z : wc.q0.w, f0);
                 d1 = dequant8_p(t == 0 ? wc.q1.x : t == 1 ? wc.q1.y : t == 2 ? wc.q1.z : wc.q1.w, f1);
                 d2 = dequant8_p(t == 0 ? wc.q2.x : t == 1 ? wc.q2.y : t == 2 ? wc.q2.z : wc.q2.w, f2);
@@ -227,11 +260,23 @@ __device__ __forceinline__ void mfma_kloop(const uint16_t *x_tile, int64_t x_row
     };
     WSet w0, w1, w2;
     dma_x(t0, b0);
+    if (SCD) dma_sc(sd0, b0);
     load_w(w0, b0);
     if (WD == 2) load_w(w1, b0 + 1 < b1 ? b0 + 1 : b1 - 1);
     wait_vmcnt<0>();
     __syncthreads();
-    if (WD == 1) {
+    if (SCD) {  // chunks of four blocks alternate between sd0 and sd1
+        for (int64_t s = b0; s < b1; s += 8) {
+            block(t0, t1, w0, w1, s, sd0, sd1, false);
+            block(t1, t0, w1, w0, s + 1, sd0, sd1, false);
+            block(t0, t1, w0, w1, s + 2, sd0, sd1, false);
+            block(t1, t0, w1, w0, s + 3, sd0, sd1, true);
+            block(t0, t1, w0, w1, s + 4, sd1, sd0, false);
+            block(t1, t0, w1, w0, s + 5, sd1, sd0, false);
+            block(t0, t1, w0, w1, s + 6, sd1, sd0, false);
+            block(t1, t0, w1, w0, s + 7, sd1, sd0, true);
+        }
+    } else if (WD == 1) {
         for (int64_t s = b0; s < b1; s += 2) {
             block(t0, t1, w0, w1, s);
             block(t1, t0, w1, w0, s + 1);

@@ -249,6 +249,24 @@ def test_shared_workspace_sequence_is_deterministic():
         assert_gemm_close(bf16_to_f64(fresh[i]), layers[i].ref(synth.bf16_bits(xs[i].cpu())), f"case {cases[i]}")
 
 
+@pytest.mark.parametrize("m,n,k,r", [
+    (300, 1000, 1280, 16),  # 10 blocks, two splits: 5 per split rounds to 6 (6 + 4)
+    (200, 520, 3328, 32),   # 26 blocks in splits of 6, 6, 6, 6, 2 (partial chunks)
+    (300, 300, 768, 8),     # one split of 6 blocks (a chunk and a half), ragged n and m
+    (129, 264, 384, 4),     # K % 256 == 128: scales by plain loads; 8 rows in the last n tile
+    (70, 1000, 2048, 24),   # 16 blocks in 4 splits of 4; 232 rows in the last n tile
+])
+def test_prefill_scale_chunks(m, n, k, r):
+    """The prefill K loop takes the scales by LDS DMA, four blocks at a time,
+    when K is a multiple of 256 and the split starts at an even block: partial
+    chunks at the end of a split, split sizes rounded up to even, weight tiles
+    with rows past n, and the plain-load path for the other K."""
+    L = Layer(n, k, r, seed=1300 + m + n + k)
+    x = _x(m, k, seed=1301 + m + k)
+    y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
+    assert_gemm_close(y, L.ref(x), f"m={m} n={n} k={k} r={r}")
+
+
 @pytest.mark.parametrize("s_t", [1e-39, 1e-30, 1e-18])
 @pytest.mark.parametrize("m", [65, 300])
 def test_tiny_tensor_scale(m, s_t):
