@@ -20,8 +20,9 @@
 //                    registers, BF16 MFMA 16x16x32 with FP32 accumulation);
 //                    s_t applied once; with K a multiple of 256 the scales
 //                    arrive by LDS DMA, four blocks at a time.  Grids of few
-//                    tiles split K (even block counts per split); then
-//   reduce_kernel    sums the FP32 partial outputs in split order.
+//                    tiles split K (even block counts per split): every
+//                    split stores its FP32 tile and the last to arrive at
+//                    the tile sums them in split order and writes y.
 #include <stdio.h>
 
 #include "device_common.h"
@@ -43,20 +44,25 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kPfWaves = QERL_PF_WAVES;  // waves of a prefill workgroup, 64 weight rows each
 constexpr int PBM = 128, PBN = 64 * kPfWaves;  // output tile: rows of x x weight rows
-// below this many tiles K is split, toward kSplitTarget workgroups (three per
-// CU, two resident): a grid of 256-511 tiles leaves a quarter to half of the
-// two-per-CU slots idle, which costs more than the split's FP32 partials (32B
-// layer at M = 2048: q, o and down have 320 tiles; 750 -> 820 TFLOP/s over
-// the layer, M = 8192 and the M = 128 / 256 steps unchanged)
+constexpr int64_t kPartTileBytes = (int64_t)PBM * PBN * 4;  // one split's FP32 tile
+// below this many tiles (two resident workgroups per CU) K may be split: the
+// split count is the one with the least modeled time, rounds of resident
+// workgroups x (blocks per split + kSplitOverhead) plus the reduce's FP32
+// traffic.  A grid of 256-511 tiles leaves a quarter to half of the slots idle
+// (32B layer at M = 2048: q, o and down have 320 tiles and take three splits,
+// two rounds); a count that spills a few workgroups into another round costs
+// a whole round (k and v there: 64 tiles, seven splits in one round of 448
+// workgroups rather than ten in two).
 constexpr int64_t kSplitTiles = 512;
-constexpr int64_t kSplitTarget = 768;
-constexpr int64_t kPrologueWgs = 128;  // below this many prologue workgroups its K is split
+constexpr double kSplitOverhead = 2.0;     // per workgroup, in K blocks: x tile start, epilogue
+constexpr double kReduceBytesPerBlock = 1.9e7;  // partial-tile bytes moved in the time of one K block
+constexpr int64_t kPrologueWgs = 512;  // below this many prologue workgroups its K is split
 constexpr int64_t kMaxSplits = 16;
 
 struct Plan {
     int64_t tiles, splits, bps;  // output tiles, K splits, 128-column blocks per split
     int64_t ksplit, kchunk;      // prologue: K ranges (FP32 partial t each when > 1), columns per range
-    int64_t t_off, tpart_off, part_off, bytes;
+    int64_t t_off, tpart_off, cnt_off, part_off, bytes;
 };
 
 __host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
@@ -66,15 +72,23 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     p.tiles = ((m + PBM - 1) / PBM) * ((n + PBN - 1) / PBN);
     const int64_t blocks = k / 128;
     p.splits = 1;
+    p.bps = blocks;
     if (p.tiles < kSplitTiles && blocks >= 8) {
-        int64_t s = (kSplitTarget + p.tiles - 1) / p.tiles;
-        if (s > blocks / 4) s = blocks / 4;              // at least four blocks per split
-        if (s > kMaxSplits) s = kMaxSplits;
-        if (s > 1) p.splits = s;
+        double best = 0.0;
+        for (int64_t s = 1; s <= blocks / 4 && s <= kMaxSplits; ++s) {  // at least four blocks per split
+            int64_t bps = (blocks + s - 1) / s;
+            if (s > 1 && blocks % 2 == 0) bps += bps & 1;  // even split starts: aligned scale chunks
+            const int64_t sp = (blocks + bps - 1) / bps;  // no empty split
+            const int64_t rounds = (p.tiles * sp + kSplitTiles - 1) / kSplitTiles;
+            const double t = (double)rounds * ((double)bps + kSplitOverhead) +
+                             (sp > 1 ? (double)m * (double)n * (4.0 * (double)sp + 2.0) / kReduceBytesPerBlock : 0.0);
+            if (s == 1 || t < best) {
+                best = t;
+                p.splits = sp;
+                p.bps = bps;
+            }
+        }
     }
-    p.bps = (blocks + p.splits - 1) / p.splits;
-    if (p.splits > 1 && blocks % 2 == 0) p.bps += p.bps & 1;  // even split starts: aligned scale chunks
-    if (p.splits > 1) p.splits = (blocks + p.bps - 1) / p.bps;  // no empty split
     // the prologue: one workgroup per 16 rows of x; with fewer than
     // kPrologueWgs of them, K is split too (ranges of at least 512 columns,
     // a multiple of 128) and t_reduce_kernel adds the ranges' FP32 partials
@@ -91,8 +105,9 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     }
     p.t_off = 0;
     p.tpart_off = align256(p.t_off + m * (int64_t)r * 4);
-    p.part_off = align256(p.tpart_off + (p.ksplit > 1 ? p.ksplit * m * (int64_t)r * 4 : 0));
-    p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * m * n * 4) : 0);
+    p.cnt_off = align256(p.tpart_off + (p.ksplit > 1 ? p.ksplit * m * (int64_t)r * 4 : 0));
+    p.part_off = align256(p.cnt_off + (p.splits > 1 ? p.tiles * 4 : 0));
+    p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * p.tiles * kPartTileBytes) : 0);
     return p;
 }
 
@@ -102,7 +117,20 @@ struct Gemm {
     __device__ uint16_t *t16() const { return reinterpret_cast<uint16_t *>(static_cast<char *>(a.workspace) + p.t_off); }
     __device__ float *part() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.part_off); }
     __device__ float *tpart() const { return reinterpret_cast<float *>(static_cast<char *>(a.workspace) + p.tpart_off); }
+    __device__ uint32_t *cnt() const { return reinterpret_cast<uint32_t *>(static_cast<char *>(a.workspace) + p.cnt_off); }
 };
+
+// The K splits of one output tile meet inside the launch: each stores its FP32
+// tile (lane order, 16 bytes a lane per MFMA tile) and adds one to the tile's
+// counter; the split that brings it to `splits` sums the tiles in split order
+// and writes y, and sets the counter back to zero.  No workgroup waits for
+// another.  The splits may run on different XCDs, whose L2 caches are not
+// coherent with each other, so the tiles and the counter use the SC1 cache
+// policy (the agent-scope coherent accesses that relaxed agent-scope atomics
+// compile to), and a split's stores have completed before it arrives.  The
+// counters are cleared by the launch before (the prologue, or
+// cnt_zero_kernel without LoRA), so nothing needs to be zero beforehand.
+constexpr int kSC1 = 16;  // cache-policy operand of the buffer builtins: SC1
 
 // The LoRA product rides in the MFMA accumulation as t * lora_scale / s_t,
 // which needs that factor finite and moderate; for tiny s_t (a subnormal or
@@ -157,6 +185,9 @@ __global__ __launch_bounds__(kThreads) void prologue_kernel(Gemm g) {
     const GemmArgs &a = g.a;
     __shared__ f32x4_t red[4][JT][64];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    if (g.p.splits > 1 && blockIdx.x == 0 && blockIdx.y == 0)  // the split tiles' counters
+        for (int64_t i = tid; i < g.p.tiles; i += kThreads)
+            __hip_atomic_store(g.cnt() + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int64_t m0 = (int64_t)blockIdx.x * 16;
     const int64_t row = m0 + lr < a.m ? m0 + lr : a.m - 1;  // rows past m: a repeat, not stored
     const uint16_t *xr = a.x + row * a.ldx;
@@ -346,60 +377,99 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
             [&](int row, int64_t kk) { return x_piece_ext(g, m0 + row, kk, klora, fold); },
             [&](int j, int64_t kk) { return w_frag_ext(a, nw + 16 * j, kk, klora); }, acc);
 
-    if (SPLIT) {  // FP32 partial outputs; reduce_kernel finishes
-        float *part = g.part() + split * a.m * a.n;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int64_t m = m0 + 16 * i + 4 * lq + v;
-                    const int64_t n = n0 + wave * 64 + 16 * j + lr;
-                    if (m < a.m && n < a.n) part[m * a.n + n] = acc[i][j][v];
-                }
-        return;
-    }
+    // y of MFMA tile (i, j): bf16(s_t acc), plus the LoRA term when it is not
+    // in the accumulation
     const float st_scale = *a.tensor_scale;
     const float *t32 = reinterpret_cast<const float *>(g.t16());
+    auto store_y = [&](int i, int j, const f32x4_t &v4) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t m = m0 + 16 * i + 4 * lq + v;
+            const int64_t n = n0 + wave * 64 + 16 * j + lr;
+            if (m < a.m && n < a.n) {
+                float yv = st_scale * v4[v];
+                if (!fold) yv += lora_term(a, t32, m, n);
+                a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
+            }
+        }
+    };
+    if (SPLIT) {  // meet the other splits of the tile (see kSC1)
+        // this split's tile: f32x4 of MFMA tile (i, j) of wave w at
+        // ((32 w + 4 i + j) 64 + lane) 16 bytes
+        auto tile_rsrc = [&](int64_t sp) {
+            return __builtin_amdgcn_make_buffer_rsrc(g.part() + (sp * p.tiles + tile) * (kPartTileBytes / 4), 0,
+                                                     (int)kPartTileBytes, 0x00020000);
+        };
+        const int lo = (wave * 32 * 64 + lane) * 16;
+        {
+            const __amdgpu_buffer_rsrc_t rm = tile_rsrc(split);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    i32x4_t v;
+                    __builtin_memcpy(&v, &acc[i][j], 16);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, rm, lo + (4 * i + j) * 1024, 0, kSC1);
+                }
+        }
+        // the arrival's verdict goes through the scale chunk's LDS, idle once
+        // every wave has passed the barrier below
+        volatile uint32_t *s_fin = reinterpret_cast<volatile uint32_t *>(g_sctile1);
+        wait_vmcnt<0>();  // this wave's stores have completed
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t fin = __hip_atomic_fetch_add(g.cnt() + tile, 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT) + 1 == (uint32_t)p.splits;
+            if (fin) __hip_atomic_store(g.cnt() + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_fin = fin;
+        }
+        __syncthreads();
+        if (!*s_fin) return;  // (uniform)
+        // the last split: every split's tile (its own too) summed in split
+        // order, eight MFMA tiles and four splits of loads in flight at a time
+#pragma unroll
+        for (int t0 = 0; t0 < 32; t0 += 8) {
+            f32x4_t sum[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sum[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int64_t s0 = 0; s0 < p.splits; s0 += 4) {
+                i32x4_t v[4][8];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (s0 + b < p.splits) {  // (uniform)
+                        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(s0 + b);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            v[b][t] = __builtin_amdgcn_raw_buffer_load_b128(rs, lo + (t0 + t) * 1024, 0, kSC1);
+                    }
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (s0 + b < p.splits)
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) {
+                            f32x4_t f;
+                            __builtin_memcpy(&f, &v[b][t], 16);
+                            sum[t] = sum[t] + f;
+                        }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) store_y((t0 + t) >> 2, (t0 + t) & 3, sum[t]);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int64_t m = m0 + 16 * i + 4 * lq + v;
-                const int64_t n = n0 + wave * 64 + 16 * j + lr;
-                if (m < a.m && n < a.n) {
-                    float yv = st_scale * acc[i][j][v];
-                    if (!fold) yv += lora_term(a, t32, m, n);
-                    a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
-                }
-            }
+        for (int j = 0; j < 4; ++j) store_y(i, j, acc[i][j]);
 }
 
 template __global__ void prefill_kernel<false>(Gemm);
 template __global__ void prefill_kernel<true>(Gemm);
 
-// y[m, n] = bf16(s_t * sum over splits of the partial outputs, in split order)
-__global__ __launch_bounds__(kThreads) void reduce_kernel(Gemm g) {
-    const GemmArgs &a = g.a;
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= a.m * a.n) return;
-    const int64_t m = i / a.n, n = i - m * a.n;
-    const float *part = g.part();
-    const int64_t plane = a.m * a.n;
-    float v[kMaxSplits];
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) v[s] = s < g.p.splits ? part[s * plane + i] : 0.0f;
-    float acc = 0.0f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s)
-        if (s < g.p.splits) acc += v[s];
-    float yv = *a.tensor_scale * acc;
-    if (a.r > 0 && !lora_fold_ok(a.lora_scale, *a.tensor_scale))
-        yv += lora_term(a, reinterpret_cast<const float *>(g.t16()), m, n);
-    a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
+// the split tiles' counters, for a launch without LoRA (no prologue to clear them)
+__global__ __launch_bounds__(kThreads) void cnt_zero_kernel(Gemm g) {
+    for (int64_t i = threadIdx.x; i < g.p.tiles; i += kThreads)
+        __hip_atomic_store(g.cnt() + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -475,8 +545,8 @@ hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t st
 
 // The workspace use of one projection's launch against its size query (the
 // decode plan's own check for m <= 64): the prologue's t region [m][r] four
-// bytes each (BF16 hi/lo or FP32), the split partial outputs and their
-// reduction, and the grid limits.
+// bytes each (BF16 hi/lo or FP32), the split counters and partial tiles, and
+// the grid limits.
 int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *msg, size_t len) {
     if (m <= kDecodeMaxM) return decode_plan_check(m, k, &n, &r, 1, false, msg, len);
     const Plan p = make_plan(m, n, k, r);
@@ -491,8 +561,12 @@ int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *
     if (p.ksplit > 1 && ((p.kchunk % 128) != 0 || (p.ksplit - 1) * p.kchunk >= k))
         return fail("prologue K ranges", (p.ksplit - 1) * p.kchunk, k - 1);
     if (p.ksplit > 0xFFFF) return fail("prologue grid", p.ksplit, 0xFFFF);
-    const int64_t part_end = p.part_off + (p.splits > 1 ? p.splits * m * n * 4 : 0);
-    if (part_end > size) return fail("partial outputs", part_end, size);
+    const int64_t cnt_end = p.cnt_off + (p.splits > 1 ? p.tiles * 4 : 0);
+    if (cnt_end > p.part_off) return fail("split counters", cnt_end, p.part_off);
+    const int64_t part_end = p.part_off + (p.splits > 1 ? p.splits * p.tiles * kPartTileBytes : 0);
+    if (part_end > size) return fail("partial tiles", part_end, size);
+    if (p.splits > 1 && p.splits * p.tiles * kPartTileBytes > 0x7FFFFFFF)
+        return fail("partial tiles (32-bit buffer offsets)", p.splits * p.tiles * kPartTileBytes, 0x7FFFFFFF);
     if (p.splits > kMaxSplits) return fail("splits", p.splits, kMaxSplits);
     if (p.splits > 1 && (p.splits - 1) * p.bps >= k / 128) return fail("empty split", (p.splits - 1) * p.bps, k / 128 - 1);
     if (p.tiles * p.splits > 0x7FFFFFFF) return fail("grid", p.tiles * p.splits, 0x7FFFFFFF);
@@ -540,16 +614,17 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
         }
     }
     const int64_t grid = g.p.tiles * g.p.splits;
-    if (grid > 0x7FFFFFFF || a.m * a.n > 0x7FFFFFFFll * kThreads) return hipErrorInvalidConfiguration;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     if (g.p.splits == 1) {
         hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
         return hipGetLastError();
     }
+    if (a.r == 0) {  // the prologue clears the counters; without LoRA this does
+        hipLaunchKernelGGL(cnt_zero_kernel, dim3(1), dim3(kThreads), 0, stream, g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((a.m * a.n + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       stream, g);
     return hipGetLastError();
 }
 
