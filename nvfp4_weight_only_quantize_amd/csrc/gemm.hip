@@ -37,8 +37,10 @@ constexpr int kThreads = 256;
 // ---------------------------------------------------------------------------
 // Launch plan and workspace layout
 // ---------------------------------------------------------------------------
-// The workspace holds the BF16 hi/lo t [m, 2r] and, when K is split, the
-// FP32 partial outputs [splits][m][n].
+// The workspace holds the BF16 hi/lo t [m, 2r] (with the prologue's K-range
+// partials of t when it splits K) and, when the main loop splits K, one
+// counter per output tile and the FP32 partial tiles [splits][tiles][PBM PBN]
+// in lane order.
 #ifndef QERL_PF_WAVES
 #define QERL_PF_WAVES 4
 #endif
