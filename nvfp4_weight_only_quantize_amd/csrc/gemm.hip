@@ -22,7 +22,8 @@
 //                    arrive by LDS DMA, four blocks at a time.  Grids of few
 //                    tiles split K (even block counts per split): every
 //                    split stores its FP32 tile and the last to arrive at
-//                    the tile sums them in split order and writes y.
+//                    the tile sums them in split order and writes y, or
+//   reduce_kernel    does, over the whole chip, when a tile has many splits.
 #include <stdio.h>
 
 #include "device_common.h"
@@ -58,11 +59,16 @@ constexpr int64_t kPartTileBytes = (int64_t)PBM * PBN * 4;  // one split's FP32 
 constexpr int64_t kSplitTiles = 512;
 constexpr double kSplitOverhead = 2.0;     // per workgroup, in K blocks: x tile start, epilogue
 constexpr double kReduceBytesPerBlock = 1.9e7;  // partial-tile bytes moved in the time of one K block
+// where the splits of a tile meet: inside the launch, the last split reading
+// every split's 128 KB tile alone (about kMeetUsPerSplit each), or in
+// reduce_kernel over the whole chip (a launch plus the partial tiles' traffic)
+constexpr double kMeetUsPerSplit = 2.0, kReduceLaunchUs = 4.0, kReduceBytesPerUs = 4.4e6;
 constexpr int64_t kPrologueWgs = 512;  // below this many prologue workgroups its K is split
 constexpr int64_t kMaxSplits = 16;
 
 struct Plan {
     int64_t tiles, splits, bps;  // output tiles, K splits, 128-column blocks per split
+    bool meet;                   // split K: the splits meet in the launch, else in reduce_kernel
     int64_t ksplit, kchunk;      // prologue: K ranges (FP32 partial t each when > 1), columns per range
     int64_t t_off, tpart_off, cnt_off, part_off, bytes;
 };
@@ -107,6 +113,8 @@ Plan make_plan(int64_t m, int64_t n, int64_t k, int r) {
     }
     p.t_off = 0;
     p.tpart_off = align256(p.t_off + m * (int64_t)r * 4);
+    p.meet = p.splits > 1 && (double)p.splits * kMeetUsPerSplit <
+                                 kReduceLaunchUs + (double)m * (double)n * (4.0 * (double)p.splits + 2.0) / kReduceBytesPerUs;
     p.cnt_off = align256(p.tpart_off + (p.ksplit > 1 ? p.ksplit * m * (int64_t)r * 4 : 0));
     p.part_off = align256(p.cnt_off + (p.splits > 1 ? p.tiles * 4 : 0));
     p.bytes = p.part_off + (p.splits > 1 ? align256(p.splits * p.tiles * kPartTileBytes) : 0);
@@ -395,11 +403,12 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
             }
         }
     };
-    if (SPLIT) {  // meet the other splits of the tile (see kSC1)
-        // this split's tile: f32x4 of MFMA tile (i, j) of wave w at
-        // ((32 w + 4 i + j) 64 + lane) 16 bytes
+    if (SPLIT) {  // the FP32 tile; the splits meet here (see kSC1) or in reduce_kernel
+        // split sp's tile of output tile pt (row-major over the output tiles):
+        // f32x4 of MFMA tile (i, j) of wave w at ((32 w + 4 i + j) 64 + lane) 16 bytes
+        const int64_t pt = (m0 / PBM) * tiles_n + n0 / PBN;
         auto tile_rsrc = [&](int64_t sp) {
-            return __builtin_amdgcn_make_buffer_rsrc(g.part() + (sp * p.tiles + tile) * (kPartTileBytes / 4), 0,
+            return __builtin_amdgcn_make_buffer_rsrc(g.part() + (sp * p.tiles + pt) * (kPartTileBytes / 4), 0,
                                                      (int)kPartTileBytes, 0x00020000);
         };
         const int lo = (wave * 32 * 64 + lane) * 16;
@@ -411,18 +420,22 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
                 for (int j = 0; j < 4; ++j) {
                     i32x4_t v;
                     __builtin_memcpy(&v, &acc[i][j], 16);
-                    __builtin_amdgcn_raw_buffer_store_b128(v, rm, lo + (4 * i + j) * 1024, 0, kSC1);
+                    if (p.meet)  // (uniform)
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rm, lo + (4 * i + j) * 1024, 0, kSC1);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rm, lo + (4 * i + j) * 1024, 0, 0);
                 }
         }
+        if (!p.meet) return;
         // the arrival's verdict goes through the scale chunk's LDS, idle once
         // every wave has passed the barrier below
         volatile uint32_t *s_fin = reinterpret_cast<volatile uint32_t *>(g_sctile1);
         wait_vmcnt<0>();  // this wave's stores have completed
         __syncthreads();
         if (tid == 0) {
-            const uint32_t fin = __hip_atomic_fetch_add(g.cnt() + tile, 1u, __ATOMIC_RELAXED,
+            const uint32_t fin = __hip_atomic_fetch_add(g.cnt() + pt, 1u, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT) + 1 == (uint32_t)p.splits;
-            if (fin) __hip_atomic_store(g.cnt() + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (fin) __hip_atomic_store(g.cnt() + pt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             *s_fin = fin;
         }
         __syncthreads();
@@ -467,6 +480,45 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
 
 template __global__ void prefill_kernel<false>(Gemm);
 template __global__ void prefill_kernel<true>(Gemm);
+
+// Split K without meeting in the launch: thread i sums f32x4 slot i % 8192 of
+// output tile i / 8192 over the splits in split order (the slot holds rows
+// 4 lq .. 4 lq + 3 of MFMA tile (i, j) of wave w, column lane % 16) and
+// writes those four outputs as prefill_kernel's epilogue does.
+__global__ __launch_bounds__(kThreads) void reduce_kernel(Gemm g) {
+    const GemmArgs &a = g.a;
+    const Plan &p = g.p;
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (idx >= p.tiles * 8192) return;
+    const int64_t pt = idx >> 13;
+    const int slot = (int)(idx & 8191), w = slot >> 11, ij = (slot >> 6) & 31, lane = slot & 63;
+    const int i = ij >> 2, j = ij & 3, lr = lane & 15, lq = lane >> 4;
+    const int64_t tiles_n = (a.n + PBN - 1) / PBN;
+    const int64_t m0 = (pt / tiles_n) * PBM, n0 = (pt % tiles_n) * PBN;
+    const int64_t n = n0 + w * 64 + 16 * j + lr;
+    const f32x4_t *part = reinterpret_cast<const f32x4_t *>(g.part()) + pt * (kPartTileBytes / 16) + slot;
+    f32x4_t v[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < p.splits) v[sp] = part[sp * p.tiles * (kPartTileBytes / 16)];
+    f32x4_t sum = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < p.splits) sum = sum + v[sp];
+    if (n >= a.n) return;
+    const float st = *a.tensor_scale;
+    const bool fold = a.r == 0 || lora_fold_ok(a.lora_scale, st);
+    const float *t32 = reinterpret_cast<const float *>(g.t16());
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + 16 * i + 4 * lq + e;
+        if (m < a.m) {
+            float yv = st * sum[e];
+            if (!fold) yv += lora_term(a, t32, m, n);
+            a.y[m * a.ldy + n] = f32_to_bf16_bits(yv);
+        }
+    }
+}
 
 // the split tiles' counters, for a launch without LoRA (no prologue to clear them)
 __global__ __launch_bounds__(kThreads) void cnt_zero_kernel(Gemm g) {
@@ -621,12 +673,17 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
         return hipGetLastError();
     }
-    if (a.r == 0) {  // the prologue clears the counters; without LoRA this does
+    if (g.p.meet && a.r == 0) {  // the prologue clears the counters; without LoRA this does
         hipLaunchKernelGGL(cnt_zero_kernel, dim3(1), dim3(kThreads), 0, stream, g);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)grid), dim3(64 * kPfWaves), 0, stream, g);
+    if (g.p.meet) return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((g.p.tiles * 8192 + kThreads - 1) / kThreads)), dim3(kThreads),
+                       0, stream, g);
     return hipGetLastError();
 }
 

@@ -229,11 +229,12 @@ def test_gpu_quantizer_feeds_gemm():
 def test_shared_workspace_sequence_is_deterministic():
     """One workspace, filled with garbage first, serves a mixed sequence of
     calls (decode with and without split K and LoRA, and the large-m path with
-    split K, with and without LoRA: the split tiles' counters start from
-    garbage); each output equals the one from a fresh workspace bit for bit."""
+    split K, the splits meeting in the launch with and without LoRA -- the
+    split tiles' counters start from garbage -- or in a reduce launch); each
+    output equals the one from a fresh workspace bit for bit."""
     cases = [(1, 3584, 3584, 32), (8, 512, 3584, 32), (64, 18944 // 4, 3584, 32), (33, 1000, 3600, 24),
              (1, 3584, 18944 // 2, 0), (100, 512, 1024, 16), (16, 77, 512, 8), (64, 3584, 3584, 32),
-             (200, 520, 2048, 0)]
+             (200, 520, 2048, 0), (1000, 2000, 1024, 0)]
     layers, xs = [], []
     for i, (m, n, k, r) in enumerate(cases):
         layers.append(Layer(n, k, r, seed=900 + i))
@@ -257,15 +258,17 @@ def test_shared_workspace_sequence_is_deterministic():
     (300, 300, 768, 8),     # one split of 6 blocks (a chunk and a half), ragged n and m
     (129, 264, 384, 4),     # K % 256 == 128: scales by plain loads; 8 rows in the last n tile
     (70, 1000, 2048, 24),   # 16 blocks in 4 splits of 4; 232 rows in the last n tile
-    (300, 1000, 2048, 0),   # split K without LoRA (no prologue: the counters are cleared by a launch of their own)
+    (300, 1000, 2048, 0),   # split K without LoRA, the splits summed by a reduce launch
+    (1000, 2000, 1024, 0),  # two splits meeting in the launch without LoRA (counters cleared by a launch of their own)
 ])
 def test_prefill_scale_chunks(m, n, k, r):
     """The prefill K loop takes the scales by LDS DMA, four blocks at a time,
     when K is a multiple of 256 and the split starts at an even block: partial
     chunks at the end of a split, split sizes rounded up to even, weight tiles
     with rows past n, and the plain-load path for the other K.  The splits of
-    a tile meet in the launch (the last to arrive sums them), with and without
-    LoRA."""
+    a tile meet in the launch (the last to arrive sums them: the two-split
+    cases) or in a reduce launch (the tiles with more splits), with and
+    without LoRA."""
     L = Layer(n, k, r, seed=1300 + m + n + k)
     x = _x(m, k, seed=1301 + m + k)
     y = bf16_to_f64(L.gpu(bits_to_gpu(x)))
