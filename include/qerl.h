@@ -179,7 +179,7 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
  *   workspace     device memory of at least the size query (partial sums;
  *                 no state is kept between calls, nothing needs to be zero);
  *                 calls that overlap in time must not share a workspace
- * m <= 64 takes the decode path: a launch that streams the packed weights
+ * m <= 128 takes the decode path: a launch that streams the packed weights
  * once (E2M1/E4M3 decode in registers, BF16 MFMA) and stores partial sums,
  * and a small launch that adds them in a fixed order with the LoRA term;
  * larger m takes a BF16-MFMA path on dequantized tiles with the LoRA product
@@ -205,7 +205,7 @@ qerl_status qerl_w4a16_lora_gemm(const void *x_bf16, int64_t m, int64_t k, int64
  * nothing (no hipMalloc, no allocating library routine).
  *   Returns QERL_ERR_WORKSPACE, before enqueueing anything, when
  *   qerl_w4a16_lora_gemm_workspace_size(m, n, k, r) exceeds the scratch (48
- *   MiB covers the decode path, m <= 64, at r <= 128 for weights of up to
+ *   MiB covers decode batches of m <= 64 at r <= 128 for weights of up to
  *   27648 x 5120 and 5120 x 27648, the largest projections of a 32B-class
  *   decoder layer).
  *   Every call on one device shares that device's scratch, which keeps the
@@ -249,7 +249,7 @@ size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qer
  * computes for x and segs[i] -- each with its own weight, tensor scale, LoRA
  * and output.  The operation is the layer of qerl_w4a16_lora_gemm (README
  * "Acknowledgement"; bitsofall "LoRA (Low-Rank Adaptation)"), applied to the
- * projections that read one normed input (q/k/v, gate/up).  For m <= 64 the
+ * projections that read one normed input (q/k/v, gate/up).  For m <= 128 the
  * segments share the launches (so a decode step spends two launches, not two
  * per projection, on them); the K split is chosen for all segments together, so
  * the FP32 summation order, and with it the last bit of y, can differ from

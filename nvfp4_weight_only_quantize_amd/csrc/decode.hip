@@ -1,5 +1,5 @@
 // decode.hip -- W4A16 (NVFP4 weight x BF16 activation) + LoRA for decode
-// batches, 1 <= m <= 64, on gfx950.
+// batches, 1 <= m <= 128, on gfx950.
 //
 //   y[m, n] = s_t * sum_k x[m,k] e2m1(q[n,k]) e4m3(sb[n,k/16])
 //           + lora_scale * sum_j t[m,j] B[n,j],        t = x A^T
@@ -28,7 +28,7 @@
 // group of loads in flight per wave, and latency is covered by several
 // resident units per CU (registers are capped for that).
 //
-// 16 < m <= 64, mfma_unit_kernel.  Units are (256 weight rows) x (slice of K)
+// 16 < m <= 128, mfma_unit_kernel.  Units are (256 weight rows) x (slice of K)
 // running the K loops of mfma_tile.h with all of x as the x tile.
 //
 // Several projections of one x (q/k/v, gate/up) share a launch: the segment
@@ -129,7 +129,7 @@ int64_t cu_count() {
 // and also sum the squares of x.
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slice_rows = 0, bool norm = false) {
     DecodePlan p{};
-    p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
+    p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : (m <= 64 ? 4 : 8));
     p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
     p.rows_per_unit = p.mt == 1 ? 16 * kSW : 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
@@ -859,6 +859,9 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
 // the first four waves of a producer work.
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile0[64 * kTileRowBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
+// the x tiles of eight m-tiles (65 <= m <= 128), a kernel of their own
+__shared__ __attribute__((aligned(1024))) uint8_t g_dxtile8_0[128 * kTileRowBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_dxtile8_1[128 * kTileRowBytes];
 // the unit's scale bytes (256 rows x its slice), when they fit: 2-byte
 // global loads of 16 rows each cost more of the CU's memory path than the
 // weights they scale
@@ -871,7 +874,7 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     const GemmArgs &a = d.a;
     const DecodePlan &p = d.p;
     if (bx < p.producers) {
-        lora_producer<MT>(d, bx, g_dxtile0);
+        lora_producer<MT>(d, bx, MT == 8 ? g_dxtile8_0 : g_dxtile0);
         return;
     }
     constexpr int NW = 4 * kUnitWaves / kWaves;  // n-tiles per wave of the four-wave tile layout
@@ -897,12 +900,13 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
         __syncthreads();
     }
     mfma_kloop<MT, kUnitWaves, 1, SCL>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k,
-                                       c_begin, fast_end, g_dxtile0, g_dxtile1, acc, g_dsc, (int)p.unit_sc_pitch);
+                                       c_begin, fast_end, MT == 8 ? g_dxtile8_0 : g_dxtile0,
+                                       MT == 8 ? g_dxtile8_1 : g_dxtile1, acc, g_dsc, (int)p.unit_sc_pitch);
     // the rest of the slice (the partial last chunk of K, or all of it for
     // very wide x rows)
     const int64_t nw = n0 + wave * 64 + lr;
     plain_kloop<MT, kUnitWaves>(
-        fast_end * kChunkK, c_end * kChunkK < a.k ? c_end * kChunkK : a.k, g_dxtile0,
+        fast_end * kChunkK, c_end * kChunkK < a.k ? c_end * kChunkK : a.k, MT == 8 ? g_dxtile8_0 : g_dxtile0,
         [&](int row, int64_t kk) {
             uint4 o = make_uint4(0, 0, 0, 0);
             if (row < a.m && kk < a.k) o = *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + kk);
@@ -1019,6 +1023,7 @@ hipError_t launch_checked(const DecodeSetN<NS> &ds, int64_t lds, bool lora, bool
     const Decode &d0 = ds.seg[0];
     if (d0.p.mt == 2) return launch_mfma_units<2>(ds, stream);
     if (d0.p.mt == 4) return launch_mfma_units<4>(ds, stream);
+    if (d0.p.mt == 8) return launch_mfma_units<8>(ds, stream);
     return (d0.a.k & 31) == 0 ? launch_stream<true>(ds, lds, lora, direct, stream)
                               : launch_stream<false>(ds, lds, lora, direct, stream);
 }
