@@ -885,7 +885,7 @@ def quantizer_variants_leg(dev, reps):
 
 # ---- roofline of the dominant decode kernel --------------------------------
 # A decode GEMM call is two launches: the streaming kernel (stream_kernel for
-# M <= 16, mfma_unit_kernel for 16 < M <= 128) and finish_kernel, which sums the
+# M <= 16, mfma_unit_kernel for 16 < M <= 256) and finish_kernel, which sums the
 # partial tiles and adds the LoRA term.  The unit of the roofline is one call
 # (its algorithmic bytes over its duration); the class whose calls take the
 # larger share of the step is reported, the other beside it.  Durations come

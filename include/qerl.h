@@ -179,7 +179,7 @@ size_t qerl_w4a16_lora_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int3
  *   workspace     device memory of at least the size query (partial sums;
  *                 no state is kept between calls, nothing needs to be zero);
  *                 calls that overlap in time must not share a workspace
- * m <= 128 takes the decode path: a launch that streams the packed weights
+ * m <= 256 takes the decode path: a launch that streams the packed weights
  * once (E2M1/E4M3 decode in registers, BF16 MFMA) and stores partial sums,
  * and a small launch that adds them in a fixed order with the LoRA term;
  * larger m takes a BF16-MFMA path on dequantized tiles with the LoRA product
@@ -249,7 +249,7 @@ size_t qerl_w4a16_lora_gemm_multi_workspace_size(int64_t m, int64_t k, const qer
  * computes for x and segs[i] -- each with its own weight, tensor scale, LoRA
  * and output.  The operation is the layer of qerl_w4a16_lora_gemm (README
  * "Acknowledgement"; bitsofall "LoRA (Low-Rank Adaptation)"), applied to the
- * projections that read one normed input (q/k/v, gate/up).  For m <= 128 the
+ * projections that read one normed input (q/k/v, gate/up).  For m <= 256 the
  * segments share the launches (so a decode step spends two launches, not two
  * per projection, on them); the K split is chosen for all segments together, so
  * the FP32 summation order, and with it the last bit of y, can differ from

@@ -353,7 +353,7 @@ def w4a16_lora_gemm_multi(x: torch.Tensor, segments, outs=None, workspace: torch
                           stream=None):
     """Several projections of x in one call: segments is a list of
     (wq, lora_a, lora_b, lora_scale) (LoRA None for none); returns the outputs
-    (given in ``outs`` or allocated).  For M <= 128 they share one launch."""
+    (given in ``outs`` or allocated).  For M <= 256 they share one launch."""
     _need(x, "x", torch.bfloat16, 2)
     if not 1 <= len(segments) <= MAX_SEGMENTS:
         raise ValueError(f"1 to {MAX_SEGMENTS} segments")

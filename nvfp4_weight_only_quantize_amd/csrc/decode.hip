@@ -1,5 +1,5 @@
 // decode.hip -- W4A16 (NVFP4 weight x BF16 activation) + LoRA for decode
-// batches, 1 <= m <= 128, on gfx950.
+// batches, 1 <= m <= 256, on gfx950.
 //
 //   y[m, n] = s_t * sum_k x[m,k] e2m1(q[n,k]) e4m3(sb[n,k/16])
 //           + lora_scale * sum_j t[m,j] B[n,j],        t = x A^T
@@ -28,8 +28,10 @@
 // group of loads in flight per wave, and latency is covered by several
 // resident units per CU (registers are capped for that).
 //
-// 16 < m <= 128, mfma_unit_kernel.  Units are (256 weight rows) x (slice of K)
-// running the K loops of mfma_tile.h with all of x as the x tile.
+// 16 < m <= 256, mfma_unit_kernel.  Units are (256 weight rows) x (slice of K)
+// running the K loops of mfma_tile.h with up to 128 rows of x as the x tile
+// (m > 128: one unit per 128-row m-block of x, the m-blocks one after another
+// in the grid).
 //
 // Several projections of one x (q/k/v, gate/up) share a launch: the segment
 // is a grid dimension; a one-segment launch is its own instantiation with a
@@ -90,6 +92,7 @@ constexpr int64_t kMaxRowBlocks = (int64_t)1 << 24;  // row blocks of one call (
 
 struct DecodePlan {
     int mt, nw, px;
+    int mb, mtp;                   // m-blocks of 16 mt rows (a unit takes one), m-tiles of the producers (mb mt)
     int64_t rows_per_unit, row_blocks;
     int64_t chunks, full_chunks;   // chunks of K (the last may be partial), full chunks
     int64_t cps, slices, units;    // chunks per slice (a multiple of 4/nw)
@@ -130,6 +133,8 @@ int64_t cu_count() {
 DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slice_rows = 0, bool norm = false) {
     DecodePlan p{};
     p.mt = m <= 16 ? 1 : (m <= 32 ? 2 : (m <= 64 ? 4 : 8));
+    p.mb = (int)((m + 16 * p.mt - 1) / (16 * p.mt));  // more than one for m > 128
+    p.mtp = p.mb * p.mt;
     p.nw = p.mt == 1 ? 1 : kUnitWaves * 4 / kWaves;  // 16 < m: MFMA units of 64 kUnitWaves weight rows
     p.rows_per_unit = p.mt == 1 ? 16 * kSW : 16 * kWaves * (int64_t)p.nw;
     p.row_blocks = (n + p.rows_per_unit - 1) / p.rows_per_unit;
@@ -141,7 +146,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     p.prod_chunks = (p.chunks + kMaxProdRanges - 1) / kMaxProdRanges;
     if (p.prod_chunks < kProdChunks) p.prod_chunks = kProdChunks;
     p.prod_kr = (p.chunks + p.prod_chunks - 1) / p.prod_chunks;
-    p.prod_groups = p.mt * ((p.jt + kProdTiles - 1) / kProdTiles);
+    p.prod_groups = p.mtp * ((p.jt + kProdTiles - 1) / kProdTiles);
     p.norm = norm && p.mt == 1;
     if (p.norm && p.prod_groups < 1) p.prod_groups = 1;  // sums of squares only
     p.producers = (r > 0 || p.norm) ? p.prod_kr * p.prod_groups : 0;
@@ -161,20 +166,20 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
         // per CU keep more loads in flight than one long unit)
         const int64_t s_work = p.chunks / kUnitMinChunks;
         if (s < s_work) s = s_work < s_cap ? s_work : s_cap;
-        const int64_t s_occ = (cu_count() * kMfmaUnitsPerCu + slice_rows - 1) / slice_rows;
+        const int64_t s_occ = (cu_count() * kMfmaUnitsPerCu + slice_rows * p.mb - 1) / (slice_rows * p.mb);
         const int64_t s_most = p.chunks / 2 < s_cap ? p.chunks / 2 : s_cap;  // at least two chunks per unit
         if (s < s_occ) s = s_occ < s_most ? s_occ : s_most;
         if (s < 1) s = 1;
         p.cps = (p.chunks + s - 1) / s;
         p.slices = (p.chunks + p.cps - 1) / p.cps;
-        p.units = p.row_blocks * p.slices;
+        p.units = p.row_blocks * p.slices * p.mb;
         int64_t scp = (p.cps * 8 + 15) / 16;  // rows an odd multiple of 16 bytes apart
         if (scp % 2 == 0) ++scp;
         p.unit_sc_pitch = scp * 16;
         p.unit_sc = p.rows_per_unit * p.unit_sc_pitch <= kUnitScBytes;
         p.part_off = 0;
         p.tpart_off = align256(p.part_off + p.units * tile);
-        p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
+        p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mtp * p.jt * 64 * 16);
         p.bytes = p.ss_off;
         return p;
     }
@@ -208,7 +213,7 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     // the producers' partial tiles of t, their sums of squares
     p.part_off = 0;
     p.tpart_off = align256(p.part_off + p.units * tile);
-    p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mt * p.jt * 64 * 16);
+    p.ss_off = align256(p.tpart_off + p.prod_kr * (int64_t)p.mtp * p.jt * 64 * 16);
     p.bytes = align256(p.ss_off + (p.norm ? p.prod_kr * 16 * 4 : 0));
     return p;
 }
@@ -275,7 +280,7 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     const int grp = (int)(p - kr * d.p.prod_groups);
     const int64_t kb = kr * d.p.prod_chunks * kChunkK;
     const int64_t ke = kb + d.p.prod_chunks * kChunkK < a.k ? kb + d.p.prod_chunks * kChunkK : a.k;
-    const int64_t tile_floats = (int64_t)MT * JT * 64 * 4;
+    const int64_t tile_floats = (int64_t)d.p.mtp * JT * 64 * 4;  // all m-tiles of x
     f32x4_t *own = reinterpret_cast<f32x4_t *>(d.tpart() + kr * tile_floats);  // this K range's tiles
     f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
     float *red_ss = reinterpret_cast<float *>(lds + kWaves * kProdTiles * 64 * 16);  // [wave][16]
@@ -710,9 +715,11 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
     const int64_t rblk = nc / R, rem = nc - rblk * R;
     const int64_t wave = rem / (16 * NW), g = (rem / 16) % NW, lr = rem % 16;
     const int64_t lq = quad % 4;
-    const int64_t slot = ((wave * MT + mt) * NW + g) * 64 + lq * 16 + lr;
+    const int mtl = mt % MT;  // m-tile in its m-block (units of m-block mt / MT follow those of the ones before)
+    const int64_t slot = ((wave * MT + mtl) * NW + g) * 64 + lq * 16 + lr;
     const int64_t tile_floats = R * 16 * MT;
-    const float *part_base = d.part() + rblk * tile_floats + slot * 4;
+    const float *part_base =
+        d.part() + ((int64_t)(mt / MT) * p.slices * p.row_blocks + rblk) * tile_floats + slot * 4;
     const int64_t sstride = p.row_blocks * tile_floats;  // floats between slices
     const int pp = part < P ? part : 0;
     const int64_t s0 = p.slices * pp / P, s1 = p.slices * (pp + 1) / P;
@@ -733,7 +740,7 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
         bq[u] = b0 + u < b1 ? *reinterpret_cast<const uint4 *>(br + 8 * (b0 + u)) : make_uint4(0, 0, 0, 0);
     const int JT = (int)p.jt, items = JT * 64, PT = items >= 256 ? 1 : 256 / items;
     const f32x4_t *tp = reinterpret_cast<const f32x4_t *>(d.tpart()) + ((int64_t)mt * JT) * 64;
-    const int64_t kstride = (int64_t)MT * JT * 64;  // f32x4 between K ranges
+    const int64_t kstride = (int64_t)p.mtp * JT * 64;  // f32x4 between K ranges
     // (r <= 64: one (item, run) per thread; larger ranks take a second one)
     auto t_run = [&](int w, int64_t &kr0, int64_t &kr1) {
         const int q = w / items;
@@ -880,7 +887,11 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     constexpr int NW = 4 * kUnitWaves / kWaves;  // n-tiles per wave of the four-wave tile layout
     constexpr int kPer = kUnitWaves / kWaves;     // unit waves per layout wave
     const int64_t u = bx - p.producers;
-    const int64_t slice = u / p.row_blocks, rblk = u - slice * p.row_blocks;
+    // unit u: m-block mbi (16 MT rows of x), then slice, then row block
+    const int64_t mbi = u / (p.slices * p.row_blocks), us = u - mbi * p.slices * p.row_blocks;
+    const int64_t slice = us / p.row_blocks, rblk = us - slice * p.row_blocks;
+    const uint16_t *xb = a.x + mbi * 16 * MT * a.ldx;  // this m-block's rows of x
+    const int64_t mrows = a.m - mbi * 16 * MT < 16 * MT ? a.m - mbi * 16 * MT : 16 * MT;
     const int64_t c_begin = slice * p.cps;
     const int64_t c_end = c_begin + p.cps < p.chunks ? c_begin + p.cps : p.chunks;
     const int64_t c_full_end = c_end < p.full_chunks ? c_end : p.full_chunks;
@@ -899,7 +910,7 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
         stage_scales(a, g_dsc, p.unit_sc_pitch, n0, p.rows_per_unit, c_begin * 8, (fast_end - c_begin) * 8);
         __syncthreads();
     }
-    mfma_kloop<MT, kUnitWaves, 1, SCL>(a.x, a.m, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k,
+    mfma_kloop<MT, kUnitWaves, 1, SCL>(xb, mrows, a.ldx, a.packed + n0 * kb, a.scales + n0 * ks, a.n - n0, a.k,
                                        c_begin, fast_end, MT == 8 ? g_dxtile8_0 : g_dxtile0,
                                        MT == 8 ? g_dxtile8_1 : g_dxtile1, acc, g_dsc, (int)p.unit_sc_pitch);
     // the rest of the slice (the partial last chunk of K, or all of it for
@@ -909,7 +920,7 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
         fast_end * kChunkK, c_end * kChunkK < a.k ? c_end * kChunkK : a.k, MT == 8 ? g_dxtile8_0 : g_dxtile0,
         [&](int row, int64_t kk) {
             uint4 o = make_uint4(0, 0, 0, 0);
-            if (row < a.m && kk < a.k) o = *reinterpret_cast<const uint4 *>(a.x + row * a.ldx + kk);
+            if (row < mrows && kk < a.k) o = *reinterpret_cast<const uint4 *>(xb + row * a.ldx + kk);
             return o;
         },
         [&](int j, int64_t kk) {
@@ -926,7 +937,7 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (16 * i + 4 * lq < a.m) tile[(((wave / kPer) * MT + i) * NW + (4 * wave + j) % NW) * 64] = acc[i][j];
+            if (16 * i + 4 * lq < mrows) tile[(((wave / kPer) * MT + i) * NW + (4 * wave + j) % NW) * 64] = acc[i][j];
 }
 
 template <int NS, int MT, bool SCL>
@@ -1101,11 +1112,12 @@ int decode_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int 
         // unit ((layout wave MT + i) NW + n-tile) 64 + lane
         const int64_t slots = p.mt == 1 ? (int64_t)kSW * 64 : (int64_t)4 * p.mt * p.nw * 64;
         if (slots * 16 > tile) return fail("unit tile slots", j, slots * 16, tile);
-        if (p.units != p.row_blocks * p.slices) return fail("units", j, p.units, p.row_blocks * p.slices);
+        if (p.units != p.row_blocks * p.slices * p.mb) return fail("units", j, p.units, p.row_blocks * p.slices * p.mb);
+        if ((int64_t)p.mb * 16 * p.mt < m) return fail("m-blocks", j, m, (int64_t)p.mb * 16 * p.mt);
         const int64_t units_end = p.part_off + p.units * tile;  // written by the units, read by finish_kernel
         if (units_end > p.tpart_off) return fail("unit tiles past their region", j, units_end, p.tpart_off);
         // producers: f32x4 (mt JT + rank tile) 64 + lane of K range kr < prod_kr
-        const int64_t prod_end = p.tpart_off + (p.producers ? p.prod_kr * p.mt * p.jt * 64 * 16 : 0);
+        const int64_t prod_end = p.tpart_off + (p.producers ? p.prod_kr * p.mtp * p.jt * 64 * 16 : 0);
         if (prod_end > p.ss_off) return fail("producer tiles past their region", j, prod_end, p.ss_off);
         const int64_t ss_end = p.ss_off + (p.norm && p.producers ? p.prod_kr * 16 * 4 : 0);
         if (ss_end > p.bytes) return fail("sums of squares past the plan", j, ss_end, p.bytes);

@@ -10,7 +10,7 @@
 // same kernel as its "Implementation and Practical Details" section asks
 // ("NVFP4 + LoRA summation").
 //
-// Larger m (m > 128; m <= 128 is the decode path of decode.hip):
+// Larger m (m > 256; m <= 256 is the decode path of decode.hip):
 //   prologue_kernel  t = x A^T in FP32 (MFMA, 16 rows of x per workgroup),
 //                    pre-multiplied by lora_scale / s_t and split into BF16
 //                    hi + lo halves, so that the LoRA product becomes 2r extra
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void t_reduce_kernel(Gemm g) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA path (m > 128)
+// MFMA path (m > 256)
 // ---------------------------------------------------------------------------
 // Workgroup tile 128 (rows of x) x 256 (weight rows): four waves side by
 // side along n, each the full 128 x 64, so no weight fragment is fetched
@@ -598,7 +598,7 @@ hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t st
 }
 
 // The workspace use of one projection's launch against its size query (the
-// decode plan's own check for m <= 128): the prologue's t region [m][r] four
+// decode plan's own check for m <= 256): the prologue's t region [m][r] four
 // bytes each (BF16 hi/lo or FP32), the split counters and partial tiles, and
 // the grid limits.
 int gemm_plan_check(int64_t m, int64_t n, int64_t k, int r, int64_t size, char *msg, size_t len) {

@@ -52,7 +52,7 @@ hipError_t launch_w4a16_lora_gemm(const GemmArgs &a, hipStream_t stream);
 // (QERL_NOALLOC_SCRATCH_BYTES), looked up on the first call on each device
 hipError_t noalloc_scratch(void **ptr);
 // decode batches (m <= kDecodeMaxM): HBM-streaming path in decode.hip
-constexpr int64_t kDecodeMaxM = 128;
+constexpr int64_t kDecodeMaxM = 256;
 size_t decode_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 hipError_t launch_decode(const GemmArgs &a, hipStream_t stream);
 // Several GEMMs sharing x (m, k, ldx) in one launch: segs[i] differ only in
@@ -69,7 +69,7 @@ constexpr int64_t kNormFuseMaxM = 16;
 size_t norm_gemm_multi_workspace_bytes(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg);
 hipError_t launch_norm_gemm_multi(const GemmArgs *segs, int nseg, hipStream_t stream);
 // Host checks of a launch's workspace use against its size query (0: in
-// bounds; else a message in msg): decode (m <= 128) launches over segments of
+// bounds; else a message in msg): decode (m <= 256) launches over segments of
 // one x, one projection's launch for a workspace of `size` bytes, and the
 // multi-segment calls with or without the RMSNorm.
 int decode_plan_check(int64_t m, int64_t k, const int64_t *n, const int *r, int nseg, bool norm, char *msg,

@@ -151,12 +151,12 @@ def test_gemm_multi_argument_errors(nseg, segs_kw, kw, status):
 def test_gemm_multi_workspace_query():
     shapes = [(3584, 32), (512, 32), (512, 32)]
     # decode sizes: one region per segment
-    for m in (1, 8, 64, 128):
+    for m in (1, 8, 64, 128, 256):
         total = q.w4a16_lora_gemm_multi_workspace_size(m, 3584, shapes)
         assert total >= 3 * 64 * 1024
-    # large m (above 128) runs the segments in turn over one region: the largest single need
-    big = q.w4a16_lora_gemm_multi_workspace_size(129, 3584, shapes)
-    assert big == max(q.w4a16_lora_gemm_workspace_size(129, n, 3584, r) for n, r in shapes)
+    # large m (above 256) runs the segments in turn over one region: the largest single need
+    big = q.w4a16_lora_gemm_multi_workspace_size(257, 3584, shapes)
+    assert big == max(q.w4a16_lora_gemm_workspace_size(257, n, 3584, r) for n, r in shapes)
     assert q.lib().qerl_w4a16_lora_gemm_multi_workspace_size(1, 3584, None, 3) == 0
 
 

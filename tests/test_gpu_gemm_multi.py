@@ -1,5 +1,5 @@
 """GPU qerl_w4a16_lora_gemm_multi: several projections of one activation in
-one call (for M <= 128 one launch), each against the fp64 oracle and against
+one call (for M <= 256 one launch), each against the fp64 oracle and against
 the single-projection call; bit-for-bit repeatability with a shared workspace.
 Tolerances as for the single call (relative L2 <= 5e-3, max |y - y_ref| <=
 1e-2 max |y_ref|)."""
@@ -41,11 +41,11 @@ def test_multi_7b_gate_up(m):
     _check(layers, m, k, seed=synth.seed_for(1007, "x", m), rows=None if m == 1 else [0, 7, 15])
 
 
-@pytest.mark.parametrize("m", [1, 5, 24, 100, 129])
+@pytest.mark.parametrize("m", [1, 5, 24, 100, 200, 257])
 def test_multi_mixed_ranks_and_widths(m):
     # four segments: ranks 16, 0 (no LoRA), 8, 4 and widths that are no
-    # multiple of the unit; m = 100 takes eight m-tiles per unit, m = 129 the
-    # large-m path one segment at a time
+    # multiple of the unit; m = 100 takes eight m-tiles per unit, m = 200 two
+    # m-blocks of them, m = 257 the large-m path one segment at a time
     k = 512
     layers = [Layer(n, k, r, seed=1100 + n + r) for n, r in ((96, 16), (77, 0), (130, 8), (64, 4))]
     _check(layers, m, k, seed=1200 + m)
