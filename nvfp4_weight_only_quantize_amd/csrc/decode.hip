@@ -866,7 +866,7 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
 // the first four waves of a producer work.
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile0[64 * kTileRowBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile1[64 * kTileRowBytes];
-// the x tiles of eight m-tiles (65 <= m <= 128), a kernel of their own
+// the x tiles of eight m-tiles (m > 64: one 128-row m-block), a kernel of their own
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile8_0[128 * kTileRowBytes];
 __shared__ __attribute__((aligned(1024))) uint8_t g_dxtile8_1[128 * kTileRowBytes];
 // the unit's scale bytes (256 rows x its slice), when they fit: 2-byte

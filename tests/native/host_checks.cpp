@@ -49,7 +49,7 @@ int main() {
         {{3584, 3584}, {512, 3584}, {512, 3584}, {3584, 3584}, {18944, 3584}, {18944, 3584}, {3584, 18944}},
         {{5120, 5120}, {1024, 5120}, {1024, 5120}, {5120, 5120}, {27648, 5120}, {27648, 5120}, {5120, 27648}}};
     const int ranks[] = {0, 8, 16, 32, 64, 128};
-    const int64_t big_m[] = {65, 100, 128, 256, 300, 1000, 2048, 8192};
+    const int64_t big_m[] = {65, 100, 128, 129, 192, 200, 256, 257, 300, 1000, 2048, 8192};
     for (const auto &layer : layers) {
         for (const int r : ranks) {
             for (int64_t m = 1; m <= 64; ++m)
