@@ -280,7 +280,7 @@ __device__ void lora_producer(const Decode &d, int64_t p, uint8_t *lds) {
     const int grp = (int)(p - kr * d.p.prod_groups);
     const int64_t kb = kr * d.p.prod_chunks * kChunkK;
     const int64_t ke = kb + d.p.prod_chunks * kChunkK < a.k ? kb + d.p.prod_chunks * kChunkK : a.k;
-    const int64_t tile_floats = (int64_t)d.p.mtp * JT * 64 * 4;  // all m-tiles of x
+    const int64_t tile_floats = (int64_t)(MT == 8 ? d.p.mtp : MT) * JT * 64 * 4;  // all m-tiles of x (m-blocks: MT == 8)
     f32x4_t *own = reinterpret_cast<f32x4_t *>(d.tpart() + kr * tile_floats);  // this K range's tiles
     f32x4_t *red = reinterpret_cast<f32x4_t *>(lds);  // [wave][2 tiles][64 lanes]
     float *red_ss = reinterpret_cast<float *>(lds + kWaves * kProdTiles * 64 * 16);  // [wave][16]
@@ -715,11 +715,13 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
     const int64_t rblk = nc / R, rem = nc - rblk * R;
     const int64_t wave = rem / (16 * NW), g = (rem / 16) % NW, lr = rem % 16;
     const int64_t lq = quad % 4;
-    const int mtl = mt % MT;  // m-tile in its m-block (units of m-block mt / MT follow those of the ones before)
+    // m-tile mt is m-tile mt % MT of m-block mt / MT, whose units follow those
+    // of the m-blocks before it (only units of eight m-tiles have several)
+    const int mtl = MT == 8 ? mt % MT : mt;
+    const int64_t mblk = MT == 8 ? mt / MT : 0;
     const int64_t slot = ((wave * MT + mtl) * NW + g) * 64 + lq * 16 + lr;
     const int64_t tile_floats = R * 16 * MT;
-    const float *part_base =
-        d.part() + ((int64_t)(mt / MT) * p.slices * p.row_blocks + rblk) * tile_floats + slot * 4;
+    const float *part_base = d.part() + (mblk * p.slices * p.row_blocks + rblk) * tile_floats + slot * 4;
     const int64_t sstride = p.row_blocks * tile_floats;  // floats between slices
     const int pp = part < P ? part : 0;
     const int64_t s0 = p.slices * pp / P, s1 = p.slices * (pp + 1) / P;
@@ -740,7 +742,7 @@ __global__ __launch_bounds__(256) void finish_kernel(DecodeSetN<NS> ds) {
         bq[u] = b0 + u < b1 ? *reinterpret_cast<const uint4 *>(br + 8 * (b0 + u)) : make_uint4(0, 0, 0, 0);
     const int JT = (int)p.jt, items = JT * 64, PT = items >= 256 ? 1 : 256 / items;
     const f32x4_t *tp = reinterpret_cast<const f32x4_t *>(d.tpart()) + ((int64_t)mt * JT) * 64;
-    const int64_t kstride = (int64_t)p.mtp * JT * 64;  // f32x4 between K ranges
+    const int64_t kstride = (int64_t)(MT == 8 ? p.mtp : MT) * JT * 64;  // f32x4 between K ranges
     // (r <= 64: one (item, run) per thread; larger ranks take a second one)
     auto t_run = [&](int w, int64_t &kr0, int64_t &kr1) {
         const int q = w / items;
@@ -888,7 +890,7 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     constexpr int kPer = kUnitWaves / kWaves;     // unit waves per layout wave
     const int64_t u = bx - p.producers;
     // unit u: m-block mbi (16 MT rows of x), then slice, then row block
-    const int64_t mbi = u / (p.slices * p.row_blocks), us = u - mbi * p.slices * p.row_blocks;
+    const int64_t mbi = MT == 8 ? u / (p.slices * p.row_blocks) : 0, us = u - mbi * p.slices * p.row_blocks;
     const int64_t slice = us / p.row_blocks, rblk = us - slice * p.row_blocks;
     const uint16_t *xb = a.x + mbi * 16 * MT * a.ldx;  // this m-block's rows of x
     const int64_t mrows = a.m - mbi * 16 * MT < 16 * MT ? a.m - mbi * 16 * MT : 16 * MT;
