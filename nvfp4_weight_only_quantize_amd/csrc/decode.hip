@@ -888,8 +888,26 @@ __device__ __forceinline__ void mfma_unit(const Decode &d, int64_t bx) {
     }
     constexpr int NW = 4 * kUnitWaves / kWaves;  // n-tiles per wave of the four-wave tile layout
     constexpr int kPer = kUnitWaves / kWaves;     // unit waves per layout wave
-    const int64_t u = bx - p.producers;
-    // unit u: m-block mbi (16 MT rows of x), then slice, then row block
+    int64_t u = bx - p.producers;
+    // unit u: m-block mbi (16 MT rows of x), then slice, then row block.  With
+    // several m-blocks the grid runs the units of one (slice, row block) eight
+    // workgroups apart, so that they share an XCD (workgroups go to the XCDs
+    // in turn) and its L2 copy of the weights: u is recovered from the
+    // position v as below (the last group of fewer than eight in order)
+    if (MT == 8 && p.mb > 1) {
+        const int64_t W = p.slices * p.row_blocks, full = W / 8 * 8, v = u;
+        int64_t w, mb_i;
+        if (v < full * p.mb) {
+            const int64_t q = v / 8;
+            mb_i = q % p.mb;
+            w = q / p.mb * 8 + v % 8;
+        } else {
+            const int64_t t = v - full * p.mb;
+            w = full + t / p.mb;
+            mb_i = t % p.mb;
+        }
+        u = mb_i * W + w;
+    }
     const int64_t mbi = MT == 8 ? u / (p.slices * p.row_blocks) : 0, us = u - mbi * p.slices * p.row_blocks;
     const int64_t slice = us / p.row_blocks, rblk = us - slice * p.row_blocks;
     const uint16_t *xb = a.x + mbi * 16 * MT * a.ldx;  // this m-block's rows of x
