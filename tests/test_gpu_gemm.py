@@ -276,12 +276,14 @@ def test_prefill_scale_chunks(m, n, k, r):
 
 
 @pytest.mark.parametrize("s_t", [1e-39, 1e-30, 1e-18])
-@pytest.mark.parametrize("m", [257, 300])
+@pytest.mark.parametrize("m", [257, 300, 1000])
 def test_tiny_tensor_scale(m, s_t):
     """The prefill path folds lambda / s_t into its accumulation only while
     that factor is finite and moderate; for a subnormal or tiny s_t the LoRA
     term is added in the epilogue (split and unsplit K both: 300 x 1000 x 2048
-    splits, 257 x 96 x 256 does not).  Decode (m <= 256) applies s_t apart."""
+    splits, 257 x 96 x 256 does not; at m = 1000 the four splits of 1000 x 1000 x
+    2048 meet in the launch, at m = 300 in a reduce launch).  Decode (m <= 256)
+    applies s_t apart."""
     for n, k, r in ((96, 256, 16), (1000, 2048, 32)):
         L = Layer(n, k, r, seed=900 + n + m)
         L.s_t = np.float32(s_t)
