@@ -427,7 +427,7 @@ __global__ __launch_bounds__(64 * kPfWaves, 8 / kPfWaves) void prefill_kernel(Ge
                 }
         }
         if (!p.meet) return;
-        // the arrival's verdict goes through the scale chunk's LDS, idle once
+        // the arrival's outcome goes through the scale chunk's LDS, idle once
         // every wave has passed the barrier below
         volatile uint32_t *s_fin = reinterpret_cast<volatile uint32_t *>(g_sctile1);
         wait_vmcnt<0>();  // this wave's stores have completed
