@@ -80,13 +80,13 @@ constexpr int kProdTiles = 1;             // rank tiles a producer accumulates
 constexpr int kBatch = 8;                // loads in flight per thread in reductions and staging
 constexpr int kMaxRank = 128;            // QERL_MAX_LORA_RANK
 constexpr int64_t kUnitScBytes = 24 * 1024;  // 16 < m: LDS for a unit's scale tile
-#ifndef QERL_MFMA_MIN_CHUNKS
-#define QERL_MFMA_MIN_CHUNKS 8
+#ifndef QERL_MFMA_UNIT_CHUNKS
+#define QERL_MFMA_UNIT_CHUNKS 10
 #endif
 #ifndef QERL_MFMA_UNITS_PER_CU
 #define QERL_MFMA_UNITS_PER_CU 1
 #endif
-constexpr int64_t kUnitMinChunks = QERL_MFMA_MIN_CHUNKS;      // 16 < m: K chunks per unit the split may go down to
+constexpr int64_t kUnitChunks = QERL_MFMA_UNIT_CHUNKS;        // 16 < m: K chunks per unit the split aims for, at most
 constexpr int64_t kMfmaUnitsPerCu = QERL_MFMA_UNITS_PER_CU;  // 16 < m: units per CU the K split aims for
 constexpr int64_t kMaxRowBlocks = (int64_t)1 << 24;  // row blocks of one call (grid x stays in range)
 
@@ -161,10 +161,13 @@ DecodePlan make_decode_plan(int64_t m, int64_t n, int64_t k, int r, int64_t slic
     if (s < 1) s = 1;
     const int64_t tile = p.rows_per_unit * 16 * p.mt * 4;
     if (p.mt > 1) {  // mfma_unit_kernel: static LDS, the whole x as its x tile
-        // fewer row blocks than CUs split K as above; more keep at least
-        // kUnitMinChunks chunks per unit but still split K (several units
-        // per CU keep more loads in flight than one long unit)
-        const int64_t s_work = p.chunks / kUnitMinChunks;
+        // fewer row blocks than CUs split K as above; more still split K so
+        // that a unit takes at most kUnitChunks chunks (several units per CU
+        // keep more loads in flight than one long unit): 32B layer at M = 64
+        // 201 -> 188 us against the floor of chunks / 8 (4 slices of 10 chunks
+        // for K = 5120 rather than 5 of 8, 22 rather than 27 for K = 27648),
+        // the 7B layer unchanged
+        const int64_t s_work = (p.chunks + kUnitChunks - 1) / kUnitChunks;
         if (s < s_work) s = s_work < s_cap ? s_work : s_cap;
         const int64_t s_occ = (cu_count() * kMfmaUnitsPerCu + slice_rows * p.mb - 1) / (slice_rows * p.mb);
         const int64_t s_most = p.chunks / 2 < s_cap ? p.chunks / 2 : s_cap;  // at least two chunks per unit
