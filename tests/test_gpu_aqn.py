@@ -59,6 +59,15 @@ def test_config3_4_width_5120(m):
     _check(*out, what=f"m={m}")
 
 
+@pytest.mark.parametrize("m,h", [(600, 8), (600, 1000), (517, 8192), (513, 8200), (600, 16384), (700, 37)])
+def test_large_m_whole_rows(m, h):
+    """Above 512 rows a workgroup takes whole rows (the vector-aligned widths
+    here; 37 keeps the per-channel path): row groups with a ragged last one,
+    the widest rows, and a width with pieces past the last full thread."""
+    out = _run(m, h, 1e-2, seed=13, step=5, layer=2, x_seed=100 + h)
+    _check(*out, what=f"m={m} h={h}")
+
+
 @pytest.mark.parametrize("h", [1, 3, 37, 1000, 4095, 16384])
 def test_ragged_widths(h):
     out = _run(3, h, 1e-2, seed=9, step=1, layer=0, x_seed=70 + h)
