@@ -32,11 +32,13 @@
 // c as the exact one.  Why that holds: with s_t of more than 8 significant
 // bits, c e s_t has more significant bits than any BF16 |w|, so |w| is never
 // a midpoint exactly, and when |w| != c e s_t the two differ by at least
-// 2^-33 relative (|w| has 8 significant bits, c e s_t at most 33).  q is
-// formed in float-float, q_hi + q_lo with a relative error below 2^-45, from
-// 1 / (e s_t) taken in double; s = fl(q_hi + q_lo) is then on the exact
-// side of every midpoint or equal to one, and an element whose s is equal to
-// one (low 21 mantissa bits zero) is decided again by the comparisons above.
+// 2^-33 relative (|w| has 8 significant bits, c e s_t at most 33).  1 /
+// (e s_t), taken in double, is split into r_hi of 16 significant bits and r_lo
+// = fl(r - r_hi), together within 2^-39 relative of it; w r_hi is exact (8 + 16
+// bits) and s = fma(w, r_lo, w r_hi) rounds w (r_hi + r_lo) once, so s is on
+// the exact side of every midpoint or equal to one (midpoints are floats and
+// rounding is monotone), and an element whose s is equal to one (low 21
+// mantissa bits zero) is decided again by the comparisons above.
 #include "device_common.h"
 #include "qerl_internal.h"
 
@@ -271,12 +273,10 @@ __device__ __forceinline__ bool fast_path_scale(float st) {
     return __builtin_ctz(sig) < 16;  // odd part of at least 9 bits
 }
 
-// q ~ f / (e s_t) as fl(q_hi + q_lo): r_hi + r_lo ~ 1 / (e s_t)
+// q ~ f / (e s_t) as fl(f (r_hi + r_lo)): r_hi + r_lo ~ 1 / (e s_t), r_hi of
+// 16 significant bits, so f r_hi is exact for a BF16 f
 __device__ __forceinline__ float fast_quotient(float f, float rh, float rl) {
-    const float qh = f * rh;
-    const float t = __builtin_fmaf(f, rh, -qh);  // the product's rounding error, exact
-    const float ql = __builtin_fmaf(f, rl, t);
-    return qh + ql;
+    return __builtin_fmaf(f, rl, f * rh);
 }
 
 // s is E2M1-grid aligned (a midpoint or grid value: low 21 mantissa bits
@@ -402,7 +402,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(EncodeParams p) {
             bool done = false;
             if (fast && am < 0x7F80u) {  // (finite block)
                 const double r = inv_st * s_inv_e[sb];
-                const float rh = (float)r, rl = (float)(r - (double)rh);
+                const float rh = __uint_as_float(__float_as_uint((float)r) & 0xFFFFFF00u);  // 16 significant bits
+                const float rl = (float)(r - (double)rh);
                 if (amax_b * rh < 0x1p100f) {
                     uint32_t suspect = 0;  // bit j: element j's quotient fell on an aligned value
                     lo = fast_codes4<0>(wd[0], wd[1], wd[2], wd[3], rh, rl, suspect);
